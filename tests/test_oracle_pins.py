@@ -1,0 +1,596 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: a library
+routine (numpy's fp16 cast, SVD, eigh), a closed form, an invariant, a value
+printed on the pages (tests/golden/), or brute force on tiny inputs.  They are
+chosen so that a plausible slip in oracle.c (a dropped term, a wrong sign or
+index, a transposed operand, a wrong rounding) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from rank_latent_kv_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ------------------------------------------------------------------ fp16
+
+def test_half_to_float_all_patterns_match_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.half_to_float(bits)
+    ref = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_float_to_half_rne_matches_numpy():
+    rng = np.random.default_rng(5)
+    parts = [
+        rng.standard_normal(200000).astype(np.float32) * 10.0 ** rng.integers(-9, 6, 200000),
+        # exact halfway points between adjacent fp16 values (ties to even)
+        (np.arange(0, 65504, dtype=np.float32) + 0.5).astype(np.float32),
+        np.float32([65504, 65519.99, 65520, 65536, 1e9, -65520, 2.0 ** -24,
+                    2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -14, 2.0 ** -14 * 0.9999,
+                    0.0, -0.0, np.inf, -np.inf]),
+    ]
+    # subnormal halfway points: (k + 0.5) * 2^-24
+    parts.append(((np.arange(0, 1024, dtype=np.float32) + 0.5) * np.float32(2.0 ** -24)))
+    f = np.concatenate(parts).astype(np.float32)
+    ours = oracle.float_to_half_bits(f)
+    ref = f.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+# ----------------------------------------------------------- energy rule
+
+def test_energy_rank_dyadic_cases():
+    # energies are dyadic so every partial sum is exact; >= is inclusive
+    s2 = [0.5, 0.25, 0.125, 0.125]
+    assert oracle.energy_rank(s2, 0.5) == 1
+    assert oracle.energy_rank(s2, 0.75) == 2
+    assert oracle.energy_rank(s2, 0.8) == 3
+    assert oracle.energy_rank(s2, 0.875) == 3
+    assert oracle.energy_rank(s2, 0.9) == 4
+    assert oracle.energy_rank(s2, 1.0) == 4
+    assert oracle.energy_rank([0.0, 0.0, 0.0], 0.9) == 1      # no energy
+    assert oracle.energy_rank([1.0] + [0.0] * 127, 0.9) == 1
+    # sum of squares, not of singular values: sigma = (3, 2, 2, 1, 1, 1)
+    # sigma^2 = 9,4,4,1,1,1 (total 20); 90% = 18 reached at k = 4 (18);
+    # the sigma-sum reading (total 10) would need 9 of 10 -> k = 5.
+    assert oracle.energy_rank([9.0, 4.0, 4.0, 1.0, 1.0, 1.0], 0.9) == 4
+
+
+def _planted(N, D, sigmas, mu, seed):
+    """X = 1 mu^T + U diag(sigma) W^T with U orthonormal and orthogonal to 1."""
+    rng = np.random.default_rng(seed)
+    k = len(sigmas)
+    U = rng.standard_normal((N, k))
+    U -= U.mean(axis=0)
+    U, _ = np.linalg.qr(U)
+    W, _ = np.linalg.qr(rng.standard_normal((D, k)))
+    return mu[None, :] + U @ np.diag(sigmas) @ W.T, W
+
+
+@pytest.mark.parametrize("expect", [1, 3, 7, 20])
+def test_energy_rule_on_planted_spectrum(expect):
+    """Spectrum with a known 90%-energy crossing; margin >= 2% of the energy
+    either side so fp16 rounding of the data cannot move it."""
+    D, N = 64, 3000
+    rng = np.random.default_rng(100 + expect)
+    # energies: `expect` big directions, then a small flat floor
+    big = np.full(expect, 1.0)
+    floor_n = 30
+    # choose floor energy so cumulative(expect) = 0.93 of total
+    floor_e = (expect / 0.93 - expect) / floor_n
+    e = np.concatenate([big * (1 + 0.01 * np.arange(expect)[::-1]), np.full(floor_n, floor_e)])
+    s = np.sqrt(e / e.sum()) * 40.0
+    X, _ = _planted(N, D, s, rng.normal(0, 0.5, D), seed=expect)
+    x16 = X.astype(np.float16)[None, None]  # [1,1,N,D]
+    # the fp16 data's own spectrum (numpy) keeps the crossing where planted
+    c = x16[0, 0].astype(np.float64)
+    sv = np.linalg.svd(c - c.mean(0), compute_uv=False) ** 2
+    cum = np.cumsum(sv) / sv.sum()
+    assert cum[expect - 1] >= 0.92 and (expect == 1 or cum[expect - 2] < 0.9)
+    f = oracle.fit(x16, [N], 1, rank=0, tau=0.90)
+    assert f.r == expect
+
+
+def test_energy_rank_in_range_and_shared_minimum():
+    w = synth.small_workload(n_kv_heads=4, n_head_groups=4, prefill=256, rank=None)
+    x = synth.batch_kv(w, 0, 256)
+    f = oracle.fit(x, [256] * w.batch, 4, rank=0, tau=0.9)
+    assert all(1 <= r <= 128 for r in f.r_groups)
+    assert f.r == min(f.r_groups)
+    # explicit rank overrides the rule and is clamped to D
+    assert oracle.fit(x, [256] * w.batch, 4, rank=5).r == 5
+    assert oracle.fit(x, [256] * w.batch, 4, rank=500).r == 128
+
+
+# ------------------------------------------------------------------ SVD
+
+@pytest.mark.parametrize("D,G,H", [(32, 2, 4), (128, 1, 2)])
+def test_fit_matches_numpy_svd(D, G, H):
+    """sigma and the leading subspace agree with numpy.linalg.svd of the
+    centred stacked rows; ragged lengths count only valid tokens."""
+    rng = np.random.default_rng(7)
+    B, S = 3, 300
+    lens = np.array([300, 211, 97], np.int32)
+    scales = 0.9 ** np.arange(D)
+    x = (rng.standard_normal((B, H, S, D)) * scales + rng.normal(0, 0.5, D)).astype(np.float16)
+    # poison padding positions: they must not enter the fit
+    for b in range(B):
+        x[b, :, lens[b]:] = np.float16(1000.0)
+    f = oracle.fit(x, lens, G, rank=6)
+    hpg = H // G
+    for g in range(G):
+        rows = np.concatenate([x[b, h, :lens[b]] for b in range(B)
+                               for h in range(g * hpg, (g + 1) * hpg)]).astype(np.float64)
+        mean = rows.mean(0)
+        _, sv, vt = np.linalg.svd(rows - mean, full_matrices=False)
+        np.testing.assert_allclose(f.sigma[g], sv, rtol=1e-9, atol=1e-9 * sv[0])
+        np.testing.assert_allclose(f.mu[g], mean.astype(np.float32), rtol=0, atol=1e-6)
+        V = f.basis[g].astype(np.float64)
+        # orthonormal up to fp32 rounding of the entries
+        np.testing.assert_allclose(V.T @ V, np.eye(D), atol=2e-6)
+        # leading subspace: principal-angle cosines ~ 1
+        cos = np.linalg.svd(V[:, :6].T @ vt[:6].T, compute_uv=False)
+        assert cos.min() > 1 - 1e-6
+        # each column is an eigenvector with the numpy singular value
+        C = (rows - mean).T @ (rows - mean)
+        for c in range(6):
+            v = V[:, c]
+            np.testing.assert_allclose(C @ v, sv[c] ** 2 * v, atol=1e-5 * sv[0] ** 2)
+            # sign: the largest-magnitude entry is positive
+            assert v[np.argmax(np.abs(v))] > 0
+
+
+def test_basis_sign_convention_on_rotated_data():
+    """Every column's largest-magnitude entry is positive (the sign reading),
+    on data whose principal axes are a dense random rotation."""
+    rng = np.random.default_rng(31)
+    D, N = 48, 2000
+    R, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    x = ((rng.standard_normal((N, D)) * (0.93 ** np.arange(D))) @ R.T).astype(np.float16)
+    f = oracle.fit(x[None, None], [N], 1, rank=D)
+    V = f.basis[0].astype(np.float64)
+    for c in range(D):
+        a = np.abs(V[:, c])
+        top2 = np.sort(a)[-2:]
+        if top2[1] - top2[0] > 1e-4:
+            assert V[np.argmax(a), c] > 0
+
+
+def test_planted_subspace_recovered():
+    """Group SVD recovers a planted rank-r subspace to reconstruction MSE
+    < 1e-3 (PALU page, "Evidence")."""
+    w = synth.small_workload(n_kv_heads=2, n_head_groups=1, prefill=512, latent_rank=8,
+                             rho=0.9, sigma_n=0.005, rank=8, batch=1)
+    x = synth.batch_kv(w, 0, 512)
+    f = oracle.fit(x, [512], 1, rank=8)
+    gp = synth.group_params(w, 0)
+    # principal angles between the fitted basis and the planted row space
+    Q, _ = np.linalg.qr(gp.A[0].T)
+    cos = np.linalg.svd(f.V(0).astype(np.float64).T @ Q, compute_uv=False)
+    assert cos.min() > 0.999
+    rows = x[0].reshape(-1, 128)
+    lat = oracle.project(rows, f.mu[0], f.V(0)).astype(np.float64)
+    rec = lat @ f.V(0).astype(np.float64).T + f.mu[0]
+    mse = np.mean((rec - rows.astype(np.float64)) ** 2)
+    assert mse < 1e-3
+
+
+# ----------------------------------------------------- exact reconstruction
+
+def test_exact_reconstruction_at_full_rank():
+    """r = D and no quantisation: fp16(L V^T + mu) reproduces x bit for bit
+    (the fp32 projection error is far below half an fp16 ulp)."""
+    rng = np.random.default_rng(11)
+    D, N = 128, 600
+    mag = rng.uniform(0.5, 8.0, (N, D)) * rng.choice([-1.0, 1.0], (N, D))
+    x = mag.astype(np.float16)
+    f = oracle.fit(x[None, None], [N], 1, rank=D)
+    assert f.r == D
+    lat = oracle.project(x, f.mu[0], f.V(0)).astype(np.float64)
+    rec = lat @ f.V(0).astype(np.float64).T + f.mu[0].astype(np.float64)
+    assert np.array_equal(rec.astype(np.float16).view(np.uint16), x.view(np.uint16))
+
+
+def test_reconstruction_on_workload_data_within_one_ulp():
+    w = synth.WORKLOADS["single_b1_s512_r32"]
+    x = synth.batch_kv(w, 1, 256)               # V of the first sequence
+    f = oracle.fit(x, [256], 4, rank=128)
+    rows = x[0, 2]                               # head 2 -> group 1
+    lat = oracle.project(rows, f.mu[1], f.V(1)).astype(np.float64)
+    rec = (lat @ f.V(1).astype(np.float64).T + f.mu[1]).astype(np.float16)
+    ulp = np.abs(rec.view(np.int16).astype(np.int32) - rows.view(np.int16).astype(np.int32))
+    big = np.abs(rows.astype(np.float32)) >= 2.0 ** -6
+    assert ulp[big].max() == 0
+    assert ulp.max() <= 1
+
+
+def test_projection_is_fixed_order_fma_chain():
+    """Latents recomputed by an exact emulation of the fp32 chain: each step
+    is the exact rational a*b + acc rounded once to the nearest fp32, which is
+    the definition of a fused multiply-add."""
+    from fractions import Fraction
+    rng = np.random.default_rng(3)
+    x = rng.normal(0, 1, (4, 128)).astype(np.float16)
+    mu = rng.normal(0, 0.5, 128).astype(np.float32)
+    V = rng.normal(0, 0.1, (128, 3)).astype(np.float32)
+    out = oracle.project(x, mu, V)
+    for i in range(4):
+        for c in range(3):
+            acc = np.float32(0.0)
+            for d in range(128):
+                y = np.float32(np.float32(x[i, d]) - mu[d])
+                exact = Fraction(float(y)) * Fraction(float(V[d, c])) + Fraction(float(acc))
+                acc = _round_frac_to_f32(exact)
+            assert out[i, c].view(np.uint32) == acc.view(np.uint32)
+
+
+def _round_frac_to_f32(fr):
+    """Round a Fraction to the nearest fp32 (ties to even), exactly."""
+    from fractions import Fraction
+    if fr == 0:
+        return np.float32(0.0)
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, -126) - 23)
+    q = a / ulp
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return np.float32(sign * float(n * ulp))
+
+
+# --------------------------------------------------------------- quantiser
+
+def test_quantizer_hand_checked_groups():
+    # channel 0 (4-bit): values 10 + 0.5 k -> zero 10, scale 0.5, codes k
+    # channel 1 (2-bit): values {0,1,2,3} -> scale 1, codes = values
+    # channel 2 (2-bit): halfway points round to even: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2
+    # channel 3 (2-bit): constant -> scale 0, codes 0, zero = the constant
+    l = np.zeros((32, 4), np.float32)
+    l[:, 0] = 10.0 + 0.5 * (np.arange(32) % 16)
+    l[:, 1] = np.arange(32) % 4
+    base = np.array([0.0, 3.0, 0.5, 1.5, 2.5] + [1.0] * 27, np.float32)
+    l[:, 2] = base
+    l[:, 3] = 7.0
+    codes, sc, zr = oracle.quantize_group(l, n_hi=1)
+    assert np.array_equal(codes[:, 0], np.arange(32) % 16)
+    assert np.array_equal(codes[:, 1], np.arange(32) % 4)
+    assert list(codes[:5, 2]) == [0, 3, 0, 2, 2]
+    assert np.all(codes[5:, 2] == 1)
+    assert np.all(codes[:, 3] == 0)
+    h = lambda v: np.float16(v).view(np.uint16)
+    assert list(sc) == [h(0.5), h(1.0), h(1.0), h(0.0)]
+    assert list(zr) == [h(10.0), h(0.0), h(0.0), h(7.0)]
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantizer_nearest_level_brute_force(bits):
+    rng = np.random.default_rng(bits)
+    levels = 2 ** bits - 1
+    for trial in range(200):
+        l = (rng.standard_normal((32, 1)) * rng.uniform(0.01, 5)).astype(np.float32)
+        codes, sc, zr = oracle.quantize_group(l, n_hi=1 if bits == 4 else 0)
+        c = codes[:, 0].astype(np.int64)
+        mn, mx = np.float64(l.min()), np.float64(l.max())
+        scale = np.float64(np.float32(np.float32(l.max()) - np.float32(l.min())) / np.float32(levels))
+        assert c.min() >= 0 and c.max() <= levels
+        assert c[np.argmin(l[:, 0])] == 0 and c[np.argmax(l[:, 0])] == levels
+        # brute force over every level: the chosen one is nearest (fp64 check,
+        # ties and near-ties of the fp32 division excluded)
+        u = (l[:, 0].astype(np.float64) - mn) / scale
+        dist = np.abs(np.arange(levels + 1)[None, :] - u[:, None])
+        best = np.argmin(dist, axis=1)
+        near_tie = np.abs(np.abs(u - np.floor(u)) - 0.5) < 1e-5
+        assert np.array_equal(best[~near_tie], c[~near_tie])
+        # reconstruction error within half a step plus fp16 rounding of the meta
+        s16 = np.float64(sc.view(np.float16)[0])
+        z16 = np.float64(zr.view(np.float16)[0])
+        rec = c * s16 + z16
+        bound = scale / 2 + levels * abs(s16 - scale) + abs(z16 - mn) + 1e-7 * abs(mx)
+        assert np.all(np.abs(rec - l[:, 0]) <= bound)
+
+
+def test_quantizer_constant_and_mixed_widths():
+    l = np.full((32, 5), -2.25, np.float32)
+    codes, sc, zr = oracle.quantize_group(l, n_hi=2)
+    assert not codes.any()
+    assert np.all(sc == 0)
+    assert np.all(zr.view(np.float16) == np.float16(-2.25))
+    rng = np.random.default_rng(9)
+    l = rng.standard_normal((32, 12)).astype(np.float32)
+    codes, _, _ = oracle.quantize_group(l, n_hi=3)
+    assert codes[:, :3].max() == 15 and codes[:, 3:].max() == 3
+
+
+# ---------------------------------------------------------------- packing
+
+def test_two_bit_packing_matches_page_shifts():
+    """V-layout lo plane of channel 0: four consecutive tokens per byte at
+    shifts 0, 2, 4, 6 (golden fixture from the bit-packing section)."""
+    for c0, c1, c2, c3, byte in _golden_rows("bitpack_2bit.txt"):
+        codes = np.zeros((32, 1), np.uint8)
+        codes[:4, 0] = [int(c0), int(c1), int(c2), int(c3)]
+        rec = oracle.pack_group(codes, np.zeros(1, np.uint16), np.zeros(1, np.uint16),
+                                n_hi=0, layout=1)
+        assert rec.view(np.uint8)[0] == int(byte, 16)
+        # the K layout with one lo channel puts token t at bit 2t as well
+        rec_k = oracle.pack_group(codes, np.zeros(1, np.uint16), np.zeros(1, np.uint16),
+                                  n_hi=0, layout=0)
+        assert rec_k.view(np.uint8)[0] == int(byte, 16)
+
+
+def test_record_layout_hand_checked():
+    """r = 4, n_hi = 1: both layouts, explicit word/bit positions."""
+    r, n_hi = 4, 1
+    codes = np.zeros((32, r), np.uint8)
+    codes[5, 0] = 0xA            # hi channel 0, token 5
+    codes[9, 3] = 0x3            # lo channel 2 (c' = 2), token 9
+    sc = np.array([0x1111, 0x2222, 0x3333, 0x4444], np.uint16)
+    zr = np.array([0x5555, 0x6666, 0x7777, 0x8888], np.uint16)
+    assert oracle.record_words(r, n_hi) == 4 + 6 + 4
+    k = oracle.pack_group(codes, sc, zr, n_hi, 0)
+    # K: hi bit 5*4*1 + 0 = 20 -> word 0 bits 20..23
+    assert k[0] == 0xA << 20 and not k[1:4].any()
+    # K: lo bit 9*2*3 + 2*2 = 58 -> word 1 of the lo plane, bits 26..27
+    assert k[4 + 1] == 0x3 << 26 and k[4] == 0 and not k[6:10].any()
+    assert list(k[10:]) == [0x55551111, 0x66662222, 0x77773333, 0x88884444]
+    v = oracle.pack_group(codes, sc, zr, n_hi, 1)
+    # V: hi bit 128*0 + 4*5 = 20 -> word 0 bits 20..23
+    assert v[0] == 0xA << 20
+    # V: lo bit 64*2 + 2*9 = 146 -> word 4 of the lo plane, bits 18..19
+    assert v[4 + 4] == 0x3 << 18
+    assert np.count_nonzero(v[:10]) == 2
+
+
+@pytest.mark.parametrize("r", [1, 2, 3, 4, 9, 10, 12, 32, 33, 64, 128])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_pack_unpack_roundtrip(r, layout):
+    rng = np.random.default_rng(r * 7 + layout)
+    n_hi = oracle.n_hi_channels(r, 0.25)
+    codes = np.empty((32, r), np.uint8)
+    codes[:, :n_hi] = rng.integers(0, 16, (32, n_hi))
+    codes[:, n_hi:] = rng.integers(0, 4, (32, r - n_hi))
+    sc = rng.integers(0, 65536, r).astype(np.uint16)
+    zr = rng.integers(0, 65536, r).astype(np.uint16)
+    rec = oracle.pack_group(codes, sc, zr, n_hi, layout)
+    assert rec.size == 4 * n_hi + 2 * (r - n_hi) + r
+    c2, s2, z2 = oracle.unpack_group(rec, r, n_hi, layout)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, sc) and np.array_equal(z2, zr)
+    # dense: every code bit is used exactly once (popcount of an all-ones fill)
+    full = np.empty_like(codes)
+    full[:, :n_hi] = 15
+    full[:, n_hi:] = 3
+    rec1 = oracle.pack_group(full, np.zeros(r, np.uint16), np.zeros(r, np.uint16), n_hi, layout)
+    nbits = int(np.unpackbits(rec1[:4 * n_hi + 2 * (r - n_hi)].view(np.uint8)).sum())
+    assert nbits == 32 * (4 * n_hi + 2 * (r - n_hi))
+
+
+def test_hi_channel_count():
+    assert [oracle.n_hi_channels(r, 0.25) for r in (1, 3, 4, 10, 12, 32, 64, 128)] == \
+        [0, 0, 1, 2, 3, 8, 16, 32]
+
+
+def test_encode_stream_tail_and_decode():
+    rng = np.random.default_rng(1)
+    lat = rng.standard_normal((75, 10)).astype(np.float32)
+    rec, tail = oracle.encode_stream(lat, 2, 4, 2, layout=0)
+    assert rec.shape == (2, 4 * 2 + 2 * 8 + 10) and tail.shape == (11, 10)
+    assert np.array_equal(tail, lat[64:])
+    dec = oracle.decode_stream(rec, tail, 75, 10, 2, 0)
+    assert np.array_equal(dec[64:], lat[64:].astype(np.float64))
+    for j in range(2):
+        codes, sc, zr = oracle.quantize_group(lat[32 * j:32 * j + 32], 2)
+        ref = codes * sc.view(np.float16).astype(np.float64) + zr.view(np.float16).astype(np.float64)
+        assert np.array_equal(dec[32 * j:32 * j + 32], ref)
+
+
+def test_fp16_latent_stream():
+    rng = np.random.default_rng(2)
+    lat = rng.standard_normal((40, 6)).astype(np.float32)
+    rec = oracle.encode_fp16_stream(lat)
+    assert rec.shape == (2, 6 * 32)
+    assert rec[1, 0 * 32 + 7] == np.float16(lat[39, 0]).view(np.uint16)
+    assert rec[0, 5 * 32 + 3] == np.float16(lat[3, 5]).view(np.uint16)
+    dec = oracle.decode_fp16_stream(rec, 40, 6)
+    assert np.array_equal(dec, lat.astype(np.float16).astype(np.float64))
+
+
+# ------------------------------------------------------------- bit rates
+
+def test_effective_bits_golden():
+    for kind, r, D, h, hb, lb, expect in _golden_rows("effective_bits.txt"):
+        r, D, expect = int(r), int(D), float(expect)
+        if kind == "mixed":
+            assert oracle.effective_bits(r, D, float(h), int(hb), int(lb)) == expect
+            n_hi = oracle.n_hi_channels(r, float(h))
+            assert oracle.realised_bits(r, D, n_hi, int(hb), int(lb)) == expect
+        elif kind == "fp16latent":
+            assert oracle.fp16_latent_bits(r, D) == expect
+        else:
+            sched = (8, 4, 2, 1, 1, 0, 0, 0)
+            assert (r / D) * (sum(sched) / len(sched)) == expect
+
+
+def test_fp16_cache_bytes_golden():
+    for tokens, D, kib in _golden_rows("fp16_cache_bytes.txt"):
+        assert int(tokens) * int(D) * 2 * 2 / 1024 == float(kib)
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa(q, K, V, scale):
+    s = (K @ q) * scale
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    return p @ V
+
+
+def test_attend_brute_force_tiny():
+    rng = np.random.default_rng(21)
+    for n in (1, 2, 17, 64):
+        D, rk, rv = 16, 5, 7
+        lk, lv = rng.standard_normal((n, rk)), rng.standard_normal((n, rv))
+        Bk = rng.standard_normal((D, rk)).astype(np.float32)
+        Bv = rng.standard_normal((D, rv)).astype(np.float32)
+        muk = rng.standard_normal(D).astype(np.float32)
+        muv = rng.standard_normal(D).astype(np.float32)
+        q = rng.standard_normal(D).astype(np.float32)
+        out = oracle.attend(lk, Bk, muk, lv, Bv, muv, q, 0.37)
+        K = lk @ Bk.T.astype(np.float64) + muk
+        V = lv @ Bv.T.astype(np.float64) + muv
+        np.testing.assert_allclose(out, _sdpa(q.astype(np.float64), K, V, 0.37), rtol=1e-12,
+                                   atol=1e-12)
+
+
+def test_attend_full_rank_equals_sdpa_on_original():
+    """r = D with exact latents: attention over the reconstruction equals
+    plain SDPA over the original fp16 K/V (to fp32-basis rounding)."""
+    w = synth.small_workload(batch=1, n_kv_heads=1, n_q_heads=1, prefill=200)
+    k = synth.batch_kv(w, 0, 200)
+    v = synth.batch_kv(w, 1, 200)
+    fk = oracle.fit(k, [200], 1, rank=128)
+    fv = oracle.fit(v, [200], 1, rank=128)
+    lk = oracle.project(k[0, 0], fk.mu[0], fk.V(0)).astype(np.float64)
+    lv = oracle.project(v[0, 0], fv.mu[0], fv.V(0)).astype(np.float64)
+    q = synth.queries(w, 0, 1)[0, 0]
+    out = oracle.attend(lk, fk.V(0), fk.mu[0], lv, fv.V(0), fv.mu[0], q, 1 / math.sqrt(128))
+    ref = _sdpa(q.astype(np.float64), k[0, 0].astype(np.float64), v[0, 0].astype(np.float64),
+                1 / math.sqrt(128))
+    np.testing.assert_allclose(out, ref, rtol=0, atol=2e-6)
+
+
+def test_attend_invariants():
+    rng = np.random.default_rng(4)
+    D, r, n = 32, 4, 50
+    lk, lv = rng.standard_normal((n, r)), rng.standard_normal((n, r))
+    Bk = rng.standard_normal((D, r)).astype(np.float32)
+    Bv = rng.standard_normal((D, r)).astype(np.float32)
+    muk = rng.standard_normal(D).astype(np.float32)
+    muv = rng.standard_normal(D).astype(np.float32)
+    q = rng.standard_normal(D).astype(np.float32)
+    # zero query -> uniform weights -> mean of the reconstructed values
+    out0 = oracle.attend(lk, Bk, muk, lv, Bv, muv, np.zeros(D, np.float32), 1.0)
+    np.testing.assert_allclose(out0, (lv @ Bv.T.astype(np.float64) + muv).mean(0), atol=1e-12)
+    # the key mean only shifts every score by q . mu_K: output unchanged
+    a = oracle.attend(lk, Bk, muk, lv, Bv, muv, q, 0.3)
+    b = oracle.attend(lk, Bk, muk * 0 + 5.0, lv, Bv, muv, q, 0.3)
+    np.testing.assert_allclose(a, b, atol=1e-12)
+    # identical values -> output is that value whatever the weights
+    same = np.tile(lv[:1], (n, 1))
+    np.testing.assert_allclose(oracle.attend(lk, Bk, muk, same, Bv, muv, q, 0.3),
+                               same[0] @ Bv.T.astype(np.float64) + muv, atol=1e-12)
+    # one dominant key -> output is its value
+    lk2 = lk.copy()
+    lk2[17] = 0
+    qd = np.zeros(D, np.float32)
+    qd[0] = 1
+    Bk2 = np.zeros((D, r), np.float32)
+    Bk2[0, 0] = 1
+    lk2[:, 0] = 0
+    lk2[17, 0] = 500.0
+    np.testing.assert_allclose(oracle.attend(lk2, Bk2, np.zeros(D, np.float32), lv, Bv, muv, qd, 1.0),
+                               lv[17] @ Bv.T.astype(np.float64) + muv, atol=1e-9)
+
+
+@pytest.mark.parametrize("gqa", [1, 2, 3])
+def test_layer_gqa_head_mapping(gqa):
+    """Query head i reads kv head i // gqa: a layer whose kv heads hold
+    distinct constant values returns, per query head, its kv head's value."""
+    Hkv, D, n = 2, 128, 40
+    w = synth.small_workload(batch=1, n_kv_heads=Hkv, n_q_heads=Hkv * gqa, prefill=n,
+                             n_head_groups=1, rank=8)
+    k = synth.batch_kv(w, 0, n)
+    v = np.zeros_like(k)
+    v[0, 0] = np.float16(1.5)
+    v[0, 1] = np.float16(-0.75)
+    fk = oracle.fit(k, [n], 1, rank=8)
+    fv = oracle.fit(v, [n], 1, rank=8)
+    layer = oracle.OracleLayer(D, Hkv * gqa, Hkv, 1, fk, fv)
+    ks = [layer.encode_head(k[0, h], h, 0) for h in range(Hkv)]
+    vs = [layer.encode_head(v[0, h], h, 1) for h in range(Hkv)]
+    q = synth.queries(w, 0, 1)[0]
+    out = layer.attend(ks, vs, q)
+    for i in range(Hkv * gqa):
+        expect = 1.5 if i // gqa == 0 else -0.75
+        np.testing.assert_allclose(out[i], expect, atol=2e-3)
+
+
+# ------------------------------------------------------------- quality
+
+def _naive_2bit_mse(x):
+    """Per-channel min/max 2-bit over 32-token groups in the original space."""
+    x = x.astype(np.float64)
+    err = 0.0
+    for j in range(0, x.shape[0] // 32 * 32, 32):
+        g = x[j:j + 32]
+        mn, mx = g.min(0), g.max(0)
+        sc = (mx - mn) / 3
+        q = np.where(sc > 0, np.rint((g - mn) / np.where(sc > 0, sc, 1)), 0)
+        err += ((q * sc + mn - g) ** 2).sum()
+    return err / (x.shape[0] // 32 * 32 * x.shape[1])
+
+
+def test_palu_beats_naive_2bit_on_low_rank_data():
+    """Rank-8 synthetic data, D = 64: PALU r = 8 with mixed 4/2-bit latents
+    has lower MSE than naive 2-bit, for K and for V (PALU page, "Evidence")."""
+    w = synth.small_workload(batch=1, n_kv_heads=1, n_q_heads=1, head_dim=64, prefill=512,
+                             latent_rank=8, rho=0.9, sigma_n=0.01, rank=8)
+    for tensor in (0, 1):
+        x = synth.batch_kv(w, tensor, 512)
+        f = oracle.fit(x, [512], 1, rank=8)
+        lat = oracle.project(x[0, 0], f.mu[0], f.V(0))
+        rec, tail = oracle.encode_stream(lat, oracle.n_hi_channels(8, 0.25), 4, 2, tensor)
+        dec = oracle.decode_stream(rec, tail, 512, 8, 2, tensor)
+        xr = dec @ f.V(0).astype(np.float64).T + f.mu[0]
+        palu = np.mean((xr - x[0, 0].astype(np.float64)) ** 2)
+        assert palu < _naive_2bit_mse(x[0, 0])
+
+
+def test_deterministic():
+    w = synth.small_workload(prefill=70, rank=None)
+    x = synth.batch_kv(w, 0, 70)
+    a = oracle.fit(x, [70, 70], 1, rank=0)
+    b = oracle.fit(x, [70, 70], 1, rank=0)
+    assert a.r == b.r and np.array_equal(a.basis, b.basis)
+    la = oracle.project(x[1, 1], a.mu[0], a.V(0))
+    lb = oracle.project(x[1, 1], b.mu[0], b.V(0))
+    assert np.array_equal(la, lb)
+    assert np.array_equal(oracle.encode_stream(la, 1, 4, 2, 0)[0],
+                          oracle.encode_stream(lb, 1, 4, 2, 0)[0])
+
+
+def test_constant_data_degenerate_fit():
+    x = np.full((1, 2, 64, 128), np.float16(0.25))
+    f = oracle.fit(x, [64], 1, rank=0)
+    assert f.r == 1 and np.all(f.sigma == 0)
+    lat = oracle.project(x[0, 0], f.mu[0], f.V(0))
+    assert np.all(lat == 0)
+    rec, _ = oracle.encode_stream(lat, 0, 4, 2, 0)
+    codes, sc, zr = oracle.unpack_group(rec[0], 1, 0, 0)
+    assert not codes.any() and sc[0] == 0 and zr[0] == 0
