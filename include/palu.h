@@ -1,0 +1,207 @@
+/*
+ * palu.h -- C ABI of the low-rank latent KV cache library (libpalu.so).
+ *
+ * The method is the PALU-style latent cache of the veloxquant-mlx "PALU"
+ * page: per head group, a mean mu_g and a truncated basis V_g (D x r) are
+ * fitted from the prefill (section "How it works", prefill steps 1-3); keys
+ * and values are stored as latents L = (x - mu_g) V_g quantised with mixed
+ * bit widths over 32-token groups (steps 4-6 and the decode steps); decode
+ * attention is computed directly from the stored latents, which equals
+ * attention over the reconstruction L V_g^T + mu_g.
+ *
+ * Conventions for every entry point:
+ *   - Return value: PALU_OK (0) or a PALU_ERR_* code.  No exception, abort
+ *     or HIP error escapes; palu_last_error() gives a message for the last
+ *     failing call on the calling thread.
+ *   - Every argument is validated on the host before any device work, so a
+ *     failing call leaves the cache and the stream untouched.
+ *   - "device" pointers are HIP device memory owned by the caller; "host"
+ *     pointers are ordinary host memory owned by the caller and only read
+ *     or written during the call.
+ *   - stream is a hipStream_t (NULL = the null stream).  Calls marked
+ *     "stream-ordered" only enqueue work; calls marked "synchronous" return
+ *     after their device work has finished.
+ *   - fp16 tensors are IEEE binary16, little-endian, densely packed in the
+ *     stated index order (last index fastest).
+ *   - A cache object must not be used by two threads at once.
+ */
+#ifndef PALU_H
+#define PALU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    PALU_OK = 0,
+    PALU_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad config       */
+    PALU_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. D > 128) */
+    PALU_ERR_NOT_FITTED = 3,    /* encode/decode/read before a basis exists */
+    PALU_ERR_CAPACITY = 4,      /* append beyond max_seq_len, bad seq slot  */
+    PALU_ERR_NOT_BOUND = 5,     /* device storage not bound yet             */
+    PALU_ERR_HIP = 6            /* a HIP runtime call failed                */
+};
+
+/* Method configuration.  Mirrors the PALU fields of KVCacheConfig on the
+ * PALU page, section "Usage" (palu_rank, palu_energy_threshold,
+ * palu_n_head_groups, palu_hi_bit, palu_lo_bit, palu_hi_fraction,
+ * palu_group_size, palu_quantize_values). */
+typedef struct palu_config {
+    int32_t head_dim;          /* D; the kernels support 16..128, multiple of 16 */
+    int32_t n_kv_heads;        /* H: heads stored by the cache                     */
+    int32_t n_q_heads;         /* query heads, a multiple of n_kv_heads; query head
+                                  i attends with kv head i / (n_q_heads/n_kv_heads) */
+    int32_t n_head_groups;     /* G contiguous groups of kv heads sharing a basis;
+                                  group g owns heads [g*H/G, (g+1)*H/G)           */
+    int32_t rank;              /* explicit rank (clamped to D); 0 = energy rule   */
+    float energy_threshold;    /* tau of the energy rule, in (0, 1]               */
+    int32_t hi_bit;            /* bits of the top channels; only 4 supported      */
+    int32_t lo_bit;            /* bits of the other channels; only 2 supported    */
+    float hi_fraction;         /* n_hi = floor(hi_fraction * r) channels at hi_bit */
+    int32_t group_size;        /* tokens per quantisation group; only 32          */
+    int32_t quantize_values;   /* 1: V mixed-bit like K; 0: V as fp16 latents     */
+    int32_t max_rank;          /* storage is sized for ranks up to this (0 = D)   */
+} palu_config;
+
+/* Fills the page's defaults (rank 0 = energy rule, threshold 0.90, G = 4,
+ * 4/2 bits, hi_fraction 0.25, group 32, quantised values) for the given
+ * shape.  Returns PALU_ERR_INVALID_ARG for a null pointer. */
+int palu_config_default(palu_config *cfg, int32_t head_dim, int32_t n_kv_heads,
+                        int32_t n_q_heads);
+
+typedef struct palu_cache palu_cache;   /* opaque; host memory only */
+
+/* Creates a cache for up to max_batch sequence slots of up to max_seq_len
+ * tokens each.  Allocates host bookkeeping only (no device memory).
+ * Errors: INVALID_ARG (null, non-positive sizes, H % G, Hq % H, bad
+ * threshold or fraction), UNSUPPORTED (D, bit widths or group size outside
+ * what the kernels implement). */
+int palu_cache_create(const palu_config *cfg, int32_t max_batch,
+                      int32_t max_seq_len, palu_cache **out);
+
+/* Device bytes the cache needs: bases, means, packed records, fp32 tails,
+ * the fit workspace and the decode split scratch, for max_rank. */
+int palu_cache_required_bytes(const palu_cache *cache, size_t *dev_bytes);
+
+/* Binds caller-allocated device storage of at least the required bytes,
+ * 256-byte aligned.  The library never allocates device memory itself.
+ * The storage must outlive the cache or the next bind.  Binding drops any
+ * fitted basis and empties every sequence. */
+int palu_cache_bind(palu_cache *cache, void *dev_buf, size_t bytes);
+
+/* Group-head fit (PALU page, "How it works", prefill steps 1-3): for K and
+ * V separately, per group, mean and truncated eigenbasis of the rows of all
+ * B sequences (first seq_lens[b] tokens) and all heads of the group; the
+ * rank is the explicit one or the smallest meeting the energy threshold
+ * (energy = sum of squared singular values), and the minimum over groups
+ * is used for every group.
+ *   k, v     : device fp16 [B][H][S_stride][D]
+ *   seq_lens : host int32 [B], 0 <= seq_lens[b] <= S_stride, sum > 0
+ * Synchronous (the eigensolve runs on the host).  Empties every sequence
+ * slot (stored codes of an older basis are meaningless).  Errors:
+ * INVALID_ARG, NOT_BOUND, HIP. */
+int palu_fit(palu_cache *cache, const void *k, const void *v,
+             const int32_t *seq_lens, int32_t B, int32_t S_stride, void *stream);
+
+/* Installs a basis instead of fitting one (tensor 0 = K, 1 = V):
+ *   basis : host fp32 [G][D][r], basis[g][d][c] = component d of channel c,
+ *           channels in descending singular-value order
+ *   mu    : host fp32 [G][D]
+ * 1 <= r <= max_rank.  Synchronous.  Empties every sequence slot. */
+int palu_set_basis(palu_cache *cache, int32_t tensor, int32_t r,
+                   const float *basis, const float *mu);
+
+/* Reads the basis of tensor 0 (K) or 1 (V).  r receives the rank; basis
+ * (host fp32 [G][D][r]), mu (host fp32 [G][D]) and sigma (host fp64 [G][D],
+ * singular values of the centred stacks, zeros if set by palu_set_basis)
+ * may each be NULL.  Errors: INVALID_ARG, NOT_FITTED. */
+int palu_get_basis(const palu_cache *cache, int32_t tensor, int32_t *r,
+                   float *basis, float *mu, double *sigma);
+
+/* Appends tokens (PALU page, "How it works", decode steps 1-2): projects
+ * each new key/value into its group's basis with a fixed-order fp32 chain,
+ * quantises every 32-token group that becomes complete (asymmetric min/max,
+ * round half to even, top n_hi channels at hi_bit, others at lo_bit) and
+ * keeps the incomplete group's latents in fp32 until it completes.
+ *   k, v     : device fp16 [B][H][T_stride][D]
+ *   seq_ids  : host int32 [B] slot of each row (NULL = 0..B-1), distinct
+ *   n_new    : host int32 [B] tokens to append per row (NULL = T_stride each),
+ *              0 <= n_new[b] <= T_stride
+ * Row b appends positions [len, len + n_new[b]) of slot seq_ids[b].
+ * Stream-ordered.  Errors: INVALID_ARG, NOT_BOUND, NOT_FITTED, CAPACITY
+ * (len + n_new > max_seq_len or slot >= max_batch), HIP. */
+int palu_encode_append(palu_cache *cache, const void *k, const void *v,
+                       const int32_t *seq_ids, const int32_t *n_new, int32_t B,
+                       int32_t T_stride, void *stream);
+
+/* Single-query decode attention over every stored token of each slot
+ * (PALU page, "How it works", decode step 3, computed directly from the
+ * latent codes): out = softmax(q K^T * scale) V with K, V the decoded
+ * reconstruction; fp32 scores and accumulation.
+ *   q, out        : device fp16 [B][Hq][D]
+ *   seq_ids       : host int32 [B] (NULL = 0..B-1); every slot must hold at
+ *                   least one token
+ *   softmax_scale : 0 means 1/sqrt(D)
+ * Stream-ordered.  Uses the split scratch inside the bound storage, so two
+ * calls on one cache must not run concurrently on different streams.
+ * Errors: INVALID_ARG, NOT_BOUND, NOT_FITTED, CAPACITY (empty slot), HIP. */
+int palu_decode_attend(palu_cache *cache, const void *q, void *out,
+                       const int32_t *seq_ids, int32_t B, float softmax_scale,
+                       void *stream);
+
+/* Tokens stored in a slot. */
+int palu_seq_len(const palu_cache *cache, int32_t seq, int32_t *len);
+
+/* Copies the stored state of one (slot, kv head, tensor) to host memory.
+ * Synchronous on the null stream after a device synchronisation.
+ *   records : host, receives the complete groups' records in order:
+ *             mixed-bit: floor(len/32) records of record_words(r) uint32
+ *             fp16 V latents: ceil(len/32) records of r*32 fp16 (c*32 + t);
+ *             may be NULL
+ *   tail    : host fp32 [len % 32][r] latents of the incomplete group (NULL
+ *             allowed; not used for fp16 V latents)
+ * The byte sizes must be at least what is copied.  Record layout:
+ *   K (tensor 0): hi plane 4*n_hi words, token t channel c at bit
+ *     t*4*n_hi + 4c; lo plane 2*n_lo words, token t channel n_hi + c' at bit
+ *     t*2*n_lo + 2c'; then r words scale16[c] | zero16[c] << 16.
+ *   V (tensor 1): hi plane channel c token t at bit 128c + 4t; lo plane
+ *     channel n_hi + c' token t at bit 64c' + 2t; then the r meta words. */
+int palu_read_codes(const palu_cache *cache, int32_t seq, int32_t head,
+                    int32_t tensor, void *records, size_t records_bytes,
+                    float *tail, size_t tail_bytes);
+
+/* Byte accounting and rates (PALU page, "Effective bit-width" and
+ * "Evidence"; SVDq cache page, "Byte accounting"). */
+typedef struct palu_stats {
+    int32_t r_k, r_v, n_hi_k, n_hi_v;
+    int64_t tokens;                  /* sum of stored tokens over slots        */
+    int64_t compressed_key_bytes;    /* records + tails + K bases and means    */
+    int64_t compressed_value_bytes;  /* same for V (fp16 latents if unquantised) */
+    int64_t fp16_key_bytes;          /* tokens * H * D * 2                     */
+    int64_t fp16_value_bytes;
+    double nominal_bits_k, nominal_bits_v;   /* (r/D)(h b_hi + (1-h) b_lo) or 16 r/D */
+    double realised_bits_k, realised_bits_v; /* (n_hi b_hi + n_lo b_lo)/D or 16 r/D */
+    double assigned_avg_bits;        /* max of the realised K and V rates      */
+} palu_stats;
+
+int palu_get_stats(const palu_cache *cache, palu_stats *out);
+
+/* Empties every slot, keeping the basis. */
+int palu_reset(palu_cache *cache);
+
+/* Words of one mixed-bit record for rank r: 4 n_hi + 2 (r - n_hi) + r. */
+int palu_record_words(const palu_cache *cache, int32_t tensor, int32_t *words);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *palu_last_error(void);
+
+void palu_cache_destroy(palu_cache *cache);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PALU_H */

@@ -1,0 +1,616 @@
+// Host runtime of libpalu.so: argument validation, cache bookkeeping, the
+// device memory layout inside the caller-bound buffer, the fit's host
+// eigensolve, and kernel launches.  Implements include/palu.h.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "palu.h"
+#include "palu_internal.h"
+
+#define PALU_API extern "C" __attribute__((visibility("default")))
+
+using namespace palu;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(PALU_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr int kGramElems = kHeadDim * kHeadDim + kHeadDim;
+constexpr int kGramMaxRowsPerBlock = 8192;   // bounds fp32 accumulation per tile
+constexpr int kAttendTargetGroups = 2048;    // workgroups aimed for per decode launch
+constexpr int kAttendMinChunk = 8;           // token groups per split, at least
+
+int n_hi_of(int r, float frac) {
+    return static_cast<int>(std::floor(static_cast<double>(frac) * static_cast<double>(r)));
+}
+
+}  // namespace
+
+struct palu_cache {
+    palu_config cfg{};
+    int max_batch = 0, max_seq_len = 0;
+    int D = 0, H = 0, Hq = 0, G = 0, hpg = 0, gqa = 0, r_max = 0, max_groups = 0;
+    int gram_nb_cap = 0;
+    // byte offsets of each region inside the bound buffer
+    size_t off_basis[2]{}, off_mu[2]{}, off_rec[2]{}, off_tail[2]{};
+    size_t off_gram_part = 0, off_gram_out = 0, off_seg = 0, off_attend = 0, total = 0;
+    char *dev = nullptr;
+    size_t dev_bytes = 0;
+    bool fitted[2] = {false, false};
+    int r[2] = {0, 0}, n_hi[2] = {0, 0};
+    std::vector<float> basis_h[2], mu_h[2];
+    std::vector<double> sigma_h[2];
+    std::vector<int> len, sel;
+
+    bool quantized(int t) const { return t == 0 || cfg.quantize_values; }
+    int words_for(int t, int rr) const {
+        return quantized(t) ? mixed_record_words(rr, n_hi_of(rr, cfg.hi_fraction))
+                            : fp16_record_words(rr);
+    }
+    TensorDev tensor_dev(int t) const {
+        TensorDev d{};
+        d.r = r[t];
+        d.n_hi = quantized(t) ? n_hi[t] : 0;
+        d.words = words_for(t, r[t]);
+        d.fp16_latents = quantized(t) ? 0 : 1;
+        d.head_stride = static_cast<int64_t>(max_groups) * d.words;
+        d.records = reinterpret_cast<uint32_t *>(dev + off_rec[t]);
+        d.tail = quantized(t) ? reinterpret_cast<float *>(dev + off_tail[t]) : nullptr;
+        d.basis = reinterpret_cast<float *>(dev + off_basis[t]);
+        d.mu = reinterpret_cast<float *>(dev + off_mu[t]);
+        return d;
+    }
+};
+
+namespace {
+
+int validate_config(const palu_config *c) {
+    if (!c) return fail(PALU_ERR_INVALID_ARG, "config is NULL");
+    if (c->head_dim <= 0 || c->n_kv_heads <= 0 || c->n_q_heads <= 0 || c->n_head_groups <= 0)
+        return fail(PALU_ERR_INVALID_ARG, "head_dim, n_kv_heads, n_q_heads and n_head_groups must be positive");
+    if (c->n_kv_heads % c->n_head_groups != 0)
+        return fail(PALU_ERR_INVALID_ARG, "n_kv_heads must be a multiple of n_head_groups (contiguous groups)");
+    if (c->n_q_heads % c->n_kv_heads != 0)
+        return fail(PALU_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
+    if (c->rank < 0) return fail(PALU_ERR_INVALID_ARG, "rank must be >= 0 (0 selects the energy rule)");
+    if (!(c->energy_threshold > 0.0f && c->energy_threshold <= 1.0f))
+        return fail(PALU_ERR_INVALID_ARG, "energy_threshold must be in (0, 1]");
+    if (!(c->hi_fraction >= 0.0f && c->hi_fraction <= 1.0f))
+        return fail(PALU_ERR_INVALID_ARG, "hi_fraction must be in [0, 1]");
+    if (c->max_rank < 0 || c->max_rank > c->head_dim)
+        return fail(PALU_ERR_INVALID_ARG, "max_rank must be in [0, head_dim]");
+    if (c->quantize_values != 0 && c->quantize_values != 1)
+        return fail(PALU_ERR_INVALID_ARG, "quantize_values must be 0 or 1");
+    if (c->head_dim != kHeadDim)
+        return fail(PALU_ERR_UNSUPPORTED, "only head_dim = 128 is implemented by the kernels");
+    if (c->hi_bit != 4 || c->lo_bit != 2)
+        return fail(PALU_ERR_UNSUPPORTED, "only hi_bit = 4 and lo_bit = 2 are implemented");
+    if (c->group_size != kTokGroup)
+        return fail(PALU_ERR_UNSUPPORTED, "only group_size = 32 is implemented");
+    if (c->n_q_heads / c->n_kv_heads > kMaxGqa)
+        return fail(PALU_ERR_UNSUPPORTED, "at most 8 query heads per kv head are implemented");
+    return PALU_OK;
+}
+
+int check_bound(const palu_cache *c) {
+    if (!c) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+    if (!c->dev) return fail(PALU_ERR_NOT_BOUND, "no device storage bound (call palu_cache_bind)");
+    return PALU_OK;
+}
+
+int check_fitted(const palu_cache *c) {
+    if (int e = check_bound(c)) return e;
+    if (!c->fitted[0] || !c->fitted[1])
+        return fail(PALU_ERR_NOT_FITTED, "no basis for K and V yet (call palu_fit or palu_set_basis)");
+    return PALU_OK;
+}
+
+void reset_seqs(palu_cache *c) {
+    std::fill(c->len.begin(), c->len.end(), 0);
+    std::fill(c->sel.begin(), c->sel.end(), 0);
+}
+
+int upload_basis(palu_cache *c, int t) {
+    const size_t nb = c->basis_h[t].size() * sizeof(float);
+    hipError_t e = hipMemcpy(c->dev + c->off_basis[t], c->basis_h[t].data(), nb, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "basis upload");
+    e = hipMemcpy(c->dev + c->off_mu[t], c->mu_h[t].data(), c->mu_h[t].size() * sizeof(float),
+                  hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "mean upload");
+    return PALU_OK;
+}
+
+}  // namespace
+
+PALU_API int palu_config_default(palu_config *cfg, int32_t head_dim, int32_t n_kv_heads,
+                                 int32_t n_q_heads) {
+    if (!cfg) return fail(PALU_ERR_INVALID_ARG, "config is NULL");
+    cfg->head_dim = head_dim;
+    cfg->n_kv_heads = n_kv_heads;
+    cfg->n_q_heads = n_q_heads;
+    cfg->n_head_groups = 4;
+    cfg->rank = 0;
+    cfg->energy_threshold = 0.90f;
+    cfg->hi_bit = 4;
+    cfg->lo_bit = 2;
+    cfg->hi_fraction = 0.25f;
+    cfg->group_size = 32;
+    cfg->quantize_values = 1;
+    cfg->max_rank = 0;
+    return PALU_OK;
+}
+
+PALU_API int palu_cache_create(const palu_config *cfg, int32_t max_batch, int32_t max_seq_len,
+                               palu_cache **out) {
+    if (!out) return fail(PALU_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (int e = validate_config(cfg)) return e;
+    if (max_batch <= 0 || max_seq_len <= 0)
+        return fail(PALU_ERR_INVALID_ARG, "max_batch and max_seq_len must be positive");
+    if (cfg->rank > 0 && cfg->max_rank > 0 && cfg->rank > cfg->max_rank)
+        return fail(PALU_ERR_INVALID_ARG, "rank exceeds max_rank");
+    palu_cache *c = new palu_cache();
+    c->cfg = *cfg;
+    c->max_batch = max_batch;
+    c->max_seq_len = max_seq_len;
+    c->D = cfg->head_dim;
+    c->H = cfg->n_kv_heads;
+    c->Hq = cfg->n_q_heads;
+    c->G = cfg->n_head_groups;
+    c->hpg = c->H / c->G;
+    c->gqa = c->Hq / c->H;
+    c->r_max = cfg->max_rank > 0 ? cfg->max_rank : c->D;
+    c->max_groups = (max_seq_len + kTokGroup - 1) / kTokGroup;
+    c->len.assign(max_batch, 0);
+    c->sel.assign(max_batch, 0);
+
+    // device layout, sized for r_max
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes, 256);
+        return o;
+    };
+    for (int t = 0; t < 2; ++t) {
+        c->off_basis[t] = take(sizeof(float) * c->G * c->D * c->r_max);
+        c->off_mu[t] = take(sizeof(float) * c->G * c->D);
+        c->off_rec[t] = take(sizeof(uint32_t) * static_cast<size_t>(max_batch) * c->H * c->max_groups *
+                             c->words_for(t, c->r_max));
+        c->off_tail[t] = c->quantized(t)
+                             ? take(sizeof(float) * static_cast<size_t>(max_batch) * c->H * 2 * kTokGroup * c->r_max)
+                             : 0;
+    }
+    const int64_t n_rows_max = static_cast<int64_t>(max_batch) * max_seq_len * c->hpg;
+    c->gram_nb_cap = static_cast<int>(std::max<int64_t>(
+        std::max(1, 512 / c->G), (n_rows_max + kGramMaxRowsPerBlock - 1) / kGramMaxRowsPerBlock));
+    c->off_gram_part = take(sizeof(float) * 2 * static_cast<size_t>(c->G) * c->gram_nb_cap * kGramElems);
+    c->off_gram_out = take(sizeof(double) * 2 * static_cast<size_t>(c->G) * kGramElems);
+    c->off_seg = take(sizeof(int64_t) * (static_cast<size_t>(max_batch) * c->hpg + 1));
+    // decode rows may repeat slots, so a launch can hold kMaxCallSeqs rows
+    // whatever max_batch is
+    c->off_attend = take(sizeof(float) * static_cast<size_t>(kMaxCallSeqs) * c->Hq * kMaxSplits * (c->r_max + 2));
+    c->total = off;
+    *out = c;
+    return PALU_OK;
+}
+
+PALU_API int palu_cache_required_bytes(const palu_cache *c, size_t *dev_bytes) {
+    if (!c || !dev_bytes) return fail(PALU_ERR_INVALID_ARG, "cache or dev_bytes is NULL");
+    *dev_bytes = c->total;
+    return PALU_OK;
+}
+
+PALU_API int palu_cache_bind(palu_cache *c, void *dev_buf, size_t bytes) {
+    if (!c || !dev_buf) return fail(PALU_ERR_INVALID_ARG, "cache or dev_buf is NULL");
+    if (bytes < c->total)
+        return fail(PALU_ERR_INVALID_ARG, "bound buffer has " + std::to_string(bytes) + " bytes, " +
+                                              std::to_string(c->total) + " required");
+    if (reinterpret_cast<uintptr_t>(dev_buf) % 256 != 0)
+        return fail(PALU_ERR_INVALID_ARG, "bound buffer must be 256-byte aligned");
+    c->dev = static_cast<char *>(dev_buf);
+    c->dev_bytes = bytes;
+    c->fitted[0] = c->fitted[1] = false;
+    reset_seqs(c);
+    return PALU_OK;
+}
+
+PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t *seq_lens, int32_t B,
+                      int32_t S_stride, void *stream) {
+    if (int e = check_bound(c)) return e;
+    if (!k || !v || !seq_lens) return fail(PALU_ERR_INVALID_ARG, "k, v and seq_lens must be non-NULL");
+    if (B <= 0 || B > c->max_batch) return fail(PALU_ERR_INVALID_ARG, "B must be in [1, max_batch]");
+    if (S_stride <= 0) return fail(PALU_ERR_INVALID_ARG, "S_stride must be positive");
+    int64_t total = 0;
+    for (int b = 0; b < B; ++b) {
+        if (seq_lens[b] < 0 || seq_lens[b] > S_stride || seq_lens[b] > c->max_seq_len)
+            return fail(PALU_ERR_INVALID_ARG, "seq_lens[" + std::to_string(b) + "] out of [0, min(S_stride, max_seq_len)]");
+        total += seq_lens[b];
+    }
+    if (total == 0) return fail(PALU_ERR_INVALID_ARG, "no valid tokens to fit");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    const int nseg = B * c->hpg;
+    std::vector<int64_t> pref(nseg + 1, 0);
+    for (int sgi = 0; sgi < nseg; ++sgi) pref[sgi + 1] = pref[sgi] + seq_lens[sgi / c->hpg];
+    const int64_t n_rows = pref[nseg];
+    const int nb_target = std::max(1, 512 / c->G);
+    int64_t rpb = std::max<int64_t>(kGramRowsPerBlockMin, (n_rows + nb_target - 1) / nb_target);
+    rpb = std::min<int64_t>(rpb, kGramMaxRowsPerBlock);
+    rpb = (rpb + 63) / 64 * 64;
+    const int nb = static_cast<int>((n_rows + rpb - 1) / rpb);
+    if (nb > c->gram_nb_cap) return fail(PALU_ERR_CAPACITY, "fit workspace too small for this many rows");
+
+    hipError_t e = hipMemcpyAsync(c->dev + c->off_seg, pref.data(), sizeof(int64_t) * pref.size(),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "fit segment upload");
+    GramArgs ga{};
+    ga.x[0] = static_cast<const uint16_t *>(k);
+    ga.x[1] = static_cast<const uint16_t *>(v);
+    ga.seg_pref = reinterpret_cast<const int64_t *>(c->dev + c->off_seg);
+    ga.partial = reinterpret_cast<float *>(c->dev + c->off_gram_part);
+    ga.B = B;
+    ga.H = c->H;
+    ga.S_stride = S_stride;
+    ga.G = c->G;
+    ga.hpg = c->hpg;
+    ga.nb = nb;
+    ga.rows_per_block = static_cast<int>(rpb);
+    ga.n_rows = n_rows;
+    if ((e = launch_gram(ga, s)) != hipSuccess) return hip_fail(e, "gram launch");
+    GramReduceArgs ra{};
+    ra.partial = ga.partial;
+    ra.out = reinterpret_cast<double *>(c->dev + c->off_gram_out);
+    ra.G = c->G;
+    ra.nb = nb;
+    if ((e = launch_gram_reduce(ra, s)) != hipSuccess) return hip_fail(e, "gram reduce launch");
+    std::vector<double> gram(2 * static_cast<size_t>(c->G) * kGramElems);
+    e = hipMemcpyAsync(gram.data(), ra.out, sizeof(double) * gram.size(), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "gram download");
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "fit synchronize");
+
+    const int D = c->D;
+    const double N = static_cast<double>(n_rows);
+    std::vector<double> cov(D * D), w(D), z(D * D);
+    std::vector<int> order(D);
+    for (int t = 0; t < 2; ++t) {
+        std::vector<double> basis_full(static_cast<size_t>(c->G) * D * D);
+        std::vector<int> rg(c->G);
+        c->mu_h[t].assign(static_cast<size_t>(c->G) * D, 0.0f);
+        c->sigma_h[t].assign(static_cast<size_t>(c->G) * D, 0.0);
+        for (int g = 0; g < c->G; ++g) {
+            const double *G2 = gram.data() + (static_cast<size_t>(t) * c->G + g) * kGramElems;
+            const double *sum = G2 + D * D;
+            // scatter about the mean: X^T X - s s^T / N
+            for (int i = 0; i < D; ++i)
+                for (int j = 0; j < D; ++j) cov[i * D + j] = G2[i * D + j] - sum[i] * sum[j] / N;
+            for (int i = 0; i < D; ++i)
+                for (int j = 0; j < i; ++j) {
+                    const double m = 0.5 * (cov[i * D + j] + cov[j * D + i]);
+                    cov[i * D + j] = cov[j * D + i] = m;
+                }
+            if (!sym_eigen(cov.data(), D, w.data(), z.data()))
+                return fail(PALU_ERR_HIP, "eigensolver did not converge");
+            std::iota(order.begin(), order.end(), 0);
+            std::stable_sort(order.begin(), order.end(), [&](int a2, int b2) { return w[a2] > w[b2]; });
+            std::vector<double> s2(D);
+            for (int cidx = 0; cidx < D; ++cidx) {
+                const int src = order[cidx];
+                s2[cidx] = w[src] > 0.0 ? w[src] : 0.0;
+                c->sigma_h[t][g * D + cidx] = std::sqrt(s2[cidx]);
+                int arg = 0;
+                for (int d = 1; d < D; ++d)
+                    if (std::fabs(z[d * D + src]) > std::fabs(z[arg * D + src])) arg = d;
+                const double sg = z[arg * D + src] < 0.0 ? -1.0 : 1.0;
+                for (int d = 0; d < D; ++d)
+                    basis_full[(static_cast<size_t>(g) * D + d) * D + cidx] = sg * z[d * D + src];
+            }
+            for (int d = 0; d < D; ++d) c->mu_h[t][g * D + d] = static_cast<float>(sum[d] / N);
+            if (c->cfg.rank > 0) {
+                rg[g] = std::min(c->cfg.rank, D);
+            } else {
+                double tot = 0.0;
+                for (int i = 0; i < D; ++i) tot += s2[i];
+                int rr = D;
+                if (tot <= 0.0) {
+                    rr = 1;
+                } else {
+                    double acc = 0.0;
+                    for (int kk = 1; kk <= D; ++kk) {
+                        acc += s2[kk - 1];
+                        if (acc >= static_cast<double>(c->cfg.energy_threshold) * tot) {
+                            rr = kk;
+                            break;
+                        }
+                    }
+                }
+                rg[g] = rr;
+            }
+        }
+        int rr = *std::min_element(rg.begin(), rg.end());
+        if (rr > c->r_max)
+            return fail(PALU_ERR_CAPACITY, "fitted rank " + std::to_string(rr) + " exceeds max_rank " +
+                                               std::to_string(c->r_max));
+        c->r[t] = rr;
+        c->n_hi[t] = n_hi_of(rr, c->cfg.hi_fraction);
+        c->basis_h[t].assign(static_cast<size_t>(c->G) * D * rr, 0.0f);
+        for (int g = 0; g < c->G; ++g)
+            for (int d = 0; d < D; ++d)
+                for (int cidx = 0; cidx < rr; ++cidx)
+                    c->basis_h[t][(static_cast<size_t>(g) * D + d) * rr + cidx] =
+                        static_cast<float>(basis_full[(static_cast<size_t>(g) * D + d) * D + cidx]);
+        if (int err = upload_basis(c, t)) return err;
+        c->fitted[t] = true;
+    }
+    reset_seqs(c);
+    return PALU_OK;
+}
+
+PALU_API int palu_set_basis(palu_cache *c, int32_t tensor, int32_t r, const float *basis, const float *mu) {
+    if (int e = check_bound(c)) return e;
+    if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
+    if (!basis || !mu) return fail(PALU_ERR_INVALID_ARG, "basis and mu must be non-NULL");
+    if (r < 1 || r > c->r_max) return fail(PALU_ERR_INVALID_ARG, "r must be in [1, max_rank]");
+    c->r[tensor] = r;
+    c->n_hi[tensor] = n_hi_of(r, c->cfg.hi_fraction);
+    c->basis_h[tensor].assign(basis, basis + static_cast<size_t>(c->G) * c->D * r);
+    c->mu_h[tensor].assign(mu, mu + static_cast<size_t>(c->G) * c->D);
+    c->sigma_h[tensor].assign(static_cast<size_t>(c->G) * c->D, 0.0);
+    c->fitted[tensor] = false;
+    if (int e = upload_basis(c, tensor)) return e;
+    c->fitted[tensor] = true;
+    reset_seqs(c);
+    return PALU_OK;
+}
+
+PALU_API int palu_get_basis(const palu_cache *c, int32_t tensor, int32_t *r, float *basis, float *mu,
+                            double *sigma) {
+    if (!c) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+    if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
+    if (!c->fitted[tensor]) return fail(PALU_ERR_NOT_FITTED, "no basis for this tensor");
+    if (r) *r = c->r[tensor];
+    if (basis) std::memcpy(basis, c->basis_h[tensor].data(), c->basis_h[tensor].size() * sizeof(float));
+    if (mu) std::memcpy(mu, c->mu_h[tensor].data(), c->mu_h[tensor].size() * sizeof(float));
+    if (sigma) std::memcpy(sigma, c->sigma_h[tensor].data(), c->sigma_h[tensor].size() * sizeof(double));
+    return PALU_OK;
+}
+
+PALU_API int palu_encode_append(palu_cache *c, const void *k, const void *v, const int32_t *seq_ids,
+                                const int32_t *n_new, int32_t B, int32_t T_stride, void *stream) {
+    if (int e = check_fitted(c)) return e;
+    if (!k || !v) return fail(PALU_ERR_INVALID_ARG, "k and v must be non-NULL");
+    if (B <= 0) return fail(PALU_ERR_INVALID_ARG, "B must be positive");
+    if (T_stride <= 0) return fail(PALU_ERR_INVALID_ARG, "T_stride must be positive");
+    std::vector<char> seen(c->max_batch, 0);
+    for (int b = 0; b < B; ++b) {
+        const int slot = seq_ids ? seq_ids[b] : b;
+        if (slot < 0 || slot >= c->max_batch)
+            return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " out of [0, max_batch)");
+        if (seen[slot]) return fail(PALU_ERR_INVALID_ARG, "sequence slot listed twice in one call");
+        seen[slot] = 1;
+        const int n = n_new ? n_new[b] : T_stride;
+        if (n < 0 || n > T_stride) return fail(PALU_ERR_INVALID_ARG, "n_new must be in [0, T_stride]");
+        if (static_cast<int64_t>(c->len[slot]) + n > c->max_seq_len)
+            return fail(PALU_ERR_CAPACITY, "append to slot " + std::to_string(slot) + " exceeds max_seq_len");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t row_elems = static_cast<size_t>(c->H) * T_stride * c->D;
+    for (int b0 = 0; b0 < B; b0 += kMaxCallSeqs) {
+        const int nb = std::min(kMaxCallSeqs, B - b0);
+        EncodeArgs ea{};
+        ea.x[0] = static_cast<const uint16_t *>(k) + b0 * row_elems;
+        ea.x[1] = static_cast<const uint16_t *>(v) + b0 * row_elems;
+        ea.t[0] = c->tensor_dev(0);
+        ea.t[1] = c->tensor_dev(1);
+        ea.B = nb;
+        ea.H = c->H;
+        ea.T_stride = T_stride;
+        ea.hpg = c->hpg;
+        ea.hi_bit = c->cfg.hi_bit;
+        ea.lo_bit = c->cfg.lo_bit;
+        int max_touched = 0;
+        for (int i = 0; i < nb; ++i) {
+            const int b = b0 + i;
+            const int slot = seq_ids ? seq_ids[b] : b;
+            const int n = n_new ? n_new[b] : T_stride;
+            const int o = c->len[slot];
+            ea.slot[i] = slot;
+            ea.old_len[i] = o;
+            ea.n_new[i] = n;
+            ea.sel_old[i] = c->sel[slot];
+            // the incomplete group after the append lives in the other tail
+            // buffer whenever a different group was incomplete before, so
+            // the workgroup that completes the old group can still read it
+            int sel_new = c->sel[slot];
+            if (n > 0 && (o + n) % kTokGroup != 0 && (o % kTokGroup) != 0 &&
+                (o + n) / kTokGroup != o / kTokGroup)
+                sel_new = 1 - sel_new;
+            ea.sel_new[i] = sel_new;
+            if (n > 0) max_touched = std::max(max_touched, (o + n - 1) / kTokGroup - o / kTokGroup + 1);
+        }
+        if (max_touched > 0) {
+            hipError_t e = launch_encode(ea, max_touched, s);
+            if (e != hipSuccess) return hip_fail(e, "encode launch");
+        }
+        for (int i = 0; i < nb; ++i) {
+            c->len[ea.slot[i]] += ea.n_new[i];
+            c->sel[ea.slot[i]] = ea.sel_new[i];
+        }
+    }
+    return PALU_OK;
+}
+
+PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids, int32_t B,
+                                float softmax_scale, void *stream) {
+    if (int e = check_fitted(c)) return e;
+    if (!q || !out) return fail(PALU_ERR_INVALID_ARG, "q and out must be non-NULL");
+    if (B <= 0) return fail(PALU_ERR_INVALID_ARG, "B must be positive");
+    if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
+        return fail(PALU_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    for (int b = 0; b < B; ++b) {
+        const int slot = seq_ids ? seq_ids[b] : b;
+        if (slot < 0 || slot >= c->max_batch)
+            return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " out of [0, max_batch)");
+        if (c->len[slot] <= 0)
+            return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " holds no tokens");
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(c->D));
+    const size_t row_elems = static_cast<size_t>(c->Hq) * c->D;
+    for (int b0 = 0; b0 < B; b0 += kMaxCallSeqs) {
+        const int nb = std::min(kMaxCallSeqs, B - b0);
+        AttendArgs aa{};
+        aa.q = static_cast<const uint16_t *>(q) + b0 * row_elems;
+        aa.out = static_cast<uint16_t *>(out) + b0 * row_elems;
+        aa.partial = reinterpret_cast<float *>(c->dev + c->off_attend);
+        aa.k = c->tensor_dev(0);
+        aa.v = c->tensor_dev(1);
+        aa.B = nb;
+        aa.Hq = c->Hq;
+        aa.Hkv = c->H;
+        aa.gqa = c->gqa;
+        aa.hpg = c->hpg;
+        aa.qscale = static_cast<float>(scale * 1.4426950408889634);
+        int64_t units = 0;
+        int max_full = 0;
+        for (int i = 0; i < nb; ++i) {
+            const int slot = seq_ids ? seq_ids[b0 + i] : b0 + i;
+            aa.slot[i] = slot;
+            aa.len[i] = c->len[slot];
+            aa.sel[i] = c->sel[slot];
+            const int nfull = c->len[slot] / kTokGroup;
+            units += static_cast<int64_t>(c->H) * std::max(1, nfull);
+            max_full = std::max(max_full, nfull);
+        }
+        int chunk = static_cast<int>(std::max<int64_t>(kAttendMinChunk, (units + kAttendTargetGroups - 1) / kAttendTargetGroups));
+        chunk = std::max(chunk, (max_full + kMaxSplits - 1) / kMaxSplits);
+        aa.chunk = chunk;
+        aa.work_prefix[0] = 0;
+        for (int i = 0; i < nb; ++i) {
+            const int nfull = aa.len[i] / kTokGroup;
+            aa.nsplit[i] = std::max(1, (nfull + chunk - 1) / chunk);
+            aa.work_prefix[i + 1] = aa.work_prefix[i] + c->H * aa.nsplit[i];
+        }
+        hipError_t e = launch_attend(aa, aa.work_prefix[nb], s);
+        if (e != hipSuccess) return hip_fail(e, "attend launch");
+        e = launch_combine(aa, s);
+        if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
+    return PALU_OK;
+}
+
+PALU_API int palu_seq_len(const palu_cache *c, int32_t seq, int32_t *len) {
+    if (!c || !len) return fail(PALU_ERR_INVALID_ARG, "cache or len is NULL");
+    if (seq < 0 || seq >= c->max_batch) return fail(PALU_ERR_CAPACITY, "sequence slot out of range");
+    *len = c->len[seq];
+    return PALU_OK;
+}
+
+PALU_API int palu_read_codes(const palu_cache *c, int32_t seq, int32_t head, int32_t tensor, void *records,
+                             size_t records_bytes, float *tail, size_t tail_bytes) {
+    if (int e = check_fitted(c)) return e;
+    if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
+    if (seq < 0 || seq >= c->max_batch) return fail(PALU_ERR_CAPACITY, "sequence slot out of range");
+    if (head < 0 || head >= c->H) return fail(PALU_ERR_INVALID_ARG, "head out of range");
+    const TensorDev td = c->tensor_dev(tensor);
+    const int len = c->len[seq];
+    const int nrec = td.fp16_latents ? (len + kTokGroup - 1) / kTokGroup : len / kTokGroup;
+    const size_t rbytes = sizeof(uint32_t) * static_cast<size_t>(nrec) * td.words;
+    const int ntail = td.fp16_latents ? 0 : len % kTokGroup;
+    const size_t tbytes = sizeof(float) * static_cast<size_t>(ntail) * td.r;
+    if (records && records_bytes < rbytes) return fail(PALU_ERR_INVALID_ARG, "records buffer too small");
+    if (tail && tail_bytes < tbytes) return fail(PALU_ERR_INVALID_ARG, "tail buffer too small");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "read synchronize");
+    const int64_t hb = static_cast<int64_t>(seq) * c->H + head;
+    if (records && rbytes) {
+        e = hipMemcpy(records, td.records + hb * td.head_stride, rbytes, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "records download");
+    }
+    if (tail && tbytes) {
+        e = hipMemcpy(tail, td.tail + (hb * 2 + c->sel[seq]) * kTokGroup * td.r, tbytes, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "tail download");
+    }
+    return PALU_OK;
+}
+
+PALU_API int palu_get_stats(const palu_cache *c, palu_stats *st) {
+    if (!c || !st) return fail(PALU_ERR_INVALID_ARG, "cache or stats is NULL");
+    if (!c->fitted[0] || !c->fitted[1]) return fail(PALU_ERR_NOT_FITTED, "no basis for K and V yet");
+    std::memset(st, 0, sizeof(*st));
+    st->r_k = c->r[0];
+    st->r_v = c->r[1];
+    st->n_hi_k = c->n_hi[0];
+    st->n_hi_v = c->quantized(1) ? c->n_hi[1] : 0;
+    int64_t tokens = 0, full_groups = 0, tail_tokens = 0, fp16_groups = 0;
+    for (int s = 0; s < c->max_batch; ++s) {
+        tokens += c->len[s];
+        full_groups += c->len[s] / kTokGroup;
+        tail_tokens += c->len[s] % kTokGroup;
+        fp16_groups += (c->len[s] + kTokGroup - 1) / kTokGroup;
+    }
+    st->tokens = tokens;
+    const double D = c->D;
+    for (int t = 0; t < 2; ++t) {
+        const int rr = c->r[t];
+        const int64_t basis_bytes = static_cast<int64_t>(c->G) * c->D * (rr + 1) * 4;
+        int64_t bytes;
+        double nominal, realised;
+        if (c->quantized(t)) {
+            bytes = c->H * (full_groups * mixed_record_words(rr, c->n_hi[t]) * 4 + tail_tokens * rr * 4) +
+                    basis_bytes;
+            nominal = (rr / D) * (c->cfg.hi_fraction * c->cfg.hi_bit + (1.0 - c->cfg.hi_fraction) * c->cfg.lo_bit);
+            realised = (c->n_hi[t] * c->cfg.hi_bit + (rr - c->n_hi[t]) * c->cfg.lo_bit) / D;
+        } else {
+            bytes = c->H * fp16_groups * static_cast<int64_t>(fp16_record_words(rr)) * 4 + basis_bytes;
+            nominal = realised = 16.0 * rr / D;
+        }
+        if (t == 0) {
+            st->compressed_key_bytes = bytes;
+            st->nominal_bits_k = nominal;
+            st->realised_bits_k = realised;
+        } else {
+            st->compressed_value_bytes = bytes;
+            st->nominal_bits_v = nominal;
+            st->realised_bits_v = realised;
+        }
+    }
+    st->fp16_key_bytes = tokens * c->H * c->D * 2;
+    st->fp16_value_bytes = st->fp16_key_bytes;
+    st->assigned_avg_bits = std::max(st->realised_bits_k, st->realised_bits_v);
+    return PALU_OK;
+}
+
+PALU_API int palu_reset(palu_cache *c) {
+    if (!c) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+    reset_seqs(c);
+    return PALU_OK;
+}
+
+PALU_API int palu_record_words(const palu_cache *c, int32_t tensor, int32_t *words) {
+    if (!c || !words) return fail(PALU_ERR_INVALID_ARG, "cache or words is NULL");
+    if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
+    if (!c->fitted[tensor]) return fail(PALU_ERR_NOT_FITTED, "no basis for this tensor");
+    *words = c->words_for(tensor, c->r[tensor]);
+    return PALU_OK;
+}
+
+PALU_API const char *palu_last_error(void) { return g_last_error.c_str(); }
+
+PALU_API void palu_cache_destroy(palu_cache *c) { delete c; }

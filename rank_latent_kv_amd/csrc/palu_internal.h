@@ -1,0 +1,90 @@
+// Internal declarations shared by the host runtime and the HIP kernels of
+// libpalu.so.  Nothing here is part of the C ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace palu {
+
+constexpr int kTokGroup = 32;      // tokens per quantisation group
+constexpr int kHeadDim = 128;      // head_dim the kernels are built for
+constexpr int kMaxCallSeqs = 64;   // sequences per launch (argument arrays)
+constexpr int kMaxSplits = 64;     // token splits per (sequence, kv head)
+constexpr int kMaxGqa = 8;         // query heads per kv head in the attend kernel
+constexpr int kGramRowsPerBlockMin = 512;
+
+// Words of one mixed-bit record: hi plane (4 bits x 32 tokens per channel),
+// lo plane (2 bits x 32 tokens per channel), then one meta word per channel.
+inline int mixed_record_words(int r, int n_hi) { return 4 * n_hi + 2 * (r - n_hi) + r; }
+// fp16 latents: r channels x 32 tokens of 2 bytes = 16 r words.
+inline int fp16_record_words(int r) { return 16 * r; }
+
+// Stored state of one tensor (K or V) in the bound device buffer.
+struct TensorDev {
+    uint32_t *records;   // [slots][H][max_groups][words]
+    float *tail;         // [slots][H][2][32][r]  (nullptr for fp16 latents)
+    float *basis;        // [G][D][r] fp32, d-major
+    float *mu;           // [G][D] fp32
+    int r, n_hi, words;
+    int fp16_latents;    // V stored as fp16 latents (no tail, no meta)
+    int64_t head_stride; // words between consecutive (slot, head) = max_groups * words
+};
+
+struct GramArgs {
+    const uint16_t *x[2];     // K, V fp16 [B][H][S_stride][D]
+    const int64_t *seg_pref;  // [B*hpg + 1] prefix of valid rows over (b, head-in-group)
+    const int32_t *seg_len;   // unused by the kernel; kept for bounds reasoning
+    float *partial;           // [2][G][nb][D*D + D]
+    int B, H, S_stride, G, hpg, nb, rows_per_block;
+    int64_t n_rows;           // rows per group (same for every group)
+};
+
+struct GramReduceArgs {
+    const float *partial;     // [2][G][nb][D*D + D]
+    double *out;              // [2][G][D*D + D]
+    int G, nb;
+};
+
+struct EncodeArgs {
+    const uint16_t *x[2];     // K, V fp16 [B][H][T_stride][D]
+    TensorDev t[2];
+    int B, H, T_stride, hpg, hi_bit, lo_bit;
+    int slot[kMaxCallSeqs];
+    int old_len[kMaxCallSeqs];
+    int n_new[kMaxCallSeqs];
+    int sel_old[kMaxCallSeqs];
+    int sel_new[kMaxCallSeqs];
+};
+
+struct AttendArgs {
+    const uint16_t *q;        // fp16 [B][Hq][D]
+    uint16_t *out;            // fp16 [B][Hq][D]
+    float *partial;           // [B][Hq][kMaxSplits][2 + r_v]
+    TensorDev k, v;
+    int B, Hq, Hkv, gqa, hpg;
+    int chunk;                // complete token groups per split
+    float qscale;             // softmax scale * log2(e)
+    int slot[kMaxCallSeqs];
+    int len[kMaxCallSeqs];
+    int sel[kMaxCallSeqs];
+    int nsplit[kMaxCallSeqs];
+    int work_prefix[kMaxCallSeqs + 1];  // workgroups before sequence i
+};
+
+// Launchers (defined in palu_kernels.hip).  They return the launch status.
+hipError_t launch_gram(const GramArgs &a, hipStream_t s);
+hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s);
+hipError_t launch_encode(const EncodeArgs &a, int max_touched, hipStream_t s);
+hipError_t launch_attend(const AttendArgs &a, int n_work, hipStream_t s);
+hipError_t launch_combine(const AttendArgs &a, hipStream_t s);
+
+// Host symmetric eigensolver (palu_eigen.cpp): Householder tridiagonalisation
+// followed by implicit-shift QL.  a: n x n row-major symmetric (destroyed);
+// w: eigenvalues (unsorted); z: n x n row-major, column j = eigenvector j.
+// Returns false if the iteration did not converge.
+bool sym_eigen(double *a, int n, double *w, double *z);
+
+}  // namespace palu

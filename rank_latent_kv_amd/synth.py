@@ -10,7 +10,8 @@ Recipe (one workload = one single attention layer):
     mean mu_g ~ N(0, 0.5^2)^D; optional outlier channels (round(frac * D)
     of them, picked at random) that are multiplied by 8 after the noise;
   * per (sequence, kv head, token): x = mu_g + z A_g + eps with
-    z ~ N(0, 1)^k and eps ~ N(0, sigma_n^2)^D, then rounded to fp16;
+    z ~ N(0, 1)^k and eps ~ N(0, sigma_n^2)^D, drawn and summed in fp32,
+    then rounded to fp16;
   * prefill tokens and decode tokens come from the same process (decode
     tokens are simply the positions after the prefill);
   * queries ~ N(0, 1)^D per (sequence, decode step, query head), fp16.
@@ -130,9 +131,12 @@ def kv_sequence(w: Workload, tensor: int, b: int, n_tokens: int,
     for h in range(w.n_kv_heads):
         g = h // hpg
         rng = np.random.default_rng([w.seed, 13, tensor, b, h])
-        z = rng.standard_normal((n_tokens, k))
-        eps = rng.standard_normal((n_tokens, D)) * w.sigma_n
-        x = gp.mu[g][None, :] + z @ gp.A[g] + eps
+        z = rng.standard_normal((n_tokens, k), dtype=np.float32)
+        eps = rng.standard_normal((n_tokens, D), dtype=np.float32)
+        eps *= np.float32(w.sigma_n)
+        x = z @ gp.A[g].astype(np.float32)
+        x += eps
+        x += gp.mu[g].astype(np.float32)[None, :]
         if gp.outliers.shape[1]:
             x[:, gp.outliers[g]] *= 8.0
         out[h] = x.astype(np.float16)

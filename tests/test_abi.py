@@ -1,0 +1,132 @@
+"""C-ABI tests that need no GPU: the library loads, exports every entry point
+include/palu.h declares, and rejects bad arguments on the host before any
+device work (every error path below returns before a HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_latent_kv_amd import palu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "palu.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(palu_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(palu.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(palu.LIB_PATH)
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def _cfg(**kw):
+    cfg = palu.palu_config_default(128, 8, 32)
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+def test_config_defaults_follow_usage_section():
+    cfg = palu.palu_config_default(128, 8, 32)
+    assert (cfg.rank, cfg.n_head_groups, cfg.hi_bit, cfg.lo_bit, cfg.group_size,
+            cfg.quantize_values) == (0, 4, 4, 2, 32, 1)
+    assert abs(cfg.energy_threshold - 0.90) < 1e-7 and abs(cfg.hi_fraction - 0.25) < 1e-7
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_head_groups=3), 1),          # H % G != 0
+    (dict(n_q_heads=12), 1),             # Hq % H != 0
+    (dict(energy_threshold=0.0), 1),
+    (dict(energy_threshold=1.5), 1),
+    (dict(hi_fraction=-0.1), 1),
+    (dict(rank=-1), 1),
+    (dict(max_rank=129), 1),
+    (dict(quantize_values=2), 1),
+    (dict(head_dim=96), 2),              # kernels built for D = 128
+    (dict(hi_bit=3), 2),
+    (dict(lo_bit=1), 2),
+    (dict(group_size=64), 2),
+    (dict(n_q_heads=8 * 16), 2),         # more than 8 query heads per kv head
+])
+def test_create_rejects_bad_config(kw, code):
+    with pytest.raises(palu.PaluError) as ei:
+        palu.palu_cache_create(_cfg(**kw), 4, 1024)
+    assert ei.value.code == code
+    assert palu.palu_last_error()
+
+
+def test_create_rejects_bad_sizes():
+    for mb, ms in [(0, 10), (4, 0), (-1, 5)]:
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_cache_create(_cfg(), mb, ms)
+        assert ei.value.code == 1
+
+
+def test_required_bytes_and_bind_validation():
+    h = palu.palu_cache_create(_cfg(max_rank=32), 4, 1000)
+    try:
+        n = palu.palu_cache_required_bytes(h)
+        assert n > 0 and n % 256 == 0
+        # capacity covers records at max_rank: 4 slots * 8 heads * 32 groups *
+        # (3*32 + 2*8) words * 4 bytes per tensor, plus the rest
+        assert n > 2 * 4 * 8 * 32 * (3 * 32 + 2 * 8) * 4
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_cache_bind(h, 0, n)
+        assert ei.value.code == 1
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_cache_bind(h, 4096, n - 1)          # too small
+        assert ei.value.code == 1
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_cache_bind(h, 4096 + 16, n)         # misaligned
+        assert ei.value.code == 1
+    finally:
+        palu.palu_cache_destroy(h)
+
+
+def test_calls_before_bind_or_fit_fail_cleanly():
+    h = palu.palu_cache_create(_cfg(), 2, 256)
+    try:
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_fit(h, 1, 1, [16, 16], 2, 16, 0)
+        assert ei.value.code == 5                          # not bound
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_encode_append(h, 1, 1, None, None, 2, 1, 0)
+        assert ei.value.code == 5
+        # bind to a fake (never dereferenced) aligned address: everything
+        # below fails validation before any device call
+        palu.palu_cache_bind(h, 1 << 20, palu.palu_cache_required_bytes(h))
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_encode_append(h, 1, 1, None, None, 2, 1, 0)
+        assert ei.value.code == 3                          # not fitted
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_decode_attend(h, 1, 1, None, 2, 0.0, 0)
+        assert ei.value.code == 3
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_get_stats(h)
+        assert ei.value.code == 3
+        for lens, B, S in [([17, 3], 2, 16), ([-1, 3], 2, 16), ([0, 0], 2, 16), ([4], 3, 16),
+                           ([300, 3], 2, 300)]:
+            with pytest.raises(palu.PaluError) as ei:
+                palu.palu_fit(h, 1, 1, lens, B, S, 0)
+            assert ei.value.code == 1, (lens, B, S)
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_set_basis(h, 2, 4, [0.0] * (4 * 128 * 4), [0.0] * (4 * 128))
+        assert ei.value.code == 1
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_set_basis(h, 0, 0, [0.0], [0.0])
+        assert ei.value.code == 1
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_seq_len(h, 2)
+        assert ei.value.code == 4
+        assert palu.palu_seq_len(h, 1) == 0
+    finally:
+        palu.palu_cache_destroy(h)

@@ -1,0 +1,368 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+  * codes, scales and tails bit-exact given the same basis and means;
+  * append-order invariance (one prefill call == token-by-token appends);
+  * decode attention within |o - o_ref| <= 2e-3 + 1e-2 |o_ref| (fp64 oracle);
+  * fit: identical rank and captured-energy difference <= 1e-4 per group;
+  * edge cases: tail-only sequences, exact multiples of 32, single tokens,
+    capacity limits, GQA factors 1/2/3, ranks 1 and D, fp16 value latents.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from rank_latent_kv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-3, 1e-2
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    if not _t.cuda.is_available():
+        pytest.skip("no GPU")
+    return _t
+
+
+def _cache(torch, w, max_seq_len, max_batch=None, rank=None, max_rank=0):
+    from rank_latent_kv_amd.palu import LatentKVCache
+    return LatentKVCache(w.head_dim, w.n_kv_heads, w.n_q_heads, w.n_head_groups,
+                         max_batch or w.batch, max_seq_len,
+                         rank=(w.rank or 0) if rank is None else rank,
+                         energy_threshold=w.energy, quantize_values=w.quantize_values,
+                         max_rank=max_rank)
+
+
+def _dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _oracle_fit_from_gpu(cache, tensor):
+    r, basis, mu, sigma = cache.get_basis(tensor)
+    G, D = basis.shape[0], basis.shape[1]
+    full = np.zeros((G, D, D), np.float32)
+    full[:, :, :r] = basis
+    return oracle.Fit(r, np.full(G, r, np.int32), full, mu, sigma)
+
+
+def _layer(cache, w):
+    fk = _oracle_fit_from_gpu(cache, 0)
+    fv = _oracle_fit_from_gpu(cache, 1)
+    return oracle.OracleLayer(w.head_dim, w.n_q_heads, w.n_kv_heads, w.n_head_groups, fk, fv,
+                              quantize_values=w.quantize_values)
+
+
+def _compare_state(cache, layer, x_seq, slot, heads=None):
+    """GPU stored state of one slot == oracle encode of x_seq (fp16 [H, n, D])."""
+    H = x_seq[0].shape[0]
+    for tensor in (0, 1):
+        for h in (range(H) if heads is None else heads):
+            st = layer.encode_head(x_seq[tensor][h], h, tensor)
+            rec, tail = cache.read_codes(slot, h, tensor)
+            if "fp16" in st:
+                n = st["n"]
+                got = rec.view(np.uint16).reshape(st["fp16"].shape)
+                r = layer.fit[1].r
+                for j in range(got.shape[0]):
+                    valid = min(32, n - 32 * j)
+                    g3 = got[j].reshape(r, 32)[:, :valid]
+                    o3 = st["fp16"][j].reshape(r, 32)[:, :valid]
+                    assert np.array_equal(g3, o3), (slot, h, tensor, j)
+            else:
+                assert rec.shape == st["records"].shape, (rec.shape, st["records"].shape)
+                if not np.array_equal(rec, st["records"]):
+                    bad = np.argwhere(rec != st["records"])
+                    raise AssertionError(f"records differ slot {slot} head {h} tensor {tensor}: "
+                                         f"first {bad[:4].tolist()} of {len(bad)}")
+                assert np.array_equal(tail.view(np.uint32), st["tail"].view(np.uint32)), \
+                    (slot, h, tensor)
+
+
+def _check_attention(got, ref, what=""):
+    got = got.astype(np.float64)
+    err = np.abs(got - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    worst = np.max(err - bound)
+    assert worst <= 0, f"{what}: max excess {worst:.3e}, max abs err {err.max():.3e}"
+    return err.max()
+
+
+def _run_small(torch, w, steps=None, chunks=None, check_every=1, lens=None):
+    """Oracle-fit basis installed on the GPU; prefill + decode steps; codes
+    bit-exact after the prefill and the last step, attention within
+    tolerance after every checked step."""
+    lens = synth.prefill_lengths(w) if lens is None else np.asarray(lens, np.int32)
+    steps = w.steps if steps is None else steps
+    total = int(lens.max()) + steps
+    k_all = synth.batch_kv(w, 0, total)
+    v_all = synth.batch_kv(w, 1, total)
+    q_all = np.stack([synth.queries(w, b, steps) for b in range(w.batch)])  # [B, steps, Hq, D]
+    S = int(lens.max())
+    fk = oracle.fit(k_all[:, :, :S], lens, w.n_head_groups, rank=w.rank or 0, tau=w.energy)
+    fv = oracle.fit(v_all[:, :, :S], lens, w.n_head_groups, rank=w.rank or 0, tau=w.energy)
+    cache = _cache(torch, w, total)
+    cache.set_basis(0, fk.bases(), fk.mu)
+    cache.set_basis(1, fv.bases(), fv.mu)
+    layer = oracle.OracleLayer(w.head_dim, w.n_q_heads, w.n_kv_heads, w.n_head_groups, fk, fv,
+                               quantize_values=w.quantize_values)
+    if chunks is None:
+        cache.encode_append(_dev(torch, k_all[:, :, :S]), _dev(torch, v_all[:, :, :S]), n_new=lens)
+    else:
+        pos = np.zeros(w.batch, np.int64)
+        for c in chunks:
+            n_new = np.minimum(c, lens - pos).astype(np.int32)
+            kc = np.zeros((w.batch, w.n_kv_heads, c, w.head_dim), np.float16)
+            vc = np.zeros_like(kc)
+            for b in range(w.batch):
+                kc[b, :, :n_new[b]] = k_all[b, :, pos[b]:pos[b] + n_new[b]]
+                vc[b, :, :n_new[b]] = v_all[b, :, pos[b]:pos[b] + n_new[b]]
+            cache.encode_append(_dev(torch, kc), _dev(torch, vc), n_new=n_new)
+            pos += n_new
+        assert np.array_equal(pos, lens)
+    torch.cuda.synchronize()
+    for b in range(w.batch):
+        assert cache.seq_len(b) == lens[b]
+        _compare_state(cache, layer, (k_all[b, :, :lens[b]], v_all[b, :, :lens[b]]), b)
+    worst = 0.0
+    for step in range(steps):
+        kt = _dev(torch, np.stack([k_all[b, :, lens[b] + step:lens[b] + step + 1] for b in range(w.batch)]))
+        vt = _dev(torch, np.stack([v_all[b, :, lens[b] + step:lens[b] + step + 1] for b in range(w.batch)]))
+        cache.encode_append(kt, vt)
+        q = q_all[:, step]
+        out = cache.decode_attend(_dev(torch, q)).cpu().numpy()
+        if step % check_every == 0 or step == steps - 1:
+            for b in range(w.batch):
+                n = lens[b] + step + 1
+                xs = (k_all[b, :, :n], v_all[b, :, :n])
+                if step == steps - 1:
+                    _compare_state(cache, layer, xs, b)
+                ks = [layer.encode_head(xs[0][h], h, 0) for h in range(w.n_kv_heads)]
+                vs = [layer.encode_head(xs[1][h], h, 1) for h in range(w.n_kv_heads)]
+                ref = layer.attend(ks, vs, q[b])
+                worst = max(worst, _check_attention(out[b], ref, f"step {step} seq {b}"))
+    return cache, worst
+
+
+# ------------------------------------------------------------ small cases
+
+def test_encode_and_attend_single_group_gqa2(torch):
+    w = synth.small_workload(batch=2, n_q_heads=4, n_kv_heads=2, n_head_groups=1, prefill=96,
+                             steps=5, rank=16)
+    _run_small(torch, w)
+
+
+@pytest.mark.parametrize("gqa", [1, 3])
+def test_gqa_factors_and_groups(torch, gqa):
+    w = synth.small_workload(batch=2, n_q_heads=4 * gqa, n_kv_heads=4, n_head_groups=2,
+                             prefill=70, steps=3, rank=12, seed=77 + gqa)
+    _run_small(torch, w)
+
+
+def test_ragged_prefill_with_tails_and_group_boundaries(torch):
+    # lengths hit: a single token, tail only (< 32), exact multiples of 32,
+    # and one past a boundary; 40 decode steps cross further boundaries
+    w = synth.small_workload(batch=5, n_q_heads=8, n_kv_heads=4, n_head_groups=4,
+                             prefill=97, steps=40, rank=10, seed=5)
+    _run_small(torch, w, check_every=7, lens=[1, 31, 32, 64, 97])
+
+
+def test_fp16_value_latents(torch):
+    w = synth.small_workload(batch=2, n_q_heads=8, n_kv_heads=2, n_head_groups=2, prefill=75,
+                             steps=6, rank=24, quantize_values=False, seed=9)
+    _run_small(torch, w)
+
+
+@pytest.mark.parametrize("rank", [1, 2, 5, 33, 64, 128])
+def test_rank_extremes(torch, rank):
+    w = synth.small_workload(batch=1, n_q_heads=2, n_kv_heads=2, n_head_groups=1, prefill=64,
+                             steps=2, rank=rank, seed=rank)
+    _run_small(torch, w)
+
+
+def test_append_order_invariance(torch):
+    w = synth.small_workload(batch=3, n_q_heads=4, n_kv_heads=2, n_head_groups=2, prefill=150,
+                             steps=1, rank=12, seed=21)
+    # same tokens appended in chunks of 1, 7, 32, 33, ... -> identical codes
+    _run_small(torch, w, chunks=[1, 7, 32, 33, 5, 40, 1, 64])
+    _run_small(torch, w, chunks=[1] * 150)
+
+
+def test_determinism(torch):
+    w = synth.small_workload(batch=2, n_q_heads=4, n_kv_heads=2, prefill=80, steps=1, rank=16)
+    outs = []
+    for _ in range(2):
+        k = _dev(torch, synth.batch_kv(w, 0, 80))
+        v = _dev(torch, synth.batch_kv(w, 1, 80))
+        cache = _cache(torch, w, 100)
+        cache.fit(k, v)
+        cache.encode_append(k, v)
+        q = _dev(torch, np.stack([synth.queries(w, b, 1)[0] for b in range(2)]))
+        outs.append((cache.decode_attend(q).cpu().numpy(), cache.read_codes(1, 1, 0)[0],
+                     cache.get_basis(0)[1]))
+    assert np.array_equal(outs[0][0].view(np.uint16), outs[1][0].view(np.uint16))
+    assert np.array_equal(outs[0][1], outs[1][1]) and np.array_equal(outs[0][2], outs[1][2])
+
+
+def test_capacity_and_empty_slot_errors(torch):
+    from rank_latent_kv_amd.palu import PaluError
+    w = synth.small_workload(batch=2, n_q_heads=4, n_kv_heads=2, prefill=40, rank=8)
+    cache = _cache(torch, w, 64)
+    k = _dev(torch, synth.batch_kv(w, 0, 40))
+    v = _dev(torch, synth.batch_kv(w, 1, 40))
+    cache.fit(k, v)
+    q = _dev(torch, np.zeros((2, 4, 128), np.float16))
+    with pytest.raises(PaluError) as ei:
+        cache.decode_attend(q)                 # slots are empty after a fit
+    assert ei.value.code == 4
+    cache.encode_append(k, v)
+    cache.encode_append(k[:, :, :24].contiguous(), v[:, :, :24].contiguous())  # 64 = max_seq_len
+    assert cache.seq_len(0) == 64
+    with pytest.raises(PaluError) as ei:
+        cache.encode_append(k[:, :, :1].contiguous(), v[:, :, :1].contiguous())
+    assert ei.value.code == 4
+    with pytest.raises(PaluError) as ei:
+        cache.encode_append(k[:1, :, :1].contiguous(), v[:1, :, :1].contiguous(), seq_ids=[5])
+    assert ei.value.code == 4
+    cache.decode_attend(q)                     # full slots still attend
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------- fit
+
+def _energy(rows, mu, V):
+    c = rows.astype(np.float64) - mu.astype(np.float64)
+    tot = np.sum(c * c)
+    proj = c @ V.astype(np.float64)
+    return np.sum(proj * proj) / tot
+
+
+@pytest.mark.parametrize("name", ["single_b1_s512_r32", "gqa3_b1_s4096_e90"])
+def test_fit_parity_small_workloads(torch, name):
+    w = synth.WORKLOADS[name]
+    lens = synth.prefill_lengths(w)
+    S = int(lens.max())
+    hpg = w.n_kv_heads // w.n_head_groups
+    cache = _cache(torch, w, S)
+    for tensor in (0, 1):
+        x = synth.batch_kv(w, tensor, S)
+        if tensor == 0:
+            kx = x
+        else:
+            cache.fit(_dev(torch, kx), _dev(torch, x), lens)
+    for tensor in (0, 1):
+        x = synth.batch_kv(w, tensor, S)
+        f = oracle.fit(x, lens, w.n_head_groups, rank=w.rank or 0, tau=w.energy)
+        r, basis, mu, sigma = cache.get_basis(tensor)
+        assert r == f.r, (tensor, r, f.r)
+        for g in range(w.n_head_groups):
+            rows = np.concatenate([x[b, h, :lens[b]] for b in range(w.batch)
+                                   for h in range(g * hpg, (g + 1) * hpg)])
+            e_gpu = _energy(rows, f.mu[g], basis[g])
+            e_or = _energy(rows, f.mu[g], f.V(g))
+            assert abs(e_gpu - e_or) <= 1e-4, (tensor, g, e_gpu, e_or)
+            np.testing.assert_allclose(mu[g], f.mu[g], atol=1e-5)
+            np.testing.assert_allclose(sigma[g][:r], f.sigma[g][:r], rtol=1e-4)
+
+
+# --------------------------------------------------- full-size, sampled
+
+def _full_size_check(torch, name, sample_seqs, sample_heads, steps=2):
+    """Full workload sizes, in the launch configuration the benchmark uses:
+    GPU fit over the whole batch; rank and captured energy of one group
+    against the oracle; codes of sampled (sequence, head) pairs bit-exact
+    against the oracle encode with the GPU basis; attention of sampled
+    (sequence, query head) pairs against the oracle."""
+    w = synth.WORKLOADS[name]
+    lens = synth.prefill_lengths(w)
+    S = int(lens.max())
+    total = S + steps
+    gpk = synth.group_params(w, 0)
+    gpv = synth.group_params(w, 1)
+    cache = _cache(torch, w, total)
+    kbuf = torch.zeros((w.batch, w.n_kv_heads, S, w.head_dim), dtype=torch.float16, device="cuda")
+    vbuf = torch.zeros_like(kbuf)
+    dec_k = np.zeros((w.batch, w.n_kv_heads, steps, w.head_dim), np.float16)
+    dec_v = np.zeros_like(dec_k)
+    hostk, hostv = {}, {}
+    for b in range(w.batch):
+        kb = synth.kv_sequence(w, 0, b, int(lens[b]) + steps, gpk)
+        vb = synth.kv_sequence(w, 1, b, int(lens[b]) + steps, gpv)
+        kbuf[b, :, :lens[b]] = _dev(torch, kb[:, :lens[b]])
+        vbuf[b, :, :lens[b]] = _dev(torch, vb[:, :lens[b]])
+        dec_k[b], dec_v[b] = kb[:, lens[b]:], vb[:, lens[b]:]
+        if b in sample_seqs:
+            hostk[b], hostv[b] = kb, vb
+    cache.fit(kbuf, vbuf, lens)
+    cache.encode_append(kbuf, vbuf, n_new=lens)
+    layer = _layer(cache, w)
+    # fit: one group against the oracle fit of that group (all sequences)
+    g = 0
+    hpg = w.n_kv_heads // w.n_head_groups
+    for tensor, buf in ((0, kbuf), (1, vbuf)):
+        xg = buf[:, g * hpg:(g + 1) * hpg].cpu().numpy()
+        r_or, basis_or, mu_or, _ = oracle.fit_group(xg, lens, 1, 0, rank=w.rank or 0, tau=w.energy)
+        rows = np.concatenate([xg[b, h, :lens[b]] for b in range(w.batch) for h in range(hpg)])
+        r = layer.fit[tensor].r
+        if w.rank:
+            assert r == r_or
+        else:
+            # the shared rank is the minimum over groups; group 0's own rank
+            # must be >= it, and the GPU rank equals the oracle's minimum
+            assert r <= r_or
+        e_gpu = _energy(rows, mu_or, layer.fit[tensor].V(g))
+        e_or = _energy(rows, mu_or, basis_or[:, :r])
+        assert abs(e_gpu - e_or) <= 1e-4, (tensor, e_gpu, e_or)
+        del rows, xg
+    del kbuf, vbuf
+    # decode steps for all sequences, attention checked on samples
+    for step in range(steps):
+        kt = np.ascontiguousarray(dec_k[:, :, step:step + 1])
+        vt = np.ascontiguousarray(dec_v[:, :, step:step + 1])
+        cache.encode_append(_dev(torch, kt), _dev(torch, vt))
+        q = np.stack([synth.queries(w, b)[step] for b in range(w.batch)])
+        out = cache.decode_attend(_dev(torch, q)).cpu().numpy()
+        if step == steps - 1:
+            for b in sample_seqs:
+                n = int(lens[b]) + step + 1
+                xs = (hostk[b][:, :n], hostv[b][:, :n])
+                _compare_state(cache, layer, xs, b, heads=sample_heads)
+                for h in sample_heads:
+                    ks = layer.encode_head(xs[0][h], h, 0)
+                    vs = layer.encode_head(xs[1][h], h, 1)
+                    for qh in range(h * w.gqa, (h + 1) * w.gqa):
+                        grp = layer.group_of(h)
+                        ref = oracle.attend(layer.decode_head(ks, 0), layer.fit[0].V(grp),
+                                            layer.fit[0].mu[grp], layer.decode_head(vs, 1),
+                                            layer.fit[1].V(grp), layer.fit[1].mu[grp], q[b, qh],
+                                            1 / math.sqrt(w.head_dim))
+                        _check_attention(out[b, qh], ref, f"{name} seq {b} qhead {qh}")
+    st = cache.stats()
+    assert st["compressed_key_bytes"] < st["fp16_key_bytes"]
+    assert st["compressed_value_bytes"] < st["fp16_value_bytes"]
+    return cache
+
+
+def test_full_single_b1_s512_r32(torch):
+    _full_size_check(torch, "single_b1_s512_r32", [0], range(8), steps=16)
+
+
+def test_full_gqa3_b1_s4096_e90(torch):
+    _full_size_check(torch, "gqa3_b1_s4096_e90", [0], [0, 5], steps=3)
+
+
+def test_full_vlat16_b8_s8192_r64(torch):
+    _full_size_check(torch, "vlat16_b8_s8192_r64", [3], [2], steps=2)
+
+
+def test_full_long_b4_s32768_e90(torch):
+    c = _full_size_check(torch, "long_b4_s32768_e90", [1], [7], steps=2)
+    st = c.stats()
+    assert st["assigned_avg_bits"] < 2.0
+
+
+def test_full_serve_b64_s1k16k_r32(torch):
+    _full_size_check(torch, "serve_b64_s1k16k_r32", [0, 63], [4], steps=2)
