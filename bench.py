@@ -1,0 +1,220 @@
+"""Benchmark of the latent KV cache hot path on one MI355X.
+
+One step = one pass of the whole path over the long-context workload
+(4 sequences x 32768 prefill tokens, 32 query / 8 kv heads, D = 128, 4 head
+groups, 90%-energy rank, 64 decode steps):
+  fit (Gram kernels + host eigensolve) -> encode of the prefill ->
+  64 x (append one token per sequence -> decode-attend).
+All inputs are resident in HBM before the timed region.
+
+`value` is decode-attend throughput: sequences x decode steps per second of
+decode-attend time, measured with HIP events recorded on the stream the
+library launches on, around every decode-attend call.  The roofline object
+prices the decode-attend call against MI355X's 8 TB/s HBM with the
+algorithmic bytes of each call (packed codes + metadata + fp32 tails + bases
+and means + query and output).  The CPU baseline times the plain oracle's
+decode attention for one sequence on the host.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from rank_latent_kv_amd import synth  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "latent decode-attend tok/s + HBM GB/s (% of peak); encode Mtok/s"
+
+
+def attend_bytes(lens, H, Hq, D, G, rk, nhk, rv, nhv, vq):
+    """Algorithmic bytes of one decode-attend call over sequences of lengths
+    `lens`: complete-group records (codes + fp16 scale/zero words), fp32 tail
+    latents, fp16 value latents of valid tokens, K/V bases and means, query
+    in and output out."""
+    wk = 4 * nhk + 2 * (rk - nhk) + rk
+    wv = 4 * nhv + 2 * (rv - nhv) + rv
+    tot = 0
+    for n in lens:
+        nf, nt = n // 32, n % 32
+        tot += H * (nf * wk * 4 + nt * rk * 4)
+        tot += H * ((nf * wv * 4 + nt * rv * 4) if vq else n * rv * 2)
+    tot += G * D * (rk + 1) * 4 + G * D * (rv + 1) * 4
+    tot += len(lens) * Hq * D * 2 * 2
+    return tot
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="long_b4_s32768_e90")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the latent KV path is built and measured "
+              "on a single MI355X (multi-GPU sharding is a design note, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rank_latent_kv_amd.palu import LatentKVCache
+
+    w = synth.WORKLOADS[args.workload]
+    lens = synth.prefill_lengths(w)
+    S = int(lens.max())
+    T = w.steps
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    # ---- inputs, generated on the host and made resident in HBM
+    t0 = time.time()
+    gpk, gpv = synth.group_params(w, 0), synth.group_params(w, 1)
+    kpre = torch.zeros((w.batch, w.n_kv_heads, S, w.head_dim), dtype=torch.float16, device=dev)
+    vpre = torch.zeros_like(kpre)
+    kdec = torch.empty((T, w.batch, w.n_kv_heads, 1, w.head_dim), dtype=torch.float16, device=dev)
+    vdec = torch.empty_like(kdec)
+    host_k0 = host_v0 = None
+    for b in range(w.batch):
+        kb = synth.kv_sequence(w, 0, b, int(lens[b]) + T, gpk)
+        vb = synth.kv_sequence(w, 1, b, int(lens[b]) + T, gpv)
+        kpre[b, :, :lens[b]] = torch.from_numpy(kb[:, :lens[b]]).to(dev)
+        vpre[b, :, :lens[b]] = torch.from_numpy(vb[:, :lens[b]]).to(dev)
+        kdec[:, b, :, 0] = torch.from_numpy(np.ascontiguousarray(kb[:, lens[b]:].transpose(1, 0, 2))).to(dev)
+        vdec[:, b, :, 0] = torch.from_numpy(np.ascontiguousarray(vb[:, lens[b]:].transpose(1, 0, 2))).to(dev)
+        if b == 0:
+            host_k0, host_v0 = kb, vb
+    q_all = torch.from_numpy(np.stack([synth.queries(w, b, T) for b in range(w.batch)], axis=1)).to(dev)
+    gen_s = time.time() - t0
+
+    cache = LatentKVCache(w.head_dim, w.n_kv_heads, w.n_q_heads, w.n_head_groups, w.batch,
+                          S + T, rank=w.rank or 0, energy_threshold=w.energy,
+                          quantize_values=w.quantize_values)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_pass(record):
+        ev = []
+        e_fit0 = torch.cuda.Event(enable_timing=True)
+        e_fit0.record(stream)
+        t_fit = time.perf_counter()
+        cache.fit(kpre, vpre, lens)
+        t_fit = time.perf_counter() - t_fit
+        e_enc0 = torch.cuda.Event(enable_timing=True)
+        e_enc1 = torch.cuda.Event(enable_timing=True)
+        e_enc0.record(stream)
+        cache.encode_append(kpre, vpre, n_new=lens)
+        e_enc1.record(stream)
+        for t in range(T):
+            ea = torch.cuda.Event(enable_timing=True)
+            eb = torch.cuda.Event(enable_timing=True)
+            ec = torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            cache.encode_append(kdec[t], vdec[t])
+            eb.record(stream)
+            cache.decode_attend(q_all[t], out=out)
+            ec.record(stream)
+            ev.append((ea, eb, ec))
+        return t_fit, (e_enc0, e_enc1), ev
+
+    for _ in range(args.warmup):
+        one_pass(False)
+    torch.cuda.synchronize()
+
+    fit_s, enc_ms, app_ms, att_ms = [], [], [], []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    results = [one_pass(True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    for t_fit, (e0, e1), ev in results:
+        fit_s.append(t_fit)
+        enc_ms.append(e0.elapsed_time(e1))
+        for ea, eb, ec in ev:
+            app_ms.append(ea.elapsed_time(eb))
+            att_ms.append(eb.elapsed_time(ec))
+
+    st = cache.stats()
+    rk, rv, nhk, nhv = st["r_k"], st["r_v"], st["n_hi_k"], st["n_hi_v"]
+    per_call_bytes = [attend_bytes([int(n) + t + 1 for n in lens], w.n_kv_heads, w.n_q_heads,
+                                   w.head_dim, w.n_head_groups, rk, nhk, rv, nhv,
+                                   w.quantize_values) for t in range(T)]
+    mean_bytes = float(np.mean(per_call_bytes))
+    att_mean_ms = float(np.mean(att_ms))
+    decode_tok_s = w.batch * len(att_ms) / (sum(att_ms) / 1e3)
+    achieved_gbps = mean_bytes / (att_mean_ms / 1e3) / 1e9
+    enc_positions = float(lens.sum())
+    encode_mtok_s = enc_positions / (float(np.mean(enc_ms)) / 1e3) / 1e6
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, cache, host_k0, host_v0, lens, q_all[0, 0].cpu().numpy())
+
+    line = {
+        "metric": METRIC,
+        "value": round(decode_tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "prefill": S, "decode_steps": T,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "head_groups": w.n_head_groups,
+                   "rank_k": rk, "rank_v": rv, "quantize_values": w.quantize_values},
+        "roofline": {"bound": "hbm", "kernel": "palu_decode_attend (attend + combine)",
+                     "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(mean_bytes), "launch_us": round(att_mean_ms * 1e3, 2)},
+        "decode_attend_us": round(att_mean_ms * 1e3, 2),
+        "append_us": round(float(np.mean(app_ms)) * 1e3, 2),
+        "encode_mtok_s": round(encode_mtok_s, 2),
+        "encode_ms": round(float(np.mean(enc_ms)), 3),
+        "fit_ms": round(float(np.mean(fit_s)) * 1e3, 2),
+        "input_gen_s": round(gen_s, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, cache, k0, v0, lens, q0):
+    """The oracle's decode attention for sequence 0 (all query heads, one
+    step), single-threaded, with the GPU's basis: dequantise the stored
+    records and reconstruct K/V in fp64 per query head."""
+    import oracle
+    fits = []
+    for t in (0, 1):
+        r, basis, mu, sigma = cache.get_basis(t)
+        full = np.zeros((w.n_head_groups, w.head_dim, w.head_dim), np.float32)
+        full[:, :, :r] = basis
+        fits.append(oracle.Fit(r, np.full(w.n_head_groups, r, np.int32), full, mu, sigma))
+    layer = oracle.OracleLayer(w.head_dim, w.n_q_heads, w.n_kv_heads, w.n_head_groups, *fits,
+                               quantize_values=w.quantize_values)
+    n = int(lens[0]) + 1
+    ks = [layer.encode_head(k0[h, :n], h, 0) for h in range(w.n_kv_heads)]
+    vs = [layer.encode_head(v0[h, :n], h, 1) for h in range(w.n_kv_heads)]
+    t = time.perf_counter()
+    layer.attend(ks, vs, np.broadcast_to(q0, (w.n_q_heads, w.head_dim)).astype(np.float16))
+    dt = time.perf_counter() - t
+    return {"value": round(1.0 / dt, 4), "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"decode-attend of 1 sequence x {w.n_q_heads} query heads over "
+                      f"{n} tokens (one decode step of one sequence), fp64, "
+                      f"{dt:.1f} s single-threaded"}
+
+
+if __name__ == "__main__":
+    main()

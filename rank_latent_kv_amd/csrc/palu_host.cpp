@@ -34,8 +34,9 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int kGramElems = kHeadDim * kHeadDim + kHeadDim;
 constexpr int kGramMaxRowsPerBlock = 8192;   // bounds fp32 accumulation per tile
-constexpr int kAttendTargetGroups = 2048;    // workgroups aimed for per decode launch
-constexpr int kAttendMinChunk = 8;           // token groups per split, at least
+constexpr int kAttendTargetGroups = 1024;    // workgroups aimed for per decode launch
+constexpr size_t kAttendLdsCap = 64 * 1024;  // LDS per workgroup the split size aims for
+constexpr size_t kAttendLdsMax = 160 * 1024; // LDS per workgroup on gfx950
 
 int n_hi_of(int r, float frac) {
     return static_cast<int>(std::floor(static_cast<double>(frac) * static_cast<double>(r)));
@@ -49,7 +50,7 @@ struct palu_cache {
     int D = 0, H = 0, Hq = 0, G = 0, hpg = 0, gqa = 0, r_max = 0, max_groups = 0;
     int gram_nb_cap = 0;
     // byte offsets of each region inside the bound buffer
-    size_t off_basis[2]{}, off_mu[2]{}, off_rec[2]{}, off_tail[2]{};
+    size_t off_basis[2]{}, off_bt16[2]{}, off_mu[2]{}, off_rec[2]{}, off_tail[2]{};
     size_t off_gram_part = 0, off_gram_out = 0, off_seg = 0, off_attend = 0, total = 0;
     char *dev = nullptr;
     size_t dev_bytes = 0;
@@ -70,10 +71,11 @@ struct palu_cache {
         d.n_hi = quantized(t) ? n_hi[t] : 0;
         d.words = words_for(t, r[t]);
         d.fp16_latents = quantized(t) ? 0 : 1;
-        d.head_stride = static_cast<int64_t>(max_groups) * d.words;
+        d.head_stride = (static_cast<int64_t>(max_groups) * d.words + 3) / 4 * 4;
         d.records = reinterpret_cast<uint32_t *>(dev + off_rec[t]);
         d.tail = quantized(t) ? reinterpret_cast<float *>(dev + off_tail[t]) : nullptr;
         d.basis = reinterpret_cast<float *>(dev + off_basis[t]);
+        d.basis_t16 = reinterpret_cast<uint16_t *>(dev + off_bt16[t]);
         d.mu = reinterpret_cast<float *>(dev + off_mu[t]);
         return d;
     }
@@ -134,6 +136,11 @@ int upload_basis(palu_cache *c, int t) {
     e = hipMemcpy(c->dev + c->off_mu[t], c->mu_h[t].data(), c->mu_h[t].size() * sizeof(float),
                   hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "mean upload");
+    e = launch_basis_t16(reinterpret_cast<const float *>(c->dev + c->off_basis[t]),
+                         reinterpret_cast<uint16_t *>(c->dev + c->off_bt16[t]), c->G, c->r[t], nullptr);
+    if (e != hipSuccess) return hip_fail(e, "basis fp16 copy");
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "basis upload synchronize");
     return PALU_OK;
 }
 
@@ -190,9 +197,10 @@ PALU_API int palu_cache_create(const palu_config *cfg, int32_t max_batch, int32_
     };
     for (int t = 0; t < 2; ++t) {
         c->off_basis[t] = take(sizeof(float) * c->G * c->D * c->r_max);
+        c->off_bt16[t] = take(sizeof(uint16_t) * c->G * c->D * c->r_max);
         c->off_mu[t] = take(sizeof(float) * c->G * c->D);
-        c->off_rec[t] = take(sizeof(uint32_t) * static_cast<size_t>(max_batch) * c->H * c->max_groups *
-                             c->words_for(t, c->r_max));
+        const size_t head_words = (static_cast<size_t>(c->max_groups) * c->words_for(t, c->r_max) + 3) / 4 * 4;
+        c->off_rec[t] = take(sizeof(uint32_t) * static_cast<size_t>(max_batch) * c->H * head_words);
         c->off_tail[t] = c->quantized(t)
                              ? take(sizeof(float) * static_cast<size_t>(max_batch) * c->H * 2 * kTokGroup * c->r_max)
                              : 0;
@@ -479,6 +487,7 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
         aa.q = static_cast<const uint16_t *>(q) + b0 * row_elems;
         aa.out = static_cast<uint16_t *>(out) + b0 * row_elems;
         aa.partial = reinterpret_cast<float *>(c->dev + c->off_attend);
+
         aa.k = c->tensor_dev(0);
         aa.v = c->tensor_dev(1);
         aa.B = nb;
@@ -498,19 +507,35 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
             units += static_cast<int64_t>(c->H) * std::max(1, nfull);
             max_full = std::max(max_full, nfull);
         }
-        int chunk = static_cast<int>(std::max<int64_t>(kAttendMinChunk, (units + kAttendTargetGroups - 1) / kAttendTargetGroups));
-        chunk = std::max(chunk, (max_full + kMaxSplits - 1) / kMaxSplits);
-        aa.chunk = chunk;
+        // split size: a multiple of the groups one workgroup iteration
+        // covers, large enough for the split limit, small enough for LDS
+        const int per_iter = 4 * (16 / c->gqa);
+        const bool vq = !aa.v.fp16_latents;
+        auto lds_for = [&](int64_t ch) {
+            return attend_lds_bytes(c->gqa, aa.k.r, aa.k.n_hi, aa.v.r, static_cast<int>(ch), aa.k.words,
+                                    aa.v.words, vq);
+        };
+        auto round_up = [](int64_t v, int64_t m) { return (v + m - 1) / m * m; };
+        int64_t chunk = round_up(std::max<int64_t>(1, (units + kAttendTargetGroups - 1) / kAttendTargetGroups), per_iter);
+        while (chunk > 1 && lds_for(chunk) > kAttendLdsCap)
+            chunk = chunk > per_iter ? chunk - per_iter : chunk - 1;
+        chunk = std::max<int64_t>(chunk, (max_full + kMaxSplits - 1) / kMaxSplits);
+        const size_t lds = lds_for(chunk);
+        if (lds > kAttendLdsMax)
+            return fail(PALU_ERR_UNSUPPORTED, "sequence too long for the split limit at this rank");
+        aa.chunk = static_cast<int>(chunk);
+        aa.stage_words = 0;
         aa.work_prefix[0] = 0;
         for (int i = 0; i < nb; ++i) {
             const int nfull = aa.len[i] / kTokGroup;
-            aa.nsplit[i] = std::max(1, (nfull + chunk - 1) / chunk);
+            aa.nsplit[i] = std::max(1, static_cast<int>((nfull + chunk - 1) / chunk));
             aa.work_prefix[i + 1] = aa.work_prefix[i] + c->H * aa.nsplit[i];
         }
-        hipError_t e = launch_attend(aa, aa.work_prefix[nb], s);
+        hipError_t e = launch_attend(aa, aa.work_prefix[nb], lds, s);
         if (e != hipSuccess) return hip_fail(e, "attend launch");
         e = launch_combine(aa, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");
+
     }
     return PALU_OK;
 }

@@ -12,7 +12,7 @@ namespace palu {
 constexpr int kTokGroup = 32;      // tokens per quantisation group
 constexpr int kHeadDim = 128;      // head_dim the kernels are built for
 constexpr int kMaxCallSeqs = 64;   // sequences per launch (argument arrays)
-constexpr int kMaxSplits = 64;     // token splits per (sequence, kv head)
+constexpr int kMaxSplits = 128;    // token splits per (sequence, kv head)
 constexpr int kMaxGqa = 8;         // query heads per kv head in the attend kernel
 constexpr int kGramRowsPerBlockMin = 512;
 
@@ -27,10 +27,12 @@ struct TensorDev {
     uint32_t *records;   // [slots][H][max_groups][words]
     float *tail;         // [slots][H][2][32][r]  (nullptr for fp16 latents)
     float *basis;        // [G][D][r] fp32, d-major
+    uint16_t *basis_t16; // [G][r][D] fp16 copy, channel-major (decode query absorption)
     float *mu;           // [G][D] fp32
     int r, n_hi, words;
     int fp16_latents;    // V stored as fp16 latents (no tail, no meta)
-    int64_t head_stride; // words between consecutive (slot, head) = max_groups * words
+    int64_t head_stride; // words between consecutive (slot, head): max_groups * words
+                         // rounded up to a multiple of 4 (16-byte aligned streams)
 };
 
 struct GramArgs {
@@ -67,6 +69,7 @@ struct AttendArgs {
     int B, Hq, Hkv, gqa, hpg;
     int chunk;                // complete token groups per split
     float qscale;             // softmax scale * log2(e)
+    int stage_words;          // LDS words reserved for staged records
     int slot[kMaxCallSeqs];
     int len[kMaxCallSeqs];
     int sel[kMaxCallSeqs];
@@ -74,12 +77,17 @@ struct AttendArgs {
     int work_prefix[kMaxCallSeqs + 1];  // workgroups before sequence i
 };
 
+// LDS bytes of one attend workgroup for a split of `chunk` token groups.
+size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int chunk, int words_k, int words_v, bool vq);
+
 // Launchers (defined in palu_kernels.hip).  They return the launch status.
 hipError_t launch_gram(const GramArgs &a, hipStream_t s);
 hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &a, int max_touched, hipStream_t s);
-hipError_t launch_attend(const AttendArgs &a, int n_work, hipStream_t s);
+hipError_t launch_attend(const AttendArgs &a, int n_work, size_t lds_bytes, hipStream_t s);
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s);
+// fp16 channel-major copy of a basis: dst[g][c][d] = fp16(src[g][d][c]).
+hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, hipStream_t s);
 
 // Host symmetric eigensolver (palu_eigen.cpp): Householder tridiagonalisation
 // followed by implicit-shift QL.  a: n x n row-major symmetric (destroyed);

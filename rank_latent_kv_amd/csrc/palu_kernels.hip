@@ -35,6 +35,16 @@ __device__ __forceinline__ uint32_t f2h_bits(float f) {
     return static_cast<uint32_t>(__half_as_ushort(__float2half_rn(f)));
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
 // ---------------------------------------------------------------- Gram ----
 //
 // Workgroup (block, group g, tensor) owns rows [block*rpb, (block+1)*rpb) of
@@ -290,24 +300,144 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 //
 // Workgroup = (call row i, kv head h, split s).  Split s covers complete
 // token groups [s*chunk, min(nfull, (s+1)*chunk)); the last split also
-// covers the incomplete group.  With the query absorbed into the key basis,
-//   score_t = qs * (q . (V_K l_t + mu_K)) = sum_c qt_c l_tc + c0,
-// where qt = qs V_K^T q and c0 = qs q . mu_K (qs = scale * log2 e, so the
-// softmax uses exp2).  The workgroup keeps a running max m, denominator l
-// and latent accumulator o_c = sum_t p_t lv_tc for each of its query heads.
+// covers the incomplete group (fp32 tail latents).  With the query absorbed
+// into the key basis, score_t = qs * q . (V_K l_t + mu_K) = qt . l_t + const
+// with qt = qs V_K^T q (qs = scale * log2 e); the constant q . mu_K is the
+// same for every token of a head and cancels in the softmax.
+//
+// Each wave owns 16 "streams" n = slot * g + head: per iteration it takes
+// S = 16 / g consecutive token groups (slots) and runs, for both 16-token
+// halves of the groups,
+//   scores  D[t][n] = sum_k A[t][k] B[k][n]    (v_mfma_f32_16x16x32_f16)
+// where k runs over (slot, 8-channel block) pairs, A holds the token's
+// latents of that block dequantised to fp16 (code * scale16 + zero16 with
+// packed fp16 arithmetic), and B is the block-diagonal constant qt in fp16
+// (B[(slot j, block)][n] = qt[head(n)][block] if j == slot(n), else 0), so
+// every output lane is a useful score.  Values use a second MFMA per slot,
+//   O[n][c] += sum_t p[n][t] lv[t][c],
+// with A = softmax weights of the slot's streams (fp16) and B = that group's
+// dequantised value latents.  The online softmax keeps one running max per
+// stream and rescales only when a new block maximum exceeds it by more than
+// kRescaleSlack (log2 units), so weights stay <= 2^kRescaleSlack.
+//
+// Channel order inside an 8-channel block follows the code extraction:
+// halves [c0, c4, c1, c5, c2, c6, c3, c7]; A and B use the same order.
 
-__device__ __forceinline__ float wave_max(float v) {
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
+constexpr int kWaves = 4;
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kBtabMaxU = 16;   // score B-operand table kept in LDS up to this many MFMA k-steps
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+// LDS layout of one attend workgroup (byte offsets).  Shared by the kernel
+// and the host, which sizes the dynamic LDS from it.
+struct AttendLds {
+    int qt, qt16, ts, mst, lst, ost, tp, hm, btab, kpair, vpair, stage, total;
+    int nbk, nub;
+    bool use_btab;
+};
+
+__host__ __device__ inline int lds_take(int &o, int bytes) {
+    const int r = o;
+    o += (bytes + 15) & ~15;
+    return r;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+__host__ __device__ inline AttendLds attend_lds(int g, int rk, int nhk, int rv, int chunk, int wk, int wv, bool vq) {
+    AttendLds L;
+    const int S = 16 / g;
+    L.nbk = (nhk + 7) / 8 + (rk - nhk + 7) / 8;
+    L.nub = (S * L.nbk + 3) / 4;
+    L.use_btab = L.nub <= kBtabMaxU;
+    int o = 0;
+    L.qt = lds_take(o, g * kHeadDim * 4);
+    L.qt16 = lds_take(o, g * 16 * 16);
+    L.ts = lds_take(o, g * (kWaves * 16 + 1) * 4);
+    L.mst = lds_take(o, (kWaves + 1) * 16 * 4);
+    L.lst = lds_take(o, (kWaves + 1) * 16 * 4);
+    L.ost = lds_take(o, (kWaves + 1) * 16 * rv * 4);
+    L.tp = lds_take(o, g * 32 * 4);
+    L.hm = lds_take(o, kMaxGqa * 4);
+    L.btab = lds_take(o, L.use_btab ? L.nub * 64 * 16 : 0);
+    L.kpair = lds_take(o, chunk * L.nbk * 8 * 4);
+    L.vpair = lds_take(o, vq ? chunk * rv * 2 * 4 : 0);
+    L.stage = lds_take(o, (chunk * (wk + (vq ? wv : 0)) + 16) * 4);
+    L.total = o;
+    return L;
 }
 
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// (code * scale + zero) for a pair of magic halves 1024 + code, in fp16
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t magic, uint32_t spair, uint32_t zpair) {
+    const h2 code = __builtin_bit_cast(h2, magic) - (h2){(_Float16)1024.0f, (_Float16)1024.0f};
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(code, __builtin_bit_cast(h2, spair),
+                                                                   __builtin_bit_cast(h2, zpair)));
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float a, float b) {
+    const h2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp16 pair, round toward zero (one instruction); used for softmax weights
+__device__ __forceinline__ uint32_t pack_rtz(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// A 32-bit constant held in a VGPR, so that three-operand ALU forms
+// (v_and_or_b32) can take it without a literal encoding.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+    return r;
+}
+
+__device__ __forceinline__ f16x8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const u4v t = {a, b, c, d};
+    return __builtin_bit_cast(f16x8, t);
+}
+
+// 8 codes of one token from a 32-bit window (channel k at bit w*k) ->
+// dequantised fp16 pairs (channel k, channel k + 4), k = 0..3.
+template <bool W4>
+__device__ __forceinline__ f16x8 dequant8(uint32_t X, const uint4 &sp, const uint4 &zp, uint32_t cm,
+                                          uint32_t magic) {
+    // 2-bit codes: move codes 4..7 (bits 8..15) up to bits 16..23
+    const uint32_t U = W4 ? X : perm_b32(X, X, 0x0C010C00u);
+    constexpr int wc = W4 ? 4 : 2;
+    return as_h8(dequant_pair((U & cm) | magic, sp.x, zp.x),
+                 dequant_pair(((U >> wc) & cm) | magic, sp.y, zp.y),
+                 dequant_pair(((U >> (2 * wc)) & cm) | magic, sp.z, zp.z),
+                 dequant_pair(((U >> (3 * wc)) & cm) | magic, sp.w, zp.w));
+}
+
+__device__ __forceinline__ f16x8 dequant8_any(uint32_t X, bool w4, const uint4 &sp, const uint4 &zp) {
+    const uint32_t U = w4 ? X : perm_b32(X, X, 0x0C010C00u);
+    const int wc = w4 ? 4 : 2;
+    const uint32_t cm = w4 ? 0x000F000Fu : 0x00030003u;
+    return as_h8(dequant_pair((U & cm) | 0x64006400u, sp.x, zp.x),
+                 dequant_pair(((U >> wc) & cm) | 0x64006400u, sp.y, zp.y),
+                 dequant_pair(((U >> (2 * wc)) & cm) | 0x64006400u, sp.z, zp.z),
+                 dequant_pair(((U >> (3 * wc)) & cm) | 0x64006400u, sp.w, zp.w));
+}
+
+// Workgroup = (call row i, kv head h, split s); see the section comment.
+// S = 16 / gqa token groups (slots) per wave iteration, NBV = value-channel
+// blocks of 16.
+template <int S, int NBV>
 __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
-    const int wid = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int ln = lane & 15, kb = lane >> 4;
+
+    // ---- work item
+    const int wid = blockIdx.x;
     int i = 0;
     while (i + 1 < a.B && a.work_prefix[i + 1] <= wid) ++i;
     const int rem = wid - a.work_prefix[i];
@@ -317,196 +447,507 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     const int nfull = len >> 5, ntail = len & 31;
     const int jb = s * a.chunk;
     const int je = jb + a.chunk < nfull ? jb + a.chunk : nfull;
+    const int ntg = je > jb ? je - jb : 0;
     const bool do_tail = (s == ns - 1) && ntail > 0;
     const int g = a.gqa, grp = h / a.hpg;
-    const int rk = a.k.r, rv = a.v.r, nhk = a.k.n_hi, nlk = a.k.r - a.k.n_hi;
-    const int nhv = a.v.n_hi;
+    const int NS = S * g;
+    const int rk = a.k.r, nhk = a.k.n_hi, nlk = rk - nhk;
+    const int nbh = (nhk + 7) >> 3;
+    const int rv = a.v.r, nhv = a.v.n_hi;
+    const int WK = a.k.words, WV = a.v.words;
+    const bool vq = !a.v.fp16_latents;
+    const int kmeta = 4 * nhk + 2 * nlk, vmeta = 4 * nhv + 2 * (rv - nhv);
 
-    __shared__ float qf[kMaxGqa][kHeadDim];
-    __shared__ float qt[kMaxGqa][kHeadDim];
-    __shared__ float c0s[kMaxGqa];
-    __shared__ float sp[kMaxGqa][256];
-    __shared__ float ot[kMaxGqa][kHeadDim];
-    __shared__ float mst[kMaxGqa], lst[kMaxGqa], alp[kMaxGqa];
-    __shared__ float red[4][kMaxGqa];
-
-    for (int e = tid; e < g * kHeadDim; e += 256) {
-        const int hh = e >> 7, d = e & 127;
-        qf[hh][d] = h2f(a.q[(static_cast<int64_t>(i) * a.Hq + h * g + hh) * kHeadDim + d]);
-        ot[hh][d] = 0.0f;
-    }
-    if (tid < g) {
-        mst[tid] = -INFINITY;
-        lst[tid] = 0.0f;
-    }
-    __syncthreads();
-    const float *bk = a.k.basis + static_cast<int64_t>(grp) * kHeadDim * rk;
-    for (int e = tid; e < g * rk; e += 256) {
-        const int hh = e / rk, c = e - (e / rk) * rk;
-        float acc = 0.0f;
-        for (int d = 0; d < kHeadDim; ++d) acc = fmaf(qf[hh][d], bk[d * rk + c], acc);
-        qt[hh][c] = acc * a.qscale;
-    }
-    for (int hh = tid; hh < g; hh += 256) {
-        float acc = 0.0f;
-        for (int d = 0; d < kHeadDim; ++d) acc = fmaf(qf[hh][d], a.k.mu[grp * kHeadDim + d], acc);
-        c0s[hh] = acc * a.qscale;
-    }
-    __syncthreads();
+    const AttendLds L = attend_lds(g, rk, nhk, rv, a.chunk, WK, WV, vq);
+    const int nbk = L.nbk, nub = L.nub, npair = S * nbk;
+    float *qt = reinterpret_cast<float *>(lds + L.qt);
+    uint4 *qt16 = reinterpret_cast<uint4 *>(lds + L.qt16);
+    _Float16 *qt16h = reinterpret_cast<_Float16 *>(lds + L.qt16);
+    float *ts = reinterpret_cast<float *>(lds + L.ts);
+    float *mst = reinterpret_cast<float *>(lds + L.mst);
+    float *lst = reinterpret_cast<float *>(lds + L.lst);
+    float *ost = reinterpret_cast<float *>(lds + L.ost);
+    float *tp = reinterpret_cast<float *>(lds + L.tp);
+    float *hm = reinterpret_cast<float *>(lds + L.hm);
+    uint4 *btab = reinterpret_cast<uint4 *>(lds + L.btab);
+    uint32_t *kpair = reinterpret_cast<uint32_t *>(lds + L.kpair);
+    uint32_t *vpair = reinterpret_cast<uint32_t *>(lds + L.vpair);
+    uint32_t *stage = reinterpret_cast<uint32_t *>(lds + L.stage);
 
     const int64_t hb = static_cast<int64_t>(slot) * a.Hkv + h;
-    const uint32_t *krec0 = a.k.records + hb * a.k.head_stride;
-    const uint32_t *vrec0 = a.v.records + hb * a.v.head_stride;
-    const float *ktail = a.k.tail ? a.k.tail + (hb * 2 + a.sel[i]) * 32 * rk : nullptr;
-    const float *vtail = a.v.tail ? a.v.tail + (hb * 2 + a.sel[i]) * 32 * rv : nullptr;
+    const uint32_t *kg = a.k.records + hb * a.k.head_stride;
+    const uint32_t *vg = a.v.records + hb * a.v.head_stride;
 
-    const int ncoded = (je - jb + 7) >> 3;
-    const int nblk = ncoded + (do_tail ? 1 : 0);
-    for (int blk = 0; blk < nblk; ++blk) {
-        const bool tb = blk == ncoded;
-        const int p0 = tb ? 32 * nfull : 32 * (jb + 8 * blk);
-        const int p1 = tb ? len : (32 * je < p0 + 256 ? 32 * je : p0 + 256);
-        const int p = p0 + tid;
-        const bool valid = p < p1;
-        // scores
-        if (valid) {
-            float sc[kMaxGqa];
-            for (int hh = 0; hh < kMaxGqa; ++hh) sc[hh] = hh < g ? c0s[hh] : 0.0f;
-            if (!tb) {
-                const uint32_t *rec = krec0 + static_cast<int64_t>(p >> 5) * a.k.words;
-                const int t = p & 31;
-                const uint32_t *meta = rec + 4 * nhk + 2 * nlk;
-                for (int c = 0; c < rk; ++c) {
-                    uint32_t code;
-                    if (c < nhk) {
-                        const int pos = t * 4 * nhk + 4 * c;
-                        code = (rec[pos >> 5] >> (pos & 31)) & 15u;
-                    } else {
-                        const int pos = t * 2 * nlk + 2 * (c - nhk);
-                        code = (rec[4 * nhk + (pos >> 5)] >> (pos & 31)) & 3u;
-                    }
-                    const uint32_t mw = meta[c];
-                    const float l = fmaf(static_cast<float>(code), h2f(mw), h2f(mw >> 16));
-                    for (int hh = 0; hh < kMaxGqa; ++hh)
-                        if (hh < g) sc[hh] = fmaf(qt[hh][c], l, sc[hh]);
-                }
-            } else {
-                const float *tl = ktail + (p & 31) * rk;
-                for (int c = 0; c < rk; ++c) {
-                    const float l = tl[c];
-                    for (int hh = 0; hh < kMaxGqa; ++hh)
-                        if (hh < g) sc[hh] = fmaf(qt[hh][c], l, sc[hh]);
-                }
+    // ---- 1. stage the split's packed records in LDS (16-byte loads, all
+    //         issued before the first store)
+    const int64_t k_a = (static_cast<int64_t>(jb) * WK) & ~3LL;
+    const int k_words = ntg ? static_cast<int>((static_cast<int64_t>(je) * WK - k_a + 3) & ~3LL) : 0;
+    const int64_t v_a = (static_cast<int64_t>(jb) * WV) & ~3LL;
+    const int v_words = (vq && ntg) ? static_cast<int>((static_cast<int64_t>(je) * WV - v_a + 3) & ~3LL) : 0;
+    const int koff = static_cast<int>(static_cast<int64_t>(jb) * WK - k_a);          // record 0 of the split
+    const int voff = k_words + static_cast<int>(static_cast<int64_t>(jb) * WV - v_a);
+    {
+        const int nk4 = k_words >> 2, nv4 = v_words >> 2, n4 = nk4 + nv4;
+        const uint4 *ksrc = reinterpret_cast<const uint4 *>(kg + k_a);
+        const uint4 *vsrc = reinterpret_cast<const uint4 *>(vg + v_a);
+        uint4 *dst = reinterpret_cast<uint4 *>(stage);
+        for (int base = 0; base < n4; base += 256 * 8) {
+            uint4 buf[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = base + u * 256 + tid;
+                const uint4 *src = e < nk4 ? ksrc + e : vsrc + (e - nk4);
+                buf[u] = make_uint4(0u, 0u, 0u, 0u);
+                if (e < n4) buf[u] = *src;
             }
-            for (int hh = 0; hh < g; ++hh) sp[hh][tid] = sc[hh];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = base + u * 256 + tid;
+                if (e < n4) dst[e] = buf[u];
+            }
+        }
+    }
+
+    // ---- 2. absorbed query qt = qs V_K^T q on MFMA: rows = query heads of
+    //         this kv head, K = d, columns = 16-channel blocks of the fp16
+    //         channel-major key basis (wave w takes blocks w, w + 4, ...)
+    {
+        const int nbc = (rk + 15) >> 4;
+        const int qrow = i * a.Hq + h * g;
+        const bool qv = ln < g;
+        const uint16_t *qsrc = a.q + static_cast<int64_t>(qrow + (qv ? ln : 0)) * kHeadDim + 8 * kb;
+        uint4 qa[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            qa[st] = qv ? *reinterpret_cast<const uint4 *>(qsrc + 32 * st) : make_uint4(0u, 0u, 0u, 0u);
+        const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * rk * kHeadDim;
+        for (int cb = wv; cb < nbc; cb += kWaves) {
+            const int c = 16 * cb + ln;
+            const bool cvq = c < rk;
+            uint4 bb[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                bb[st] = cvq ? *reinterpret_cast<const uint4 *>(bt + static_cast<int64_t>(c) * kHeadDim + 32 * st + 8 * kb)
+                             : make_uint4(0u, 0u, 0u, 0u);
+            f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(qa[st].x, qa[st].y, qa[st].z, qa[st].w),
+                                                            as_h8(bb[st].x, bb[st].y, bb[st].z, bb[st].w), acc, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int hh = 4 * kb + v;
+                if (hh < g && cvq) qt[hh * rk + c] = acc[v] * a.qscale;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. per-split tables
+    // (a) qt in fp16 per (head, channel block), channel order [c0,c4,c1,c5,..]
+    for (int e = tid; e < g * nbk * 8; e += 256) {
+        const int hh = e / (nbk * 8), r2 = e - hh * nbk * 8;
+        const int q = r2 >> 3, idx = r2 & 7;
+        const int kk = (idx >> 1) + 4 * (idx & 1);
+        const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
+        const int chanend = q < nbh ? nhk : rk;
+        const int c = chan0 + kk;
+        qt16h[(hh * nbk + q) * 8 + idx] = c < chanend ? static_cast<_Float16>(qt[hh * rk + c])
+                                                      : static_cast<_Float16>(0.0f);
+    }
+    // (b) K scale/zero pairs per (group, channel block): words 0..3 scale
+    //     pairs (k, k + 4), words 4..7 zero pairs; padding channels are 0
+    for (int e = tid; e < ntg * nbk * 4; e += 256) {
+        const int tg = e / (nbk * 4), r2 = e - tg * nbk * 4;
+        const int q = r2 >> 2, k = r2 & 3;
+        const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
+        const int chanend = q < nbh ? nhk : rk;
+        const uint32_t *rec = stage + koff + tg * WK + kmeta;
+        const uint32_t wa = chan0 + k < chanend ? rec[chan0 + k] : 0u;
+        const uint32_t wb = chan0 + k + 4 < chanend ? rec[chan0 + k + 4] : 0u;
+        uint32_t *dst = kpair + (tg * nbk + q) * 8;
+        dst[k] = perm_b32(wb, wa, 0x05040100u);
+        dst[4 + k] = perm_b32(wb, wa, 0x07060302u);
+    }
+    // (c) V per (group, channel): fp32 scale and zero - 1024 * scale, for
+    //     the value epilogue (the value MFMA runs on 1024 + code)
+    float *vsz = reinterpret_cast<float *>(vpair);
+    if (vq) {
+        for (int e = tid; e < ntg * rv; e += 256) {
+            const int tg = e / rv, c = e - (e / rv) * rv;
+            const uint32_t mw = stage[voff + tg * WV + vmeta + c];
+            const float sc = h2f(mw), zr = h2f(mw >> 16);
+            vsz[2 * e] = sc;
+            vsz[2 * e + 1] = fmaf(-1024.0f, sc, zr);
+        }
+    }
+    __syncthreads();
+    // (d) block-diagonal score B operand per k-step u and lane
+    if (L.use_btab) {
+        for (int e = tid; e < nub * 64; e += 256) {
+            const int u = e >> 6, l2 = e & 63, n2 = l2 & 15;
+            const int p = 4 * u + (l2 >> 4);
+            const int q = p / S, j = p - (p / S) * S;
+            const bool ok = p < npair && n2 < NS && j == n2 / g;
+            btab[e] = ok ? qt16[(n2 - (n2 / g) * g) * nbk + q] : make_uint4(0u, 0u, 0u, 0u);
         }
         __syncthreads();
-        for (int hh = 0; hh < g; ++hh) {
-            const float m = wave_max(valid ? sp[hh][tid] : -INFINITY);
-            if (lane == 0) red[wv][hh] = m;
+    }
+
+    // ---- 4. main loop over token groups
+    const int slot_n = ln / g, head_n = ln - (ln / g) * g;
+    const bool live_n = ln < NS;
+    float m_run = -INFINITY, l_run = 0.0f;
+    f4 oacc[NBV];
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) oacc[nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
+    // per-lane value-channel addressing (column c = 16 nb + ln, clamped)
+    int vch[NBV], vw0[NBV], vw1[NBV], vs0[NBV], vwid[NBV], vwc[NBV];
+    uint32_t vcm[NBV], vbase[NBV];
+    const bool ones_col = vq && (rv & 15) != 0;     // column 15 of the last block is free
+    int row_slot[4];                                 // slot of value-output row 4*kb + v
+#pragma unroll
+    for (int v = 0; v < 4; ++v) row_slot[v] = (4 * kb + v) / g;
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) {
+        int c = 16 * nb + ln;
+        c = c < rv ? c : rv - 1;
+        const bool w4c = c < nhv;
+        const int wc = w4c ? 4 : 2;
+        const int bitbase = w4c ? 128 * c : 128 * nhv + 64 * (c - nhv);
+        const int b0 = bitbase + 4 * kb * wc, b1 = b0 + 16 * wc;
+        vch[nb] = c;
+        vw0[nb] = b0 >> 5;
+        vw1[nb] = b1 >> 5;
+        vs0[nb] = b0 & 31;          // b1 - b0 = 16 wc is a multiple of 32 bits
+        vwid[nb] = 4 * wc;
+        vwc[nb] = wc;
+        const bool one = ones_col && nb == NBV - 1 && ln == 15;
+        vcm[nb] = one ? 0u : (w4c ? 0x000F000Fu : 0x00030003u);
+        vbase[nb] = one ? 0x3C003C00u : 0x64006400u;
+    }
+    const uint32_t kmagic = vgpr_const(0x64006400u), km4 = vgpr_const(0x000F000Fu),
+                   km2 = vgpr_const(0x00030003u);
+    constexpr int per_iter = kWaves * S;
+    const int n_iter = (ntg + per_iter - 1) / per_iter;
+    for (int it = 0; it < n_iter; ++it) {
+        const int tb0 = (it * kWaves + wv) * S;      // split-relative group of slot 0
+        f4 sacc0 = {0.0f, 0.0f, 0.0f, 0.0f}, sacc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int u = 0; u < nub; ++u) {
+            const int p = 4 * u + kb;
+            int q, j;
+            if constexpr (S % 4 == 0) {
+                q = (4 * u) / S;            // the same for every lane of the wave
+                j = p - q * S;
+            } else {
+                q = p / S;
+                j = p - q * S;
+            }
+            // invalid pairs and groups past the split are read from a valid
+            // (clamped) record; their scores belong to masked streams
+            int tg = tb0 + j;
+            tg = tg < ntg ? tg : ntg - 1;
+            const int qc = q < nbk ? q : nbk - 1;
+            const uint32_t *rec = stage + koff + tg * WK;
+            const uint4 *kp = reinterpret_cast<const uint4 *>(kpair + (tg * nbk + qc) * 8);
+            const uint4 sp = kp[0], zp = kp[1];
+            uint4 bq;
+            if (L.use_btab) {
+                bq = btab[u * 64 + lane];
+            } else {
+                const bool ok = p < npair && live_n && j == slot_n;
+                bq = ok ? qt16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
+            }
+            const f16x8 bop = as_h8(bq.x, bq.y, bq.z, bq.w);
+            const bool w4 = qc < nbh;
+            const int base = w4 ? 32 * qc : 128 * nhk + 16 * (qc - nbh);
+            const int stride = w4 ? 4 * nhk : 2 * nlk;
+            const int bit0 = base + ln * stride, bit1 = bit0 + 16 * stride;
+            const uint32_t X0 = __builtin_amdgcn_alignbit(rec[(bit0 >> 5) + 1], rec[bit0 >> 5], bit0 & 31);
+            const uint32_t X1 = __builtin_amdgcn_alignbit(rec[(bit1 >> 5) + 1], rec[bit1 >> 5], bit1 & 31);
+            f16x8 a0, a1;
+            if constexpr (S % 4 == 0) {
+                if (w4) {
+                    a0 = dequant8<true>(X0, sp, zp, km4, kmagic);
+                    a1 = dequant8<true>(X1, sp, zp, km4, kmagic);
+                } else {
+                    a0 = dequant8<false>(X0, sp, zp, km2, kmagic);
+                    a1 = dequant8<false>(X1, sp, zp, km2, kmagic);
+                }
+            } else {
+                a0 = dequant8_any(X0, w4, sp, zp);
+                a1 = dequant8_any(X1, w4, sp, zp);
+            }
+            sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bop, sacc0, 0, 0, 0);
+            sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bop, sacc1, 0, 0, 0);
+        }
+
+        // online softmax of stream ln (rows 4*kb + v of both 16-token halves)
+        const bool sv = live_n && (tb0 + slot_n) < ntg;
+        const float sc[8] = {sacc0[0], sacc0[1], sacc0[2], sacc0[3], sacc1[0], sacc1[1], sacc1[2], sacc1[3]};
+        float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        mloc = sv ? mloc : -INFINITY;
+        const bool need = mloc > m_run + kRescaleSlack;
+        if (__any(need)) {
+            float mm = fmaxf(mloc, __shfl_xor(mloc, 16));
+            mm = fmaxf(mm, __shfl_xor(mm, 32));
+            const bool upd = mm > m_run + kRescaleSlack;
+            const float m_new = upd ? mm : m_run;
+            const float alpha = upd ? exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float av = __shfl(alpha, 4 * kb + v);
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb) oacc[nb][v] *= av;
+            }
+            m_run = m_new;
+        }
+        // weights of streams whose group is past the split never reach a
+        // value MFMA (that slot is skipped), so only the sum is masked
+        const float msafe = m_run == -INFINITY ? 0.0f : m_run;
+        float pr[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(sc[k] - msafe);
+        const float psum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+        l_run += sv ? psum : 0.0f;
+        const uint32_t pp0 = pack_rtz(pr[0], pr[4]), pp1 = pack_rtz(pr[1], pr[5]);
+        const uint32_t pp2 = pack_rtz(pr[2], pr[6]), pp3 = pack_rtz(pr[3], pr[7]);
+
+        // values: one MFMA per slot and 16-channel block on exact codes
+        // (1024 + code in fp16); per-group scale and zero are applied in the
+        // epilogue: sum_t p (code s + z) = s (D - 1024 P) + z P, with
+        // P = sum_t p read from a constant-one column when one is free.
+        f4 dacc[NBV];
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) dacc[nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < S; ++m) {
+            const int tg = tb0 + m;
+            if (tg >= ntg) break;
+            const bool arow = live_n && slot_n == m;
+            const f16x8 aop = arow ? as_h8(pp0, pp1, pp2, pp3) : as_h8(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                uint32_t bp0, bp1, bp2, bp3;
+                if (vq) {
+                    const uint32_t *rec = stage + voff + tg * WV;
+                    const uint32_t X = __builtin_amdgcn_ubfe(rec[vw0[nb]], vs0[nb], vwid[nb]) |
+                                       (__builtin_amdgcn_ubfe(rec[vw1[nb]], vs0[nb], vwid[nb]) << 16);
+                    const int wc = vwc[nb];
+                    bp0 = (X & vcm[nb]) | vbase[nb];
+                    bp1 = ((X >> wc) & vcm[nb]) | vbase[nb];
+                    bp2 = ((X >> (2 * wc)) & vcm[nb]) | vbase[nb];
+                    bp3 = ((X >> (3 * wc)) & vcm[nb]) | vbase[nb];
+                } else {
+                    const uint16_t *r16 =
+                        reinterpret_cast<const uint16_t *>(vg + static_cast<int64_t>(jb + tg) * WV) + vch[nb] * 32;
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(r16 + 4 * kb);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(r16 + 16 + 4 * kb);
+                    bp0 = perm_b32(hi.x, lo.x, 0x05040100u);
+                    bp1 = perm_b32(hi.x, lo.x, 0x07060302u);
+                    bp2 = perm_b32(hi.y, lo.y, 0x05040100u);
+                    bp3 = perm_b32(hi.y, lo.y, 0x07060302u);
+                }
+                dacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, as_h8(bp0, bp1, bp2, bp3), dacc[nb], 0, 0, 0);
+            }
+        }
+        if (vq) {
+            // P per output row 4*kb + v (stream); rows of invalid groups are 0
+            float Pv[4];
+            if (ones_col) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) Pv[v] = __shfl(dacc[NBV - 1][v], (lane & 48) | 15);
+            } else {
+                const h2 q0 = __builtin_bit_cast(h2, pp0), q1 = __builtin_bit_cast(h2, pp1);
+                const h2 q2 = __builtin_bit_cast(h2, pp2), q3 = __builtin_bit_cast(h2, pp3);
+                float P = ((static_cast<float>(q0[0]) + static_cast<float>(q0[1])) +
+                           (static_cast<float>(q1[0]) + static_cast<float>(q1[1]))) +
+                          ((static_cast<float>(q2[0]) + static_cast<float>(q2[1])) +
+                           (static_cast<float>(q3[0]) + static_cast<float>(q3[1])));
+                P += __shfl_xor(P, 16);
+                P += __shfl_xor(P, 32);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) Pv[v] = __shfl(P, 4 * kb + v);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                int tgr = tb0 + row_slot[v];
+                tgr = tgr < ntg ? tgr : ntg - 1;
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb) {
+                    const float2 sz = *reinterpret_cast<const float2 *>(vsz + 2 * (tgr * rv + vch[nb]));
+                    oacc[nb][v] = fmaf(sz.x, dacc[nb][v], fmaf(sz.y, Pv[v], oacc[nb][v]));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) oacc[nb] += dacc[nb];
+        }
+    }
+
+    // ---- 5. per-wave stream results to LDS
+    float lsum = l_run;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    float msum = fmaxf(m_run, __shfl_xor(m_run, 16));
+    msum = fmaxf(msum, __shfl_xor(msum, 32));
+    if (lane < 16) {
+        mst[wv * 16 + lane] = msum;
+        lst[wv * 16 + lane] = lsum;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) {
+        const int c = 16 * nb + ln;
+        if (c < rv) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ost[(wv * 16 + 4 * kb + v) * rv + c] = oacc[nb][v];
+        }
+    }
+
+    // ---- 6. incomplete group (fp32 latents; fp16 value latents live in
+    //         the partial record), as one more stream per head
+    if (do_tail) {
+        const int64_t tb = (hb * 2 + a.sel[i]) * 32;
+        const float *kt = a.k.tail + tb * rk;
+        for (int e = tid; e < g * 32; e += 256) {
+            const int hh = e >> 5, t = e & 31;
+            float acc = -INFINITY;
+            if (t < ntail) {
+                acc = 0.0f;
+                for (int c = 0; c < rk; ++c) acc = fmaf(qt[hh * rk + c], kt[t * rk + c], acc);
+            }
+            ts[e] = acc;
         }
         __syncthreads();
         if (tid < g) {
-            const float bm = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-            const float mo = mst[tid];
-            const float mn = fmaxf(mo, bm);
-            alp[tid] = exp2f(mo - mn);
-            mst[tid] = mn;
+            float mx = -INFINITY;
+            for (int t = 0; t < ntail; ++t) mx = fmaxf(mx, ts[tid * 32 + t]);
+            float l = 0.0f;
+            for (int t = 0; t < 32; ++t) {
+                const float pv = t < ntail ? exp2f(ts[tid * 32 + t] - mx) : 0.0f;
+                tp[tid * 32 + t] = pv;
+                l += pv;
+            }
+            mst[kWaves * 16 + tid] = mx;
+            lst[kWaves * 16 + tid] = l;
         }
         __syncthreads();
-        for (int hh = 0; hh < g; ++hh) {
-            const float pv = valid ? exp2f(sp[hh][tid] - mst[hh]) : 0.0f;
-            if (valid) sp[hh][tid] = pv;
-            const float sum = wave_sum(pv);
-            if (lane == 0) red[wv][hh] = sum;
-        }
-        __syncthreads();
-        if (tid < g) lst[tid] = lst[tid] * alp[tid] + (red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]);
-        // values
         for (int e = tid; e < g * rv; e += 256) {
             const int hh = e / rv, c = e - (e / rv) * rv;
-            float acc = ot[hh][c] * alp[hh];
-            if (!tb) {
-                for (int jj = p0 >> 5; jj < (p1 + 31) >> 5; ++jj) {
-                    const float *pr = &sp[hh][32 * jj - p0];
-                    const uint32_t *rec = vrec0 + static_cast<int64_t>(jj) * a.v.words;
-                    if (a.v.fp16_latents) {
-                        const uint16_t *r16 = reinterpret_cast<const uint16_t *>(rec) + c * 32;
-                        for (int t = 0; t < 32; ++t) acc = fmaf(pr[t], h2f(r16[t]), acc);
-                    } else {
-                        const uint32_t mw = rec[4 * nhv + 2 * (rv - nhv) + c];
-                        float spc = 0.0f, sps = 0.0f;
-                        if (c < nhv) {
-                            for (int t = 0; t < 32; ++t) {
-                                const uint32_t code = (rec[4 * c + (t >> 3)] >> (4 * (t & 7))) & 15u;
-                                spc = fmaf(pr[t], static_cast<float>(code), spc);
-                                sps += pr[t];
-                            }
-                        } else {
-                            const int cl = c - nhv;
-                            for (int t = 0; t < 32; ++t) {
-                                const uint32_t code = (rec[4 * nhv + 2 * cl + (t >> 4)] >> (2 * (t & 15))) & 3u;
-                                spc = fmaf(pr[t], static_cast<float>(code), spc);
-                                sps += pr[t];
-                            }
-                        }
-                        acc = fmaf(h2f(mw), spc, fmaf(h2f(mw >> 16), sps, acc));
-                    }
-                }
+            float acc = 0.0f;
+            if (vq) {
+                const float *vt = a.v.tail + tb * rv;
+                for (int t = 0; t < ntail; ++t) acc = fmaf(tp[hh * 32 + t], vt[t * rv + c], acc);
             } else {
-                const int nt = p1 - p0;
-                if (a.v.fp16_latents) {
-                    const uint16_t *r16 = reinterpret_cast<const uint16_t *>(
-                        vrec0 + static_cast<int64_t>(nfull) * a.v.words) + c * 32;
-                    for (int t = 0; t < nt; ++t) acc = fmaf(sp[hh][t], h2f(r16[t]), acc);
-                } else {
-                    for (int t = 0; t < nt; ++t) acc = fmaf(sp[hh][t], vtail[t * rv + c], acc);
-                }
+                const uint16_t *r16 =
+                    reinterpret_cast<const uint16_t *>(vg + static_cast<int64_t>(nfull) * WV) + c * 32;
+                for (int t = 0; t < ntail; ++t) acc = fmaf(tp[hh * 32 + t], h2f(r16[t]), acc);
             }
-            ot[hh][c] = acc;
+            ost[(kWaves * 16 + hh) * rv + c] = acc;
         }
-        __syncthreads();
     }
+    __syncthreads();
 
-    // partials: [i][q head][split][m, l, o_0 .. o_{rv-1}]
+    // ---- 7. merge the streams of each head; write the split's partial.
+    //         Stream index sidx: waves' streams w*16 + slot*g + head, then the
+    //         tail stream kWaves*16 + head.
+    const int nsw = kWaves * S + (do_tail ? 1 : 0);   // streams per head
+    float *wts = ts;                                   // reuse: [g][<= 4*16 + 1]
+    if (tid < g) {
+        float M = -INFINITY;
+        for (int k = 0; k < nsw; ++k) {
+            const int sidx = k < kWaves * S ? (k / S) * 16 + (k % S) * g + tid : kWaves * 16 + tid;
+            M = fmaxf(M, mst[sidx]);
+        }
+        hm[tid] = M;
+    }
+    __syncthreads();
+    for (int e = tid; e < g * nsw; e += 256) {
+        const int hh = e / nsw, k = e - (e / nsw) * nsw;
+        const int sidx = k < kWaves * S ? (k / S) * 16 + (k % S) * g + hh : kWaves * 16 + hh;
+        const float ms = mst[sidx];
+        wts[e] = ms == -INFINITY ? 0.0f : exp2f(ms - hm[hh]);
+    }
+    __syncthreads();
     for (int e = tid; e < g * (rv + 2); e += 256) {
         const int hh = e / (rv + 2), k = e - (e / (rv + 2)) * (rv + 2);
-        float *part = a.partial +
-            ((static_cast<int64_t>(i) * a.Hq + h * g + hh) * kMaxSplits + s) * (rv + 2);
-        part[k] = k == 0 ? mst[hh] : (k == 1 ? lst[hh] : ot[hh][k - 2]);
+        const float *wrow = wts + hh * nsw;
+        float val;
+        if (k == 0) {
+            val = hm[hh];
+        } else {
+            const int c = k - 2;
+            float acc = 0.0f;
+#pragma unroll 4
+            for (int kk = 0; kk < nsw; ++kk) {
+                const int sidx = kk < kWaves * S ? (kk / S) * 16 + (kk % S) * g + hh : kWaves * 16 + hh;
+                acc = fmaf(wrow[kk], k == 1 ? lst[sidx] : ost[sidx * rv + c], acc);
+            }
+            val = acc;
+        }
+        a.partial[((static_cast<int64_t>(i) * a.Hq + h * g + hh) * kMaxSplits + s) * (rv + 2) + k] = val;
+    }
+
+}
+
+// One wave per (call row, query head): merge the splits by log-sum-exp and
+// project back with the value basis, o = V_V (o_lat / l) + mu_V, in fp16.
+// Lane sp holds split sp (and sp + 64); every partial is read once, all
+// loads of a wave are independent.
+__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int task = blockIdx.x * 4 + wv;
+    const bool active = task < a.B * a.Hq;
+    __shared__ float ov[4][kHeadDim];
+    const int i = active ? task / a.Hq : 0, qh = active ? task - (task / a.Hq) * a.Hq : 0;
+    const int h = qh / a.gqa, grp = h / a.hpg, ns = a.nsplit[i], rv = a.v.r;
+    const float *part = a.partial + (static_cast<int64_t>(i) * a.Hq + qh) * kMaxSplits * (rv + 2);
+    const bool s0 = lane < ns, s1 = lane + 64 < ns;
+    const float m0 = s0 ? part[lane * (rv + 2)] : -INFINITY;
+    const float m1 = s1 ? part[(lane + 64) * (rv + 2)] : -INFINITY;
+    const float l0 = s0 ? part[lane * (rv + 2) + 1] : 0.0f;
+    const float l1 = s1 ? part[(lane + 64) * (rv + 2) + 1] : 0.0f;
+    const float M = wave_max(fmaxf(m0, m1));
+    const float w0 = s0 ? exp2f(m0 - M) : 0.0f, w1 = s1 ? exp2f(m1 - M) : 0.0f;
+    const float l = wave_sum(fmaf(w0, l0, w1 * l1));
+    const float inv_l = 1.0f / l;
+    for (int c0 = 0; c0 < rv; c0 += 4) {
+        float acc[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const int c = c0 + cc;
+            float t = 0.0f;
+            if (c < rv) {
+                if (s0) t = w0 * part[lane * (rv + 2) + 2 + c];
+                if (s1) t = fmaf(w1, part[(lane + 64) * (rv + 2) + 2 + c], t);
+            }
+            acc[cc] = t;
+        }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) acc[cc] = wave_sum(acc[cc]);
+        if (lane < 4 && c0 + lane < rv && active)
+            ov[wv][c0 + lane] = (lane == 0 ? acc[0] : lane == 1 ? acc[1] : lane == 2 ? acc[2] : acc[3]) * inv_l;
+    }
+    __syncthreads();
+    if (!active) return;
+    const float *bv = a.v.basis + static_cast<int64_t>(grp) * kHeadDim * rv;
+    for (int d = lane; d < kHeadDim; d += 64) {
+        float o = a.v.mu[grp * kHeadDim + d];
+        for (int c = 0; c < rv; ++c) o = fmaf(bv[d * rv + c], ov[wv][c], o);
+        a.out[(static_cast<int64_t>(i) * a.Hq + qh) * kHeadDim + d] = static_cast<uint16_t>(f2h_bits(o));
     }
 }
 
-__global__ __launch_bounds__(128) void combine_kernel(AttendArgs a) {
-    const int i = blockIdx.x / a.Hq, qh = blockIdx.x - (blockIdx.x / a.Hq) * a.Hq;
-    const int h = qh / a.gqa, grp = h / a.hpg, ns = a.nsplit[i], rv = a.v.r;
-    const int tid = threadIdx.x;
-    const float *part = a.partial + (static_cast<int64_t>(i) * a.Hq + qh) * kMaxSplits * (rv + 2);
-    __shared__ float wsp[kMaxSplits];
-    __shared__ float ov[kHeadDim];
-    __shared__ float ltot;
-    if (tid == 0) {
-        float m = -INFINITY;
-        for (int s = 0; s < ns; ++s) m = fmaxf(m, part[s * (rv + 2)]);
-        float l = 0.0f;
-        for (int s = 0; s < ns; ++s) {
-            const float w = exp2f(part[s * (rv + 2)] - m);
-            wsp[s] = w;
-            l = fmaf(w, part[s * (rv + 2) + 1], l);
-        }
-        ltot = l;
-    }
-    __syncthreads();
-    for (int c = tid; c < rv; c += 128) {
-        float acc = 0.0f;
-        for (int s = 0; s < ns; ++s) acc = fmaf(wsp[s], part[s * (rv + 2) + 2 + c], acc);
-        ov[c] = acc / ltot;
-    }
-    __syncthreads();
-    const float *bv = a.v.basis + static_cast<int64_t>(grp) * kHeadDim * rv;
-    float o = a.v.mu[grp * kHeadDim + tid];
-    for (int c = 0; c < rv; ++c) o = fmaf(bv[tid * rv + c], ov[c], o);
-    a.out[(static_cast<int64_t>(i) * a.Hq + qh) * kHeadDim + tid] = static_cast<uint16_t>(f2h_bits(o));
+__global__ __launch_bounds__(256) void basis_t16_kernel(const float *src, uint16_t *dst, int G, int r) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t n = static_cast<int64_t>(G) * r * kHeadDim;
+    if (e >= n) return;
+    const int d = static_cast<int>(e % kHeadDim);
+    const int64_t gc = e / kHeadDim;
+    const int c = static_cast<int>(gc % r), g = static_cast<int>(gc / r);
+    dst[e] = static_cast<uint16_t>(f2h_bits(src[(static_cast<int64_t>(g) * kHeadDim + d) * r + c]));
 }
 
 }  // namespace
@@ -527,13 +968,51 @@ hipError_t launch_encode(const EncodeArgs &a, int max_touched, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_attend(const AttendArgs &a, int n_work, hipStream_t s) {
-    hipLaunchKernelGGL(attend_kernel, dim3(n_work), dim3(256), 0, s, a);
+size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int chunk, int words_k, int words_v, bool vq) {
+    return static_cast<size_t>(attend_lds(gqa, r_k, n_hi_k, r_v, chunk, words_k, words_v, vq).total);
+}
+
+template <int S, int NBV>
+static hipError_t launch_attend_t(const AttendArgs &a, int n_work, size_t lds_bytes, hipStream_t s) {
+    static bool configured = false;
+    if (!configured) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<S, NBV>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    hipLaunchKernelGGL((attend_kernel<S, NBV>), dim3(n_work), dim3(256), lds_bytes, s, a);
+    return hipGetLastError();
+}
+
+template <int S>
+static hipError_t launch_attend_s(const AttendArgs &a, int n_work, size_t lds_bytes, hipStream_t s) {
+    const int nbv = (a.v.r + 15) / 16;
+    if (nbv <= 1) return launch_attend_t<S, 1>(a, n_work, lds_bytes, s);
+    if (nbv <= 2) return launch_attend_t<S, 2>(a, n_work, lds_bytes, s);
+    if (nbv <= 4) return launch_attend_t<S, 4>(a, n_work, lds_bytes, s);
+    return launch_attend_t<S, 8>(a, n_work, lds_bytes, s);
+}
+
+hipError_t launch_attend(const AttendArgs &a, int n_work, size_t lds_bytes, hipStream_t s) {
+    switch (16 / a.gqa) {
+        case 16: return launch_attend_s<16>(a, n_work, lds_bytes, s);
+        case 8: return launch_attend_s<8>(a, n_work, lds_bytes, s);
+        case 5: return launch_attend_s<5>(a, n_work, lds_bytes, s);
+        case 4: return launch_attend_s<4>(a, n_work, lds_bytes, s);
+        case 3: return launch_attend_s<3>(a, n_work, lds_bytes, s);
+        default: return launch_attend_s<2>(a, n_work, lds_bytes, s);
+    }
+}
+
+hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, hipStream_t s) {
+    const int64_t n = static_cast<int64_t>(G) * r * kHeadDim;
+    hipLaunchKernelGGL(basis_t16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, src, dst, G, r);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel, dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
