@@ -50,7 +50,7 @@ enum {
  * palu_n_head_groups, palu_hi_bit, palu_lo_bit, palu_hi_fraction,
  * palu_group_size, palu_quantize_values). */
 typedef struct palu_config {
-    int32_t head_dim;          /* D; the kernels support 16..128, multiple of 16 */
+    int32_t head_dim;          /* D; the kernels are built for D = 128 only      */
     int32_t n_kv_heads;        /* H: heads stored by the cache                     */
     int32_t n_q_heads;         /* query heads, a multiple of n_kv_heads; query head
                                   i attends with kv head i / (n_q_heads/n_kv_heads) */
@@ -64,6 +64,11 @@ typedef struct palu_config {
     int32_t group_size;        /* tokens per quantisation group; only 32          */
     int32_t quantize_values;   /* 1: V mixed-bit like K; 0: V as fp16 latents     */
     int32_t max_rank;          /* storage is sized for ranks up to this (0 = D)   */
+    int32_t split_groups;      /* decode: complete token groups per split (work of
+                                  one workgroup); 0 = automatic.  Raised to fit the
+                                  split limit (128 splits per sequence and head);
+                                  a value whose LDS need exceeds 160 KiB makes
+                                  palu_decode_attend fail with UNSUPPORTED.      */
 } palu_config;
 
 /* Fills the page's defaults (rank 0 = energy rule, threshold 0.90, G = 4,

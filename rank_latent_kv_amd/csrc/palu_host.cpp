@@ -98,6 +98,7 @@ int validate_config(const palu_config *c) {
         return fail(PALU_ERR_INVALID_ARG, "hi_fraction must be in [0, 1]");
     if (c->max_rank < 0 || c->max_rank > c->head_dim)
         return fail(PALU_ERR_INVALID_ARG, "max_rank must be in [0, head_dim]");
+    if (c->split_groups < 0) return fail(PALU_ERR_INVALID_ARG, "split_groups must be >= 0 (0 = automatic)");
     if (c->quantize_values != 0 && c->quantize_values != 1)
         return fail(PALU_ERR_INVALID_ARG, "quantize_values must be 0 or 1");
     if (c->head_dim != kHeadDim)
@@ -161,6 +162,7 @@ PALU_API int palu_config_default(palu_config *cfg, int32_t head_dim, int32_t n_k
     cfg->group_size = 32;
     cfg->quantize_values = 1;
     cfg->max_rank = 0;
+    cfg->split_groups = 0;
     return PALU_OK;
 }
 
@@ -516,9 +518,14 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
                                     aa.v.words, vq);
         };
         auto round_up = [](int64_t v, int64_t m) { return (v + m - 1) / m * m; };
-        int64_t chunk = round_up(std::max<int64_t>(1, (units + kAttendTargetGroups - 1) / kAttendTargetGroups), per_iter);
-        while (chunk > 1 && lds_for(chunk) > kAttendLdsCap)
-            chunk = chunk > per_iter ? chunk - per_iter : chunk - 1;
+        int64_t chunk;
+        if (c->cfg.split_groups > 0) {
+            chunk = c->cfg.split_groups;
+        } else {
+            chunk = round_up(std::max<int64_t>(1, (units + kAttendTargetGroups - 1) / kAttendTargetGroups), per_iter);
+            while (chunk > 1 && lds_for(chunk) > kAttendLdsCap)
+                chunk = chunk > per_iter ? chunk - per_iter : chunk - 1;
+        }
         chunk = std::max<int64_t>(chunk, (max_full + kMaxSplits - 1) / kMaxSplits);
         const size_t lds = lds_for(chunk);
         if (lds > kAttendLdsMax)

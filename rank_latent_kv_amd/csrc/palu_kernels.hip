@@ -705,7 +705,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             m_run = m_new;
         }
         // weights of streams whose group is past the split never reach a
-        // value MFMA (that slot is skipped), so only the sum is masked
+        // value MFMA (that slot is skipped), so only the sums (l and P) are
+        // masked
         const float msafe = m_run == -INFINITY ? 0.0f : m_run;
         float pr[8];
 #pragma unroll
@@ -766,6 +767,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                            (static_cast<float>(q1[0]) + static_cast<float>(q1[1]))) +
                           ((static_cast<float>(q2[0]) + static_cast<float>(q2[1])) +
                            (static_cast<float>(q3[0]) + static_cast<float>(q3[1])));
+                P = sv ? P : 0.0f;        // weights of masked streams are not zeroed
                 P += __shfl_xor(P, 16);
                 P += __shfl_xor(P, 32);
 #pragma unroll

@@ -41,7 +41,8 @@ class palu_config(ctypes.Structure):
                 ("rank", ctypes.c_int32), ("energy_threshold", ctypes.c_float),
                 ("hi_bit", ctypes.c_int32), ("lo_bit", ctypes.c_int32),
                 ("hi_fraction", ctypes.c_float), ("group_size", ctypes.c_int32),
-                ("quantize_values", ctypes.c_int32), ("max_rank", ctypes.c_int32)]
+                ("quantize_values", ctypes.c_int32), ("max_rank", ctypes.c_int32),
+                ("split_groups", ctypes.c_int32)]
 
 
 class palu_stats(ctypes.Structure):
@@ -223,7 +224,7 @@ class LatentKVCache:
                  max_batch: int, max_seq_len: int, rank: int = 0, energy_threshold: float = 0.90,
                  hi_bit: int = 4, lo_bit: int = 2, hi_fraction: float = 0.25,
                  group_size: int = 32, quantize_values: bool = True, max_rank: int = 0,
-                 device=None):
+                 split_groups: int = 0, device=None):
         import torch
         self.torch = torch
         cfg = palu_config_default(head_dim, n_kv_heads, n_q_heads)
@@ -234,6 +235,7 @@ class LatentKVCache:
         cfg.group_size = group_size
         cfg.quantize_values = 1 if quantize_values else 0
         cfg.max_rank = max_rank
+        cfg.split_groups = split_groups
         self.cfg = cfg
         self.D, self.H, self.Hq, self.G = head_dim, n_kv_heads, n_q_heads, n_head_groups
         self.max_batch, self.max_seq_len = max_batch, max_seq_len

@@ -28,13 +28,13 @@ def torch():
     return _t
 
 
-def _cache(torch, w, max_seq_len, max_batch=None, rank=None, max_rank=0):
+def _cache(torch, w, max_seq_len, max_batch=None, rank=None, max_rank=0, split_groups=0):
     from rank_latent_kv_amd.palu import LatentKVCache
     return LatentKVCache(w.head_dim, w.n_kv_heads, w.n_q_heads, w.n_head_groups,
                          max_batch or w.batch, max_seq_len,
                          rank=(w.rank or 0) if rank is None else rank,
                          energy_threshold=w.energy, quantize_values=w.quantize_values,
-                         max_rank=max_rank)
+                         max_rank=max_rank, split_groups=split_groups)
 
 
 def _dev(torch, a):
@@ -91,7 +91,7 @@ def _check_attention(got, ref, what=""):
     return err.max()
 
 
-def _run_small(torch, w, steps=None, chunks=None, check_every=1, lens=None):
+def _run_small(torch, w, steps=None, chunks=None, check_every=1, lens=None, split_groups=0):
     """Oracle-fit basis installed on the GPU; prefill + decode steps; codes
     bit-exact after the prefill and the last step, attention within
     tolerance after every checked step."""
@@ -104,7 +104,7 @@ def _run_small(torch, w, steps=None, chunks=None, check_every=1, lens=None):
     S = int(lens.max())
     fk = oracle.fit(k_all[:, :, :S], lens, w.n_head_groups, rank=w.rank or 0, tau=w.energy)
     fv = oracle.fit(v_all[:, :, :S], lens, w.n_head_groups, rank=w.rank or 0, tau=w.energy)
-    cache = _cache(torch, w, total)
+    cache = _cache(torch, w, total, split_groups=split_groups)
     cache.set_basis(0, fk.bases(), fk.mu)
     cache.set_basis(1, fv.bases(), fv.mu)
     layer = oracle.OracleLayer(w.head_dim, w.n_q_heads, w.n_kv_heads, w.n_head_groups, fk, fv,
@@ -181,6 +181,22 @@ def test_rank_extremes(torch, rank):
     w = synth.small_workload(batch=1, n_q_heads=2, n_kv_heads=2, n_head_groups=1, prefill=64,
                              steps=2, rank=rank, seed=rank)
     _run_small(torch, w)
+
+
+@pytest.mark.parametrize("gqa,rank,vq", [(1, 32, True), (2, 32, True), (3, 32, True), (4, 32, True),
+                                         (8, 32, True), (2, 20, True), (4, 20, True), (8, 20, True),
+                                         (4, 24, False)])
+def test_multi_iteration_splits(torch, gqa, rank, vq):
+    # a split covers more token groups than one pass of the workgroup's four
+    # waves, with a partial last pass; lengths leave a partial last split and a
+    # tail.  rank 32 takes the value path without a free constant-one column.
+    per_pass = 4 * (16 // gqa)
+    split = per_pass + 7
+    n0 = 32 * (2 * split + per_pass // 2) + 13
+    w = synth.small_workload(batch=2, n_q_heads=2 * gqa, n_kv_heads=2, n_head_groups=1,
+                             prefill=n0, steps=2, rank=rank, quantize_values=vq,
+                             seed=300 + 10 * gqa + rank)
+    _run_small(torch, w, lens=[n0, 32 * split + 5], split_groups=split)
 
 
 def test_append_order_invariance(torch):
