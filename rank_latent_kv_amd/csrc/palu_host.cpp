@@ -502,15 +502,16 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
         int max_full = 0;
         for (int i = 0; i < nb; ++i) {
             const int slot = seq_ids ? seq_ids[b0 + i] : b0 + i;
-            aa.slot[i] = slot;
-            aa.len[i] = c->len[slot];
-            aa.sel[i] = c->sel[slot];
+            aa.row[i].slot = slot;
+            aa.row[i].len = c->len[slot];
+            aa.row[i].sel = c->sel[slot];
             const int nfull = c->len[slot] / kTokGroup;
             units += static_cast<int64_t>(c->H) * std::max(1, nfull);
             max_full = std::max(max_full, nfull);
         }
-        // split size: a multiple of the groups one workgroup iteration
-        // covers, large enough for the split limit, small enough for LDS
+        // split size: a multiple of the groups one workgroup pass covers,
+        // large enough for the split limit, small enough for LDS; the same
+        // for every row, so a row has ceil(groups / chunk) splits
         const int per_iter = 4 * (16 / c->gqa);
         const bool vq = !aa.v.fp16_latents;
         auto lds_for = [&](int64_t ch) {
@@ -527,18 +528,25 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
                 chunk = chunk > per_iter ? chunk - per_iter : chunk - 1;
         }
         chunk = std::max<int64_t>(chunk, (max_full + kMaxSplits - 1) / kMaxSplits);
+        int nsplit_max = 1;
+        for (int i = 0; i < nb; ++i) {
+            const int nfull = aa.row[i].len / kTokGroup;
+            aa.row[i].nsplit = std::max(1, static_cast<int>((nfull + chunk - 1) / chunk));
+            nsplit_max = std::max(nsplit_max, aa.row[i].nsplit);
+        }
         const size_t lds = lds_for(chunk);
         if (lds > kAttendLdsMax)
             return fail(PALU_ERR_UNSUPPORTED, "sequence too long for the split limit at this rank");
         aa.chunk = static_cast<int>(chunk);
-        aa.stage_words = 0;
-        aa.work_prefix[0] = 0;
-        for (int i = 0; i < nb; ++i) {
-            const int nfull = aa.len[i] / kTokGroup;
-            aa.nsplit[i] = std::max(1, static_cast<int>((nfull + chunk - 1) / chunk));
-            aa.work_prefix[i + 1] = aa.work_prefix[i] + c->H * aa.nsplit[i];
+        aa.nsplit_max = nsplit_max;
+        {
+            const int nbk = (aa.k.n_hi + 7) / 8 + (aa.k.r - aa.k.n_hi + 7) / 8;
+            volatile float one = 1.0f;   // IEEE fp32 divisions, not folded to other precisions
+            aa.inv_rv = one / static_cast<float>(aa.v.r);
+            aa.inv_nbk4 = one / static_cast<float>(4 * nbk);
+            aa.inv_nbk8 = one / static_cast<float>(8 * nbk);
         }
-        hipError_t e = launch_attend(aa, aa.work_prefix[nb], lds, s);
+        hipError_t e = launch_attend(aa, lds, s);
         if (e != hipSuccess) return hip_fail(e, "attend launch");
         e = launch_combine(aa, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");

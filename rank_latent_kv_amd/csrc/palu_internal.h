@@ -61,6 +61,12 @@ struct EncodeArgs {
     int sel_new[kMaxCallSeqs];
 };
 
+// One decode row: cache slot, stored length, live tail buffer, and its
+// number of splits (16 bytes, one load).
+struct AttendRow {
+    int slot, len, sel, nsplit;
+};
+
 struct AttendArgs {
     const uint16_t *q;        // fp16 [B][Hq][D]
     uint16_t *out;            // fp16 [B][Hq][D]
@@ -68,13 +74,12 @@ struct AttendArgs {
     TensorDev k, v;
     int B, Hq, Hkv, gqa, hpg;
     int chunk;                // complete token groups per split
+    int nsplit_max;           // grid x; splits s >= row.nsplit exit at once
     float qscale;             // softmax scale * log2(e)
-    int stage_words;          // LDS words reserved for staged records
-    int slot[kMaxCallSeqs];
-    int len[kMaxCallSeqs];
-    int sel[kMaxCallSeqs];
-    int nsplit[kMaxCallSeqs];
-    int work_prefix[kMaxCallSeqs + 1];  // workgroups before sequence i
+    // correctly rounded fp32 reciprocals of table index divisors: r_v, and
+    // 4 and 8 times the key channel blocks
+    float inv_rv, inv_nbk4, inv_nbk8;
+    AttendRow row[kMaxCallSeqs];
 };
 
 // LDS bytes of one attend workgroup for a split of `chunk` token groups.
@@ -84,7 +89,8 @@ size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int chunk, int wo
 hipError_t launch_gram(const GramArgs &a, hipStream_t s);
 hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &a, int max_touched, hipStream_t s);
-hipError_t launch_attend(const AttendArgs &a, int n_work, size_t lds_bytes, hipStream_t s);
+// Grid (nsplit_max, Hkv, B): one workgroup per (split, kv head, row).
+hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s);
 // fp16 channel-major copy of a basis: dst[g][c][d] = fp16(src[g][d][c]).
 hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, hipStream_t s);

@@ -35,14 +35,40 @@ __device__ __forceinline__ uint32_t f2h_bits(float f) {
     return static_cast<uint32_t>(__half_as_ushort(__float2half_rn(f)));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
+// Lane exchange inside rows of 16 lanes through DPP (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E;            // quad_perm [1,0,3,2], [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141, kDppMirror = 0x140;  // lane i <- 7-i (per 8), 15-i
+
+// Every lane of a 16-lane row gets the row's max / sum: pairs, quads, then
+// the mirrored halves of 8 and of 16 lanes.
+__device__ __forceinline__ float row_max(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    return fmaxf(v, dpp<kDppMirror>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    return v + dpp<kDppMirror>(v);
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
+// Whole-wave max / sum, the same (wave-uniform) value in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+    v = row_max(v);
+    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+    v = row_sum(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 // ---------------------------------------------------------------- Gram ----
@@ -363,10 +389,20 @@ __host__ __device__ inline AttendLds attend_lds(int g, int rk, int nhk, int rv, 
     L.btab = lds_take(o, L.use_btab ? L.nub * 64 * 16 : 0);
     L.kpair = lds_take(o, chunk * L.nbk * 8 * 4);
     L.vpair = lds_take(o, vq ? chunk * rv * 2 * 4 : 0);
-    L.stage = lds_take(o, (chunk * (wk + (vq ? wv : 0)) + 16) * 4);
+    // staged records of the split (+ alignment slack) and the tail latents
+    L.stage = lds_take(o, (chunk * (wk + (vq ? wv : 0)) + 16 + 32 * rk + (vq ? 32 * rv : 16 * rv)) * 4);
     L.total = o;
     return L;
 }
+
+// floor(e / d) for 0 <= e < 2^21 and d >= 1 from a correctly rounded fp32
+// reciprocal: (e + 1/2) / d lies at least 1/(2d) away from an integer, and
+// the two roundings perturb it by at most (e + 1/2) / d * 2^-23 < 1/(2d).
+struct FastDiv {
+    float inv;   // the correctly rounded fp32 1 / d, computed on the host
+    __device__ explicit FastDiv(float inv_d) : inv(inv_d) {}
+    __device__ int quo(int e) const { return static_cast<int>((static_cast<float>(e) + 0.5f) * inv); }
+};
 
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);
@@ -379,7 +415,7 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t magic, uint32_t spair,
                                                                    __builtin_bit_cast(h2, zpair)));
 }
 
-__device__ __forceinline__ uint32_t pack_half2(float a, float b) {
+[[maybe_unused]] __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
     const h2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
     return __builtin_bit_cast(uint32_t, v);
 }
@@ -427,30 +463,34 @@ __device__ __forceinline__ f16x8 dequant8_any(uint32_t X, bool w4, const uint4 &
 }
 
 // Workgroup = (call row i, kv head h, split s); see the section comment.
-// S = 16 / gqa token groups (slots) per wave iteration, NBV = value-channel
-// blocks of 16.
-template <int S, int NBV>
+// G = query heads per kv head, NBV = value-channel blocks of 16.
+template <int G, int NBV>
 __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
+    constexpr int g = G, S = 16 / G, NS = S * G;
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int ln = lane & 15, kb = lane >> 4;
 
-    // ---- work item
-    const int wid = blockIdx.x;
-    int i = 0;
-    while (i + 1 < a.B && a.work_prefix[i + 1] <= wid) ++i;
-    const int rem = wid - a.work_prefix[i];
-    const int ns = a.nsplit[i];
-    const int h = rem / ns, s = rem - (rem / ns) * ns;
-    const int slot = a.slot[i], len = a.len[i];
+    // ---- work item: grid (split, kv head, row); one 16-byte row descriptor
+    const int s = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+    const AttendRow rw = a.row[i];
+    // Pin the kernel arguments the prologue needs before the first branch so
+    // their scalar loads are issued together (one round trip instead of a
+    // chain of dependent ones).
+    asm volatile("" ::"s"(a.k.records), "s"(a.v.records), "s"(a.k.tail), "s"(a.v.tail), "s"(a.k.basis_t16),
+                 "s"(a.q), "s"(a.k.head_stride), "s"(a.v.head_stride), "s"(a.k.r), "s"(a.k.n_hi), "s"(a.k.words),
+                 "s"(a.v.r), "s"(a.v.n_hi), "s"(a.v.words), "s"(a.v.fp16_latents), "s"(a.chunk), "s"(a.hpg),
+                 "s"(a.Hq), "s"(a.Hkv), "s"(a.qscale), "s"(rw.slot), "s"(rw.len), "s"(rw.sel), "s"(rw.nsplit));
+    const int ns = rw.nsplit;
+    if (s >= ns) return;                          // whole workgroup: no barrier reached
+    const int slot = rw.slot, len = rw.len;
     const int nfull = len >> 5, ntail = len & 31;
     const int jb = s * a.chunk;
     const int je = jb + a.chunk < nfull ? jb + a.chunk : nfull;
     const int ntg = je > jb ? je - jb : 0;
     const bool do_tail = (s == ns - 1) && ntail > 0;
-    const int g = a.gqa, grp = h / a.hpg;
-    const int NS = S * g;
+    const int grp = h / a.hpg;
     const int rk = a.k.r, nhk = a.k.n_hi, nlk = rk - nhk;
     const int nbh = (nhk + 7) >> 3;
     const int rv = a.v.r, nhv = a.v.n_hi;
@@ -468,7 +508,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     float *lst = reinterpret_cast<float *>(lds + L.lst);
     float *ost = reinterpret_cast<float *>(lds + L.ost);
     float *tp = reinterpret_cast<float *>(lds + L.tp);
-    float *hm = reinterpret_cast<float *>(lds + L.hm);
     uint4 *btab = reinterpret_cast<uint4 *>(lds + L.btab);
     uint32_t *kpair = reinterpret_cast<uint32_t *>(lds + L.kpair);
     uint32_t *vpair = reinterpret_cast<uint32_t *>(lds + L.vpair);
@@ -478,87 +517,150 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     const uint32_t *kg = a.k.records + hb * a.k.head_stride;
     const uint32_t *vg = a.v.records + hb * a.v.head_stride;
 
-    // ---- 1. stage the split's packed records in LDS (16-byte loads, all
-    //         issued before the first store)
+    // ---- 1. issue every global load the prologue needs before waiting on
+    //         any: the query rows and key-basis blocks of the absorbed query,
+    //         then the split's packed records and the tail latents (copied
+    //         to LDS in 16-byte pieces; the first 8 pieces per thread are in
+    //         flight while the query MFMA waits only on its own operands)
+    // only the waves that own a 16-channel block of qt load the query and
+    // their basis block (wave-uniform branches)
+    const int nbc = (rk + 15) >> 4;              // 16-channel blocks of qt (<= 8)
+    const bool own0 = wv < nbc, own1 = wv + kWaves < nbc;
+    const int qrow = i * a.Hq + h * g;
+    uint4 qa[4], bb[2][4];
+    if (own0) {
+        const uint16_t *qsrc = a.q + static_cast<int64_t>(qrow + (ln < g ? ln : 0)) * kHeadDim + 8 * kb;
+        // rows ln >= g repeat a valid query; their MFMA output rows are never stored
+#pragma unroll
+        for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const uint4 *>(qsrc + 32 * st);
+        const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * rk * kHeadDim;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            if (x == 1 && !own1) break;
+            int c = 16 * (wv + kWaves * x) + ln;
+            c = c < rk ? c : rk - 1;              // clamped rows are never stored
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                bb[x][st] = *reinterpret_cast<const uint4 *>(bt + static_cast<int64_t>(c) * kHeadDim + 32 * st + 8 * kb);
+        }
+    }
+
     const int64_t k_a = (static_cast<int64_t>(jb) * WK) & ~3LL;
     const int k_words = ntg ? static_cast<int>((static_cast<int64_t>(je) * WK - k_a + 3) & ~3LL) : 0;
     const int64_t v_a = (static_cast<int64_t>(jb) * WV) & ~3LL;
     const int v_words = (vq && ntg) ? static_cast<int>((static_cast<int64_t>(je) * WV - v_a + 3) & ~3LL) : 0;
     const int koff = static_cast<int>(static_cast<int64_t>(jb) * WK - k_a);          // record 0 of the split
     const int voff = k_words + static_cast<int>(static_cast<int64_t>(jb) * WV - v_a);
-    {
-        const int nk4 = k_words >> 2, nv4 = v_words >> 2, n4 = nk4 + nv4;
-        const uint4 *ksrc = reinterpret_cast<const uint4 *>(kg + k_a);
-        const uint4 *vsrc = reinterpret_cast<const uint4 *>(vg + v_a);
-        uint4 *dst = reinterpret_cast<uint4 *>(stage);
-        for (int base = 0; base < n4; base += 256 * 8) {
-            uint4 buf[8];
+    // tail latents of the last split: fp32 [32][r] buffers (only the filled
+    // rows, rounded up to 16 bytes), or the fp16 value record of group nfull
+    const int64_t tsel = (hb * 2 + rw.sel) * kTokGroup;
+    const int tk_words = do_tail ? min((ntail * rk + 3) & ~3, kTokGroup * rk) : 0;
+    const int tv_words = do_tail ? (vq ? min((ntail * rv + 3) & ~3, kTokGroup * rv) : 16 * rv) : 0;
+    const int tk_off = k_words + v_words, tv_off = tk_off + tk_words;
+    const int nk4 = k_words >> 2, nv4 = v_words >> 2, ntk4 = tk_words >> 2, n4 = nk4 + nv4 + ntk4 + (tv_words >> 2);
+    const u4v *ksrc = reinterpret_cast<const u4v *>(kg + k_a);
+    const u4v *vsrc = reinterpret_cast<const u4v *>(vg + v_a);
+    const u4v *tksrc = reinterpret_cast<const u4v *>(a.k.tail + tsel * rk);
+    const u4v *tvsrc = vq ? reinterpret_cast<const u4v *>(a.v.tail + tsel * rv)
+                          : reinterpret_cast<const u4v *>(vg + static_cast<int64_t>(nfull) * WV);
+    // source of 16-byte piece e (selects only, so the loads stay straight-line)
+    auto piece = [&](int e) -> const u4v * {
+        const u4v *p0 = e < nk4 ? ksrc + e : vsrc + (e - nk4);
+        const u4v *p1 = e < nk4 + nv4 + ntk4 ? tksrc + (e - nk4 - nv4) : tvsrc + (e - nk4 - nv4 - ntk4);
+        const u4v *pe = e < nk4 + nv4 ? p0 : p1;
+        return e < n4 ? pe : reinterpret_cast<const u4v *>(a.k.records);   // unused slot: a valid address
+    };
+    u4v buf[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int e = base + u * 256 + tid;
-                const uint4 *src = e < nk4 ? ksrc + e : vsrc + (e - nk4);
-                buf[u] = make_uint4(0u, 0u, 0u, 0u);
-                if (e < n4) buf[u] = *src;
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int e = base + u * 256 + tid;
-                if (e < n4) dst[e] = buf[u];
-            }
-        }
-    }
+    for (int u = 0; u < 8; ++u)
+        if (u * 256 < n4) buf[u] = *piece(u * 256 + tid);     // wave-uniform guard
 
     // ---- 2. absorbed query qt = qs V_K^T q on MFMA: rows = query heads of
     //         this kv head, K = d, columns = 16-channel blocks of the fp16
-    //         channel-major key basis (wave w takes blocks w, w + 4, ...)
-    {
-        const int nbc = (rk + 15) >> 4;
-        const int qrow = i * a.Hq + h * g;
-        const bool qv = ln < g;
-        const uint16_t *qsrc = a.q + static_cast<int64_t>(qrow + (qv ? ln : 0)) * kHeadDim + 8 * kb;
-        uint4 qa[4];
+    //         channel-major key basis (wave w takes blocks w and w + 4)
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-            qa[st] = qv ? *reinterpret_cast<const uint4 *>(qsrc + 32 * st) : make_uint4(0u, 0u, 0u, 0u);
-        const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * rk * kHeadDim;
-        for (int cb = wv; cb < nbc; cb += kWaves) {
-            const int c = 16 * cb + ln;
-            const bool cvq = c < rk;
-            uint4 bb[4];
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                bb[st] = cvq ? *reinterpret_cast<const uint4 *>(bt + static_cast<int64_t>(c) * kHeadDim + 32 * st + 8 * kb)
-                             : make_uint4(0u, 0u, 0u, 0u);
+    for (int x = 0; x < 2; ++x) {
+        const int cb = wv + kWaves * x;
+        if (x == 0 ? own0 : own1) {
             f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int st = 0; st < 4; ++st)
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(qa[st].x, qa[st].y, qa[st].z, qa[st].w),
-                                                            as_h8(bb[st].x, bb[st].y, bb[st].z, bb[st].w), acc, 0, 0, 0);
+                                                            as_h8(bb[x][st].x, bb[x][st].y, bb[x][st].z, bb[x][st].w),
+                                                            acc, 0, 0, 0);
+            const int c = 16 * cb + ln;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int hh = 4 * kb + v;
-                if (hh < g && cvq) qt[hh * rk + c] = acc[v] * a.qscale;
+                if (hh < g && c < rk) qt[hh * rk + c] = acc[v] * a.qscale;
+            }
+        }
+    }
+    {
+        u4v *dst = reinterpret_cast<u4v *>(stage);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int e = u * 256 + tid;
+            if (u * 256 < n4 && e < n4) dst[e] = buf[u];
+        }
+        for (int base = 8 * 256; base < n4; base += 8 * 256) {
+            u4v more[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) more[u] = *piece(base + u * 256 + tid);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = base + u * 256 + tid;
+                if (e < n4) dst[e] = more[u];
             }
         }
     }
     __syncthreads();
 
-    // ---- 3. per-split tables
-    // (a) qt in fp16 per (head, channel block), channel order [c0,c4,c1,c5,..]
-    for (int e = tid; e < g * nbk * 8; e += 256) {
-        const int hh = e / (nbk * 8), r2 = e - hh * nbk * 8;
-        const int q = r2 >> 3, idx = r2 & 7;
-        const int kk = (idx >> 1) + 4 * (idx & 1);
-        const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
-        const int chanend = q < nbh ? nhk : rk;
-        const int c = chan0 + kk;
-        qt16h[(hh * nbk + q) * 8 + idx] = c < chanend ? static_cast<_Float16>(qt[hh * rk + c])
-                                                      : static_cast<_Float16>(0.0f);
+    // ---- 3. per-split tables in one pass (they read only the staged
+    //         records and qt); indices split by exact float reciprocals
+    const FastDiv div_nbk8(a.inv_nbk8), div_nbk4(a.inv_nbk4), div_rv(a.inv_rv);
+    // (a) score B operand: per k-step u and lane the block-diagonal fp16 qt
+    //     (channel order [c0,c4,c1,c5,..]); without the table, qt16 per
+    //     (head, channel block) and the main loop builds the operand
+    if (L.use_btab) {
+        for (int e = tid; e < nub * 64; e += 256) {
+            const int u = e >> 6, l2 = e & 63, n2 = l2 & 15;
+            const int p = 4 * u + (l2 >> 4);
+            const int q = p / S, j = p - (p / S) * S;
+            const bool ok = p < npair && n2 < NS && j == n2 / g;
+            const int hh = n2 - (n2 / g) * g;
+            const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
+            const int chanend = q < nbh ? nhk : rk;
+            const float *qrow = qt + hh * rk;
+            _Float16 hv[8];
+#pragma unroll
+            for (int idx = 0; idx < 8; ++idx) {
+                const int c = chan0 + (idx >> 1) + 4 * (idx & 1);
+                hv[idx] = static_cast<_Float16>(ok && c < chanend ? qrow[c] : 0.0f);
+            }
+            uint4 w;
+            w.x = __builtin_bit_cast(uint32_t, (h2){hv[0], hv[1]});
+            w.y = __builtin_bit_cast(uint32_t, (h2){hv[2], hv[3]});
+            w.z = __builtin_bit_cast(uint32_t, (h2){hv[4], hv[5]});
+            w.w = __builtin_bit_cast(uint32_t, (h2){hv[6], hv[7]});
+            btab[e] = w;
+        }
+    } else {
+        for (int e = tid; e < g * nbk * 8; e += 256) {
+            const int hh = div_nbk8.quo(e), r2 = e - hh * nbk * 8;
+            const int q = r2 >> 3, idx = r2 & 7;
+            const int kk = (idx >> 1) + 4 * (idx & 1);
+            const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
+            const int chanend = q < nbh ? nhk : rk;
+            const int c = chan0 + kk;
+            qt16h[(hh * nbk + q) * 8 + idx] = c < chanend ? static_cast<_Float16>(qt[hh * rk + c])
+                                                          : static_cast<_Float16>(0.0f);
+        }
     }
     // (b) K scale/zero pairs per (group, channel block): words 0..3 scale
     //     pairs (k, k + 4), words 4..7 zero pairs; padding channels are 0
     for (int e = tid; e < ntg * nbk * 4; e += 256) {
-        const int tg = e / (nbk * 4), r2 = e - tg * nbk * 4;
+        const int tg = div_nbk4.quo(e), r2 = e - tg * nbk * 4;
         const int q = r2 >> 2, k = r2 & 3;
         const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
         const int chanend = q < nbh ? nhk : rk;
@@ -574,7 +676,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     float *vsz = reinterpret_cast<float *>(vpair);
     if (vq) {
         for (int e = tid; e < ntg * rv; e += 256) {
-            const int tg = e / rv, c = e - (e / rv) * rv;
+            const int tg = div_rv.quo(e), c = e - tg * rv;
             const uint32_t mw = stage[voff + tg * WV + vmeta + c];
             const float sc = h2f(mw), zr = h2f(mw >> 16);
             vsz[2 * e] = sc;
@@ -582,17 +684,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         }
     }
     __syncthreads();
-    // (d) block-diagonal score B operand per k-step u and lane
-    if (L.use_btab) {
-        for (int e = tid; e < nub * 64; e += 256) {
-            const int u = e >> 6, l2 = e & 63, n2 = l2 & 15;
-            const int p = 4 * u + (l2 >> 4);
-            const int q = p / S, j = p - (p / S) * S;
-            const bool ok = p < npair && n2 < NS && j == n2 / g;
-            btab[e] = ok ? qt16[(n2 - (n2 / g) * g) * nbk + q] : make_uint4(0u, 0u, 0u, 0u);
-        }
-        __syncthreads();
-    }
 
     // ---- 4. main loop over token groups
     const int slot_n = ln / g, head_n = ln - (ln / g) * g;
@@ -604,7 +695,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     // per-lane value-channel addressing (column c = 16 nb + ln, clamped)
     int vch[NBV], vw0[NBV], vw1[NBV], vs0[NBV], vwid[NBV], vwc[NBV];
     uint32_t vcm[NBV], vbase[NBV];
-    const bool ones_col = vq && (rv & 15) != 0;     // column 15 of the last block is free
     int row_slot[4];                                 // slot of value-output row 4*kb + v
 #pragma unroll
     for (int v = 0; v < 4; ++v) row_slot[v] = (4 * kb + v) / g;
@@ -622,9 +712,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         vs0[nb] = b0 & 31;          // b1 - b0 = 16 wc is a multiple of 32 bits
         vwid[nb] = 4 * wc;
         vwc[nb] = wc;
-        const bool one = ones_col && nb == NBV - 1 && ln == 15;
-        vcm[nb] = one ? 0u : (w4c ? 0x000F000Fu : 0x00030003u);
-        vbase[nb] = one ? 0x3C003C00u : 0x64006400u;
+        vcm[nb] = w4c ? 0x000F000Fu : 0x00030003u;
+        vbase[nb] = 0x64006400u;
     }
     const uint32_t kmagic = vgpr_const(0x64006400u), km4 = vgpr_const(0x000F000Fu),
                    km2 = vgpr_const(0x00030003u);
@@ -718,17 +807,21 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 
         // values: one MFMA per slot and 16-channel block on exact codes
         // (1024 + code in fp16); per-group scale and zero are applied in the
-        // epilogue: sum_t p (code s + z) = s (D - 1024 P) + z P, with
-        // P = sum_t p read from a constant-one column when one is free.
+        // epilogue: sum_t p (code s + z) = s (D - 1024 P) + z P, with the
+        // weight sum P = sum_t p of each stream from one more MFMA against a
+        // constant-one operand (so it sums exactly the fp16 weights used).
         f4 dacc[NBV];
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb) dacc[nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
+        f4 dP = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f16x8 ones8 = as_h8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
 #pragma unroll
         for (int m = 0; m < S; ++m) {
             const int tg = tb0 + m;
             if (tg >= ntg) break;
             const bool arow = live_n && slot_n == m;
             const f16x8 aop = arow ? as_h8(pp0, pp1, pp2, pp3) : as_h8(0u, 0u, 0u, 0u);
+            if (vq) dP = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, ones8, dP, 0, 0, 0);
 #pragma unroll
             for (int nb = 0; nb < NBV; ++nb) {
                 uint32_t bp0, bp1, bp2, bp3;
@@ -756,23 +849,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         }
         if (vq) {
             // P per output row 4*kb + v (stream); rows of invalid groups are 0
-            float Pv[4];
-            if (ones_col) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) Pv[v] = __shfl(dacc[NBV - 1][v], (lane & 48) | 15);
-            } else {
-                const h2 q0 = __builtin_bit_cast(h2, pp0), q1 = __builtin_bit_cast(h2, pp1);
-                const h2 q2 = __builtin_bit_cast(h2, pp2), q3 = __builtin_bit_cast(h2, pp3);
-                float P = ((static_cast<float>(q0[0]) + static_cast<float>(q0[1])) +
-                           (static_cast<float>(q1[0]) + static_cast<float>(q1[1]))) +
-                          ((static_cast<float>(q2[0]) + static_cast<float>(q2[1])) +
-                           (static_cast<float>(q3[0]) + static_cast<float>(q3[1])));
-                P = sv ? P : 0.0f;        // weights of masked streams are not zeroed
-                P += __shfl_xor(P, 16);
-                P += __shfl_xor(P, 32);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) Pv[v] = __shfl(P, 4 * kb + v);
-            }
+            const float Pv[4] = {dP[0], dP[1], dP[2], dP[3]};
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 int tgr = tb0 + row_slot[v];
@@ -808,138 +885,176 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         }
     }
 
-    // ---- 6. incomplete group (fp32 latents; fp16 value latents live in
-    //         the partial record), as one more stream per head
+    // ---- 6. incomplete group (fp32 latents staged in LDS; fp16 value
+    //         latents of the partial record), as one more stream per head:
+    //         thread (head tid / 32, token tid % 32), softmax within the 32
+    //         lanes of a head
     if (do_tail) {
-        const int64_t tb = (hb * 2 + a.sel[i]) * 32;
-        const float *kt = a.k.tail + tb * rk;
-        for (int e = tid; e < g * 32; e += 256) {
-            const int hh = e >> 5, t = e & 31;
-            float acc = -INFINITY;
-            if (t < ntail) {
-                acc = 0.0f;
-                for (int c = 0; c < rk; ++c) acc = fmaf(qt[hh * rk + c], kt[t * rk + c], acc);
-            }
-            ts[e] = acc;
+        const float *tk = reinterpret_cast<const float *>(stage + tk_off);
+        const int hh = tid >> 5, t = tid & 31;
+        const bool ok = hh < g && t < ntail;
+        float sc = -INFINITY;
+        if (ok) {
+            float acc = 0.0f;
+            for (int c = 0; c < rk; ++c) acc = fmaf(qt[hh * rk + c], tk[t * rk + c], acc);
+            sc = acc;
         }
-        __syncthreads();
-        if (tid < g) {
-            float mx = -INFINITY;
-            for (int t = 0; t < ntail; ++t) mx = fmaxf(mx, ts[tid * 32 + t]);
-            float l = 0.0f;
-            for (int t = 0; t < 32; ++t) {
-                const float pv = t < ntail ? exp2f(ts[tid * 32 + t] - mx) : 0.0f;
-                tp[tid * 32 + t] = pv;
-                l += pv;
+        float mx = row_max(sc);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        const float pv = ok ? exp2f(sc - mx) : 0.0f;
+        float ls = row_sum(pv);
+        ls += __shfl_xor(ls, 16);
+        if (hh < g) {
+            tp[hh * 32 + t] = pv;
+            if (t == 0) {
+                mst[kWaves * 16 + hh] = mx;
+                lst[kWaves * 16 + hh] = ls;
             }
-            mst[kWaves * 16 + tid] = mx;
-            lst[kWaves * 16 + tid] = l;
         }
         __syncthreads();
         for (int e = tid; e < g * rv; e += 256) {
-            const int hh = e / rv, c = e - (e / rv) * rv;
+            const int hv = div_rv.quo(e), c = e - hv * rv;
             float acc = 0.0f;
             if (vq) {
-                const float *vt = a.v.tail + tb * rv;
-                for (int t = 0; t < ntail; ++t) acc = fmaf(tp[hh * 32 + t], vt[t * rv + c], acc);
+                const float *tv = reinterpret_cast<const float *>(stage + tv_off);
+                for (int t2 = 0; t2 < ntail; ++t2) acc = fmaf(tp[hv * 32 + t2], tv[t2 * rv + c], acc);
             } else {
-                const uint16_t *r16 =
-                    reinterpret_cast<const uint16_t *>(vg + static_cast<int64_t>(nfull) * WV) + c * 32;
-                for (int t = 0; t < ntail; ++t) acc = fmaf(tp[hh * 32 + t], h2f(r16[t]), acc);
+                const _Float16 *tv = reinterpret_cast<const _Float16 *>(stage + tv_off) + c * 32;
+                for (int t2 = 0; t2 < ntail; ++t2) acc = fmaf(tp[hv * 32 + t2], static_cast<float>(tv[t2]), acc);
             }
-            ost[(kWaves * 16 + hh) * rv + c] = acc;
+            ost[(kWaves * 16 + hv) * rv + c] = acc;
         }
     }
     __syncthreads();
 
-    // ---- 7. merge the streams of each head; write the split's partial.
-    //         Stream index sidx: waves' streams w*16 + slot*g + head, then the
-    //         tail stream kWaves*16 + head.
-    const int nsw = kWaves * S + (do_tail ? 1 : 0);   // streams per head
-    float *wts = ts;                                   // reuse: [g][<= 4*16 + 1]
-    if (tid < g) {
-        float M = -INFINITY;
-        for (int k = 0; k < nsw; ++k) {
-            const int sidx = k < kWaves * S ? (k / S) * 16 + (k % S) * g + tid : kWaves * 16 + tid;
-            M = fmaxf(M, mst[sidx]);
+    // ---- 7. merge the streams of each head and write the split's partial.
+    //         Stream k of a head: k < kWaves * S -> wave k / S, slot k % S
+    //         (LDS stream (k / S) * 16 + (k % S) * g + head); k = kWaves * S
+    //         -> the tail stream kWaves * 16 + head.  Wave w merges heads
+    //         w, w + 4 with its lanes over streams.
+    const int nsw = kWaves * S + (do_tail ? 1 : 0);   // <= 65
+    float *wts = ts;                                   // [g][65]
+    float *part = a.partial + (static_cast<int64_t>(i) * a.Hq + h * g) * kMaxSplits * (rv + 2) +
+                  static_cast<int64_t>(s) * (rv + 2);
+    const int64_t head_stride = static_cast<int64_t>(kMaxSplits) * (rv + 2);
+    for (int hh = wv; hh < g; hh += kWaves) {
+        const int k1 = lane + 64;
+        const int sid0 = lane < kWaves * S ? (lane / S) * 16 + (lane % S) * g + hh : kWaves * 16 + hh;
+        const float m0 = lane < nsw ? mst[sid0] : -INFINITY;
+        const float l0 = lane < nsw ? lst[sid0] : 0.0f;
+        const float m1 = k1 < nsw ? mst[kWaves * 16 + hh] : -INFINITY;   // only k = 64 (the tail at S = 16)
+        const float l1 = k1 < nsw ? lst[kWaves * 16 + hh] : 0.0f;
+        const float M = wave_max(fmaxf(m0, m1));
+        const float w0 = m0 == -INFINITY ? 0.0f : exp2f(m0 - M);
+        const float w1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - M);
+        const float lt = wave_sum(fmaf(w0, l0, w1 * l1));
+        if (lane < nsw) wts[hh * 65 + lane] = w0;
+        if (k1 < nsw) wts[hh * 65 + k1] = w1;
+        if (lane == 0) {
+            part[hh * head_stride] = M;
+            part[hh * head_stride + 1] = lt;
         }
-        hm[tid] = M;
     }
     __syncthreads();
-    for (int e = tid; e < g * nsw; e += 256) {
-        const int hh = e / nsw, k = e - (e / nsw) * nsw;
-        const int sidx = k < kWaves * S ? (k / S) * 16 + (k % S) * g + hh : kWaves * 16 + hh;
-        const float ms = mst[sidx];
-        wts[e] = ms == -INFINITY ? 0.0f : exp2f(ms - hm[hh]);
-    }
-    __syncthreads();
-    for (int e = tid; e < g * (rv + 2); e += 256) {
-        const int hh = e / (rv + 2), k = e - (e / (rv + 2)) * (rv + 2);
-        const float *wrow = wts + hh * nsw;
-        float val;
-        if (k == 0) {
-            val = hm[hh];
-        } else {
-            const int c = k - 2;
-            float acc = 0.0f;
+    for (int e = tid; e < g * rv; e += 256) {
+        const int hh = div_rv.quo(e), c = e - hh * rv;
+        const float *wrow = wts + hh * 65;
+        float acc = 0.0f;
 #pragma unroll 4
-            for (int kk = 0; kk < nsw; ++kk) {
-                const int sidx = kk < kWaves * S ? (kk / S) * 16 + (kk % S) * g + hh : kWaves * 16 + hh;
-                acc = fmaf(wrow[kk], k == 1 ? lst[sidx] : ost[sidx * rv + c], acc);
-            }
-            val = acc;
+        for (int k = 0; k < nsw; ++k) {
+            const int sidx = k < kWaves * S ? (k / S) * 16 + (k % S) * g + hh : kWaves * 16 + hh;
+            acc = fmaf(wrow[k], ost[sidx * rv + c], acc);
         }
-        a.partial[((static_cast<int64_t>(i) * a.Hq + h * g + hh) * kMaxSplits + s) * (rv + 2) + k] = val;
+        part[hh * head_stride + 2 + c] = acc;
     }
-
 }
 
-// One wave per (call row, query head): merge the splits by log-sum-exp and
-// project back with the value basis, o = V_V (o_lat / l) + mu_V, in fp16.
-// Lane sp holds split sp (and sp + 64); every partial is read once, all
-// loads of a wave are independent.
-__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int task = blockIdx.x * 4 + wv;
-    const bool active = task < a.B * a.Hq;
-    __shared__ float ov[4][kHeadDim];
-    const int i = active ? task / a.Hq : 0, qh = active ? task - (task / a.Hq) * a.Hq : 0;
-    const int h = qh / a.gqa, grp = h / a.hpg, ns = a.nsplit[i], rv = a.v.r;
+// One workgroup of one wave per (call row, query head): merge the splits by
+// log-sum-exp and project back with the value basis,
+// o = V_V (o_lat / l) + mu_V, rounded to fp16.  The row's split partials and
+// its group's value basis and mean are first copied to LDS with independent
+// 16-byte loads, so the kernel waits on memory once; all later steps read LDS.
+__host__ __device__ inline int combine_lds_floats(int ns, int rv) {
+    return ((ns * (rv + 2) + 3) & ~3) + kHeadDim * rv + kHeadDim + ((ns + 3) & ~3) + ((rv + 3) & ~3);
+}
+
+__global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
+    extern __shared__ __align__(16) float cl[];
+    const int lane = threadIdx.x;
+    const int qh = blockIdx.x, i = blockIdx.y;   // grid (Hq, B)
+    // all argument loads issued together (one scalar round trip)
+    asm volatile("" ::"s"(a.partial), "s"(a.out), "s"(a.v.basis), "s"(a.v.mu), "s"(a.v.r), "s"(a.gqa),
+                 "s"(a.hpg), "s"(a.Hq), "s"(a.row[i].nsplit));
+    const int h = qh / a.gqa, grp = h / a.hpg, ns = a.row[i].nsplit, rv = a.v.r;
+    const int np = ns * (rv + 2), npa = (np + 3) & ~3;
+    float *pl = cl;                            // [ns][rv + 2]: m, l, o_lat
+    float *bl = cl + npa;                      // [D][rv] value basis
+    float *ml = bl + kHeadDim * rv;            // [D] value mean
+    float *wl = ml + kHeadDim;                 // [ns] split weights
+    float *ol = wl + ((ns + 3) & ~3);          // [rv] merged latent output
     const float *part = a.partial + (static_cast<int64_t>(i) * a.Hq + qh) * kMaxSplits * (rv + 2);
-    const bool s0 = lane < ns, s1 = lane + 64 < ns;
-    const float m0 = s0 ? part[lane * (rv + 2)] : -INFINITY;
-    const float m1 = s1 ? part[(lane + 64) * (rv + 2)] : -INFINITY;
-    const float l0 = s0 ? part[lane * (rv + 2) + 1] : 0.0f;
-    const float l1 = s1 ? part[(lane + 64) * (rv + 2) + 1] : 0.0f;
-    const float M = wave_max(fmaxf(m0, m1));
-    const float w0 = s0 ? exp2f(m0 - M) : 0.0f, w1 = s1 ? exp2f(m1 - M) : 0.0f;
-    const float l = wave_sum(fmaf(w0, l0, w1 * l1));
-    const float inv_l = 1.0f / l;
-    for (int c0 = 0; c0 < rv; c0 += 4) {
-        float acc[4];
+    const float *bv = a.v.basis + static_cast<int64_t>(grp) * kHeadDim * rv;
+    const float *mv = a.v.mu + grp * kHeadDim;
+
+    // 1. copy to LDS: whole 16-byte pieces of the partials, the basis
+    //    (128 rv floats) and the mean; the < 4 trailing partial floats singly
+    {
+        const int n4p = np >> 2, n4b = (kHeadDim * rv) >> 2, n4 = n4p + n4b + kHeadDim / 4;
+        for (int base = 0; base < n4; base += 64 * 8) {
+            float4 buf[8];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            const int c = c0 + cc;
-            float t = 0.0f;
-            if (c < rv) {
-                if (s0) t = w0 * part[lane * (rv + 2) + 2 + c];
-                if (s1) t = fmaf(w1, part[(lane + 64) * (rv + 2) + 2 + c], t);
+            for (int u = 0; u < 8; ++u) {
+                const int e = base + 64 * u + lane;
+                const float4 *src = e < n4p ? reinterpret_cast<const float4 *>(part) + e
+                                  : e < n4p + n4b ? reinterpret_cast<const float4 *>(bv) + (e - n4p)
+                                                  : reinterpret_cast<const float4 *>(mv) + (e - n4p - n4b);
+                buf[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (e < n4) buf[u] = *src;
             }
-            acc[cc] = t;
-        }
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) acc[cc] = wave_sum(acc[cc]);
-        if (lane < 4 && c0 + lane < rv && active)
-            ov[wv][c0 + lane] = (lane == 0 ? acc[0] : lane == 1 ? acc[1] : lane == 2 ? acc[2] : acc[3]) * inv_l;
+            for (int u = 0; u < 8; ++u) {
+                const int e = base + 64 * u + lane;
+                float4 *dst = e < n4p ? reinterpret_cast<float4 *>(pl) + e
+                            : e < n4p + n4b ? reinterpret_cast<float4 *>(bl) + (e - n4p)
+                                            : reinterpret_cast<float4 *>(ml) + (e - n4p - n4b);
+                if (e < n4) *dst = buf[u];
+            }
+        }
+        if (lane < np - 4 * n4p) pl[4 * n4p + lane] = part[4 * n4p + lane];
     }
     __syncthreads();
-    if (!active) return;
-    const float *bv = a.v.basis + static_cast<int64_t>(grp) * kHeadDim * rv;
-    for (int d = lane; d < kHeadDim; d += 64) {
-        float o = a.v.mu[grp * kHeadDim + d];
-        for (int c = 0; c < rv; ++c) o = fmaf(bv[d * rv + c], ov[wv][c], o);
-        a.out[(static_cast<int64_t>(i) * a.Hq + qh) * kHeadDim + d] = static_cast<uint16_t>(f2h_bits(o));
+
+    // 2. split weights relative to the largest split maximum, and l
+    const bool s0 = lane < ns, s1 = lane + 64 < ns;
+    const float m0 = s0 ? pl[lane * (rv + 2)] : -INFINITY;
+    const float m1 = s1 ? pl[(lane + 64) * (rv + 2)] : -INFINITY;
+    const float M = wave_max(fmaxf(m0, m1));
+    const float w0 = s0 ? exp2f(m0 - M) : 0.0f, w1 = s1 ? exp2f(m1 - M) : 0.0f;
+    const float l = wave_sum(fmaf(w0, s0 ? pl[lane * (rv + 2) + 1] : 0.0f,
+                                  w1 * (s1 ? pl[(lane + 64) * (rv + 2) + 1] : 0.0f)));
+    if (s0) wl[lane] = w0;
+    if (s1) wl[lane + 64] = w1;
+    __syncthreads();
+
+    // 3. merged latent output per channel
+    const float inv_l = 1.0f / l;
+    for (int c = lane; c < rv; c += 64) {
+        float acc = 0.0f;
+        for (int sp = 0; sp < ns; ++sp) acc = fmaf(wl[sp], pl[sp * (rv + 2) + 2 + c], acc);
+        ol[c] = acc * inv_l;
     }
+    __syncthreads();
+
+    // 4. output projection, two adjacent outputs per lane
+    const int d0 = 2 * lane;
+    float o0 = ml[d0], o1 = ml[d0 + 1];
+    for (int c = 0; c < rv; ++c) {
+        const float oc = ol[c];
+        o0 = fmaf(bl[d0 * rv + c], oc, o0);
+        o1 = fmaf(bl[(d0 + 1) * rv + c], oc, o1);
+    }
+    reinterpret_cast<uint32_t *>(a.out + (static_cast<int64_t>(i) * a.Hq + qh) * kHeadDim)[lane] =
+        f2h_bits(o0) | (f2h_bits(o1) << 16);
 }
 
 __global__ __launch_bounds__(256) void basis_t16_kernel(const float *src, uint16_t *dst, int G, int r) {
@@ -974,36 +1089,39 @@ size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int chunk, int wo
     return static_cast<size_t>(attend_lds(gqa, r_k, n_hi_k, r_v, chunk, words_k, words_v, vq).total);
 }
 
-template <int S, int NBV>
-static hipError_t launch_attend_t(const AttendArgs &a, int n_work, size_t lds_bytes, hipStream_t s) {
+template <int G, int NBV>
+static hipError_t launch_attend_t(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
     static bool configured = false;
     if (!configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<S, NBV>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<G, NBV>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((attend_kernel<S, NBV>), dim3(n_work), dim3(256), lds_bytes, s, a);
+    hipLaunchKernelGGL((attend_kernel<G, NBV>), dim3(a.nsplit_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
     return hipGetLastError();
 }
 
-template <int S>
-static hipError_t launch_attend_s(const AttendArgs &a, int n_work, size_t lds_bytes, hipStream_t s) {
+template <int G>
+static hipError_t launch_attend_g(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
     const int nbv = (a.v.r + 15) / 16;
-    if (nbv <= 1) return launch_attend_t<S, 1>(a, n_work, lds_bytes, s);
-    if (nbv <= 2) return launch_attend_t<S, 2>(a, n_work, lds_bytes, s);
-    if (nbv <= 4) return launch_attend_t<S, 4>(a, n_work, lds_bytes, s);
-    return launch_attend_t<S, 8>(a, n_work, lds_bytes, s);
+    if (nbv <= 1) return launch_attend_t<G, 1>(a, lds_bytes, s);
+    if (nbv <= 2) return launch_attend_t<G, 2>(a, lds_bytes, s);
+    if (nbv <= 4) return launch_attend_t<G, 4>(a, lds_bytes, s);
+    return launch_attend_t<G, 8>(a, lds_bytes, s);
 }
 
-hipError_t launch_attend(const AttendArgs &a, int n_work, size_t lds_bytes, hipStream_t s) {
-    switch (16 / a.gqa) {
-        case 16: return launch_attend_s<16>(a, n_work, lds_bytes, s);
-        case 8: return launch_attend_s<8>(a, n_work, lds_bytes, s);
-        case 5: return launch_attend_s<5>(a, n_work, lds_bytes, s);
-        case 4: return launch_attend_s<4>(a, n_work, lds_bytes, s);
-        case 3: return launch_attend_s<3>(a, n_work, lds_bytes, s);
-        default: return launch_attend_s<2>(a, n_work, lds_bytes, s);
+hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+    switch (a.gqa) {
+        case 1: return launch_attend_g<1>(a, lds_bytes, s);
+        case 2: return launch_attend_g<2>(a, lds_bytes, s);
+        case 3: return launch_attend_g<3>(a, lds_bytes, s);
+        case 4: return launch_attend_g<4>(a, lds_bytes, s);
+        case 5: return launch_attend_g<5>(a, lds_bytes, s);
+        case 6: return launch_attend_g<6>(a, lds_bytes, s);
+        case 7: return launch_attend_g<7>(a, lds_bytes, s);
+        case 8: return launch_attend_g<8>(a, lds_bytes, s);
+        default: return hipErrorInvalidValue;
     }
 }
 
@@ -1014,7 +1132,15 @@ hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, hipSt
 }
 
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(combine_kernel, dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(combine_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const size_t lds = static_cast<size_t>(combine_lds_floats(a.nsplit_max, a.v.r)) * sizeof(float);
+    hipLaunchKernelGGL(combine_kernel, dim3(a.Hq, a.B), dim3(64), lds, s, a);
     return hipGetLastError();
 }
 

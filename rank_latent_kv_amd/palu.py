@@ -240,15 +240,18 @@ class LatentKVCache:
         self.D, self.H, self.Hq, self.G = head_dim, n_kv_heads, n_q_heads, n_head_groups
         self.max_batch, self.max_seq_len = max_batch, max_seq_len
         self.handle = palu_cache_create(cfg, max_batch, max_seq_len)
+        self._destroy = lib().palu_cache_destroy
         nbytes = palu_cache_required_bytes(self.handle)
         dev = torch.device("cuda") if device is None else torch.device(device)
         self.storage = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         palu_cache_bind(self.handle, self.storage.data_ptr(), nbytes)
 
     def __del__(self):
-        h = getattr(self, "handle", None)
-        if h:
-            palu_cache_destroy(h)
+        # the library handle is kept on the instance: module globals may
+        # already be gone when this runs at interpreter exit
+        h, destroy = getattr(self, "handle", None), getattr(self, "_destroy", None)
+        if h and destroy is not None:
+            destroy(h)
             self.handle = None
 
     def _stream(self):
