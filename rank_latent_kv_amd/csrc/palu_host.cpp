@@ -35,7 +35,6 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 constexpr int kGramElems = kHeadDim * kHeadDim + kHeadDim;
 constexpr int kGramMaxRowsPerBlock = 8192;   // bounds fp32 accumulation per tile
 constexpr int kAttendTargetGroups = 1024;    // workgroups aimed for per decode launch
-constexpr size_t kAttendLdsCap = 64 * 1024;  // LDS per workgroup the split size aims for
 constexpr size_t kAttendLdsMax = 160 * 1024; // LDS per workgroup on gfx950
 
 int n_hi_of(int r, float frac) {
@@ -504,39 +503,40 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
             const int slot = seq_ids ? seq_ids[b0 + i] : b0 + i;
             aa.row[i].slot = slot;
             aa.row[i].len = c->len[slot];
-            aa.row[i].sel = c->sel[slot];
+            aa.row[i].qi = i;
+            aa.row[i].sel_ns = c->sel[slot];
             const int nfull = c->len[slot] / kTokGroup;
             units += static_cast<int64_t>(c->H) * std::max(1, nfull);
             max_full = std::max(max_full, nfull);
         }
-        // split size: a multiple of the groups one workgroup pass covers,
-        // large enough for the split limit, small enough for LDS; the same
-        // for every row, so a row has ceil(groups / chunk) splits
-        const int per_iter = 4 * (16 / c->gqa);
+        // split size: a multiple of the groups one workgroup pass covers
+        // (double-buffered passes keep the LDS independent of it), about
+        // kAttendTargetGroups workgroups per launch, and large enough for the
+        // split limit; the same for every row, so a row has
+        // ceil(groups / chunk) splits
+        const int per_pass = 4 * (16 / c->gqa);
         const bool vq = !aa.v.fp16_latents;
-        auto lds_for = [&](int64_t ch) {
-            return attend_lds_bytes(c->gqa, aa.k.r, aa.k.n_hi, aa.v.r, static_cast<int>(ch), aa.k.words,
-                                    aa.v.words, vq);
-        };
         auto round_up = [](int64_t v, int64_t m) { return (v + m - 1) / m * m; };
         int64_t chunk;
         if (c->cfg.split_groups > 0) {
             chunk = c->cfg.split_groups;
         } else {
-            chunk = round_up(std::max<int64_t>(1, (units + kAttendTargetGroups - 1) / kAttendTargetGroups), per_iter);
-            while (chunk > 1 && lds_for(chunk) > kAttendLdsCap)
-                chunk = chunk > per_iter ? chunk - per_iter : chunk - 1;
+            chunk = round_up(std::max<int64_t>(1, (units + kAttendTargetGroups - 1) / kAttendTargetGroups), per_pass);
         }
         chunk = std::max<int64_t>(chunk, (max_full + kMaxSplits - 1) / kMaxSplits);
         int nsplit_max = 1;
         for (int i = 0; i < nb; ++i) {
             const int nfull = aa.row[i].len / kTokGroup;
-            aa.row[i].nsplit = std::max(1, static_cast<int>((nfull + chunk - 1) / chunk));
-            nsplit_max = std::max(nsplit_max, aa.row[i].nsplit);
+            const int ns = std::max(1, static_cast<int>((nfull + chunk - 1) / chunk));
+            aa.row[i].sel_ns |= ns << 1;
+            aa.nsplit_call[i] = ns;
+            nsplit_max = std::max(nsplit_max, ns);
         }
-        const size_t lds = lds_for(chunk);
+        // longest rows first in the grid's z order (stable, so equal lengths keep call order)
+        std::stable_sort(aa.row, aa.row + nb, [](const AttendRow &x, const AttendRow &y) { return x.len > y.len; });
+        const size_t lds = attend_lds_bytes(c->gqa, aa.k.r, aa.k.n_hi, aa.v.r, aa.k.words, aa.v.words, vq);
         if (lds > kAttendLdsMax)
-            return fail(PALU_ERR_UNSUPPORTED, "sequence too long for the split limit at this rank");
+            return fail(PALU_ERR_UNSUPPORTED, "decode workgroup needs more than 160 KiB of LDS at these ranks");
         aa.chunk = static_cast<int>(chunk);
         aa.nsplit_max = nsplit_max;
         {

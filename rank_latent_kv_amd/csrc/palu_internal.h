@@ -61,10 +61,12 @@ struct EncodeArgs {
     int sel_new[kMaxCallSeqs];
 };
 
-// One decode row: cache slot, stored length, live tail buffer, and its
-// number of splits (16 bytes, one load).
+// One decode row (16 bytes, one load): cache slot, stored length, the
+// call's row index of its query/output, and sel | nsplit << 1 (live tail
+// buffer, number of splits).  Rows are ordered longest first so that the
+// longest workgroups are dispatched first.
 struct AttendRow {
-    int slot, len, sel, nsplit;
+    int slot, len, qi, sel_ns;
 };
 
 struct AttendArgs {
@@ -79,11 +81,12 @@ struct AttendArgs {
     // correctly rounded fp32 reciprocals of table index divisors: r_v, and
     // 4 and 8 times the key channel blocks
     float inv_rv, inv_nbk4, inv_nbk8;
-    AttendRow row[kMaxCallSeqs];
+    AttendRow row[kMaxCallSeqs];       // grid z order (longest first)
+    int nsplit_call[kMaxCallSeqs];     // splits of call row i (combine)
 };
 
-// LDS bytes of one attend workgroup for a split of `chunk` token groups.
-size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int chunk, int words_k, int words_v, bool vq);
+// LDS bytes of one attend workgroup (independent of the split size).
+size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int words_k, int words_v, bool vq);
 
 // Launchers (defined in palu_kernels.hip).  They return the launch status.
 hipError_t launch_gram(const GramArgs &a, hipStream_t s);

@@ -352,6 +352,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 constexpr int kWaves = 4;
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kBtabMaxU = 16;   // score B-operand table kept in LDS up to this many MFMA k-steps
+constexpr int kStageBudgetWords = 24 * 1024;   // both record buffers together (96 KiB)
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -360,8 +361,10 @@ typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 // LDS layout of one attend workgroup (byte offsets).  Shared by the kernel
 // and the host, which sizes the dynamic LDS from it.
 struct AttendLds {
-    int qt, qt16, ts, mst, lst, ost, tp, hm, btab, kpair, vpair, stage, total;
-    int nbk, nub;
+    int qt, qt16, btab, kpw, stage, sb;          // sb: words per stage buffer
+    int pp;                                      // token groups per pass
+    int ts, mst, lst, ost, tp;                   // merge state: byte offsets inside a stage buffer
+    int total, nbk, nub;
     bool use_btab;
 };
 
@@ -371,26 +374,38 @@ __host__ __device__ inline int lds_take(int &o, int bytes) {
     return r;
 }
 
-__host__ __device__ inline AttendLds attend_lds(int g, int rk, int nhk, int rv, int chunk, int wk, int wv, bool vq) {
+// Dynamic LDS of one attend workgroup; the same for every split size.
+__host__ __device__ inline AttendLds attend_lds(int g, int rk, int nhk, int rv, int wk, int wv, bool vq) {
     AttendLds L;
-    const int S = 16 / g;
+    const int S = 16 / g, P = kWaves * S;
     L.nbk = (nhk + 7) / 8 + (rk - nhk + 7) / 8;
     L.nub = (S * L.nbk + 3) / 4;
     L.use_btab = L.nub <= kBtabMaxU;
     int o = 0;
     L.qt = lds_take(o, g * kHeadDim * 4);
     L.qt16 = lds_take(o, g * 16 * 16);
-    L.ts = lds_take(o, g * (kWaves * 16 + 1) * 4);
-    L.mst = lds_take(o, (kWaves + 1) * 16 * 4);
-    L.lst = lds_take(o, (kWaves + 1) * 16 * 4);
-    L.ost = lds_take(o, (kWaves + 1) * 16 * rv * 4);
-    L.tp = lds_take(o, g * 32 * 4);
-    L.hm = lds_take(o, kMaxGqa * 4);
     L.btab = lds_take(o, L.use_btab ? L.nub * 64 * 16 : 0);
-    L.kpair = lds_take(o, chunk * L.nbk * 8 * 4);
-    L.vpair = lds_take(o, vq ? chunk * rv * 2 * 4 : 0);
-    // staged records of the split (+ alignment slack) and the tail latents
-    L.stage = lds_take(o, (chunk * (wk + (vq ? wv : 0)) + 16 + 32 * rk + (vq ? 32 * rv : 16 * rv)) * 4);
+    L.kpw = lds_take(o, kWaves * S * L.nbk * 8 * 4);
+    // two stage buffers.  Each holds one pass of records (+ 16-byte
+    // alignment slack); a pass is the 4 S groups the waves take, fewer when
+    // that would not fit the budget.  The last split's tail latents go to
+    // the buffer its last pass leaves free, and after the main loop the
+    // other buffer holds the merge state.
+    const int rec_words = wk + (vq ? wv : 0);
+    const int fit = (kStageBudgetWords / 2 - 16) / rec_words;
+    L.pp = fit < P ? (fit > 1 ? fit : 1) : P;
+    int m = 0;
+    L.ts = lds_take(m, g * (kWaves * 16 + 1) * 4);
+    L.mst = lds_take(m, (kWaves + 1) * 16 * 4);
+    L.lst = lds_take(m, (kWaves + 1) * 16 * 4);
+    L.ost = lds_take(m, (kWaves + 1) * 16 * rv * 4);
+    L.tp = lds_take(m, g * 32 * 4);
+    int sb = L.pp * rec_words + 16;
+    const int tail_words = 32 * rk + (vq ? 32 * rv : 16 * rv);
+    sb = sb > tail_words ? sb : tail_words;
+    sb = sb > m / 4 ? sb : m / 4;
+    L.sb = (sb + 3) & ~3;
+    L.stage = lds_take(o, 2 * L.sb * 4);
     L.total = o;
     return L;
 }
@@ -463,10 +478,14 @@ __device__ __forceinline__ f16x8 dequant8_any(uint32_t X, bool w4, const uint4 &
 }
 
 // Workgroup = (call row i, kv head h, split s); see the section comment.
-// G = query heads per kv head, NBV = value-channel blocks of 16.
-template <int G, int NBV>
+// G = query heads per kv head, NBV = value-channel blocks of 16.  A split is
+// processed in passes of up to 4 S token groups (S per wave); the records of
+// pass p + 1 are copied global -> LDS (direct 16-byte loads into LDS, no
+// registers) into the other of two buffers while pass p is computed.
+template <int G, int NBV, bool VQ>
 __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     constexpr int g = G, S = 16 / G, NS = S * G;
+    constexpr bool vq = VQ;                      // V stored as mixed-bit codes
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -481,8 +500,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     asm volatile("" ::"s"(a.k.records), "s"(a.v.records), "s"(a.k.tail), "s"(a.v.tail), "s"(a.k.basis_t16),
                  "s"(a.q), "s"(a.k.head_stride), "s"(a.v.head_stride), "s"(a.k.r), "s"(a.k.n_hi), "s"(a.k.words),
                  "s"(a.v.r), "s"(a.v.n_hi), "s"(a.v.words), "s"(a.v.fp16_latents), "s"(a.chunk), "s"(a.hpg),
-                 "s"(a.Hq), "s"(a.Hkv), "s"(a.qscale), "s"(rw.slot), "s"(rw.len), "s"(rw.sel), "s"(rw.nsplit));
-    const int ns = rw.nsplit;
+                 "s"(a.Hq), "s"(a.Hkv), "s"(a.qscale), "s"(rw.slot), "s"(rw.len), "s"(rw.qi), "s"(rw.sel_ns));
+    const int ns = rw.sel_ns >> 1, qi = rw.qi;
     if (s >= ns) return;                          // whole workgroup: no barrier reached
     const int slot = rw.slot, len = rw.len;
     const int nfull = len >> 5, ntail = len & 31;
@@ -495,133 +514,124 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     const int nbh = (nhk + 7) >> 3;
     const int rv = a.v.r, nhv = a.v.n_hi;
     const int WK = a.k.words, WV = a.v.words;
-    const bool vq = !a.v.fp16_latents;
     const int kmeta = 4 * nhk + 2 * nlk, vmeta = 4 * nhv + 2 * (rv - nhv);
 
-    const AttendLds L = attend_lds(g, rk, nhk, rv, a.chunk, WK, WV, vq);
+    const AttendLds L = attend_lds(g, rk, nhk, rv, WK, WV, vq);
     const int nbk = L.nbk, nub = L.nub, npair = S * nbk;
+    const int PP = L.pp;                          // groups per pass (<= P)
+    const int npass = (ntg + PP - 1) / PP;
     float *qt = reinterpret_cast<float *>(lds + L.qt);
     uint4 *qt16 = reinterpret_cast<uint4 *>(lds + L.qt16);
     _Float16 *qt16h = reinterpret_cast<_Float16 *>(lds + L.qt16);
-    float *ts = reinterpret_cast<float *>(lds + L.ts);
-    float *mst = reinterpret_cast<float *>(lds + L.mst);
-    float *lst = reinterpret_cast<float *>(lds + L.lst);
-    float *ost = reinterpret_cast<float *>(lds + L.ost);
-    float *tp = reinterpret_cast<float *>(lds + L.tp);
     uint4 *btab = reinterpret_cast<uint4 *>(lds + L.btab);
-    uint32_t *kpair = reinterpret_cast<uint32_t *>(lds + L.kpair);
-    uint32_t *vpair = reinterpret_cast<uint32_t *>(lds + L.vpair);
-    uint32_t *stage = reinterpret_cast<uint32_t *>(lds + L.stage);
+    uint32_t *kpw = reinterpret_cast<uint32_t *>(lds + L.kpw) + wv * (S * nbk * 8);   // this wave's
+    // stage buffer tb holds the tail latents (the one the last pass leaves
+    // free); after the main loop the other one holds the merge state
+    const int tb = npass & 1;
+    const int tail_off = L.stage + tb * L.sb * 4, post = L.stage + (1 - tb) * L.sb * 4;
+    const uint32_t *tails = reinterpret_cast<const uint32_t *>(lds + tail_off);
+    float *ts = reinterpret_cast<float *>(lds + post + L.ts);
+    float *mst = reinterpret_cast<float *>(lds + post + L.mst);
+    float *lst = reinterpret_cast<float *>(lds + post + L.lst);
+    float *ost = reinterpret_cast<float *>(lds + post + L.ost);
+    float *tp = reinterpret_cast<float *>(lds + post + L.tp);
 
     const int64_t hb = static_cast<int64_t>(slot) * a.Hkv + h;
     const uint32_t *kg = a.k.records + hb * a.k.head_stride;
     const uint32_t *vg = a.v.records + hb * a.v.head_stride;
 
-    // ---- 1. issue every global load the prologue needs before waiting on
-    //         any: the query rows and key-basis blocks of the absorbed query,
-    //         then the split's packed records and the tail latents (copied
-    //         to LDS in 16-byte pieces; the first 8 pieces per thread are in
-    //         flight while the query MFMA waits only on its own operands)
-    // only the waves that own a 16-channel block of qt load the query and
-    // their basis block (wave-uniform branches)
-    const int nbc = (rk + 15) >> 4;              // 16-channel blocks of qt (<= 8)
-    const bool own0 = wv < nbc, own1 = wv + kWaves < nbc;
-    const int qrow = i * a.Hq + h * g;
-    uint4 qa[4], bb[2][4];
-    if (own0) {
-        const uint16_t *qsrc = a.q + static_cast<int64_t>(qrow + (ln < g ? ln : 0)) * kHeadDim + 8 * kb;
-        // rows ln >= g repeat a valid query; their MFMA output rows are never stored
-#pragma unroll
-        for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const uint4 *>(qsrc + 32 * st);
-        const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * rk * kHeadDim;
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            if (x == 1 && !own1) break;
-            int c = 16 * (wv + kWaves * x) + ln;
-            c = c < rk ? c : rk - 1;              // clamped rows are never stored
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                bb[x][st] = *reinterpret_cast<const uint4 *>(bt + static_cast<int64_t>(c) * kHeadDim + 32 * st + 8 * kb);
+    // ---- 1. copies global -> LDS: a pass of records (K records, then V
+    //         records; each block starts at the 16-byte boundary at or below
+    //         its first word) and, in the last split, the tail latents
+    auto pass_words = [&](int p, int &nk4, int &nv4, int &koff, int &voff) {
+        const int64_t g0 = jb + p * PP, g1 = g0 + PP < je ? g0 + PP : je;
+        const int64_t ka = (g0 * WK) & ~3LL, va = (g0 * WV) & ~3LL;
+        nk4 = static_cast<int>((g1 * WK - ka + 3) >> 2);
+        nv4 = vq ? static_cast<int>((g1 * WV - va + 3) >> 2) : 0;
+        koff = static_cast<int>(g0 * WK - ka);
+        voff = 4 * nk4 + static_cast<int>(g0 * WV - va);
+    };
+    auto copy_pass = [&](int p) {
+        int nk4, nv4, koff, voff;
+        pass_words(p, nk4, nv4, koff, voff);
+        const int64_t g0 = jb + p * PP;
+        const u4v *ks = reinterpret_cast<const u4v *>(kg + ((g0 * WK) & ~3LL));
+        const u4v *vs = reinterpret_cast<const u4v *>(vg + ((g0 * WV) & ~3LL));
+        const int n4 = nk4 + nv4, boff = L.stage + (p & 1) * L.sb * 4;
+        for (int c = wv; c * 64 < n4; c += kWaves) {
+            const int e = c * 64 + lane;
+            if (e < n4)
+                __builtin_amdgcn_global_load_lds(e < nk4 ? ks + e : vs + (e - nk4), lds + boff + c * 1024, 16, 0, 0);
         }
-    }
-
-    const int64_t k_a = (static_cast<int64_t>(jb) * WK) & ~3LL;
-    const int k_words = ntg ? static_cast<int>((static_cast<int64_t>(je) * WK - k_a + 3) & ~3LL) : 0;
-    const int64_t v_a = (static_cast<int64_t>(jb) * WV) & ~3LL;
-    const int v_words = (vq && ntg) ? static_cast<int>((static_cast<int64_t>(je) * WV - v_a + 3) & ~3LL) : 0;
-    const int koff = static_cast<int>(static_cast<int64_t>(jb) * WK - k_a);          // record 0 of the split
-    const int voff = k_words + static_cast<int>(static_cast<int64_t>(jb) * WV - v_a);
-    // tail latents of the last split: fp32 [32][r] buffers (only the filled
-    // rows, rounded up to 16 bytes), or the fp16 value record of group nfull
-    const int64_t tsel = (hb * 2 + rw.sel) * kTokGroup;
+    };
+    const int64_t tsel = (hb * 2 + (rw.sel_ns & 1)) * kTokGroup;
     const int tk_words = do_tail ? min((ntail * rk + 3) & ~3, kTokGroup * rk) : 0;
     const int tv_words = do_tail ? (vq ? min((ntail * rv + 3) & ~3, kTokGroup * rv) : 16 * rv) : 0;
-    const int tk_off = k_words + v_words, tv_off = tk_off + tk_words;
-    const int nk4 = k_words >> 2, nv4 = v_words >> 2, ntk4 = tk_words >> 2, n4 = nk4 + nv4 + ntk4 + (tv_words >> 2);
-    const u4v *ksrc = reinterpret_cast<const u4v *>(kg + k_a);
-    const u4v *vsrc = reinterpret_cast<const u4v *>(vg + v_a);
-    const u4v *tksrc = reinterpret_cast<const u4v *>(a.k.tail + tsel * rk);
-    const u4v *tvsrc = vq ? reinterpret_cast<const u4v *>(a.v.tail + tsel * rv)
-                          : reinterpret_cast<const u4v *>(vg + static_cast<int64_t>(nfull) * WV);
-    // source of 16-byte piece e (selects only, so the loads stay straight-line)
-    auto piece = [&](int e) -> const u4v * {
-        const u4v *p0 = e < nk4 ? ksrc + e : vsrc + (e - nk4);
-        const u4v *p1 = e < nk4 + nv4 + ntk4 ? tksrc + (e - nk4 - nv4) : tvsrc + (e - nk4 - nv4 - ntk4);
-        const u4v *pe = e < nk4 + nv4 ? p0 : p1;
-        return e < n4 ? pe : reinterpret_cast<const u4v *>(a.k.records);   // unused slot: a valid address
+    auto copy_tail = [&]() {
+        const u4v *tks = reinterpret_cast<const u4v *>(a.k.tail + tsel * rk);
+        const u4v *tvs = vq ? reinterpret_cast<const u4v *>(a.v.tail + tsel * rv)
+                            : reinterpret_cast<const u4v *>(vg + static_cast<int64_t>(nfull) * WV);
+        const int ntk4 = tk_words >> 2, n4 = ntk4 + (tv_words >> 2);
+        for (int c = wv; c * 64 < n4; c += kWaves) {
+            const int e = c * 64 + lane;
+            if (e < n4)
+                __builtin_amdgcn_global_load_lds(e < ntk4 ? tks + e : tvs + (e - ntk4), lds + tail_off + c * 1024, 16,
+                                                 0, 0);
+        }
     };
-    u4v buf[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-        if (u * 256 < n4) buf[u] = *piece(u * 256 + tid);     // wave-uniform guard
+    if (npass > 0) copy_pass(0);
+    else if (do_tail) copy_tail();
 
     // ---- 2. absorbed query qt = qs V_K^T q on MFMA: rows = query heads of
     //         this kv head, K = d, columns = 16-channel blocks of the fp16
-    //         channel-major key basis (wave w takes blocks w and w + 4)
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const int cb = wv + kWaves * x;
-        if (x == 0 ? own0 : own1) {
-            f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(qa[st].x, qa[st].y, qa[st].z, qa[st].w),
-                                                            as_h8(bb[x][st].x, bb[x][st].y, bb[x][st].z, bb[x][st].w),
-                                                            acc, 0, 0, 0);
-            const int c = 16 * cb + ln;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int hh = 4 * kb + v;
-                if (hh < g && c < rk) qt[hh * rk + c] = acc[v] * a.qscale;
-            }
-        }
-    }
+    //         channel-major key basis (wave w takes blocks w and w + 4); only
+    //         the waves that own a block load the query and the basis
     {
-        u4v *dst = reinterpret_cast<u4v *>(stage);
+        const int nbc = (rk + 15) >> 4;              // 16-channel blocks of qt (<= 8)
+        const bool own0 = wv < nbc, own1 = wv + kWaves < nbc;
+        if (own0) {
+            const int qrow = qi * a.Hq + h * g;
+            // rows ln >= g repeat a valid query; their MFMA output rows are never stored
+            const uint16_t *qsrc = a.q + static_cast<int64_t>(qrow + (ln < g ? ln : 0)) * kHeadDim + 8 * kb;
+            uint4 qa[4], bb[2][4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int e = u * 256 + tid;
-            if (u * 256 < n4 && e < n4) dst[e] = buf[u];
-        }
-        for (int base = 8 * 256; base < n4; base += 8 * 256) {
-            u4v more[8];
+            for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const uint4 *>(qsrc + 32 * st);
+            const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * rk * kHeadDim;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) more[u] = *piece(base + u * 256 + tid);
+            for (int x = 0; x < 2; ++x) {
+                if (x == 1 && !own1) break;
+                int c = 16 * (wv + kWaves * x) + ln;
+                c = c < rk ? c : rk - 1;              // clamped rows are never stored
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int e = base + u * 256 + tid;
-                if (e < n4) dst[e] = more[u];
+                for (int st = 0; st < 4; ++st)
+                    bb[x][st] = *reinterpret_cast<const uint4 *>(bt + static_cast<int64_t>(c) * kHeadDim + 32 * st +
+                                                                 8 * kb);
+            }
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                if (x == 1 && !own1) break;
+                f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(qa[st].x, qa[st].y, qa[st].z, qa[st].w),
+                                                                as_h8(bb[x][st].x, bb[x][st].y, bb[x][st].z,
+                                                                      bb[x][st].w),
+                                                                acc, 0, 0, 0);
+                const int c = 16 * (wv + kWaves * x) + ln;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int hh = 4 * kb + v;
+                    if (hh < g && c < rk) qt[hh * rk + c] = acc[v] * a.qscale;
+                }
             }
         }
     }
+    __builtin_amdgcn_s_waitcnt(0);                    // this wave's copies have landed
     __syncthreads();
 
-    // ---- 3. per-split tables in one pass (they read only the staged
-    //         records and qt); indices split by exact float reciprocals
-    const FastDiv div_nbk8(a.inv_nbk8), div_nbk4(a.inv_nbk4), div_rv(a.inv_rv);
-    // (a) score B operand: per k-step u and lane the block-diagonal fp16 qt
-    //     (channel order [c0,c4,c1,c5,..]); without the table, qt16 per
-    //     (head, channel block) and the main loop builds the operand
+    // ---- 3. score B operand: per k-step u and lane the block-diagonal fp16
+    //         qt (channel order [c0,c4,c1,c5,..]); without the table, qt16
+    //         per (head, channel block) and the main loop builds the operand
     if (L.use_btab) {
         for (int e = tid; e < nub * 64; e += 256) {
             const int u = e >> 6, l2 = e & 63, n2 = l2 & 15;
@@ -636,7 +646,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 #pragma unroll
             for (int idx = 0; idx < 8; ++idx) {
                 const int c = chan0 + (idx >> 1) + 4 * (idx & 1);
-                hv[idx] = static_cast<_Float16>(ok && c < chanend ? qrow[c] : 0.0f);
+                const float val = qrow[c < rk ? c : rk - 1];
+                hv[idx] = static_cast<_Float16>(ok && c < chanend ? val : 0.0f);
             }
             uint4 w;
             w.x = __builtin_bit_cast(uint32_t, (h2){hv[0], hv[1]});
@@ -646,6 +657,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             btab[e] = w;
         }
     } else {
+        const FastDiv div_nbk8(a.inv_nbk8);
         for (int e = tid; e < g * nbk * 8; e += 256) {
             const int hh = div_nbk8.quo(e), r2 = e - hh * nbk * 8;
             const int q = r2 >> 3, idx = r2 & 7;
@@ -657,35 +669,10 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                                                           : static_cast<_Float16>(0.0f);
         }
     }
-    // (b) K scale/zero pairs per (group, channel block): words 0..3 scale
-    //     pairs (k, k + 4), words 4..7 zero pairs; padding channels are 0
-    for (int e = tid; e < ntg * nbk * 4; e += 256) {
-        const int tg = div_nbk4.quo(e), r2 = e - tg * nbk * 4;
-        const int q = r2 >> 2, k = r2 & 3;
-        const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
-        const int chanend = q < nbh ? nhk : rk;
-        const uint32_t *rec = stage + koff + tg * WK + kmeta;
-        const uint32_t wa = chan0 + k < chanend ? rec[chan0 + k] : 0u;
-        const uint32_t wb = chan0 + k + 4 < chanend ? rec[chan0 + k + 4] : 0u;
-        uint32_t *dst = kpair + (tg * nbk + q) * 8;
-        dst[k] = perm_b32(wb, wa, 0x05040100u);
-        dst[4 + k] = perm_b32(wb, wa, 0x07060302u);
-    }
-    // (c) V per (group, channel): fp32 scale and zero - 1024 * scale, for
-    //     the value epilogue (the value MFMA runs on 1024 + code)
-    float *vsz = reinterpret_cast<float *>(vpair);
-    if (vq) {
-        for (int e = tid; e < ntg * rv; e += 256) {
-            const int tg = div_rv.quo(e), c = e - tg * rv;
-            const uint32_t mw = stage[voff + tg * WV + vmeta + c];
-            const float sc = h2f(mw), zr = h2f(mw >> 16);
-            vsz[2 * e] = sc;
-            vsz[2 * e + 1] = fmaf(-1024.0f, sc, zr);
-        }
-    }
     __syncthreads();
 
-    // ---- 4. main loop over token groups
+    // ---- 4. main loop: passes of PP token groups, wave w takes pass-relative
+    //         groups [w S, w S + S)
     const int slot_n = ln / g, head_n = ln - (ln / g) * g;
     const bool live_n = ln < NS;
     float m_run = -INFINITY, l_run = 0.0f;
@@ -694,7 +681,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     for (int nb = 0; nb < NBV; ++nb) oacc[nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
     // per-lane value-channel addressing (column c = 16 nb + ln, clamped)
     int vch[NBV], vw0[NBV], vw1[NBV], vs0[NBV], vwid[NBV], vwc[NBV];
-    uint32_t vcm[NBV], vbase[NBV];
+    uint32_t vcm[NBV];
     int row_slot[4];                                 // slot of value-output row 4*kb + v
 #pragma unroll
     for (int v = 0; v < 4; ++v) row_slot[v] = (4 * kb + v) / g;
@@ -713,14 +700,42 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         vwid[nb] = 4 * wc;
         vwc[nb] = wc;
         vcm[nb] = w4c ? 0x000F000Fu : 0x00030003u;
-        vbase[nb] = 0x64006400u;
     }
     const uint32_t kmagic = vgpr_const(0x64006400u), km4 = vgpr_const(0x000F000Fu),
                    km2 = vgpr_const(0x00030003u);
-    constexpr int per_iter = kWaves * S;
-    const int n_iter = (ntg + per_iter - 1) / per_iter;
-    for (int it = 0; it < n_iter; ++it) {
-        const int tb0 = (it * kWaves + wv) * S;      // split-relative group of slot 0
+    const FastDiv div_nbk4(a.inv_nbk4);
+    const int tb0 = wv * S;                          // pass-relative group of slot 0
+    for (int pi = 0; pi < npass; ++pi) {
+        if (pi + 1 < npass) copy_pass(pi + 1);       // into the other buffer
+        else if (do_tail) copy_tail();               // the last pass leaves buffer tb free
+        int nk4, nv4, koff, voff;
+        pass_words(pi, nk4, nv4, koff, voff);
+        const int npg = min(PP, ntg - pi * PP);      // groups in this pass (>= 1)
+        const int64_t g0 = jb + pi * PP;             // absolute group of pass group 0
+        const uint32_t *stage = reinterpret_cast<const uint32_t *>(lds + L.stage) + (pi & 1) * L.sb;
+
+        // (a) this wave's K scale/zero pairs per (slot, channel block):
+        //     words 0..3 scale pairs (k, k + 4), words 4..7 zero pairs;
+        //     padding channels are 0; slots past the pass repeat its last group
+        for (int e = lane; e < S * nbk * 4; e += 64) {
+            const int m = div_nbk4.quo(e), r2 = e - m * nbk * 4;
+            const int q = r2 >> 2, k = r2 & 3;
+            const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
+            const int chanend = q < nbh ? nhk : rk;
+            int tg = tb0 + m;
+            tg = tg < npg ? tg : npg - 1;
+            const uint32_t *rec = stage + koff + tg * WK + kmeta;
+            const uint32_t wa = chan0 + k < chanend ? rec[chan0 + k] : 0u;
+            const uint32_t wb = chan0 + k + 4 < chanend ? rec[chan0 + k + 4] : 0u;
+            uint32_t *dst = kpw + (m * nbk + q) * 8;
+            dst[k] = perm_b32(wb, wa, 0x05040100u);
+            dst[4 + k] = perm_b32(wb, wa, 0x07060302u);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // (b) scores
         f4 sacc0 = {0.0f, 0.0f, 0.0f, 0.0f}, sacc1 = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int u = 0; u < nub; ++u) {
             const int p = 4 * u + kb;
@@ -732,13 +747,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                 q = p / S;
                 j = p - q * S;
             }
-            // invalid pairs and groups past the split are read from a valid
+            // invalid pairs and groups past the pass are read from a valid
             // (clamped) record; their scores belong to masked streams
             int tg = tb0 + j;
-            tg = tg < ntg ? tg : ntg - 1;
+            tg = tg < npg ? tg : npg - 1;
             const int qc = q < nbk ? q : nbk - 1;
             const uint32_t *rec = stage + koff + tg * WK;
-            const uint4 *kp = reinterpret_cast<const uint4 *>(kpair + (tg * nbk + qc) * 8);
+            const uint4 *kp = reinterpret_cast<const uint4 *>(kpw + (j * nbk + qc) * 8);
             const uint4 sp = kp[0], zp = kp[1];
             uint4 bq;
             if (L.use_btab) {
@@ -771,8 +786,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bop, sacc1, 0, 0, 0);
         }
 
-        // online softmax of stream ln (rows 4*kb + v of both 16-token halves)
-        const bool sv = live_n && (tb0 + slot_n) < ntg;
+        // (c) online softmax of stream ln (rows 4*kb + v of both 16-token halves)
+        const bool sv = live_n && (tb0 + slot_n) < npg;
         const float sc[8] = {sacc0[0], sacc0[1], sacc0[2], sacc0[3], sacc1[0], sacc1[1], sacc1[2], sacc1[3]};
         float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
@@ -793,9 +808,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             }
             m_run = m_new;
         }
-        // weights of streams whose group is past the split never reach a
-        // value MFMA (that slot is skipped), so only the sums (l and P) are
-        // masked
+        // weights of streams whose group is past the pass never reach a
+        // value MFMA (their slot's A rows are zero), so only l is masked
         const float msafe = m_run == -INFINITY ? 0.0f : m_run;
         float pr[8];
 #pragma unroll
@@ -805,40 +819,63 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         const uint32_t pp0 = pack_rtz(pr[0], pr[4]), pp1 = pack_rtz(pr[1], pr[5]);
         const uint32_t pp2 = pack_rtz(pr[2], pr[6]), pp3 = pack_rtz(pr[3], pr[7]);
 
-        // values: one MFMA per slot and 16-channel block on exact codes
-        // (1024 + code in fp16); per-group scale and zero are applied in the
-        // epilogue: sum_t p (code s + z) = s (D - 1024 P) + z P, with the
-        // weight sum P = sum_t p of each stream from one more MFMA against a
-        // constant-one operand (so it sums exactly the fp16 weights used).
+        // (d) values: one MFMA per slot and 16-channel block on exact codes
+        //     (1024 + code in fp16); per-group scale and zero are applied in
+        //     the epilogue: sum_t p (code s + z) = s (D - 1024 P) + z P, with
+        //     the weight sum P = sum_t p of each stream from one more MFMA
+        //     against a constant-one operand (so it sums exactly the fp16
+        //     weights used).  fp16 value latents are read from memory, all
+        //     slots' loads issued before the first MFMA.
         f4 dacc[NBV];
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb) dacc[nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
         f4 dP = {0.0f, 0.0f, 0.0f, 0.0f};
         const f16x8 ones8 = as_h8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+        // fp16 value latents: with few (slot, block) pairs all loads are
+        // issued up front, else each slot's loads right before its MFMAs
+        constexpr bool kPreV = !VQ && S * NBV <= 8;
+        uint2 vlo[kPreV ? S : 1][NBV], vhi[kPreV ? S : 1][NBV];
+        if constexpr (kPreV) {
+#pragma unroll
+            for (int m = 0; m < S; ++m) {
+                const int tg = tb0 + m < npg ? tb0 + m : npg - 1;
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb) {
+                    const uint16_t *r16 = reinterpret_cast<const uint16_t *>(vg + (g0 + tg) * WV) + vch[nb] * 32;
+                    vlo[m][nb] = *reinterpret_cast<const uint2 *>(r16 + 4 * kb);
+                    vhi[m][nb] = *reinterpret_cast<const uint2 *>(r16 + 16 + 4 * kb);
+                }
+            }
+        }
 #pragma unroll
         for (int m = 0; m < S; ++m) {
-            const int tg = tb0 + m;
-            if (tg >= ntg) break;
+            if (tb0 + m >= npg) break;               // wave-uniform
             const bool arow = live_n && slot_n == m;
             const f16x8 aop = arow ? as_h8(pp0, pp1, pp2, pp3) : as_h8(0u, 0u, 0u, 0u);
             if (vq) dP = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, ones8, dP, 0, 0, 0);
 #pragma unroll
             for (int nb = 0; nb < NBV; ++nb) {
                 uint32_t bp0, bp1, bp2, bp3;
-                if (vq) {
-                    const uint32_t *rec = stage + voff + tg * WV;
+                if constexpr (VQ) {
+                    const uint32_t *rec = stage + voff + (tb0 + m) * WV;
                     const uint32_t X = __builtin_amdgcn_ubfe(rec[vw0[nb]], vs0[nb], vwid[nb]) |
                                        (__builtin_amdgcn_ubfe(rec[vw1[nb]], vs0[nb], vwid[nb]) << 16);
                     const int wc = vwc[nb];
-                    bp0 = (X & vcm[nb]) | vbase[nb];
-                    bp1 = ((X >> wc) & vcm[nb]) | vbase[nb];
-                    bp2 = ((X >> (2 * wc)) & vcm[nb]) | vbase[nb];
-                    bp3 = ((X >> (3 * wc)) & vcm[nb]) | vbase[nb];
+                    bp0 = (X & vcm[nb]) | kmagic;
+                    bp1 = ((X >> wc) & vcm[nb]) | kmagic;
+                    bp2 = ((X >> (2 * wc)) & vcm[nb]) | kmagic;
+                    bp3 = ((X >> (3 * wc)) & vcm[nb]) | kmagic;
                 } else {
-                    const uint16_t *r16 =
-                        reinterpret_cast<const uint16_t *>(vg + static_cast<int64_t>(jb + tg) * WV) + vch[nb] * 32;
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(r16 + 4 * kb);
-                    const uint2 hi = *reinterpret_cast<const uint2 *>(r16 + 16 + 4 * kb);
+                    uint2 lo, hi;
+                    if constexpr (kPreV) {
+                        lo = vlo[m][nb];
+                        hi = vhi[m][nb];
+                    } else {
+                        const uint16_t *r16 =
+                            reinterpret_cast<const uint16_t *>(vg + (g0 + tb0 + m) * WV) + vch[nb] * 32;
+                        lo = *reinterpret_cast<const uint2 *>(r16 + 4 * kb);
+                        hi = *reinterpret_cast<const uint2 *>(r16 + 16 + 4 * kb);
+                    }
                     bp0 = perm_b32(hi.x, lo.x, 0x05040100u);
                     bp1 = perm_b32(hi.x, lo.x, 0x07060302u);
                     bp2 = perm_b32(hi.y, lo.y, 0x05040100u);
@@ -848,25 +885,32 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             }
         }
         if (vq) {
-            // P per output row 4*kb + v (stream); rows of invalid groups are 0
-            const float Pv[4] = {dP[0], dP[1], dP[2], dP[3]};
+            // (e) epilogue per output row 4*kb + v (stream): the row's group
+            //     scale s and z - 1024 s from its metadata word; rows of
+            //     groups past the pass have D = P = 0
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 int tgr = tb0 + row_slot[v];
-                tgr = tgr < ntg ? tgr : ntg - 1;
+                tgr = tgr < npg ? tgr : npg - 1;
+                const uint32_t *meta = stage + voff + tgr * WV + vmeta;
 #pragma unroll
                 for (int nb = 0; nb < NBV; ++nb) {
-                    const float2 sz = *reinterpret_cast<const float2 *>(vsz + 2 * (tgr * rv + vch[nb]));
-                    oacc[nb][v] = fmaf(sz.x, dacc[nb][v], fmaf(sz.y, Pv[v], oacc[nb][v]));
+                    const uint32_t mw = meta[vch[nb]];
+                    const float sc16 = h2f(mw);
+                    const float zr = fmaf(-1024.0f, sc16, h2f(mw >> 16));
+                    oacc[nb][v] = fmaf(sc16, dacc[nb][v], fmaf(zr, dP[v], oacc[nb][v]));
                 }
             }
         } else {
 #pragma unroll
             for (int nb = 0; nb < NBV; ++nb) oacc[nb] += dacc[nb];
         }
+        __builtin_amdgcn_s_waitcnt(0);                // the next pass's copies have landed
+        __syncthreads();                              // and every wave is done with this buffer
     }
 
     // ---- 5. per-wave stream results to LDS
+    const FastDiv div_rv(a.inv_rv);
     float lsum = l_run;
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
@@ -890,7 +934,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     //         thread (head tid / 32, token tid % 32), softmax within the 32
     //         lanes of a head
     if (do_tail) {
-        const float *tk = reinterpret_cast<const float *>(stage + tk_off);
+        const float *tk = reinterpret_cast<const float *>(tails);
         const int hh = tid >> 5, t = tid & 31;
         const bool ok = hh < g && t < ntail;
         float sc = -INFINITY;
@@ -916,10 +960,10 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             const int hv = div_rv.quo(e), c = e - hv * rv;
             float acc = 0.0f;
             if (vq) {
-                const float *tv = reinterpret_cast<const float *>(stage + tv_off);
+                const float *tv = reinterpret_cast<const float *>(tails + tk_words);
                 for (int t2 = 0; t2 < ntail; ++t2) acc = fmaf(tp[hv * 32 + t2], tv[t2 * rv + c], acc);
             } else {
-                const _Float16 *tv = reinterpret_cast<const _Float16 *>(stage + tv_off) + c * 32;
+                const _Float16 *tv = reinterpret_cast<const _Float16 *>(tails + tk_words) + c * 32;
                 for (int t2 = 0; t2 < ntail; ++t2) acc = fmaf(tp[hv * 32 + t2], static_cast<float>(tv[t2]), acc);
             }
             ost[(kWaves * 16 + hv) * rv + c] = acc;
@@ -934,7 +978,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     //         w, w + 4 with its lanes over streams.
     const int nsw = kWaves * S + (do_tail ? 1 : 0);   // <= 65
     float *wts = ts;                                   // [g][65]
-    float *part = a.partial + (static_cast<int64_t>(i) * a.Hq + h * g) * kMaxSplits * (rv + 2) +
+    float *part = a.partial + (static_cast<int64_t>(qi) * a.Hq + h * g) * kMaxSplits * (rv + 2) +
                   static_cast<int64_t>(s) * (rv + 2);
     const int64_t head_stride = static_cast<int64_t>(kMaxSplits) * (rv + 2);
     for (int hh = wv; hh < g; hh += kWaves) {
@@ -984,8 +1028,8 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
     const int qh = blockIdx.x, i = blockIdx.y;   // grid (Hq, B)
     // all argument loads issued together (one scalar round trip)
     asm volatile("" ::"s"(a.partial), "s"(a.out), "s"(a.v.basis), "s"(a.v.mu), "s"(a.v.r), "s"(a.gqa),
-                 "s"(a.hpg), "s"(a.Hq), "s"(a.row[i].nsplit));
-    const int h = qh / a.gqa, grp = h / a.hpg, ns = a.row[i].nsplit, rv = a.v.r;
+                 "s"(a.hpg), "s"(a.Hq), "s"(a.nsplit_call[i]));
+    const int h = qh / a.gqa, grp = h / a.hpg, ns = a.nsplit_call[i], rv = a.v.r;
     const int np = ns * (rv + 2), npa = (np + 3) & ~3;
     float *pl = cl;                            // [ns][rv + 2]: m, l, o_lat
     float *bl = cl + npa;                      // [D][rv] value basis
@@ -1085,30 +1129,35 @@ hipError_t launch_encode(const EncodeArgs &a, int max_touched, hipStream_t s) {
     return hipGetLastError();
 }
 
-size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int chunk, int words_k, int words_v, bool vq) {
-    return static_cast<size_t>(attend_lds(gqa, r_k, n_hi_k, r_v, chunk, words_k, words_v, vq).total);
+size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int words_k, int words_v, bool vq) {
+    return static_cast<size_t>(attend_lds(gqa, r_k, n_hi_k, r_v, words_k, words_v, vq).total);
 }
 
-template <int G, int NBV>
+template <int G, int NBV, bool VQ>
 static hipError_t launch_attend_t(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
     static bool configured = false;
     if (!configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<G, NBV>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<G, NBV, VQ>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((attend_kernel<G, NBV>), dim3(a.nsplit_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
+    hipLaunchKernelGGL((attend_kernel<G, NBV, VQ>), dim3(a.nsplit_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
     return hipGetLastError();
+}
+
+template <int G, bool VQ>
+static hipError_t launch_attend_v(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+    const int nbv = (a.v.r + 15) / 16;
+    if (nbv <= 1) return launch_attend_t<G, 1, VQ>(a, lds_bytes, s);
+    if (nbv <= 2) return launch_attend_t<G, 2, VQ>(a, lds_bytes, s);
+    if (nbv <= 4) return launch_attend_t<G, 4, VQ>(a, lds_bytes, s);
+    return launch_attend_t<G, 8, VQ>(a, lds_bytes, s);
 }
 
 template <int G>
 static hipError_t launch_attend_g(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
-    const int nbv = (a.v.r + 15) / 16;
-    if (nbv <= 1) return launch_attend_t<G, 1>(a, lds_bytes, s);
-    if (nbv <= 2) return launch_attend_t<G, 2>(a, lds_bytes, s);
-    if (nbv <= 4) return launch_attend_t<G, 4>(a, lds_bytes, s);
-    return launch_attend_t<G, 8>(a, lds_bytes, s);
+    return a.v.fp16_latents ? launch_attend_v<G, false>(a, lds_bytes, s) : launch_attend_v<G, true>(a, lds_bytes, s);
 }
 
 hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
