@@ -433,7 +433,7 @@ PALU_API int palu_encode_append(palu_cache *c, const void *k, const void *v, con
         ea.hpg = c->hpg;
         ea.hi_bit = c->cfg.hi_bit;
         ea.lo_bit = c->cfg.lo_bit;
-        int max_touched = 0;
+        int max_units = 0;   // group pairs touched by a row (one wave each)
         for (int i = 0; i < nb; ++i) {
             const int b = b0 + i;
             const int slot = seq_ids ? seq_ids[b] : b;
@@ -451,10 +451,10 @@ PALU_API int palu_encode_append(palu_cache *c, const void *k, const void *v, con
                 (o + n) / kTokGroup != o / kTokGroup)
                 sel_new = 1 - sel_new;
             ea.sel_new[i] = sel_new;
-            if (n > 0) max_touched = std::max(max_touched, (o + n - 1) / kTokGroup - o / kTokGroup + 1);
+            if (n > 0) max_units = std::max(max_units, (o + n - 1) / kTokGroup / 2 - o / kTokGroup / 2 + 1);
         }
-        if (max_touched > 0) {
-            hipError_t e = launch_encode(ea, max_touched, s);
+        if (max_units > 0) {
+            hipError_t e = launch_encode(ea, max_units, s);
             if (e != hipSuccess) return hip_fail(e, "encode launch");
         }
         for (int i = 0; i < nb; ++i) {

@@ -91,7 +91,8 @@ size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int words_k, int 
 // Launchers (defined in palu_kernels.hip).  They return the launch status.
 hipError_t launch_gram(const GramArgs &a, hipStream_t s);
 hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s);
-hipError_t launch_encode(const EncodeArgs &a, int max_touched, hipStream_t s);
+// One wave per (pair of touched token groups, call row x head, tensor).
+hipError_t launch_encode(const EncodeArgs &a, int max_units, hipStream_t s);
 // Grid (nsplit_max, Hkv, B): one workgroup per (split, kv head, row).
 hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s);

@@ -71,6 +71,15 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
+// floor(e / d) for 0 <= e < 2^21 and d >= 1 from a correctly rounded fp32
+// reciprocal: (e + 1/2) / d lies at least 1/(2d) away from an integer, and
+// the two roundings perturb it by at most (e + 1/2) / d * 2^-23 < 1/(2d).
+struct FastDiv {
+    float inv;   // the correctly rounded fp32 1 / d
+    __device__ explicit FastDiv(float inv_d) : inv(inv_d) {}
+    __device__ int quo(int e) const { return static_cast<int>((static_cast<float>(e) + 0.5f) * inv); }
+};
+
 // ---------------------------------------------------------------- Gram ----
 //
 // Workgroup (block, group g, tensor) owns rows [block*rpb, (block+1)*rpb) of
@@ -168,157 +177,221 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(GramReduceArgs a) {
 
 // -------------------------------------------------------------- encode ----
 //
-// Workgroup (touched group u, call row bi * H + head h, tensor tz).  The
-// group index is j = old_len / 32 + u; its new positions are
-// [max(32j, old), min(32j + 32, old + n)).
+// One wave per pair of token groups (64 positions, lane = position) of one
+// (call row, kv head, tensor); four independent waves per workgroup, no
+// workgroup barriers.  Wave unit u of a row covers groups 2 (j0/2 + u) and
+// 2 (j0/2 + u) + 1, j0 = old_len / 32.  A lane's position is new (in
+// [old, old + n)), old (an earlier position of group j0, read back from the
+// tail buffer) or outside the call.  Per lane y_d = float(x_d) - mu_d in
+// fp32, then per channel the fixed-order chain acc = fma(y_d, V[d][c], acc),
+// d = 0..D-1; the group's basis (rows padded to a multiple of 4 floats) and
+// mean are staged in LDS once per workgroup and read as broadcasts.  The 32
+// lanes of a complete group quantise it (min/max by lane reductions, IEEE
+// division, round-half-even) and OR their codes into an LDS copy of the
+// record at the layout's bit positions; an incomplete group's new latents go
+// to the tail buffer; fp16 value latents are stored directly.
+
+constexpr int kEncWaves = 4;
+
+// max / min over the 32 lanes of each half-wave
+__device__ __forceinline__ float half_max(float v) {
+    v = row_max(v);
+    return fmaxf(v, __shfl_xor(v, 16));
+}
+__device__ __forceinline__ float half_min(float v) { return -half_max(-v); }
+
+struct EncLane {
+    int t, half;                // token in its group, which group of the pair
+    bool is_new, is_old, complete, touched;
+};
+
+// Quantise / store channel c of this lane's latent (see the section comment).
+__device__ __forceinline__ void encode_channel(const EncodeArgs &a, const TensorDev &T, const EncLane &e, int c,
+                                               float lat, const float *told, float *tnew, uint32_t *rec_lds,
+                                               uint16_t *rec16, int layout, bool any_complete) {
+    const int r = T.r, n_hi = T.n_hi, n_lo = r - n_hi;
+    // fp16 latents have no tail buffer (told and tnew are null): only new
+    // positions are stored
+    if (T.fp16_latents) {
+        if (e.is_new) rec16[c * 32 + e.t] = static_cast<uint16_t>(f2h_bits(lat));
+        return;
+    }
+    if (e.is_old) lat = told[e.t * r + c];
+    if (!any_complete) {                             // wave-uniform: no group completes
+        if (e.touched && e.is_new) tnew[e.t * r + c] = lat;
+        return;
+    }
+    // every lane takes part in the half-wave reductions; only complete
+    // groups use the result
+    const float mn = half_min(lat), mx = half_max(lat);
+    if (e.complete) {
+        const bool hi = c < n_hi;
+        const float levels = static_cast<float>((1 << (hi ? a.hi_bit : a.lo_bit)) - 1);
+        const float scale = (mx - mn) / levels;
+        int q = 0;
+        if (scale > 0.0f) {
+            float uq = rintf((lat - mn) / scale);
+            uq = uq < 0.0f ? 0.0f : (uq > levels ? levels : uq);
+            q = static_cast<int>(uq);
+        }
+        int bit;
+        if (hi) bit = layout == 0 ? e.t * 4 * n_hi + 4 * c : 128 * c + 4 * e.t;
+        else {
+            const int cl = c - n_hi;
+            bit = 128 * n_hi + (layout == 0 ? e.t * 2 * n_lo + 2 * cl : 64 * cl + 2 * e.t);
+        }
+        if (q) atomicOr(rec_lds + (bit >> 5), static_cast<uint32_t>(q) << (bit & 31));
+        if (e.t == 0) rec_lds[4 * n_hi + 2 * n_lo + c] = f2h_bits(scale) | (f2h_bits(mn) << 16);
+    } else if (e.touched && e.is_new) {
+        tnew[e.t * r + c] = lat;
+    }
+}
+
+// W consecutive channels c0.. of this lane's latent (W a multiple of 4): W
+// independent fixed-order chains over d = 0..D-1, run in four quarters of
+// 32 rows so that only 32 values y_d = float(x_d) - mu_d are live at a time;
+// basis rows are read from LDS as 16-byte broadcasts.
+template <int W>
+__device__ __forceinline__ void project_to_lds(const uint16_t *xrow, const float *msh, const float *vsh, int rp,
+                                               int c0, float *lat, int lane) {
+    float l[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) l[k] = 0.0f;
+    // the next quarter's 64 bytes are loaded while this one is computed
+    uint4 xa[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xa[k] = *reinterpret_cast<const uint4 *>(xrow + 8 * k);
+    for (int q = 0; q < kHeadDim / 32; ++q) {
+        uint4 xb[4];
+        const int qn = q + 1 < kHeadDim / 32 ? q + 1 : q;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xb[k] = *reinterpret_cast<const uint4 *>(xrow + 32 * qn + 8 * k);
+        float y[32];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t wq[4] = {xa[k].x, xa[k].y, xa[k].z, xa[k].w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                y[8 * k + 2 * m] = h2f(wq[m]) - msh[32 * q + 8 * k + 2 * m];
+                y[8 * k + 2 * m + 1] = h2f(wq[m] >> 16) - msh[32 * q + 8 * k + 2 * m + 1];
+            }
+        }
+#pragma unroll
+        for (int dd = 0; dd < 32; ++dd) {
+            const float *vrow = vsh + (32 * q + dd) * rp + c0;
+#pragma unroll
+            for (int k = 0; k < W; k += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(vrow + k);
+                l[k] = __builtin_fmaf(y[dd], v.x, l[k]);
+                l[k + 1] = __builtin_fmaf(y[dd], v.y, l[k + 1]);
+                l[k + 2] = __builtin_fmaf(y[dd], v.z, l[k + 2]);
+                l[k + 3] = __builtin_fmaf(y[dd], v.w, l[k + 3]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xa[k] = xb[k];
+    }
+#pragma unroll
+    for (int k = 0; k < W; ++k) lat[k * 64 + lane] = l[k];
+}
+
+// Dynamic LDS of one encode workgroup: basis [D][rp] + mean [D] + per wave
+// two record buffers (none for fp16 latents) and a [32 channels][64 lanes]
+// latent buffer.
+__host__ __device__ inline int encode_rec_words(int words, bool fp16) { return fp16 ? 0 : words; }
+__host__ __device__ inline int encode_lds_bytes(int r, int words, bool fp16) {
+    const int rp = (r + 3) & ~3;
+    return (kHeadDim * rp + kHeadDim + kEncWaves * (2 * encode_rec_words(words, fp16) + 32 * 64)) * 4;
+}
 
 __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
-    const int u = blockIdx.x;
+    extern __shared__ __align__(16) float esh[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int u = blockIdx.x * kEncWaves + wv;
     const int bi = blockIdx.y / a.H, h = blockIdx.y - (blockIdx.y / a.H) * a.H;
     const int tz = blockIdx.z;
     const int o = a.old_len[bi], n = a.n_new[bi];
-    if (n <= 0) return;
-    const int j0 = o >> 5, jl = (o + n - 1) >> 5, j = j0 + u;
-    if (j > jl) return;
+    if (n <= 0) return;                              // whole workgroup
+    const int j0 = o >> 5, jl = (o + n - 1) >> 5;
+    if (2 * ((j0 >> 1) + blockIdx.x * kEncWaves) > jl) return;   // whole workgroup
     const TensorDev &T = tz ? a.t[1] : a.t[0];
-    const int r = T.r, n_hi = T.n_hi, n_lo = T.r - T.n_hi;
-    const int g = h / a.hpg, slot = a.slot[bi], tid = threadIdx.x;
-    const int pb = 32 * j > o ? 32 * j : o;
-    const int pe = 32 * j + 32 < o + n ? 32 * j + 32 : o + n;
-    const bool complete = (o + n) >= 32 * j + 32;
+    const int r = T.r, rp = (r + 3) & ~3, W = T.words;
+    const int grp = h / a.hpg, slot = a.slot[bi];
 
-    __shared__ float ys[kHeadDim][33];       // (x - mu) transposed: [d][t]
-    __shared__ float vs[kHeadDim][32];       // basis columns chunk [d][c]
-    __shared__ float lat[32][kHeadDim + 1];  // latents [t][c]
-    __shared__ uint8_t codes[32][kHeadDim];
-    __shared__ uint32_t meta[kHeadDim];
-
-    // 1. y = float(x) - mu for the new tokens
-    const uint16_t *xin = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim;
-    const float *mu = T.mu + g * kHeadDim;
-    for (int e = tid; e < 32 * 16; e += 256) {
-        const int t = e >> 4, dc = e & 15;
-        const int p = 32 * j + t;
-        if (p >= pb && p < pe) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(xin + static_cast<int64_t>(p - o) * kHeadDim + dc * 8);
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-            for (int q = 0; q < 4; ++q) {
-                const int d = dc * 8 + 2 * q;
-                ys[d][t] = h2f(wv[q]) - mu[d];
-                ys[d + 1][t] = h2f(wv[q] >> 16) - mu[d + 1];
-            }
+    // 0. the group's basis (rows padded to rp floats) and mean -> LDS
+    float *vsh = esh;
+    float *msh = esh + kHeadDim * rp;
+    {
+        const float *vb = T.basis + static_cast<int64_t>(grp) * kHeadDim * r;
+        const FastDiv div_rp(1.0f / static_cast<float>(rp));
+        for (int e = tid; e < kHeadDim * rp; e += 256) {
+            const int d = div_rp.quo(e), c = e - d * rp;
+            vsh[e] = c < r ? vb[d * r + c] : 0.0f;
         }
+        if (tid < kHeadDim) msh[tid] = T.mu[grp * kHeadDim + tid];
+    }
+    __syncthreads();
+    const int jp = (j0 >> 1) + u;                    // group pair of this wave
+    if (2 * jp > jl) return;                         // wave-uniform; no barrier follows
+
+    const int p = 64 * jp + lane;                    // this lane's position
+    EncLane e;
+    const int j = p >> 5;
+    e.t = p & 31;
+    e.half = lane >> 5;
+    e.is_new = p >= o && p < o + n;
+    e.is_old = p < o && j == j0;
+    e.touched = j >= j0 && j <= jl;
+    e.complete = e.touched && o + n >= 32 * j + 32;
+    // complete groups that get a quantised record (fp16 latents have none)
+    const bool any_complete = !T.fp16_latents && __any(e.complete);
+    const int64_t head_base = static_cast<int64_t>(slot) * a.H + h;
+
+    const int WR = encode_rec_words(W, T.fp16_latents);
+    uint32_t *rec_lds = reinterpret_cast<uint32_t *>(msh + kHeadDim) + (wv * 2 + e.half) * WR;
+    float *lat = msh + kHeadDim + kEncWaves * 2 * WR + wv * 32 * 64;   // this wave's [32][64]
+    if (any_complete) {
+        for (int w = e.t; w < W; w += 32) rec_lds[w] = 0u;
     }
 
-    // 2. latents: acc = fma(y_d, V[d][c], acc) for d = 0..D-1, in order
-    const float *basis = T.basis + static_cast<int64_t>(g) * kHeadDim * r;
+    // 1. this lane's input row (a valid row is read for every lane; only
+    //    new positions use theirs)
+    const int row = e.is_new ? p - o : 0;
+    const uint16_t *xrow = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim +
+                           static_cast<int64_t>(row) * kHeadDim;
+
+    // 2. latents in chunks of up to 32 channels (one fma chain per channel),
+    //    parked in LDS, then quantised / stored channel by channel
+    const float *told = T.fp16_latents ? nullptr : T.tail + (head_base * 2 + a.sel_old[bi]) * 32 * r;
+    float *tnew = T.fp16_latents ? nullptr : T.tail + (head_base * 2 + a.sel_new[bi]) * 32 * r;
+    uint16_t *rec16 = reinterpret_cast<uint16_t *>(T.records + head_base * T.head_stride +
+                                                   static_cast<int64_t>(j) * W);
     for (int c0 = 0; c0 < r; c0 += 32) {
         const int nc = r - c0 < 32 ? r - c0 : 32;
-        __syncthreads();
-        for (int e = tid; e < kHeadDim * 32; e += 256) {
-            const int d = e >> 5, c = e & 31;
-            vs[d][c] = c < nc ? basis[d * r + c0 + c] : 0.0f;
+        switch ((nc + 3) >> 2) {
+            case 1: project_to_lds<4>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 2: project_to_lds<8>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 3: project_to_lds<12>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 4: project_to_lds<16>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 5: project_to_lds<20>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 6: project_to_lds<24>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 7: project_to_lds<28>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            default: project_to_lds<32>(xrow, msh, vsh, rp, c0, lat, lane); break;
         }
-        __syncthreads();
-        const int t = tid & 31, cq = tid >> 5;
-        const int p = 32 * j + t;
-        if (p >= pb && p < pe && 4 * cq < nc) {
-            float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-            for (int d = 0; d < kHeadDim; ++d) {
-                const float y = ys[d][t];
-                const float4 v = *reinterpret_cast<const float4 *>(&vs[d][4 * cq]);
-                a0 = __builtin_fmaf(y, v.x, a0);
-                a1 = __builtin_fmaf(y, v.y, a1);
-                a2 = __builtin_fmaf(y, v.z, a2);
-                a3 = __builtin_fmaf(y, v.w, a3);
-            }
-            const int c = c0 + 4 * cq;
-            lat[t][c] = a0;
-            if (4 * cq + 1 < nc) lat[t][c + 1] = a1;
-            if (4 * cq + 2 < nc) lat[t][c + 2] = a2;
-            if (4 * cq + 3 < nc) lat[t][c + 3] = a3;
-        }
+        for (int k = 0; k < nc; ++k)
+            encode_channel(a, T, e, c0 + k, lat[k * 64 + lane], told, tnew, rec_lds, rec16, tz, any_complete);
     }
-    __syncthreads();
 
-    const int64_t head_base = (static_cast<int64_t>(slot) * a.H + h);
-    if (T.fp16_latents) {
-        uint16_t *rec16 = reinterpret_cast<uint16_t *>(T.records + head_base * T.head_stride +
-                                                       static_cast<int64_t>(j) * T.words);
-        for (int e = tid; e < 32 * r; e += 256) {
-            const int c = e >> 5, t = e & 31;
-            const int p = 32 * j + t;
-            if (p >= pb && p < pe) rec16[c * 32 + t] = static_cast<uint16_t>(f2h_bits(lat[t][c]));
+    // 3. complete groups: LDS record -> memory
+    if (any_complete) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (e.complete) {
+            uint32_t *rec = T.records + head_base * T.head_stride + static_cast<int64_t>(j) * W;
+            for (int w = e.t; w < W; w += 32) rec[w] = rec_lds[w];
         }
-        return;
-    }
-    if (!complete) {
-        float *tl = T.tail + (head_base * 2 + a.sel_new[bi]) * 32 * r;
-        for (int e = tid; e < 32 * r; e += 256) {
-            const int t = e / r, c = e - (e / r) * r;
-            const int p = 32 * j + t;
-            if (p >= pb && p < pe) tl[t * r + c] = lat[t][c];
-        }
-        return;
-    }
-    // 3. the group is complete: older latents of the group come from the tail
-    if (j == j0 && (o & 31)) {
-        const float *tl = T.tail + (head_base * 2 + a.sel_old[bi]) * 32 * r;
-        const int nold = o & 31;
-        for (int e = tid; e < nold * r; e += 256) {
-            const int t = e / r, c = e - (e / r) * r;
-            lat[t][c] = tl[t * r + c];
-        }
-    }
-    __syncthreads();
-    // 4. min/max quantiser per channel
-    for (int c = tid; c < r; c += 256) {
-        const int bits = c < n_hi ? a.hi_bit : a.lo_bit;
-        const float levels = static_cast<float>((1 << bits) - 1);
-        float mn = lat[0][c], mx = lat[0][c];
-        for (int t = 1; t < 32; ++t) {
-            const float v = lat[t][c];
-            mn = v < mn ? v : mn;
-            mx = v > mx ? v : mx;
-        }
-        const float scale = (mx - mn) / levels;
-        for (int t = 0; t < 32; ++t) {
-            int q = 0;
-            if (scale > 0.0f) {
-                float uq = rintf((lat[t][c] - mn) / scale);
-                uq = uq < 0.0f ? 0.0f : (uq > levels ? levels : uq);
-                q = static_cast<int>(uq);
-            }
-            codes[t][c] = static_cast<uint8_t>(q);
-        }
-        meta[c] = f2h_bits(scale) | (f2h_bits(mn) << 16);
-    }
-    __syncthreads();
-    // 5. pack: each thread assembles whole words
-    uint32_t *rec = T.records + head_base * T.head_stride + static_cast<int64_t>(j) * T.words;
-    for (int wd = tid; wd < T.words; wd += 256) {
-        uint32_t word = 0;
-        if (wd < 4 * n_hi) {
-            for (int m = 0; m < 8; ++m) {
-                const int pos = 32 * wd + 4 * m;
-                int t, c;
-                if (tz == 0) { t = pos / (4 * n_hi); c = (pos - t * 4 * n_hi) >> 2; }
-                else { c = pos >> 7; t = (pos & 127) >> 2; }
-                word |= static_cast<uint32_t>(codes[t][c]) << (4 * m);
-            }
-        } else if (wd < 4 * n_hi + 2 * n_lo) {
-            const int wl = wd - 4 * n_hi;
-            for (int m = 0; m < 16; ++m) {
-                const int pos = 32 * wl + 2 * m;
-                int t, c;
-                if (tz == 0) { t = pos / (2 * n_lo); c = n_hi + ((pos - t * 2 * n_lo) >> 1); }
-                else { c = n_hi + (pos >> 6); t = (pos & 63) >> 1; }
-                word |= static_cast<uint32_t>(codes[t][c]) << (2 * m);
-            }
-        } else {
-            word = meta[wd - 4 * n_hi - 2 * n_lo];
-        }
-        rec[wd] = word;
     }
 }
 
@@ -410,14 +483,6 @@ __host__ __device__ inline AttendLds attend_lds(int g, int rk, int nhk, int rv, 
     return L;
 }
 
-// floor(e / d) for 0 <= e < 2^21 and d >= 1 from a correctly rounded fp32
-// reciprocal: (e + 1/2) / d lies at least 1/(2d) away from an integer, and
-// the two roundings perturb it by at most (e + 1/2) / d * 2^-23 < 1/(2d).
-struct FastDiv {
-    float inv;   // the correctly rounded fp32 1 / d, computed on the host
-    __device__ explicit FastDiv(float inv_d) : inv(inv_d) {}
-    __device__ int quo(int e) const { return static_cast<int>((static_cast<float>(e) + 0.5f) * inv); }
-};
 
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
     return __builtin_amdgcn_perm(hi, lo, sel);
@@ -1124,8 +1189,18 @@ hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_encode(const EncodeArgs &a, int max_touched, hipStream_t s) {
-    hipLaunchKernelGGL(encode_kernel, dim3(max_touched, a.B * a.H, 2), dim3(256), 0, s, a);
+hipError_t launch_encode(const EncodeArgs &a, int max_units, hipStream_t s) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(encode_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int l0 = encode_lds_bytes(a.t[0].r, a.t[0].words, a.t[0].fp16_latents),
+              l1 = encode_lds_bytes(a.t[1].r, a.t[1].words, a.t[1].fp16_latents);
+    hipLaunchKernelGGL(encode_kernel, dim3((max_units + kEncWaves - 1) / kEncWaves, a.B * a.H, 2), dim3(256),
+                       static_cast<size_t>(l0 > l1 ? l0 : l1), s, a);
     return hipGetLastError();
 }
 
