@@ -73,9 +73,10 @@ void tridiagonalize(double *a, int n, double *d, double *e, double *q) {
 }
 
 // Implicit-shift QL on the tridiagonal (d, e); the rotations are applied to
-// the columns of z (which enters holding Q).  Returns false on no
+// the rows of zt (which enters holding Q^T, so row i is column i of Q and the
+// two rows a rotation touches are contiguous).  Returns false on no
 // convergence.
-bool tridiagonal_ql(double *d, double *e, int n, double *z) {
+bool tridiagonal_ql(double *d, double *e, int n, double *zt) {
     for (int l = 0; l < n; ++l) {
         int iter = 0;
         for (;;) {
@@ -111,11 +112,11 @@ bool tridiagonal_ql(double *d, double *e, int n, double *z) {
                 p = s * r;
                 d[i + 1] = g + p;
                 g = c * r - b;
+                double *zi = zt + i * n, *zj = zt + (i + 1) * n;
                 for (int k = 0; k < n; ++k) {
-                    double *zr = z + k * n;
-                    const double t = zr[i + 1];
-                    zr[i + 1] = s * zr[i] + c * t;
-                    zr[i] = c * zr[i] - s * t;
+                    const double t = zj[k];
+                    zj[k] = s * zi[k] + c * t;
+                    zi[k] = c * zi[k] - s * t;
                 }
             }
             if (underflow) continue;
@@ -130,9 +131,14 @@ bool tridiagonal_ql(double *d, double *e, int n, double *z) {
 }  // namespace
 
 bool sym_eigen(double *a, int n, double *w, double *z) {
-    std::vector<double> e(n > 0 ? n : 1);
+    std::vector<double> e(n > 0 ? n : 1), zt(static_cast<size_t>(n) * n);
     tridiagonalize(a, n, w, e.data(), z);
-    return tridiagonal_ql(w, e.data(), n, z);
+    for (int i = 0; i < n; ++i)
+        for (int k = 0; k < n; ++k) zt[static_cast<size_t>(i) * n + k] = z[static_cast<size_t>(k) * n + i];
+    if (!tridiagonal_ql(w, e.data(), n, zt.data())) return false;
+    for (int i = 0; i < n; ++i)
+        for (int k = 0; k < n; ++k) z[static_cast<size_t>(k) * n + i] = zt[static_cast<size_t>(i) * n + k];
+    return true;
 }
 
 }  // namespace palu

@@ -8,6 +8,7 @@
 #include <cstring>
 #include <numeric>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "palu.h"
@@ -296,7 +297,38 @@ PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t
 
     const int D = c->D;
     const double N = static_cast<double>(n_rows);
-    std::vector<double> cov(D * D), w(D), z(D * D);
+    // scatter matrices about the mean, X^T X - s s^T / N, and their
+    // eigendecompositions: the 2 G (tensor, group) problems are independent
+    // and run on host threads
+    const int nprob = 2 * c->G;
+    std::vector<double> covs(static_cast<size_t>(nprob) * D * D), ws(static_cast<size_t>(nprob) * D),
+        zs(static_cast<size_t>(nprob) * D * D);
+    for (int pb = 0; pb < nprob; ++pb) {
+        const double *G2 = gram.data() + static_cast<size_t>(pb) * kGramElems;
+        const double *sum = G2 + D * D;
+        double *cov = covs.data() + static_cast<size_t>(pb) * D * D;
+        for (int i = 0; i < D; ++i)
+            for (int j = 0; j < D; ++j) cov[i * D + j] = G2[i * D + j] - sum[i] * sum[j] / N;
+        for (int i = 0; i < D; ++i)
+            for (int j = 0; j < i; ++j) {
+                const double m = 0.5 * (cov[i * D + j] + cov[j * D + i]);
+                cov[i * D + j] = cov[j * D + i] = m;
+            }
+    }
+    std::vector<char> converged(nprob, 0);
+    {
+        const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+        const int nthreads = static_cast<int>(std::min<unsigned>(hw, static_cast<unsigned>(nprob)));
+        std::vector<std::thread> pool;
+        for (int th = 0; th < nthreads; ++th)
+            pool.emplace_back([&, th]() {
+                for (int pb = th; pb < nprob; pb += nthreads)
+                    converged[pb] = sym_eigen(covs.data() + static_cast<size_t>(pb) * D * D, D,
+                                              ws.data() + static_cast<size_t>(pb) * D,
+                                              zs.data() + static_cast<size_t>(pb) * D * D);
+            });
+        for (auto &t : pool) t.join();
+    }
     std::vector<int> order(D);
     for (int t = 0; t < 2; ++t) {
         std::vector<double> basis_full(static_cast<size_t>(c->G) * D * D);
@@ -304,18 +336,12 @@ PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t
         c->mu_h[t].assign(static_cast<size_t>(c->G) * D, 0.0f);
         c->sigma_h[t].assign(static_cast<size_t>(c->G) * D, 0.0);
         for (int g = 0; g < c->G; ++g) {
-            const double *G2 = gram.data() + (static_cast<size_t>(t) * c->G + g) * kGramElems;
+            const int pb = t * c->G + g;
+            const double *G2 = gram.data() + static_cast<size_t>(pb) * kGramElems;
             const double *sum = G2 + D * D;
-            // scatter about the mean: X^T X - s s^T / N
-            for (int i = 0; i < D; ++i)
-                for (int j = 0; j < D; ++j) cov[i * D + j] = G2[i * D + j] - sum[i] * sum[j] / N;
-            for (int i = 0; i < D; ++i)
-                for (int j = 0; j < i; ++j) {
-                    const double m = 0.5 * (cov[i * D + j] + cov[j * D + i]);
-                    cov[i * D + j] = cov[j * D + i] = m;
-                }
-            if (!sym_eigen(cov.data(), D, w.data(), z.data()))
-                return fail(PALU_ERR_HIP, "eigensolver did not converge");
+            if (!converged[pb]) return fail(PALU_ERR_HIP, "eigensolver did not converge");
+            const double *w = ws.data() + static_cast<size_t>(pb) * D;
+            const double *z = zs.data() + static_cast<size_t>(pb) * D * D;
             std::iota(order.begin(), order.end(), 0);
             std::stable_sort(order.begin(), order.end(), [&](int a2, int b2) { return w[a2] > w[b2]; });
             std::vector<double> s2(D);

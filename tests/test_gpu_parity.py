@@ -199,6 +199,39 @@ def test_multi_iteration_splits(torch, gqa, rank, vq):
     _run_small(torch, w, lens=[n0, 32 * split + 5], split_groups=split)
 
 
+def test_slot_mapping_and_row_order(torch):
+    # slots are filled through seq_ids in a scrambled order; decode calls
+    # address a subset of slots, in an order unrelated to their lengths (the
+    # kernel visits rows longest first), one slot more than once
+    w = synth.small_workload(batch=5, n_q_heads=8, n_kv_heads=2, n_head_groups=1, prefill=300,
+                             steps=1, rank=16, seed=31)
+    lens = np.array([37, 300, 5, 160, 96], np.int32)
+    k_all = synth.batch_kv(w, 0, int(lens.max()) + 1)
+    v_all = synth.batch_kv(w, 1, int(lens.max()) + 1)
+    fk = oracle.fit(k_all[:, :, :int(lens.max())], lens, 1, rank=16, tau=w.energy)
+    fv = oracle.fit(v_all[:, :, :int(lens.max())], lens, 1, rank=16, tau=w.energy)
+    cache = _cache(torch, w, int(lens.max()) + 1)
+    cache.set_basis(0, fk.bases(), fk.mu)
+    cache.set_basis(1, fv.bases(), fv.mu)
+    layer = oracle.OracleLayer(w.head_dim, w.n_q_heads, w.n_kv_heads, 1, fk, fv)
+    slots = [3, 0, 4, 1, 2]                 # row b of the inputs goes to slot slots[b]
+    cache.encode_append(_dev(torch, k_all[:, :, :int(lens.max())]), _dev(torch, v_all[:, :, :int(lens.max())]),
+                        seq_ids=np.array(slots, np.int32), n_new=lens)
+    torch.cuda.synchronize()
+    for b, sl in enumerate(slots):
+        assert cache.seq_len(sl) == lens[b]
+        _compare_state(cache, layer, (k_all[b, :, :lens[b]], v_all[b, :, :lens[b]]), sl)
+    call = [4, 1, 3, 1]                     # slots, in call order
+    q = synth.queries(w, 0, 4)[:, :, :]     # [4, Hq, D]
+    out = cache.decode_attend(_dev(torch, q), seq_ids=np.array(call, np.int32)).cpu().numpy()
+    for row, sl in enumerate(call):
+        b = slots.index(sl)
+        n = lens[b]
+        ks = [layer.encode_head(k_all[b, h, :n], h, 0) for h in range(w.n_kv_heads)]
+        vs = [layer.encode_head(v_all[b, h, :n], h, 1) for h in range(w.n_kv_heads)]
+        _check_attention(out[row], layer.attend(ks, vs, q[row]), f"row {row} slot {sl}")
+
+
 def test_append_order_invariance(torch):
     w = synth.small_workload(batch=3, n_q_heads=4, n_kv_heads=2, n_head_groups=2, prefill=150,
                              steps=1, rank=12, seed=21)
