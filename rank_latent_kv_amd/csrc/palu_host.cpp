@@ -138,7 +138,8 @@ int upload_basis(palu_cache *c, int t) {
                   hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "mean upload");
     e = launch_basis_t16(reinterpret_cast<const float *>(c->dev + c->off_basis[t]),
-                         reinterpret_cast<uint16_t *>(c->dev + c->off_bt16[t]), c->G, c->r[t], nullptr);
+                         reinterpret_cast<uint16_t *>(c->dev + c->off_bt16[t]), c->G, c->r[t],
+                         n_hi_of(c->r[t], c->cfg.hi_fraction), nullptr);
     if (e != hipSuccess) return hip_fail(e, "basis fp16 copy");
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "basis upload synchronize");
@@ -199,7 +200,7 @@ PALU_API int palu_cache_create(const palu_config *cfg, int32_t max_batch, int32_
     };
     for (int t = 0; t < 2; ++t) {
         c->off_basis[t] = take(sizeof(float) * c->G * c->D * c->r_max);
-        c->off_bt16[t] = take(sizeof(uint16_t) * c->G * c->D * c->r_max);
+        c->off_bt16[t] = take(sizeof(uint16_t) * c->G * c->D * (c->r_max + 16));   // >= basis_t16_rows
         c->off_mu[t] = take(sizeof(float) * c->G * c->D);
         const size_t head_words = (static_cast<size_t>(c->max_groups) * c->words_for(t, c->r_max) + 3) / 4 * 4;
         c->off_rec[t] = take(sizeof(uint32_t) * static_cast<size_t>(max_batch) * c->H * head_words);
@@ -479,7 +480,12 @@ PALU_API int palu_encode_append(palu_cache *c, const void *k, const void *v, con
             ea.sel_new[i] = sel_new;
             if (n > 0) max_units = std::max(max_units, (o + n - 1) / kTokGroup / 2 - o / kTokGroup / 2 + 1);
         }
-        if (max_units > 0) {
+        int max_new = 0;
+        for (int i = 0; i < nb; ++i) max_new = std::max(max_new, ea.n_new[i]);
+        if (max_new == 1) {
+            hipError_t e = launch_append1(ea, s);
+            if (e != hipSuccess) return hip_fail(e, "append launch");
+        } else if (max_units > 0) {
             hipError_t e = launch_encode(ea, max_units, s);
             if (e != hipSuccess) return hip_fail(e, "encode launch");
         }
@@ -570,7 +576,6 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
             volatile float one = 1.0f;   // IEEE fp32 divisions, not folded to other precisions
             aa.inv_rv = one / static_cast<float>(aa.v.r);
             aa.inv_nbk4 = one / static_cast<float>(4 * nbk);
-            aa.inv_nbk8 = one / static_cast<float>(8 * nbk);
         }
         hipError_t e = launch_attend(aa, lds, s);
         if (e != hipSuccess) return hip_fail(e, "attend launch");

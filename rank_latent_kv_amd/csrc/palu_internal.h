@@ -27,7 +27,9 @@ struct TensorDev {
     uint32_t *records;   // [slots][H][max_groups][words]
     float *tail;         // [slots][H][2][32][r]  (nullptr for fp16 latents)
     float *basis;        // [G][D][r] fp32, d-major
-    uint16_t *basis_t16; // [G][r][D] fp16 copy, channel-major (decode query absorption)
+    uint16_t *basis_t16; // [G][P][D] fp16 copy, row n = channel of score-operand position n
+                         // (8-channel blocks, hi blocks first, [c0,c4,c1,c5,..] inside a
+                         // block; zero rows for padding), P = 8 * blocks (query absorption)
     float *mu;           // [G][D] fp32
     int r, n_hi, words;
     int fp16_latents;    // V stored as fp16 latents (no tail, no meta)
@@ -78,9 +80,9 @@ struct AttendArgs {
     int chunk;                // complete token groups per split
     int nsplit_max;           // grid x; splits s >= row.nsplit exit at once
     float qscale;             // softmax scale * log2(e)
-    // correctly rounded fp32 reciprocals of table index divisors: r_v, and
-    // 4 and 8 times the key channel blocks
-    float inv_rv, inv_nbk4, inv_nbk8;
+    // correctly rounded fp32 reciprocals of index divisors: r_v and 4 times
+    // the key channel blocks
+    float inv_rv, inv_nbk4;
     AttendRow row[kMaxCallSeqs];       // grid z order (longest first)
     int nsplit_call[kMaxCallSeqs];     // splits of call row i (combine)
 };
@@ -93,11 +95,16 @@ hipError_t launch_gram(const GramArgs &a, hipStream_t s);
 hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s);
 // One wave per (pair of touched token groups, call row x head, tensor).
 hipError_t launch_encode(const EncodeArgs &a, int max_units, hipStream_t s);
+// Appends of at most one token per row: one workgroup per (call row x head,
+// tensor), one thread per latent channel.
+hipError_t launch_append1(const EncodeArgs &a, hipStream_t s);
 // Grid (nsplit_max, Hkv, B): one workgroup per (split, kv head, row).
 hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s);
 // fp16 channel-major copy of a basis: dst[g][c][d] = fp16(src[g][d][c]).
-hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, hipStream_t s);
+hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, int n_hi, hipStream_t s);
+// rows of the position-ordered fp16 basis copy for rank r (8 per channel block)
+inline int basis_t16_rows(int r, int n_hi) { return 8 * ((n_hi + 7) / 8 + (r - n_hi + 7) / 8); }
 
 // Host symmetric eigensolver (palu_eigen.cpp): Householder tridiagonalisation
 // followed by implicit-shift QL.  a: n x n row-major symmetric (destroyed);

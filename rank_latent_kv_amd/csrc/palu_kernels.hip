@@ -395,6 +395,101 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     }
 }
 
+// ------------------------------------------------------ append one token ----
+//
+// Appends of at most one token per row (the decode step).  Workgroup =
+// (call row x kv head, tensor), 128 threads, thread c < r owns latent
+// channel c.  y = float(x) - mu and the group's basis are staged in LDS; each
+// channel runs the fixed-order fma chain over d.  The token either extends
+// the fp32 tail of the incomplete group or completes it; then every
+// channel's 32 latents (31 from the tail, the new one) are quantised in
+// token order and the codes OR-ed into an LDS copy of the record.
+
+constexpr int kApp1Threads = 128;
+
+__host__ __device__ inline int append1_lds_bytes(int r, int words) {
+    return (kHeadDim + r * kHeadDim + words) * 4;     // y [D], basis [D][r], record
+}
+
+__global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
+    extern __shared__ __align__(16) float ash[];
+    const int tid = threadIdx.x;
+    const int bi = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
+    const int tz = blockIdx.y;
+    const int o = a.old_len[bi], n = a.n_new[bi];
+    if (n <= 0) return;                               // whole workgroup
+    const TensorDev &T = tz ? a.t[1] : a.t[0];
+    const int r = T.r, n_hi = T.n_hi, n_lo = r - n_hi, W = T.words;
+    const int grp = h / a.hpg, slot = a.slot[bi];
+    const int64_t head_base = static_cast<int64_t>(slot) * a.H + h;
+    const int j = o >> 5, t = o & 31;                 // group and position of the new token
+    const bool complete = t == 31;
+    float *ys = ash;
+    float *vs = ash + kHeadDim;
+    uint32_t *rec = reinterpret_cast<uint32_t *>(vs + r * kHeadDim);
+
+    // 1. y = float(x) - mu and the basis -> LDS
+    const uint16_t *xin = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim;
+    if (tid < kHeadDim) ys[tid] = h2f(xin[tid]) - T.mu[grp * kHeadDim + tid];
+    const float *vb = T.basis + static_cast<int64_t>(grp) * kHeadDim * r;
+    for (int e = tid; e < kHeadDim * r; e += kApp1Threads) vs[e] = vb[e];
+    if (complete && !T.fp16_latents)
+        for (int w = tid; w < W; w += kApp1Threads) rec[w] = 0u;
+    __syncthreads();
+
+    // 2. channel c of the latent: acc = fma(y_d, V[d][c], acc), d = 0..D-1
+    const int c = tid;
+    float lat = 0.0f;
+    if (c < r)
+        for (int d = 0; d < kHeadDim; ++d) lat = __builtin_fmaf(ys[d], vs[d * r + c], lat);
+    if (T.fp16_latents) {                             // uniform: no tail, no quantiser
+        if (c < r) {
+            uint16_t *rec16 = reinterpret_cast<uint16_t *>(T.records + head_base * T.head_stride +
+                                                           static_cast<int64_t>(j) * W);
+            rec16[c * 32 + t] = static_cast<uint16_t>(f2h_bits(lat));
+        }
+        return;
+    }
+    if (!complete) {                                  // uniform
+        if (c < r) T.tail[(head_base * 2 + a.sel_new[bi]) * 32 * r + t * r + c] = lat;
+        return;
+    }
+
+    // 3. the group completes: channel c over its 32 latents in token order
+    if (c < r) {
+        const float *told = T.tail + (head_base * 2 + a.sel_old[bi]) * 32 * r;
+        float mn = told[c], mx = mn;                  // token 0 (t == 31 here, so it is old)
+        for (int tt = 1; tt < 32; ++tt) {
+            const float v = tt == 31 ? lat : told[tt * r + c];
+            mn = v < mn ? v : mn;
+            mx = v > mx ? v : mx;
+        }
+        const bool hi = c < n_hi;
+        const float levels = static_cast<float>((1 << (hi ? a.hi_bit : a.lo_bit)) - 1);
+        const float scale = (mx - mn) / levels;
+        for (int tt = 0; tt < 32; ++tt) {
+            const float v = tt == 31 ? lat : told[tt * r + c];
+            int q = 0;
+            if (scale > 0.0f) {
+                float uq = rintf((v - mn) / scale);
+                uq = uq < 0.0f ? 0.0f : (uq > levels ? levels : uq);
+                q = static_cast<int>(uq);
+            }
+            int bit;
+            if (hi) bit = tz == 0 ? tt * 4 * n_hi + 4 * c : 128 * c + 4 * tt;
+            else {
+                const int cl = c - n_hi;
+                bit = 128 * n_hi + (tz == 0 ? tt * 2 * n_lo + 2 * cl : 64 * cl + 2 * tt);
+            }
+            if (q) atomicOr(rec + (bit >> 5), static_cast<uint32_t>(q) << (bit & 31));
+        }
+        rec[4 * n_hi + 2 * n_lo + c] = f2h_bits(scale) | (f2h_bits(mn) << 16);
+    }
+    __syncthreads();
+    uint32_t *dst = T.records + head_base * T.head_stride + static_cast<int64_t>(j) * W;
+    for (int w = tid; w < W; w += kApp1Threads) dst[w] = rec[w];
+}
+
 // -------------------------------------------------------------- attend ----
 //
 // Workgroup = (call row i, kv head h, split s).  Split s covers complete
@@ -424,7 +519,6 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 
 constexpr int kWaves = 4;
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kBtabMaxU = 16;   // score B-operand table kept in LDS up to this many MFMA k-steps
 constexpr int kStageBudgetWords = 24 * 1024;   // both record buffers together (96 KiB)
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -434,11 +528,10 @@ typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 // LDS layout of one attend workgroup (byte offsets).  Shared by the kernel
 // and the host, which sizes the dynamic LDS from it.
 struct AttendLds {
-    int qt, qt16, btab, kpw, stage, sb;          // sb: words per stage buffer
+    int qt, qt16, kpw, stage, sb;                // sb: words per stage buffer
     int pp;                                      // token groups per pass
     int ts, mst, lst, ost, tp;                   // merge state: byte offsets inside a stage buffer
     int total, nbk, nub;
-    bool use_btab;
 };
 
 __host__ __device__ inline int lds_take(int &o, int bytes) {
@@ -453,11 +546,9 @@ __host__ __device__ inline AttendLds attend_lds(int g, int rk, int nhk, int rv, 
     const int S = 16 / g, P = kWaves * S;
     L.nbk = (nhk + 7) / 8 + (rk - nhk + 7) / 8;
     L.nub = (S * L.nbk + 3) / 4;
-    L.use_btab = L.nub <= kBtabMaxU;
     int o = 0;
     L.qt = lds_take(o, g * kHeadDim * 4);
     L.qt16 = lds_take(o, g * 16 * 16);
-    L.btab = lds_take(o, L.use_btab ? L.nub * 64 * 16 : 0);
     L.kpw = lds_take(o, kWaves * S * L.nbk * 8 * 4);
     // two stage buffers.  Each holds one pass of records (+ 16-byte
     // alignment slack); a pass is the 4 S groups the waves take, fewer when
@@ -588,7 +679,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     float *qt = reinterpret_cast<float *>(lds + L.qt);
     uint4 *qt16 = reinterpret_cast<uint4 *>(lds + L.qt16);
     _Float16 *qt16h = reinterpret_cast<_Float16 *>(lds + L.qt16);
-    uint4 *btab = reinterpret_cast<uint4 *>(lds + L.btab);
     uint32_t *kpw = reinterpret_cast<uint32_t *>(lds + L.kpw) + wv * (S * nbk * 8);   // this wave's
     // stage buffer tb holds the tail latents (the one the last pass leaves
     // free); after the main loop the other one holds the merge state
@@ -648,11 +738,15 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     else if (do_tail) copy_tail();
 
     // ---- 2. absorbed query qt = qs V_K^T q on MFMA: rows = query heads of
-    //         this kv head, K = d, columns = 16-channel blocks of the fp16
-    //         channel-major key basis (wave w takes blocks w and w + 4); only
-    //         the waves that own a block load the query and the basis
+    //         this kv head, K = d, columns = 16 score-operand positions of
+    //         the position-ordered fp16 key basis (wave w takes blocks w and
+    //         w + 4).  The result goes straight to the fp16 score operand
+    //         qt16[head][position] (padding positions come out 0) and, for
+    //         the tail stream, to fp32 qt[head][channel]; only the waves
+    //         that own a block load the query and the basis.
     {
-        const int nbc = (rk + 15) >> 4;              // 16-channel blocks of qt (<= 8)
+        const int np = 8 * nbk;                      // positions (<= 128)
+        const int nbc = (np + 15) >> 4;              // 16-position blocks (<= 8)
         const bool own0 = wv < nbc, own1 = wv + kWaves < nbc;
         if (own0) {
             const int qrow = qi * a.Hq + h * g;
@@ -661,15 +755,15 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             uint4 qa[4], bb[2][4];
 #pragma unroll
             for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const uint4 *>(qsrc + 32 * st);
-            const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * rk * kHeadDim;
+            const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * np * kHeadDim;
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 if (x == 1 && !own1) break;
-                int c = 16 * (wv + kWaves * x) + ln;
-                c = c < rk ? c : rk - 1;              // clamped rows are never stored
+                int n = 16 * (wv + kWaves * x) + ln;
+                n = n < np ? n : np - 1;              // clamped rows are never stored
 #pragma unroll
                 for (int st = 0; st < 4; ++st)
-                    bb[x][st] = *reinterpret_cast<const uint4 *>(bt + static_cast<int64_t>(c) * kHeadDim + 32 * st +
+                    bb[x][st] = *reinterpret_cast<const uint4 *>(bt + static_cast<int64_t>(n) * kHeadDim + 32 * st +
                                                                  8 * kb);
             }
 #pragma unroll
@@ -682,58 +776,24 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                                                                 as_h8(bb[x][st].x, bb[x][st].y, bb[x][st].z,
                                                                       bb[x][st].w),
                                                                 acc, 0, 0, 0);
-                const int c = 16 * (wv + kWaves * x) + ln;
+                const int n = 16 * (wv + kWaves * x) + ln;
+                const int q = n >> 3, idx = n & 7;
+                const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
+                const int chanend = q < nbh ? nhk : rk;
+                const int c = chan0 + (idx >> 1) + 4 * (idx & 1);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int hh = 4 * kb + v;
-                    if (hh < g && c < rk) qt[hh * rk + c] = acc[v] * a.qscale;
+                    if (hh < g && n < np) {
+                        const float val = acc[v] * a.qscale;
+                        qt16h[hh * np + n] = static_cast<_Float16>(val);
+                        if (c < chanend) qt[hh * rk + c] = val;
+                    }
                 }
             }
         }
     }
     __builtin_amdgcn_s_waitcnt(0);                    // this wave's copies have landed
-    __syncthreads();
-
-    // ---- 3. score B operand: per k-step u and lane the block-diagonal fp16
-    //         qt (channel order [c0,c4,c1,c5,..]); without the table, qt16
-    //         per (head, channel block) and the main loop builds the operand
-    if (L.use_btab) {
-        for (int e = tid; e < nub * 64; e += 256) {
-            const int u = e >> 6, l2 = e & 63, n2 = l2 & 15;
-            const int p = 4 * u + (l2 >> 4);
-            const int q = p / S, j = p - (p / S) * S;
-            const bool ok = p < npair && n2 < NS && j == n2 / g;
-            const int hh = n2 - (n2 / g) * g;
-            const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
-            const int chanend = q < nbh ? nhk : rk;
-            const float *qrow = qt + hh * rk;
-            _Float16 hv[8];
-#pragma unroll
-            for (int idx = 0; idx < 8; ++idx) {
-                const int c = chan0 + (idx >> 1) + 4 * (idx & 1);
-                const float val = qrow[c < rk ? c : rk - 1];
-                hv[idx] = static_cast<_Float16>(ok && c < chanend ? val : 0.0f);
-            }
-            uint4 w;
-            w.x = __builtin_bit_cast(uint32_t, (h2){hv[0], hv[1]});
-            w.y = __builtin_bit_cast(uint32_t, (h2){hv[2], hv[3]});
-            w.z = __builtin_bit_cast(uint32_t, (h2){hv[4], hv[5]});
-            w.w = __builtin_bit_cast(uint32_t, (h2){hv[6], hv[7]});
-            btab[e] = w;
-        }
-    } else {
-        const FastDiv div_nbk8(a.inv_nbk8);
-        for (int e = tid; e < g * nbk * 8; e += 256) {
-            const int hh = div_nbk8.quo(e), r2 = e - hh * nbk * 8;
-            const int q = r2 >> 3, idx = r2 & 7;
-            const int kk = (idx >> 1) + 4 * (idx & 1);
-            const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
-            const int chanend = q < nbh ? nhk : rk;
-            const int c = chan0 + kk;
-            qt16h[(hh * nbk + q) * 8 + idx] = c < chanend ? static_cast<_Float16>(qt[hh * rk + c])
-                                                          : static_cast<_Float16>(0.0f);
-        }
-    }
     __syncthreads();
 
     // ---- 4. main loop: passes of PP token groups, wave w takes pass-relative
@@ -820,13 +880,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             const uint32_t *rec = stage + koff + tg * WK;
             const uint4 *kp = reinterpret_cast<const uint4 *>(kpw + (j * nbk + qc) * 8);
             const uint4 sp = kp[0], zp = kp[1];
-            uint4 bq;
-            if (L.use_btab) {
-                bq = btab[u * 64 + lane];
-            } else {
-                const bool ok = p < npair && live_n && j == slot_n;
-                bq = ok ? qt16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
-            }
+            const bool ok = p < npair && live_n && j == slot_n;
+            const uint4 bq = ok ? qt16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
             const f16x8 bop = as_h8(bq.x, bq.y, bq.z, bq.w);
             const bool w4 = qc < nbh;
             const int base = w4 ? 32 * qc : 128 * nhk + 16 * (qc - nbh);
@@ -1166,14 +1221,22 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
         f2h_bits(o0) | (f2h_bits(o1) << 16);
 }
 
-__global__ __launch_bounds__(256) void basis_t16_kernel(const float *src, uint16_t *dst, int G, int r) {
+// dst[g][n][d] = fp16(V[g][d][chan(n)]) for the score-operand position n
+// (block q = n / 8 of 8 channels, hi blocks first; slot idx = n % 8 holds
+// channel (idx >> 1) + 4 (idx & 1) of the block), 0 where n is padding.
+__global__ __launch_bounds__(256) void basis_t16_kernel(const float *src, uint16_t *dst, int G, int r, int n_hi) {
+    const int nbh = (n_hi + 7) >> 3, rows = 8 * (nbh + ((r - n_hi + 7) >> 3));
     const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t n = static_cast<int64_t>(G) * r * kHeadDim;
-    if (e >= n) return;
+    if (e >= static_cast<int64_t>(G) * rows * kHeadDim) return;
     const int d = static_cast<int>(e % kHeadDim);
-    const int64_t gc = e / kHeadDim;
-    const int c = static_cast<int>(gc % r), g = static_cast<int>(gc / r);
-    dst[e] = static_cast<uint16_t>(f2h_bits(src[(static_cast<int64_t>(g) * kHeadDim + d) * r + c]));
+    const int64_t gn = e / kHeadDim;
+    const int n = static_cast<int>(gn % rows), g = static_cast<int>(gn / rows);
+    const int q = n >> 3, idx = n & 7;
+    const int chan0 = q < nbh ? 8 * q : n_hi + 8 * (q - nbh);
+    const int chanend = q < nbh ? n_hi : r;
+    const int c = chan0 + (idx >> 1) + 4 * (idx & 1);
+    dst[e] = c < chanend ? static_cast<uint16_t>(f2h_bits(src[(static_cast<int64_t>(g) * kHeadDim + d) * r + c]))
+                         : static_cast<uint16_t>(0);
 }
 
 }  // namespace
@@ -1186,6 +1249,20 @@ hipError_t launch_gram(const GramArgs &a, hipStream_t s) {
 hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s) {
     constexpr int kElems = kHeadDim * kHeadDim + kHeadDim;
     hipLaunchKernelGGL(gram_reduce_kernel, dim3((kElems + 255) / 256, a.G, 2), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_append1(const EncodeArgs &a, hipStream_t s) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(append1_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int l0 = append1_lds_bytes(a.t[0].r, a.t[0].words), l1 = append1_lds_bytes(a.t[1].r, a.t[1].words);
+    hipLaunchKernelGGL(append1_kernel, dim3(a.B * a.H, 2), dim3(kApp1Threads), static_cast<size_t>(l0 > l1 ? l0 : l1),
+                       s, a);
     return hipGetLastError();
 }
 
@@ -1249,9 +1326,10 @@ hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
     }
 }
 
-hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, hipStream_t s) {
-    const int64_t n = static_cast<int64_t>(G) * r * kHeadDim;
-    hipLaunchKernelGGL(basis_t16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, src, dst, G, r);
+hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, int n_hi, hipStream_t s) {
+    const int64_t n = static_cast<int64_t>(G) * basis_t16_rows(r, n_hi) * kHeadDim;
+    hipLaunchKernelGGL(basis_t16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, src, dst, G, r,
+                       n_hi);
     return hipGetLastError();
 }
 
