@@ -200,6 +200,34 @@ int palu_reset(palu_cache *cache);
 /* Words of one mixed-bit record for rank r: 4 n_hi + 2 (r - n_hi) + r. */
 int palu_record_words(const palu_cache *cache, int32_t tensor, int32_t *words);
 
+/* Save / restore of one sequence slot: the prompt-cache round trip that the
+ * "add TurboQuant KV cache compression" pull-request page lists among its
+ * proposed changes and fixes in its review thread, applied here to the
+ * latent cache.  The
+ * serialized form is a 64-byte header followed by, for K then V, the records
+ * of every kv head in head order (len / 32 records of words_t uint32 each;
+ * fp16 value latents keep ceil(len / 32), the last one partial) and then the
+ * fp32 tail latents of every kv head in head order (len % 32 rows of r_t
+ * floats; none for fp16 value latents).  Header, all
+ * little-endian: uint32 magic 0x564B4C50 ("PLKV"), uint32 version 1, int32
+ * head_dim, n_kv_heads, n_head_groups, r_K, r_V, n_hi_K, n_hi_V, words_K,
+ * words_V, quantize_values, len, uint64 FNV-1a hash of the fp32 bases and
+ * means of both tensors, 4 zero bytes.  The basis itself is not included
+ * (palu_get_basis / palu_set_basis move it).
+ *
+ * palu_export_bytes: bytes of the serialized slot.  palu_export_seq:
+ * synchronous (waits for the device), writes exactly that many bytes to
+ * host_dst.  palu_import_seq: synchronous; replaces the slot's contents.
+ * Errors: NOT_BOUND / NOT_FITTED as elsewhere; INVALID_ARG for a NULL
+ * buffer, an export buffer smaller than palu_export_bytes, an import buffer
+ * whose size differs from what its header describes, a bad magic or version,
+ * or a header whose shape, ranks or basis hash differ from the cache's
+ * current ones; CAPACITY for a slot out of range or len > max_seq_len.  A
+ * failed import leaves the slot unchanged (all checks come first). */
+int palu_export_bytes(const palu_cache *cache, int32_t seq, size_t *bytes);
+int palu_export_seq(const palu_cache *cache, int32_t seq, void *host_dst, size_t bytes);
+int palu_import_seq(palu_cache *cache, int32_t seq, const void *host_src, size_t bytes);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char *palu_last_error(void);
 

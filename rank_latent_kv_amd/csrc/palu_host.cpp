@@ -682,6 +682,174 @@ PALU_API int palu_record_words(const palu_cache *c, int32_t tensor, int32_t *wor
     return PALU_OK;
 }
 
+namespace {
+
+constexpr uint32_t kSeqMagic = 0x564B4C50u;   // "PLKV" little-endian
+constexpr uint32_t kSeqVersion = 1;
+constexpr size_t kSeqHeaderBytes = 64;
+constexpr int kSeqHeaderInts = 13;            // magic .. len
+
+uint64_t fnv1a(uint64_t h, const void *p, size_t n) {
+    const unsigned char *b = static_cast<const unsigned char *>(p);
+    for (size_t i = 0; i < n; ++i) {
+        h ^= b[i];
+        h *= 0x100000001B3ull;
+    }
+    return h;
+}
+
+uint64_t basis_hash(const palu_cache *c) {
+    uint64_t h = 0xCBF29CE484222325ull;
+    for (int t = 0; t < 2; ++t) {
+        h = fnv1a(h, c->basis_h[t].data(), c->basis_h[t].size() * sizeof(float));
+        h = fnv1a(h, c->mu_h[t].data(), c->mu_h[t].size() * sizeof(float));
+    }
+    return h;
+}
+
+// Per-tensor sizes of one slot of length len.
+struct SeqPart {
+    int nrec, words, ntail, r;
+    size_t rec_bytes() const { return sizeof(uint32_t) * static_cast<size_t>(nrec) * words; }
+    size_t tail_bytes() const { return sizeof(float) * static_cast<size_t>(ntail) * r; }
+};
+
+SeqPart seq_part(const palu_cache *c, int t, int len) {
+    const TensorDev td = c->tensor_dev(t);
+    SeqPart p;
+    p.words = td.words;
+    p.r = td.r;
+    p.nrec = td.fp16_latents ? (len + kTokGroup - 1) / kTokGroup : len / kTokGroup;
+    p.ntail = td.fp16_latents ? 0 : len % kTokGroup;
+    return p;
+}
+
+size_t seq_bytes(const palu_cache *c, int len) {
+    size_t n = kSeqHeaderBytes;
+    for (int t = 0; t < 2; ++t) {
+        const SeqPart p = seq_part(c, t, len);
+        n += static_cast<size_t>(c->H) * (p.rec_bytes() + p.tail_bytes());
+    }
+    return n;
+}
+
+// The header's int fields for this cache at slot length len.
+void seq_header(const palu_cache *c, int len, int32_t f[kSeqHeaderInts]) {
+    f[0] = static_cast<int32_t>(kSeqMagic);
+    f[1] = static_cast<int32_t>(kSeqVersion);
+    f[2] = c->D;
+    f[3] = c->H;
+    f[4] = c->G;
+    f[5] = c->r[0];
+    f[6] = c->r[1];
+    f[7] = c->n_hi[0];
+    f[8] = c->quantized(1) ? c->n_hi[1] : 0;
+    f[9] = c->words_for(0, c->r[0]);
+    f[10] = c->words_for(1, c->r[1]);
+    f[11] = c->cfg.quantize_values;
+    f[12] = len;
+}
+
+int check_seq(const palu_cache *c, int32_t seq) {
+    if (int e = check_fitted(c)) return e;
+    if (seq < 0 || seq >= c->max_batch) return fail(PALU_ERR_CAPACITY, "sequence slot out of range");
+    return PALU_OK;
+}
+
+}  // namespace
+
+PALU_API int palu_export_bytes(const palu_cache *c, int32_t seq, size_t *bytes) {
+    if (!bytes) return fail(PALU_ERR_INVALID_ARG, "bytes is NULL");
+    if (int e = check_seq(c, seq)) return e;
+    *bytes = seq_bytes(c, c->len[seq]);
+    return PALU_OK;
+}
+
+PALU_API int palu_export_seq(const palu_cache *c, int32_t seq, void *host_dst, size_t bytes) {
+    if (int e = check_seq(c, seq)) return e;
+    if (!host_dst) return fail(PALU_ERR_INVALID_ARG, "destination is NULL");
+    const int len = c->len[seq];
+    if (bytes < seq_bytes(c, len)) return fail(PALU_ERR_INVALID_ARG, "destination smaller than palu_export_bytes");
+    char *out = static_cast<char *>(host_dst);
+    std::memset(out, 0, kSeqHeaderBytes);
+    int32_t f[kSeqHeaderInts];
+    seq_header(c, len, f);
+    std::memcpy(out, f, sizeof(f));
+    const uint64_t h = basis_hash(c);
+    std::memcpy(out + sizeof(f), &h, sizeof(h));
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "export synchronize");
+    char *p = out + kSeqHeaderBytes;
+    const int64_t hb0 = static_cast<int64_t>(seq) * c->H;
+    for (int t = 0; t < 2; ++t) {
+        const TensorDev td = c->tensor_dev(t);
+        const SeqPart sp = seq_part(c, t, len);
+        if (sp.rec_bytes()) {
+            e = hipMemcpy2D(p, sp.rec_bytes(), td.records + hb0 * td.head_stride, td.head_stride * sizeof(uint32_t),
+                            sp.rec_bytes(), c->H, hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_fail(e, "records download");
+            p += sp.rec_bytes() * c->H;
+        }
+        if (sp.tail_bytes()) {
+            const float *src = td.tail + (hb0 * 2 + c->sel[seq]) * kTokGroup * td.r;
+            e = hipMemcpy2D(p, sp.tail_bytes(), src, sizeof(float) * 2 * kTokGroup * td.r, sp.tail_bytes(), c->H,
+                            hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_fail(e, "tail download");
+            p += sp.tail_bytes() * c->H;
+        }
+    }
+    return PALU_OK;
+}
+
+PALU_API int palu_import_seq(palu_cache *c, int32_t seq, const void *host_src, size_t bytes) {
+    if (int e = check_seq(c, seq)) return e;
+    if (!host_src) return fail(PALU_ERR_INVALID_ARG, "source is NULL");
+    if (bytes < kSeqHeaderBytes) return fail(PALU_ERR_INVALID_ARG, "source shorter than the header");
+    const char *in = static_cast<const char *>(host_src);
+    int32_t f[kSeqHeaderInts];
+    std::memcpy(f, in, sizeof(f));
+    uint64_t h;
+    std::memcpy(&h, in + sizeof(f), sizeof(h));
+    if (static_cast<uint32_t>(f[0]) != kSeqMagic) return fail(PALU_ERR_INVALID_ARG, "bad magic");
+    if (static_cast<uint32_t>(f[1]) != kSeqVersion) return fail(PALU_ERR_INVALID_ARG, "unsupported version");
+    const int len = f[12];
+    if (len < 0) return fail(PALU_ERR_INVALID_ARG, "negative length");
+    int32_t mine[kSeqHeaderInts];
+    seq_header(c, len, mine);
+    for (int i = 2; i < 12; ++i)
+        if (f[i] != mine[i])
+            return fail(PALU_ERR_INVALID_ARG, "slot was saved under a different shape, rank or value coding");
+    if (h != basis_hash(c)) return fail(PALU_ERR_INVALID_ARG, "slot was saved under a different basis");
+    if (len > c->max_seq_len) return fail(PALU_ERR_CAPACITY, "saved length exceeds max_seq_len");
+    if (bytes != seq_bytes(c, len)) return fail(PALU_ERR_INVALID_ARG, "source size does not match its header");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "import synchronize");
+    const char *p = in + kSeqHeaderBytes;
+    const int64_t hb0 = static_cast<int64_t>(seq) * c->H;
+    for (int t = 0; t < 2; ++t) {
+        const TensorDev td = c->tensor_dev(t);
+        const SeqPart sp = seq_part(c, t, len);
+        if (sp.rec_bytes()) {
+            e = hipMemcpy2D(td.records + hb0 * td.head_stride, td.head_stride * sizeof(uint32_t), p, sp.rec_bytes(),
+                            sp.rec_bytes(), c->H, hipMemcpyHostToDevice);
+            if (e != hipSuccess) return hip_fail(e, "records upload");
+            p += sp.rec_bytes() * c->H;
+        }
+        if (sp.tail_bytes()) {
+            float *dst = td.tail + hb0 * 2 * kTokGroup * td.r;   // tail buffer 0
+            e = hipMemcpy2D(dst, sizeof(float) * 2 * kTokGroup * td.r, p, sp.tail_bytes(), sp.tail_bytes(), c->H,
+                            hipMemcpyHostToDevice);
+            if (e != hipSuccess) return hip_fail(e, "tail upload");
+            p += sp.tail_bytes() * c->H;
+        }
+    }
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "import synchronize");
+    c->len[seq] = len;
+    c->sel[seq] = 0;
+    return PALU_OK;
+}
+
 PALU_API const char *palu_last_error(void) { return g_last_error.c_str(); }
 
 PALU_API void palu_cache_destroy(palu_cache *c) { delete c; }

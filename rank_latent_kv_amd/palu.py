@@ -25,8 +25,8 @@ ERROR_NAMES = {1: "PALU_ERR_INVALID_ARG", 2: "PALU_ERR_UNSUPPORTED", 3: "PALU_ER
 EXPORTED = ["palu_config_default", "palu_cache_create", "palu_cache_required_bytes",
             "palu_cache_bind", "palu_fit", "palu_set_basis", "palu_get_basis",
             "palu_encode_append", "palu_decode_attend", "palu_seq_len", "palu_read_codes",
-            "palu_get_stats", "palu_reset", "palu_record_words", "palu_last_error",
-            "palu_cache_destroy"]
+            "palu_get_stats", "palu_reset", "palu_record_words", "palu_export_bytes",
+            "palu_export_seq", "palu_import_seq", "palu_last_error", "palu_cache_destroy"]
 
 
 class PaluError(RuntimeError):
@@ -87,6 +87,9 @@ def lib():
         "palu_get_stats": [_vp, ctypes.POINTER(palu_stats)],
         "palu_reset": [_vp],
         "palu_record_words": [_vp, _i32, _i32p],
+        "palu_export_bytes": [_vp, _i32, ctypes.POINTER(_sz)],
+        "palu_export_seq": [_vp, _i32, _vp, _sz],
+        "palu_import_seq": [_vp, _i32, _vp, _sz],
         "palu_cache_destroy": [_vp],
     }
     for name, args in sig.items():
@@ -182,6 +185,24 @@ def palu_record_words(cache: int, tensor: int) -> int:
     n = ctypes.c_int32()
     _check(lib().palu_record_words(cache, tensor, ctypes.byref(n)))
     return n.value
+
+
+def palu_export_bytes(cache: int, seq: int) -> int:
+    n = _sz()
+    _check(lib().palu_export_bytes(cache, seq, ctypes.byref(n)))
+    return n.value
+
+
+def palu_export_seq(cache: int, seq: int) -> bytes:
+    n = palu_export_bytes(cache, seq)
+    buf = ctypes.create_string_buffer(n)
+    _check(lib().palu_export_seq(cache, seq, buf, n))
+    return buf.raw
+
+
+def palu_import_seq(cache: int, seq: int, data: bytes):
+    buf = ctypes.create_string_buffer(bytes(data), len(data))
+    _check(lib().palu_import_seq(cache, seq, buf, len(data)))
 
 
 def palu_read_codes(cache: int, seq: int, head: int, tensor: int, n_records: int, words: int,
@@ -311,6 +332,15 @@ class LatentKVCache:
         nrec = (n + 31) // 32 if fp16 else n // 32
         ntail = 0 if fp16 else n % 32
         return palu_read_codes(self.handle, seq, head, tensor, nrec, words, ntail, r)
+
+    def export_seq(self, seq: int) -> bytes:
+        """Serialized codes and tails of one slot (header + records + tails)."""
+        return palu_export_seq(self.handle, seq)
+
+    def import_seq(self, seq: int, data: bytes):
+        """Replace one slot's contents with an exported slot; the cache must
+        hold the basis the slot was saved under."""
+        palu_import_seq(self.handle, seq, data)
 
     def stats(self) -> dict:
         return palu_get_stats(self.handle).as_dict()
