@@ -22,6 +22,10 @@
  *              "The Bit-Packing Problem") in the record layout below.
  *   attend   : reconstruct K/V = l_hat V_g^T + mu_g in fp64 and run plain
  *              single-query softmax attention over every stored token.
+ *   prefill  : reconstruct K/V of every stored token the same way, then
+ *              causal softmax attention of each prefill query over the
+ *              tokens up to and including its own position (prefill step 6:
+ *              the reconstruction feeds the downstream attention call).
  *
  * Record layout (one record per sequence, kv head, tensor and complete
  * 32-token group; 32-bit little-endian words):
@@ -546,4 +550,66 @@ void orc_attend(const double *lk, const float *Bk, int ldk, const float *muk,
     }
     free(s);
     free(kt);
+}
+
+/*
+ * Causal prefill attention over n reconstructed tokens (PALU page, "How it
+ * works", prefill step 6: K/V are reconstructed as L V_g^T + mu_g for the
+ * attention call that follows).  The whole K and V are reconstructed first,
+ * then each query i, sitting at position pos[i], attends to tokens
+ * 0..pos[i] (causal mask, the plain reading for a prefill).
+ *   lk, lv : fp64 dequantised latents [n][rk], [n][rv]
+ *   Bk, Bv : fp32 bases [D][ldk], [D][ldv] (first rk / rv columns used)
+ *   q      : fp32 queries [nq][D] (fp16 values widened)
+ *   pos    : [nq] positions, 0 <= pos[i] < n
+ *   out    : fp64 [nq][D]
+ * Everything is fp64; each softmax subtracts its row's maximum score.
+ */
+void orc_prefill_attend(const double *lk, const float *Bk, int ldk, const float *muk,
+                        int rk, const double *lv, const float *Bv, int ldv,
+                        const float *muv, int rv, int64_t n, int D, const float *q,
+                        const int64_t *pos, int64_t nq, double scale, double *out)
+{
+    double *kh = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
+    double *vh = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * D);
+    double *s = malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    /* 1. reconstruction of every stored token */
+    for (int64_t t = 0; t < n; t++)
+        for (int d = 0; d < D; d++) {
+            double ak = (double)muk[d], av = (double)muv[d];
+            for (int c = 0; c < rk; c++)
+                ak += (double)Bk[(int64_t)d * ldk + c] * lk[t * rk + c];
+            for (int c = 0; c < rv; c++)
+                av += (double)Bv[(int64_t)d * ldv + c] * lv[t * rv + c];
+            kh[t * D + d] = ak;
+            vh[t * D + d] = av;
+        }
+    /* 2. one causal softmax attention row per query */
+    for (int64_t i = 0; i < nq; i++) {
+        const int64_t last = pos[i];
+        double smax = -INFINITY;
+        for (int64_t t = 0; t <= last; t++) {
+            double dot = 0.0;
+            for (int d = 0; d < D; d++)
+                dot += (double)q[i * D + d] * kh[t * D + d];
+            s[t] = dot * scale;
+            if (s[t] > smax)
+                smax = s[t];
+        }
+        double denom = 0.0;
+        for (int64_t t = 0; t <= last; t++) {
+            s[t] = exp(s[t] - smax);
+            denom += s[t];
+        }
+        for (int d = 0; d < D; d++)
+            out[i * D + d] = 0.0;
+        for (int64_t t = 0; t <= last; t++) {
+            const double p = s[t] / denom;
+            for (int d = 0; d < D; d++)
+                out[i * D + d] += p * vh[t * D + d];
+        }
+    }
+    free(kh);
+    free(vh);
+    free(s);
 }

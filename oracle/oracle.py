@@ -28,6 +28,7 @@ _u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
 _f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
 _c_int, _c_i64, _c_dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
 
 
@@ -69,6 +70,9 @@ def lib():
         L.orc_attend.argtypes = [_f64p, _f32p, _c_int, _f32p, _c_int, _f64p, _f32p,
                                  _c_int, _f32p, _c_int, _c_i64, _c_int, _f32p,
                                  _c_dbl, _f64p]
+        L.orc_prefill_attend.argtypes = [_f64p, _f32p, _c_int, _f32p, _c_int, _f64p,
+                                         _f32p, _c_int, _f32p, _c_int, _c_i64, _c_int,
+                                         _f32p, _i64p, _c_i64, _c_dbl, _f64p]
         _lib = L
     return _lib
 
@@ -267,6 +271,30 @@ def attend(lk, Bk, muk, lv, Bv, muv, q, scale: float) -> np.ndarray:
     return out
 
 
+def prefill_attend(lk, Bk, muk, lv, Bv, muv, q, positions, scale: float) -> np.ndarray:
+    """Causal attention of queries q [nq, D] at the given positions over the
+    reconstructed tokens (query i sees tokens 0..positions[i]); fp64 [nq, D]."""
+    lk = _c(lk, np.float64)
+    lv = _c(lv, np.float64)
+    Bk = _c(Bk, np.float32)
+    Bv = _c(Bv, np.float32)
+    n, rk = lk.shape
+    rv = lv.shape[1]
+    D = Bk.shape[0]
+    qf = half_to_float(q) if np.asarray(q).dtype in (np.float16, np.uint16) \
+        else _c(q, np.float32)
+    qf = _c(qf, np.float32).reshape(-1, D)
+    pos = _c(positions, np.int64).reshape(-1)
+    if pos.size != qf.shape[0] or (pos.size and (pos.min() < 0 or pos.max() >= n)):
+        raise ValueError("positions must give one position in [0, n) per query")
+    out = np.empty((qf.shape[0], D), np.float64)
+    if qf.shape[0]:
+        lib().orc_prefill_attend(lk, Bk, Bk.shape[1], _c(muk, np.float32), rk, lv, Bv,
+                                 Bv.shape[1], _c(muv, np.float32), rv, n, D, qf, pos,
+                                 qf.shape[0], scale, out)
+    return out
+
+
 # ------------------------------------------------------------ bit accounting
 
 def effective_bits(r: int, D: int, hi_fraction: float, hi_bit: int, lo_bit: int):
@@ -345,4 +373,23 @@ class OracleLayer:
             grp = self.group_of(h)
             out[i] = attend(lks[h], fK.V(grp), fK.mu[grp], lvs[h], fV.V(grp),
                             fV.mu[grp], q[i], scale)
+        return out
+
+    def prefill_attend(self, kstates, vstates, q, positions, scale=None):
+        """Causal prefill attention.  q fp16 [Hq, nq, D]; query j of every
+        head sits at positions[j] and sees the stored tokens 0..positions[j].
+        Returns fp64 [Hq, nq, D]."""
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.D)
+        g = self.Hq // self.Hkv
+        fK, fV = self.fit
+        nq = len(positions)
+        out = np.empty((self.Hq, nq, self.D), np.float64)
+        lks = [self.decode_head(s, 0) for s in kstates]
+        lvs = [self.decode_head(s, 1) for s in vstates]
+        for i in range(self.Hq):
+            h = i // g
+            grp = self.group_of(h)
+            out[i] = prefill_attend(lks[h], fK.V(grp), fK.mu[grp], lvs[h], fV.V(grp),
+                                    fV.mu[grp], q[i], positions, scale)
         return out

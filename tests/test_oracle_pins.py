@@ -541,6 +541,91 @@ def test_layer_gqa_head_mapping(gqa):
         np.testing.assert_allclose(out[i], expect, atol=2e-3)
 
 
+def _orthonormal(rng, D):
+    Q, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    return Q.astype(np.float32)
+
+
+def test_prefill_full_rank_equals_causal_sdpa():
+    """Orthonormal full-rank bases and exact latents (x - mu) B: the causal
+    prefill attention over the reconstruction equals torch's causal SDPA over
+    the original K/V (query i sees keys 0..i)."""
+    import torch
+    rng = np.random.default_rng(77)
+    D, n = 32, 45
+    Bk, Bv = _orthonormal(rng, D), _orthonormal(rng, D)
+    muk = rng.standard_normal(D).astype(np.float32)
+    muv = rng.standard_normal(D).astype(np.float32)
+    xk, xv = rng.standard_normal((n, D)) + 3.0, rng.standard_normal((n, D)) - 1.0
+    lk = (xk - muk) @ Bk.astype(np.float64)
+    lv = (xv - muv) @ Bv.astype(np.float64)
+    q = rng.standard_normal((n, D)).astype(np.float32)
+    out = oracle.prefill_attend(lk, Bk, muk, lv, Bv, muv, q, np.arange(n), 0.41)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64))[None], torch.from_numpy(xk)[None],
+        torch.from_numpy(xv)[None], is_causal=True, scale=0.41)[0].numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=2e-5)
+
+
+def test_prefill_rows_equal_single_query_attend_over_prefix():
+    """Query at position p equals the single-query attention over the first
+    p + 1 tokens, for any set of positions (bottom-right prefill rows,
+    group boundaries, the first and last token)."""
+    rng = np.random.default_rng(78)
+    D, rk, rv, n = 24, 5, 7, 70
+    lk, lv = rng.standard_normal((n, rk)), rng.standard_normal((n, rv))
+    Bk = rng.standard_normal((D, rk)).astype(np.float32)
+    Bv = rng.standard_normal((D, rv)).astype(np.float32)
+    muk = rng.standard_normal(D).astype(np.float32)
+    muv = rng.standard_normal(D).astype(np.float32)
+    pos = np.array([0, 1, 31, 32, 33, 63, 64, 69])
+    q = rng.standard_normal((len(pos), D)).astype(np.float32)
+    out = oracle.prefill_attend(lk, Bk, muk, lv, Bv, muv, q, pos, 0.29)
+    for i, p in enumerate(pos):
+        one = oracle.attend(lk[:p + 1], Bk, muk, lv[:p + 1], Bv, muv, q[i], 0.29)
+        np.testing.assert_allclose(out[i], one, rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.prefill_attend(lk, Bk, muk, lv, Bv, muv, q[:1], [n], 0.29)
+
+
+def test_prefill_invariants():
+    rng = np.random.default_rng(79)
+    D, r, n = 16, 3, 40
+    lk, lv = rng.standard_normal((n, r)), rng.standard_normal((n, r))
+    Bk = rng.standard_normal((D, r)).astype(np.float32)
+    Bv = rng.standard_normal((D, r)).astype(np.float32)
+    muk = rng.standard_normal(D).astype(np.float32)
+    muv = rng.standard_normal(D).astype(np.float32)
+    vhat = lv @ Bv.T.astype(np.float64) + muv
+    # zero queries -> uniform weights -> running (causal) mean of the values
+    out0 = oracle.prefill_attend(lk, Bk, muk, lv, Bv, muv, np.zeros((n, D), np.float32),
+                                 np.arange(n), 1.0)
+    np.testing.assert_allclose(out0, np.cumsum(vhat, 0) / np.arange(1, n + 1)[:, None], atol=1e-12)
+    # the first token sees only itself
+    q = rng.standard_normal((1, D)).astype(np.float32)
+    np.testing.assert_allclose(oracle.prefill_attend(lk, Bk, muk, lv, Bv, muv, q, [0], 0.5)[0],
+                               vhat[0], atol=1e-12)
+
+
+@pytest.mark.parametrize("gqa", [1, 3])
+def test_layer_prefill_last_row_equals_decode(gqa):
+    """The layer's prefill row at the last position is the layer's decode
+    attention (same head mapping, same stored state)."""
+    Hkv, n = 2, 45
+    w = synth.small_workload(batch=1, n_kv_heads=Hkv, n_q_heads=Hkv * gqa, prefill=n,
+                             n_head_groups=2, rank=8)
+    k = synth.batch_kv(w, 0, n)
+    v = synth.batch_kv(w, 1, n)
+    fk = oracle.fit(k, [n], 2, rank=8)
+    fv = oracle.fit(v, [n], 2, rank=8)
+    layer = oracle.OracleLayer(128, Hkv * gqa, Hkv, 2, fk, fv)
+    ks = [layer.encode_head(k[0, h], h, 0) for h in range(Hkv)]
+    vs = [layer.encode_head(v[0, h], h, 1) for h in range(Hkv)]
+    q = synth.queries(w, 0, 3).transpose(1, 0, 2)          # [Hq, 3, D]
+    pre = layer.prefill_attend(ks, vs, q, [n - 3, n - 2, n - 1])
+    np.testing.assert_allclose(pre[:, 2], layer.attend(ks, vs, q[:, 2]), rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------- quality
 
 def _naive_2bit_mse(x):
