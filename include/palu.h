@@ -157,6 +157,26 @@ int palu_decode_attend(palu_cache *cache, const void *q, void *out,
                        const int32_t *seq_ids, int32_t B, float softmax_scale,
                        void *stream);
 
+/* Causal prefill attention over the stored latents (PALU page, "How it
+ * works", prefill step 6: the stored latents feed the attention call that
+ * follows the encode), computed directly from the codes like
+ * palu_decode_attend.  Row b's queries are the last n_q[b] positions
+ * [len - n_q[b], len) of slot seq_ids[b] (append the prompt's K/V first);
+ * the query at position p attends to the slot's tokens 0..p.
+ *   q, out        : device fp16 [B][Hq][T_stride][D], 16-byte aligned; query
+ *                   j of row b at [b][head][j]; only j < n_q[b] is written
+ *   seq_ids       : host int32 [B] (NULL = 0..B-1); slots may repeat
+ *   n_q           : host int32 [B] (NULL = T_stride each),
+ *                   0 <= n_q[b] <= min(T_stride, len of the slot)
+ *   softmax_scale : 0 means 1/sqrt(D)
+ * Stream-ordered; reads only the cache (no scratch), so calls may overlap.
+ * fp32 scores and accumulation, fp16 weights into the value contraction.
+ * Errors: INVALID_ARG, NOT_BOUND, NOT_FITTED, CAPACITY (slot out of range or
+ * n_q beyond the slot's length), UNSUPPORTED (LDS need above 160 KiB), HIP. */
+int palu_prefill_attend(palu_cache *cache, const void *q, void *out,
+                        const int32_t *seq_ids, const int32_t *n_q, int32_t B,
+                        int32_t T_stride, float softmax_scale, void *stream);
+
 /* Tokens stored in a slot. */
 int palu_seq_len(const palu_cache *cache, int32_t seq, int32_t *len);
 

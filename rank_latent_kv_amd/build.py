@@ -24,7 +24,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
 DEVICE = [f"--offload-arch={ARCH}", "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_SOURCES = ["palu_host.cpp", "palu_eigen.cpp"]
-DEVICE_SOURCES = ["palu_kernels.hip"]
+DEVICE_SOURCES = ["palu_kernels.hip", "palu_prefill.hip"]
 
 
 def _run(cmd, verbose):

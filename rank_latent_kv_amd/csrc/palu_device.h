@@ -1,0 +1,143 @@
+// Device helpers shared by the HIP kernel sources of libpalu.so: vector
+// types, fp16 conversions, lane exchanges inside a 64-lane wave, the fp16
+// dequantisation of packed codes and exact small integer division.  Each
+// source that includes this gets its own internal copy (anonymous
+// namespace); nothing here is part of the C ABI.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+namespace palu {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+    return __half2float(__ushort_as_half(static_cast<unsigned short>(bits & 0xffffu)));
+}
+
+__device__ __forceinline__ uint32_t f2h_bits(float f) {
+    return static_cast<uint32_t>(__half_as_ushort(__float2half_rn(f)));
+}
+
+// Lane exchange inside rows of 16 lanes through DPP (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E;            // quad_perm [1,0,3,2], [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141, kDppMirror = 0x140;  // lane i <- 7-i (per 8), 15-i
+
+// Every lane of a 16-lane row gets the row's max / sum: pairs, quads, then
+// the mirrored halves of 8 and of 16 lanes.
+__device__ __forceinline__ float row_max(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    return fmaxf(v, dpp<kDppMirror>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    return v + dpp<kDppMirror>(v);
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Whole-wave max / sum, the same (wave-uniform) value in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+    v = row_max(v);
+    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row_sum(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+// floor(e / d) for 0 <= e < 2^21 and d >= 1 from a correctly rounded fp32
+// reciprocal: (e + 1/2) / d lies at least 1/(2d) away from an integer, and
+// the two roundings perturb it by at most (e + 1/2) / d * 2^-23 < 1/(2d).
+struct FastDiv {
+    float inv;   // the correctly rounded fp32 1 / d
+    __device__ explicit FastDiv(float inv_d) : inv(inv_d) {}
+    __device__ int quo(int e) const { return static_cast<int>((static_cast<float>(e) + 0.5f) * inv); }
+};
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+// Bump allocator for a workgroup's dynamic LDS (16-byte aligned pieces).
+__host__ __device__ inline int lds_take(int &o, int bytes) {
+    const int r = o;
+    o += (bytes + 15) & ~15;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// (code * scale + zero) for a pair of magic halves 1024 + code, in fp16
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t magic, uint32_t spair, uint32_t zpair) {
+    const h2 code = __builtin_bit_cast(h2, magic) - (h2){(_Float16)1024.0f, (_Float16)1024.0f};
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(code, __builtin_bit_cast(h2, spair),
+                                                                   __builtin_bit_cast(h2, zpair)));
+}
+
+[[maybe_unused]] __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
+    const h2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp16 pair, round toward zero (one instruction); used for softmax weights
+__device__ __forceinline__ uint32_t pack_rtz(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// A 32-bit constant held in a VGPR, so that three-operand ALU forms
+// (v_and_or_b32) can take it without a literal encoding.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+    return r;
+}
+
+__device__ __forceinline__ f16x8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const u4v t = {a, b, c, d};
+    return __builtin_bit_cast(f16x8, t);
+}
+
+// 8 codes of one token from a 32-bit window (channel k at bit w*k) ->
+// dequantised fp16 pairs (channel k, channel k + 4), k = 0..3.
+template <bool W4>
+__device__ __forceinline__ f16x8 dequant8(uint32_t X, const uint4 &sp, const uint4 &zp, uint32_t cm,
+                                          uint32_t magic) {
+    // 2-bit codes: move codes 4..7 (bits 8..15) up to bits 16..23
+    const uint32_t U = W4 ? X : perm_b32(X, X, 0x0C010C00u);
+    constexpr int wc = W4 ? 4 : 2;
+    return as_h8(dequant_pair((U & cm) | magic, sp.x, zp.x),
+                 dequant_pair(((U >> wc) & cm) | magic, sp.y, zp.y),
+                 dequant_pair(((U >> (2 * wc)) & cm) | magic, sp.z, zp.z),
+                 dequant_pair(((U >> (3 * wc)) & cm) | magic, sp.w, zp.w));
+}
+
+__device__ __forceinline__ f16x8 dequant8_any(uint32_t X, bool w4, const uint4 &sp, const uint4 &zp) {
+    const uint32_t U = w4 ? X : perm_b32(X, X, 0x0C010C00u);
+    const int wc = w4 ? 4 : 2;
+    const uint32_t cm = w4 ? 0x000F000Fu : 0x00030003u;
+    return as_h8(dequant_pair((U & cm) | 0x64006400u, sp.x, zp.x),
+                 dequant_pair(((U >> wc) & cm) | 0x64006400u, sp.y, zp.y),
+                 dequant_pair(((U >> (2 * wc)) & cm) | 0x64006400u, sp.z, zp.z),
+                 dequant_pair(((U >> (3 * wc)) & cm) | 0x64006400u, sp.w, zp.w));
+}
+
+}  // namespace
+}  // namespace palu

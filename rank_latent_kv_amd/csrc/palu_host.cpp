@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 #include <numeric>
 #include <string>
@@ -582,6 +583,66 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
         e = launch_combine(aa, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");
 
+    }
+    return PALU_OK;
+}
+
+PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids,
+                                 const int32_t *n_q, int32_t B, int32_t T_stride, float softmax_scale,
+                                 void *stream) {
+    if (int e = check_fitted(c)) return e;
+    if (!q || !out) return fail(PALU_ERR_INVALID_ARG, "q and out must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+        return fail(PALU_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+    if (B <= 0 || T_stride <= 0) return fail(PALU_ERR_INVALID_ARG, "B and T_stride must be positive");
+    if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
+        return fail(PALU_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    for (int b = 0; b < B; ++b) {
+        const int slot = seq_ids ? seq_ids[b] : b;
+        if (slot < 0 || slot >= c->max_batch)
+            return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " out of [0, max_batch)");
+        const int n = n_q ? n_q[b] : T_stride;
+        if (n < 0 || n > T_stride) return fail(PALU_ERR_INVALID_ARG, "n_q must be in [0, T_stride]");
+        if (n > c->len[slot])
+            return fail(PALU_ERR_CAPACITY, "n_q exceeds the tokens stored in slot " + std::to_string(slot));
+    }
+    const TensorDev kd = c->tensor_dev(0), vd = c->tensor_dev(1);
+    const size_t lds = prefill_lds_bytes(kd.r, kd.n_hi, vd.r, kd.words, vd.words);
+    if (lds > kAttendLdsMax)
+        return fail(PALU_ERR_UNSUPPORTED, "prefill workgroup needs more than 160 KiB of LDS at these ranks");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(c->D));
+    const int ks = prefill_ks(kd.r, kd.n_hi), nbv = prefill_nbv(vd.r);
+    const int qp = 64 * prefill_nq(ks, nbv) / c->gqa;   // query positions per workgroup
+    const size_t row_elems = static_cast<size_t>(c->Hq) * T_stride * c->D;
+    for (int b0 = 0; b0 < B; b0 += kMaxCallSeqs) {
+        const int nb = std::min(kMaxCallSeqs, B - b0);
+        PrefillArgs pa{};
+        pa.q = static_cast<const uint16_t *>(q) + b0 * row_elems;
+        pa.out = static_cast<uint16_t *>(out) + b0 * row_elems;
+        pa.k = kd;
+        pa.v = vd;
+        pa.B = nb;
+        pa.Hq = c->Hq;
+        pa.Hkv = c->H;
+        pa.gqa = c->gqa;
+        pa.hpg = c->hpg;
+        pa.T_stride = T_stride;
+        pa.qp = qp;
+        pa.qscale = static_cast<float>(scale * 1.4426950408889634);
+        int tiles = 0;
+        for (int i = 0; i < nb; ++i) {
+            const int slot = seq_ids ? seq_ids[b0 + i] : b0 + i;
+            pa.row[i].slot = slot;
+            pa.row[i].len = c->len[slot];
+            pa.row[i].nq = n_q ? n_q[b0 + i] : T_stride;
+            pa.row[i].sel = c->sel[slot];
+            tiles = std::max(tiles, (pa.row[i].nq + qp - 1) / qp);
+        }
+        if (tiles == 0) continue;
+        pa.tiles_max = tiles;
+        hipError_t e = launch_prefill(pa, lds, s);
+        if (e != hipSuccess) return hip_fail(e, "prefill launch");
     }
     return PALU_OK;
 }

@@ -87,6 +87,35 @@ struct AttendArgs {
     int nsplit_call[kMaxCallSeqs];     // splits of call row i (combine)
 };
 
+// One call row of a prefill attention launch: the queries are the last nq
+// positions [len - nq, len) of the slot.
+struct PrefillRow {
+    int slot, len, nq, sel;
+};
+
+struct PrefillArgs {
+    const uint16_t *q;        // fp16 [B][Hq][T_stride][D]
+    uint16_t *out;            // fp16 [B][Hq][T_stride][D]
+    TensorDev k, v;
+    int B, Hq, Hkv, gqa, hpg, T_stride;
+    int qp;                   // query positions per workgroup
+    int tiles_max;            // grid x; tiles past a row's last exit at once
+    float qscale;             // softmax scale * log2(e)
+    PrefillRow row[kMaxCallSeqs];
+};
+
+// Score K-steps (32 key-basis positions each), value blocks (16 channels,
+// one of them the all-ones column that yields the softmax denominator) and
+// query tiles per wave (16 columns each) of the prefill kernel variant that
+// serves these ranks.
+int prefill_ks(int r_k, int n_hi_k);
+int prefill_nbv(int r_v);
+int prefill_nq(int ks, int nbv);
+// LDS bytes of one prefill workgroup.
+size_t prefill_lds_bytes(int r_k, int n_hi_k, int r_v, int words_k, int words_v);
+// Grid (tiles_max, Hkv, B), 256 threads (defined in palu_prefill.hip).
+hipError_t launch_prefill(const PrefillArgs &a, size_t lds_bytes, hipStream_t s);
+
 // LDS bytes of one attend workgroup (independent of the split size).
 size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int words_k, int words_v, bool vq);
 

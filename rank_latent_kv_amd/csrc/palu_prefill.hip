@@ -1,0 +1,485 @@
+// Causal prefill attention over the latent cache, for gfx950 (MI355X).
+//
+// The PALU page ("How it works", prefill step 6) reconstructs K/V from the
+// stored latents for the attention call that follows the encode.  This
+// kernel computes that attention without materialising K or V in head
+// space.  With the query absorbed into the key basis,
+//   score(p, t) = qs q_p . (V_K l_t + mu_K) = qt_p . l_t + const(p),
+//   qt_p = qs V_K^T q_p,  qs = softmax scale * log2 e,
+// and the per-query constant cancels in the softmax.  The value side
+// accumulates o_lat = sum_t w_t lv_t in latent space and projects once at
+// the end: o = V_V o_lat / l + mu_V.
+//
+// Workgroup = (query tile x, kv head h, call row i), four waves.  Its 64 NQ
+// columns are (query position, query head) pairs: column c holds position
+// c / g and head c % g of the kv head's g query heads.  Wave w owns columns
+// [16 NQ w, 16 NQ (w + 1)) as NQ MFMA tiles of 16.  The key loop walks the
+// 32-token groups 0 .. (last position) / 32.  Each group is staged once per
+// workgroup as two fp16 tiles in LDS:
+//   key tile   [32 tokens][32 KS positions]: score-operand position order
+//              (8-channel blocks, hi blocks first, channels c0,c4,c1,c5,...
+//              inside a block; padding positions 0), matching the
+//              position-ordered fp16 key basis the query is absorbed with;
+//   value tile [16 NBV channels][32 tokens]: natural channel order; channel
+//              r_V is all ones, so the value MFMA also sums the weights.
+// A complete group comes from its packed record (code * fp16 scale + fp16
+// zero in fp16, the decode kernel's dequantisation).  The incomplete group
+// comes from the fp32 tail (or the partial fp16 record) rounded to fp16.
+// Records are copied global -> LDS two groups ahead (direct 16-byte loads
+// into LDS); tiles are built one group ahead; one barrier per group.
+//
+// Per wave and group: scores S^T[t][col] = sum_k Khat[t][k] Qt[col][k] on
+// v_mfma_f32_16x16x32_f16 (two 16-token halves, KS K-steps, NQ column
+// tiles), with the running maximum folded into the accumulator input
+// (C = -m).  Causal masking runs only on groups that reach past one of the
+// wave's positions.  The online softmax is lazy: it rescales only when a
+// group's maximum exceeds the running one by more than kPfSlack (log2
+// units).  Weights 2^(s - m) are rounded to fp16, and
+// O[col][c] += sum_t P[col][t] Vhat[t][c] runs on MFMA.  In both MFMAs the
+// K index 8 kb + 2 v + hh stands for token (or position) 16 hh + 4 kb + v,
+// the order the score accumulator already holds.
+#include "palu_device.h"
+#include "palu_internal.h"
+
+namespace palu {
+
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr float kPfSlack = 8.0f;
+constexpr int kVRow = 40;   // halves per value-tile row: 32 tokens + 8 padding
+
+__host__ __device__ inline int pf_krow(int ks) { return 32 * ks + 8; }   // halves per key-tile row
+
+struct PrefillLds {
+    int raw, raw_words;    // two raw record buffers (K record, then V record)
+    int tiles, ktile, vtile;   // two (key tile, value tile) pairs; bytes of each tile
+    int basis;             // epilogue: fp32 value basis [D][r_V] + mean [D] (aliases the above)
+    int olat;              // per wave [16 NQ][16 NBV] fp32 normalised latent outputs
+    int total;
+};
+
+__host__ __device__ inline PrefillLds prefill_lds(int ks, int nbv, int nq, int wk, int wv, int rv) {
+    PrefillLds L;
+    L.raw_words = ((wk + 3) & ~3) + 4 + ((wv + 3) & ~3) + 4;
+    L.ktile = 32 * pf_krow(ks) * 2;
+    L.vtile = 16 * nbv * kVRow * 2;
+    int a = 0;
+    L.raw = lds_take(a, 2 * L.raw_words * 4);
+    L.tiles = lds_take(a, 2 * (L.ktile + L.vtile));
+    int b = 0;
+    L.basis = lds_take(b, (kHeadDim * rv + kHeadDim) * 4);
+    int o = a > b ? a : b;
+    L.olat = lds_take(o, kPfWaves * 16 * nq * 16 * nbv * 4);
+    L.total = o;
+    return L;
+}
+
+// MFMA operand for K index 8 kb + 2 v + hh <- element 16 hh + 4 kb + v of a
+// row: lo = elements 4 kb .. 4 kb + 3, hi = elements 16 + 4 kb .. 19 + 4 kb.
+__device__ __forceinline__ f16x8 pair_operand(const uint2 &lo, const uint2 &hi) {
+    return as_h8(perm_b32(hi.x, lo.x, 0x05040100u), perm_b32(hi.x, lo.x, 0x07060302u),
+                 perm_b32(hi.y, lo.y, 0x05040100u), perm_b32(hi.y, lo.y, 0x07060302u));
+}
+
+template <int KS, int NBV, int NQ>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ln = lane & 15, kb = lane >> 4;
+    const int i = blockIdx.z, h = blockIdx.y;
+    const PrefillRow rw = a.row[i];
+    const int nq = rw.nq;
+    const int ntiles = (nq + a.qp - 1) / a.qp;
+    if (static_cast<int>(blockIdx.x) >= ntiles) return;   // whole workgroup, before any barrier
+    const int x = ntiles - 1 - static_cast<int>(blockIdx.x);   // longest tiles first
+    const int g = a.gqa, len = rw.len;
+    const int nfull = len >> 5, ntail = len & 31;
+    const int grp = h / a.hpg;
+    const int rk = a.k.r, nhk = a.k.n_hi, nlk = rk - nhk, nbh = (nhk + 7) >> 3;
+    const int nbk = nbh + ((nlk + 7) >> 3), np = 8 * nbk;
+    const int rv = a.v.r, nhv = a.v.n_hi;
+    const int WK = a.k.words, WV = a.v.words;
+    const bool vq = !a.v.fp16_latents;
+    const int kmeta = 4 * nhk + 2 * nlk, vmeta = 4 * nhv + 2 * (rv - nhv);
+    const PrefillLds L = prefill_lds(KS, NBV, NQ, WK, WV, rv);
+    constexpr int krow = 32 * KS + 8;
+
+    // ---- query columns: index qi -> position len - nq + qi; columns past
+    //      the tile or the call repeat the tile's last query and are not stored
+    const int q0 = x * a.qp;
+    const int qlast = min(q0 + a.qp, nq) - 1;
+    const int pbase = len - nq;
+    const int c_lo = wv * 16 * NQ;
+    const int pw_lo = pbase + min(q0 + c_lo / g, qlast);
+    const int pw_hi = pbase + min(q0 + (c_lo + 16 * NQ - 1) / g, qlast);
+    const int ngroups = (pbase + qlast) / 32 + 1;
+    int pcol[NQ];
+    const uint16_t *qsrc[NQ];
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
+        const int c = c_lo + 16 * t + ln, pl = c / g, hd = c - pl * g;
+        const int qi = min(q0 + pl, qlast);
+        pcol[t] = pbase + qi;
+        qsrc[t] = a.q + ((static_cast<int64_t>(i) * a.Hq + h * g + hd) * a.T_stride + qi) * kHeadDim;
+    }
+
+    const int64_t hb = static_cast<int64_t>(rw.slot) * a.Hkv + h;
+    const uint32_t *kg = a.k.records + hb * a.k.head_stride;
+    const uint32_t *vg = a.v.records + hb * a.v.head_stride;
+
+    // ---- raw records of group j (< nfull) -> raw buffer j & 1
+    auto rec_offsets = [&](int j, int &koff, int &nk4, int &voff, int &nv4) {
+        const int64_t ka = (static_cast<int64_t>(j) * WK) & ~3LL, va = (static_cast<int64_t>(j) * WV) & ~3LL;
+        koff = static_cast<int>(static_cast<int64_t>(j) * WK - ka);
+        nk4 = static_cast<int>((static_cast<int64_t>(j + 1) * WK - ka + 3) >> 2);
+        voff = 4 * nk4 + static_cast<int>(static_cast<int64_t>(j) * WV - va);
+        nv4 = static_cast<int>((static_cast<int64_t>(j + 1) * WV - va + 3) >> 2);
+    };
+    auto copy_raw = [&](int j) {
+        int koff, nk4, voff, nv4;
+        rec_offsets(j, koff, nk4, voff, nv4);
+        const u4v *ks = reinterpret_cast<const u4v *>(kg + ((static_cast<int64_t>(j) * WK) & ~3LL));
+        const u4v *vs = reinterpret_cast<const u4v *>(vg + ((static_cast<int64_t>(j) * WV) & ~3LL));
+        const int n4 = nk4 + nv4;
+        unsigned char *dst = lds + L.raw + (j & 1) * L.raw_words * 4;
+        for (int c = wv; c * 64 < n4; c += kPfWaves) {
+            const int e = c * 64 + lane;
+            if (e < n4) __builtin_amdgcn_global_load_lds(e < nk4 ? ks + e : vs + (e - nk4), dst + c * 1024, 16, 0, 0);
+        }
+    };
+
+    // ---- fp16 tiles of group j -> tile pair j & 1
+    auto build_tiles = [&](int j) {
+        _Float16 *kt = reinterpret_cast<_Float16 *>(lds + L.tiles + (j & 1) * (L.ktile + L.vtile));
+        _Float16 *vt = reinterpret_cast<_Float16 *>(lds + L.tiles + (j & 1) * (L.ktile + L.vtile) + L.ktile);
+        const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+        const uint4 ones4 = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+        if (j < nfull) {
+            int koff, nk4, voff, nv4;
+            rec_offsets(j, koff, nk4, voff, nv4);
+            const uint32_t *raw = reinterpret_cast<const uint32_t *>(lds + L.raw) + (j & 1) * L.raw_words;
+            const uint32_t *kr = raw + koff, *vr = raw + voff;
+            // keys: item = (token t, 8-position block q)
+            for (int e = tid; e < 32 * 4 * KS; e += 256) {
+                const int q = e & (4 * KS - 1), t = e / (4 * KS);
+                uint4 val = zero4;
+                if (q < nbk) {
+                    const bool w4 = q < nbh;
+                    const int base = w4 ? 32 * q : 128 * nhk + 16 * (q - nbh);
+                    const int bit = base + t * (w4 ? 4 * nhk : 2 * nlk);
+                    const uint32_t X = __builtin_amdgcn_alignbit(kr[(bit >> 5) + 1], kr[bit >> 5], bit & 31);
+                    const int chan0 = w4 ? 8 * q : nhk + 8 * (q - nbh), chanend = w4 ? nhk : rk;
+                    uint32_t sp[4], zp[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t wa = chan0 + k < chanend ? kr[kmeta + chan0 + k] : 0u;
+                        const uint32_t wb = chan0 + k + 4 < chanend ? kr[kmeta + chan0 + k + 4] : 0u;
+                        sp[k] = perm_b32(wb, wa, 0x05040100u);
+                        zp[k] = perm_b32(wb, wa, 0x07060302u);
+                    }
+                    val = __builtin_bit_cast(uint4, dequant8_any(X, w4, make_uint4(sp[0], sp[1], sp[2], sp[3]),
+                                                                 make_uint4(zp[0], zp[1], zp[2], zp[3])));
+                }
+                *reinterpret_cast<uint4 *>(kt + t * krow + 8 * q) = val;
+            }
+            // values: item = (channel c, 8-token block tb)
+            for (int e = tid; e < 16 * NBV * 4; e += 256) {
+                const int c = e >> 2, tb = e & 3;
+                uint4 val = c == rv ? ones4 : zero4;
+                if (c < rv) {
+                    if (vq) {
+                        const bool w4 = c < nhv;
+                        const int wc = w4 ? 4 : 2;
+                        const int bit = (w4 ? 128 * c : 128 * nhv + 64 * (c - nhv)) + 8 * tb * wc;
+                        const uint32_t X = __builtin_amdgcn_alignbit(vr[(bit >> 5) + 1], vr[bit >> 5], bit & 31);
+                        const uint32_t mw = vr[vmeta + c];
+                        const uint32_t spair = (mw & 0xFFFFu) | (mw << 16), zpair = (mw >> 16) | (mw & 0xFFFF0000u);
+                        const uint32_t m = w4 ? 0xFu : 0x3u;
+                        uint32_t wd[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const uint32_t lo = (X >> (2 * k * wc)) & m, hi = (X >> ((2 * k + 1) * wc)) & m;
+                            wd[k] = dequant_pair(lo | (hi << 16) | 0x64006400u, spair, zpair);
+                        }
+                        val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                    } else {
+                        val = *reinterpret_cast<const uint4 *>(vr + c * 16 + 4 * tb);
+                    }
+                }
+                *reinterpret_cast<uint4 *>(vt + c * kVRow + 8 * tb) = val;
+            }
+        } else {
+            // the incomplete group: tokens < ntail from the fp32 tails (or the
+            // partial fp16 value record), rounded to fp16; later tokens are 0
+            const float *tk = a.k.tail + (hb * 2 + rw.sel) * kTokGroup * rk;
+            for (int e = tid; e < 32 * 4 * KS; e += 256) {
+                const int q = e & (4 * KS - 1), t = e / (4 * KS);
+                uint32_t wd[4] = {0u, 0u, 0u, 0u};
+                if (q < nbk && t < ntail) {
+                    const bool w4 = q < nbh;
+                    const int chan0 = w4 ? 8 * q : nhk + 8 * (q - nbh), chanend = w4 ? nhk : rk;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float fa = chan0 + k < chanend ? tk[t * rk + chan0 + k] : 0.0f;
+                        const float fb = chan0 + k + 4 < chanend ? tk[t * rk + chan0 + k + 4] : 0.0f;
+                        wd[k] = f2h_bits(fa) | (f2h_bits(fb) << 16);
+                    }
+                }
+                *reinterpret_cast<uint4 *>(kt + t * krow + 8 * q) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            }
+            const float *tv = vq ? a.v.tail + (hb * 2 + rw.sel) * kTokGroup * rv : nullptr;
+            const uint16_t *r16 = reinterpret_cast<const uint16_t *>(vg + static_cast<int64_t>(nfull) * WV);
+            for (int e = tid; e < 16 * NBV * 4; e += 256) {
+                const int c = e >> 2, tb = e & 3;
+                uint4 val = c == rv ? ones4 : zero4;
+                if (c < rv) {
+                    uint32_t wd[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        uint32_t hv[2];
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int tok = 8 * tb + 2 * k + u;
+                            hv[u] = tok < ntail ? (vq ? f2h_bits(tv[tok * rv + c]) : static_cast<uint32_t>(r16[c * 32 + tok]))
+                                                : 0u;
+                        }
+                        wd[k] = hv[0] | (hv[1] << 16);
+                    }
+                    val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                }
+                *reinterpret_cast<uint4 *>(vt + c * kVRow + 8 * tb) = val;
+            }
+        }
+    };
+
+    // ---- prologue: records of groups 0 and 1 in flight while the query is
+    //      absorbed: qt = qs V_K^T q on MFMA, A = position-ordered key basis
+    //      rows (16 positions x 32 d), B = the column's query (32 d x 16
+    //      columns); D[position][column] packed straight into the fp16 score
+    //      operand qb (K index 8 kb + 2 v + hh <- position 32 ks + 16 hh + 4 kb + v)
+    if (nfull > 0) copy_raw(0);
+    if (nfull > 1 && ngroups > 1) copy_raw(1);
+    f16x8 qb[NQ][KS];
+    {
+        const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * np * kHeadDim;
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+            uint4 qa[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const uint4 *>(qsrc[t] + 32 * st + 8 * kb);
+            f4 acc[2 * KS];
+#pragma unroll
+            for (int blk = 0; blk < 2 * KS; ++blk) {
+                const int n = 16 * blk + ln;
+                acc[blk] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const uint4 bb = n < np ? *reinterpret_cast<const uint4 *>(bt + static_cast<int64_t>(n) * kHeadDim +
+                                                                               32 * st + 8 * kb)
+                                            : make_uint4(0u, 0u, 0u, 0u);
+                    acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(bb.x, bb.y, bb.z, bb.w),
+                                                                     as_h8(qa[st].x, qa[st].y, qa[st].z, qa[st].w),
+                                                                     acc[blk], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                uint32_t wd[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    wd[v] = pack_half2(acc[2 * ks][v] * a.qscale, acc[2 * ks + 1][v] * a.qscale);
+                qb[t][ks] = as_h8(wd[0], wd[1], wd[2], wd[3]);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    build_tiles(0);
+    __syncthreads();
+
+    // ---- key loop
+    float m_run[NQ];
+    f4 oacc[NQ][NBV];
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
+        m_run[t] = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) oacc[t][nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    for (int j = 0; j < ngroups; ++j) {
+        if (j + 2 < ngroups && j + 2 < nfull) copy_raw(j + 2);
+        if (j + 1 < ngroups) build_tiles(j + 1);
+        if (32 * j <= pw_hi) {                       // wave-uniform
+            const _Float16 *kt = reinterpret_cast<const _Float16 *>(lds + L.tiles + (j & 1) * (L.ktile + L.vtile));
+            const _Float16 *vt = reinterpret_cast<const _Float16 *>(lds + L.tiles + (j & 1) * (L.ktile + L.vtile) +
+                                                                    L.ktile);
+            f16x8 ka[2][KS];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const _Float16 *p = kt + (16 * hh + ln) * krow + 32 * ks + 4 * kb;
+                    ka[hh][ks] = pair_operand(*reinterpret_cast<const uint2 *>(p), *reinterpret_cast<const uint2 *>(p + 16));
+                }
+            }
+            f16x8 vb[NBV];
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                const _Float16 *p = vt + (16 * nb + ln) * kVRow + 4 * kb;
+                vb[nb] = pair_operand(*reinterpret_cast<const uint2 *>(p), *reinterpret_cast<const uint2 *>(p + 16));
+            }
+            const bool masked = 32 * j + 31 > pw_lo;    // wave-uniform
+#pragma unroll
+            for (int t = 0; t < NQ; ++t) {
+                const float mb = -m_run[t];
+                f4 s0 = {mb, mb, mb, mb}, s1 = s0;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[0][ks], qb[t][ks], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[1][ks], qb[t][ks], s1, 0, 0, 0);
+                }
+                float xv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+                if (masked) {
+                    const int lim = pcol[t] - 32 * j - 4 * kb;   // token 16 hh + 4 kb + v allowed iff 16 hh + v <= lim
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) xv[k] = 16 * (k >> 2) + (k & 3) <= lim ? xv[k] : -INFINITY;
+                }
+                const float mloc = fmaxf(fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3])),
+                                         fmaxf(fmaxf(xv[4], xv[5]), fmaxf(xv[6], xv[7])));
+                const bool need = j == 0 || mloc > kPfSlack;
+                if (__any(need)) {
+                    // column maximum of s - m over the 4 lanes that hold the
+                    // column; every valid column sees token 0 in group 0
+                    float mm = fmaxf(mloc, __shfl_xor(mloc, 16));
+                    mm = fmaxf(mm, __shfl_xor(mm, 32));
+                    const bool upd = j == 0 || mm > kPfSlack;
+                    const float delta = upd ? mm : 0.0f;
+                    const float alpha = j == 0 ? 0.0f : exp2f(-delta);
+                    m_run[t] += delta;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) xv[k] -= delta;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float av = __shfl(alpha, 4 * kb + v);
+#pragma unroll
+                        for (int nb = 0; nb < NBV; ++nb) oacc[t][nb][v] *= av;
+                    }
+                }
+                float pr[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(xv[k]);
+                const f16x8 pa = as_h8(pack_rtz(pr[0], pr[4]), pack_rtz(pr[1], pr[5]), pack_rtz(pr[2], pr[6]),
+                                       pack_rtz(pr[3], pr[7]));
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb)
+                    oacc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb[nb], oacc[t][nb], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);                // this wave's record copies have landed
+        __syncthreads();                              // and every wave is done with this group's tiles
+    }
+
+    // ---- normalise by the ones column (channel r_V) and park the latent
+    //      outputs: row 4 kb + v of tile t, channel 16 nb + ln
+    float *ol = reinterpret_cast<float *>(lds + L.olat) + wv * (16 * NQ) * (16 * NBV);
+    const int nbl = rv >> 4, lnl = rv & 15;
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float lq = 0.0f;
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) lq = nb == nbl ? oacc[t][nb][v] : lq;
+            lq = __shfl(lq, 16 * kb + lnl);
+            const float inv = 1.0f / lq;
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) ol[(16 * t + 4 * kb + v) * (16 * NBV) + 16 * nb + ln] = oacc[t][nb][v] * inv;
+        }
+    }
+    // value basis and mean into the (now idle) record/tile area
+    float *bl = reinterpret_cast<float *>(lds + L.basis);
+    float *ml = bl + kHeadDim * rv;
+    {
+        const float *bv = a.v.basis + static_cast<int64_t>(grp) * kHeadDim * rv;
+        const float *mv = a.v.mu + grp * kHeadDim;
+        for (int e = tid; e < kHeadDim * rv; e += 256) bl[e] = bv[e];
+        if (tid < kHeadDim) ml[tid] = mv[tid];
+    }
+    __syncthreads();
+
+    // ---- output projection o = V_V o_lat + mu_V (fp32 fma chain in channel
+    //      order), two adjacent outputs per lane, one column at a time
+    const int d0 = 2 * lane;
+    for (int col = 0; col < 16 * NQ; ++col) {
+        const int c = c_lo + col, pl = c / g, hd = c - pl * g, qi = q0 + pl;
+        if (pl >= a.qp || qi >= nq) continue;       // wave-uniform
+        const float *o = ol + col * (16 * NBV);
+        float acc0 = ml[d0], acc1 = ml[d0 + 1];
+        for (int cc = 0; cc < rv; ++cc) {
+            const float oc = o[cc];
+            acc0 = fmaf(bl[d0 * rv + cc], oc, acc0);
+            acc1 = fmaf(bl[(d0 + 1) * rv + cc], oc, acc1);
+        }
+        uint16_t *dst = a.out + ((static_cast<int64_t>(i) * a.Hq + h * g + hd) * a.T_stride + qi) * kHeadDim;
+        reinterpret_cast<uint32_t *>(dst)[lane] = f2h_bits(acc0) | (f2h_bits(acc1) << 16);
+    }
+}
+
+template <int KS, int NBV>
+hipError_t launch_prefill_t(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
+    constexpr int NQ = KS + NBV <= 3 ? 4 : (KS + NBV <= 6 ? 2 : 1);
+    static bool configured = false;
+    if (!configured) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<KS, NBV, NQ>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    hipLaunchKernelGGL((prefill_kernel<KS, NBV, NQ>), dim3(a.tiles_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
+    return hipGetLastError();
+}
+
+template <int KS>
+hipError_t launch_prefill_v(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
+    switch (prefill_nbv(a.v.r)) {
+        case 1: return launch_prefill_t<KS, 1>(a, lds_bytes, s);
+        case 2: return launch_prefill_t<KS, 2>(a, lds_bytes, s);
+        case 3: return launch_prefill_t<KS, 3>(a, lds_bytes, s);
+        case 5: return launch_prefill_t<KS, 5>(a, lds_bytes, s);
+        case 9: return launch_prefill_t<KS, 9>(a, lds_bytes, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int prefill_ks(int r_k, int n_hi_k) {
+    const int np = basis_t16_rows(r_k, n_hi_k);
+    const int ks = (np + 31) / 32;
+    return ks <= 1 ? 1 : (ks <= 2 ? 2 : 4);
+}
+
+int prefill_nbv(int r_v) {
+    const int n = (r_v + 1 + 15) / 16;
+    return n <= 1 ? 1 : n <= 2 ? 2 : n <= 3 ? 3 : n <= 5 ? 5 : 9;
+}
+
+int prefill_nq(int ks, int nbv) { return ks + nbv <= 3 ? 4 : (ks + nbv <= 6 ? 2 : 1); }
+
+size_t prefill_lds_bytes(int r_k, int n_hi_k, int r_v, int words_k, int words_v) {
+    const int ks = prefill_ks(r_k, n_hi_k), nbv = prefill_nbv(r_v);
+    return static_cast<size_t>(prefill_lds(ks, nbv, prefill_nq(ks, nbv), words_k, words_v, r_v).total);
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
+    switch (prefill_ks(a.k.r, a.k.n_hi)) {
+        case 1: return launch_prefill_v<1>(a, lds_bytes, s);
+        case 2: return launch_prefill_v<2>(a, lds_bytes, s);
+        case 4: return launch_prefill_v<4>(a, lds_bytes, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace palu

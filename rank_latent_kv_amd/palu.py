@@ -24,7 +24,8 @@ ERROR_NAMES = {1: "PALU_ERR_INVALID_ARG", 2: "PALU_ERR_UNSUPPORTED", 3: "PALU_ER
 
 EXPORTED = ["palu_config_default", "palu_cache_create", "palu_cache_required_bytes",
             "palu_cache_bind", "palu_fit", "palu_set_basis", "palu_get_basis",
-            "palu_encode_append", "palu_decode_attend", "palu_seq_len", "palu_read_codes",
+            "palu_encode_append", "palu_decode_attend", "palu_prefill_attend", "palu_seq_len",
+            "palu_read_codes",
             "palu_get_stats", "palu_reset", "palu_record_words", "palu_export_bytes",
             "palu_export_seq", "palu_import_seq", "palu_last_error", "palu_cache_destroy"]
 
@@ -82,6 +83,7 @@ def lib():
         "palu_get_basis": [_vp, _i32, _i32p, _vp, _vp, _vp],
         "palu_encode_append": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, _vp],
         "palu_decode_attend": [_vp, _vp, _vp, _i32p, _i32, ctypes.c_float, _vp],
+        "palu_prefill_attend": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, ctypes.c_float, _vp],
         "palu_seq_len": [_vp, _i32, _i32p],
         "palu_read_codes": [_vp, _i32, _i32, _i32, _vp, _sz, _vp, _sz],
         "palu_get_stats": [_vp, ctypes.POINTER(palu_stats)],
@@ -173,6 +175,14 @@ def palu_decode_attend(cache: int, q_ptr: int, out_ptr: int, seq_ids, B: int,
     s = _i32_array(seq_ids)
     _check(lib().palu_decode_attend(cache, q_ptr, out_ptr, s[1] if s else None, B,
                                     softmax_scale, stream))
+
+
+def palu_prefill_attend(cache: int, q_ptr: int, out_ptr: int, seq_ids, n_q, B: int,
+                        T_stride: int, softmax_scale: float, stream: int):
+    s = _i32_array(seq_ids)
+    n = _i32_array(n_q)
+    _check(lib().palu_prefill_attend(cache, q_ptr, out_ptr, s[1] if s else None,
+                                     n[1] if n else None, B, T_stride, softmax_scale, stream))
 
 
 def palu_seq_len(cache: int, seq: int) -> int:
@@ -316,6 +326,17 @@ class LatentKVCache:
             out = self.torch.empty_like(q)
         palu_decode_attend(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, q.shape[0],
                            softmax_scale, self._stream())
+        return out
+
+    def prefill_attend(self, q, seq_ids=None, n_q=None, softmax_scale: float = 0.0, out=None):
+        """q: fp16 [B, Hq, T, D]; row b's first n_q[b] (default T) queries
+        sit at the slot's last n_q[b] positions and attend causally.
+        Returns fp16 [B, Hq, T, D] (entries past n_q[b] are left as they were)."""
+        self._check_half(q, (self.Hq, q.shape[2], self.D), "q")
+        if out is None:
+            out = self.torch.empty_like(q)
+        palu_prefill_attend(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, n_q, q.shape[0],
+                            q.shape[2], softmax_scale, self._stream())
         return out
 
     def seq_len(self, seq: int) -> int:

@@ -150,6 +150,13 @@ def queries(w: Workload, b: int, n_steps: Optional[int] = None) -> np.ndarray:
     return rng.standard_normal((n, w.n_q_heads, w.head_dim)).astype(np.float16)
 
 
+def prefill_queries(w: Workload, b: int, n: int) -> np.ndarray:
+    """Prefill queries of sequence b, one per prompt position: fp16
+    [n_q_heads, n, D], N(0, 1) like the decode queries."""
+    rng = np.random.default_rng([w.seed, 19, b])
+    return rng.standard_normal((w.n_q_heads, n, w.head_dim), dtype=np.float32).astype(np.float16)
+
+
 def batch_kv(w: Workload, tensor: int, n_tokens: int, seqs=None) -> np.ndarray:
     """[len(seqs), n_kv_heads, n_tokens, D] fp16 (each sequence's own stream,
     truncated or generated to n_tokens positions)."""
