@@ -25,6 +25,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_SOURCES = ["palu_host.cpp", "palu_eigen.cpp"]
 DEVICE_SOURCES = ["palu_kernels.hip", "palu_prefill.hip"]
+# Per-source extras.  The prefill kernel's inputs are never NaN (reading the
+# max of MFMA results needs no quieting), and its MFMA accumulators stay in
+# ordinary VGPRs (no AGPR copies around the softmax).
+SOURCE_FLAGS = {"palu_prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd, verbose):
@@ -45,7 +49,8 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in DEVICE_SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        _run([HIPCC, *COMMON, *DEVICE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run([HIPCC, *COMMON, *DEVICE, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj],
+             verbose)
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(objdir, src + ".o")

@@ -51,7 +51,7 @@ struct palu_cache {
     int D = 0, H = 0, Hq = 0, G = 0, hpg = 0, gqa = 0, r_max = 0, max_groups = 0;
     int gram_nb_cap = 0;
     // byte offsets of each region inside the bound buffer
-    size_t off_basis[2]{}, off_bt16[2]{}, off_mu[2]{}, off_rec[2]{}, off_tail[2]{};
+    size_t off_basis[2]{}, off_bt16[2]{}, off_bcm[2]{}, off_mu[2]{}, off_rec[2]{}, off_tail[2]{};
     size_t off_gram_part = 0, off_gram_out = 0, off_seg = 0, off_attend = 0, total = 0;
     char *dev = nullptr;
     size_t dev_bytes = 0;
@@ -77,6 +77,7 @@ struct palu_cache {
         d.tail = quantized(t) ? reinterpret_cast<float *>(dev + off_tail[t]) : nullptr;
         d.basis = reinterpret_cast<float *>(dev + off_basis[t]);
         d.basis_t16 = reinterpret_cast<uint16_t *>(dev + off_bt16[t]);
+        d.basis_cm = reinterpret_cast<float *>(dev + off_bcm[t]);
         d.mu = reinterpret_cast<float *>(dev + off_mu[t]);
         return d;
     }
@@ -138,6 +139,17 @@ int upload_basis(palu_cache *c, int t) {
     e = hipMemcpy(c->dev + c->off_mu[t], c->mu_h[t].data(), c->mu_h[t].size() * sizeof(float),
                   hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "mean upload");
+    {
+        // channel-major copy [G][r][D]
+        const int G = c->G, D = c->D, rr = c->r[t];
+        std::vector<float> cm(static_cast<size_t>(G) * rr * D);
+        for (int g = 0; g < G; ++g)
+            for (int d = 0; d < D; ++d)
+                for (int k = 0; k < rr; ++k)
+                    cm[(static_cast<size_t>(g) * rr + k) * D + d] = c->basis_h[t][(static_cast<size_t>(g) * D + d) * rr + k];
+        e = hipMemcpy(c->dev + c->off_bcm[t], cm.data(), cm.size() * sizeof(float), hipMemcpyHostToDevice);
+        if (e != hipSuccess) return hip_fail(e, "channel-major basis upload");
+    }
     e = launch_basis_t16(reinterpret_cast<const float *>(c->dev + c->off_basis[t]),
                          reinterpret_cast<uint16_t *>(c->dev + c->off_bt16[t]), c->G, c->r[t],
                          n_hi_of(c->r[t], c->cfg.hi_fraction), nullptr);
@@ -202,6 +214,7 @@ PALU_API int palu_cache_create(const palu_config *cfg, int32_t max_batch, int32_
     for (int t = 0; t < 2; ++t) {
         c->off_basis[t] = take(sizeof(float) * c->G * c->D * c->r_max);
         c->off_bt16[t] = take(sizeof(uint16_t) * c->G * c->D * (c->r_max + 16));   // >= basis_t16_rows
+        c->off_bcm[t] = take(sizeof(float) * c->G * c->D * c->r_max);
         c->off_mu[t] = take(sizeof(float) * c->G * c->D);
         const size_t head_words = (static_cast<size_t>(c->max_groups) * c->words_for(t, c->r_max) + 3) / 4 * 4;
         c->off_rec[t] = take(sizeof(uint32_t) * static_cast<size_t>(max_batch) * c->H * head_words);

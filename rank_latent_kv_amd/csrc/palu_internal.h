@@ -30,6 +30,7 @@ struct TensorDev {
     uint16_t *basis_t16; // [G][P][D] fp16 copy, row n = channel of score-operand position n
                          // (8-channel blocks, hi blocks first, [c0,c4,c1,c5,..] inside a
                          // block; zero rows for padding), P = 8 * blocks (query absorption)
+    float *basis_cm;     // [G][r][D] fp32, channel-major copy (output projection)
     float *mu;           // [G][D] fp32
     int r, n_hi, words;
     int fp16_latents;    // V stored as fp16 latents (no tail, no meta)

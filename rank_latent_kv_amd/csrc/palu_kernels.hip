@@ -1025,17 +1025,17 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
     const int lane = threadIdx.x;
     const int qh = blockIdx.x, i = blockIdx.y;   // grid (Hq, B)
     // all argument loads issued together (one scalar round trip)
-    asm volatile("" ::"s"(a.partial), "s"(a.out), "s"(a.v.basis), "s"(a.v.mu), "s"(a.v.r), "s"(a.gqa),
+    asm volatile("" ::"s"(a.partial), "s"(a.out), "s"(a.v.basis_cm), "s"(a.v.mu), "s"(a.v.r), "s"(a.gqa),
                  "s"(a.hpg), "s"(a.Hq), "s"(a.nsplit_call[i]));
     const int h = qh / a.gqa, grp = h / a.hpg, ns = a.nsplit_call[i], rv = a.v.r;
     const int np = ns * (rv + 2), npa = (np + 3) & ~3;
     float *pl = cl;                            // [ns][rv + 2]: m, l, o_lat
-    float *bl = cl + npa;                      // [D][rv] value basis
+    float *bl = cl + npa;                      // [rv][D] value basis (channel-major)
     float *ml = bl + kHeadDim * rv;            // [D] value mean
     float *wl = ml + kHeadDim;                 // [ns] split weights
     float *ol = wl + ((ns + 3) & ~3);          // [rv] merged latent output
     const float *part = a.partial + (static_cast<int64_t>(i) * a.Hq + qh) * kMaxSplits * (rv + 2);
-    const float *bv = a.v.basis + static_cast<int64_t>(grp) * kHeadDim * rv;
+    const float *bv = a.v.basis_cm + static_cast<int64_t>(grp) * rv * kHeadDim;
     const float *mv = a.v.mu + grp * kHeadDim;
 
     // 1. copy to LDS: whole 16-byte pieces of the partials, the basis
@@ -1092,8 +1092,9 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
     float o0 = ml[d0], o1 = ml[d0 + 1];
     for (int c = 0; c < rv; ++c) {
         const float oc = ol[c];
-        o0 = fmaf(bl[d0 * rv + c], oc, o0);
-        o1 = fmaf(bl[(d0 + 1) * rv + c], oc, o1);
+        const float2 b = *reinterpret_cast<const float2 *>(bl + c * kHeadDim + d0);   // conflict-free
+        o0 = fmaf(b.x, oc, o0);
+        o1 = fmaf(b.y, oc, o1);
     }
     reinterpret_cast<uint32_t *>(a.out + (static_cast<int64_t>(i) * a.Hq + qh) * kHeadDim)[lane] =
         f2h_bits(o0) | (f2h_bits(o1) << 16);

@@ -75,6 +75,12 @@ __host__ __device__ inline PrefillLds prefill_lds(int ks, int nbv, int nq, int w
     return L;
 }
 
+// Query tiles per wave: the query operand (4 KS registers per tile) and the
+// value accumulators (4 NBV per tile) stay within about 64 registers.
+__host__ __device__ constexpr int prefill_nq_c(int ks, int nbv) {
+    return 16 / (ks + nbv) >= 4 ? 4 : (16 / (ks + nbv) >= 2 ? 2 : 1);
+}
+
 // MFMA operand for K index 8 kb + 2 v + hh <- element 16 hh + 4 kb + v of a
 // row: lo = elements 4 kb .. 4 kb + 3, hi = elements 16 + 4 kb .. 19 + 4 kb.
 __device__ __forceinline__ f16x8 pair_operand(const uint2 &lo, const uint2 &hi) {
@@ -150,27 +156,36 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // ---- fp16 tiles of group j -> tile pair j & 1
+    // ---- fp16 tiles of group j -> tile pair j & 1 (data parts only).  The
+    //      items come in rounds of 64 (one per lane): key rounds, then value
+    //      rounds; round r goes to wave (j + r) % 4, so whole waves build
+    //      (no partly filled item loops in every wave) and the building
+    //      rotates over the waves from group to group.
+    const int nrk = (32 * nbk + 63) >> 6, nrv = (4 * rv + 63) >> 6;
     auto build_tiles = [&](int j) {
         _Float16 *kt = reinterpret_cast<_Float16 *>(lds + L.tiles + (j & 1) * (L.ktile + L.vtile));
         _Float16 *vt = reinterpret_cast<_Float16 *>(lds + L.tiles + (j & 1) * (L.ktile + L.vtile) + L.ktile);
-        const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-        const uint4 ones4 = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-        if (j < nfull) {
-            int koff, nk4, voff, nv4;
-            rec_offsets(j, koff, nk4, voff, nv4);
-            const uint32_t *raw = reinterpret_cast<const uint32_t *>(lds + L.raw) + (j & 1) * L.raw_words;
-            const uint32_t *kr = raw + koff, *vr = raw + voff;
-            // keys: item = (token t, 8-position block q)
-            for (int e = tid; e < 32 * 4 * KS; e += 256) {
-                const int q = e & (4 * KS - 1), t = e / (4 * KS);
-                uint4 val = zero4;
-                if (q < nbk) {
-                    const bool w4 = q < nbh;
+        const bool full = j < nfull;
+        int koff = 0, nk4 = 0, voff = 0, nv4 = 0;
+        if (full) rec_offsets(j, koff, nk4, voff, nv4);
+        const uint32_t *raw = reinterpret_cast<const uint32_t *>(lds + L.raw) + (j & 1) * L.raw_words;
+        const uint32_t *kr = raw + koff, *vr = raw + voff;
+        const float *tk = a.k.tail + (hb * 2 + rw.sel) * kTokGroup * rk;
+        const float *tv = vq ? a.v.tail + (hb * 2 + rw.sel) * kTokGroup * rv : nullptr;
+        const uint16_t *r16 = reinterpret_cast<const uint16_t *>(vg + static_cast<int64_t>(nfull) * WV);
+        for (int r = (wv - j) & (kPfWaves - 1); r < nrk + nrv; r += kPfWaves) {
+            if (r < nrk) {
+                // key item: (8-position block q < nbk, token t)
+                const int e = 64 * r + lane;
+                if (e >= 32 * nbk) continue;
+                const int q = e >> 5, t = e & 31;
+                const bool w4 = q < nbh;
+                const int chan0 = w4 ? 8 * q : nhk + 8 * (q - nbh), chanend = w4 ? nhk : rk;
+                uint4 val;
+                if (full) {
                     const int base = w4 ? 32 * q : 128 * nhk + 16 * (q - nbh);
                     const int bit = base + t * (w4 ? 4 * nhk : 2 * nlk);
                     const uint32_t X = __builtin_amdgcn_alignbit(kr[(bit >> 5) + 1], kr[bit >> 5], bit & 31);
-                    const int chan0 = w4 ? 8 * q : nhk + 8 * (q - nbh), chanend = w4 ? nhk : rk;
                     uint32_t sp[4], zp[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
@@ -181,60 +196,44 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                     }
                     val = __builtin_bit_cast(uint4, dequant8_any(X, w4, make_uint4(sp[0], sp[1], sp[2], sp[3]),
                                                                  make_uint4(zp[0], zp[1], zp[2], zp[3])));
-                }
-                *reinterpret_cast<uint4 *>(kt + t * krow + 8 * q) = val;
-            }
-            // values: item = (channel c, 8-token block tb)
-            for (int e = tid; e < 16 * NBV * 4; e += 256) {
-                const int c = e >> 2, tb = e & 3;
-                uint4 val = c == rv ? ones4 : zero4;
-                if (c < rv) {
-                    if (vq) {
-                        const bool w4 = c < nhv;
-                        const int wc = w4 ? 4 : 2;
-                        const int bit = (w4 ? 128 * c : 128 * nhv + 64 * (c - nhv)) + 8 * tb * wc;
-                        const uint32_t X = __builtin_amdgcn_alignbit(vr[(bit >> 5) + 1], vr[bit >> 5], bit & 31);
-                        const uint32_t mw = vr[vmeta + c];
-                        const uint32_t spair = (mw & 0xFFFFu) | (mw << 16), zpair = (mw >> 16) | (mw & 0xFFFF0000u);
-                        const uint32_t m = w4 ? 0xFu : 0x3u;
-                        uint32_t wd[4];
+                } else {
+                    // incomplete group: fp32 tail rounded to fp16, 0 past ntail
+                    uint32_t wd[4] = {0u, 0u, 0u, 0u};
+                    if (t < ntail) {
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
-                            const uint32_t lo = (X >> (2 * k * wc)) & m, hi = (X >> ((2 * k + 1) * wc)) & m;
-                            wd[k] = dequant_pair(lo | (hi << 16) | 0x64006400u, spair, zpair);
+                            const float fa = chan0 + k < chanend ? tk[t * rk + chan0 + k] : 0.0f;
+                            const float fb = chan0 + k + 4 < chanend ? tk[t * rk + chan0 + k + 4] : 0.0f;
+                            wd[k] = f2h_bits(fa) | (f2h_bits(fb) << 16);
                         }
-                        val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-                    } else {
-                        val = *reinterpret_cast<const uint4 *>(vr + c * 16 + 4 * tb);
                     }
+                    val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
                 }
-                *reinterpret_cast<uint4 *>(vt + c * kVRow + 8 * tb) = val;
-            }
-        } else {
-            // the incomplete group: tokens < ntail from the fp32 tails (or the
-            // partial fp16 value record), rounded to fp16; later tokens are 0
-            const float *tk = a.k.tail + (hb * 2 + rw.sel) * kTokGroup * rk;
-            for (int e = tid; e < 32 * 4 * KS; e += 256) {
-                const int q = e & (4 * KS - 1), t = e / (4 * KS);
-                uint32_t wd[4] = {0u, 0u, 0u, 0u};
-                if (q < nbk && t < ntail) {
-                    const bool w4 = q < nbh;
-                    const int chan0 = w4 ? 8 * q : nhk + 8 * (q - nbh), chanend = w4 ? nhk : rk;
+                *reinterpret_cast<uint4 *>(kt + t * krow + 8 * q) = val;
+            } else {
+                // value item: (channel c < r_V, 8-token block tb)
+                const int e = 64 * (r - nrk) + lane;
+                if (e >= 4 * rv) continue;
+                const int c = e >> 2, tb = e & 3;
+                uint4 val;
+                if (full && vq) {
+                    const bool w4 = c < nhv;
+                    const int wc = w4 ? 4 : 2;
+                    const int bit = (w4 ? 128 * c : 128 * nhv + 64 * (c - nhv)) + 8 * tb * wc;
+                    const uint32_t X = __builtin_amdgcn_alignbit(vr[(bit >> 5) + 1], vr[bit >> 5], bit & 31);
+                    const uint32_t mw = vr[vmeta + c];
+                    const uint32_t spair = (mw & 0xFFFFu) | (mw << 16), zpair = (mw >> 16) | (mw & 0xFFFF0000u);
+                    const uint32_t m = w4 ? 0xFu : 0x3u;
+                    uint32_t wd[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
-                        const float fa = chan0 + k < chanend ? tk[t * rk + chan0 + k] : 0.0f;
-                        const float fb = chan0 + k + 4 < chanend ? tk[t * rk + chan0 + k + 4] : 0.0f;
-                        wd[k] = f2h_bits(fa) | (f2h_bits(fb) << 16);
+                        const uint32_t lo = (X >> (2 * k * wc)) & m, hi = (X >> ((2 * k + 1) * wc)) & m;
+                        wd[k] = dequant_pair(lo | (hi << 16) | 0x64006400u, spair, zpair);
                     }
-                }
-                *reinterpret_cast<uint4 *>(kt + t * krow + 8 * q) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-            }
-            const float *tv = vq ? a.v.tail + (hb * 2 + rw.sel) * kTokGroup * rv : nullptr;
-            const uint16_t *r16 = reinterpret_cast<const uint16_t *>(vg + static_cast<int64_t>(nfull) * WV);
-            for (int e = tid; e < 16 * NBV * 4; e += 256) {
-                const int c = e >> 2, tb = e & 3;
-                uint4 val = c == rv ? ones4 : zero4;
-                if (c < rv) {
+                    val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                } else if (full) {
+                    val = *reinterpret_cast<const uint4 *>(vr + c * 16 + 4 * tb);
+                } else {
                     uint32_t wd[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
@@ -253,6 +252,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             }
         }
     };
+
+    // ---- the tiles' constant parts, written once for both buffers: key
+    //      positions past the last channel block are 0; value channel r_V is
+    //      all ones and the channels after it are 0
+    for (int e = tid; e < 2 * 32 * (4 * KS - nbk); e += 256) {
+        const int bf = e & 1, r = e >> 1, t = r & 31, q = nbk + (r >> 5);
+        *reinterpret_cast<uint4 *>(lds + L.tiles + bf * (L.ktile + L.vtile) + (t * krow + 8 * q) * 2) =
+            make_uint4(0u, 0u, 0u, 0u);
+    }
+    for (int e = tid; e < 2 * 4 * (16 * NBV - rv); e += 256) {
+        const int bf = e & 1, r = e >> 1, tb = r & 3, c = rv + (r >> 2);
+        const uint32_t w = c == rv ? 0x3C003C00u : 0u;
+        *reinterpret_cast<uint4 *>(lds + L.tiles + bf * (L.ktile + L.vtile) + L.ktile + (c * kVRow + 8 * tb) * 2) =
+            make_uint4(w, w, w, w);
+    }
 
     // ---- prologue: records of groups 0 and 1 in flight while the query is
     //      absorbed: qt = qs V_K^T q on MFMA, A = position-ordered key basis
@@ -300,11 +314,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     __syncthreads();
 
     // ---- key loop
-    float m_run[NQ];
+    f4 negm[NQ];            // -(running maximum) of each column, as the score MFMA's C operand
     f4 oacc[NQ][NBV];
 #pragma unroll
     for (int t = 0; t < NQ; ++t) {
-        m_run[t] = 0.0f;
+        negm[t] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb) oacc[t][nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -333,8 +347,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             const bool masked = 32 * j + 31 > pw_lo;    // wave-uniform
 #pragma unroll
             for (int t = 0; t < NQ; ++t) {
-                const float mb = -m_run[t];
-                f4 s0 = {mb, mb, mb, mb}, s1 = s0;
+                f4 s0 = negm[t], s1 = negm[t];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[0][ks], qb[t][ks], s0, 0, 0, 0);
@@ -348,8 +361,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 }
                 const float mloc = fmaxf(fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3])),
                                          fmaxf(fmaxf(xv[4], xv[5]), fmaxf(xv[6], xv[7])));
-                const bool need = j == 0 || mloc > kPfSlack;
-                if (__any(need)) {
+                if (j == 0 || __builtin_amdgcn_ballot_w64(mloc > kPfSlack) != 0) {
                     // column maximum of s - m over the 4 lanes that hold the
                     // column; every valid column sees token 0 in group 0
                     float mm = fmaxf(mloc, __shfl_xor(mloc, 16));
@@ -357,7 +369,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                     const bool upd = j == 0 || mm > kPfSlack;
                     const float delta = upd ? mm : 0.0f;
                     const float alpha = j == 0 ? 0.0f : exp2f(-delta);
-                    m_run[t] += delta;
+                    negm[t] -= (f4){delta, delta, delta, delta};
 #pragma unroll
                     for (int k = 0; k < 8; ++k) xv[k] -= delta;
 #pragma unroll
@@ -398,19 +410,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             for (int nb = 0; nb < NBV; ++nb) ol[(16 * t + 4 * kb + v) * (16 * NBV) + 16 * nb + ln] = oacc[t][nb][v] * inv;
         }
     }
-    // value basis and mean into the (now idle) record/tile area
+    // channel-major value basis [r_V][D] and mean into the (now idle)
+    //      record/tile area, 16 bytes per thread and step
     float *bl = reinterpret_cast<float *>(lds + L.basis);
     float *ml = bl + kHeadDim * rv;
     {
-        const float *bv = a.v.basis + static_cast<int64_t>(grp) * kHeadDim * rv;
-        const float *mv = a.v.mu + grp * kHeadDim;
-        for (int e = tid; e < kHeadDim * rv; e += 256) bl[e] = bv[e];
-        if (tid < kHeadDim) ml[tid] = mv[tid];
+        const float4 *bv = reinterpret_cast<const float4 *>(a.v.basis_cm + static_cast<int64_t>(grp) * rv * kHeadDim);
+        for (int e = tid; e < kHeadDim * rv / 4; e += 256) reinterpret_cast<float4 *>(bl)[e] = bv[e];
+        if (tid < kHeadDim) ml[tid] = a.v.mu[grp * kHeadDim + tid];
     }
     __syncthreads();
 
     // ---- output projection o = V_V o_lat + mu_V (fp32 fma chain in channel
-    //      order), two adjacent outputs per lane, one column at a time
+    //      order), two adjacent outputs per lane (8 consecutive bytes of a
+    //      basis row: conflict-free LDS reads), one column at a time
     const int d0 = 2 * lane;
     for (int col = 0; col < 16 * NQ; ++col) {
         const int c = c_lo + col, pl = c / g, hd = c - pl * g, qi = q0 + pl;
@@ -419,8 +432,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         float acc0 = ml[d0], acc1 = ml[d0 + 1];
         for (int cc = 0; cc < rv; ++cc) {
             const float oc = o[cc];
-            acc0 = fmaf(bl[d0 * rv + cc], oc, acc0);
-            acc1 = fmaf(bl[(d0 + 1) * rv + cc], oc, acc1);
+            const float2 b = *reinterpret_cast<const float2 *>(bl + cc * kHeadDim + d0);
+            acc0 = fmaf(b.x, oc, acc0);
+            acc1 = fmaf(b.y, oc, acc1);
         }
         uint16_t *dst = a.out + ((static_cast<int64_t>(i) * a.Hq + h * g + hd) * a.T_stride + qi) * kHeadDim;
         reinterpret_cast<uint32_t *>(dst)[lane] = f2h_bits(acc0) | (f2h_bits(acc1) << 16);
@@ -429,7 +443,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
 template <int KS, int NBV>
 hipError_t launch_prefill_t(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
-    constexpr int NQ = KS + NBV <= 3 ? 4 : (KS + NBV <= 6 ? 2 : 1);
+    constexpr int NQ = prefill_nq_c(KS, NBV);
     static bool configured = false;
     if (!configured) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<KS, NBV, NQ>),
@@ -466,7 +480,7 @@ int prefill_nbv(int r_v) {
     return n <= 1 ? 1 : n <= 2 ? 2 : n <= 3 ? 3 : n <= 5 ? 5 : 9;
 }
 
-int prefill_nq(int ks, int nbv) { return ks + nbv <= 3 ? 4 : (ks + nbv <= 6 ? 2 : 1); }
+int prefill_nq(int ks, int nbv) { return prefill_nq_c(ks, nbv); }
 
 size_t prefill_lds_bytes(int r_k, int n_hi_k, int r_v, int words_k, int words_v) {
     const int ks = prefill_ks(r_k, n_hi_k), nbv = prefill_nbv(r_v);
