@@ -49,6 +49,7 @@ constexpr int kPfWaves = 4;
 constexpr float kPfSlack = 8.0f;
 constexpr int kVRow = 40;   // halves per value-tile row: 32 tokens + 8 padding
 
+
 __host__ __device__ inline int pf_krow(int ks) { return 32 * ks + 8; }   // halves per key-tile row
 
 struct PrefillLds {
@@ -345,6 +346,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 vb[nb] = pair_operand(*reinterpret_cast<const uint2 *>(p), *reinterpret_cast<const uint2 *>(p + 16));
             }
             const bool masked = 32 * j + 31 > pw_lo;    // wave-uniform
+            // (a) every tile's scores first (the softmax of tile t then finds
+            //     its MFMA results long done); running max as the C operand
+            float xv[NQ][8];
 #pragma unroll
             for (int t = 0; t < NQ; ++t) {
                 f4 s0 = negm[t], s1 = negm[t];
@@ -353,25 +357,42 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[0][ks], qb[t][ks], s0, 0, 0, 0);
                     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[1][ks], qb[t][ks], s1, 0, 0, 0);
                 }
-                float xv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-                if (masked) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    xv[t][v] = s0[v];
+                    xv[t][4 + v] = s1[v];
+                }
+            }
+            // (b) causal mask on the groups that reach past a column's position
+            if (masked) {
+#pragma unroll
+                for (int t = 0; t < NQ; ++t) {
                     const int lim = pcol[t] - 32 * j - 4 * kb;   // token 16 hh + 4 kb + v allowed iff 16 hh + v <= lim
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) xv[k] = 16 * (k >> 2) + (k & 3) <= lim ? xv[k] : -INFINITY;
+                    for (int k = 0; k < 8; ++k) xv[t][k] = 16 * (k >> 2) + (k & 3) <= lim ? xv[t][k] : -INFINITY;
                 }
-                const float mloc = fmaxf(fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3])),
-                                         fmaxf(fmaxf(xv[4], xv[5]), fmaxf(xv[6], xv[7])));
-                if (j == 0 || __builtin_amdgcn_ballot_w64(mloc > kPfSlack) != 0) {
+            }
+            // (c) lazy rescale: one test for the whole wave and all tiles
+            float mloc[NQ], mall = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < NQ; ++t) {
+                mloc[t] = fmaxf(fmaxf(fmaxf(xv[t][0], xv[t][1]), fmaxf(xv[t][2], xv[t][3])),
+                                fmaxf(fmaxf(xv[t][4], xv[t][5]), fmaxf(xv[t][6], xv[t][7])));
+                mall = fmaxf(mall, mloc[t]);
+            }
+            if (j == 0 || __builtin_amdgcn_ballot_w64(mall > kPfSlack) != 0) {
+#pragma unroll
+                for (int t = 0; t < NQ; ++t) {
                     // column maximum of s - m over the 4 lanes that hold the
                     // column; every valid column sees token 0 in group 0
-                    float mm = fmaxf(mloc, __shfl_xor(mloc, 16));
+                    float mm = fmaxf(mloc[t], __shfl_xor(mloc[t], 16));
                     mm = fmaxf(mm, __shfl_xor(mm, 32));
                     const bool upd = j == 0 || mm > kPfSlack;
                     const float delta = upd ? mm : 0.0f;
                     const float alpha = j == 0 ? 0.0f : exp2f(-delta);
                     negm[t] -= (f4){delta, delta, delta, delta};
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) xv[k] -= delta;
+                    for (int k = 0; k < 8; ++k) xv[t][k] -= delta;
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const float av = __shfl(alpha, 4 * kb + v);
@@ -379,9 +400,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                         for (int nb = 0; nb < NBV; ++nb) oacc[t][nb][v] *= av;
                     }
                 }
+            }
+            // (d) weights 2^(s - m) in fp16 and the value contraction
+#pragma unroll
+            for (int t = 0; t < NQ; ++t) {
                 float pr[8];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(xv[k]);
+                for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(xv[t][k]);
                 const f16x8 pa = as_h8(pack_rtz(pr[0], pr[4]), pack_rtz(pr[1], pr[5]), pack_rtz(pr[2], pr[6]),
                                        pack_rtz(pr[3], pr[7]));
 #pragma unroll
