@@ -4,6 +4,7 @@ One step = one pass of the whole path over the long-context workload
 (4 sequences x 32768 prefill tokens, 32 query / 8 kv heads, D = 128, 4 head
 groups, 90%-energy rank, 64 decode steps):
   fit (Gram kernels + host eigensolve) -> encode of the prefill ->
+  causal prefill attention of every prompt position over the latent cache ->
   64 x (append one token per sequence -> decode-attend).
 All inputs are resident in HBM before the timed region.
 
@@ -13,7 +14,10 @@ library launches on, around every decode-attend call.  The roofline object
 prices the decode-attend call against MI355X's 8 TB/s HBM with the
 algorithmic bytes of each call (packed codes + metadata + fp32 tails + bases
 and means + query and output).  The CPU baseline times the plain oracle's
-decode attention for one sequence on the host.
+decode attention for one sequence on the host.  The prefill-attention
+object reports its time and score pairs per second (query head x key pairs
+under the causal mask) against the vector-ALU issue rate, counting 2.5 lane
+operations per pair (exp2, running max, half an fp16 conversion).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -32,6 +36,13 @@ sys.path.insert(0, ROOT)
 from rank_latent_kv_amd import synth  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+# Non-packed fp32 VALU issue rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz (the published 157.3 TFLOP/s counts packed fp32 FMAs: x2 x2).
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Lane operations a causal softmax pair needs at least on the vector unit:
+# one exp2, one running-max comparison and half of an fp32 -> fp16 pair
+# conversion (the two contractions run on the matrix cores).
+PREFILL_OPS_PER_PAIR = 2.5
 METRIC = "latent decode-attend tok/s + HBM GB/s (% of peak); encode Mtok/s"
 
 
@@ -131,18 +142,24 @@ def main():
         if b == 0:
             host_k0, host_v0 = kb, vb
     q_all = torch.from_numpy(np.stack([synth.queries(w, b, T) for b in range(w.batch)], axis=1)).to(dev)
+    # prefill queries: one per prompt position and query head
+    qpre = torch.zeros((w.batch, w.n_q_heads, S, w.head_dim), dtype=torch.float16, device=dev)
+    for b in range(w.batch):
+        qpre[b, :, :lens[b]] = torch.from_numpy(synth.prefill_queries(w, b, int(lens[b]))).to(dev)
     gen_s = time.time() - t0
 
     cache = LatentKVCache(w.head_dim, w.n_kv_heads, w.n_q_heads, w.n_head_groups, w.batch,
                           S + T, rank=w.rank or 0, energy_threshold=w.energy,
                           quantize_values=w.quantize_values)
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+    out_pre = torch.empty_like(qpre)
     stream = torch.cuda.current_stream(dev)
 
     def one_pass(record):
         ev = []
         e_fit0 = torch.cuda.Event(enable_timing=True)
         e_fit0.record(stream)
+        torch.cuda.synchronize()       # the fit is host-synchronous: time it alone
         t_fit = time.perf_counter()
         cache.fit(kpre, vpre, lens)
         t_fit = time.perf_counter() - t_fit
@@ -151,6 +168,9 @@ def main():
         e_enc0.record(stream)
         cache.encode_append(kpre, vpre, n_new=lens)
         e_enc1.record(stream)
+        cache.prefill_attend(qpre, n_q=lens, out=out_pre)
+        e_pre1 = torch.cuda.Event(enable_timing=True)
+        e_pre1.record(stream)
         for t in range(T):
             ea = torch.cuda.Event(enable_timing=True)
             eb = torch.cuda.Event(enable_timing=True)
@@ -161,21 +181,22 @@ def main():
             cache.decode_attend(q_all[t], out=out)
             ec.record(stream)
             ev.append((ea, eb, ec))
-        return t_fit, (e_enc0, e_enc1), ev
+        return t_fit, (e_enc0, e_enc1, e_pre1), ev
 
     for _ in range(args.warmup):
         one_pass(False)
     torch.cuda.synchronize()
 
-    fit_s, enc_ms, app_ms, att_ms = [], [], [], []
+    fit_s, enc_ms, pre_ms, app_ms, att_ms = [], [], [], [], []
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     results = [one_pass(True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    for t_fit, (e0, e1), ev in results:
+    for t_fit, (e0, e1, e2), ev in results:
         fit_s.append(t_fit)
         enc_ms.append(e0.elapsed_time(e1))
+        pre_ms.append(e1.elapsed_time(e2))
         for ea, eb, ec in ev:
             app_ms.append(ea.elapsed_time(eb))
             att_ms.append(eb.elapsed_time(ec))
@@ -191,6 +212,10 @@ def main():
     achieved_gbps = mean_bytes / (att_mean_ms / 1e3) / 1e9
     enc_positions = float(lens.sum())
     encode_mtok_s = enc_positions / (float(np.mean(enc_ms)) / 1e3) / 1e6
+
+    pairs = float(sum(int(n) * (int(n) + 1) // 2 for n in lens)) * w.n_q_heads
+    pre_mean_ms = float(np.mean(pre_ms))
+    pre_ops = pairs * PREFILL_OPS_PER_PAIR / (pre_mean_ms / 1e3) / 1e12
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -220,6 +245,12 @@ def main():
         "decode_attend_us": round(att_mean_ms * 1e3, 2),
         "append_us": round(float(np.mean(app_ms)) * 1e3, 2),
         "encode_mtok_s": round(encode_mtok_s, 2),
+        "prefill_attend": {"ms": round(pre_mean_ms, 3), "score_pairs_per_s": round(pairs / (pre_mean_ms / 1e3), 1),
+                           "tok_per_s": round(float(lens.sum()) / (pre_mean_ms / 1e3), 1),
+                           "roofline": {"bound": "alu", "achieved": round(pre_ops, 2),
+                                        "peak": round(VALU_PEAK_TOPS, 2), "unit": "T lane-op/s",
+                                        "frac": round(pre_ops / VALU_PEAK_TOPS, 4),
+                                        "ops_per_pair": PREFILL_OPS_PER_PAIR}},
         "encode_ms": round(float(np.mean(enc_ms)), 3),
         "fit_ms": round(float(np.mean(fit_s)) * 1e3, 2),
         "input_gen_s": round(gen_s, 1),
