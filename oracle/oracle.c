@@ -65,6 +65,31 @@ float orc_half_to_float(uint16_t h)
     return sign ? -v : v;
 }
 
+/* bfloat16 bits -> float: the 16 bits are the high half of the binary32
+ * pattern, so the widening is exact. */
+float orc_bf16_to_float(uint16_t b)
+{
+    union {
+        uint32_t u;
+        float f;
+    } v;
+    v.u = (uint32_t)b << 16;
+    return v.f;
+}
+
+/* An input element (K, V or q) in its storage format: fmt 0 = fp16,
+ * fmt 1 = bf16; both widen to float exactly. */
+static float orc_in_to_float(uint16_t v, int fmt)
+{
+    return fmt ? orc_bf16_to_float(v) : orc_half_to_float(v);
+}
+
+void orc_bf16_to_float_n(const uint16_t *b, float *f, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++)
+        f[i] = orc_bf16_to_float(b[i]);
+}
+
 /* Round-to-nearest-even conversion float -> binary16. */
 uint16_t orc_float_to_half(float f)
 {
@@ -185,7 +210,8 @@ int orc_energy_rank(const double *s2, int n, double tau)
 /*
  * Group-head fit of one head group (PALU page, "How it works", prefill
  * steps 1-2).
- *   x      : fp16 [B][H][S_stride][D]; group g owns heads [g*H/G, (g+1)*H/G)
+ *   x      : fp16 (fmt 0) or bf16 (fmt 1) [B][H][S_stride][D]; group g owns
+ *            heads [g*H/G, (g+1)*H/G)
  *   lens   : valid tokens per sequence
  *   rank   : > 0 explicit rank (clamped to D), 0 -> energy rule with tau
  * Outputs (every column of the sorted eigenbasis is returned; the rank picks
@@ -197,7 +223,7 @@ int orc_energy_rank(const double *s2, int n, double tau)
  */
 int orc_fit_group(const uint16_t *x, const int32_t *lens, int B, int H,
                   int S_stride, int D, int G, int g, int rank, double tau,
-                  float *basis, float *mu, double *sigma)
+                  float *basis, float *mu, double *sigma, int fmt)
 {
     if (B <= 0 || H <= 0 || D <= 0 || G <= 0 || H % G != 0 || g < 0 || g >= G)
         return -1;
@@ -218,7 +244,7 @@ int orc_fit_group(const uint16_t *x, const int32_t *lens, int B, int H,
             for (int t = 0; t < lens[b]; t++) {
                 const uint16_t *xr = x + (((int64_t)b * H + h) * S_stride + t) * D;
                 for (int d = 0; d < D; d++)
-                    mean[d] += (double)orc_half_to_float(xr[d]);
+                    mean[d] += (double)orc_in_to_float(xr[d], fmt);
                 N++;
             }
     for (int d = 0; d < D; d++)
@@ -232,7 +258,7 @@ int orc_fit_group(const uint16_t *x, const int32_t *lens, int B, int H,
             for (int t = 0; t < lens[b]; t++) {
                 const uint16_t *xr = x + (((int64_t)b * H + h) * S_stride + t) * D;
                 for (int d = 0; d < D; d++)
-                    row[d] = (double)orc_half_to_float(xr[d]) - mean[d];
+                    row[d] = (double)orc_in_to_float(xr[d], fmt) - mean[d];
                 for (int i = 0; i < D; i++)
                     for (int j = i; j < D; j++)
                         cov[i * D + j] += row[i] * row[j];
@@ -292,13 +318,13 @@ int orc_fit_group(const uint16_t *x, const int32_t *lens, int B, int H,
  * rg [G] = per-group ranks.  Returns the shared rank or -1. */
 int orc_fit(const uint16_t *x, const int32_t *lens, int B, int H, int S_stride,
             int D, int G, int rank, double tau, float *basis, float *mu,
-            double *sigma, int32_t *rg)
+            double *sigma, int32_t *rg, int fmt)
 {
     int shared = -1;
     for (int g = 0; g < G; g++) {
         int r = orc_fit_group(x, lens, B, H, S_stride, D, G, g, rank, tau,
                               basis + (int64_t)g * D * D, mu + (int64_t)g * D,
-                              sigma + (int64_t)g * D);
+                              sigma + (int64_t)g * D, fmt);
         if (r < 0)
             return -1;
         rg[g] = r;
@@ -310,17 +336,18 @@ int orc_fit(const uint16_t *x, const int32_t *lens, int B, int H, int S_stride,
 
 /* ------------------------------------------------------------------------ */
 /* Projection: l_c = fma chain over d of (float(x_d) - mu_d) * V[d][c]       */
-/* x: fp16 [n][D]; V: fp32 [D][ldv] (first r columns used); out [n][r]       */
+/* x: fp16 or bf16 [n][D] (fmt); V: fp32 [D][ldv] (first r columns used);     */
+/* out [n][r]                                                                */
 /* ------------------------------------------------------------------------ */
 
 void orc_project(const uint16_t *x, int64_t n, int D, const float *mu,
-                 const float *V, int ldv, int r, float *out)
+                 const float *V, int ldv, int r, float *out, int fmt)
 {
     for (int64_t i = 0; i < n; i++) {
         for (int c = 0; c < r; c++) {
             float acc = 0.0f;
             for (int d = 0; d < D; d++) {
-                float y = orc_half_to_float(x[i * D + d]) - mu[d];
+                float y = orc_in_to_float(x[i * D + d], fmt) - mu[d];
                 acc = fmaf(y, V[(int64_t)d * ldv + c], acc);
             }
             out[i * r + c] = acc;

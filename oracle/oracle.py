@@ -46,13 +46,14 @@ def lib():
         L.orc_energy_rank.restype = _c_int
         L.orc_fit_group.argtypes = [_u16p, _i32p, _c_int, _c_int, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_dbl, _f32p, _f32p,
-                                    _f64p]
+                                    _f64p, _c_int]
         L.orc_fit_group.restype = _c_int
         L.orc_fit.argtypes = [_u16p, _i32p, _c_int, _c_int, _c_int, _c_int, _c_int,
-                              _c_int, _c_dbl, _f32p, _f32p, _f64p, _i32p]
+                              _c_int, _c_dbl, _f32p, _f32p, _f64p, _i32p, _c_int]
         L.orc_fit.restype = _c_int
         L.orc_project.argtypes = [_u16p, _c_i64, _c_int, _f32p, _f32p, _c_int,
-                                  _c_int, _f32p]
+                                  _c_int, _f32p, _c_int]
+        L.orc_bf16_to_float_n.argtypes = [_u16p, _f32p, _c_i64]
         L.orc_quantize_group.argtypes = [_f32p, _c_int, _c_int, _c_int, _c_int,
                                          _u8p, _u16p, _u16p]
         L.orc_record_words.argtypes = [_c_int, _c_int]
@@ -97,6 +98,19 @@ def half_to_float(h) -> np.ndarray:
     return out
 
 
+def bf16_to_float(b) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float32, exactly."""
+    b = _c(b, np.uint16)
+    out = np.empty(b.shape, np.float32)
+    lib().orc_bf16_to_float_n(b.reshape(-1), out.reshape(-1), b.size)
+    return out
+
+
+def widen(x, bf16: bool = False) -> np.ndarray:
+    """An input array (fp16 values, or bf16 bit patterns when bf16) -> float32."""
+    return bf16_to_float(x) if bf16 else half_to_float(x)
+
+
 def float_to_half_bits(f) -> np.ndarray:
     f = _c(f, np.float32)
     out = np.empty(f.shape, np.uint16)
@@ -135,8 +149,9 @@ class Fit:
         return np.ascontiguousarray(self.basis[:, :, :self.r])
 
 
-def fit(x, lens, n_groups: int, rank: int = 0, tau: float = 0.90) -> Fit:
-    """x: fp16 [B, H, S, D]; lens: [B] valid tokens; rank 0 -> energy rule."""
+def fit(x, lens, n_groups: int, rank: int = 0, tau: float = 0.90, bf16: bool = False) -> Fit:
+    """x: fp16 [B, H, S, D] (bf16 bit patterns, uint16, when bf16); lens: [B]
+    valid tokens; rank 0 -> energy rule."""
     x = _bits16(x)
     B, H, S, D = x.shape
     lens = _c(lens, np.int32)
@@ -145,13 +160,13 @@ def fit(x, lens, n_groups: int, rank: int = 0, tau: float = 0.90) -> Fit:
     sigma = np.empty((n_groups, D), np.float64)
     rg = np.empty(n_groups, np.int32)
     r = lib().orc_fit(x, lens, B, H, S, D, n_groups, int(rank or 0), tau, basis,
-                      mu, sigma, rg)
+                      mu, sigma, rg, 1 if bf16 else 0)
     if r < 0:
         raise ValueError("oracle fit: bad arguments")
     return Fit(r, rg, basis, mu, sigma)
 
 
-def fit_group(x, lens, n_groups: int, g: int, rank: int = 0, tau: float = 0.90):
+def fit_group(x, lens, n_groups: int, g: int, rank: int = 0, tau: float = 0.90, bf16: bool = False):
     """One group only: (rank_g, basis [D, D], mu [D], sigma [D])."""
     x = _bits16(x)
     B, H, S, D = x.shape
@@ -160,7 +175,7 @@ def fit_group(x, lens, n_groups: int, g: int, rank: int = 0, tau: float = 0.90):
     mu = np.empty(D, np.float32)
     sigma = np.empty(D, np.float64)
     r = lib().orc_fit_group(x, lens, B, H, S, D, n_groups, g, int(rank or 0), tau,
-                            basis, mu, sigma)
+                            basis, mu, sigma, 1 if bf16 else 0)
     if r < 0:
         raise ValueError("oracle fit: bad arguments")
     return r, basis, mu, sigma
@@ -168,14 +183,15 @@ def fit_group(x, lens, n_groups: int, g: int, rank: int = 0, tau: float = 0.90):
 
 # ------------------------------------------------------------ encode/decode
 
-def project(x, mu, V) -> np.ndarray:
-    """x fp16 [n, D]; mu fp32 [D]; V fp32 [D, r] -> fp32 [n, r]."""
+def project(x, mu, V, bf16: bool = False) -> np.ndarray:
+    """x fp16 [n, D] (bf16 bit patterns when bf16); mu fp32 [D]; V fp32
+    [D, r] -> fp32 [n, r]."""
     x = _bits16(x)
     n, D = x.shape
     V = _c(V, np.float32)
     r = V.shape[1]
     out = np.empty((n, r), np.float32)
-    lib().orc_project(x.reshape(-1), n, D, _c(mu, np.float32), V, r, r, out)
+    lib().orc_project(x.reshape(-1), n, D, _c(mu, np.float32), V, r, r, out, 1 if bf16 else 0)
     return out
 
 
@@ -325,11 +341,12 @@ class OracleLayer:
     mapping); kv head h uses the basis of group h // (Hkv / G)."""
 
     def __init__(self, D, n_q_heads, n_kv_heads, n_groups, fitK: Fit, fitV: Fit,
-                 hi_fraction=0.25, hi_bit=4, lo_bit=2, quantize_values=True):
+                 hi_fraction=0.25, hi_bit=4, lo_bit=2, quantize_values=True, bf16=False):
         self.D, self.Hq, self.Hkv, self.G = D, n_q_heads, n_kv_heads, n_groups
         self.fit = (fitK, fitV)
         self.hi_fraction, self.hi_bit, self.lo_bit = hi_fraction, hi_bit, lo_bit
         self.quantize_values = quantize_values
+        self.bf16 = bf16          # inputs (K, V, q) are bf16 bit patterns
 
     def n_hi(self, tensor):
         return n_hi_channels(self.fit[tensor].r, self.hi_fraction)
@@ -340,7 +357,7 @@ class OracleLayer:
     def latents(self, x_head, h, tensor):
         f = self.fit[tensor]
         g = self.group_of(h)
-        return project(x_head, f.mu[g], f.V(g))
+        return project(x_head, f.mu[g], f.V(g), bf16=self.bf16)
 
     def encode_head(self, x_head, h, tensor):
         """x_head fp16 [n, D] -> stored state of one (sequence, head, tensor)."""
@@ -363,6 +380,8 @@ class OracleLayer:
         Returns fp64 [Hq, D]."""
         if scale is None:
             scale = 1.0 / math.sqrt(self.D)
+        if self.bf16:
+            q = bf16_to_float(q)
         g = self.Hq // self.Hkv
         fK, fV = self.fit
         out = np.empty((self.Hq, self.D), np.float64)
@@ -381,6 +400,8 @@ class OracleLayer:
         Returns fp64 [Hq, nq, D]."""
         if scale is None:
             scale = 1.0 / math.sqrt(self.D)
+        if self.bf16:
+            q = bf16_to_float(q)
         g = self.Hq // self.Hkv
         fK, fV = self.fit
         nq = len(positions)

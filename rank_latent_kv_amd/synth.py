@@ -117,9 +117,16 @@ def group_params(w: Workload, tensor: int) -> GroupParams:
     return GroupParams(A, mu, outl)
 
 
+def to_bf16_bits(x) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
 def kv_sequence(w: Workload, tensor: int, b: int, n_tokens: int,
-                gp: Optional[GroupParams] = None) -> np.ndarray:
-    """K or V of sequence b: fp16 [n_kv_heads, n_tokens, D].
+                gp: Optional[GroupParams] = None, bf16: bool = False) -> np.ndarray:
+    """K or V of sequence b: fp16 [n_kv_heads, n_tokens, D] (bf16 bit
+    patterns, uint16, when bf16).
 
     Tokens [0, prefill) are the prefill, later ones the decode appends; a
     shorter n_tokens returns a prefix of the same stream."""
@@ -127,7 +134,7 @@ def kv_sequence(w: Workload, tensor: int, b: int, n_tokens: int,
         gp = group_params(w, tensor)
     D, k = w.head_dim, w.latent_rank
     hpg = w.n_kv_heads // w.n_head_groups
-    out = np.empty((w.n_kv_heads, n_tokens, D), dtype=np.float16)
+    out = np.empty((w.n_kv_heads, n_tokens, D), dtype=np.uint16 if bf16 else np.float16)
     for h in range(w.n_kv_heads):
         g = h // hpg
         rng = np.random.default_rng([w.seed, 13, tensor, b, h])
@@ -139,30 +146,34 @@ def kv_sequence(w: Workload, tensor: int, b: int, n_tokens: int,
         x += gp.mu[g].astype(np.float32)[None, :]
         if gp.outliers.shape[1]:
             x[:, gp.outliers[g]] *= 8.0
-        out[h] = x.astype(np.float16)
+        out[h] = to_bf16_bits(x) if bf16 else x.astype(np.float16)
     return out
 
 
-def queries(w: Workload, b: int, n_steps: Optional[int] = None) -> np.ndarray:
-    """Decode queries of sequence b: fp16 [n_steps, n_q_heads, D]."""
+def queries(w: Workload, b: int, n_steps: Optional[int] = None, bf16: bool = False) -> np.ndarray:
+    """Decode queries of sequence b: fp16 [n_steps, n_q_heads, D] (bf16 bit
+    patterns when bf16)."""
     n = w.steps if n_steps is None else n_steps
     rng = np.random.default_rng([w.seed, 17, b])
-    return rng.standard_normal((n, w.n_q_heads, w.head_dim)).astype(np.float16)
+    x = rng.standard_normal((n, w.n_q_heads, w.head_dim))
+    return to_bf16_bits(x.astype(np.float32)) if bf16 else x.astype(np.float16)
 
 
-def prefill_queries(w: Workload, b: int, n: int) -> np.ndarray:
+def prefill_queries(w: Workload, b: int, n: int, bf16: bool = False) -> np.ndarray:
     """Prefill queries of sequence b, one per prompt position: fp16
-    [n_q_heads, n, D], N(0, 1) like the decode queries."""
+    [n_q_heads, n, D], N(0, 1) like the decode queries (bf16 bit patterns
+    when bf16)."""
     rng = np.random.default_rng([w.seed, 19, b])
-    return rng.standard_normal((w.n_q_heads, n, w.head_dim), dtype=np.float32).astype(np.float16)
+    x = rng.standard_normal((w.n_q_heads, n, w.head_dim), dtype=np.float32)
+    return to_bf16_bits(x) if bf16 else x.astype(np.float16)
 
 
-def batch_kv(w: Workload, tensor: int, n_tokens: int, seqs=None) -> np.ndarray:
+def batch_kv(w: Workload, tensor: int, n_tokens: int, seqs=None, bf16: bool = False) -> np.ndarray:
     """[len(seqs), n_kv_heads, n_tokens, D] fp16 (each sequence's own stream,
-    truncated or generated to n_tokens positions)."""
+    truncated or generated to n_tokens positions; bf16 bit patterns when bf16)."""
     gp = group_params(w, tensor)
     seqs = range(w.batch) if seqs is None else seqs
-    return np.stack([kv_sequence(w, tensor, b, n_tokens, gp) for b in seqs])
+    return np.stack([kv_sequence(w, tensor, b, n_tokens, gp, bf16) for b in seqs])
 
 
 def small_workload(name: str = "tiny", *, batch=2, n_q_heads=4, n_kv_heads=2,

@@ -626,6 +626,60 @@ def test_layer_prefill_last_row_equals_decode(gqa):
     np.testing.assert_allclose(pre[:, 2], layer.attend(ks, vs, q[:, 2]), rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------------------------ bf16
+
+def test_bf16_widening_matches_torch_all_patterns():
+    import torch
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    got = oracle.bf16_to_float(bits)
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite].view(np.uint32), ref[finite].view(np.uint32))
+    assert np.all(np.isnan(got[~finite]) == np.isnan(ref[~finite]))
+
+
+def test_bf16_inputs_match_fp16_on_shared_values():
+    """Values representable in both formats give bitwise the same fit,
+    projection and layer attention whichever format carries them."""
+    w = synth.small_workload(batch=2, n_kv_heads=2, n_q_heads=4, prefill=70, n_head_groups=2)
+    k16 = synth.batch_kv(w, 0, 70)
+    kb = synth.to_bf16_bits(k16.astype(np.float32))              # bf16 rounding of the data
+    k16b = oracle.bf16_to_float(kb).astype(np.float16)           # the same values in fp16 (exact)
+    assert np.array_equal(k16b.astype(np.float32), oracle.bf16_to_float(kb))
+    f_b = oracle.fit(kb, [70, 50], 2, rank=0, tau=0.9, bf16=True)
+    f_h = oracle.fit(k16b, [70, 50], 2, rank=0, tau=0.9)
+    assert f_b.r == f_h.r
+    assert np.array_equal(f_b.basis, f_h.basis) and np.array_equal(f_b.mu, f_h.mu)
+    lb = oracle.project(kb[0, 0], f_b.mu[0], f_b.V(0), bf16=True)
+    lh = oracle.project(k16b[0, 0], f_h.mu[0], f_h.V(0))
+    assert np.array_equal(lb, lh)
+    layer_b = oracle.OracleLayer(128, 4, 2, 2, f_b, f_b, bf16=True)
+    layer_h = oracle.OracleLayer(128, 4, 2, 2, f_h, f_h)
+    ks_b = [layer_b.encode_head(kb[0, h], h, 0) for h in range(2)]
+    ks_h = [layer_h.encode_head(k16b[0, h], h, 0) for h in range(2)]
+    assert all(np.array_equal(a["records"], b["records"]) for a, b in zip(ks_b, ks_h))
+    qb = synth.to_bf16_bits(synth.queries(w, 0, 1)[0].astype(np.float32))
+    qh = oracle.bf16_to_float(qb).astype(np.float16)
+    np.testing.assert_array_equal(layer_b.attend(ks_b, ks_b, qb), layer_h.attend(ks_h, ks_h, qh))
+
+
+def test_bf16_beyond_fp16_range_reconstructs():
+    """Keys far outside the fp16 range (a channel mean of 1e5) are fine in
+    bf16: at full rank without quantisation the reconstruction returns them
+    to fp32 precision, which no fp16 cast of the input could."""
+    w = synth.small_workload(batch=1, n_kv_heads=1, n_q_heads=1, prefill=64)
+    x = synth.batch_kv(w, 0, 64).astype(np.float32)
+    x[..., 5] += 1.0e5
+    xb = synth.to_bf16_bits(x)
+    xv = oracle.bf16_to_float(xb)
+    assert np.abs(xv).max() > 65504
+    f = oracle.fit(xb, [64], 1, rank=128, bf16=True)
+    lat = oracle.project(xb[0, 0], f.mu[0], f.V(0), bf16=True).astype(np.float64)
+    rec = lat @ f.V(0).T.astype(np.float64) + f.mu[0]
+    np.testing.assert_allclose(rec, xv[0, 0], rtol=0, atol=2e-2)
+    assert abs(f.mu[0][5] - xv[0, 0, :, 5].mean()) < 1e-2
+
+
 # ------------------------------------------------------------- quality
 
 def _naive_2bit_mse(x):
