@@ -69,6 +69,14 @@ typedef struct palu_config {
                                   split limit (128 splits per sequence and head);
                                   a value whose LDS need exceeds 160 KiB makes
                                   palu_decode_attend fail with UNSUPPORTED.      */
+    int32_t input_dtype;       /* element type of every K, V and q input and of the
+                                  attention outputs: 0 = fp16, 1 = bf16 (review
+                                  thread of the "add TurboQuant KV cache
+                                  compression" pull-request page: bf16 keys beyond
+                                  the fp16 range must not be cast).  Codes,
+                                  their fp16 scale/zero words and the fp32 tails
+                                  are the same for both; with bf16, latents must
+                                  stay within the fp16 range like with fp16.     */
 } palu_config;
 
 /* Fills the page's defaults (rank 0 = energy rule, threshold 0.90, G = 4,
@@ -103,7 +111,7 @@ int palu_cache_bind(palu_cache *cache, void *dev_buf, size_t bytes);
  * rank is the explicit one or the smallest meeting the energy threshold
  * (energy = sum of squared singular values), and the minimum over groups
  * is used for every group.
- *   k, v     : device fp16 [B][H][S_stride][D]
+ *   k, v     : device fp16 or bf16 (input_dtype) [B][H][S_stride][D]
  *   seq_lens : host int32 [B], 0 <= seq_lens[b] <= S_stride, sum > 0
  * Synchronous (the eigensolve runs on the host).  Empties every sequence
  * slot (stored codes of an older basis are meaningless).  Errors:
@@ -131,7 +139,7 @@ int palu_get_basis(const palu_cache *cache, int32_t tensor, int32_t *r,
  * quantises every 32-token group that becomes complete (asymmetric min/max,
  * round half to even, top n_hi channels at hi_bit, others at lo_bit) and
  * keeps the incomplete group's latents in fp32 until it completes.
- *   k, v     : device fp16 [B][H][T_stride][D]
+ *   k, v     : device fp16 or bf16 (input_dtype) [B][H][T_stride][D]
  *   seq_ids  : host int32 [B] slot of each row (NULL = 0..B-1), distinct
  *   n_new    : host int32 [B] tokens to append per row (NULL = T_stride each),
  *              0 <= n_new[b] <= T_stride
@@ -146,7 +154,7 @@ int palu_encode_append(palu_cache *cache, const void *k, const void *v,
  * (PALU page, "How it works", decode step 3, computed directly from the
  * latent codes): out = softmax(q K^T * scale) V with K, V the decoded
  * reconstruction; fp32 scores and accumulation.
- *   q, out        : device fp16 [B][Hq][D]
+ *   q, out        : device fp16 or bf16 (input_dtype) [B][Hq][D]
  *   seq_ids       : host int32 [B] (NULL = 0..B-1); every slot must hold at
  *                   least one token
  *   softmax_scale : 0 means 1/sqrt(D)
@@ -163,7 +171,7 @@ int palu_decode_attend(palu_cache *cache, const void *q, void *out,
  * palu_decode_attend.  Row b's queries are the last n_q[b] positions
  * [len - n_q[b], len) of slot seq_ids[b] (append the prompt's K/V first);
  * the query at position p attends to the slot's tokens 0..p.
- *   q, out        : device fp16 [B][Hq][T_stride][D], 16-byte aligned; query
+ *   q, out        : device fp16 or bf16 (input_dtype) [B][Hq][T_stride][D], 16-byte aligned; query
  *                   j of row b at [b][head][j]; only j < n_q[b] is written
  *   seq_ids       : host int32 [B] (NULL = 0..B-1); slots may repeat
  *   n_q           : host int32 [B] (NULL = T_stride each),

@@ -25,6 +25,31 @@ __device__ __forceinline__ uint32_t f2h_bits(float f) {
     return static_cast<uint32_t>(__half_as_ushort(__float2half_rn(f)));
 }
 
+// bf16 bits (low 16 bits of the argument) -> float, exact.
+__device__ __forceinline__ float bf2f(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// An input element (fp16 or bf16 bits in the low half) -> float, exact.
+template <bool BF16>
+__device__ __forceinline__ float in2f(uint32_t bits) {
+    if constexpr (BF16) return bf2f(bits & 0xFFFFu);
+    else return __half2float(__ushort_as_half(static_cast<unsigned short>(bits & 0xFFFFu)));
+}
+// The high half of a 32-bit pair of inputs -> float.
+template <bool BF16>
+__device__ __forceinline__ float in2f_hi(uint32_t pair) {
+    if constexpr (BF16) return __uint_as_float(pair & 0xFFFF0000u);
+    else return __half2float(__ushort_as_half(static_cast<unsigned short>(pair >> 16)));
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f2bf_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// An output element in the input type (fp16 or bf16), round to nearest even.
+__device__ __forceinline__ uint32_t out_bits(float f, bool bf16) { return bf16 ? f2bf_bits(f) : f2h_bits(f); }
+
 // Lane exchange inside rows of 16 lanes through DPP (no LDS round trip).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -73,6 +98,47 @@ struct FastDiv {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+// bf16 query rows for an fp16 MFMA: the 32 elements a lane holds (4 x 8
+// bf16 in qa) of a row spread over the 4 lanes ln, ln + 16, ln + 32, ln + 48
+// are scaled by 2^-k, with k chosen per row so that the row's largest
+// magnitude lands in [2^14, 2^15), and rounded to fp16.  bf16 carries 8
+// significand bits, so every element that stays in the fp16 normal range
+// converts exactly; elements more than 2^28 below the row maximum may round
+// (fp16 subnormals), far below what any dot product resolves.  Returns k;
+// qa is rewritten in place as fp16.
+__device__ __forceinline__ int bf16_rows_to_fp16(uint4 (&qa)[4]) {
+    uint32_t emax = 0;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const uint32_t w[4] = {qa[st].x, qa[st].y, qa[st].z, qa[st].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t e0 = w[i] & 0x7F80u, e1 = (w[i] >> 16) & 0x7F80u;
+            emax = emax > e0 ? emax : e0;
+            emax = emax > e1 ? emax : e1;
+        }
+    }
+    uint32_t o = __shfl_xor(emax, 16);
+    emax = emax > o ? emax : o;
+    o = __shfl_xor(emax, 32);
+    emax = emax > o ? emax : o;
+    // |x| < 2^(E - 126) with E the biased exponent: scale by 2^-(E - 141)
+    const int E = static_cast<int>(emax >> 7);
+    int k = E == 0 ? 0 : E - 141;
+    k = k < -100 ? -100 : (k > 100 ? 100 : k);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        uint32_t w[4] = {qa[st].x, qa[st].y, qa[st].z, qa[st].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = ldexpf(bf2f(w[i] & 0xFFFFu), -k), hi = ldexpf(__uint_as_float(w[i] & 0xFFFF0000u), -k);
+            w[i] = f2h_bits(lo) | (f2h_bits(hi) << 16);
+        }
+        qa[st] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return k;
+}
 
 // Bump allocator for a workgroup's dynamic LDS (16-byte aligned pieces).
 __host__ __device__ inline int lds_take(int &o, int bytes) {

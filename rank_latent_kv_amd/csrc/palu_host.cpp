@@ -103,6 +103,8 @@ int validate_config(const palu_config *c) {
     if (c->split_groups < 0) return fail(PALU_ERR_INVALID_ARG, "split_groups must be >= 0 (0 = automatic)");
     if (c->quantize_values != 0 && c->quantize_values != 1)
         return fail(PALU_ERR_INVALID_ARG, "quantize_values must be 0 or 1");
+    if (c->input_dtype != 0 && c->input_dtype != 1)
+        return fail(PALU_ERR_INVALID_ARG, "input_dtype must be 0 (fp16) or 1 (bf16)");
     if (c->head_dim != kHeadDim)
         return fail(PALU_ERR_UNSUPPORTED, "only head_dim = 128 is implemented by the kernels");
     if (c->hi_bit != 4 || c->lo_bit != 2)
@@ -177,6 +179,7 @@ PALU_API int palu_config_default(palu_config *cfg, int32_t head_dim, int32_t n_k
     cfg->quantize_values = 1;
     cfg->max_rank = 0;
     cfg->split_groups = 0;
+    cfg->input_dtype = 0;
     return PALU_OK;
 }
 
@@ -293,6 +296,7 @@ PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t
     ga.B = B;
     ga.H = c->H;
     ga.S_stride = S_stride;
+    ga.bf16 = c->cfg.input_dtype;
     ga.G = c->G;
     ga.hpg = c->hpg;
     ga.nb = nb;
@@ -473,6 +477,7 @@ PALU_API int palu_encode_append(palu_cache *c, const void *k, const void *v, con
         ea.T_stride = T_stride;
         ea.hpg = c->hpg;
         ea.hi_bit = c->cfg.hi_bit;
+        ea.bf16 = c->cfg.input_dtype;
         ea.lo_bit = c->cfg.lo_bit;
         int max_units = 0;   // group pairs touched by a row (one wave each)
         for (int i = 0; i < nb; ++i) {
@@ -543,6 +548,7 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
         aa.gqa = c->gqa;
         aa.hpg = c->hpg;
         aa.qscale = static_cast<float>(scale * 1.4426950408889634);
+        aa.bf16 = c->cfg.input_dtype;
         int64_t units = 0;
         int max_full = 0;
         for (int i = 0; i < nb; ++i) {
@@ -643,6 +649,7 @@ PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const 
         pa.T_stride = T_stride;
         pa.qp = qp;
         pa.qscale = static_cast<float>(scale * 1.4426950408889634);
+        pa.bf16 = c->cfg.input_dtype;
         int tiles = 0;
         for (int i = 0; i < nb; ++i) {
             const int slot = seq_ids ? seq_ids[b0 + i] : b0 + i;

@@ -39,12 +39,13 @@ struct TensorDev {
 };
 
 struct GramArgs {
-    const uint16_t *x[2];     // K, V fp16 [B][H][S_stride][D]
+    const uint16_t *x[2];     // K, V fp16 or bf16 [B][H][S_stride][D]
     const int64_t *seg_pref;  // [B*hpg + 1] prefix of valid rows over (b, head-in-group)
     const int32_t *seg_len;   // unused by the kernel; kept for bounds reasoning
     float *partial;           // [2][G][nb][D*D + D]
     int B, H, S_stride, G, hpg, nb, rows_per_block;
     int64_t n_rows;           // rows per group (same for every group)
+    int bf16;                 // inputs are bf16 (else fp16)
 };
 
 struct GramReduceArgs {
@@ -54,9 +55,10 @@ struct GramReduceArgs {
 };
 
 struct EncodeArgs {
-    const uint16_t *x[2];     // K, V fp16 [B][H][T_stride][D]
+    const uint16_t *x[2];     // K, V fp16 or bf16 [B][H][T_stride][D]
     TensorDev t[2];
     int B, H, T_stride, hpg, hi_bit, lo_bit;
+    int bf16;                 // inputs are bf16 (else fp16)
     int slot[kMaxCallSeqs];
     int old_len[kMaxCallSeqs];
     int n_new[kMaxCallSeqs];
@@ -73,8 +75,8 @@ struct AttendRow {
 };
 
 struct AttendArgs {
-    const uint16_t *q;        // fp16 [B][Hq][D]
-    uint16_t *out;            // fp16 [B][Hq][D]
+    const uint16_t *q;        // fp16 or bf16 [B][Hq][D]
+    uint16_t *out;            // same type as q, [B][Hq][D]
     float *partial;           // [B][Hq][kMaxSplits][2 + r_v]
     TensorDev k, v;
     int B, Hq, Hkv, gqa, hpg;
@@ -84,6 +86,7 @@ struct AttendArgs {
     // correctly rounded fp32 reciprocals of index divisors: r_v and 4 times
     // the key channel blocks
     float inv_rv, inv_nbk4;
+    int bf16;                 // q and out are bf16 (else fp16)
     AttendRow row[kMaxCallSeqs];       // grid z order (longest first)
     int nsplit_call[kMaxCallSeqs];     // splits of call row i (combine)
 };
@@ -95,13 +98,14 @@ struct PrefillRow {
 };
 
 struct PrefillArgs {
-    const uint16_t *q;        // fp16 [B][Hq][T_stride][D]
-    uint16_t *out;            // fp16 [B][Hq][T_stride][D]
+    const uint16_t *q;        // fp16 or bf16 [B][Hq][T_stride][D]
+    uint16_t *out;            // same type as q, [B][Hq][T_stride][D]
     TensorDev k, v;
     int B, Hq, Hkv, gqa, hpg, T_stride;
     int qp;                   // query positions per workgroup
     int tiles_max;            // grid x; tiles past a row's last exit at once
     float qscale;             // softmax scale * log2(e)
+    int bf16;                 // q and out are bf16 (else fp16)
     PrefillRow row[kMaxCallSeqs];
 };
 

@@ -17,6 +17,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "palu_device.h"
 #include "palu_internal.h"
@@ -37,6 +38,11 @@ namespace {
 constexpr int kGramTile = 64;
 constexpr int kGramPad = 136;   // LDS row stride in halves
 
+// bf16 rows use the bf16 MFMA: bf16 x bf16 products are exact in fp32 just
+// like fp16 x fp16.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <bool BF16>
 __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
     const int blk = blockIdx.x, g = blockIdx.y, tz = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -45,11 +51,15 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
     const uint16_t *x = a.x[tz];
     const int nseg = a.B * a.hpg;
 
-    __shared__ _Float16 tile[kGramTile][kGramPad];
+    __shared__ uint16_t tile[kGramTile][kGramPad];
 
     f32x16 acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {}, accs = {};
-    f16x8 ones;
-    for (int u = 0; u < 8; ++u) ones[u] = static_cast<_Float16>(1.0f);
+    // operand element type of the input; 1.0 is 0x3C00 in fp16, 0x3F80 in bf16
+    using vec8 = typename std::conditional<BF16, bf16x8, f16x8>::type;
+    using elem = typename std::conditional<BF16, __bf16, _Float16>::type;
+    const uint16_t one_bits = BF16 ? 0x3F80 : 0x3C00;
+    vec8 ones;
+    for (int u = 0; u < 8; ++u) ones[u] = __builtin_bit_cast(elem, one_bits);
 
     for (int64_t base = row0; base < row1; base += kGramTile) {
         for (int k = 0; k < 4; ++k) {
@@ -76,19 +86,27 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
         for (int ks = 0; ks < kGramTile / 16; ++ks) {
             const int rb = ks * 16 + (lane >> 5) * 8;
             const int f = lane & 31;
-            f16x8 o0, o1, o2, o3;
+            vec8 o0, o1, o2, o3;
             for (int u = 0; u < 8; ++u) {
-                o0[u] = tile[rb + u][f];
-                o1[u] = tile[rb + u][32 + f];
-                o2[u] = tile[rb + u][64 + f];
-                o3[u] = tile[rb + u][96 + f];
+                o0[u] = __builtin_bit_cast(elem, tile[rb + u][f]);
+                o1[u] = __builtin_bit_cast(elem, tile[rb + u][32 + f]);
+                o2[u] = __builtin_bit_cast(elem, tile[rb + u][64 + f]);
+                o3[u] = __builtin_bit_cast(elem, tile[rb + u][96 + f]);
             }
-            const f16x8 oa = w == 0 ? o0 : w == 1 ? o1 : w == 2 ? o2 : o3;
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa, o0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa, o1, acc1, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa, o2, acc2, 0, 0, 0);
-            acc3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa, o3, acc3, 0, 0, 0);
-            accs = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, oa, accs, 0, 0, 0);
+            const vec8 oa = w == 0 ? o0 : w == 1 ? o1 : w == 2 ? o2 : o3;
+            if constexpr (BF16) {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, o0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, o1, acc1, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, o2, acc2, 0, 0, 0);
+                acc3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, o3, acc3, 0, 0, 0);
+                accs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, oa, accs, 0, 0, 0);
+            } else {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa, o0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa, o1, acc1, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa, o2, acc2, 0, 0, 0);
+                acc3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa, o3, acc3, 0, 0, 0);
+                accs = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, oa, accs, 0, 0, 0);
+            }
         }
         __syncthreads();
     }
@@ -196,7 +214,7 @@ __device__ __forceinline__ void encode_channel(const EncodeArgs &a, const Tensor
 // independent fixed-order chains over d = 0..D-1, run in four quarters of
 // 32 rows so that only 32 values y_d = float(x_d) - mu_d are live at a time;
 // basis rows are read from LDS as 16-byte broadcasts.
-template <int W>
+template <int W, bool BF16>
 __device__ __forceinline__ void project_to_lds(const uint16_t *xrow, const float *msh, const float *vsh, int rp,
                                                int c0, float *lat, int lane) {
     float l[W];
@@ -217,8 +235,8 @@ __device__ __forceinline__ void project_to_lds(const uint16_t *xrow, const float
             const uint32_t wq[4] = {xa[k].x, xa[k].y, xa[k].z, xa[k].w};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                y[8 * k + 2 * m] = h2f(wq[m]) - msh[32 * q + 8 * k + 2 * m];
-                y[8 * k + 2 * m + 1] = h2f(wq[m] >> 16) - msh[32 * q + 8 * k + 2 * m + 1];
+                y[8 * k + 2 * m] = in2f<BF16>(wq[m]) - msh[32 * q + 8 * k + 2 * m];
+                y[8 * k + 2 * m + 1] = in2f_hi<BF16>(wq[m]) - msh[32 * q + 8 * k + 2 * m + 1];
             }
         }
 #pragma unroll
@@ -249,6 +267,7 @@ __host__ __device__ inline int encode_lds_bytes(int r, int words, bool fp16) {
     return (kHeadDim * rp + kHeadDim + kEncWaves * (2 * encode_rec_words(words, fp16) + 32 * 64)) * 4;
 }
 
+template <bool BF16>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     extern __shared__ __align__(16) float esh[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -315,14 +334,14 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     for (int c0 = 0; c0 < r; c0 += 32) {
         const int nc = r - c0 < 32 ? r - c0 : 32;
         switch ((nc + 3) >> 2) {
-            case 1: project_to_lds<4>(xrow, msh, vsh, rp, c0, lat, lane); break;
-            case 2: project_to_lds<8>(xrow, msh, vsh, rp, c0, lat, lane); break;
-            case 3: project_to_lds<12>(xrow, msh, vsh, rp, c0, lat, lane); break;
-            case 4: project_to_lds<16>(xrow, msh, vsh, rp, c0, lat, lane); break;
-            case 5: project_to_lds<20>(xrow, msh, vsh, rp, c0, lat, lane); break;
-            case 6: project_to_lds<24>(xrow, msh, vsh, rp, c0, lat, lane); break;
-            case 7: project_to_lds<28>(xrow, msh, vsh, rp, c0, lat, lane); break;
-            default: project_to_lds<32>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 1: project_to_lds<4, BF16>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 2: project_to_lds<8, BF16>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 3: project_to_lds<12, BF16>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 4: project_to_lds<16, BF16>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 5: project_to_lds<20, BF16>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 6: project_to_lds<24, BF16>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            case 7: project_to_lds<28, BF16>(xrow, msh, vsh, rp, c0, lat, lane); break;
+            default: project_to_lds<32, BF16>(xrow, msh, vsh, rp, c0, lat, lane); break;
         }
         for (int k = 0; k < nc; ++k)
             encode_channel(a, T, e, c0 + k, lat[k * 64 + lane], told, tnew, rec_lds, rec16, tz, any_complete);
@@ -356,6 +375,7 @@ __host__ __device__ inline int append1_lds_bytes(int r, int words) {
     return (kHeadDim + r * kHeadDim + words) * 4;     // y [D], basis [D][r], record
 }
 
+template <bool BF16>
 __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
     extern __shared__ __align__(16) float ash[];
     const int tid = threadIdx.x;
@@ -375,7 +395,7 @@ __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
 
     // 1. y = float(x) - mu and the basis -> LDS
     const uint16_t *xin = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim;
-    if (tid < kHeadDim) ys[tid] = h2f(xin[tid]) - T.mu[grp * kHeadDim + tid];
+    if (tid < kHeadDim) ys[tid] = in2f<BF16>(xin[tid]) - T.mu[grp * kHeadDim + tid];
     const float *vb = T.basis + static_cast<int64_t>(grp) * kHeadDim * r;
     for (int e = tid; e < kHeadDim * r; e += kApp1Threads) vs[e] = vb[e];
     if (complete && !T.fp16_latents)
@@ -633,6 +653,14 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             uint4 qa[4], bb[2][4];
 #pragma unroll
             for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const uint4 *>(qsrc + 32 * st);
+            // bf16 queries: exact per-row power-of-two rescale into fp16,
+            // undone on the MFMA result (output row 4 kb + v = query row)
+            float qsc[4] = {a.qscale, a.qscale, a.qscale, a.qscale};
+            if (a.bf16) {
+                const int kq = bf16_rows_to_fp16(qa);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) qsc[v] = ldexpf(a.qscale, __shfl(kq, 4 * kb + v));
+            }
             const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * np * kHeadDim;
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
@@ -663,7 +691,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                 for (int v = 0; v < 4; ++v) {
                     const int hh = 4 * kb + v;
                     if (hh < g && n < np) {
-                        const float val = acc[v] * a.qscale;
+                        const float val = acc[v] * qsc[v];
                         qt16h[hh * np + n] = static_cast<_Float16>(val);
                         if (c < chanend) qt[hh * rk + c] = val;
                     }
@@ -1097,7 +1125,7 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
         o1 = fmaf(b.y, oc, o1);
     }
     reinterpret_cast<uint32_t *>(a.out + (static_cast<int64_t>(i) * a.Hq + qh) * kHeadDim)[lane] =
-        f2h_bits(o0) | (f2h_bits(o1) << 16);
+        out_bits(o0, a.bf16) | (out_bits(o1, a.bf16) << 16);
 }
 
 // dst[g][n][d] = fp16(V[g][d][chan(n)]) for the score-operand position n
@@ -1121,7 +1149,8 @@ __global__ __launch_bounds__(256) void basis_t16_kernel(const float *src, uint16
 }  // namespace
 
 hipError_t launch_gram(const GramArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(gram_kernel, dim3(a.nb, a.G, 2), dim3(256), 0, s, a);
+    if (a.bf16) hipLaunchKernelGGL(gram_kernel<true>, dim3(a.nb, a.G, 2), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(gram_kernel<false>, dim3(a.nb, a.G, 2), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1131,33 +1160,43 @@ hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_append1(const EncodeArgs &a, hipStream_t s) {
+template <bool BF16>
+static hipError_t launch_append1_t(const EncodeArgs &a, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(append1_kernel),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(append1_kernel<BF16>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int l0 = append1_lds_bytes(a.t[0].r, a.t[0].words), l1 = append1_lds_bytes(a.t[1].r, a.t[1].words);
-    hipLaunchKernelGGL(append1_kernel, dim3(a.B * a.H, 2), dim3(kApp1Threads), static_cast<size_t>(l0 > l1 ? l0 : l1),
-                       s, a);
+    hipLaunchKernelGGL(append1_kernel<BF16>, dim3(a.B * a.H, 2), dim3(kApp1Threads),
+                       static_cast<size_t>(l0 > l1 ? l0 : l1), s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_encode(const EncodeArgs &a, int max_units, hipStream_t s) {
+hipError_t launch_append1(const EncodeArgs &a, hipStream_t s) {
+    return a.bf16 ? launch_append1_t<true>(a, s) : launch_append1_t<false>(a, s);
+}
+
+template <bool BF16>
+static hipError_t launch_encode_t(const EncodeArgs &a, int max_units, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(encode_kernel),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(encode_kernel<BF16>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int l0 = encode_lds_bytes(a.t[0].r, a.t[0].words, a.t[0].fp16_latents),
               l1 = encode_lds_bytes(a.t[1].r, a.t[1].words, a.t[1].fp16_latents);
-    hipLaunchKernelGGL(encode_kernel, dim3((max_units + kEncWaves - 1) / kEncWaves, a.B * a.H, 2), dim3(256),
+    hipLaunchKernelGGL(encode_kernel<BF16>, dim3((max_units + kEncWaves - 1) / kEncWaves, a.B * a.H, 2), dim3(256),
                        static_cast<size_t>(l0 > l1 ? l0 : l1), s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_encode(const EncodeArgs &a, int max_units, hipStream_t s) {
+    return a.bf16 ? launch_encode_t<true>(a, max_units, s) : launch_encode_t<false>(a, max_units, s);
 }
 
 size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int words_k, int words_v, bool vq) {

@@ -284,6 +284,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             uint4 qa[4];
 #pragma unroll
             for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const uint4 *>(qsrc[t] + 32 * st + 8 * kb);
+            // bf16 queries: exact per-column power-of-two rescale into fp16
+            // (the MFMA result of column ln sits in this lane)
+            const float qsc = a.bf16 ? ldexpf(a.qscale, bf16_rows_to_fp16(qa)) : a.qscale;
             f4 acc[2 * KS];
 #pragma unroll
             for (int blk = 0; blk < 2 * KS; ++blk) {
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 uint32_t wd[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    wd[v] = pack_half2(acc[2 * ks][v] * a.qscale, acc[2 * ks + 1][v] * a.qscale);
+                    wd[v] = pack_half2(acc[2 * ks][v] * qsc, acc[2 * ks + 1][v] * qsc);
                 qb[t][ks] = as_h8(wd[0], wd[1], wd[2], wd[3]);
             }
         }
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             acc1 = fmaf(b.y, oc, acc1);
         }
         uint16_t *dst = a.out + ((static_cast<int64_t>(i) * a.Hq + h * g + hd) * a.T_stride + qi) * kHeadDim;
-        reinterpret_cast<uint32_t *>(dst)[lane] = f2h_bits(acc0) | (f2h_bits(acc1) << 16);
+        reinterpret_cast<uint32_t *>(dst)[lane] = out_bits(acc0, a.bf16) | (out_bits(acc1, a.bf16) << 16);
     }
 }
 

@@ -43,7 +43,7 @@ class palu_config(ctypes.Structure):
                 ("hi_bit", ctypes.c_int32), ("lo_bit", ctypes.c_int32),
                 ("hi_fraction", ctypes.c_float), ("group_size", ctypes.c_int32),
                 ("quantize_values", ctypes.c_int32), ("max_rank", ctypes.c_int32),
-                ("split_groups", ctypes.c_int32)]
+                ("split_groups", ctypes.c_int32), ("input_dtype", ctypes.c_int32)]
 
 
 class palu_stats(ctypes.Structure):
@@ -255,7 +255,7 @@ class LatentKVCache:
                  max_batch: int, max_seq_len: int, rank: int = 0, energy_threshold: float = 0.90,
                  hi_bit: int = 4, lo_bit: int = 2, hi_fraction: float = 0.25,
                  group_size: int = 32, quantize_values: bool = True, max_rank: int = 0,
-                 split_groups: int = 0, device=None):
+                 split_groups: int = 0, input_dtype: str = "fp16", device=None):
         import torch
         self.torch = torch
         cfg = palu_config_default(head_dim, n_kv_heads, n_q_heads)
@@ -267,6 +267,9 @@ class LatentKVCache:
         cfg.quantize_values = 1 if quantize_values else 0
         cfg.max_rank = max_rank
         cfg.split_groups = split_groups
+        if input_dtype not in ("fp16", "bf16"):
+            raise ValueError("input_dtype must be 'fp16' or 'bf16'")
+        cfg.input_dtype = 1 if input_dtype == "bf16" else 0
         self.cfg = cfg
         self.D, self.H, self.Hq, self.G = head_dim, n_kv_heads, n_q_heads, n_head_groups
         self.max_batch, self.max_seq_len = max_batch, max_seq_len
@@ -290,8 +293,9 @@ class LatentKVCache:
 
     def _check_half(self, t, shape_tail, name):
         torch = self.torch
-        if t.dtype != torch.float16 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous fp16 CUDA tensor")
+        want = torch.bfloat16 if self.cfg.input_dtype == 1 else torch.float16
+        if t.dtype != want or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {want} CUDA tensor")
         if tuple(t.shape[-len(shape_tail):]) != tuple(shape_tail):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected [..., {shape_tail}]")
 

@@ -38,7 +38,7 @@ def _cfg(**kw):
 def test_config_defaults_follow_usage_section():
     cfg = palu.palu_config_default(128, 8, 32)
     assert (cfg.rank, cfg.n_head_groups, cfg.hi_bit, cfg.lo_bit, cfg.group_size,
-            cfg.quantize_values, cfg.max_rank, cfg.split_groups) == (0, 4, 4, 2, 32, 1, 0, 0)
+            cfg.quantize_values, cfg.max_rank, cfg.split_groups, cfg.input_dtype) == (0, 4, 4, 2, 32, 1, 0, 0, 0)
     assert abs(cfg.energy_threshold - 0.90) < 1e-7 and abs(cfg.hi_fraction - 0.25) < 1e-7
 
 
@@ -52,6 +52,7 @@ def test_config_defaults_follow_usage_section():
     (dict(max_rank=129), 1),
     (dict(split_groups=-1), 1),
     (dict(quantize_values=2), 1),
+    (dict(input_dtype=2), 1),
     (dict(head_dim=96), 2),              # kernels built for D = 128
     (dict(hi_bit=3), 2),
     (dict(lo_bit=1), 2),
