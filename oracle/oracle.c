@@ -363,11 +363,66 @@ void orc_project(const uint16_t *x, int64_t n, int D, const float *mu,
 /* l: fp32 [32][r]; codes: [32][r]; scale16/zero16: fp16 bits [r]            */
 /* ------------------------------------------------------------------------ */
 
-void orc_quantize_group(const float *l, int r, int n_hi, int hi_bit, int lo_bit,
-                        uint8_t *codes, uint16_t *scale16, uint16_t *zero16)
+/*
+ * The coder works on segments: contiguous ranges of latent channels in
+ * descending-singular-value order, segment s holding seg_n[s] channels coded
+ * with seg_bits[s] bits (0, 1, 2, 4 or 8).  PALU's split (PALU page,
+ * "Usage": the top hi_fraction of channels at hi_bit, the rest at lo_bit) is
+ * the two-segment case; the SVDq cache page's bit schedule (section on the
+ * SVDq cache: r channels split into len(schedule) equal contiguous groups,
+ * 0 bits truncating a group to exactly zero) is the general one.  A 0-bit
+ * channel is not stored in any form: no codes, no metadata, no tail entry;
+ * its latent is exactly 0.
+ */
+static int seg_of(int c, int nseg, const int *seg_n, int *c0)
+{
+    int start = 0;
+    for (int s = 0; s < nseg; s++) {
+        if (c < start + seg_n[s]) {
+            *c0 = start;
+            return s;
+        }
+        start += seg_n[s];
+    }
+    *c0 = start;
+    return nseg;
+}
+
+/* channels with a nonzero bit width */
+int orc_coded_channels(int nseg, const int *seg_n, const int *seg_bits)
+{
+    int n = 0;
+    for (int s = 0; s < nseg; s++)
+        if (seg_bits[s] > 0)
+            n += seg_n[s];
+    return n;
+}
+
+/* words of one record: a code plane of seg_n * seg_bits words per coded
+ * segment (32 tokens), then one metadata word per coded channel */
+int orc_record_words_seg(int nseg, const int *seg_n, const int *seg_bits)
+{
+    int w = 0;
+    for (int s = 0; s < nseg; s++)
+        w += seg_n[s] * seg_bits[s];
+    return w + orc_coded_channels(nseg, seg_n, seg_bits);
+}
+
+void orc_quantize_group_seg(const float *l, int r, int nseg, const int *seg_n,
+                            const int *seg_bits, uint8_t *codes,
+                            uint16_t *scale16, uint16_t *zero16)
 {
     for (int c = 0; c < r; c++) {
-        int bits = c < n_hi ? hi_bit : lo_bit;
+        int c0;
+        int s = seg_of(c, nseg, seg_n, &c0);
+        int bits = s < nseg ? seg_bits[s] : 0;
+        if (bits == 0) {
+            for (int t = 0; t < 32; t++)
+                codes[t * r + c] = 0;
+            scale16[c] = 0;
+            zero16[c] = 0;
+            continue;
+        }
         int levels = (1 << bits) - 1;
         float mn = l[c], mx = l[c];
         for (int t = 1; t < 32; t++) {
@@ -391,11 +446,6 @@ void orc_quantize_group(const float *l, int r, int n_hi, int hi_bit, int lo_bit,
     }
 }
 
-int orc_record_words(int r, int n_hi)
-{
-    return 4 * n_hi + 2 * (r - n_hi) + r;
-}
-
 static void put_bits(uint32_t *w, int64_t bitpos, uint32_t val)
 {
     w[bitpos >> 5] |= val << (bitpos & 31);
@@ -406,78 +456,183 @@ static uint32_t get_bits(const uint32_t *w, int64_t bitpos, int width)
     return (w[bitpos >> 5] >> (bitpos & 31)) & ((1u << width) - 1u);
 }
 
-/* Pack one complete group.  layout 0 = K (token-major planes),
- * 1 = V (channel-major planes).  Requires hi_bit == 4, lo_bit == 2. */
+/* Bit of (token t, channel c) inside its segment's plane.  layout 0 = K
+ * (token-major: t * bits * n + bits * c'), 1 = V (channel-major:
+ * 32 * bits * c' + bits * t), c' = channel index inside the segment. */
+static int64_t code_bit(int layout, int t, int cc, int bits, int n)
+{
+    return layout == 0 ? (int64_t)t * bits * n + (int64_t)bits * cc
+                       : (int64_t)32 * bits * cc + (int64_t)bits * t;
+}
+
+void orc_pack_group_seg(const uint8_t *codes, const uint16_t *scale16,
+                        const uint16_t *zero16, int r, int nseg,
+                        const int *seg_n, const int *seg_bits, int layout,
+                        uint32_t *rec)
+{
+    int words = orc_record_words_seg(nseg, seg_n, seg_bits);
+    memset(rec, 0, sizeof(uint32_t) * words);
+    int plane = 0, c0 = 0, m = 0;
+    int meta0 = words - orc_coded_channels(nseg, seg_n, seg_bits);
+    for (int s = 0; s < nseg; s++) {
+        int n = seg_n[s], bits = seg_bits[s];
+        if (bits > 0) {
+            for (int t = 0; t < 32; t++)
+                for (int cc = 0; cc < n; cc++)
+                    put_bits(rec + plane, code_bit(layout, t, cc, bits, n),
+                             codes[t * r + c0 + cc]);
+            for (int cc = 0; cc < n; cc++, m++)
+                rec[meta0 + m] = (uint32_t)scale16[c0 + cc] | ((uint32_t)zero16[c0 + cc] << 16);
+        }
+        plane += n * bits;
+        c0 += n;
+    }
+    (void)r;
+}
+
+void orc_unpack_group_seg(const uint32_t *rec, int r, int nseg, const int *seg_n,
+                          const int *seg_bits, int layout, uint8_t *codes,
+                          uint16_t *scale16, uint16_t *zero16)
+{
+    int words = orc_record_words_seg(nseg, seg_n, seg_bits);
+    int meta0 = words - orc_coded_channels(nseg, seg_n, seg_bits);
+    int plane = 0, c0 = 0, m = 0;
+    for (int s = 0; s < nseg; s++) {
+        int n = seg_n[s], bits = seg_bits[s];
+        for (int cc = 0; cc < n; cc++) {
+            int c = c0 + cc;
+            if (bits > 0) {
+                for (int t = 0; t < 32; t++)
+                    codes[t * r + c] = (uint8_t)get_bits(rec + plane, code_bit(layout, t, cc, bits, n), bits);
+                scale16[c] = (uint16_t)(rec[meta0 + m] & 0xffff);
+                zero16[c] = (uint16_t)(rec[meta0 + m] >> 16);
+                m++;
+            } else {
+                for (int t = 0; t < 32; t++)
+                    codes[t * r + c] = 0;
+                scale16[c] = 0;
+                zero16[c] = 0;
+            }
+        }
+        plane += n * bits;
+        c0 += n;
+    }
+}
+
+/*
+ * Encode a stream of n latents [n][r] (token order) of one (sequence, head,
+ * tensor): complete 32-token groups are quantised and packed into records;
+ * the last n % 32 latents of the coded channels (in channel order) are
+ * copied to the fp32 tail [n % 32][coded channels].
+ */
+void orc_encode_stream_seg(const float *lat, int64_t n, int r, int nseg,
+                           const int *seg_n, const int *seg_bits, int layout,
+                           uint32_t *records, float *tail)
+{
+    int words = orc_record_words_seg(nseg, seg_n, seg_bits);
+    int rc = orc_coded_channels(nseg, seg_n, seg_bits);
+    int64_t full = n / 32;
+    uint8_t *codes = malloc((size_t)32 * (r > 0 ? r : 1));
+    uint16_t *sc = malloc(sizeof(uint16_t) * (r > 0 ? r : 1)), *zr = malloc(sizeof(uint16_t) * (r > 0 ? r : 1));
+    for (int64_t j = 0; j < full; j++) {
+        orc_quantize_group_seg(lat + j * 32 * r, r, nseg, seg_n, seg_bits, codes, sc, zr);
+        orc_pack_group_seg(codes, sc, zr, r, nseg, seg_n, seg_bits, layout, records + j * words);
+    }
+    for (int64_t i = full * 32; i < n; i++) {
+        int k = 0;
+        for (int c = 0; c < r; c++) {
+            int c0;
+            int s = seg_of(c, nseg, seg_n, &c0);
+            if (s < nseg && seg_bits[s] > 0)
+                tail[(i - full * 32) * rc + k++] = lat[i * r + c];
+        }
+    }
+    free(codes);
+    free(sc);
+    free(zr);
+}
+
+/* Dequantised latents (fp64) [n][r] of n tokens: complete groups from
+ * records, l_hat = code * scale16 + zero16 evaluated exactly in fp64; the
+ * remaining n % 32 from the fp32 tail; 0-bit channels are 0. */
+void orc_decode_stream_seg(const uint32_t *records, const float *tail, int64_t n,
+                           int r, int nseg, const int *seg_n, const int *seg_bits,
+                           int layout, double *out)
+{
+    int words = orc_record_words_seg(nseg, seg_n, seg_bits);
+    int rc = orc_coded_channels(nseg, seg_n, seg_bits);
+    int64_t full = n / 32;
+    uint8_t *codes = malloc((size_t)32 * (r > 0 ? r : 1));
+    uint16_t *sc = malloc(sizeof(uint16_t) * (r > 0 ? r : 1)), *zr = malloc(sizeof(uint16_t) * (r > 0 ? r : 1));
+    for (int64_t j = 0; j < full; j++) {
+        orc_unpack_group_seg(records + j * words, r, nseg, seg_n, seg_bits, layout, codes, sc, zr);
+        for (int t = 0; t < 32; t++)
+            for (int c = 0; c < r; c++)
+                out[(j * 32 + t) * r + c] =
+                    (double)codes[t * r + c] * (double)orc_half_to_float(sc[c]) +
+                    (double)orc_half_to_float(zr[c]);
+    }
+    for (int64_t i = full * 32; i < n; i++) {
+        int k = 0;
+        for (int c = 0; c < r; c++) {
+            int c0;
+            int s = seg_of(c, nseg, seg_n, &c0);
+            out[i * r + c] = (s < nseg && seg_bits[s] > 0) ? (double)tail[(i - full * 32) * rc + k++] : 0.0;
+        }
+    }
+    free(codes);
+    free(sc);
+    free(zr);
+}
+
+/* The PALU split as segments: [n_hi channels at hi_bit, the rest at lo_bit]. */
+static void palu_segments(int r, int n_hi, int hi_bit, int lo_bit, int *seg_n, int *seg_bits)
+{
+    seg_n[0] = n_hi;
+    seg_bits[0] = hi_bit;
+    seg_n[1] = r - n_hi;
+    seg_bits[1] = lo_bit;
+}
+
+void orc_quantize_group(const float *l, int r, int n_hi, int hi_bit, int lo_bit,
+                        uint8_t *codes, uint16_t *scale16, uint16_t *zero16)
+{
+    int sn[2], sb[2];
+    palu_segments(r, n_hi, hi_bit, lo_bit, sn, sb);
+    orc_quantize_group_seg(l, r, 2, sn, sb, codes, scale16, zero16);
+}
+
+int orc_record_words(int r, int n_hi)
+{
+    return 4 * n_hi + 2 * (r - n_hi) + r;
+}
+
+/* Pack one complete group with the PALU split at 4 / 2 bits.  layout 0 = K
+ * (token-major planes), 1 = V (channel-major planes). */
 void orc_pack_group(const uint8_t *codes, const uint16_t *scale16,
                     const uint16_t *zero16, int r, int n_hi, int layout,
                     uint32_t *rec)
 {
-    int n_lo = r - n_hi;
-    int words = orc_record_words(r, n_hi);
-    memset(rec, 0, sizeof(uint32_t) * words);
-    uint32_t *hi = rec, *lo = rec + 4 * n_hi, *meta = rec + 4 * n_hi + 2 * n_lo;
-    for (int t = 0; t < 32; t++) {
-        for (int c = 0; c < n_hi; c++) {
-            int64_t pos = layout == 0 ? (int64_t)t * 4 * n_hi + 4 * c
-                                      : (int64_t)c * 128 + 4 * t;
-            put_bits(hi, pos, codes[t * r + c]);
-        }
-        for (int c = 0; c < n_lo; c++) {
-            int64_t pos = layout == 0 ? (int64_t)t * 2 * n_lo + 2 * c
-                                      : (int64_t)c * 64 + 2 * t;
-            put_bits(lo, pos, codes[t * r + n_hi + c]);
-        }
-    }
-    for (int c = 0; c < r; c++)
-        meta[c] = (uint32_t)scale16[c] | ((uint32_t)zero16[c] << 16);
+    int sn[2], sb[2];
+    palu_segments(r, n_hi, 4, 2, sn, sb);
+    orc_pack_group_seg(codes, scale16, zero16, r, 2, sn, sb, layout, rec);
 }
 
 void orc_unpack_group(const uint32_t *rec, int r, int n_hi, int layout,
                       uint8_t *codes, uint16_t *scale16, uint16_t *zero16)
 {
-    int n_lo = r - n_hi;
-    const uint32_t *hi = rec, *lo = rec + 4 * n_hi,
-                   *meta = rec + 4 * n_hi + 2 * n_lo;
-    for (int t = 0; t < 32; t++) {
-        for (int c = 0; c < n_hi; c++) {
-            int64_t pos = layout == 0 ? (int64_t)t * 4 * n_hi + 4 * c
-                                      : (int64_t)c * 128 + 4 * t;
-            codes[t * r + c] = (uint8_t)get_bits(hi, pos, 4);
-        }
-        for (int c = 0; c < n_lo; c++) {
-            int64_t pos = layout == 0 ? (int64_t)t * 2 * n_lo + 2 * c
-                                      : (int64_t)c * 64 + 2 * t;
-            codes[t * r + n_hi + c] = (uint8_t)get_bits(lo, pos, 2);
-        }
-    }
-    for (int c = 0; c < r; c++) {
-        scale16[c] = (uint16_t)(meta[c] & 0xffff);
-        zero16[c] = (uint16_t)(meta[c] >> 16);
-    }
+    int sn[2], sb[2];
+    palu_segments(r, n_hi, 4, 2, sn, sb);
+    orc_unpack_group_seg(rec, r, 2, sn, sb, layout, codes, scale16, zero16);
 }
 
-/*
- * Encode a stream of n latents (token order) of one (sequence, head, tensor):
- * complete 32-token groups are quantised and packed into records, the last
- * n % 32 latents are copied to the fp32 tail.
- */
 void orc_encode_stream(const float *lat, int64_t n, int r, int n_hi,
                        int hi_bit, int lo_bit, int layout, uint32_t *records,
                        float *tail)
 {
-    int words = orc_record_words(r, n_hi);
-    int64_t full = n / 32;
-    uint8_t *codes = malloc((size_t)32 * r);
-    uint16_t *sc = malloc(sizeof(uint16_t) * r), *zr = malloc(sizeof(uint16_t) * r);
-    for (int64_t j = 0; j < full; j++) {
-        orc_quantize_group(lat + j * 32 * r, r, n_hi, hi_bit, lo_bit, codes, sc, zr);
-        orc_pack_group(codes, sc, zr, r, n_hi, layout, records + j * words);
-    }
-    int64_t rem = n - full * 32;
-    memcpy(tail, lat + full * 32 * r, sizeof(float) * rem * r);
-    free(codes);
-    free(sc);
-    free(zr);
+    int sn[2], sb[2];
+    palu_segments(r, n_hi, hi_bit, lo_bit, sn, sb);
+    orc_encode_stream_seg(lat, n, r, 2, sn, sb, layout, records, tail);
 }
 
 /* fp16 value latents: records of r*32 halves (channel-major); the last,
@@ -494,30 +649,13 @@ void orc_encode_fp16_stream(const float *lat, int64_t n, int r, uint16_t *record
     }
 }
 
-/* Dequantised latents (fp64) of n tokens: complete groups from records,
- * the remaining n % 32 from the fp32 tail.
- * l_hat = code * scale16 + zero16, evaluated exactly in fp64. */
+/* Dequantised latents (fp64) of n tokens with the PALU split at 4 / 2 bits. */
 void orc_decode_stream(const uint32_t *records, const float *tail, int64_t n,
                        int r, int n_hi, int layout, double *out)
 {
-    int words = orc_record_words(r, n_hi);
-    int64_t full = n / 32;
-    uint8_t *codes = malloc((size_t)32 * r);
-    uint16_t *sc = malloc(sizeof(uint16_t) * r), *zr = malloc(sizeof(uint16_t) * r);
-    for (int64_t j = 0; j < full; j++) {
-        orc_unpack_group(records + j * words, r, n_hi, layout, codes, sc, zr);
-        for (int t = 0; t < 32; t++)
-            for (int c = 0; c < r; c++)
-                out[(j * 32 + t) * r + c] =
-                    (double)codes[t * r + c] * (double)orc_half_to_float(sc[c]) +
-                    (double)orc_half_to_float(zr[c]);
-    }
-    for (int64_t i = full * 32; i < n; i++)
-        for (int c = 0; c < r; c++)
-            out[i * r + c] = (double)tail[(i - full * 32) * r + c];
-    free(codes);
-    free(sc);
-    free(zr);
+    int sn[2], sb[2];
+    palu_segments(r, n_hi, 4, 2, sn, sb);
+    orc_decode_stream_seg(records, tail, n, r, 2, sn, sb, layout, out);
 }
 
 void orc_decode_fp16_stream(const uint16_t *records, int64_t n, int r, double *out)

@@ -68,6 +68,20 @@ def lib():
         L.orc_decode_stream.argtypes = [_u32p, _f32p, _c_i64, _c_int, _c_int,
                                         _c_int, _f64p]
         L.orc_decode_fp16_stream.argtypes = [_u16p, _c_i64, _c_int, _f64p]
+        L.orc_coded_channels.argtypes = [_c_int, _i32p, _i32p]
+        L.orc_coded_channels.restype = _c_int
+        L.orc_record_words_seg.argtypes = [_c_int, _i32p, _i32p]
+        L.orc_record_words_seg.restype = _c_int
+        L.orc_quantize_group_seg.argtypes = [_f32p, _c_int, _c_int, _i32p, _i32p, _u8p, _u16p,
+                                             _u16p]
+        L.orc_pack_group_seg.argtypes = [_u8p, _u16p, _u16p, _c_int, _c_int, _i32p, _i32p,
+                                         _c_int, _u32p]
+        L.orc_unpack_group_seg.argtypes = [_u32p, _c_int, _c_int, _i32p, _i32p, _c_int, _u8p,
+                                           _u16p, _u16p]
+        L.orc_encode_stream_seg.argtypes = [_f32p, _c_i64, _c_int, _c_int, _i32p, _i32p,
+                                            _c_int, _u32p, _f32p]
+        L.orc_decode_stream_seg.argtypes = [_u32p, _f32p, _c_i64, _c_int, _c_int, _i32p,
+                                            _i32p, _c_int, _f64p]
         L.orc_attend.argtypes = [_f64p, _f32p, _c_int, _f32p, _c_int, _f64p, _f32p,
                                  _c_int, _f32p, _c_int, _c_i64, _c_int, _f32p,
                                  _c_dbl, _f64p]
@@ -262,6 +276,103 @@ def decode_stream(records, tail, n: int, r: int, n_hi: int, layout: int):
     return out
 
 
+# -------------------------------------------------------- segment coder
+
+@dataclasses.dataclass
+class Segments:
+    """Latent channels in contiguous segments, descending singular value
+    first: seg_n[s] channels coded with seg_bits[s] bits (0 = not stored)."""
+    seg_n: np.ndarray     # int32 [nseg]
+    seg_bits: np.ndarray  # int32 [nseg]
+
+    @property
+    def r(self) -> int:
+        return int(self.seg_n.sum())
+
+    @property
+    def coded(self) -> int:
+        return lib().orc_coded_channels(len(self.seg_n), self.seg_n, self.seg_bits)
+
+    def words(self) -> int:
+        return lib().orc_record_words_seg(len(self.seg_n), self.seg_n, self.seg_bits)
+
+
+def palu_segments(r: int, hi_fraction: float = 0.25, hi_bit: int = 4, lo_bit: int = 2) -> Segments:
+    """PALU's split (PALU page, "Usage"): the first floor(hi_fraction r)
+    channels at hi_bit, the rest at lo_bit."""
+    n_hi = n_hi_channels(r, hi_fraction)
+    return Segments(np.array([n_hi, r - n_hi], np.int32), np.array([hi_bit, lo_bit], np.int32))
+
+
+def schedule_segments(r: int, schedule) -> Segments:
+    """A bit schedule (SVDq cache page): r channels split into len(schedule)
+    contiguous groups of equal size, the first r % len(schedule) groups one
+    channel larger (the plain reading when r is not a multiple), group i
+    coded with schedule[i] bits."""
+    L = len(schedule)
+    base, extra = divmod(r, L)
+    n = np.array([base + (1 if i < extra else 0) for i in range(L)], np.int32)
+    return Segments(n, np.array(schedule, np.int32))
+
+
+def schedule_effective_bits(r: int, D: int, schedule) -> float:
+    """Nominal key rate (r / D) * mean(schedule) of the SVDq cache page."""
+    return (r / D) * float(np.mean(schedule))
+
+
+def quantize_group_seg(l, seg: Segments):
+    l = _c(l, np.float32)
+    r = l.shape[1]
+    codes = np.empty((32, r), np.uint8)
+    sc = np.empty(r, np.uint16)
+    zr = np.empty(r, np.uint16)
+    lib().orc_quantize_group_seg(l, r, len(seg.seg_n), seg.seg_n, seg.seg_bits, codes, sc, zr)
+    return codes, sc, zr
+
+
+def pack_group_seg(codes, scale16, zero16, seg: Segments, layout: int) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    rec = np.empty(seg.words(), np.uint32)
+    lib().orc_pack_group_seg(codes, _c(scale16, np.uint16), _c(zero16, np.uint16), codes.shape[1],
+                             len(seg.seg_n), seg.seg_n, seg.seg_bits, layout, rec)
+    return rec
+
+
+def unpack_group_seg(rec, seg: Segments, layout: int):
+    r = seg.r
+    codes = np.empty((32, r), np.uint8)
+    sc = np.empty(r, np.uint16)
+    zr = np.empty(r, np.uint16)
+    lib().orc_unpack_group_seg(_c(rec, np.uint32), r, len(seg.seg_n), seg.seg_n, seg.seg_bits,
+                               layout, codes, sc, zr)
+    return codes, sc, zr
+
+
+def encode_stream_seg(lat, seg: Segments, layout: int):
+    """lat fp32 [n, r] -> (records u32 [n // 32, W], tail fp32 [n % 32, coded])."""
+    lat = _c(lat, np.float32)
+    n, r = lat.shape
+    rec = np.zeros((n // 32, seg.words()), np.uint32)
+    tail = np.zeros((n % 32, seg.coded), np.float32)
+    lib().orc_encode_stream_seg(lat, n, r, len(seg.seg_n), seg.seg_n, seg.seg_bits, layout,
+                                rec.reshape(-1) if rec.size else np.zeros(1, np.uint32),
+                                tail.reshape(-1) if tail.size else np.zeros(1, np.float32))
+    return rec, tail
+
+
+def decode_stream_seg(records, tail, n: int, seg: Segments, layout: int) -> np.ndarray:
+    r = seg.r
+    out = np.empty((n, r), np.float64)
+    if n == 0:
+        return out
+    rec = _c(records, np.uint32).reshape(-1)
+    tl = _c(tail, np.float32).reshape(-1)
+    lib().orc_decode_stream_seg(rec if rec.size else np.zeros(1, np.uint32),
+                                tl if tl.size else np.zeros(1, np.float32), n, r,
+                                len(seg.seg_n), seg.seg_n, seg.seg_bits, layout, out)
+    return out
+
+
 def decode_fp16_stream(records, n: int, r: int) -> np.ndarray:
     out = np.empty((n, r), np.float64)
     if n:
@@ -341,15 +452,23 @@ class OracleLayer:
     mapping); kv head h uses the basis of group h // (Hkv / G)."""
 
     def __init__(self, D, n_q_heads, n_kv_heads, n_groups, fitK: Fit, fitV: Fit,
-                 hi_fraction=0.25, hi_bit=4, lo_bit=2, quantize_values=True, bf16=False):
+                 hi_fraction=0.25, hi_bit=4, lo_bit=2, quantize_values=True, bf16=False,
+                 schedule=None):
         self.D, self.Hq, self.Hkv, self.G = D, n_q_heads, n_kv_heads, n_groups
         self.fit = (fitK, fitV)
         self.hi_fraction, self.hi_bit, self.lo_bit = hi_fraction, hi_bit, lo_bit
         self.quantize_values = quantize_values
         self.bf16 = bf16          # inputs (K, V, q) are bf16 bit patterns
+        self.schedule = None if schedule is None else list(schedule)   # bit schedule or PALU split
 
     def n_hi(self, tensor):
         return n_hi_channels(self.fit[tensor].r, self.hi_fraction)
+
+    def segments(self, tensor) -> Segments:
+        r = self.fit[tensor].r
+        if self.schedule is not None:
+            return schedule_segments(r, self.schedule)
+        return palu_segments(r, self.hi_fraction, self.hi_bit, self.lo_bit)
 
     def group_of(self, h):
         return h // (self.Hkv // self.G)
@@ -364,16 +483,14 @@ class OracleLayer:
         lat = self.latents(x_head, h, tensor)
         if tensor == 1 and not self.quantize_values:
             return {"fp16": encode_fp16_stream(lat), "n": lat.shape[0]}
-        rec, tail = encode_stream(lat, self.n_hi(tensor), self.hi_bit, self.lo_bit,
-                                  tensor)
+        rec, tail = encode_stream_seg(lat, self.segments(tensor), tensor)
         return {"records": rec, "tail": tail, "n": lat.shape[0]}
 
     def decode_head(self, st, tensor):
         r = self.fit[tensor].r
         if "fp16" in st:
             return decode_fp16_stream(st["fp16"], st["n"], r)
-        return decode_stream(st["records"], st["tail"], st["n"], r,
-                             self.n_hi(tensor), tensor)
+        return decode_stream_seg(st["records"], st["tail"], st["n"], self.segments(tensor), tensor)
 
     def attend(self, kstates, vstates, q, scale=None):
         """kstates / vstates: per kv head stored state; q fp16 [Hq, D].

@@ -434,7 +434,10 @@ def test_effective_bits_golden():
             assert oracle.fp16_latent_bits(r, D) == expect
         else:
             sched = (8, 4, 2, 1, 1, 0, 0, 0)
-            assert (r / D) * (sum(sched) / len(sched)) == expect
+            assert oracle.schedule_effective_bits(r, D, sched) == expect
+            # the stored code bits per element of that schedule at r = 64
+            seg = oracle.schedule_segments(r, sched)
+            assert float(np.sum(seg.seg_n * seg.seg_bits)) / D == expect
 
 
 def test_fp16_cache_bytes_golden():
@@ -678,6 +681,119 @@ def test_bf16_beyond_fp16_range_reconstructs():
     rec = lat @ f.V(0).T.astype(np.float64) + f.mu[0]
     np.testing.assert_allclose(rec, xv[0, 0], rtol=0, atol=2e-2)
     assert abs(f.mu[0][5] - xv[0, 0, :, 5].mean()) < 1e-2
+
+
+# ------------------------------------------------------- segment coder
+
+@pytest.mark.parametrize("r,L", [(32, 8), (30, 8), (9, 8), (7, 8), (64, 3), (1, 2)])
+def test_schedule_split_matches_array_split(r, L):
+    seg = oracle.schedule_segments(r, [1] * L)
+    want = [len(a) for a in np.array_split(np.arange(r), L)]
+    assert seg.seg_n.tolist() == want and seg.r == r
+
+
+@pytest.mark.parametrize("bits", [1, 8])
+def test_quantizer_nearest_level_other_widths(bits):
+    rng = np.random.default_rng(100 + bits)
+    levels = 2 ** bits - 1
+    seg = oracle.Segments(np.array([1], np.int32), np.array([bits], np.int32))
+    for trial in range(200):
+        l = (rng.standard_normal((32, 1)) * rng.uniform(0.01, 5)).astype(np.float32)
+        codes, sc, zr = oracle.quantize_group_seg(l, seg)
+        c = codes[:, 0].astype(np.int64)
+        mn = np.float64(l.min())
+        scale = np.float64(np.float32(np.float32(l.max()) - np.float32(l.min())) / np.float32(levels))
+        assert c.min() == 0 and c.max() == levels
+        u = (l[:, 0].astype(np.float64) - mn) / scale
+        best = np.argmin(np.abs(np.arange(levels + 1)[None, :] - u[:, None]), axis=1)
+        near_tie = np.abs(np.abs(u - np.floor(u)) - 0.5) < 1e-5
+        assert np.array_equal(best[~near_tie], c[~near_tie])
+
+
+def test_segment_record_layout_hand_checked():
+    """Segments [2 channels x 8 bits, 3 channels x 1 bit]: planes of 16 and
+    3 words, then 5 metadata words.  K: token t, channel c of the 8-bit
+    segment at bit 16 t + 8 c; the 1-bit plane starts at word 16, token t,
+    channel c' at bit 3 t + c'.  V: channel c, token t at bit 256 c + 8 t;
+    1-bit channel c', token t at bit 32 c' + t of its plane."""
+    seg = oracle.Segments(np.array([2, 3], np.int32), np.array([8, 1], np.int32))
+    assert seg.words() == 2 * 8 + 3 * 1 + 5
+    rng = np.random.default_rng(3)
+    codes = np.zeros((32, 5), np.uint8)
+    codes[:, :2] = rng.integers(0, 256, (32, 2))
+    codes[:, 2:] = rng.integers(0, 2, (32, 3))
+    sc = np.arange(1, 6, dtype=np.uint16)
+    zr = np.arange(11, 16, dtype=np.uint16)
+    for layout in (0, 1):
+        rec = oracle.pack_group_seg(codes, sc, zr, seg, layout)
+        bits = np.unpackbits(rec.view(np.uint8), bitorder="little")
+        for t in range(32):
+            for c in range(2):
+                pos = 16 * t + 8 * c if layout == 0 else 256 * c + 8 * t
+                assert int(np.packbits(bits[pos:pos + 8], bitorder="little")[0]) == codes[t, c]
+            for c in range(3):
+                pos = 32 * 16 + (3 * t + c if layout == 0 else 32 * c + t)
+                assert bits[pos] == codes[t, 2 + c]
+        assert np.array_equal(rec[19:], (sc.astype(np.uint32) | (zr.astype(np.uint32) << 16)))
+        back = oracle.unpack_group_seg(rec, seg, layout)
+        assert np.array_equal(back[0], codes) and np.array_equal(back[1], sc) and np.array_equal(back[2], zr)
+
+
+@pytest.mark.parametrize("sched", [(8, 4, 2, 1, 1, 0, 0, 0), (4, 0, 2), (1, 8), (2,), (0, 4)])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_zero_bit_segments_are_truncation(sched, layout):
+    """A 0-bit segment stores nothing and decodes to exactly 0: encoding with
+    the schedule equals encoding only the coded channels with the schedule's
+    nonzero entries, and the decoded latents of the coded channels agree."""
+    rng = np.random.default_rng(len(sched) * 7 + layout)
+    r = 27
+    lat = (rng.standard_normal((75, r)) * np.linspace(3, 0.2, r)).astype(np.float32)
+    seg = oracle.schedule_segments(r, sched)
+    coded = np.concatenate([np.full(n, b > 0) for n, b in zip(seg.seg_n, seg.seg_bits)])
+    keep = seg.seg_bits > 0
+    seg2 = oracle.Segments(seg.seg_n[keep], seg.seg_bits[keep])
+    rec, tail = oracle.encode_stream_seg(lat, seg, layout)
+    rec2, tail2 = oracle.encode_stream_seg(lat[:, coded], seg2, layout)
+    assert np.array_equal(rec, rec2) and np.array_equal(tail, tail2)
+    dec = oracle.decode_stream_seg(rec, tail, 75, seg, layout)
+    dec2 = oracle.decode_stream_seg(rec2, tail2, 75, seg2, layout)
+    assert np.all(dec[:, ~coded] == 0.0)
+    assert np.array_equal(dec[:, coded], dec2)
+    # the tail keeps the fp32 latents of the coded channels exactly
+    assert np.array_equal(dec[64:, coded], lat[64:, coded].astype(np.float64))
+
+
+def test_two_segment_coder_is_the_palu_split():
+    rng = np.random.default_rng(5)
+    for r in (9, 12, 32, 33):
+        lat = rng.standard_normal((70, r)).astype(np.float32)
+        n_hi = oracle.n_hi_channels(r, 0.25)
+        for layout in (0, 1):
+            a = oracle.encode_stream(lat, n_hi, 4, 2, layout)
+            b = oracle.encode_stream_seg(lat, oracle.palu_segments(r), layout)
+            assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_layer_with_bit_schedule_attends():
+    """A layer coded with the SVDq default schedule: decode attention equals
+    brute-force softmax attention over its own decoded latents."""
+    w = synth.small_workload(batch=1, n_kv_heads=1, n_q_heads=2, prefill=70, rank=24)
+    k = synth.batch_kv(w, 0, 70)
+    v = synth.batch_kv(w, 1, 70)
+    fk = oracle.fit(k, [70], 1, rank=24)
+    fv = oracle.fit(v, [70], 1, rank=24)
+    layer = oracle.OracleLayer(128, 2, 1, 1, fk, fv, schedule=(8, 4, 2, 1, 1, 0, 0, 0))
+    ks = [layer.encode_head(k[0, 0], 0, 0)]
+    vs = [layer.encode_head(v[0, 0], 0, 1)]
+    assert ks[0]["tail"].shape == (70 % 32, 15)               # 24 channels, 9 of them 0-bit
+    q = synth.queries(w, 0, 1)[0]
+    out = layer.attend(ks, vs, q)
+    lk, lv = layer.decode_head(ks[0], 0), layer.decode_head(vs[0], 1)
+    K = lk @ fk.V(0).T.astype(np.float64) + fk.mu[0]
+    V = lv @ fv.V(0).T.astype(np.float64) + fv.mu[0]
+    for i in range(2):
+        np.testing.assert_allclose(out[i], _sdpa(q[i].astype(np.float64), K, V, 1 / np.sqrt(128)),
+                                   rtol=1e-12, atol=1e-12)
 
 
 # ------------------------------------------------------------- quality
