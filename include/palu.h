@@ -58,8 +58,8 @@ typedef struct palu_config {
                                   group g owns heads [g*H/G, (g+1)*H/G)           */
     int32_t rank;              /* explicit rank (clamped to D); 0 = energy rule   */
     float energy_threshold;    /* tau of the energy rule, in (0, 1]               */
-    int32_t hi_bit;            /* bits of the top channels; only 4 supported      */
-    int32_t lo_bit;            /* bits of the other channels; only 2 supported    */
+    int32_t hi_bit;            /* bits of the top channels: 1, 2, 4 or 8          */
+    int32_t lo_bit;            /* bits of the other channels: 1, 2, 4 or 8        */
     float hi_fraction;         /* n_hi = floor(hi_fraction * r) channels at hi_bit */
     int32_t group_size;        /* tokens per quantisation group; only 32          */
     int32_t quantize_values;   /* 1: V mixed-bit like K; 0: V as fp16 latents     */
@@ -77,6 +77,18 @@ typedef struct palu_config {
                                   their fp16 scale/zero words and the fp32 tails
                                   are the same for both; with bf16, latents must
                                   stay within the fp16 range like with fp16.     */
+    int32_t schedule_len;      /* 0: PALU's split above (hi_fraction, hi_bit,
+                                  lo_bit).  1..8: a bit schedule as on the SVDq
+                                  cache page: the r latent channels form
+                                  schedule_len contiguous groups of equal size
+                                  (the first r % schedule_len one channel
+                                  larger), largest singular values first, group
+                                  i coded with bit_schedule[i] bits; 0 bits drops
+                                  the group (its latent is exactly zero and is
+                                  stored nowhere).  Applies to K, and to V when
+                                  quantize_values is 1.                          */
+    int32_t bit_schedule[8];   /* bits per group: 0, 1, 2, 4 or 8; at least one
+                                  nonzero among the first schedule_len           */
 } palu_config;
 
 /* Fills the page's defaults (rank 0 = energy rule, threshold 0.90, G = 4,
@@ -137,8 +149,9 @@ int palu_get_basis(const palu_cache *cache, int32_t tensor, int32_t *r,
 /* Appends tokens (PALU page, "How it works", decode steps 1-2): projects
  * each new key/value into its group's basis with a fixed-order fp32 chain,
  * quantises every 32-token group that becomes complete (asymmetric min/max,
- * round half to even, top n_hi channels at hi_bit, others at lo_bit) and
- * keeps the incomplete group's latents in fp32 until it completes.
+ * round half to even, each channel at its segment's width: PALU's split or
+ * the bit schedule) and keeps the incomplete group's latents of the coded
+ * channels in fp32 until it completes.
  *   k, v     : device fp16 or bf16 (input_dtype) [B][H][T_stride][D]
  *   seq_ids  : host int32 [B] slot of each row (NULL = 0..B-1), distinct
  *   n_new    : host int32 [B] tokens to append per row (NULL = T_stride each),
@@ -191,17 +204,21 @@ int palu_seq_len(const palu_cache *cache, int32_t seq, int32_t *len);
 /* Copies the stored state of one (slot, kv head, tensor) to host memory.
  * Synchronous on the null stream after a device synchronisation.
  *   records : host, receives the complete groups' records in order:
- *             mixed-bit: floor(len/32) records of record_words(r) uint32
+ *             quantised: floor(len/32) records of palu_record_words uint32
  *             fp16 V latents: ceil(len/32) records of r*32 fp16 (c*32 + t);
  *             may be NULL
- *   tail    : host fp32 [len % 32][r] latents of the incomplete group (NULL
- *             allowed; not used for fp16 V latents)
- * The byte sizes must be at least what is copied.  Record layout:
- *   K (tensor 0): hi plane 4*n_hi words, token t channel c at bit
- *     t*4*n_hi + 4c; lo plane 2*n_lo words, token t channel n_hi + c' at bit
- *     t*2*n_lo + 2c'; then r words scale16[c] | zero16[c] << 16.
- *   V (tensor 1): hi plane channel c token t at bit 128c + 4t; lo plane
- *     channel n_hi + c' token t at bit 64c' + 2t; then the r meta words. */
+ *   tail    : host fp32 [len % 32][coded] latents of the incomplete group,
+ *             coded = the stats' coded_k / coded_v (NULL allowed; not used
+ *             for fp16 V latents)
+ * The byte sizes must be at least what is copied.  Record layout: the coded
+ * channels (0-bit channels dropped, order kept) form segments of n_s
+ * channels at b_s bits; segment s has a code plane of n_s * b_s words, the
+ * planes in segment order, then one word scale16[c] | zero16[c] << 16 per
+ * coded channel.  Inside a plane (c' = channel index in the segment):
+ *   K (tensor 0): token t, channel c' at bit t * b_s * n_s + b_s * c'
+ *   V (tensor 1): channel c', token t at bit 32 * b_s * c' + b_s * t
+ * PALU's split gives a 4-bit plane of 4 n_hi words and a 2-bit plane of
+ * 2 (r - n_hi) words. */
 int palu_read_codes(const palu_cache *cache, int32_t seq, int32_t head,
                     int32_t tensor, void *records, size_t records_bytes,
                     float *tail, size_t tail_bytes);
@@ -209,15 +226,20 @@ int palu_read_codes(const palu_cache *cache, int32_t seq, int32_t head,
 /* Byte accounting and rates (PALU page, "Effective bit-width" and
  * "Evidence"; SVDq cache page, "Byte accounting"). */
 typedef struct palu_stats {
-    int32_t r_k, r_v, n_hi_k, n_hi_v;
+    int32_t r_k, r_v, n_hi_k, n_hi_v;  /* fitted ranks; channels of the first coder
+                                         segment (PALU: n_hi; 0 for fp16 latents) */
     int64_t tokens;                  /* sum of stored tokens over slots        */
     int64_t compressed_key_bytes;    /* records + tails + K bases and means    */
     int64_t compressed_value_bytes;  /* same for V (fp16 latents if unquantised) */
     int64_t fp16_key_bytes;          /* tokens * H * D * 2                     */
     int64_t fp16_value_bytes;
-    double nominal_bits_k, nominal_bits_v;   /* (r/D)(h b_hi + (1-h) b_lo) or 16 r/D */
-    double realised_bits_k, realised_bits_v; /* (n_hi b_hi + n_lo b_lo)/D or 16 r/D */
+    double nominal_bits_k, nominal_bits_v;   /* (r/D)(h b_hi + (1-h) b_lo), with a schedule
+                                                (r/D) mean(schedule); 16 r/D for fp16 latents */
+    double realised_bits_k, realised_bits_v; /* code bits per element: sum over channels of
+                                                their widths / D, or 16 r/D            */
     double assigned_avg_bits;        /* max of the realised K and V rates      */
+    int32_t coded_k, coded_v;        /* latent channels stored (0-bit channels dropped):
+                                        the tail width returned by palu_read_codes */
 } palu_stats;
 
 int palu_get_stats(const palu_cache *cache, palu_stats *out);
@@ -225,7 +247,9 @@ int palu_get_stats(const palu_cache *cache, palu_stats *out);
 /* Empties every slot, keeping the basis. */
 int palu_reset(palu_cache *cache);
 
-/* Words of one mixed-bit record for rank r: 4 n_hi + 2 (r - n_hi) + r. */
+/* Words of one record: the code planes (channels x bits words per segment)
+ * plus one metadata word per coded channel; PALU's split gives
+ * 4 n_hi + 2 (r - n_hi) + r; fp16 value latents 16 r. */
 int palu_record_words(const palu_cache *cache, int32_t tensor, int32_t *words);
 
 /* Save / restore of one sequence slot: the prompt-cache round trip that the
@@ -235,12 +259,13 @@ int palu_record_words(const palu_cache *cache, int32_t tensor, int32_t *words);
  * serialized form is a 64-byte header followed by, for K then V, the records
  * of every kv head in head order (len / 32 records of words_t uint32 each;
  * fp16 value latents keep ceil(len / 32), the last one partial) and then the
- * fp32 tail latents of every kv head in head order (len % 32 rows of r_t
- * floats; none for fp16 value latents).  Header, all
+ * fp32 tail latents of every kv head in head order (len % 32 rows of
+ * coded_t floats; none for fp16 value latents).  Header, all
  * little-endian: uint32 magic 0x564B4C50 ("PLKV"), uint32 version 1, int32
- * head_dim, n_kv_heads, n_head_groups, r_K, r_V, n_hi_K, n_hi_V, words_K,
- * words_V, quantize_values, len, uint64 FNV-1a hash of the fp32 bases and
- * means of both tensors, 4 zero bytes.  The basis itself is not included
+ * head_dim, n_kv_heads, n_head_groups, r_K, r_V, coder_K, coder_V (32-bit
+ * FNV-1a hashes of each tensor's segment layout), words_K, words_V,
+ * quantize_values, len, uint64 FNV-1a hash of the fp32 bases and means of
+ * both tensors, 4 zero bytes.  The basis itself is not included
  * (palu_get_basis / palu_set_basis move it).
  *
  * palu_export_bytes: bytes of the serialized slot.  palu_export_seq:

@@ -11,6 +11,8 @@
 #include <cmath>
 #include <cstdint>
 
+#include "palu_internal.h"
+
 namespace palu {
 namespace {
 
@@ -140,6 +142,62 @@ __device__ __forceinline__ int bf16_rows_to_fp16(uint4 (&qa)[4]) {
     return k;
 }
 
+// ---- segment coder lookups (see Coder).  Select chains over the fixed
+//      8-entry arrays: no dynamic indexing of kernel arguments.
+template <int N>
+__device__ __forceinline__ int pick(const int (&v)[N], int s) {
+    int r = v[0];
+#pragma unroll
+    for (int k = 1; k < N; ++k) r = s == k ? v[k] : r;
+    return r;
+}
+// segment holding channel c / 8-channel block q
+__device__ __forceinline__ int seg_of_channel(const Coder &cd, int c) {
+    int s = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxSegs; ++k) s += (k < cd.nseg && c >= cd.c0[k]) ? 1 : 0;
+    return s;
+}
+__device__ __forceinline__ int seg_of_block(const Coder &cd, int q) {
+    int s = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxSegs; ++k) s += (k < cd.nseg && q >= cd.q0[k]) ? 1 : 0;
+    return s;
+}
+
+// Key-record addressing of 8-channel block q (token-major planes): the
+// block's codes of token t start at bit base + t * stride, channel k of the
+// block at bit w * k after that; channels [chan0, chanend) are real.
+struct KBlock {
+    int base, stride, w, chan0, chanend;
+};
+__device__ __forceinline__ KBlock key_block(const Coder &cd, int q) {
+    const int s = seg_of_block(cd, q);
+    const int c0 = pick(cd.c0, s), c1 = pick(cd.c0, s + 1), w = pick(cd.bits, s), qq = q - pick(cd.q0, s);
+    KBlock b;
+    b.base = 32 * pick(cd.plane0, s) + 8 * qq * w;
+    b.stride = w * (c1 - c0);
+    b.w = w;
+    b.chan0 = c0 + 8 * qq;
+    b.chanend = c1;
+    return b;
+}
+// Value-record addressing of channel c (channel-major planes): token t's
+// code at bit base + w * t.
+__device__ __forceinline__ int2 value_channel(const Coder &cd, int c) {
+    const int s = seg_of_channel(cd, c);
+    const int w = pick(cd.bits, s);
+    return make_int2(32 * pick(cd.plane0, s) + 32 * w * (c - pick(cd.c0, s)), w);
+}
+// Bit of (token t, channel c) in a record of either layout (0 = K, 1 = V),
+// and the channel's width.
+__device__ __forceinline__ int2 code_bit(const Coder &cd, int layout, int c, int t) {
+    const int s = seg_of_channel(cd, c);
+    const int w = pick(cd.bits, s), c0 = pick(cd.c0, s), n = pick(cd.c0, s + 1) - c0;
+    const int p = 32 * pick(cd.plane0, s);
+    return make_int2(layout == 0 ? p + t * w * n + w * (c - c0) : p + 32 * w * (c - c0) + w * t, w);
+}
+
 // Bump allocator for a workgroup's dynamic LDS (16-byte aligned pieces).
 __host__ __device__ inline int lds_take(int &o, int bytes) {
     const int r = o;
@@ -203,6 +261,28 @@ __device__ __forceinline__ f16x8 dequant8_any(uint32_t X, bool w4, const uint4 &
                  dequant_pair(((U >> wc) & cm) | 0x64006400u, sp.y, zp.y),
                  dequant_pair(((U >> (2 * wc)) & cm) | 0x64006400u, sp.z, zp.z),
                  dequant_pair(((U >> (3 * wc)) & cm) | 0x64006400u, sp.w, zp.w));
+}
+
+// 8 codes of width w (1, 2, 4 or 8) of one token: channel k at bit w * k of
+// the 64-bit window X1:X0 -> dequantised fp16 pairs (channel k, k + 4).
+__device__ __forceinline__ f16x8 dequant8_w(uint32_t X0, uint32_t X1, int w, const uint4 &sp, const uint4 &zp) {
+    constexpr uint32_t magic = 0x64006400u;
+    if (w == 8) {
+        // pair k: byte k of X0 (channel k) and byte k of X1 (channel k + 4)
+        return as_h8(dequant_pair(perm_b32(X1, X0, 0x0C040C00u) | magic, sp.x, zp.x),
+                     dequant_pair(perm_b32(X1, X0, 0x0C050C01u) | magic, sp.y, zp.y),
+                     dequant_pair(perm_b32(X1, X0, 0x0C060C02u) | magic, sp.z, zp.z),
+                     dequant_pair(perm_b32(X1, X0, 0x0C070C03u) | magic, sp.w, zp.w));
+    }
+    if (w == 1) {
+        // channels 4..7 (bits 4..7) up to bits 16..19
+        const uint32_t U = (X0 & 0x0Fu) | ((X0 & 0xF0u) << 12);
+        return as_h8(dequant_pair((U & 0x00010001u) | magic, sp.x, zp.x),
+                     dequant_pair(((U >> 1) & 0x00010001u) | magic, sp.y, zp.y),
+                     dequant_pair(((U >> 2) & 0x00010001u) | magic, sp.z, zp.z),
+                     dequant_pair(((U >> 3) & 0x00010001u) | magic, sp.w, zp.w));
+    }
+    return dequant8_any(X0, w == 4, sp, zp);
 }
 
 }  // namespace

@@ -43,6 +43,54 @@ int n_hi_of(int r, float frac) {
     return static_cast<int>(std::floor(static_cast<double>(frac) * static_cast<double>(r)));
 }
 
+// The latent channels of rank r as (channels, bits) segments: PALU's split,
+// or the bit schedule's equal contiguous groups (the first r % L one larger).
+void split_segments(const palu_config &cfg, int r, std::vector<int> &n, std::vector<int> &bits) {
+    n.clear();
+    bits.clear();
+    if (cfg.schedule_len == 0) {
+        const int nh = n_hi_of(r, cfg.hi_fraction);
+        n = {nh, r - nh};
+        bits = {cfg.hi_bit, cfg.lo_bit};
+        return;
+    }
+    const int L = cfg.schedule_len, base = r / L, extra = r % L;
+    for (int i = 0; i < L; ++i) {
+        n.push_back(base + (i < extra ? 1 : 0));
+        bits.push_back(cfg.bit_schedule[i]);
+    }
+}
+
+// Coder of the coded segments at rank r, and the coded channels' indices.
+Coder coder_for(const palu_config &cfg, int r, std::vector<int> *coded) {
+    std::vector<int> n, bits, cn, cb;
+    split_segments(cfg, r, n, bits);
+    int c = 0;
+    if (coded) coded->clear();
+    for (size_t s = 0; s < n.size(); ++s) {
+        if (n[s] > 0 && bits[s] > 0) {
+            cn.push_back(n[s]);
+            cb.push_back(bits[s]);
+            if (coded)
+                for (int k = 0; k < n[s]; ++k) coded->push_back(c + k);
+        }
+        c += n[s];
+    }
+    return make_coder(cn.data(), cb.data(), static_cast<int>(cn.size()));
+}
+
+bool valid_width(int b) { return b == 1 || b == 2 || b == 4 || b == 8; }
+
+uint32_t fnv1a32(const void *p, size_t n) {
+    const unsigned char *b = static_cast<const unsigned char *>(p);
+    uint32_t h = 0x811C9DC5u;
+    for (size_t i = 0; i < n; ++i) {
+        h ^= b[i];
+        h *= 0x01000193u;
+    }
+    return h;
+}
+
 }  // namespace
 
 struct palu_cache {
@@ -56,20 +104,23 @@ struct palu_cache {
     char *dev = nullptr;
     size_t dev_bytes = 0;
     bool fitted[2] = {false, false};
-    int r[2] = {0, 0}, n_hi[2] = {0, 0};
+    int r[2] = {0, 0};                 // fitted ranks
+    int rc[2] = {0, 0};                // coded (stored) latent channels
+    Coder cd[2]{};
+    std::vector<int> coded[2];         // fitted-basis column of each coded channel
     std::vector<float> basis_h[2], mu_h[2];
     std::vector<double> sigma_h[2];
     std::vector<int> len, sel;
 
     bool quantized(int t) const { return t == 0 || cfg.quantize_values; }
+    // words of one record at fitted rank rr
     int words_for(int t, int rr) const {
-        return quantized(t) ? mixed_record_words(rr, n_hi_of(rr, cfg.hi_fraction))
-                            : fp16_record_words(rr);
+        return quantized(t) ? coder_words(coder_for(cfg, rr, nullptr)) : fp16_record_words(rr);
     }
     TensorDev tensor_dev(int t) const {
         TensorDev d{};
-        d.r = r[t];
-        d.n_hi = quantized(t) ? n_hi[t] : 0;
+        d.r = rc[t];
+        d.cd = cd[t];
         d.words = words_for(t, r[t]);
         d.fp16_latents = quantized(t) ? 0 : 1;
         d.head_stride = (static_cast<int64_t>(max_groups) * d.words + 3) / 4 * 4;
@@ -107,8 +158,19 @@ int validate_config(const palu_config *c) {
         return fail(PALU_ERR_INVALID_ARG, "input_dtype must be 0 (fp16) or 1 (bf16)");
     if (c->head_dim != kHeadDim)
         return fail(PALU_ERR_UNSUPPORTED, "only head_dim = 128 is implemented by the kernels");
-    if (c->hi_bit != 4 || c->lo_bit != 2)
-        return fail(PALU_ERR_UNSUPPORTED, "only hi_bit = 4 and lo_bit = 2 are implemented");
+    if (!valid_width(c->hi_bit) || !valid_width(c->lo_bit))
+        return fail(PALU_ERR_UNSUPPORTED, "hi_bit and lo_bit must be 1, 2, 4 or 8");
+    if (c->schedule_len < 0 || c->schedule_len > 8)
+        return fail(PALU_ERR_INVALID_ARG, "schedule_len must be in [0, 8]");
+    if (c->schedule_len > 0) {
+        bool any = false;
+        for (int i = 0; i < c->schedule_len; ++i) {
+            if (c->bit_schedule[i] != 0 && !valid_width(c->bit_schedule[i]))
+                return fail(PALU_ERR_UNSUPPORTED, "bit_schedule entries must be 0, 1, 2, 4 or 8");
+            any = any || c->bit_schedule[i] > 0;
+        }
+        if (!any) return fail(PALU_ERR_INVALID_ARG, "bit_schedule codes no channel (all entries 0)");
+    }
     if (c->group_size != kTokGroup)
         return fail(PALU_ERR_UNSUPPORTED, "only group_size = 32 is implemented");
     if (c->n_q_heads / c->n_kv_heads > kMaxGqa)
@@ -134,28 +196,42 @@ void reset_seqs(palu_cache *c) {
     std::fill(c->sel.begin(), c->sel.end(), 0);
 }
 
+// Sets tensor t's coder for its fitted rank and uploads the basis of the
+// coded channels (fp32 [G][D][rc], channel-major fp32 [G][rc][D] and the
+// position-ordered fp16 copy) and the mean.  0-bit channels are left out:
+// their latents are zero by definition.
 int upload_basis(palu_cache *c, int t) {
-    const size_t nb = c->basis_h[t].size() * sizeof(float);
-    hipError_t e = hipMemcpy(c->dev + c->off_basis[t], c->basis_h[t].data(), nb, hipMemcpyHostToDevice);
+    const int G = c->G, D = c->D, rr = c->r[t];
+    if (c->quantized(t)) {
+        c->cd[t] = coder_for(c->cfg, rr, &c->coded[t]);
+    } else {
+        c->cd[t] = Coder{};
+        c->coded[t].resize(rr);
+        std::iota(c->coded[t].begin(), c->coded[t].end(), 0);
+    }
+    const int rc = static_cast<int>(c->coded[t].size());
+    if (rc == 0) return fail(PALU_ERR_UNSUPPORTED, "the bit schedule codes no channel at rank " + std::to_string(rr));
+    c->rc[t] = rc;
+    std::vector<float> bk(static_cast<size_t>(G) * D * rc), cm(static_cast<size_t>(G) * rc * D);
+    for (int g = 0; g < G; ++g)
+        for (int d = 0; d < D; ++d)
+            for (int k = 0; k < rc; ++k) {
+                const float v = c->basis_h[t][(static_cast<size_t>(g) * D + d) * rr + c->coded[t][k]];
+                bk[(static_cast<size_t>(g) * D + d) * rc + k] = v;
+                cm[(static_cast<size_t>(g) * rc + k) * D + d] = v;
+            }
+    hipError_t e = hipMemcpy(c->dev + c->off_basis[t], bk.data(), bk.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "basis upload");
     e = hipMemcpy(c->dev + c->off_mu[t], c->mu_h[t].data(), c->mu_h[t].size() * sizeof(float),
                   hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "mean upload");
-    {
-        // channel-major copy [G][r][D]
-        const int G = c->G, D = c->D, rr = c->r[t];
-        std::vector<float> cm(static_cast<size_t>(G) * rr * D);
-        for (int g = 0; g < G; ++g)
-            for (int d = 0; d < D; ++d)
-                for (int k = 0; k < rr; ++k)
-                    cm[(static_cast<size_t>(g) * rr + k) * D + d] = c->basis_h[t][(static_cast<size_t>(g) * D + d) * rr + k];
-        e = hipMemcpy(c->dev + c->off_bcm[t], cm.data(), cm.size() * sizeof(float), hipMemcpyHostToDevice);
-        if (e != hipSuccess) return hip_fail(e, "channel-major basis upload");
+    e = hipMemcpy(c->dev + c->off_bcm[t], cm.data(), cm.size() * sizeof(float), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "channel-major basis upload");
+    if (t == 0) {   // only the key basis is absorbed into queries
+        e = launch_basis_t16(reinterpret_cast<const float *>(c->dev + c->off_basis[t]),
+                             reinterpret_cast<uint16_t *>(c->dev + c->off_bt16[t]), G, rc, c->cd[t], nullptr);
+        if (e != hipSuccess) return hip_fail(e, "basis fp16 copy");
     }
-    e = launch_basis_t16(reinterpret_cast<const float *>(c->dev + c->off_basis[t]),
-                         reinterpret_cast<uint16_t *>(c->dev + c->off_bt16[t]), c->G, c->r[t],
-                         n_hi_of(c->r[t], c->cfg.hi_fraction), nullptr);
-    if (e != hipSuccess) return hip_fail(e, "basis fp16 copy");
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "basis upload synchronize");
     return PALU_OK;
@@ -180,6 +256,8 @@ PALU_API int palu_config_default(palu_config *cfg, int32_t head_dim, int32_t n_k
     cfg->max_rank = 0;
     cfg->split_groups = 0;
     cfg->input_dtype = 0;
+    cfg->schedule_len = 0;
+    for (int i = 0; i < 8; ++i) cfg->bit_schedule[i] = 0;
     return PALU_OK;
 }
 
@@ -216,7 +294,7 @@ PALU_API int palu_cache_create(const palu_config *cfg, int32_t max_batch, int32_
     };
     for (int t = 0; t < 2; ++t) {
         c->off_basis[t] = take(sizeof(float) * c->G * c->D * c->r_max);
-        c->off_bt16[t] = take(sizeof(uint16_t) * c->G * c->D * (c->r_max + 16));   // >= basis_t16_rows
+        c->off_bt16[t] = take(sizeof(uint16_t) * c->G * c->D * (c->r_max + 8 * kMaxSegs));   // >= basis_t16_rows
         c->off_bcm[t] = take(sizeof(float) * c->G * c->D * c->r_max);
         c->off_mu[t] = take(sizeof(float) * c->G * c->D);
         const size_t head_words = (static_cast<size_t>(c->max_groups) * c->words_for(t, c->r_max) + 3) / 4 * 4;
@@ -402,7 +480,6 @@ PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t
             return fail(PALU_ERR_CAPACITY, "fitted rank " + std::to_string(rr) + " exceeds max_rank " +
                                                std::to_string(c->r_max));
         c->r[t] = rr;
-        c->n_hi[t] = n_hi_of(rr, c->cfg.hi_fraction);
         c->basis_h[t].assign(static_cast<size_t>(c->G) * D * rr, 0.0f);
         for (int g = 0; g < c->G; ++g)
             for (int d = 0; d < D; ++d)
@@ -422,7 +499,6 @@ PALU_API int palu_set_basis(palu_cache *c, int32_t tensor, int32_t r, const floa
     if (!basis || !mu) return fail(PALU_ERR_INVALID_ARG, "basis and mu must be non-NULL");
     if (r < 1 || r > c->r_max) return fail(PALU_ERR_INVALID_ARG, "r must be in [1, max_rank]");
     c->r[tensor] = r;
-    c->n_hi[tensor] = n_hi_of(r, c->cfg.hi_fraction);
     c->basis_h[tensor].assign(basis, basis + static_cast<size_t>(c->G) * c->D * r);
     c->mu_h[tensor].assign(mu, mu + static_cast<size_t>(c->G) * c->D);
     c->sigma_h[tensor].assign(static_cast<size_t>(c->G) * c->D, 0.0);
@@ -476,9 +552,7 @@ PALU_API int palu_encode_append(palu_cache *c, const void *k, const void *v, con
         ea.H = c->H;
         ea.T_stride = T_stride;
         ea.hpg = c->hpg;
-        ea.hi_bit = c->cfg.hi_bit;
         ea.bf16 = c->cfg.input_dtype;
-        ea.lo_bit = c->cfg.lo_bit;
         int max_units = 0;   // group pairs touched by a row (one wave each)
         for (int i = 0; i < nb; ++i) {
             const int b = b0 + i;
@@ -586,13 +660,13 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
         }
         // longest rows first in the grid's z order (stable, so equal lengths keep call order)
         std::stable_sort(aa.row, aa.row + nb, [](const AttendRow &x, const AttendRow &y) { return x.len > y.len; });
-        const size_t lds = attend_lds_bytes(c->gqa, aa.k.r, aa.k.n_hi, aa.v.r, aa.k.words, aa.v.words, vq);
+        const size_t lds = attend_lds_bytes(c->gqa, coder_blocks(aa.k.cd), aa.k.r, aa.v.r, aa.k.words, aa.v.words, vq);
         if (lds > kAttendLdsMax)
             return fail(PALU_ERR_UNSUPPORTED, "decode workgroup needs more than 160 KiB of LDS at these ranks");
         aa.chunk = static_cast<int>(chunk);
         aa.nsplit_max = nsplit_max;
         {
-            const int nbk = (aa.k.n_hi + 7) / 8 + (aa.k.r - aa.k.n_hi + 7) / 8;
+            const int nbk = coder_blocks(aa.k.cd);
             volatile float one = 1.0f;   // IEEE fp32 divisions, not folded to other precisions
             aa.inv_rv = one / static_cast<float>(aa.v.r);
             aa.inv_nbk4 = one / static_cast<float>(4 * nbk);
@@ -626,12 +700,12 @@ PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const 
             return fail(PALU_ERR_CAPACITY, "n_q exceeds the tokens stored in slot " + std::to_string(slot));
     }
     const TensorDev kd = c->tensor_dev(0), vd = c->tensor_dev(1);
-    const size_t lds = prefill_lds_bytes(kd.r, kd.n_hi, vd.r, kd.words, vd.words);
+    const size_t lds = prefill_lds_bytes(coder_blocks(kd.cd), kd.r, vd.r, kd.words, vd.words);
     if (lds > kAttendLdsMax)
         return fail(PALU_ERR_UNSUPPORTED, "prefill workgroup needs more than 160 KiB of LDS at these ranks");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(c->D));
-    const int ks = prefill_ks(kd.r, kd.n_hi), nbv = prefill_nbv(vd.r);
+    const int ks = prefill_ks(coder_blocks(kd.cd)), nbv = prefill_nbv(vd.r);
     const int qp = 64 * prefill_nq(ks, nbv) / c->gqa;   // query positions per workgroup
     const size_t row_elems = static_cast<size_t>(c->Hq) * T_stride * c->D;
     for (int b0 = 0; b0 < B; b0 += kMaxCallSeqs) {
@@ -708,8 +782,15 @@ PALU_API int palu_get_stats(const palu_cache *c, palu_stats *st) {
     std::memset(st, 0, sizeof(*st));
     st->r_k = c->r[0];
     st->r_v = c->r[1];
-    st->n_hi_k = c->n_hi[0];
-    st->n_hi_v = c->quantized(1) ? c->n_hi[1] : 0;
+    for (int t = 0; t < 2; ++t) {
+        std::vector<int> n, bits;
+        split_segments(c->cfg, c->r[t], n, bits);
+        const int first = c->quantized(t) ? n[0] : 0;
+        if (t == 0) st->n_hi_k = first;
+        else st->n_hi_v = first;
+    }
+    st->coded_k = c->rc[0];
+    st->coded_v = c->rc[1];
     int64_t tokens = 0, full_groups = 0, tail_tokens = 0, fp16_groups = 0;
     for (int s = 0; s < c->max_batch; ++s) {
         tokens += c->len[s];
@@ -720,15 +801,22 @@ PALU_API int palu_get_stats(const palu_cache *c, palu_stats *st) {
     st->tokens = tokens;
     const double D = c->D;
     for (int t = 0; t < 2; ++t) {
-        const int rr = c->r[t];
-        const int64_t basis_bytes = static_cast<int64_t>(c->G) * c->D * (rr + 1) * 4;
+        const int rr = c->r[t], rc = c->rc[t];
+        const int64_t basis_bytes = static_cast<int64_t>(c->G) * c->D * (rc + 1) * 4;
         int64_t bytes;
         double nominal, realised;
         if (c->quantized(t)) {
-            bytes = c->H * (full_groups * mixed_record_words(rr, c->n_hi[t]) * 4 + tail_tokens * rr * 4) +
-                    basis_bytes;
-            nominal = (rr / D) * (c->cfg.hi_fraction * c->cfg.hi_bit + (1.0 - c->cfg.hi_fraction) * c->cfg.lo_bit);
-            realised = (c->n_hi[t] * c->cfg.hi_bit + (rr - c->n_hi[t]) * c->cfg.lo_bit) / D;
+            bytes = c->H * (full_groups * coder_words(c->cd[t]) * 4 + tail_tokens * rc * 4) + basis_bytes;
+            if (c->cfg.schedule_len > 0) {
+                double mean = 0.0;
+                for (int i = 0; i < c->cfg.schedule_len; ++i) mean += c->cfg.bit_schedule[i];
+                nominal = (rr / D) * (mean / c->cfg.schedule_len);
+            } else {
+                nominal = (rr / D) * (c->cfg.hi_fraction * c->cfg.hi_bit + (1.0 - c->cfg.hi_fraction) * c->cfg.lo_bit);
+            }
+            // the code planes hold sum(channels x bits) words per 32 tokens,
+            // i.e. that many code bits per token
+            realised = static_cast<double>(c->cd[t].meta0) / D;
         } else {
             bytes = c->H * fp16_groups * static_cast<int64_t>(fp16_record_words(rr)) * 4 + basis_bytes;
             nominal = realised = 16.0 * rr / D;
@@ -823,8 +911,8 @@ void seq_header(const palu_cache *c, int len, int32_t f[kSeqHeaderInts]) {
     f[4] = c->G;
     f[5] = c->r[0];
     f[6] = c->r[1];
-    f[7] = c->n_hi[0];
-    f[8] = c->quantized(1) ? c->n_hi[1] : 0;
+    f[7] = static_cast<int32_t>(fnv1a32(&c->cd[0], sizeof(Coder)));
+    f[8] = static_cast<int32_t>(fnv1a32(&c->cd[1], sizeof(Coder)));
     f[9] = c->words_for(0, c->r[0]);
     f[10] = c->words_for(1, c->r[1]);
     f[11] = c->cfg.quantize_values;

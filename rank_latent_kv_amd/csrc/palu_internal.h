@@ -7,6 +7,13 @@
 
 #include <hip/hip_runtime_api.h>
 
+// Helpers used by both the host runtime and the kernels.
+#if defined(__HIP__)
+#define PALU_HD __host__ __device__
+#else
+#define PALU_HD
+#endif
+
 namespace palu {
 
 constexpr int kTokGroup = 32;      // tokens per quantisation group
@@ -16,9 +23,49 @@ constexpr int kMaxSplits = 128;    // token splits per (sequence, kv head)
 constexpr int kMaxGqa = 8;         // query heads per kv head in the attend kernel
 constexpr int kGramRowsPerBlockMin = 512;
 
-// Words of one mixed-bit record: hi plane (4 bits x 32 tokens per channel),
-// lo plane (2 bits x 32 tokens per channel), then one meta word per channel.
-inline int mixed_record_words(int r, int n_hi) { return 4 * n_hi + 2 * (r - n_hi) + r; }
+constexpr int kMaxSegs = 8;        // coded segments of a tensor's latent channels
+
+// The coded latent channels of a tensor as contiguous segments, descending
+// singular value first (0-bit channels are removed before this point):
+// segment s holds channels [c0[s], c0[s+1]) at bits[s] bits (1, 2, 4 or 8);
+// its code plane starts at record word plane0[s] (32 tokens x bits x
+// channels bits long); its channels fill the 8-channel blocks
+// [q0[s], q0[s+1]) of the score-operand position order (each segment's
+// last block padded); one metadata word per channel follows all planes, at
+// meta0 + c.  PALU's split is the two-segment case (hi channels at 4 bits,
+// the rest at 2).
+struct Coder {
+    int nseg;
+    int bits[kMaxSegs];
+    int c0[kMaxSegs + 1];
+    int plane0[kMaxSegs];
+    int q0[kMaxSegs + 1];
+    int meta0;
+};
+
+// Segments (channels, bits) with channels > 0 and bits > 0 -> Coder.
+PALU_HD inline Coder make_coder(const int *seg_n, const int *seg_bits, int nseg) {
+    Coder cd{};
+    int c = 0, w = 0, q = 0;
+    for (int s = 0; s < nseg; ++s) {
+        cd.bits[s] = seg_bits[s];
+        cd.c0[s] = c;
+        cd.plane0[s] = w;
+        cd.q0[s] = q;
+        c += seg_n[s];
+        w += seg_n[s] * seg_bits[s];
+        q += (seg_n[s] + 7) / 8;
+    }
+    cd.nseg = nseg;
+    cd.c0[nseg] = c;
+    cd.q0[nseg] = q;
+    cd.meta0 = w;
+    return cd;
+}
+PALU_HD inline int coder_channels(const Coder &cd) { return cd.c0[cd.nseg]; }
+PALU_HD inline int coder_blocks(const Coder &cd) { return cd.q0[cd.nseg]; }
+// Words of one record: the code planes, then one meta word per channel.
+PALU_HD inline int coder_words(const Coder &cd) { return cd.meta0 + coder_channels(cd); }
 // fp16 latents: r channels x 32 tokens of 2 bytes = 16 r words.
 inline int fp16_record_words(int r) { return 16 * r; }
 
@@ -32,8 +79,9 @@ struct TensorDev {
                          // block; zero rows for padding), P = 8 * blocks (query absorption)
     float *basis_cm;     // [G][r][D] fp32, channel-major copy (output projection)
     float *mu;           // [G][D] fp32
-    int r, n_hi, words;
+    int r, words;        // coded latent channels, words per record
     int fp16_latents;    // V stored as fp16 latents (no tail, no meta)
+    Coder cd;            // segments of the quantised records (unused for fp16 latents)
     int64_t head_stride; // words between consecutive (slot, head): max_groups * words
                          // rounded up to a multiple of 4 (16-byte aligned streams)
 };
@@ -57,7 +105,7 @@ struct GramReduceArgs {
 struct EncodeArgs {
     const uint16_t *x[2];     // K, V fp16 or bf16 [B][H][T_stride][D]
     TensorDev t[2];
-    int B, H, T_stride, hpg, hi_bit, lo_bit;
+    int B, H, T_stride, hpg;
     int bf16;                 // inputs are bf16 (else fp16)
     int slot[kMaxCallSeqs];
     int old_len[kMaxCallSeqs];
@@ -113,16 +161,16 @@ struct PrefillArgs {
 // one of them the all-ones column that yields the softmax denominator) and
 // query tiles per wave (16 columns each) of the prefill kernel variant that
 // serves these ranks.
-int prefill_ks(int r_k, int n_hi_k);
+int prefill_ks(int nbk);             // nbk = key channel blocks (coder_blocks)
 int prefill_nbv(int r_v);
 int prefill_nq(int ks, int nbv);
 // LDS bytes of one prefill workgroup.
-size_t prefill_lds_bytes(int r_k, int n_hi_k, int r_v, int words_k, int words_v);
+size_t prefill_lds_bytes(int nbk, int r_k, int r_v, int words_k, int words_v);
 // Grid (tiles_max, Hkv, B), 256 threads (defined in palu_prefill.hip).
 hipError_t launch_prefill(const PrefillArgs &a, size_t lds_bytes, hipStream_t s);
 
 // LDS bytes of one attend workgroup (independent of the split size).
-size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int words_k, int words_v, bool vq);
+size_t attend_lds_bytes(int gqa, int nbk, int r_k, int r_v, int words_k, int words_v, bool vq);
 
 // Launchers (defined in palu_kernels.hip).  They return the launch status.
 hipError_t launch_gram(const GramArgs &a, hipStream_t s);
@@ -135,10 +183,12 @@ hipError_t launch_append1(const EncodeArgs &a, hipStream_t s);
 // Grid (nsplit_max, Hkv, B): one workgroup per (split, kv head, row).
 hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s);
-// fp16 channel-major copy of a basis: dst[g][c][d] = fp16(src[g][d][c]).
-hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, int n_hi, hipStream_t s);
-// rows of the position-ordered fp16 basis copy for rank r (8 per channel block)
-inline int basis_t16_rows(int r, int n_hi) { return 8 * ((n_hi + 7) / 8 + (r - n_hi + 7) / 8); }
+// Position-ordered fp16 copy of a basis [G][D][r]: dst[g][n][d] =
+// fp16(src[g][d][channel of position n]) for the coder's blocks, 0 where n
+// is padding.
+hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, const Coder &cd, hipStream_t s);
+// rows of the position-ordered fp16 basis copy (8 per channel block)
+PALU_HD inline int basis_t16_rows(const Coder &cd) { return 8 * coder_blocks(cd); }
 
 // Host symmetric eigensolver (palu_eigen.cpp): Householder tridiagonalisation
 // followed by implicit-shift QL.  a: n x n row-major symmetric (destroyed);

@@ -172,7 +172,7 @@ struct EncLane {
 __device__ __forceinline__ void encode_channel(const EncodeArgs &a, const TensorDev &T, const EncLane &e, int c,
                                                float lat, const float *told, float *tnew, uint32_t *rec_lds,
                                                uint16_t *rec16, int layout, bool any_complete) {
-    const int r = T.r, n_hi = T.n_hi, n_lo = r - n_hi;
+    const int r = T.r;
     // fp16 latents have no tail buffer (told and tnew are null): only new
     // positions are stored
     if (T.fp16_latents) {
@@ -188,8 +188,8 @@ __device__ __forceinline__ void encode_channel(const EncodeArgs &a, const Tensor
     // groups use the result
     const float mn = half_min(lat), mx = half_max(lat);
     if (e.complete) {
-        const bool hi = c < n_hi;
-        const float levels = static_cast<float>((1 << (hi ? a.hi_bit : a.lo_bit)) - 1);
+        const int2 bw = code_bit(T.cd, layout, c, e.t);   // bit position, width (c is wave-uniform)
+        const float levels = static_cast<float>((1 << bw.y) - 1);
         const float scale = (mx - mn) / levels;
         int q = 0;
         if (scale > 0.0f) {
@@ -197,14 +197,9 @@ __device__ __forceinline__ void encode_channel(const EncodeArgs &a, const Tensor
             uq = uq < 0.0f ? 0.0f : (uq > levels ? levels : uq);
             q = static_cast<int>(uq);
         }
-        int bit;
-        if (hi) bit = layout == 0 ? e.t * 4 * n_hi + 4 * c : 128 * c + 4 * e.t;
-        else {
-            const int cl = c - n_hi;
-            bit = 128 * n_hi + (layout == 0 ? e.t * 2 * n_lo + 2 * cl : 64 * cl + 2 * e.t);
-        }
-        if (q) atomicOr(rec_lds + (bit >> 5), static_cast<uint32_t>(q) << (bit & 31));
-        if (e.t == 0) rec_lds[4 * n_hi + 2 * n_lo + c] = f2h_bits(scale) | (f2h_bits(mn) << 16);
+        // codes never straddle a word: a code of width w sits at a multiple of w
+        if (q) atomicOr(rec_lds + (bw.x >> 5), static_cast<uint32_t>(q) << (bw.x & 31));
+        if (e.t == 0) rec_lds[T.cd.meta0 + c] = f2h_bits(scale) | (f2h_bits(mn) << 16);
     } else if (e.touched && e.is_new) {
         tnew[e.t * r + c] = lat;
     }
@@ -384,7 +379,7 @@ __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
     const int o = a.old_len[bi], n = a.n_new[bi];
     if (n <= 0) return;                               // whole workgroup
     const TensorDev &T = tz ? a.t[1] : a.t[0];
-    const int r = T.r, n_hi = T.n_hi, n_lo = r - n_hi, W = T.words;
+    const int r = T.r, W = T.words;
     const int grp = h / a.hpg, slot = a.slot[bi];
     const int64_t head_base = static_cast<int64_t>(slot) * a.H + h;
     const int j = o >> 5, t = o & 31;                 // group and position of the new token
@@ -429,8 +424,9 @@ __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
             mn = v < mn ? v : mn;
             mx = v > mx ? v : mx;
         }
-        const bool hi = c < n_hi;
-        const float levels = static_cast<float>((1 << (hi ? a.hi_bit : a.lo_bit)) - 1);
+        const int2 b0 = code_bit(T.cd, tz, c, 0);    // token 0's bit, width
+        const int tstep = tz == 0 ? code_bit(T.cd, 0, c, 1).x - b0.x : b0.y;   // bits between tokens
+        const float levels = static_cast<float>((1 << b0.y) - 1);
         const float scale = (mx - mn) / levels;
         for (int tt = 0; tt < 32; ++tt) {
             const float v = tt == 31 ? lat : told[tt * r + c];
@@ -440,15 +436,10 @@ __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
                 uq = uq < 0.0f ? 0.0f : (uq > levels ? levels : uq);
                 q = static_cast<int>(uq);
             }
-            int bit;
-            if (hi) bit = tz == 0 ? tt * 4 * n_hi + 4 * c : 128 * c + 4 * tt;
-            else {
-                const int cl = c - n_hi;
-                bit = 128 * n_hi + (tz == 0 ? tt * 2 * n_lo + 2 * cl : 64 * cl + 2 * tt);
-            }
+            const int bit = b0.x + tt * tstep;
             if (q) atomicOr(rec + (bit >> 5), static_cast<uint32_t>(q) << (bit & 31));
         }
-        rec[4 * n_hi + 2 * n_lo + c] = f2h_bits(scale) | (f2h_bits(mn) << 16);
+        rec[T.cd.meta0 + c] = f2h_bits(scale) | (f2h_bits(mn) << 16);
     }
     __syncthreads();
     uint32_t *dst = T.records + head_base * T.head_stride + static_cast<int64_t>(j) * W;
@@ -489,7 +480,7 @@ constexpr int kStageBudgetWords = 24 * 1024;   // both record buffers together (
 // LDS layout of one attend workgroup (byte offsets).  Shared by the kernel
 // and the host, which sizes the dynamic LDS from it.
 struct AttendLds {
-    int qt, qt16, kpw, stage, sb;                // sb: words per stage buffer
+    int qt, qt16, kpw, blk, stage, sb;           // sb: words per stage buffer
     int pp;                                      // token groups per pass
     int ts, mst, lst, ost, tp;                   // merge state: byte offsets inside a stage buffer
     int total, nbk, nub;
@@ -497,15 +488,16 @@ struct AttendLds {
 
 
 // Dynamic LDS of one attend workgroup; the same for every split size.
-__host__ __device__ inline AttendLds attend_lds(int g, int rk, int nhk, int rv, int wk, int wv, bool vq) {
+__host__ __device__ inline AttendLds attend_lds(int g, int nbk, int rk, int rv, int wk, int wv, bool vq) {
     AttendLds L;
     const int S = 16 / g, P = kWaves * S;
-    L.nbk = (nhk + 7) / 8 + (rk - nhk + 7) / 8;
+    L.nbk = nbk;
     L.nub = (S * L.nbk + 3) / 4;
     int o = 0;
     L.qt = lds_take(o, g * kHeadDim * 4);
     L.qt16 = lds_take(o, g * 16 * 16);
     L.kpw = lds_take(o, kWaves * S * L.nbk * 8 * 4);
+    L.blk = lds_take(o, L.nbk * 16);             // key block addressing (base, stride, width, channels)
     // two stage buffers.  Each holds one pass of records (+ 16-byte
     // alignment slack); a pass is the 4 S groups the waves take, fewer when
     // that would not fit the budget.  The last split's tail latents go to
@@ -552,8 +544,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     // their scalar loads are issued together (one round trip instead of a
     // chain of dependent ones).
     asm volatile("" ::"s"(a.k.records), "s"(a.v.records), "s"(a.k.tail), "s"(a.v.tail), "s"(a.k.basis_t16),
-                 "s"(a.q), "s"(a.k.head_stride), "s"(a.v.head_stride), "s"(a.k.r), "s"(a.k.n_hi), "s"(a.k.words),
-                 "s"(a.v.r), "s"(a.v.n_hi), "s"(a.v.words), "s"(a.v.fp16_latents), "s"(a.chunk), "s"(a.hpg),
+                 "s"(a.q), "s"(a.k.head_stride), "s"(a.v.head_stride), "s"(a.k.r), "s"(a.k.cd.meta0), "s"(a.k.words),
+                 "s"(a.v.r), "s"(a.v.cd.meta0), "s"(a.v.words), "s"(a.v.fp16_latents), "s"(a.chunk), "s"(a.hpg),
                  "s"(a.Hq), "s"(a.Hkv), "s"(a.qscale), "s"(rw.slot), "s"(rw.len), "s"(rw.qi), "s"(rw.sel_ns));
     const int ns = rw.sel_ns >> 1, qi = rw.qi;
     if (s >= ns) return;                          // whole workgroup: no barrier reached
@@ -564,13 +556,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     const int ntg = je > jb ? je - jb : 0;
     const bool do_tail = (s == ns - 1) && ntail > 0;
     const int grp = h / a.hpg;
-    const int rk = a.k.r, nhk = a.k.n_hi, nlk = rk - nhk;
-    const int nbh = (nhk + 7) >> 3;
-    const int rv = a.v.r, nhv = a.v.n_hi;
+    const int rk = a.k.r;
+    const int rv = a.v.r;
     const int WK = a.k.words, WV = a.v.words;
-    const int kmeta = 4 * nhk + 2 * nlk, vmeta = 4 * nhv + 2 * (rv - nhv);
+    const int kmeta = a.k.cd.meta0, vmeta = a.v.cd.meta0;
 
-    const AttendLds L = attend_lds(g, rk, nhk, rv, WK, WV, vq);
+    const AttendLds L = attend_lds(g, coder_blocks(a.k.cd), rk, rv, WK, WV, vq);
     const int nbk = L.nbk, nub = L.nub, npair = S * nbk;
     const int PP = L.pp;                          // groups per pass (<= P)
     const int npass = (ntg + PP - 1) / PP;
@@ -684,8 +675,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                                                                 acc, 0, 0, 0);
                 const int n = 16 * (wv + kWaves * x) + ln;
                 const int q = n >> 3, idx = n & 7;
-                const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
-                const int chanend = q < nbh ? nhk : rk;
+                const KBlock kbq = key_block(a.k.cd, q < nbk ? q : nbk - 1);
+                const int chan0 = kbq.chan0, chanend = kbq.chanend;
                 const int c = chan0 + (idx >> 1) + 4 * (idx & 1);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -699,6 +690,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             }
         }
     }
+    // ---- 3. key block addressing table (one entry per 8-channel block)
+    int4 *blk = reinterpret_cast<int4 *>(lds + L.blk);
+    if (tid < nbk) {
+        const KBlock b = key_block(a.k.cd, tid);
+        blk[tid] = make_int4(b.base, b.stride, b.w, b.chan0 | (b.chanend << 16));
+    }
     __builtin_amdgcn_s_waitcnt(0);                    // this wave's copies have landed
     __syncthreads();
 
@@ -711,7 +708,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NBV; ++nb) oacc[nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
     // per-lane value-channel addressing (column c = 16 nb + ln, clamped)
-    int vch[NBV], vw0[NBV], vw1[NBV], vs0[NBV], vwid[NBV], vwc[NBV];
+    int vch[NBV], vw0[NBV], vw1[NBV], vs0[NBV], vs1[NBV], vwid[NBV], vwc[NBV];
     uint32_t vcm[NBV];
     int row_slot[4];                                 // slot of value-output row 4*kb + v
 #pragma unroll
@@ -720,17 +717,18 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     for (int nb = 0; nb < NBV; ++nb) {
         int c = 16 * nb + ln;
         c = c < rv ? c : rv - 1;
-        const bool w4c = c < nhv;
-        const int wc = w4c ? 4 : 2;
-        const int bitbase = w4c ? 128 * c : 128 * nhv + 64 * (c - nhv);
-        const int b0 = bitbase + 4 * kb * wc, b1 = b0 + 16 * wc;
+        const int2 vc = VQ ? value_channel(a.v.cd, c) : make_int2(0, 2);   // base bit, width
+        const int wc = vc.y;
+        const int b0 = vc.x + 4 * kb * wc, b1 = b0 + 16 * wc;
         vch[nb] = c;
         vw0[nb] = b0 >> 5;
         vw1[nb] = b1 >> 5;
-        vs0[nb] = b0 & 31;          // b1 - b0 = 16 wc is a multiple of 32 bits
-        vwid[nb] = 4 * wc;
+        vs0[nb] = b0 & 31;
+        vs1[nb] = b1 & 31;          // differs from vs0 only for 1-bit codes (b1 - b0 = 16 wc)
+        vwid[nb] = 4 * wc;          // 4 tokens; width 8 takes whole words instead
         vwc[nb] = wc;
-        vcm[nb] = w4c ? 0x000F000Fu : 0x00030003u;
+        const uint32_t m = (1u << wc) - 1u;
+        vcm[nb] = m | (m << 16);
     }
     const uint32_t kmagic = vgpr_const(0x64006400u), km4 = vgpr_const(0x000F000Fu),
                    km2 = vgpr_const(0x00030003u);
@@ -751,8 +749,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         for (int e = lane; e < S * nbk * 4; e += 64) {
             const int m = div_nbk4.quo(e), r2 = e - m * nbk * 4;
             const int q = r2 >> 2, k = r2 & 3;
-            const int chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
-            const int chanend = q < nbh ? nhk : rk;
+            const int cc = blk[q].w;
+            const int chan0 = cc & 0xFFFF, chanend = cc >> 16;
             int tg = tb0 + m;
             tg = tg < npg ? tg : npg - 1;
             const uint32_t *rec = stage + koff + tg * WK + kmeta;
@@ -789,24 +787,26 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             const bool ok = p < npair && live_n && j == slot_n;
             const uint4 bq = ok ? qt16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
             const f16x8 bop = as_h8(bq.x, bq.y, bq.z, bq.w);
-            const bool w4 = qc < nbh;
-            const int base = w4 ? 32 * qc : 128 * nhk + 16 * (qc - nbh);
-            const int stride = w4 ? 4 * nhk : 2 * nlk;
-            const int bit0 = base + ln * stride, bit1 = bit0 + 16 * stride;
+            const int4 bq4 = blk[qc];                    // base, stride, width
+            const int wq = bq4.z;
+            const int bit0 = bq4.x + ln * bq4.y, bit1 = bit0 + 16 * bq4.y;
             const uint32_t X0 = __builtin_amdgcn_alignbit(rec[(bit0 >> 5) + 1], rec[bit0 >> 5], bit0 & 31);
             const uint32_t X1 = __builtin_amdgcn_alignbit(rec[(bit1 >> 5) + 1], rec[bit1 >> 5], bit1 & 31);
             f16x8 a0, a1;
-            if constexpr (S % 4 == 0) {
-                if (w4) {
-                    a0 = dequant8<true>(X0, sp, zp, km4, kmagic);
-                    a1 = dequant8<true>(X1, sp, zp, km4, kmagic);
-                } else {
-                    a0 = dequant8<false>(X0, sp, zp, km2, kmagic);
-                    a1 = dequant8<false>(X1, sp, zp, km2, kmagic);
-                }
+            if (S % 4 == 0 && wq == 4) {                 // wave-uniform fast paths (PALU's widths)
+                a0 = dequant8<true>(X0, sp, zp, km4, kmagic);
+                a1 = dequant8<true>(X1, sp, zp, km4, kmagic);
+            } else if (S % 4 == 0 && wq == 2) {
+                a0 = dequant8<false>(X0, sp, zp, km2, kmagic);
+                a1 = dequant8<false>(X1, sp, zp, km2, kmagic);
             } else {
-                a0 = dequant8_any(X0, w4, sp, zp);
-                a1 = dequant8_any(X1, w4, sp, zp);
+                // 8-bit blocks span 64 bits: the second word of each window
+                const uint32_t Y0 = wq == 8 ? __builtin_amdgcn_alignbit(rec[(bit0 >> 5) + 2], rec[(bit0 >> 5) + 1],
+                                                                       bit0 & 31) : 0u;
+                const uint32_t Y1 = wq == 8 ? __builtin_amdgcn_alignbit(rec[(bit1 >> 5) + 2], rec[(bit1 >> 5) + 1],
+                                                                       bit1 & 31) : 0u;
+                a0 = dequant8_w(X0, Y0, wq, sp, zp);
+                a1 = dequant8_w(X1, Y1, wq, sp, zp);
             }
             sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bop, sacc0, 0, 0, 0);
             sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bop, sacc1, 0, 0, 0);
@@ -884,13 +884,22 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                 uint32_t bp0, bp1, bp2, bp3;
                 if constexpr (VQ) {
                     const uint32_t *rec = stage + voff + (tb0 + m) * WV;
-                    const uint32_t X = __builtin_amdgcn_ubfe(rec[vw0[nb]], vs0[nb], vwid[nb]) |
-                                       (__builtin_amdgcn_ubfe(rec[vw1[nb]], vs0[nb], vwid[nb]) << 16);
+                    const uint32_t L0 = rec[vw0[nb]], L1 = rec[vw1[nb]];
                     const int wc = vwc[nb];
-                    bp0 = (X & vcm[nb]) | kmagic;
-                    bp1 = ((X >> wc) & vcm[nb]) | kmagic;
-                    bp2 = ((X >> (2 * wc)) & vcm[nb]) | kmagic;
-                    bp3 = ((X >> (3 * wc)) & vcm[nb]) | kmagic;
+                    if (wc == 8) {
+                        // tokens 4 kb + k (word L0, byte k) and 16 + 4 kb + k (L1)
+                        bp0 = perm_b32(L1, L0, 0x0C040C00u) | kmagic;
+                        bp1 = perm_b32(L1, L0, 0x0C050C01u) | kmagic;
+                        bp2 = perm_b32(L1, L0, 0x0C060C02u) | kmagic;
+                        bp3 = perm_b32(L1, L0, 0x0C070C03u) | kmagic;
+                    } else {
+                        const uint32_t X = __builtin_amdgcn_ubfe(L0, vs0[nb], vwid[nb]) |
+                                           (__builtin_amdgcn_ubfe(L1, vs1[nb], vwid[nb]) << 16);
+                        bp0 = (X & vcm[nb]) | kmagic;
+                        bp1 = ((X >> wc) & vcm[nb]) | kmagic;
+                        bp2 = ((X >> (2 * wc)) & vcm[nb]) | kmagic;
+                        bp3 = ((X >> (3 * wc)) & vcm[nb]) | kmagic;
+                    }
                 } else {
                     uint2 lo, hi;
                     if constexpr (kPreV) {
@@ -1131,16 +1140,16 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
 // dst[g][n][d] = fp16(V[g][d][chan(n)]) for the score-operand position n
 // (block q = n / 8 of 8 channels, hi blocks first; slot idx = n % 8 holds
 // channel (idx >> 1) + 4 (idx & 1) of the block), 0 where n is padding.
-__global__ __launch_bounds__(256) void basis_t16_kernel(const float *src, uint16_t *dst, int G, int r, int n_hi) {
-    const int nbh = (n_hi + 7) >> 3, rows = 8 * (nbh + ((r - n_hi + 7) >> 3));
+__global__ __launch_bounds__(256) void basis_t16_kernel(const float *src, uint16_t *dst, int G, int r, Coder cd) {
+    const int rows = 8 * cd.q0[cd.nseg];
     const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (e >= static_cast<int64_t>(G) * rows * kHeadDim) return;
     const int d = static_cast<int>(e % kHeadDim);
     const int64_t gn = e / kHeadDim;
     const int n = static_cast<int>(gn % rows), g = static_cast<int>(gn / rows);
     const int q = n >> 3, idx = n & 7;
-    const int chan0 = q < nbh ? 8 * q : n_hi + 8 * (q - nbh);
-    const int chanend = q < nbh ? n_hi : r;
+    const KBlock kbq = key_block(cd, q);
+    const int chan0 = kbq.chan0, chanend = kbq.chanend;
     const int c = chan0 + (idx >> 1) + 4 * (idx & 1);
     dst[e] = c < chanend ? static_cast<uint16_t>(f2h_bits(src[(static_cast<int64_t>(g) * kHeadDim + d) * r + c]))
                          : static_cast<uint16_t>(0);
@@ -1199,8 +1208,8 @@ hipError_t launch_encode(const EncodeArgs &a, int max_units, hipStream_t s) {
     return a.bf16 ? launch_encode_t<true>(a, max_units, s) : launch_encode_t<false>(a, max_units, s);
 }
 
-size_t attend_lds_bytes(int gqa, int r_k, int n_hi_k, int r_v, int words_k, int words_v, bool vq) {
-    return static_cast<size_t>(attend_lds(gqa, r_k, n_hi_k, r_v, words_k, words_v, vq).total);
+size_t attend_lds_bytes(int gqa, int nbk, int r_k, int r_v, int words_k, int words_v, bool vq) {
+    return static_cast<size_t>(attend_lds(gqa, nbk, r_k, r_v, words_k, words_v, vq).total);
 }
 
 template <int G, int NBV, bool VQ>
@@ -1244,10 +1253,10 @@ hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
     }
 }
 
-hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, int n_hi, hipStream_t s) {
-    const int64_t n = static_cast<int64_t>(G) * basis_t16_rows(r, n_hi) * kHeadDim;
+hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, const Coder &cd, hipStream_t s) {
+    const int64_t n = static_cast<int64_t>(G) * basis_t16_rows(cd) * kHeadDim;
     hipLaunchKernelGGL(basis_t16_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, src, dst, G, r,
-                       n_hi);
+                       cd);
     return hipGetLastError();
 }
 

@@ -56,11 +56,12 @@ struct PrefillLds {
     int raw, raw_words;    // two raw record buffers (K record, then V record)
     int tiles, ktile, vtile;   // two (key tile, value tile) pairs; bytes of each tile
     int basis;             // epilogue: fp32 value basis [D][r_V] + mean [D] (aliases the above)
+    int tab;               // key block table (int4 per block) + value channel table (int2 per channel)
     int olat;              // per wave [16 NQ][16 NBV] fp32 normalised latent outputs
     int total;
 };
 
-__host__ __device__ inline PrefillLds prefill_lds(int ks, int nbv, int nq, int wk, int wv, int rv) {
+__host__ __device__ inline PrefillLds prefill_lds(int ks, int nbv, int nq, int wk, int wv, int rv, int nbk) {
     PrefillLds L;
     L.raw_words = ((wk + 3) & ~3) + 4 + ((wv + 3) & ~3) + 4;
     L.ktile = 32 * pf_krow(ks) * 2;
@@ -72,6 +73,7 @@ __host__ __device__ inline PrefillLds prefill_lds(int ks, int nbv, int nq, int w
     L.basis = lds_take(b, (kHeadDim * rv + kHeadDim) * 4);
     int o = a > b ? a : b;
     L.olat = lds_take(o, kPfWaves * 16 * nq * 16 * nbv * 4);
+    L.tab = lds_take(o, nbk * 16 + rv * 8);
     L.total = o;
     return L;
 }
@@ -104,13 +106,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int g = a.gqa, len = rw.len;
     const int nfull = len >> 5, ntail = len & 31;
     const int grp = h / a.hpg;
-    const int rk = a.k.r, nhk = a.k.n_hi, nlk = rk - nhk, nbh = (nhk + 7) >> 3;
-    const int nbk = nbh + ((nlk + 7) >> 3), np = 8 * nbk;
-    const int rv = a.v.r, nhv = a.v.n_hi;
+    const int rk = a.k.r;
+    const int nbk = coder_blocks(a.k.cd), np = 8 * nbk;
+    const int rv = a.v.r;
     const int WK = a.k.words, WV = a.v.words;
     const bool vq = !a.v.fp16_latents;
-    const int kmeta = 4 * nhk + 2 * nlk, vmeta = 4 * nhv + 2 * (rv - nhv);
-    const PrefillLds L = prefill_lds(KS, NBV, NQ, WK, WV, rv);
+    const int kmeta = a.k.cd.meta0, vmeta = a.v.cd.meta0;
+    const PrefillLds L = prefill_lds(KS, NBV, NQ, WK, WV, rv, nbk);
+    int4 *ktab = reinterpret_cast<int4 *>(lds + L.tab);          // base, stride, width, chan0 | chanend << 16
+    int2 *vtab = reinterpret_cast<int2 *>(lds + L.tab + nbk * 16);   // base bit, width
     constexpr int krow = 32 * KS + 8;
 
     // ---- query columns: index qi -> position len - nq + qi; columns past
@@ -180,13 +184,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 const int e = 64 * r + lane;
                 if (e >= 32 * nbk) continue;
                 const int q = e >> 5, t = e & 31;
-                const bool w4 = q < nbh;
-                const int chan0 = w4 ? 8 * q : nhk + 8 * (q - nbh), chanend = w4 ? nhk : rk;
+                const int4 kq = ktab[q];
+                const int chan0 = kq.w & 0xFFFF, chanend = kq.w >> 16;
                 uint4 val;
                 if (full) {
-                    const int base = w4 ? 32 * q : 128 * nhk + 16 * (q - nbh);
-                    const int bit = base + t * (w4 ? 4 * nhk : 2 * nlk);
+                    const int bit = kq.x + t * kq.y;
                     const uint32_t X = __builtin_amdgcn_alignbit(kr[(bit >> 5) + 1], kr[bit >> 5], bit & 31);
+                    const uint32_t Y = kq.z == 8 ? __builtin_amdgcn_alignbit(kr[(bit >> 5) + 2], kr[(bit >> 5) + 1],
+                                                                             bit & 31)
+                                                 : 0u;
                     uint32_t sp[4], zp[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
@@ -195,8 +201,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                         sp[k] = perm_b32(wb, wa, 0x05040100u);
                         zp[k] = perm_b32(wb, wa, 0x07060302u);
                     }
-                    val = __builtin_bit_cast(uint4, dequant8_any(X, w4, make_uint4(sp[0], sp[1], sp[2], sp[3]),
-                                                                 make_uint4(zp[0], zp[1], zp[2], zp[3])));
+                    val = __builtin_bit_cast(uint4, dequant8_w(X, Y, kq.z, make_uint4(sp[0], sp[1], sp[2], sp[3]),
+                                                               make_uint4(zp[0], zp[1], zp[2], zp[3])));
                 } else {
                     // incomplete group: fp32 tail rounded to fp16, 0 past ntail
                     uint32_t wd[4] = {0u, 0u, 0u, 0u};
@@ -218,18 +224,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 const int c = e >> 2, tb = e & 3;
                 uint4 val;
                 if (full && vq) {
-                    const bool w4 = c < nhv;
-                    const int wc = w4 ? 4 : 2;
-                    const int bit = (w4 ? 128 * c : 128 * nhv + 64 * (c - nhv)) + 8 * tb * wc;
-                    const uint32_t X = __builtin_amdgcn_alignbit(vr[(bit >> 5) + 1], vr[bit >> 5], bit & 31);
+                    const int2 vcw = vtab[c];
+                    const int wc = vcw.y;
+                    const int bit = vcw.x + 8 * tb * wc;
                     const uint32_t mw = vr[vmeta + c];
                     const uint32_t spair = (mw & 0xFFFFu) | (mw << 16), zpair = (mw >> 16) | (mw & 0xFFFF0000u);
-                    const uint32_t m = w4 ? 0xFu : 0x3u;
                     uint32_t wd[4];
+                    if (wc == 8) {
+                        // 8 tokens = 2 whole words; token u is byte u of the pair
+                        const uint32_t Xa = vr[bit >> 5], Xb = vr[(bit >> 5) + 1];
+                        wd[0] = dequant_pair(perm_b32(Xb, Xa, 0x0C010C00u) | 0x64006400u, spair, zpair);
+                        wd[1] = dequant_pair(perm_b32(Xb, Xa, 0x0C030C02u) | 0x64006400u, spair, zpair);
+                        wd[2] = dequant_pair(perm_b32(Xb, Xa, 0x0C050C04u) | 0x64006400u, spair, zpair);
+                        wd[3] = dequant_pair(perm_b32(Xb, Xa, 0x0C070C06u) | 0x64006400u, spair, zpair);
+                    } else {
+                        const uint32_t X = __builtin_amdgcn_alignbit(vr[(bit >> 5) + 1], vr[bit >> 5], bit & 31);
+                        const uint32_t m = (1u << wc) - 1u;
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t lo = (X >> (2 * k * wc)) & m, hi = (X >> ((2 * k + 1) * wc)) & m;
-                        wd[k] = dequant_pair(lo | (hi << 16) | 0x64006400u, spair, zpair);
+                        for (int k = 0; k < 4; ++k) {
+                            const uint32_t lo = (X >> (2 * k * wc)) & m, hi = (X >> ((2 * k + 1) * wc)) & m;
+                            wd[k] = dequant_pair(lo | (hi << 16) | 0x64006400u, spair, zpair);
+                        }
                     }
                     val = make_uint4(wd[0], wd[1], wd[2], wd[3]);
                 } else if (full) {
@@ -268,6 +283,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         *reinterpret_cast<uint4 *>(lds + L.tiles + bf * (L.ktile + L.vtile) + L.ktile + (c * kVRow + 8 * tb) * 2) =
             make_uint4(w, w, w, w);
     }
+
+    // ---- record addressing tables (per key block, per value channel)
+    if (tid < nbk) {
+        const KBlock b = key_block(a.k.cd, tid);
+        ktab[tid] = make_int4(b.base, b.stride, b.w, b.chan0 | (b.chanend << 16));
+    }
+    if (vq && tid < rv) vtab[tid] = value_channel(a.v.cd, tid);
 
     // ---- prologue: records of groups 0 and 1 in flight while the query is
     //      absorbed: qt = qs V_K^T q on MFMA, A = position-ordered key basis
@@ -497,8 +519,8 @@ hipError_t launch_prefill_v(const PrefillArgs &a, size_t lds_bytes, hipStream_t 
 
 }  // namespace
 
-int prefill_ks(int r_k, int n_hi_k) {
-    const int np = basis_t16_rows(r_k, n_hi_k);
+int prefill_ks(int nbk) {
+    const int np = 8 * nbk;
     const int ks = (np + 31) / 32;
     return ks <= 1 ? 1 : (ks <= 2 ? 2 : 4);
 }
@@ -510,13 +532,14 @@ int prefill_nbv(int r_v) {
 
 int prefill_nq(int ks, int nbv) { return prefill_nq_c(ks, nbv); }
 
-size_t prefill_lds_bytes(int r_k, int n_hi_k, int r_v, int words_k, int words_v) {
-    const int ks = prefill_ks(r_k, n_hi_k), nbv = prefill_nbv(r_v);
-    return static_cast<size_t>(prefill_lds(ks, nbv, prefill_nq(ks, nbv), words_k, words_v, r_v).total);
+size_t prefill_lds_bytes(int nbk, int r_k, int r_v, int words_k, int words_v) {
+    (void)r_k;
+    const int ks = prefill_ks(nbk), nbv = prefill_nbv(r_v);
+    return static_cast<size_t>(prefill_lds(ks, nbv, prefill_nq(ks, nbv), words_k, words_v, r_v, nbk).total);
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
-    switch (prefill_ks(a.k.r, a.k.n_hi)) {
+    switch (prefill_ks(coder_blocks(a.k.cd))) {
         case 1: return launch_prefill_v<1>(a, lds_bytes, s);
         case 2: return launch_prefill_v<2>(a, lds_bytes, s);
         case 4: return launch_prefill_v<4>(a, lds_bytes, s);

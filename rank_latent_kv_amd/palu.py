@@ -43,7 +43,8 @@ class palu_config(ctypes.Structure):
                 ("hi_bit", ctypes.c_int32), ("lo_bit", ctypes.c_int32),
                 ("hi_fraction", ctypes.c_float), ("group_size", ctypes.c_int32),
                 ("quantize_values", ctypes.c_int32), ("max_rank", ctypes.c_int32),
-                ("split_groups", ctypes.c_int32), ("input_dtype", ctypes.c_int32)]
+                ("split_groups", ctypes.c_int32), ("input_dtype", ctypes.c_int32),
+                ("schedule_len", ctypes.c_int32), ("bit_schedule", ctypes.c_int32 * 8)]
 
 
 class palu_stats(ctypes.Structure):
@@ -53,7 +54,8 @@ class palu_stats(ctypes.Structure):
                 ("fp16_key_bytes", ctypes.c_int64), ("fp16_value_bytes", ctypes.c_int64),
                 ("nominal_bits_k", ctypes.c_double), ("nominal_bits_v", ctypes.c_double),
                 ("realised_bits_k", ctypes.c_double), ("realised_bits_v", ctypes.c_double),
-                ("assigned_avg_bits", ctypes.c_double)]
+                ("assigned_avg_bits", ctypes.c_double), ("coded_k", ctypes.c_int32),
+                ("coded_v", ctypes.c_int32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -255,7 +257,7 @@ class LatentKVCache:
                  max_batch: int, max_seq_len: int, rank: int = 0, energy_threshold: float = 0.90,
                  hi_bit: int = 4, lo_bit: int = 2, hi_fraction: float = 0.25,
                  group_size: int = 32, quantize_values: bool = True, max_rank: int = 0,
-                 split_groups: int = 0, input_dtype: str = "fp16", device=None):
+                 split_groups: int = 0, input_dtype: str = "fp16", bit_schedule=None, device=None):
         import torch
         self.torch = torch
         cfg = palu_config_default(head_dim, n_kv_heads, n_q_heads)
@@ -270,6 +272,13 @@ class LatentKVCache:
         if input_dtype not in ("fp16", "bf16"):
             raise ValueError("input_dtype must be 'fp16' or 'bf16'")
         cfg.input_dtype = 1 if input_dtype == "bf16" else 0
+        if bit_schedule is not None:
+            sched = [int(b) for b in bit_schedule]
+            if not 1 <= len(sched) <= 8:
+                raise ValueError("bit_schedule needs 1 to 8 entries")
+            cfg.schedule_len = len(sched)
+            for i, b in enumerate(sched):
+                cfg.bit_schedule[i] = b
         self.cfg = cfg
         self.D, self.H, self.Hq, self.G = head_dim, n_kv_heads, n_q_heads, n_head_groups
         self.max_batch, self.max_seq_len = max_batch, max_seq_len
@@ -350,7 +359,8 @@ class LatentKVCache:
         """(records uint32 [n, words], tail fp32 [len % 32, r]) of one
         (slot, kv head, tensor); fp16 value latents come back as uint32
         words holding two halves each."""
-        r, _, _, _ = self.get_basis(tensor)
+        st = self.stats()
+        r = st["coded_k"] if tensor == 0 else st["coded_v"]
         words = palu_record_words(self.handle, tensor)
         n = self.seq_len(seq)
         fp16 = tensor == 1 and not self.cfg.quantize_values

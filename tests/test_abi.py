@@ -55,7 +55,9 @@ def test_config_defaults_follow_usage_section():
     (dict(input_dtype=2), 1),
     (dict(head_dim=96), 2),              # kernels built for D = 128
     (dict(hi_bit=3), 2),
-    (dict(lo_bit=1), 2),
+    (dict(lo_bit=5), 2),
+    (dict(schedule_len=9), 1),
+    (dict(schedule_len=-1), 1),
     (dict(group_size=64), 2),
     (dict(n_q_heads=8 * 16), 2),         # more than 8 query heads per kv head
 ])
@@ -64,6 +66,28 @@ def test_create_rejects_bad_config(kw, code):
         palu.palu_cache_create(_cfg(**kw), 4, 1024)
     assert ei.value.code == code
     assert palu.palu_last_error()
+
+
+@pytest.mark.parametrize("sched,code", [((8, 4, 3), 2), ((0, 0), 1), ((0, 16), 2)])
+def test_create_rejects_bad_schedule(sched, code):
+    cfg = _cfg(schedule_len=len(sched))
+    for i, b in enumerate(sched):
+        cfg.bit_schedule[i] = b
+    with pytest.raises(palu.PaluError) as ei:
+        palu.palu_cache_create(cfg, 4, 1024)
+    assert ei.value.code == code
+
+
+def test_create_accepts_schedules_and_widths():
+    for kw in (dict(hi_bit=8, lo_bit=1), dict(hi_bit=1, lo_bit=8)):
+        h = palu.palu_cache_create(_cfg(**kw), 2, 64)
+        palu.lib().palu_cache_destroy(h)
+    cfg = _cfg(schedule_len=8)
+    for i, b in enumerate((8, 4, 2, 1, 1, 0, 0, 0)):
+        cfg.bit_schedule[i] = b
+    h = palu.palu_cache_create(cfg, 2, 64)
+    assert palu.palu_cache_required_bytes(h) > 0
+    palu.lib().palu_cache_destroy(h)
 
 
 def test_create_rejects_bad_sizes():
