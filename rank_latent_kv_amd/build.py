@@ -44,19 +44,22 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
+    """Compiles every source (in parallel) and links libpalu.so."""
+    from concurrent.futures import ThreadPoolExecutor
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    jobs = []
     for src in DEVICE_SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        _run([HIPCC, *COMMON, *DEVICE, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj],
-             verbose)
-        objs.append(obj)
+        jobs.append(([HIPCC, *COMMON, *DEVICE, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj],
+                     obj))
     for src in HOST_SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        _run([HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c",
-              os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append(([HIPCC, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-c",
+                      os.path.join(CSRC, src), "-o", obj], obj))
+    with ThreadPoolExecutor(max_workers=min(4, len(jobs))) as pool:
+        list(pool.map(lambda j: _run(j[0], verbose), jobs))
+    objs = [obj for _, obj in jobs]
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

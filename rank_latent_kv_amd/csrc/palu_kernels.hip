@@ -524,11 +524,14 @@ __host__ __device__ inline AttendLds attend_lds(int g, int nbk, int rk, int rv, 
 
 
 // Workgroup = (call row i, kv head h, split s); see the section comment.
+// GEN = false serves PALU-shaped layouts (a 4-bit segment, then 2-bit
+// channels) with closed-form record addressing; GEN = true any coder, through
+// a per-block address table in LDS.
 // G = query heads per kv head, NBV = value-channel blocks of 16.  A split is
 // processed in passes of up to 4 S token groups (S per wave); the records of
 // pass p + 1 are copied global -> LDS (direct 16-byte loads into LDS, no
 // registers) into the other of two buffers while pass p is computed.
-template <int G, int NBV, bool VQ>
+template <int G, int NBV, bool VQ, bool GEN>
 __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     constexpr int g = G, S = 16 / G, NS = S * G;
     constexpr bool vq = VQ;                      // V stored as mixed-bit codes
@@ -560,6 +563,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     const int rv = a.v.r;
     const int WK = a.k.words, WV = a.v.words;
     const int kmeta = a.k.cd.meta0, vmeta = a.v.cd.meta0;
+    // PALU-shaped layouts: nhk 4-bit channels, then 2-bit ones
+    const int nhk = a.k.cd.bits[0] == 4 ? a.k.cd.c0[1] : 0, nlk = rk - nhk, nbh = (nhk + 7) >> 3;
+    const int nhv = a.v.cd.bits[0] == 4 ? a.v.cd.c0[1] : 0;
 
     const AttendLds L = attend_lds(g, coder_blocks(a.k.cd), rk, rv, WK, WV, vq);
     const int nbk = L.nbk, nub = L.nub, npair = S * nbk;
@@ -692,7 +698,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     }
     // ---- 3. key block addressing table (one entry per 8-channel block)
     int4 *blk = reinterpret_cast<int4 *>(lds + L.blk);
-    if (tid < nbk) {
+    if (GEN && tid < nbk) {
         const KBlock b = key_block(a.k.cd, tid);
         blk[tid] = make_int4(b.base, b.stride, b.w, b.chan0 | (b.chanend << 16));
     }
@@ -717,7 +723,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     for (int nb = 0; nb < NBV; ++nb) {
         int c = 16 * nb + ln;
         c = c < rv ? c : rv - 1;
-        const int2 vc = VQ ? value_channel(a.v.cd, c) : make_int2(0, 2);   // base bit, width
+        int2 vc = make_int2(0, 2);                   // base bit, width
+        if constexpr (VQ && GEN) vc = value_channel(a.v.cd, c);
+        else if constexpr (VQ) vc = c < nhv ? make_int2(128 * c, 4) : make_int2(128 * nhv + 64 * (c - nhv), 2);
         const int wc = vc.y;
         const int b0 = vc.x + 4 * kb * wc, b1 = b0 + 16 * wc;
         vch[nb] = c;
@@ -749,8 +757,15 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         for (int e = lane; e < S * nbk * 4; e += 64) {
             const int m = div_nbk4.quo(e), r2 = e - m * nbk * 4;
             const int q = r2 >> 2, k = r2 & 3;
-            const int cc = blk[q].w;
-            const int chan0 = cc & 0xFFFF, chanend = cc >> 16;
+            int chan0, chanend;
+            if constexpr (GEN) {
+                const int cc = blk[q].w;
+                chan0 = cc & 0xFFFF;
+                chanend = cc >> 16;
+            } else {
+                chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
+                chanend = q < nbh ? nhk : rk;
+            }
             int tg = tb0 + m;
             tg = tg < npg ? tg : npg - 1;
             const uint32_t *rec = stage + koff + tg * WK + kmeta;
@@ -787,19 +802,32 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             const bool ok = p < npair && live_n && j == slot_n;
             const uint4 bq = ok ? qt16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
             const f16x8 bop = as_h8(bq.x, bq.y, bq.z, bq.w);
-            const int4 bq4 = blk[qc];                    // base, stride, width
-            const int wq = bq4.z;
-            const int bit0 = bq4.x + ln * bq4.y, bit1 = bit0 + 16 * bq4.y;
-            const uint32_t X0 = __builtin_amdgcn_alignbit(rec[(bit0 >> 5) + 1], rec[bit0 >> 5], bit0 & 31);
-            const uint32_t X1 = __builtin_amdgcn_alignbit(rec[(bit1 >> 5) + 1], rec[bit1 >> 5], bit1 & 31);
             f16x8 a0, a1;
-            if (S % 4 == 0 && wq == 4) {                 // wave-uniform fast paths (PALU's widths)
-                a0 = dequant8<true>(X0, sp, zp, km4, kmagic);
-                a1 = dequant8<true>(X1, sp, zp, km4, kmagic);
-            } else if (S % 4 == 0 && wq == 2) {
-                a0 = dequant8<false>(X0, sp, zp, km2, kmagic);
-                a1 = dequant8<false>(X1, sp, zp, km2, kmagic);
+            if constexpr (!GEN) {
+                const bool w4 = qc < nbh;
+                const int base = w4 ? 32 * qc : 128 * nhk + 16 * (qc - nbh);
+                const int stride = w4 ? 4 * nhk : 2 * nlk;
+                const int bit0 = base + ln * stride, bit1 = bit0 + 16 * stride;
+                const uint32_t X0 = __builtin_amdgcn_alignbit(rec[(bit0 >> 5) + 1], rec[bit0 >> 5], bit0 & 31);
+                const uint32_t X1 = __builtin_amdgcn_alignbit(rec[(bit1 >> 5) + 1], rec[bit1 >> 5], bit1 & 31);
+                if constexpr (S % 4 == 0) {
+                    if (w4) {
+                        a0 = dequant8<true>(X0, sp, zp, km4, kmagic);
+                        a1 = dequant8<true>(X1, sp, zp, km4, kmagic);
+                    } else {
+                        a0 = dequant8<false>(X0, sp, zp, km2, kmagic);
+                        a1 = dequant8<false>(X1, sp, zp, km2, kmagic);
+                    }
+                } else {
+                    a0 = dequant8_any(X0, w4, sp, zp);
+                    a1 = dequant8_any(X1, w4, sp, zp);
+                }
             } else {
+                const int4 bq4 = blk[qc];                // base, stride, width
+                const int wq = bq4.z;
+                const int bit0 = bq4.x + ln * bq4.y, bit1 = bit0 + 16 * bq4.y;
+                const uint32_t X0 = __builtin_amdgcn_alignbit(rec[(bit0 >> 5) + 1], rec[bit0 >> 5], bit0 & 31);
+                const uint32_t X1 = __builtin_amdgcn_alignbit(rec[(bit1 >> 5) + 1], rec[bit1 >> 5], bit1 & 31);
                 // 8-bit blocks span 64 bits: the second word of each window
                 const uint32_t Y0 = wq == 8 ? __builtin_amdgcn_alignbit(rec[(bit0 >> 5) + 2], rec[(bit0 >> 5) + 1],
                                                                        bit0 & 31) : 0u;
@@ -886,7 +914,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                     const uint32_t *rec = stage + voff + (tb0 + m) * WV;
                     const uint32_t L0 = rec[vw0[nb]], L1 = rec[vw1[nb]];
                     const int wc = vwc[nb];
-                    if (wc == 8) {
+                    if (GEN && wc == 8) {
                         // tokens 4 kb + k (word L0, byte k) and 16 + 4 kb + k (L1)
                         bp0 = perm_b32(L1, L0, 0x0C040C00u) | kmagic;
                         bp1 = perm_b32(L1, L0, 0x0C050C01u) | kmagic;
@@ -894,7 +922,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                         bp3 = perm_b32(L1, L0, 0x0C070C03u) | kmagic;
                     } else {
                         const uint32_t X = __builtin_amdgcn_ubfe(L0, vs0[nb], vwid[nb]) |
-                                           (__builtin_amdgcn_ubfe(L1, vs1[nb], vwid[nb]) << 16);
+                                           (__builtin_amdgcn_ubfe(L1, GEN ? vs1[nb] : vs0[nb], vwid[nb]) << 16);
                         bp0 = (X & vcm[nb]) | kmagic;
                         bp1 = ((X >> wc) & vcm[nb]) | kmagic;
                         bp2 = ((X >> (2 * wc)) & vcm[nb]) | kmagic;
@@ -1212,17 +1240,29 @@ size_t attend_lds_bytes(int gqa, int nbk, int r_k, int r_v, int words_k, int wor
     return static_cast<size_t>(attend_lds(gqa, nbk, r_k, r_v, words_k, words_v, vq).total);
 }
 
-template <int G, int NBV, bool VQ>
-static hipError_t launch_attend_t(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+template <int G, int NBV, bool VQ, bool GEN>
+static hipError_t launch_attend_tg(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
     static bool configured = false;
     if (!configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<G, NBV, VQ>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<G, NBV, VQ, GEN>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((attend_kernel<G, NBV, VQ>), dim3(a.nsplit_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
+    hipLaunchKernelGGL((attend_kernel<G, NBV, VQ, GEN>), dim3(a.nsplit_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
     return hipGetLastError();
+}
+
+// A PALU-shaped coder: one 4-bit or 2-bit segment, or 4-bit then 2-bit.
+static bool palu_shaped(const Coder &cd) {
+    if (cd.nseg == 1) return cd.bits[0] == 4 || cd.bits[0] == 2;
+    return cd.nseg == 2 && cd.bits[0] == 4 && cd.bits[1] == 2;
+}
+
+template <int G, int NBV, bool VQ>
+static hipError_t launch_attend_t(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+    const bool gen = !palu_shaped(a.k.cd) || (VQ && !palu_shaped(a.v.cd));
+    return gen ? launch_attend_tg<G, NBV, VQ, true>(a, lds_bytes, s) : launch_attend_tg<G, NBV, VQ, false>(a, lds_bytes, s);
 }
 
 template <int G, bool VQ>

@@ -91,8 +91,11 @@ __device__ __forceinline__ f16x8 pair_operand(const uint2 &lo, const uint2 &hi) 
                  perm_b32(hi.y, lo.y, 0x05040100u), perm_b32(hi.y, lo.y, 0x07060302u));
 }
 
-template <int KS, int NBV, int NQ>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+// GEN = false: PALU-shaped layouts (a 4-bit segment, then 2-bit channels),
+// closed-form record addressing; GEN = true: any coder, through LDS tables.
+template <int KS, int NBV, int NQ, bool GEN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KS + NBV <= 2 ? 4 : 1)))
+void prefill_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -115,6 +118,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const PrefillLds L = prefill_lds(KS, NBV, NQ, WK, WV, rv, nbk);
     int4 *ktab = reinterpret_cast<int4 *>(lds + L.tab);          // base, stride, width, chan0 | chanend << 16
     int2 *vtab = reinterpret_cast<int2 *>(lds + L.tab + nbk * 16);   // base bit, width
+    // PALU-shaped layouts: nhk (nhv) 4-bit channels, then 2-bit ones
+    const int nhk = a.k.cd.bits[0] == 4 ? a.k.cd.c0[1] : 0, nlk = rk - nhk, nbh = (nhk + 7) >> 3;
+    const int nhv = a.v.cd.bits[0] == 4 ? a.v.cd.c0[1] : 0;
     constexpr int krow = 32 * KS + 8;
 
     // ---- query columns: index qi -> position len - nq + qi; columns past
@@ -184,15 +190,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 const int e = 64 * r + lane;
                 if (e >= 32 * nbk) continue;
                 const int q = e >> 5, t = e & 31;
-                const int4 kq = ktab[q];
+                int4 kq;                                  // base, stride, width, channels
+                if constexpr (GEN) {
+                    kq = ktab[q];
+                } else {
+                    const bool w4 = q < nbh;
+                    kq = make_int4(w4 ? 32 * q : 128 * nhk + 16 * (q - nbh), w4 ? 4 * nhk : 2 * nlk, w4 ? 4 : 2,
+                                   (w4 ? 8 * q : nhk + 8 * (q - nbh)) | ((w4 ? nhk : rk) << 16));
+                }
                 const int chan0 = kq.w & 0xFFFF, chanend = kq.w >> 16;
                 uint4 val;
                 if (full) {
                     const int bit = kq.x + t * kq.y;
                     const uint32_t X = __builtin_amdgcn_alignbit(kr[(bit >> 5) + 1], kr[bit >> 5], bit & 31);
-                    const uint32_t Y = kq.z == 8 ? __builtin_amdgcn_alignbit(kr[(bit >> 5) + 2], kr[(bit >> 5) + 1],
-                                                                             bit & 31)
-                                                 : 0u;
+                    const uint32_t Y = GEN && kq.z == 8 ? __builtin_amdgcn_alignbit(kr[(bit >> 5) + 2],
+                                                                                   kr[(bit >> 5) + 1], bit & 31)
+                                                        : 0u;
                     uint32_t sp[4], zp[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
@@ -201,8 +214,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                         sp[k] = perm_b32(wb, wa, 0x05040100u);
                         zp[k] = perm_b32(wb, wa, 0x07060302u);
                     }
-                    val = __builtin_bit_cast(uint4, dequant8_w(X, Y, kq.z, make_uint4(sp[0], sp[1], sp[2], sp[3]),
-                                                               make_uint4(zp[0], zp[1], zp[2], zp[3])));
+                    const uint4 spv = make_uint4(sp[0], sp[1], sp[2], sp[3]), zpv = make_uint4(zp[0], zp[1], zp[2], zp[3]);
+                    val = __builtin_bit_cast(uint4, GEN ? dequant8_w(X, Y, kq.z, spv, zpv)
+                                                        : dequant8_any(X, kq.z == 4, spv, zpv));
                 } else {
                     // incomplete group: fp32 tail rounded to fp16, 0 past ntail
                     uint32_t wd[4] = {0u, 0u, 0u, 0u};
@@ -224,13 +238,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 const int c = e >> 2, tb = e & 3;
                 uint4 val;
                 if (full && vq) {
-                    const int2 vcw = vtab[c];
+                    const int2 vcw = GEN ? vtab[c]
+                                         : (c < nhv ? make_int2(128 * c, 4) : make_int2(128 * nhv + 64 * (c - nhv), 2));
                     const int wc = vcw.y;
                     const int bit = vcw.x + 8 * tb * wc;
                     const uint32_t mw = vr[vmeta + c];
                     const uint32_t spair = (mw & 0xFFFFu) | (mw << 16), zpair = (mw >> 16) | (mw & 0xFFFF0000u);
                     uint32_t wd[4];
-                    if (wc == 8) {
+                    if (GEN && wc == 8) {
                         // 8 tokens = 2 whole words; token u is byte u of the pair
                         const uint32_t Xa = vr[bit >> 5], Xb = vr[(bit >> 5) + 1];
                         wd[0] = dequant_pair(perm_b32(Xb, Xa, 0x0C010C00u) | 0x64006400u, spair, zpair);
@@ -285,11 +300,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- record addressing tables (per key block, per value channel)
-    if (tid < nbk) {
+    if (GEN && tid < nbk) {
         const KBlock b = key_block(a.k.cd, tid);
         ktab[tid] = make_int4(b.base, b.stride, b.w, b.chan0 | (b.chanend << 16));
     }
-    if (vq && tid < rv) vtab[tid] = value_channel(a.v.cd, tid);
+    if (GEN && vq && tid < rv) vtab[tid] = value_channel(a.v.cd, tid);
 
     // ---- prologue: records of groups 0 and 1 in flight while the query is
     //      absorbed: qt = qs V_K^T q on MFMA, A = position-ordered key basis
@@ -491,18 +506,30 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int KS, int NBV>
-hipError_t launch_prefill_t(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
+template <int KS, int NBV, bool GEN>
+hipError_t launch_prefill_tg(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
     constexpr int NQ = prefill_nq_c(KS, NBV);
     static bool configured = false;
     if (!configured) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<KS, NBV, NQ>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<KS, NBV, NQ, GEN>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((prefill_kernel<KS, NBV, NQ>), dim3(a.tiles_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
+    hipLaunchKernelGGL((prefill_kernel<KS, NBV, NQ, GEN>), dim3(a.tiles_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
     return hipGetLastError();
+}
+
+// A PALU-shaped coder: one 4-bit or 2-bit segment, or 4-bit then 2-bit.
+bool palu_shaped_pf(const Coder &cd) {
+    if (cd.nseg == 1) return cd.bits[0] == 4 || cd.bits[0] == 2;
+    return cd.nseg == 2 && cd.bits[0] == 4 && cd.bits[1] == 2;
+}
+
+template <int KS, int NBV>
+hipError_t launch_prefill_t(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
+    const bool gen = !palu_shaped_pf(a.k.cd) || (!a.v.fp16_latents && !palu_shaped_pf(a.v.cd));
+    return gen ? launch_prefill_tg<KS, NBV, true>(a, lds_bytes, s) : launch_prefill_tg<KS, NBV, false>(a, lds_bytes, s);
 }
 
 template <int KS>
