@@ -46,13 +46,11 @@ PREFILL_OPS_PER_PAIR = 2.5
 METRIC = "latent decode-attend tok/s + HBM GB/s (% of peak); encode Mtok/s"
 
 
-def attend_bytes(lens, H, Hq, D, G, rk, nhk, rv, nhv, vq):
+def attend_bytes(lens, H, Hq, D, G, wk, rk, wv, rv, vq):
     """Algorithmic bytes of one decode-attend call over sequences of lengths
-    `lens`: complete-group records (codes + fp16 scale/zero words), fp32 tail
-    latents, fp16 value latents of valid tokens, K/V bases and means, query
-    in and output out."""
-    wk = 4 * nhk + 2 * (rk - nhk) + rk
-    wv = 4 * nhv + 2 * (rv - nhv) + rv
+    `lens`: complete-group records (wk / wv words: codes + fp16 scale/zero
+    words), fp32 tail latents of the rk / rv coded channels, fp16 value
+    latents of valid tokens, K/V bases and means, query in and output out."""
     tot = 0
     for n in lens:
         nf, nt = n // 32, n % 32
@@ -102,6 +100,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="long_b4_s32768_e90")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--input-dtype", choices=("fp16", "bf16"), default="fp16",
+                    help="element type of K, V and q (the workload's values, rounded to it)")
+    ap.add_argument("--bit-schedule", default="",
+                    help="comma-separated bit schedule (e.g. 8,4,2,1,1,0,0,0); default: PALU's 25%%/75%% 4/2-bit split")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -118,6 +120,14 @@ def main():
     from rank_latent_kv_amd.palu import LatentKVCache
 
     w = synth.WORKLOADS[args.workload]
+    bf16 = args.input_dtype == "bf16"
+    schedule = [int(b) for b in args.bit_schedule.split(",")] if args.bit_schedule else None
+    tdt = torch.bfloat16 if bf16 else torch.float16
+
+    def to_dev(a):
+        """host input (fp16 values, or bf16 bit patterns) -> device tensor of the input type"""
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if bf16 else np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if bf16 else t).to(dev)
     lens = synth.prefill_lengths(w)
     S = int(lens.max())
     T = w.steps
@@ -127,31 +137,33 @@ def main():
     # ---- inputs, generated on the host and made resident in HBM
     t0 = time.time()
     gpk, gpv = synth.group_params(w, 0), synth.group_params(w, 1)
-    kpre = torch.zeros((w.batch, w.n_kv_heads, S, w.head_dim), dtype=torch.float16, device=dev)
+    kpre = torch.zeros((w.batch, w.n_kv_heads, S, w.head_dim), dtype=tdt, device=dev)
     vpre = torch.zeros_like(kpre)
-    kdec = torch.empty((T, w.batch, w.n_kv_heads, 1, w.head_dim), dtype=torch.float16, device=dev)
+    kdec = torch.empty((T, w.batch, w.n_kv_heads, 1, w.head_dim), dtype=tdt, device=dev)
     vdec = torch.empty_like(kdec)
     host_k0 = host_v0 = None
     for b in range(w.batch):
-        kb = synth.kv_sequence(w, 0, b, int(lens[b]) + T, gpk)
-        vb = synth.kv_sequence(w, 1, b, int(lens[b]) + T, gpv)
-        kpre[b, :, :lens[b]] = torch.from_numpy(kb[:, :lens[b]]).to(dev)
-        vpre[b, :, :lens[b]] = torch.from_numpy(vb[:, :lens[b]]).to(dev)
-        kdec[:, b, :, 0] = torch.from_numpy(np.ascontiguousarray(kb[:, lens[b]:].transpose(1, 0, 2))).to(dev)
-        vdec[:, b, :, 0] = torch.from_numpy(np.ascontiguousarray(vb[:, lens[b]:].transpose(1, 0, 2))).to(dev)
+        kb = synth.kv_sequence(w, 0, b, int(lens[b]) + T, gpk, bf16)
+        vb = synth.kv_sequence(w, 1, b, int(lens[b]) + T, gpv, bf16)
+        kpre[b, :, :lens[b]] = to_dev(kb[:, :lens[b]])
+        vpre[b, :, :lens[b]] = to_dev(vb[:, :lens[b]])
+        kdec[:, b, :, 0] = to_dev(kb[:, lens[b]:].transpose(1, 0, 2))
+        vdec[:, b, :, 0] = to_dev(vb[:, lens[b]:].transpose(1, 0, 2))
         if b == 0:
             host_k0, host_v0 = kb, vb
-    q_all = torch.from_numpy(np.stack([synth.queries(w, b, T) for b in range(w.batch)], axis=1)).to(dev)
+    q_host = np.stack([synth.queries(w, b, T, bf16) for b in range(w.batch)], axis=1)
+    q_all = to_dev(q_host)
     # prefill queries: one per prompt position and query head
-    qpre = torch.zeros((w.batch, w.n_q_heads, S, w.head_dim), dtype=torch.float16, device=dev)
+    qpre = torch.zeros((w.batch, w.n_q_heads, S, w.head_dim), dtype=tdt, device=dev)
     for b in range(w.batch):
-        qpre[b, :, :lens[b]] = torch.from_numpy(synth.prefill_queries(w, b, int(lens[b]))).to(dev)
+        qpre[b, :, :lens[b]] = to_dev(synth.prefill_queries(w, b, int(lens[b]), bf16))
     gen_s = time.time() - t0
 
     cache = LatentKVCache(w.head_dim, w.n_kv_heads, w.n_q_heads, w.n_head_groups, w.batch,
                           S + T, rank=w.rank or 0, energy_threshold=w.energy,
-                          quantize_values=w.quantize_values)
-    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+                          quantize_values=w.quantize_values, input_dtype=args.input_dtype,
+                          bit_schedule=schedule)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=tdt, device=dev)
     out_pre = torch.empty_like(qpre)
     stream = torch.cuda.current_stream(dev)
 
@@ -203,8 +215,10 @@ def main():
 
     st = cache.stats()
     rk, rv, nhk, nhv = st["r_k"], st["r_v"], st["n_hi_k"], st["n_hi_v"]
+    from rank_latent_kv_amd.palu import palu_record_words
+    wk, wv = palu_record_words(cache.handle, 0), palu_record_words(cache.handle, 1)
     per_call_bytes = [attend_bytes([int(n) + t + 1 for n in lens], w.n_kv_heads, w.n_q_heads,
-                                   w.head_dim, w.n_head_groups, rk, nhk, rv, nhv,
+                                   w.head_dim, w.n_head_groups, wk, st["coded_k"], wv, st["coded_v"],
                                    w.quantize_values) for t in range(T)]
     mean_bytes = float(np.mean(per_call_bytes))
     att_mean_ms = float(np.mean(att_ms))
@@ -219,7 +233,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, cache, host_k0, host_v0, lens, q_all[0, 0].cpu().numpy())
+        cpu = cpu_baseline(w, cache, host_k0, host_v0, lens, q_host[0, 0], bf16, schedule)
 
     line = {
         "metric": METRIC,
@@ -237,10 +251,12 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "prefill": S, "decode_steps": T,
                    "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "head_groups": w.n_head_groups,
-                   "rank_k": rk, "rank_v": rv, "quantize_values": w.quantize_values},
+                   "rank_k": rk, "rank_v": rv, "quantize_values": w.quantize_values,
+                   "input_dtype": args.input_dtype,
+                   "bit_schedule": schedule if schedule else "palu 25% x 4 bit + 75% x 2 bit"},
         "roofline": {"bound": "hbm", "kernel": "palu_decode_attend (attend + combine)",
                      "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
+                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name) if not (bf16 or schedule) else None,
                      "bytes_per_launch": int(mean_bytes), "launch_us": round(att_mean_ms * 1e3, 2)},
         "decode_attend_us": round(att_mean_ms * 1e3, 2),
         "append_us": round(float(np.mean(app_ms)) * 1e3, 2),
@@ -259,7 +275,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, cache, k0, v0, lens, q0, budget_s=10.0):
+def cpu_baseline(w, cache, k0, v0, lens, q0, bf16=False, schedule=None, budget_s=10.0):
     """The oracle's decode attention (dequantise the stored records,
     reconstruct K/V in fp64, softmax per query head) for the first decode step
     of sequence 0 with the GPU's basis, repeated until about `budget_s`
@@ -272,11 +288,11 @@ def cpu_baseline(w, cache, k0, v0, lens, q0, budget_s=10.0):
         full[:, :, :r] = basis
         fits.append(oracle.Fit(r, np.full(w.n_head_groups, r, np.int32), full, mu, sigma))
     layer = oracle.OracleLayer(w.head_dim, w.n_q_heads, w.n_kv_heads, w.n_head_groups, *fits,
-                               quantize_values=w.quantize_values)
+                               quantize_values=w.quantize_values, bf16=bf16, schedule=schedule)
     n = int(lens[0]) + 1
     ks = [layer.encode_head(k0[h, :n], h, 0) for h in range(w.n_kv_heads)]
     vs = [layer.encode_head(v0[h, :n], h, 1) for h in range(w.n_kv_heads)]
-    q = np.ascontiguousarray(q0, dtype=np.float16)
+    q = np.ascontiguousarray(q0)
     runs, t0 = 0, time.perf_counter()
     while runs < 3 or time.perf_counter() - t0 < budget_s:
         layer.attend(ks, vs, q)
