@@ -46,17 +46,18 @@ PREFILL_OPS_PER_PAIR = 2.5
 METRIC = "latent decode-attend tok/s + HBM GB/s (% of peak); encode Mtok/s"
 
 
-def attend_bytes(lens, H, Hq, D, G, wk, rk, wv, rv, vq):
+def attend_bytes(lens, H, Hq, D, G, wk, rk, wv, rv, vq, basis_sets=1):
     """Algorithmic bytes of one decode-attend call over sequences of lengths
     `lens`: complete-group records (wk / wv words: codes + fp16 scale/zero
     words), fp32 tail latents of the rk / rv coded channels, fp16 value
-    latents of valid tokens, K/V bases and means, query in and output out."""
+    latents of valid tokens, K/V bases and means (one set, or one per
+    sequence), query in and output out."""
     tot = 0
     for n in lens:
         nf, nt = n // 32, n % 32
         tot += H * (nf * wk * 4 + nt * rk * 4)
         tot += H * ((nf * wv * 4 + nt * rv * 4) if vq else n * rv * 2)
-    tot += G * D * (rk + 1) * 4 + G * D * (rv + 1) * 4
+    tot += basis_sets * (G * D * (rk + 1) * 4 + G * D * (rv + 1) * 4)
     tot += len(lens) * Hq * D * 2 * 2
     return tot
 
@@ -104,6 +105,9 @@ def main():
                     help="element type of K, V and q (the workload's values, rounded to it)")
     ap.add_argument("--bit-schedule", default="",
                     help="comma-separated bit schedule (e.g. 8,4,2,1,1,0,0,0); default: PALU's 25%%/75%% 4/2-bit split")
+    ap.add_argument("--per-seq-rank", type=int, default=0,
+                    help="per-sequence bases (each prompt fitted alone) at this explicit rank; "
+                         "default: one basis per head group shared by the batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -160,9 +164,9 @@ def main():
     gen_s = time.time() - t0
 
     cache = LatentKVCache(w.head_dim, w.n_kv_heads, w.n_q_heads, w.n_head_groups, w.batch,
-                          S + T, rank=w.rank or 0, energy_threshold=w.energy,
+                          S + T, rank=args.per_seq_rank or w.rank or 0, energy_threshold=w.energy,
                           quantize_values=w.quantize_values, input_dtype=args.input_dtype,
-                          bit_schedule=schedule)
+                          bit_schedule=schedule, per_seq_basis=args.per_seq_rank > 0)
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=tdt, device=dev)
     out_pre = torch.empty_like(qpre)
     stream = torch.cuda.current_stream(dev)
@@ -219,7 +223,7 @@ def main():
     wk, wv = palu_record_words(cache.handle, 0), palu_record_words(cache.handle, 1)
     per_call_bytes = [attend_bytes([int(n) + t + 1 for n in lens], w.n_kv_heads, w.n_q_heads,
                                    w.head_dim, w.n_head_groups, wk, st["coded_k"], wv, st["coded_v"],
-                                   w.quantize_values) for t in range(T)]
+                                   w.quantize_values, w.batch if args.per_seq_rank else 1) for t in range(T)]
     mean_bytes = float(np.mean(per_call_bytes))
     att_mean_ms = float(np.mean(att_ms))
     decode_tok_s = w.batch * len(att_ms) / (sum(att_ms) / 1e3)
@@ -233,7 +237,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, cache, host_k0, host_v0, lens, q_host[0, 0], bf16, schedule)
+        cpu = cpu_baseline(w, cache, host_k0, host_v0, lens, q_host[0, 0], bf16, schedule,
+                           seq=0 if args.per_seq_rank else None)
 
     line = {
         "metric": METRIC,
@@ -253,10 +258,11 @@ def main():
                    "head_dim": w.head_dim, "head_groups": w.n_head_groups,
                    "rank_k": rk, "rank_v": rv, "quantize_values": w.quantize_values,
                    "input_dtype": args.input_dtype,
-                   "bit_schedule": schedule if schedule else "palu 25% x 4 bit + 75% x 2 bit"},
+                   "bit_schedule": schedule if schedule else "palu 25% x 4 bit + 75% x 2 bit",
+                   "bases": "per sequence" if args.per_seq_rank else "shared per head group"},
         "roofline": {"bound": "hbm", "kernel": "palu_decode_attend (attend + combine)",
                      "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name) if not (bf16 or schedule) else None,
+                     "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name) if not (bf16 or schedule or args.per_seq_rank) else None,
                      "bytes_per_launch": int(mean_bytes), "launch_us": round(att_mean_ms * 1e3, 2)},
         "decode_attend_us": round(att_mean_ms * 1e3, 2),
         "append_us": round(float(np.mean(app_ms)) * 1e3, 2),
@@ -275,7 +281,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, cache, k0, v0, lens, q0, bf16=False, schedule=None, budget_s=10.0):
+def cpu_baseline(w, cache, k0, v0, lens, q0, bf16=False, schedule=None, seq=None, budget_s=10.0):
     """The oracle's decode attention (dequantise the stored records,
     reconstruct K/V in fp64, softmax per query head) for the first decode step
     of sequence 0 with the GPU's basis, repeated until about `budget_s`
@@ -283,7 +289,7 @@ def cpu_baseline(w, cache, k0, v0, lens, q0, bf16=False, schedule=None, budget_s
     import oracle
     fits = []
     for t in (0, 1):
-        r, basis, mu, sigma = cache.get_basis(t)
+        r, basis, mu, sigma = cache.get_basis(t, seq=seq)
         full = np.zeros((w.n_head_groups, w.head_dim, w.head_dim), np.float32)
         full[:, :, :r] = basis
         fits.append(oracle.Fit(r, np.full(w.n_head_groups, r, np.int32), full, mu, sigma))

@@ -89,6 +89,13 @@ typedef struct palu_config {
                                   quantize_values is 1.                          */
     int32_t bit_schedule[8];   /* bits per group: 0, 1, 2, 4 or 8; at least one
                                   nonzero among the first schedule_len           */
+    int32_t per_seq_basis;     /* 0: one basis per (tensor, head group), fitted
+                                  over every sequence given to palu_fit and
+                                  shared by all slots.  1: every slot has its own
+                                  bases, fitted from its own prompt (palu_fit /
+                                  palu_fit_seq) or installed with
+                                  palu_set_basis_seq; needs an explicit rank (all
+                                  slots share one record layout).                 */
 } palu_config;
 
 /* Fills the page's defaults (rank 0 = energy rule, threshold 0.90, G = 4,
@@ -145,6 +152,25 @@ int palu_set_basis(palu_cache *cache, int32_t tensor, int32_t r,
  * may each be NULL.  Errors: INVALID_ARG, NOT_FITTED. */
 int palu_get_basis(const palu_cache *cache, int32_t tensor, int32_t *r,
                    float *basis, float *mu, double *sigma);
+
+/* Per-sequence bases (per_seq_basis = 1): fits row b of k / v
+ * ([B][H][S_stride][D], seq_lens[b] valid tokens, > 0) into the bases of
+ * slot seq_ids[b] (distinct), with the cache's explicit rank, and empties
+ * those slots; other slots keep their bases and tokens.  palu_fit in this
+ * mode fits row b into slot b for every row.  Synchronous.
+ * Errors: INVALID_ARG (not in per-sequence mode, bad sizes, repeated slot),
+ * CAPACITY (slot out of range), NOT_BOUND, HIP. */
+int palu_fit_seq(palu_cache *cache, const void *k, const void *v,
+                 const int32_t *seq_ids, const int32_t *seq_lens, int32_t B,
+                 int32_t S_stride, void *stream);
+
+/* Per-sequence bases: installs (set) or copies out (get) one slot's basis
+ * for tensor 0 (K) or 1 (V), in the layout of palu_set_basis /
+ * palu_get_basis; r must equal the cache's rank.  set empties the slot. */
+int palu_set_basis_seq(palu_cache *cache, int32_t seq, int32_t tensor, int32_t r,
+                       const float *basis, const float *mu);
+int palu_get_basis_seq(const palu_cache *cache, int32_t seq, int32_t tensor, int32_t *r,
+                       float *basis, float *mu, double *sigma);
 
 /* Appends tokens (PALU page, "How it works", decode steps 1-2): projects
  * each new key/value into its group's basis with a fixed-order fp32 chain,
@@ -265,8 +291,11 @@ int palu_record_words(const palu_cache *cache, int32_t tensor, int32_t *words);
  * head_dim, n_kv_heads, n_head_groups, r_K, r_V, coder_K, coder_V (32-bit
  * FNV-1a hashes of each tensor's segment layout), words_K, words_V,
  * quantize_values, len, uint64 FNV-1a hash of the fp32 bases and means of
- * both tensors, 4 zero bytes.  The basis itself is not included
- * (palu_get_basis / palu_set_basis move it).
+ * both tensors, uint32 flags.  With shared bases (flags 0) the basis is not
+ * included (palu_get_basis / palu_set_basis move it) and must match the
+ * cache's.  With per-sequence bases (flags 1) the slot's bases follow the
+ * header (K basis [G][D][r_K], K mean [G][D], V basis, V mean, fp32) and
+ * an import installs them into the target slot.
  *
  * palu_export_bytes: bytes of the serialized slot.  palu_export_seq:
  * synchronous (waits for the device), writes exactly that many bytes to

@@ -103,16 +103,27 @@ struct palu_cache {
     size_t off_gram_part = 0, off_gram_out = 0, off_seg = 0, off_attend = 0, total = 0;
     char *dev = nullptr;
     size_t dev_bytes = 0;
-    bool fitted[2] = {false, false};
+    // basis sets: one per slot with per-sequence bases (the rank, and so
+    // the record layout, fixed at creation), else one shared by all slots
+    bool per_seq = false;
+    int nbs = 1;
+    int64_t sb_basis = 0, sb_bt16 = 0, sb_bcm = 0, sb_mu = 0;   // device elements per set
+    std::vector<char> ready[2];        // set s of tensor t installed
     int r[2] = {0, 0};                 // fitted ranks
     int rc[2] = {0, 0};                // coded (stored) latent channels
     Coder cd[2]{};
     std::vector<int> coded[2];         // fitted-basis column of each coded channel
-    std::vector<float> basis_h[2], mu_h[2];
-    std::vector<double> sigma_h[2];
+    std::vector<float> basis_h[2], mu_h[2];   // nbs sets of [G][D][r] and [G][D]
+    std::vector<double> sigma_h[2];           // nbs sets of [G][D]
     std::vector<int> len, sel;
 
     bool quantized(int t) const { return t == 0 || cfg.quantize_values; }
+    int bset(int slot) const { return per_seq ? slot : 0; }
+    bool slot_ready(int slot) const { return ready[0][bset(slot)] && ready[1][bset(slot)]; }
+    // rank and record layout of tensor t are known
+    bool layout_known(int t) const { return per_seq || ready[t][0]; }
+    size_t basis_elems(int t) const { return static_cast<size_t>(G) * D * r[t]; }
+    size_t mu_elems() const { return static_cast<size_t>(G) * D; }
     // words of one record at fitted rank rr
     int words_for(int t, int rr) const {
         return quantized(t) ? coder_words(coder_for(cfg, rr, nullptr)) : fp16_record_words(rr);
@@ -130,6 +141,12 @@ struct palu_cache {
         d.basis_t16 = reinterpret_cast<uint16_t *>(dev + off_bt16[t]);
         d.basis_cm = reinterpret_cast<float *>(dev + off_bcm[t]);
         d.mu = reinterpret_cast<float *>(dev + off_mu[t]);
+        if (per_seq) {
+            d.set_basis = sb_basis;
+            d.set_bt16 = sb_bt16;
+            d.set_bcm = sb_bcm;
+            d.set_mu = sb_mu;
+        }
         return d;
     }
 };
@@ -175,6 +192,10 @@ int validate_config(const palu_config *c) {
         return fail(PALU_ERR_UNSUPPORTED, "only group_size = 32 is implemented");
     if (c->n_q_heads / c->n_kv_heads > kMaxGqa)
         return fail(PALU_ERR_UNSUPPORTED, "at most 8 query heads per kv head are implemented");
+    if (c->per_seq_basis != 0 && c->per_seq_basis != 1)
+        return fail(PALU_ERR_INVALID_ARG, "per_seq_basis must be 0 or 1");
+    if (c->per_seq_basis && c->rank <= 0)
+        return fail(PALU_ERR_UNSUPPORTED, "per-sequence bases need an explicit rank (all slots share one record layout)");
     return PALU_OK;
 }
 
@@ -184,10 +205,22 @@ int check_bound(const palu_cache *c) {
     return PALU_OK;
 }
 
+// Bound, and with shared bases both installed (per-sequence bases are
+// checked per slot by check_slot).
 int check_fitted(const palu_cache *c) {
     if (int e = check_bound(c)) return e;
-    if (!c->fitted[0] || !c->fitted[1])
+    if (!c->per_seq && (!c->ready[0][0] || !c->ready[1][0]))
         return fail(PALU_ERR_NOT_FITTED, "no basis for K and V yet (call palu_fit or palu_set_basis)");
+    return PALU_OK;
+}
+
+// slot in range and its bases installed
+int check_slot(const palu_cache *c, int slot) {
+    if (slot < 0 || slot >= c->max_batch)
+        return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " out of [0, max_batch)");
+    if (!c->slot_ready(slot))
+        return fail(PALU_ERR_NOT_FITTED, "no K and V bases for slot " + std::to_string(slot) +
+                                             " (call palu_fit_seq or palu_set_basis_seq)");
     return PALU_OK;
 }
 
@@ -196,12 +229,9 @@ void reset_seqs(palu_cache *c) {
     std::fill(c->sel.begin(), c->sel.end(), 0);
 }
 
-// Sets tensor t's coder for its fitted rank and uploads the basis of the
-// coded channels (fp32 [G][D][rc], channel-major fp32 [G][rc][D] and the
-// position-ordered fp16 copy) and the mean.  0-bit channels are left out:
-// their latents are zero by definition.
-int upload_basis(palu_cache *c, int t) {
-    const int G = c->G, D = c->D, rr = c->r[t];
+// Sets tensor t's coder (segments, coded channels) for its rank.
+int set_coder(palu_cache *c, int t) {
+    const int rr = c->r[t];
     if (c->quantized(t)) {
         c->cd[t] = coder_for(c->cfg, rr, &c->coded[t]);
     } else {
@@ -212,29 +242,62 @@ int upload_basis(palu_cache *c, int t) {
     const int rc = static_cast<int>(c->coded[t].size());
     if (rc == 0) return fail(PALU_ERR_UNSUPPORTED, "the bit schedule codes no channel at rank " + std::to_string(rr));
     c->rc[t] = rc;
+    return PALU_OK;
+}
+
+// Uploads basis set `set` of tensor t (host copy in basis_h / mu_h) for the
+// coded channels: fp32 [G][D][rc], channel-major fp32 [G][rc][D], the
+// position-ordered fp16 copy and the mean.  0-bit channels are left out:
+// their latents are zero by definition.  The coder must be set.
+int upload_basis(palu_cache *c, int t, int set) {
+    const int G = c->G, D = c->D, rr = c->r[t], rc = c->rc[t];
+    const float *src = c->basis_h[t].data() + set * c->basis_elems(t);
     std::vector<float> bk(static_cast<size_t>(G) * D * rc), cm(static_cast<size_t>(G) * rc * D);
     for (int g = 0; g < G; ++g)
         for (int d = 0; d < D; ++d)
             for (int k = 0; k < rc; ++k) {
-                const float v = c->basis_h[t][(static_cast<size_t>(g) * D + d) * rr + c->coded[t][k]];
+                const float v = src[(static_cast<size_t>(g) * D + d) * rr + c->coded[t][k]];
                 bk[(static_cast<size_t>(g) * D + d) * rc + k] = v;
                 cm[(static_cast<size_t>(g) * rc + k) * D + d] = v;
             }
-    hipError_t e = hipMemcpy(c->dev + c->off_basis[t], bk.data(), bk.size() * sizeof(float), hipMemcpyHostToDevice);
+    const TensorDev td = c->tensor_dev(t);
+    float *basis = td.basis + set * td.set_basis;
+    hipError_t e = hipMemcpy(basis, bk.data(), bk.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "basis upload");
-    e = hipMemcpy(c->dev + c->off_mu[t], c->mu_h[t].data(), c->mu_h[t].size() * sizeof(float),
+    e = hipMemcpy(td.mu + set * td.set_mu, c->mu_h[t].data() + set * c->mu_elems(), c->mu_elems() * sizeof(float),
                   hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "mean upload");
-    e = hipMemcpy(c->dev + c->off_bcm[t], cm.data(), cm.size() * sizeof(float), hipMemcpyHostToDevice);
+    e = hipMemcpy(td.basis_cm + set * td.set_bcm, cm.data(), cm.size() * sizeof(float), hipMemcpyHostToDevice);
     if (e != hipSuccess) return hip_fail(e, "channel-major basis upload");
     if (t == 0) {   // only the key basis is absorbed into queries
-        e = launch_basis_t16(reinterpret_cast<const float *>(c->dev + c->off_basis[t]),
-                             reinterpret_cast<uint16_t *>(c->dev + c->off_bt16[t]), G, rc, c->cd[t], nullptr);
+        e = launch_basis_t16(basis, td.basis_t16 + set * td.set_bt16, G, rc, c->cd[t], nullptr);
         if (e != hipSuccess) return hip_fail(e, "basis fp16 copy");
     }
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "basis upload synchronize");
     return PALU_OK;
+}
+
+// Installs a basis (host [G][D][r], mean [G][D], sigma [G][D] or null)
+// as set `set` of tensor t and uploads it.
+int install_basis(palu_cache *c, int t, int set, const float *basis, const float *mu, const double *sigma) {
+    const size_t nb = c->basis_elems(t), nm = c->mu_elems();
+    c->ready[t][set] = 0;
+    std::copy(basis, basis + nb, c->basis_h[t].begin() + set * nb);
+    std::copy(mu, mu + nm, c->mu_h[t].begin() + set * nm);
+    if (sigma) std::copy(sigma, sigma + nm, c->sigma_h[t].begin() + set * nm);
+    else std::fill(c->sigma_h[t].begin() + set * nm, c->sigma_h[t].begin() + (set + 1) * nm, 0.0);
+    if (int e = upload_basis(c, t, set)) return e;
+    c->ready[t][set] = 1;
+    return PALU_OK;
+}
+
+// Shared bases: sizes the host copies of tensor t for rank rr.
+void size_shared(palu_cache *c, int t, int rr) {
+    c->r[t] = rr;
+    c->basis_h[t].assign(c->basis_elems(t), 0.0f);
+    c->mu_h[t].assign(c->mu_elems(), 0.0f);
+    c->sigma_h[t].assign(c->mu_elems(), 0.0);
 }
 
 }  // namespace
@@ -258,6 +321,7 @@ PALU_API int palu_config_default(palu_config *cfg, int32_t head_dim, int32_t n_k
     cfg->input_dtype = 0;
     cfg->schedule_len = 0;
     for (int i = 0; i < 8; ++i) cfg->bit_schedule[i] = 0;
+    cfg->per_seq_basis = 0;
     return PALU_OK;
 }
 
@@ -292,23 +356,44 @@ PALU_API int palu_cache_create(const palu_config *cfg, int32_t max_batch, int32_
         off = align_up(off + bytes, 256);
         return o;
     };
+    c->per_seq = cfg->per_seq_basis != 0;
+    c->nbs = c->per_seq ? max_batch : 1;
+    // with per-sequence bases the rank is fixed: regions sized for it
+    const int r_alloc = c->per_seq ? std::min(cfg->rank, c->D) : c->r_max;
+    c->sb_basis = static_cast<int64_t>(c->G) * c->D * r_alloc;
+    c->sb_bt16 = static_cast<int64_t>(c->G) * c->D * (r_alloc + 8 * kMaxSegs);   // >= basis_t16_rows
+    c->sb_bcm = c->sb_basis;
+    c->sb_mu = static_cast<int64_t>(c->G) * c->D;
     for (int t = 0; t < 2; ++t) {
-        c->off_basis[t] = take(sizeof(float) * c->G * c->D * c->r_max);
-        c->off_bt16[t] = take(sizeof(uint16_t) * c->G * c->D * (c->r_max + 8 * kMaxSegs));   // >= basis_t16_rows
-        c->off_bcm[t] = take(sizeof(float) * c->G * c->D * c->r_max);
-        c->off_mu[t] = take(sizeof(float) * c->G * c->D);
-        const size_t head_words = (static_cast<size_t>(c->max_groups) * c->words_for(t, c->r_max) + 3) / 4 * 4;
+        c->ready[t].assign(c->nbs, 0);
+        c->off_basis[t] = take(sizeof(float) * c->nbs * c->sb_basis);
+        // only the key basis is absorbed into queries: no fp16 copy of V's
+        c->off_bt16[t] = t == 0 ? take(sizeof(uint16_t) * c->nbs * c->sb_bt16) : 0;
+        c->off_bcm[t] = take(sizeof(float) * c->nbs * c->sb_bcm);
+        c->off_mu[t] = take(sizeof(float) * c->nbs * c->sb_mu);
+        const size_t head_words = (static_cast<size_t>(c->max_groups) * c->words_for(t, r_alloc) + 3) / 4 * 4;
         c->off_rec[t] = take(sizeof(uint32_t) * static_cast<size_t>(max_batch) * c->H * head_words);
         c->off_tail[t] = c->quantized(t)
-                             ? take(sizeof(float) * static_cast<size_t>(max_batch) * c->H * 2 * kTokGroup * c->r_max)
+                             ? take(sizeof(float) * static_cast<size_t>(max_batch) * c->H * 2 * kTokGroup * r_alloc)
                              : 0;
+        if (c->per_seq) {
+            c->r[t] = r_alloc;
+            if (int e = set_coder(c, t)) {
+                delete c;
+                return e;
+            }
+            c->basis_h[t].assign(c->nbs * c->basis_elems(t), 0.0f);
+            c->mu_h[t].assign(c->nbs * c->mu_elems(), 0.0f);
+            c->sigma_h[t].assign(c->nbs * c->mu_elems(), 0.0);
+        }
     }
     const int64_t n_rows_max = static_cast<int64_t>(max_batch) * max_seq_len * c->hpg;
     c->gram_nb_cap = static_cast<int>(std::max<int64_t>(
         std::max(1, 512 / c->G), (n_rows_max + kGramMaxRowsPerBlock - 1) / kGramMaxRowsPerBlock));
     c->off_gram_part = take(sizeof(float) * 2 * static_cast<size_t>(c->G) * c->gram_nb_cap * kGramElems);
     c->off_gram_out = take(sizeof(double) * 2 * static_cast<size_t>(c->G) * kGramElems);
-    c->off_seg = take(sizeof(int64_t) * (static_cast<size_t>(max_batch) * c->hpg + 1));
+    // one prefix over all rows (shared fit) or one per row (per-sequence fit)
+    c->off_seg = take(sizeof(int64_t) * (static_cast<size_t>(max_batch) * (c->hpg + 1) + 1));
     // decode rows may repeat slots, so a launch can hold kMaxCallSeqs rows
     // whatever max_batch is
     c->off_attend = take(sizeof(float) * static_cast<size_t>(kMaxCallSeqs) * c->Hq * kMaxSplits * (c->r_max + 2));
@@ -332,44 +417,29 @@ PALU_API int palu_cache_bind(palu_cache *c, void *dev_buf, size_t bytes) {
         return fail(PALU_ERR_INVALID_ARG, "bound buffer must be 256-byte aligned");
     c->dev = static_cast<char *>(dev_buf);
     c->dev_bytes = bytes;
-    c->fitted[0] = c->fitted[1] = false;
+    for (int t = 0; t < 2; ++t) std::fill(c->ready[t].begin(), c->ready[t].end(), 0);
     reset_seqs(c);
     return PALU_OK;
 }
 
-PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t *seq_lens, int32_t B,
-                      int32_t S_stride, void *stream) {
-    if (int e = check_bound(c)) return e;
-    if (!k || !v || !seq_lens) return fail(PALU_ERR_INVALID_ARG, "k, v and seq_lens must be non-NULL");
-    if (B <= 0 || B > c->max_batch) return fail(PALU_ERR_INVALID_ARG, "B must be in [1, max_batch]");
-    if (S_stride <= 0) return fail(PALU_ERR_INVALID_ARG, "S_stride must be positive");
-    int64_t total = 0;
-    for (int b = 0; b < B; ++b) {
-        if (seq_lens[b] < 0 || seq_lens[b] > S_stride || seq_lens[b] > c->max_seq_len)
-            return fail(PALU_ERR_INVALID_ARG, "seq_lens[" + std::to_string(b) + "] out of [0, min(S_stride, max_seq_len)]");
-        total += seq_lens[b];
-    }
-    if (total == 0) return fail(PALU_ERR_INVALID_ARG, "no valid tokens to fit");
-    hipStream_t s = static_cast<hipStream_t>(stream);
+namespace {
 
-    const int nseg = B * c->hpg;
-    std::vector<int64_t> pref(nseg + 1, 0);
-    for (int sgi = 0; sgi < nseg; ++sgi) pref[sgi + 1] = pref[sgi] + seq_lens[sgi / c->hpg];
-    const int64_t n_rows = pref[nseg];
+// Gram partials of rows [b0, b0 + B) of k / v, each row's valid tokens
+// prefixed in seg (device, B * hpg + 1 entries), reduced into the fp64
+// [2][G][D*D + D] result, whose download into gram_host is queued on s.
+int queue_gram(palu_cache *c, const void *k, const void *v, int b0, int B, int S_stride, const int64_t *seg,
+               int64_t n_rows, hipStream_t s, double *gram_host) {
     const int nb_target = std::max(1, 512 / c->G);
     int64_t rpb = std::max<int64_t>(kGramRowsPerBlockMin, (n_rows + nb_target - 1) / nb_target);
     rpb = std::min<int64_t>(rpb, kGramMaxRowsPerBlock);
     rpb = (rpb + 63) / 64 * 64;
     const int nb = static_cast<int>((n_rows + rpb - 1) / rpb);
     if (nb > c->gram_nb_cap) return fail(PALU_ERR_CAPACITY, "fit workspace too small for this many rows");
-
-    hipError_t e = hipMemcpyAsync(c->dev + c->off_seg, pref.data(), sizeof(int64_t) * pref.size(),
-                                  hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "fit segment upload");
+    const size_t row_elems = static_cast<size_t>(c->H) * S_stride * c->D;
     GramArgs ga{};
-    ga.x[0] = static_cast<const uint16_t *>(k);
-    ga.x[1] = static_cast<const uint16_t *>(v);
-    ga.seg_pref = reinterpret_cast<const int64_t *>(c->dev + c->off_seg);
+    ga.x[0] = static_cast<const uint16_t *>(k) + b0 * row_elems;
+    ga.x[1] = static_cast<const uint16_t *>(v) + b0 * row_elems;
+    ga.seg_pref = seg;
     ga.partial = reinterpret_cast<float *>(c->dev + c->off_gram_part);
     ga.B = B;
     ga.H = c->H;
@@ -380,145 +450,298 @@ PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t
     ga.nb = nb;
     ga.rows_per_block = static_cast<int>(rpb);
     ga.n_rows = n_rows;
-    if ((e = launch_gram(ga, s)) != hipSuccess) return hip_fail(e, "gram launch");
+    hipError_t e = launch_gram(ga, s);
+    if (e != hipSuccess) return hip_fail(e, "gram launch");
     GramReduceArgs ra{};
     ra.partial = ga.partial;
     ra.out = reinterpret_cast<double *>(c->dev + c->off_gram_out);
     ra.G = c->G;
     ra.nb = nb;
     if ((e = launch_gram_reduce(ra, s)) != hipSuccess) return hip_fail(e, "gram reduce launch");
-    std::vector<double> gram(2 * static_cast<size_t>(c->G) * kGramElems);
-    e = hipMemcpyAsync(gram.data(), ra.out, sizeof(double) * gram.size(), hipMemcpyDeviceToHost, s);
+    e = hipMemcpyAsync(gram_host, ra.out, sizeof(double) * 2 * c->G * kGramElems, hipMemcpyDeviceToHost, s);
     if (e != hipSuccess) return hip_fail(e, "gram download");
+    return PALU_OK;
+}
+
+// One fitted (tensor, group) problem: eigenpairs of the scatter matrix
+// about the mean, X^T X - s s^T / N.
+struct FitProblem {
+    const double *gram;   // D*D Gram, then D column sums
+    double n;             // rows
+    std::vector<double> w, z;
+    bool ok = false;
+};
+
+// Eigendecompositions of all problems on host threads (they are independent).
+void solve_all(int D, std::vector<FitProblem> &pr) {
+    for (auto &p : pr) {
+        p.z.assign(static_cast<size_t>(D) * D, 0.0);
+        p.w.assign(D, 0.0);
+    }
+    const int np = static_cast<int>(pr.size());
+    const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+    const int nthreads = static_cast<int>(std::min<unsigned>(hw, static_cast<unsigned>(np)));
+    std::vector<std::thread> pool;
+    for (int th = 0; th < nthreads; ++th)
+        pool.emplace_back([&, th]() {
+            std::vector<double> cov(static_cast<size_t>(D) * D);
+            for (int i = th; i < np; i += nthreads) {
+                FitProblem &p = pr[i];
+                const double *sum = p.gram + D * D;
+                for (int a = 0; a < D; ++a)
+                    for (int b = 0; b < D; ++b) cov[a * D + b] = p.gram[a * D + b] - sum[a] * sum[b] / p.n;
+                for (int a = 0; a < D; ++a)
+                    for (int b = 0; b < a; ++b) {
+                        const double m = 0.5 * (cov[a * D + b] + cov[b * D + a]);
+                        cov[a * D + b] = cov[b * D + a] = m;
+                    }
+                p.ok = sym_eigen(cov.data(), D, p.w.data(), p.z.data());
+            }
+        });
+    for (auto &t : pool) t.join();
+}
+
+// Basis of one problem: eigenvectors by descending eigenvalue, each signed
+// so that its largest-magnitude component is positive, into full [D][D]
+// (column = channel); squared singular values s2, sigma and the mean.
+void basis_of(const FitProblem &p, int D, double *full, double *s2, double *sigma, float *mu) {
+    std::vector<int> order(D);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return p.w[a] > p.w[b]; });
+    for (int cidx = 0; cidx < D; ++cidx) {
+        const int src = order[cidx];
+        s2[cidx] = p.w[src] > 0.0 ? p.w[src] : 0.0;
+        sigma[cidx] = std::sqrt(s2[cidx]);
+        int arg = 0;
+        for (int d = 1; d < D; ++d)
+            if (std::fabs(p.z[d * D + src]) > std::fabs(p.z[arg * D + src])) arg = d;
+        const double sg = p.z[arg * D + src] < 0.0 ? -1.0 : 1.0;
+        for (int d = 0; d < D; ++d) full[d * D + cidx] = sg * p.z[d * D + src];
+    }
+    const double *sum = p.gram + D * D;
+    for (int d = 0; d < D; ++d) mu[d] = static_cast<float>(sum[d] / p.n);
+}
+
+// Smallest rank whose leading squared singular values reach tau of the
+// total (1 when the total is zero).
+int energy_rank(const double *s2, int D, float tau) {
+    double tot = 0.0;
+    for (int i = 0; i < D; ++i) tot += s2[i];
+    if (tot <= 0.0) return 1;
+    double acc = 0.0;
+    for (int kk = 1; kk <= D; ++kk) {
+        acc += s2[kk - 1];
+        if (acc >= static_cast<double>(tau) * tot) return kk;
+    }
+    return D;
+}
+
+// Fit argument checks shared by both modes.
+int check_fit_args(const palu_cache *c, const void *k, const void *v, const int32_t *seq_lens, int B,
+                   int S_stride) {
+    if (int e = check_bound(c)) return e;
+    if (!k || !v || !seq_lens) return fail(PALU_ERR_INVALID_ARG, "k, v and seq_lens must be non-NULL");
+    if (B <= 0 || B > c->max_batch) return fail(PALU_ERR_INVALID_ARG, "B must be in [1, max_batch]");
+    if (S_stride <= 0) return fail(PALU_ERR_INVALID_ARG, "S_stride must be positive");
+    for (int b = 0; b < B; ++b)
+        if (seq_lens[b] < 0 || seq_lens[b] > S_stride || seq_lens[b] > c->max_seq_len)
+            return fail(PALU_ERR_INVALID_ARG, "seq_lens[" + std::to_string(b) + "] out of [0, min(S_stride, max_seq_len)]");
+    return PALU_OK;
+}
+
+// Per-sequence fit: row b of k / v -> basis sets of slot ids[b].
+int fit_per_seq(palu_cache *c, const void *k, const void *v, const int32_t *ids, const int32_t *seq_lens, int B,
+                int S_stride, hipStream_t s) {
+    const int hpg = c->hpg, D = c->D, G = c->G;
+    std::vector<char> seen(c->max_batch, 0);
+    for (int b = 0; b < B; ++b) {
+        const int slot = ids ? ids[b] : b;
+        if (slot < 0 || slot >= c->max_batch)
+            return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " out of [0, max_batch)");
+        if (seen[slot]) return fail(PALU_ERR_INVALID_ARG, "sequence slot listed twice in one call");
+        seen[slot] = 1;
+        if (seq_lens[b] <= 0) return fail(PALU_ERR_INVALID_ARG, "a per-sequence fit needs at least one token per row");
+    }
+    // each row's segment prefix: hpg heads of seq_lens[b] rows
+    std::vector<int64_t> pref(static_cast<size_t>(B) * (hpg + 1));
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i <= hpg; ++i) pref[static_cast<size_t>(b) * (hpg + 1) + i] = static_cast<int64_t>(i) * seq_lens[b];
+    hipError_t e = hipMemcpyAsync(c->dev + c->off_seg, pref.data(), sizeof(int64_t) * pref.size(),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "fit segment upload");
+    const size_t per = 2 * static_cast<size_t>(G) * kGramElems;
+    std::vector<double> gram(per * B);
+    const int64_t *seg = reinterpret_cast<const int64_t *>(c->dev + c->off_seg);
+    for (int b = 0; b < B; ++b)
+        if (int err = queue_gram(c, k, v, b, 1, S_stride, seg + static_cast<size_t>(b) * (hpg + 1),
+                                 static_cast<int64_t>(hpg) * seq_lens[b], s, gram.data() + per * b))
+            return err;
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "fit synchronize");
 
-    const int D = c->D;
-    const double N = static_cast<double>(n_rows);
-    // scatter matrices about the mean, X^T X - s s^T / N, and their
-    // eigendecompositions: the 2 G (tensor, group) problems are independent
-    // and run on host threads
-    const int nprob = 2 * c->G;
-    std::vector<double> covs(static_cast<size_t>(nprob) * D * D), ws(static_cast<size_t>(nprob) * D),
-        zs(static_cast<size_t>(nprob) * D * D);
-    for (int pb = 0; pb < nprob; ++pb) {
-        const double *G2 = gram.data() + static_cast<size_t>(pb) * kGramElems;
-        const double *sum = G2 + D * D;
-        double *cov = covs.data() + static_cast<size_t>(pb) * D * D;
-        for (int i = 0; i < D; ++i)
-            for (int j = 0; j < D; ++j) cov[i * D + j] = G2[i * D + j] - sum[i] * sum[j] / N;
-        for (int i = 0; i < D; ++i)
-            for (int j = 0; j < i; ++j) {
-                const double m = 0.5 * (cov[i * D + j] + cov[j * D + i]);
-                cov[i * D + j] = cov[j * D + i] = m;
-            }
-    }
-    std::vector<char> converged(nprob, 0);
-    {
-        const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
-        const int nthreads = static_cast<int>(std::min<unsigned>(hw, static_cast<unsigned>(nprob)));
-        std::vector<std::thread> pool;
-        for (int th = 0; th < nthreads; ++th)
-            pool.emplace_back([&, th]() {
-                for (int pb = th; pb < nprob; pb += nthreads)
-                    converged[pb] = sym_eigen(covs.data() + static_cast<size_t>(pb) * D * D, D,
-                                              ws.data() + static_cast<size_t>(pb) * D,
-                                              zs.data() + static_cast<size_t>(pb) * D * D);
-            });
-        for (auto &t : pool) t.join();
-    }
-    std::vector<int> order(D);
-    for (int t = 0; t < 2; ++t) {
-        std::vector<double> basis_full(static_cast<size_t>(c->G) * D * D);
-        std::vector<int> rg(c->G);
-        c->mu_h[t].assign(static_cast<size_t>(c->G) * D, 0.0f);
-        c->sigma_h[t].assign(static_cast<size_t>(c->G) * D, 0.0);
-        for (int g = 0; g < c->G; ++g) {
-            const int pb = t * c->G + g;
-            const double *G2 = gram.data() + static_cast<size_t>(pb) * kGramElems;
-            const double *sum = G2 + D * D;
-            if (!converged[pb]) return fail(PALU_ERR_HIP, "eigensolver did not converge");
-            const double *w = ws.data() + static_cast<size_t>(pb) * D;
-            const double *z = zs.data() + static_cast<size_t>(pb) * D * D;
-            std::iota(order.begin(), order.end(), 0);
-            std::stable_sort(order.begin(), order.end(), [&](int a2, int b2) { return w[a2] > w[b2]; });
-            std::vector<double> s2(D);
-            for (int cidx = 0; cidx < D; ++cidx) {
-                const int src = order[cidx];
-                s2[cidx] = w[src] > 0.0 ? w[src] : 0.0;
-                c->sigma_h[t][g * D + cidx] = std::sqrt(s2[cidx]);
-                int arg = 0;
-                for (int d = 1; d < D; ++d)
-                    if (std::fabs(z[d * D + src]) > std::fabs(z[arg * D + src])) arg = d;
-                const double sg = z[arg * D + src] < 0.0 ? -1.0 : 1.0;
-                for (int d = 0; d < D; ++d)
-                    basis_full[(static_cast<size_t>(g) * D + d) * D + cidx] = sg * z[d * D + src];
-            }
-            for (int d = 0; d < D; ++d) c->mu_h[t][g * D + d] = static_cast<float>(sum[d] / N);
-            if (c->cfg.rank > 0) {
-                rg[g] = std::min(c->cfg.rank, D);
-            } else {
-                double tot = 0.0;
-                for (int i = 0; i < D; ++i) tot += s2[i];
-                int rr = D;
-                if (tot <= 0.0) {
-                    rr = 1;
-                } else {
-                    double acc = 0.0;
-                    for (int kk = 1; kk <= D; ++kk) {
-                        acc += s2[kk - 1];
-                        if (acc >= static_cast<double>(c->cfg.energy_threshold) * tot) {
-                            rr = kk;
-                            break;
-                        }
-                    }
-                }
-                rg[g] = rr;
-            }
+    std::vector<FitProblem> pr(static_cast<size_t>(B) * 2 * G);
+    for (int b = 0; b < B; ++b)
+        for (int pb = 0; pb < 2 * G; ++pb) {
+            FitProblem &p = pr[static_cast<size_t>(b) * 2 * G + pb];
+            p.gram = gram.data() + per * b + static_cast<size_t>(pb) * kGramElems;
+            p.n = static_cast<double>(hpg) * seq_lens[b];
         }
-        int rr = *std::min_element(rg.begin(), rg.end());
+    solve_all(D, pr);
+    for (const auto &p : pr)
+        if (!p.ok) return fail(PALU_ERR_HIP, "eigensolver did not converge");
+    std::vector<double> full(static_cast<size_t>(D) * D), s2(D);
+    for (int b = 0; b < B; ++b) {
+        const int slot = ids ? ids[b] : b;
+        c->len[slot] = 0;
+        c->sel[slot] = 0;
+        for (int t = 0; t < 2; ++t) {
+            const int rr = c->r[t];
+            std::vector<float> basis(c->basis_elems(t)), mu(c->mu_elems());
+            std::vector<double> sigma(c->mu_elems());
+            for (int g = 0; g < G; ++g) {
+                basis_of(pr[(static_cast<size_t>(b) * 2 + t) * G + g], D, full.data(), s2.data(),
+                         sigma.data() + static_cast<size_t>(g) * D, mu.data() + static_cast<size_t>(g) * D);
+                for (int d = 0; d < D; ++d)
+                    for (int cidx = 0; cidx < rr; ++cidx)
+                        basis[(static_cast<size_t>(g) * D + d) * rr + cidx] = static_cast<float>(full[d * D + cidx]);
+            }
+            if (int err = install_basis(c, t, slot, basis.data(), mu.data(), sigma.data())) return err;
+        }
+    }
+    return PALU_OK;
+}
+
+}  // namespace
+
+PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t *seq_lens, int32_t B,
+                      int32_t S_stride, void *stream) {
+    if (int e = check_fit_args(c, k, v, seq_lens, B, S_stride)) return e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (c->per_seq) return fit_per_seq(c, k, v, nullptr, seq_lens, B, S_stride, s);
+    int64_t total = 0;
+    for (int b = 0; b < B; ++b) total += seq_lens[b];
+    if (total == 0) return fail(PALU_ERR_INVALID_ARG, "no valid tokens to fit");
+    c->ready[0][0] = c->ready[1][0] = 0;
+    reset_seqs(c);
+
+    const int nseg = B * c->hpg;
+    std::vector<int64_t> pref(nseg + 1, 0);
+    for (int sgi = 0; sgi < nseg; ++sgi) pref[sgi + 1] = pref[sgi] + seq_lens[sgi / c->hpg];
+    const int64_t n_rows = pref[nseg];
+    hipError_t e = hipMemcpyAsync(c->dev + c->off_seg, pref.data(), sizeof(int64_t) * pref.size(),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "fit segment upload");
+    std::vector<double> gram(2 * static_cast<size_t>(c->G) * kGramElems);
+    if (int err = queue_gram(c, k, v, 0, B, S_stride, reinterpret_cast<const int64_t *>(c->dev + c->off_seg), n_rows,
+                             s, gram.data()))
+        return err;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "fit synchronize");
+
+    const int D = c->D, G = c->G;
+    std::vector<FitProblem> pr(2 * G);
+    for (int pb = 0; pb < 2 * G; ++pb) {
+        pr[pb].gram = gram.data() + static_cast<size_t>(pb) * kGramElems;
+        pr[pb].n = static_cast<double>(n_rows);
+    }
+    solve_all(D, pr);
+    for (const auto &p : pr)
+        if (!p.ok) return fail(PALU_ERR_HIP, "eigensolver did not converge");
+    for (int t = 0; t < 2; ++t) {
+        std::vector<double> full(static_cast<size_t>(G) * D * D), s2(static_cast<size_t>(G) * D),
+            sigma(static_cast<size_t>(G) * D);
+        std::vector<float> mu(static_cast<size_t>(G) * D);
+        int rr = D;
+        for (int g = 0; g < G; ++g) {
+            double *sg = s2.data() + static_cast<size_t>(g) * D;
+            basis_of(pr[t * G + g], D, full.data() + static_cast<size_t>(g) * D * D, sg,
+                     sigma.data() + static_cast<size_t>(g) * D, mu.data() + static_cast<size_t>(g) * D);
+            rr = std::min(rr, c->cfg.rank > 0 ? std::min(c->cfg.rank, D) : energy_rank(sg, D, c->cfg.energy_threshold));
+        }
         if (rr > c->r_max)
             return fail(PALU_ERR_CAPACITY, "fitted rank " + std::to_string(rr) + " exceeds max_rank " +
                                                std::to_string(c->r_max));
-        c->r[t] = rr;
-        c->basis_h[t].assign(static_cast<size_t>(c->G) * D * rr, 0.0f);
-        for (int g = 0; g < c->G; ++g)
+        size_shared(c, t, rr);
+        std::vector<float> basis(c->basis_elems(t));
+        for (int g = 0; g < G; ++g)
             for (int d = 0; d < D; ++d)
                 for (int cidx = 0; cidx < rr; ++cidx)
-                    c->basis_h[t][(static_cast<size_t>(g) * D + d) * rr + cidx] =
-                        static_cast<float>(basis_full[(static_cast<size_t>(g) * D + d) * D + cidx]);
-        if (int err = upload_basis(c, t)) return err;
-        c->fitted[t] = true;
+                    basis[(static_cast<size_t>(g) * D + d) * rr + cidx] =
+                        static_cast<float>(full[(static_cast<size_t>(g) * D + d) * D + cidx]);
+        if (int err = set_coder(c, t)) return err;
+        if (int err = install_basis(c, t, 0, basis.data(), mu.data(), sigma.data())) return err;
     }
-    reset_seqs(c);
     return PALU_OK;
+}
+
+PALU_API int palu_fit_seq(palu_cache *c, const void *k, const void *v, const int32_t *seq_ids,
+                          const int32_t *seq_lens, int32_t B, int32_t S_stride, void *stream) {
+    if (int e = check_fit_args(c, k, v, seq_lens, B, S_stride)) return e;
+    if (!c->per_seq) return fail(PALU_ERR_INVALID_ARG, "palu_fit_seq needs per_seq_basis = 1");
+    if (!seq_ids) return fail(PALU_ERR_INVALID_ARG, "seq_ids must be non-NULL");
+    return fit_per_seq(c, k, v, seq_ids, seq_lens, B, S_stride, static_cast<hipStream_t>(stream));
 }
 
 PALU_API int palu_set_basis(palu_cache *c, int32_t tensor, int32_t r, const float *basis, const float *mu) {
     if (int e = check_bound(c)) return e;
     if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
     if (!basis || !mu) return fail(PALU_ERR_INVALID_ARG, "basis and mu must be non-NULL");
+    if (c->per_seq) {
+        // the same basis in every slot
+        if (r != c->r[tensor]) return fail(PALU_ERR_INVALID_ARG, "r must equal the cache's rank");
+        for (int set = 0; set < c->nbs; ++set)
+            if (int e = install_basis(c, tensor, set, basis, mu, nullptr)) return e;
+        reset_seqs(c);
+        return PALU_OK;
+    }
     if (r < 1 || r > c->r_max) return fail(PALU_ERR_INVALID_ARG, "r must be in [1, max_rank]");
-    c->r[tensor] = r;
-    c->basis_h[tensor].assign(basis, basis + static_cast<size_t>(c->G) * c->D * r);
-    c->mu_h[tensor].assign(mu, mu + static_cast<size_t>(c->G) * c->D);
-    c->sigma_h[tensor].assign(static_cast<size_t>(c->G) * c->D, 0.0);
-    c->fitted[tensor] = false;
-    if (int e = upload_basis(c, tensor)) return e;
-    c->fitted[tensor] = true;
+    c->ready[tensor][0] = 0;
     reset_seqs(c);
+    size_shared(c, tensor, r);
+    if (int e = set_coder(c, tensor)) return e;
+    return install_basis(c, tensor, 0, basis, mu, nullptr);
+}
+
+PALU_API int palu_set_basis_seq(palu_cache *c, int32_t seq, int32_t tensor, int32_t r, const float *basis,
+                                const float *mu) {
+    if (int e = check_bound(c)) return e;
+    if (!c->per_seq) return fail(PALU_ERR_INVALID_ARG, "palu_set_basis_seq needs per_seq_basis = 1");
+    if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
+    if (seq < 0 || seq >= c->max_batch) return fail(PALU_ERR_CAPACITY, "sequence slot out of range");
+    if (!basis || !mu) return fail(PALU_ERR_INVALID_ARG, "basis and mu must be non-NULL");
+    if (r != c->r[tensor]) return fail(PALU_ERR_INVALID_ARG, "r must equal the cache's rank");
+    c->len[seq] = 0;
+    c->sel[seq] = 0;
+    return install_basis(c, tensor, seq, basis, mu, nullptr);
+}
+
+namespace {
+
+int get_set(const palu_cache *c, int tensor, int set, int32_t *r, float *basis, float *mu, double *sigma) {
+    if (!c->ready[tensor][set]) return fail(PALU_ERR_NOT_FITTED, "no basis for this tensor");
+    const size_t nb = c->basis_elems(tensor), nm = c->mu_elems();
+    if (r) *r = c->r[tensor];
+    if (basis) std::memcpy(basis, c->basis_h[tensor].data() + set * nb, nb * sizeof(float));
+    if (mu) std::memcpy(mu, c->mu_h[tensor].data() + set * nm, nm * sizeof(float));
+    if (sigma) std::memcpy(sigma, c->sigma_h[tensor].data() + set * nm, nm * sizeof(double));
     return PALU_OK;
 }
+
+}  // namespace
 
 PALU_API int palu_get_basis(const palu_cache *c, int32_t tensor, int32_t *r, float *basis, float *mu,
                             double *sigma) {
     if (!c) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
     if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
-    if (!c->fitted[tensor]) return fail(PALU_ERR_NOT_FITTED, "no basis for this tensor");
-    if (r) *r = c->r[tensor];
-    if (basis) std::memcpy(basis, c->basis_h[tensor].data(), c->basis_h[tensor].size() * sizeof(float));
-    if (mu) std::memcpy(mu, c->mu_h[tensor].data(), c->mu_h[tensor].size() * sizeof(float));
-    if (sigma) std::memcpy(sigma, c->sigma_h[tensor].data(), c->sigma_h[tensor].size() * sizeof(double));
-    return PALU_OK;
+    if (c->per_seq) return fail(PALU_ERR_INVALID_ARG, "per-sequence bases: use palu_get_basis_seq");
+    return get_set(c, tensor, 0, r, basis, mu, sigma);
+}
+
+PALU_API int palu_get_basis_seq(const palu_cache *c, int32_t seq, int32_t tensor, int32_t *r, float *basis,
+                                float *mu, double *sigma) {
+    if (!c) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+    if (!c->per_seq) return fail(PALU_ERR_INVALID_ARG, "palu_get_basis_seq needs per_seq_basis = 1");
+    if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
+    if (seq < 0 || seq >= c->max_batch) return fail(PALU_ERR_CAPACITY, "sequence slot out of range");
+    return get_set(c, tensor, seq, r, basis, mu, sigma);
 }
 
 PALU_API int palu_encode_append(palu_cache *c, const void *k, const void *v, const int32_t *seq_ids,
@@ -530,8 +753,7 @@ PALU_API int palu_encode_append(palu_cache *c, const void *k, const void *v, con
     std::vector<char> seen(c->max_batch, 0);
     for (int b = 0; b < B; ++b) {
         const int slot = seq_ids ? seq_ids[b] : b;
-        if (slot < 0 || slot >= c->max_batch)
-            return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " out of [0, max_batch)");
+        if (int e = check_slot(c, slot)) return e;
         if (seen[slot]) return fail(PALU_ERR_INVALID_ARG, "sequence slot listed twice in one call");
         seen[slot] = 1;
         const int n = n_new ? n_new[b] : T_stride;
@@ -599,8 +821,7 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
         return fail(PALU_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
     for (int b = 0; b < B; ++b) {
         const int slot = seq_ids ? seq_ids[b] : b;
-        if (slot < 0 || slot >= c->max_batch)
-            return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " out of [0, max_batch)");
+        if (int e = check_slot(c, slot)) return e;
         if (c->len[slot] <= 0)
             return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " holds no tokens");
     }
@@ -631,6 +852,7 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
             aa.row[i].len = c->len[slot];
             aa.row[i].qi = i;
             aa.row[i].sel_ns = c->sel[slot];
+            aa.slot_call[i] = slot;
             const int nfull = c->len[slot] / kTokGroup;
             units += static_cast<int64_t>(c->H) * std::max(1, nfull);
             max_full = std::max(max_full, nfull);
@@ -692,8 +914,7 @@ PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const 
         return fail(PALU_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
     for (int b = 0; b < B; ++b) {
         const int slot = seq_ids ? seq_ids[b] : b;
-        if (slot < 0 || slot >= c->max_batch)
-            return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " out of [0, max_batch)");
+        if (int e = check_slot(c, slot)) return e;
         const int n = n_q ? n_q[b] : T_stride;
         if (n < 0 || n > T_stride) return fail(PALU_ERR_INVALID_ARG, "n_q must be in [0, T_stride]");
         if (n > c->len[slot])
@@ -752,7 +973,7 @@ PALU_API int palu_read_codes(const palu_cache *c, int32_t seq, int32_t head, int
                              size_t records_bytes, float *tail, size_t tail_bytes) {
     if (int e = check_fitted(c)) return e;
     if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
-    if (seq < 0 || seq >= c->max_batch) return fail(PALU_ERR_CAPACITY, "sequence slot out of range");
+    if (int e = check_slot(c, seq)) return e;
     if (head < 0 || head >= c->H) return fail(PALU_ERR_INVALID_ARG, "head out of range");
     const TensorDev td = c->tensor_dev(tensor);
     const int len = c->len[seq];
@@ -778,7 +999,7 @@ PALU_API int palu_read_codes(const palu_cache *c, int32_t seq, int32_t head, int
 
 PALU_API int palu_get_stats(const palu_cache *c, palu_stats *st) {
     if (!c || !st) return fail(PALU_ERR_INVALID_ARG, "cache or stats is NULL");
-    if (!c->fitted[0] || !c->fitted[1]) return fail(PALU_ERR_NOT_FITTED, "no basis for K and V yet");
+    if (!c->layout_known(0) || !c->layout_known(1)) return fail(PALU_ERR_NOT_FITTED, "no basis for K and V yet");
     std::memset(st, 0, sizeof(*st));
     st->r_k = c->r[0];
     st->r_v = c->r[1];
@@ -802,7 +1023,9 @@ PALU_API int palu_get_stats(const palu_cache *c, palu_stats *st) {
     const double D = c->D;
     for (int t = 0; t < 2; ++t) {
         const int rr = c->r[t], rc = c->rc[t];
-        const int64_t basis_bytes = static_cast<int64_t>(c->G) * c->D * (rc + 1) * 4;
+        // stored bases and means: one set, or one per slot that has its own
+        const int64_t sets = std::count(c->ready[t].begin(), c->ready[t].end(), 1);
+        const int64_t basis_bytes = sets * c->G * c->D * (rc + 1) * 4;
         int64_t bytes;
         double nominal, realised;
         if (c->quantized(t)) {
@@ -846,7 +1069,7 @@ PALU_API int palu_reset(palu_cache *c) {
 PALU_API int palu_record_words(const palu_cache *c, int32_t tensor, int32_t *words) {
     if (!c || !words) return fail(PALU_ERR_INVALID_ARG, "cache or words is NULL");
     if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
-    if (!c->fitted[tensor]) return fail(PALU_ERR_NOT_FITTED, "no basis for this tensor");
+    if (!c->layout_known(tensor)) return fail(PALU_ERR_NOT_FITTED, "no basis for this tensor");
     *words = c->words_for(tensor, c->r[tensor]);
     return PALU_OK;
 }
@@ -867,13 +1090,29 @@ uint64_t fnv1a(uint64_t h, const void *p, size_t n) {
     return h;
 }
 
-uint64_t basis_hash(const palu_cache *c) {
+// Hash of K basis, K mean, V basis, V mean (fp32), each given as a pointer.
+uint64_t basis_hash(const palu_cache *c, const float *const part[4]) {
     uint64_t h = 0xCBF29CE484222325ull;
     for (int t = 0; t < 2; ++t) {
-        h = fnv1a(h, c->basis_h[t].data(), c->basis_h[t].size() * sizeof(float));
-        h = fnv1a(h, c->mu_h[t].data(), c->mu_h[t].size() * sizeof(float));
+        h = fnv1a(h, part[2 * t], c->basis_elems(t) * sizeof(float));
+        h = fnv1a(h, part[2 * t + 1], c->mu_elems() * sizeof(float));
     }
     return h;
+}
+
+// The four parts of basis set `set` in the host copies.
+void set_parts(const palu_cache *c, int set, const float *part[4]) {
+    for (int t = 0; t < 2; ++t) {
+        part[2 * t] = c->basis_h[t].data() + set * c->basis_elems(t);
+        part[2 * t + 1] = c->mu_h[t].data() + set * c->mu_elems();
+    }
+}
+
+// Bytes of a slot's bases and means stored after the header (per-sequence
+// bases only).
+size_t seq_basis_bytes(const palu_cache *c) {
+    if (!c->per_seq) return 0;
+    return sizeof(float) * (c->basis_elems(0) + c->basis_elems(1) + 2 * c->mu_elems());
 }
 
 // Per-tensor sizes of one slot of length len.
@@ -894,7 +1133,7 @@ SeqPart seq_part(const palu_cache *c, int t, int len) {
 }
 
 size_t seq_bytes(const palu_cache *c, int len) {
-    size_t n = kSeqHeaderBytes;
+    size_t n = kSeqHeaderBytes + seq_basis_bytes(c);
     for (int t = 0; t < 2; ++t) {
         const SeqPart p = seq_part(c, t, len);
         n += static_cast<size_t>(c->H) * (p.rec_bytes() + p.tail_bytes());
@@ -921,8 +1160,7 @@ void seq_header(const palu_cache *c, int len, int32_t f[kSeqHeaderInts]) {
 
 int check_seq(const palu_cache *c, int32_t seq) {
     if (int e = check_fitted(c)) return e;
-    if (seq < 0 || seq >= c->max_batch) return fail(PALU_ERR_CAPACITY, "sequence slot out of range");
-    return PALU_OK;
+    return check_slot(c, seq);
 }
 
 }  // namespace
@@ -944,11 +1182,21 @@ PALU_API int palu_export_seq(const palu_cache *c, int32_t seq, void *host_dst, s
     int32_t f[kSeqHeaderInts];
     seq_header(c, len, f);
     std::memcpy(out, f, sizeof(f));
-    const uint64_t h = basis_hash(c);
+    const float *part[4];
+    set_parts(c, c->bset(seq), part);
+    const uint64_t h = basis_hash(c, part);
     std::memcpy(out + sizeof(f), &h, sizeof(h));
+    const uint32_t flags = c->per_seq ? 1u : 0u;
+    std::memcpy(out + sizeof(f) + sizeof(h), &flags, sizeof(flags));
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "export synchronize");
     char *p = out + kSeqHeaderBytes;
+    if (c->per_seq)
+        for (int i = 0; i < 4; ++i) {
+            const size_t n = sizeof(float) * (i % 2 ? c->mu_elems() : c->basis_elems(i / 2));
+            std::memcpy(p, part[i], n);
+            p += n;
+        }
     const int64_t hb0 = static_cast<int64_t>(seq) * c->H;
     for (int t = 0; t < 2; ++t) {
         const TensorDev td = c->tensor_dev(t);
@@ -971,7 +1219,11 @@ PALU_API int palu_export_seq(const palu_cache *c, int32_t seq, void *host_dst, s
 }
 
 PALU_API int palu_import_seq(palu_cache *c, int32_t seq, const void *host_src, size_t bytes) {
-    if (int e = check_seq(c, seq)) return e;
+    // a per-sequence import installs the slot's bases, so they need not be there yet
+    if (int e = check_fitted(c)) return e;
+    if (seq < 0 || seq >= c->max_batch) return fail(PALU_ERR_CAPACITY, "sequence slot out of range");
+    if (!c->per_seq)
+        if (int e = check_slot(c, seq)) return e;
     if (!host_src) return fail(PALU_ERR_INVALID_ARG, "source is NULL");
     if (bytes < kSeqHeaderBytes) return fail(PALU_ERR_INVALID_ARG, "source shorter than the header");
     const char *in = static_cast<const char *>(host_src);
@@ -979,6 +1231,8 @@ PALU_API int palu_import_seq(palu_cache *c, int32_t seq, const void *host_src, s
     std::memcpy(f, in, sizeof(f));
     uint64_t h;
     std::memcpy(&h, in + sizeof(f), sizeof(h));
+    uint32_t flags;
+    std::memcpy(&flags, in + sizeof(f) + sizeof(h), sizeof(flags));
     if (static_cast<uint32_t>(f[0]) != kSeqMagic) return fail(PALU_ERR_INVALID_ARG, "bad magic");
     if (static_cast<uint32_t>(f[1]) != kSeqVersion) return fail(PALU_ERR_INVALID_ARG, "unsupported version");
     const int len = f[12];
@@ -988,12 +1242,34 @@ PALU_API int palu_import_seq(palu_cache *c, int32_t seq, const void *host_src, s
     for (int i = 2; i < 12; ++i)
         if (f[i] != mine[i])
             return fail(PALU_ERR_INVALID_ARG, "slot was saved under a different shape, rank or value coding");
-    if (h != basis_hash(c)) return fail(PALU_ERR_INVALID_ARG, "slot was saved under a different basis");
+    if (flags != (c->per_seq ? 1u : 0u))
+        return fail(PALU_ERR_INVALID_ARG, c->per_seq ? "slot was saved without its bases (shared-basis cache)"
+                                                     : "slot was saved with its own bases (per-sequence cache)");
     if (len > c->max_seq_len) return fail(PALU_ERR_CAPACITY, "saved length exceeds max_seq_len");
     if (bytes != seq_bytes(c, len)) return fail(PALU_ERR_INVALID_ARG, "source size does not match its header");
+    const char *p = in + kSeqHeaderBytes;
+    const float *part[4];
+    if (c->per_seq) {
+        // the bases travel with the slot: check them against the hash, then install
+        std::vector<float> buf(seq_basis_bytes(c) / sizeof(float));
+        std::memcpy(buf.data(), p, seq_basis_bytes(c));
+        p += seq_basis_bytes(c);
+        const float *q = buf.data();
+        for (int i = 0; i < 4; ++i) {
+            part[i] = q;
+            q += i % 2 ? c->mu_elems() : c->basis_elems(i / 2);
+        }
+        if (h != basis_hash(c, part)) return fail(PALU_ERR_INVALID_ARG, "saved bases do not match their hash");
+        c->len[seq] = 0;
+        c->sel[seq] = 0;
+        for (int t = 0; t < 2; ++t)
+            if (int e = install_basis(c, t, seq, part[2 * t], part[2 * t + 1], nullptr)) return e;
+    } else {
+        set_parts(c, 0, part);
+        if (h != basis_hash(c, part)) return fail(PALU_ERR_INVALID_ARG, "slot was saved under a different basis");
+    }
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "import synchronize");
-    const char *p = in + kSeqHeaderBytes;
     const int64_t hb0 = static_cast<int64_t>(seq) * c->H;
     for (int t = 0; t < 2; ++t) {
         const TensorDev td = c->tensor_dev(t);

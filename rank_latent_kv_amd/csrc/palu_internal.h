@@ -74,7 +74,7 @@ struct TensorDev {
     uint32_t *records;   // [slots][H][max_groups][words]
     float *tail;         // [slots][H][2][32][r]  (nullptr for fp16 latents)
     float *basis;        // [G][D][r] fp32, d-major
-    uint16_t *basis_t16; // [G][P][D] fp16 copy, row n = channel of score-operand position n
+    uint16_t *basis_t16; // K only: [G][P][D] fp16 copy, row n = channel of score-operand position n
                          // (8-channel blocks, hi blocks first, [c0,c4,c1,c5,..] inside a
                          // block; zero rows for padding), P = 8 * blocks (query absorption)
     float *basis_cm;     // [G][r][D] fp32, channel-major copy (output projection)
@@ -84,6 +84,9 @@ struct TensorDev {
     Coder cd;            // segments of the quantised records (unused for fp16 latents)
     int64_t head_stride; // words between consecutive (slot, head): max_groups * words
                          // rounded up to a multiple of 4 (16-byte aligned streams)
+    // elements between the basis sets of consecutive slots (per-sequence
+    // bases); 0 when one basis set serves every slot
+    int64_t set_basis, set_bt16, set_bcm, set_mu;
 };
 
 struct GramArgs {
@@ -137,6 +140,7 @@ struct AttendArgs {
     int bf16;                 // q and out are bf16 (else fp16)
     AttendRow row[kMaxCallSeqs];       // grid z order (longest first)
     int nsplit_call[kMaxCallSeqs];     // splits of call row i (combine)
+    int slot_call[kMaxCallSeqs];       // cache slot of call row i (combine)
 };
 
 // One call row of a prefill attention launch: the queries are the last nq

@@ -282,13 +282,13 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     float *vsh = esh;
     float *msh = esh + kHeadDim * rp;
     {
-        const float *vb = T.basis + static_cast<int64_t>(grp) * kHeadDim * r;
+        const float *vb = T.basis + slot * T.set_basis + static_cast<int64_t>(grp) * kHeadDim * r;
         const FastDiv div_rp(1.0f / static_cast<float>(rp));
         for (int e = tid; e < kHeadDim * rp; e += 256) {
             const int d = div_rp.quo(e), c = e - d * rp;
             vsh[e] = c < r ? vb[d * r + c] : 0.0f;
         }
-        if (tid < kHeadDim) msh[tid] = T.mu[grp * kHeadDim + tid];
+        if (tid < kHeadDim) msh[tid] = T.mu[slot * T.set_mu + grp * kHeadDim + tid];
     }
     __syncthreads();
     const int jp = (j0 >> 1) + u;                    // group pair of this wave
@@ -390,8 +390,8 @@ __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
 
     // 1. y = float(x) - mu and the basis -> LDS
     const uint16_t *xin = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim;
-    if (tid < kHeadDim) ys[tid] = in2f<BF16>(xin[tid]) - T.mu[grp * kHeadDim + tid];
-    const float *vb = T.basis + static_cast<int64_t>(grp) * kHeadDim * r;
+    if (tid < kHeadDim) ys[tid] = in2f<BF16>(xin[tid]) - T.mu[slot * T.set_mu + grp * kHeadDim + tid];
+    const float *vb = T.basis + slot * T.set_basis + static_cast<int64_t>(grp) * kHeadDim * r;
     for (int e = tid; e < kHeadDim * r; e += kApp1Threads) vs[e] = vb[e];
     if (complete && !T.fp16_latents)
         for (int w = tid; w < W; w += kApp1Threads) rec[w] = 0u;
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) qsc[v] = ldexpf(a.qscale, __shfl(kq, 4 * kb + v));
             }
-            const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * np * kHeadDim;
+            const uint16_t *bt = a.k.basis_t16 + slot * a.k.set_bt16 + static_cast<int64_t>(grp) * np * kHeadDim;
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 if (x == 1 && !own1) break;
@@ -1091,8 +1091,9 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
     const int qh = blockIdx.x, i = blockIdx.y;   // grid (Hq, B)
     // all argument loads issued together (one scalar round trip)
     asm volatile("" ::"s"(a.partial), "s"(a.out), "s"(a.v.basis_cm), "s"(a.v.mu), "s"(a.v.r), "s"(a.gqa),
-                 "s"(a.hpg), "s"(a.Hq), "s"(a.nsplit_call[i]));
+                 "s"(a.hpg), "s"(a.Hq), "s"(a.nsplit_call[i]), "s"(a.slot_call[i]), "s"(a.v.set_bcm), "s"(a.v.set_mu));
     const int h = qh / a.gqa, grp = h / a.hpg, ns = a.nsplit_call[i], rv = a.v.r;
+    const int64_t slot = a.slot_call[i];
     const int np = ns * (rv + 2), npa = (np + 3) & ~3;
     float *pl = cl;                            // [ns][rv + 2]: m, l, o_lat
     float *bl = cl + npa;                      // [rv][D] value basis (channel-major)
@@ -1100,8 +1101,8 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
     float *wl = ml + kHeadDim;                 // [ns] split weights
     float *ol = wl + ((ns + 3) & ~3);          // [rv] merged latent output
     const float *part = a.partial + (static_cast<int64_t>(i) * a.Hq + qh) * kMaxSplits * (rv + 2);
-    const float *bv = a.v.basis_cm + static_cast<int64_t>(grp) * rv * kHeadDim;
-    const float *mv = a.v.mu + grp * kHeadDim;
+    const float *bv = a.v.basis_cm + slot * a.v.set_bcm + static_cast<int64_t>(grp) * rv * kHeadDim;
+    const float *mv = a.v.mu + slot * a.v.set_mu + grp * kHeadDim;
 
     // 1. copy to LDS: whole 16-byte pieces of the partials, the basis
     //    (128 rv floats) and the mean; the < 4 trailing partial floats singly

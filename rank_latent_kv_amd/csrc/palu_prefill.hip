@@ -315,7 +315,7 @@ void prefill_kernel(PrefillArgs a) {
     if (nfull > 1 && ngroups > 1) copy_raw(1);
     f16x8 qb[NQ][KS];
     {
-        const uint16_t *bt = a.k.basis_t16 + static_cast<int64_t>(grp) * np * kHeadDim;
+        const uint16_t *bt = a.k.basis_t16 + rw.slot * a.k.set_bt16 + static_cast<int64_t>(grp) * np * kHeadDim;
 #pragma unroll
         for (int t = 0; t < NQ; ++t) {
             uint4 qa[4];
@@ -480,9 +480,10 @@ void prefill_kernel(PrefillArgs a) {
     float *bl = reinterpret_cast<float *>(lds + L.basis);
     float *ml = bl + kHeadDim * rv;
     {
-        const float4 *bv = reinterpret_cast<const float4 *>(a.v.basis_cm + static_cast<int64_t>(grp) * rv * kHeadDim);
+        const float4 *bv = reinterpret_cast<const float4 *>(a.v.basis_cm + rw.slot * a.v.set_bcm +
+                                                            static_cast<int64_t>(grp) * rv * kHeadDim);
         for (int e = tid; e < kHeadDim * rv / 4; e += 256) reinterpret_cast<float4 *>(bl)[e] = bv[e];
-        if (tid < kHeadDim) ml[tid] = a.v.mu[grp * kHeadDim + tid];
+        if (tid < kHeadDim) ml[tid] = a.v.mu[rw.slot * a.v.set_mu + grp * kHeadDim + tid];
     }
     __syncthreads();
 

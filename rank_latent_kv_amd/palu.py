@@ -24,6 +24,7 @@ ERROR_NAMES = {1: "PALU_ERR_INVALID_ARG", 2: "PALU_ERR_UNSUPPORTED", 3: "PALU_ER
 
 EXPORTED = ["palu_config_default", "palu_cache_create", "palu_cache_required_bytes",
             "palu_cache_bind", "palu_fit", "palu_set_basis", "palu_get_basis",
+            "palu_fit_seq", "palu_set_basis_seq", "palu_get_basis_seq",
             "palu_encode_append", "palu_decode_attend", "palu_prefill_attend", "palu_seq_len",
             "palu_read_codes",
             "palu_get_stats", "palu_reset", "palu_record_words", "palu_export_bytes",
@@ -44,7 +45,8 @@ class palu_config(ctypes.Structure):
                 ("hi_fraction", ctypes.c_float), ("group_size", ctypes.c_int32),
                 ("quantize_values", ctypes.c_int32), ("max_rank", ctypes.c_int32),
                 ("split_groups", ctypes.c_int32), ("input_dtype", ctypes.c_int32),
-                ("schedule_len", ctypes.c_int32), ("bit_schedule", ctypes.c_int32 * 8)]
+                ("schedule_len", ctypes.c_int32), ("bit_schedule", ctypes.c_int32 * 8),
+                ("per_seq_basis", ctypes.c_int32)]
 
 
 class palu_stats(ctypes.Structure):
@@ -83,6 +85,9 @@ def lib():
         "palu_fit": [_vp, _vp, _vp, _i32p, _i32, _i32, _vp],
         "palu_set_basis": [_vp, _i32, _i32, _vp, _vp],
         "palu_get_basis": [_vp, _i32, _i32p, _vp, _vp, _vp],
+        "palu_fit_seq": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, _vp],
+        "palu_set_basis_seq": [_vp, _i32, _i32, _i32, _vp, _vp],
+        "palu_get_basis_seq": [_vp, _i32, _i32, _i32p, _vp, _vp, _vp],
         "palu_encode_append": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, _vp],
         "palu_decode_attend": [_vp, _vp, _vp, _i32p, _i32, ctypes.c_float, _vp],
         "palu_prefill_attend": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, ctypes.c_float, _vp],
@@ -161,6 +166,31 @@ def palu_get_basis(cache: int, tensor: int, G: int, D: int):
     sigma = np.empty((G, D), np.float64)
     _check(lib().palu_get_basis(cache, tensor, ctypes.byref(r), basis.ctypes.data,
                                 mu.ctypes.data, sigma.ctypes.data))
+    return r.value, basis, mu, sigma
+
+
+def palu_fit_seq(cache: int, k_ptr: int, v_ptr: int, seq_ids, seq_lens, B: int, S_stride: int,
+                 stream: int):
+    s = _i32_array(seq_ids)
+    n = _i32_array(seq_lens)
+    _check(lib().palu_fit_seq(cache, k_ptr, v_ptr, s[1] if s else None, n[1] if n else None, B,
+                              S_stride, stream))
+
+
+def palu_set_basis_seq(cache: int, seq: int, tensor: int, r: int, basis: np.ndarray, mu: np.ndarray):
+    basis = np.ascontiguousarray(basis, dtype=np.float32)
+    mu = np.ascontiguousarray(mu, dtype=np.float32)
+    _check(lib().palu_set_basis_seq(cache, seq, tensor, r, basis.ctypes.data, mu.ctypes.data))
+
+
+def palu_get_basis_seq(cache: int, seq: int, tensor: int, G: int, D: int):
+    r = ctypes.c_int32()
+    _check(lib().palu_get_basis_seq(cache, seq, tensor, ctypes.byref(r), None, None, None))
+    basis = np.empty((G, D, r.value), np.float32)
+    mu = np.empty((G, D), np.float32)
+    sigma = np.empty((G, D), np.float64)
+    _check(lib().palu_get_basis_seq(cache, seq, tensor, ctypes.byref(r), basis.ctypes.data,
+                                    mu.ctypes.data, sigma.ctypes.data))
     return r.value, basis, mu, sigma
 
 
@@ -257,7 +287,8 @@ class LatentKVCache:
                  max_batch: int, max_seq_len: int, rank: int = 0, energy_threshold: float = 0.90,
                  hi_bit: int = 4, lo_bit: int = 2, hi_fraction: float = 0.25,
                  group_size: int = 32, quantize_values: bool = True, max_rank: int = 0,
-                 split_groups: int = 0, input_dtype: str = "fp16", bit_schedule=None, device=None):
+                 split_groups: int = 0, input_dtype: str = "fp16", bit_schedule=None,
+                 per_seq_basis: bool = False, device=None):
         import torch
         self.torch = torch
         cfg = palu_config_default(head_dim, n_kv_heads, n_q_heads)
@@ -279,6 +310,7 @@ class LatentKVCache:
             cfg.schedule_len = len(sched)
             for i, b in enumerate(sched):
                 cfg.bit_schedule[i] = b
+        cfg.per_seq_basis = 1 if per_seq_basis else 0
         self.cfg = cfg
         self.D, self.H, self.Hq, self.G = head_dim, n_kv_heads, n_q_heads, n_head_groups
         self.max_batch, self.max_seq_len = max_batch, max_seq_len
@@ -308,20 +340,31 @@ class LatentKVCache:
         if tuple(t.shape[-len(shape_tail):]) != tuple(shape_tail):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected [..., {shape_tail}]")
 
-    def fit(self, k, v, seq_lens: Optional[Sequence[int]] = None):
-        """k, v: fp16 [B, H, S, D]."""
+    def fit(self, k, v, seq_lens: Optional[Sequence[int]] = None, seq_ids=None):
+        """k, v: fp16 [B, H, S, D].  With per-sequence bases, row b is fitted
+        into slot seq_ids[b] (default b)."""
         self._check_half(k, (self.H, k.shape[2], self.D), "k")
         self._check_half(v, tuple(k.shape[1:]), "v")
         B, _, S, _ = k.shape
         lens = [S] * B if seq_lens is None else list(seq_lens)
-        palu_fit(self.handle, k.data_ptr(), v.data_ptr(), lens, B, S, self._stream())
+        if seq_ids is None:
+            palu_fit(self.handle, k.data_ptr(), v.data_ptr(), lens, B, S, self._stream())
+        else:
+            palu_fit_seq(self.handle, k.data_ptr(), v.data_ptr(), seq_ids, lens, B, S, self._stream())
 
-    def set_basis(self, tensor: int, basis: np.ndarray, mu: np.ndarray):
+    def set_basis(self, tensor: int, basis: np.ndarray, mu: np.ndarray, seq: Optional[int] = None):
+        """Install a basis: the shared one, every slot's (per-sequence bases,
+        seq None) or one slot's."""
         basis = np.asarray(basis, np.float32)
-        palu_set_basis(self.handle, tensor, basis.shape[-1], basis, mu)
+        if seq is None:
+            palu_set_basis(self.handle, tensor, basis.shape[-1], basis, mu)
+        else:
+            palu_set_basis_seq(self.handle, seq, tensor, basis.shape[-1], basis, mu)
 
-    def get_basis(self, tensor: int):
-        return palu_get_basis(self.handle, tensor, self.G, self.D)
+    def get_basis(self, tensor: int, seq: Optional[int] = None):
+        if seq is None:
+            return palu_get_basis(self.handle, tensor, self.G, self.D)
+        return palu_get_basis_seq(self.handle, seq, tensor, self.G, self.D)
 
     def encode_append(self, k, v, seq_ids=None, n_new=None):
         """k, v: fp16 [B, H, T, D]; appends n_new[b] (default T) tokens of row
@@ -373,8 +416,9 @@ class LatentKVCache:
         return palu_export_seq(self.handle, seq)
 
     def import_seq(self, seq: int, data: bytes):
-        """Replace one slot's contents with an exported slot; the cache must
-        hold the basis the slot was saved under."""
+        """Replace one slot's contents with an exported slot; with shared
+        bases the cache must hold the basis the slot was saved under, with
+        per-sequence bases the slot's own bases come with it."""
         palu_import_seq(self.handle, seq, data)
 
     def stats(self) -> dict:

@@ -156,3 +156,49 @@ def test_calls_before_bind_or_fit_fail_cleanly():
         assert palu.palu_seq_len(h, 1) == 0
     finally:
         palu.palu_cache_destroy(h)
+
+
+def test_per_seq_basis_config_and_host_checks():
+    with pytest.raises(palu.PaluError) as ei:
+        palu.palu_cache_create(_cfg(per_seq_basis=1), 2, 64)      # energy rule: layout unknown
+    assert ei.value.code == 2
+    with pytest.raises(palu.PaluError) as ei:
+        palu.palu_cache_create(_cfg(per_seq_basis=2, rank=8), 2, 64)
+    assert ei.value.code == 1
+    shared = palu.palu_cache_create(_cfg(rank=16), 3, 256)
+    h = palu.palu_cache_create(_cfg(per_seq_basis=1, rank=16), 3, 256)
+    one = palu.palu_cache_create(_cfg(per_seq_basis=1, rank=16), 1, 256)
+    try:
+        # the record layout is fixed at creation: rank 16 splits 4 channels
+        # at 4 bits and 12 at 2 bits, plus 16 scale/zero words
+        assert palu.palu_record_words(h, 0) == 4 * 4 + 12 * 2 + 16
+        st = palu.palu_get_stats(h)
+        assert (st.r_k, st.r_v, st.tokens, st.compressed_key_bytes) == (16, 16, 0, 0)
+        assert palu.palu_cache_required_bytes(h) > palu.palu_cache_required_bytes(one)
+        basis, mu = [0.0] * (4 * 128 * 16), [0.0] * (4 * 128)
+        for c in (h, shared):
+            palu.palu_cache_bind(c, 1 << 20, palu.palu_cache_required_bytes(c))
+        calls = [
+            (lambda: palu.palu_get_basis(h, 0, 4, 128), 1),              # no shared basis
+            (lambda: palu.palu_set_basis(h, 0, 8, basis, mu), 1),        # rank fixed at 16
+            (lambda: palu.palu_set_basis_seq(h, 3, 0, 16, basis, mu), 4),
+            (lambda: palu.palu_set_basis_seq(h, 0, 0, 8, basis, mu), 1),
+            (lambda: palu.palu_get_basis_seq(h, 0, 0, 4, 128), 3),
+            (lambda: palu.palu_fit_seq(h, 1, 1, [0, 1], [4, 0], 2, 16, 0), 1),   # empty row
+            (lambda: palu.palu_fit_seq(h, 1, 1, [1, 1], [4, 4], 2, 16, 0), 1),   # repeated slot
+            (lambda: palu.palu_fit_seq(h, 1, 1, [0, 5], [4, 4], 2, 16, 0), 4),
+            (lambda: palu.palu_encode_append(h, 1, 1, None, None, 2, 1, 0), 3),  # slots without bases
+            (lambda: palu.palu_decode_attend(h, 1, 1, None, 2, 0.0, 0), 3),
+            (lambda: palu.palu_export_bytes(h, 0), 3),
+            (lambda: palu.palu_import_seq(h, 0, b"x" * 10), 1),
+            (lambda: palu.palu_fit_seq(shared, 1, 1, [0], [4], 1, 16, 0), 1),   # shared-basis cache
+            (lambda: palu.palu_set_basis_seq(shared, 0, 0, 16, basis, mu), 1),
+            (lambda: palu.palu_get_basis_seq(shared, 0, 0, 4, 128), 1),
+        ]
+        for i, (call, code) in enumerate(calls):
+            with pytest.raises(palu.PaluError) as ei:
+                call()
+            assert ei.value.code == code, (i, ei.value)
+    finally:
+        for c in (h, shared, one):
+            palu.palu_cache_destroy(c)
