@@ -35,7 +35,9 @@ int hip_fail(hipError_t e, const char *what) {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 constexpr int kGramElems = kHeadDim * kHeadDim + kHeadDim;
-constexpr int kGramMaxRowsPerBlock = 8192;   // bounds fp32 accumulation per tile
+constexpr int kGramMaxRowsPerBlock = 8192;   // bounds fp32 accumulation per block
+// full Gram blocks per (tensor, group) at most: 1024 workgroups a fit
+inline int gram_nb_target(int G) { return std::max(1, 512 / G); }
 constexpr int kAttendTargetGroups = 1024;    // workgroups aimed for per decode launch
 constexpr size_t kAttendLdsMax = 160 * 1024; // LDS per workgroup on gfx950
 
@@ -97,7 +99,9 @@ struct palu_cache {
     palu_config cfg{};
     int max_batch = 0, max_seq_len = 0;
     int D = 0, H = 0, Hq = 0, G = 0, hpg = 0, gqa = 0, r_max = 0, max_groups = 0;
-    int gram_nb_cap = 0;
+    int gram_nb_cap = 0;          // Gram blocks (partials) of one launch
+    int64_t gram_tab_cap = 0;     // block-table entries of one fit
+    int gram_resident = 0;        // Gram workgroups the device holds at once (0: not queried yet)
     // byte offsets of each region inside the bound buffer
     size_t off_basis[2]{}, off_bt16[2]{}, off_bcm[2]{}, off_mu[2]{}, off_rec[2]{}, off_tail[2]{};
     size_t off_gram_part = 0, off_gram_out = 0, off_seg = 0, off_attend = 0, total = 0;
@@ -387,13 +391,19 @@ PALU_API int palu_cache_create(const palu_config *cfg, int32_t max_batch, int32_
             c->sigma_h[t].assign(c->nbs * c->mu_elems(), 0.0);
         }
     }
+    // Gram blocks of one fit: at most the target count of full blocks (or
+    // the count at the largest block size), plus one partial block per
+    // (sequence, head-in-group) segment
     const int64_t n_rows_max = static_cast<int64_t>(max_batch) * max_seq_len * c->hpg;
-    c->gram_nb_cap = static_cast<int>(std::max<int64_t>(
-        std::max(1, 512 / c->G), (n_rows_max + kGramMaxRowsPerBlock - 1) / kGramMaxRowsPerBlock));
+    c->gram_nb_cap = static_cast<int>(std::max<int64_t>(gram_nb_target(c->G), (n_rows_max + kGramMaxRowsPerBlock - 1) /
+                                                                                  kGramMaxRowsPerBlock) +
+                                      static_cast<int64_t>(max_batch) * c->hpg);
     c->off_gram_part = take(sizeof(float) * 2 * static_cast<size_t>(c->G) * c->gram_nb_cap * kGramElems);
     c->off_gram_out = take(sizeof(double) * 2 * static_cast<size_t>(c->G) * kGramElems);
-    // one prefix over all rows (shared fit) or one per row (per-sequence fit)
-    c->off_seg = take(sizeof(int64_t) * (static_cast<size_t>(max_batch) * (c->hpg + 1) + 1));
+    // block tables: one fit's (shared), or one per row (per-sequence fit)
+    c->gram_tab_cap = std::max<int64_t>(c->gram_nb_cap, static_cast<int64_t>(max_batch) *
+                                                            (gram_nb_target(c->G) + c->hpg));
+    c->off_seg = take(sizeof(GramBlock) * static_cast<size_t>(c->gram_tab_cap));
     // decode rows may repeat slots, so a launch can hold kMaxCallSeqs rows
     // whatever max_batch is
     c->off_attend = take(sizeof(float) * static_cast<size_t>(kMaxCallSeqs) * c->Hq * kMaxSplits * (c->r_max + 2));
@@ -424,22 +434,44 @@ PALU_API int palu_cache_bind(palu_cache *c, void *dev_buf, size_t bytes) {
 
 namespace {
 
-// Gram partials of rows [b0, b0 + B) of k / v, each row's valid tokens
-// prefixed in seg (device, B * hpg + 1 entries), reduced into the fp64
-// [2][G][D*D + D] result, whose download into gram_host is queued on s.
-int queue_gram(palu_cache *c, const void *k, const void *v, int b0, int B, int S_stride, const int64_t *seg,
-               int64_t n_rows, hipStream_t s, double *gram_host) {
-    const int nb_target = std::max(1, 512 / c->G);
-    int64_t rpb = std::max<int64_t>(kGramRowsPerBlockMin, (n_rows + nb_target - 1) / nb_target);
-    rpb = std::min<int64_t>(rpb, kGramMaxRowsPerBlock);
-    rpb = (rpb + 63) / 64 * 64;
-    const int nb = static_cast<int>((n_rows + rpb - 1) / rpb);
+// Gram blocks over rows b < B of k / v (seq_lens[b] tokens, every head of
+// the group): at most R rows of one (sequence, head-in-group) segment each,
+// R chosen for about nb_target full blocks per (tensor, group).
+void gram_blocks(const int32_t *seq_lens, int B, int hpg, int G, int nb_target, std::vector<GramBlock> &out) {
+    int64_t n_rows = 0;
+    for (int b = 0; b < B; ++b) n_rows += static_cast<int64_t>(hpg) * seq_lens[b];
+    int64_t R = std::max<int64_t>(kGramRowsPerBlockMin, (n_rows + nb_target - 1) / nb_target);
+    R = std::min<int64_t>((R + 63) / 64 * 64, kGramMaxRowsPerBlock);
+    for (int b = 0; b < B; ++b)
+        for (int hh = 0; hh < hpg; ++hh)
+            for (int64_t t0 = 0; t0 < seq_lens[b]; t0 += R)
+                out.push_back(GramBlock{b * hpg + hh, static_cast<int>(t0),
+                                        static_cast<int>(std::min<int64_t>(t0 + R, seq_lens[b])), 0});
+}
+
+// Full Gram blocks per (tensor, group): as many as the device holds at once
+// over both tensors and all groups (one round of equal blocks), within
+// gram_nb_target.
+int gram_target(palu_cache *c) {
+    if (c->gram_resident == 0) {
+        int n = 0;
+        if (gram_resident_blocks(&n) != hipSuccess || n <= 0) n = 1024;
+        c->gram_resident = n;
+    }
+    return std::max(1, std::min(gram_nb_target(c->G), c->gram_resident / (2 * c->G)));
+}
+
+// Gram partials of rows [b0, b0 + B) of k / v over the nb blocks at tab
+// (device), reduced into the fp64 [2][G][D*D + D] result, whose download
+// into gram_host is queued on s.
+int queue_gram(palu_cache *c, const void *k, const void *v, int b0, int B, int S_stride, const GramBlock *tab,
+               int nb, hipStream_t s, double *gram_host) {
     if (nb > c->gram_nb_cap) return fail(PALU_ERR_CAPACITY, "fit workspace too small for this many rows");
     const size_t row_elems = static_cast<size_t>(c->H) * S_stride * c->D;
     GramArgs ga{};
     ga.x[0] = static_cast<const uint16_t *>(k) + b0 * row_elems;
     ga.x[1] = static_cast<const uint16_t *>(v) + b0 * row_elems;
-    ga.seg_pref = seg;
+    ga.blocks = tab;
     ga.partial = reinterpret_cast<float *>(c->dev + c->off_gram_part);
     ga.B = B;
     ga.H = c->H;
@@ -448,8 +480,6 @@ int queue_gram(palu_cache *c, const void *k, const void *v, int b0, int B, int S
     ga.G = c->G;
     ga.hpg = c->hpg;
     ga.nb = nb;
-    ga.rows_per_block = static_cast<int>(rpb);
-    ga.n_rows = n_rows;
     hipError_t e = launch_gram(ga, s);
     if (e != hipSuccess) return hip_fail(e, "gram launch");
     GramReduceArgs ra{};
@@ -562,19 +592,24 @@ int fit_per_seq(palu_cache *c, const void *k, const void *v, const int32_t *ids,
         seen[slot] = 1;
         if (seq_lens[b] <= 0) return fail(PALU_ERR_INVALID_ARG, "a per-sequence fit needs at least one token per row");
     }
-    // each row's segment prefix: hpg heads of seq_lens[b] rows
-    std::vector<int64_t> pref(static_cast<size_t>(B) * (hpg + 1));
-    for (int b = 0; b < B; ++b)
-        for (int i = 0; i <= hpg; ++i) pref[static_cast<size_t>(b) * (hpg + 1) + i] = static_cast<int64_t>(i) * seq_lens[b];
-    hipError_t e = hipMemcpyAsync(c->dev + c->off_seg, pref.data(), sizeof(int64_t) * pref.size(),
+    // each row's block table, all uploaded at once
+    std::vector<GramBlock> tab;
+    std::vector<size_t> first(B + 1, 0);
+    for (int b = 0; b < B; ++b) {
+        gram_blocks(seq_lens + b, 1, hpg, G, gram_target(c), tab);
+        first[b + 1] = tab.size();
+    }
+    if (static_cast<int64_t>(tab.size()) > c->gram_tab_cap)
+        return fail(PALU_ERR_CAPACITY, "fit workspace too small for this many rows");
+    hipError_t e = hipMemcpyAsync(c->dev + c->off_seg, tab.data(), sizeof(GramBlock) * tab.size(),
                                   hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "fit segment upload");
+    if (e != hipSuccess) return hip_fail(e, "fit block table upload");
     const size_t per = 2 * static_cast<size_t>(G) * kGramElems;
     std::vector<double> gram(per * B);
-    const int64_t *seg = reinterpret_cast<const int64_t *>(c->dev + c->off_seg);
+    const GramBlock *dtab = reinterpret_cast<const GramBlock *>(c->dev + c->off_seg);
     for (int b = 0; b < B; ++b)
-        if (int err = queue_gram(c, k, v, b, 1, S_stride, seg + static_cast<size_t>(b) * (hpg + 1),
-                                 static_cast<int64_t>(hpg) * seq_lens[b], s, gram.data() + per * b))
+        if (int err = queue_gram(c, k, v, b, 1, S_stride, dtab + first[b], static_cast<int>(first[b + 1] - first[b]),
+                                 s, gram.data() + per * b))
             return err;
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "fit synchronize");
 
@@ -623,16 +658,17 @@ PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t
     c->ready[0][0] = c->ready[1][0] = 0;
     reset_seqs(c);
 
-    const int nseg = B * c->hpg;
-    std::vector<int64_t> pref(nseg + 1, 0);
-    for (int sgi = 0; sgi < nseg; ++sgi) pref[sgi + 1] = pref[sgi] + seq_lens[sgi / c->hpg];
-    const int64_t n_rows = pref[nseg];
-    hipError_t e = hipMemcpyAsync(c->dev + c->off_seg, pref.data(), sizeof(int64_t) * pref.size(),
+    const int64_t n_rows = total * c->hpg;
+    std::vector<GramBlock> tab;
+    gram_blocks(seq_lens, B, c->hpg, c->G, gram_target(c), tab);
+    if (static_cast<int64_t>(tab.size()) > c->gram_tab_cap)
+        return fail(PALU_ERR_CAPACITY, "fit workspace too small for this many rows");
+    hipError_t e = hipMemcpyAsync(c->dev + c->off_seg, tab.data(), sizeof(GramBlock) * tab.size(),
                                   hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "fit segment upload");
+    if (e != hipSuccess) return hip_fail(e, "fit block table upload");
     std::vector<double> gram(2 * static_cast<size_t>(c->G) * kGramElems);
-    if (int err = queue_gram(c, k, v, 0, B, S_stride, reinterpret_cast<const int64_t *>(c->dev + c->off_seg), n_rows,
-                             s, gram.data()))
+    if (int err = queue_gram(c, k, v, 0, B, S_stride, reinterpret_cast<const GramBlock *>(c->dev + c->off_seg),
+                             static_cast<int>(tab.size()), s, gram.data()))
         return err;
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail(e, "fit synchronize");
 

@@ -89,13 +89,16 @@ struct TensorDev {
     int64_t set_basis, set_bt16, set_bcm, set_mu;
 };
 
+// One Gram block: tokens [t0, t1) of segment seg = b * hpg + head-in-group.
+struct GramBlock {
+    int seg, t0, t1, pad;
+};
+
 struct GramArgs {
     const uint16_t *x[2];     // K, V fp16 or bf16 [B][H][S_stride][D]
-    const int64_t *seg_pref;  // [B*hpg + 1] prefix of valid rows over (b, head-in-group)
-    const int32_t *seg_len;   // unused by the kernel; kept for bounds reasoning
+    const GramBlock *blocks;  // [nb], device
     float *partial;           // [2][G][nb][D*D + D]
-    int B, H, S_stride, G, hpg, nb, rows_per_block;
-    int64_t n_rows;           // rows per group (same for every group)
+    int B, H, S_stride, G, hpg, nb;
     int bf16;                 // inputs are bf16 (else fp16)
 };
 
@@ -178,6 +181,8 @@ size_t attend_lds_bytes(int gqa, int nbk, int r_k, int r_v, int words_k, int wor
 
 // Launchers (defined in palu_kernels.hip).  They return the launch status.
 hipError_t launch_gram(const GramArgs &a, hipStream_t s);
+// Gram workgroups the current device holds at once (CUs x blocks per CU).
+hipError_t gram_resident_blocks(int *n);
 hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s);
 // One wave per (pair of touched token groups, call row x head, tensor).
 hipError_t launch_encode(const EncodeArgs &a, int max_units, hipStream_t s);

@@ -28,15 +28,19 @@ namespace {
 
 // ---------------------------------------------------------------- Gram ----
 //
-// Workgroup (block, group g, tensor) owns rows [block*rpb, (block+1)*rpb) of
-// the group's stacked rows.  Row index -> (sequence b, head in group, token)
-// through the prefix over (b, head) segments.  64-row tiles are staged in
-// LDS; wave w accumulates the 32-row band I = w of the 128 x 128 Gram matrix
-// (four 32x32 MFMA tiles) plus the column sums of feature block w (an MFMA
-// with an all-ones A operand).
+// Workgroup (block, group g, tensor) owns one block of rows: tokens
+// [t0, t1) of one (sequence, head-in-group) segment, so its rows are
+// consecutive in memory.  64-row tiles go global -> registers -> LDS,
+// transposed to feature-major order (two rows per 32-bit word) so that an
+// MFMA operand (8 rows of one feature) is one 16-byte LDS read; the loads of
+// the next two tiles are in flight while the current one is multiplied (two
+// register buffers, two LDS buffers, one barrier per tile).  Wave w accumulates the 32-row band I = w
+// of the 128 x 128 Gram matrix (four 32x32 MFMA tiles) plus the column sums
+// of feature block w (an MFMA with an all-ones A operand).
 
-constexpr int kGramTile = 64;
-constexpr int kGramPad = 136;   // LDS row stride in halves
+constexpr int kGramTile = 64;      // rows per tile
+constexpr int kGramTStride = 72;   // LDS halves per feature run of a tile (64 rows + 8; 16-byte aligned,
+                                   // 36 words = 4 mod 32 keeps 8 lanes' 16-byte reads on distinct banks)
 
 // bf16 rows use the bf16 MFMA: bf16 x bf16 products are exact in fp32 just
 // like fp16 x fp16.
@@ -45,54 +49,68 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 template <bool BF16>
 __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
     const int blk = blockIdx.x, g = blockIdx.y, tz = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int64_t row0 = static_cast<int64_t>(blk) * a.rows_per_block;
-    const int64_t row1 = row0 + a.rows_per_block < a.n_rows ? row0 + a.rows_per_block : a.n_rows;
-    const uint16_t *x = a.x[tz];
-    const int nseg = a.B * a.hpg;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const GramBlock bd = a.blocks[blk];
+    const int sb = bd.seg / a.hpg, hh = bd.seg - sb * a.hpg;
+    const int nrows = bd.t1 - bd.t0;
+    const uint16_t *src =
+        a.x[tz] + ((static_cast<int64_t>(sb) * a.H + g * a.hpg + hh) * a.S_stride + bd.t0) * kHeadDim;
 
-    __shared__ uint16_t tile[kGramTile][kGramPad];
+    __shared__ __align__(16) uint32_t tt[2][kHeadDim][kGramTStride / 2];
 
-    f32x16 acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {}, accs = {};
-    // operand element type of the input; 1.0 is 0x3C00 in fp16, 0x3F80 in bf16
     using vec8 = typename std::conditional<BF16, bf16x8, f16x8>::type;
     using elem = typename std::conditional<BF16, __bf16, _Float16>::type;
-    const uint16_t one_bits = BF16 ? 0x3F80 : 0x3C00;
+    const uint16_t one_bits = BF16 ? 0x3F80 : 0x3C00;   // 1.0
     vec8 ones;
     for (int u = 0; u < 8; ++u) ones[u] = __builtin_bit_cast(elem, one_bits);
 
-    for (int64_t base = row0; base < row1; base += kGramTile) {
-        for (int k = 0; k < 4; ++k) {
-            const int id = tid + 256 * k;
-            const int rr = id >> 4, fc = id & 15;
-            const int64_t row = base + rr;
-            uint4 val = make_uint4(0u, 0u, 0u, 0u);
-            if (row < row1) {
-                int lo = 0, hi = nseg - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (a.seg_pref[mid] <= row) lo = mid; else hi = mid - 1;
-                }
-                const int b = lo / a.hpg, hh = lo - b * a.hpg;
-                const int64_t t = row - a.seg_pref[lo];
-                const uint16_t *src =
-                    x + ((static_cast<int64_t>(b) * a.H + g * a.hpg + hh) * a.S_stride + t) * kHeadDim +
-                    fc * 8;
-                val = *reinterpret_cast<const uint4 *>(src);
-            }
-            *reinterpret_cast<uint4 *>(&tile[rr][fc * 8]) = val;
+    // loads: thread (w, lane) takes rows 2p, 2p + 1 (p = lane % 32) and the
+    // 16-byte feature chunks c0, c0 + 1 (c0 = 4 w + 2 (lane / 32)); rows past
+    // the block read as zero
+    const int p = lane & 31, c0 = 4 * w + 2 * (lane >> 5);
+    // two register buffers [row of the pair][chunk], for even and odd tiles
+    uint4 buf0[2][2], buf1[2][2];
+    auto load = [&](int t, uint4 (&bt)[2][2]) {
+#pragma unroll
+        for (int rp = 0; rp < 2; ++rp) {
+            const int r = t * kGramTile + 2 * p + rp;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                bt[rp][c] = r < nrows ? *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(r) * kHeadDim +
+                                                                         8 * (c0 + c))
+                                      : make_uint4(0u, 0u, 0u, 0u);
         }
-        __syncthreads();
-        for (int ks = 0; ks < kGramTile / 16; ++ks) {
-            const int rb = ks * 16 + (lane >> 5) * 8;
-            const int f = lane & 31;
-            vec8 o0, o1, o2, o3;
-            for (int u = 0; u < 8; ++u) {
-                o0[u] = __builtin_bit_cast(elem, tile[rb + u][f]);
-                o1[u] = __builtin_bit_cast(elem, tile[rb + u][32 + f]);
-                o2[u] = __builtin_bit_cast(elem, tile[rb + u][64 + f]);
-                o3[u] = __builtin_bit_cast(elem, tile[rb + u][96 + f]);
+    };
+    // word p of feature f's run = (row 2p, row 2p + 1) of feature f
+    auto store = [&](int t, const uint4 (&bt)[2][2]) {
+        uint32_t(*T)[kGramTStride / 2] = tt[t & 1];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const uint32_t r0[4] = {bt[0][c].x, bt[0][c].y, bt[0][c].z, bt[0][c].w};
+            const uint32_t r1[4] = {bt[1][c].x, bt[1][c].y, bt[1][c].z, bt[1][c].w};
+            const int f0 = 8 * (c0 + c);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                T[f0 + 2 * u][p] = __builtin_amdgcn_perm(r1[u], r0[u], 0x05040100u);
+                T[f0 + 2 * u + 1][p] = __builtin_amdgcn_perm(r1[u], r0[u], 0x07060302u);
             }
+        }
+    };
+
+    f32x16 acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {}, accs = {};
+    const int ntile = (nrows + kGramTile - 1) / kGramTile;
+    const int f = lane & 31, kh = lane >> 5;
+    auto tile = [&](int t) {
+        const uint32_t(*T)[kGramTStride / 2] = tt[t & 1];
+#pragma unroll
+        for (int ks = 0; ks < kGramTile / 16; ++ks) {
+            // operand of feature 32 j + f: rows 16 ks + 8 kh .. + 7 (words 8 ks + 4 kh .. + 3)
+            uint4 q[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) q[j] = *reinterpret_cast<const uint4 *>(&T[32 * j + f][8 * ks + 4 * kh]);
+            const vec8 o0 = __builtin_bit_cast(vec8, q[0]), o1 = __builtin_bit_cast(vec8, q[1]);
+            const vec8 o2 = __builtin_bit_cast(vec8, q[2]), o3 = __builtin_bit_cast(vec8, q[3]);
             const vec8 oa = w == 0 ? o0 : w == 1 ? o1 : w == 2 ? o2 : o3;
             if constexpr (BF16) {
                 acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, o0, acc0, 0, 0, 0);
@@ -108,7 +126,27 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
                 accs = __builtin_amdgcn_mfma_f32_32x32x16_f16(ones, oa, accs, 0, 0, 0);
             }
         }
+    };
+    // tile t: store it from its register buffer, refill that buffer with
+    // tile t + 2, barrier (tile t stored; every wave is past tile t - 1,
+    // whose LDS buffer the next store reuses), multiply
+    if (ntile > 0) load(0, buf0);
+    if (ntile > 1) load(1, buf1);
+    int t = 0;
+    for (; t + 1 < ntile; t += 2) {
+        store(t, buf0);
+        if (t + 2 < ntile) load(t + 2, buf0);
         __syncthreads();
+        tile(t);
+        store(t + 1, buf1);
+        if (t + 3 < ntile) load(t + 3, buf1);
+        __syncthreads();
+        tile(t + 1);
+    }
+    if (t < ntile) {
+        store(t, buf0);
+        __syncthreads();
+        tile(t);
     }
 
     constexpr int kElems = kHeadDim * kHeadDim + kHeadDim;
@@ -133,8 +171,17 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(GramReduceArgs a) {
     if (e >= kElems) return;
     const int g = blockIdx.y, tz = blockIdx.z;
     const float *p = a.partial + (static_cast<int64_t>(tz) * a.G + g) * a.nb * kElems + e;
+    // blocks in order; loads issued eight at a time
     double s = 0.0;
-    for (int b = 0; b < a.nb; ++b) s += static_cast<double>(p[static_cast<int64_t>(b) * kElems]);
+    int b = 0;
+    for (; b + 8 <= a.nb; b += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = p[static_cast<int64_t>(b + u) * kElems];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += static_cast<double>(x[u]);
+    }
+    for (; b < a.nb; ++b) s += static_cast<double>(p[static_cast<int64_t>(b) * kElems]);
     a.out[(static_cast<int64_t>(tz) * a.G + g) * kElems + e] = s;
 }
 
@@ -1185,6 +1232,17 @@ __global__ __launch_bounds__(256) void basis_t16_kernel(const float *src, uint16
 }
 
 }  // namespace
+
+hipError_t gram_resident_blocks(int *n) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(gram_kernel<false>), 256,
+                                                         0);
+    *n = cus * per_cu;
+    return e;
+}
 
 hipError_t launch_gram(const GramArgs &a, hipStream_t s) {
     if (a.bf16) hipLaunchKernelGGL(gram_kernel<true>, dim3(a.nb, a.G, 2), dim3(256), 0, s, a);
