@@ -10,7 +10,9 @@ All inputs are resident in HBM before the timed region.
 
 `value` is decode-attend throughput: sequences x decode steps per second of
 decode-attend time, measured with HIP events recorded on the stream the
-library launches on, around every decode-attend call.  The roofline object
+library launches on, around every decode-attend call.  The events are
+created without the system-scope fence a default HIP event adds (its cache
+writeback and invalidation would otherwise land between the timed kernels).  The roofline object
 prices the decode-attend call against MI355X's 8 TB/s HBM with the
 algorithmic bytes of each call (packed codes + metadata + fp32 tails + bases
 and means + query and output).  The CPU baseline times the plain oracle's
@@ -62,7 +64,7 @@ def attend_bytes(lens, H, Hq, D, G, wk, rk, wv, rv, vq, basis_sets=1):
     return tot
 
 
-KERNEL_SRC = os.path.join(ROOT, "rank_latent_kv_amd", "csrc", "palu_kernels.hip")
+KERNEL_SRC = os.path.join(ROOT, "rank_latent_kv_amd", "csrc", "palu_decode.hip")
 PROFILE = os.path.join(ROOT, "profiles", "decode_attend_long_b4_s32768_e90.md")
 
 
@@ -80,6 +82,47 @@ def measured_traffic(workload):
             if parts.get("kernel_sha256") == src:
                 return int(parts["bytes"])
     return None
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence
+    in the HIP runtime torch has loaded (its streams are only valid there)."""
+    _lib = None
+
+    @classmethod
+    def _hip(cls):
+        if cls._lib is None:
+            import ctypes
+            path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+            L = ctypes.CDLL(path)
+            L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._lib = L
+        return cls._lib
+
+    def __init__(self):
+        import ctypes
+        self.ev = ctypes.c_void_p()
+        if self._hip().hipEventCreateWithFlags(ctypes.byref(self.ev), 0x20000000) != 0:   # hipEventDisableSystemFence
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if self._hip().hipEventRecord(self.ev, stream.cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        """milliseconds from this event to `end` (both complete)"""
+        import ctypes
+        ms = ctypes.c_float()
+        if self._hip().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._lib is not None and self.ev:
+            self._lib.hipEventDestroy(self.ev)
 
 
 def copy_calibration():
@@ -171,26 +214,25 @@ def main():
     out_pre = torch.empty_like(qpre)
     stream = torch.cuda.current_stream(dev)
 
-    def one_pass(record):
+    # every timing event of a pass is created up front, so that no event
+    # creation sits between the calls it brackets
+    pass_events = [[tuple(TimingEvent() for _ in range(3)) for _ in range(T)] + [tuple(TimingEvent() for _ in range(3))]
+                   for _ in range(args.steps + args.warmup)]
+
+    def one_pass(pi):
         ev = []
-        e_fit0 = torch.cuda.Event(enable_timing=True)
-        e_fit0.record(stream)
         torch.cuda.synchronize()       # the fit is host-synchronous: time it alone
         t_fit = time.perf_counter()
         cache.fit(kpre, vpre, lens)
         t_fit = time.perf_counter() - t_fit
-        e_enc0 = torch.cuda.Event(enable_timing=True)
-        e_enc1 = torch.cuda.Event(enable_timing=True)
+        e_enc0, e_enc1, e_pre1 = pass_events[pi][T]
         e_enc0.record(stream)
         cache.encode_append(kpre, vpre, n_new=lens)
         e_enc1.record(stream)
         cache.prefill_attend(qpre, n_q=lens, out=out_pre)
-        e_pre1 = torch.cuda.Event(enable_timing=True)
         e_pre1.record(stream)
         for t in range(T):
-            ea = torch.cuda.Event(enable_timing=True)
-            eb = torch.cuda.Event(enable_timing=True)
-            ec = torch.cuda.Event(enable_timing=True)
+            ea, eb, ec = pass_events[pi][t]
             ea.record(stream)
             cache.encode_append(kdec[t], vdec[t])
             eb.record(stream)
@@ -199,14 +241,14 @@ def main():
             ev.append((ea, eb, ec))
         return t_fit, (e_enc0, e_enc1, e_pre1), ev
 
-    for _ in range(args.warmup):
-        one_pass(False)
+    for wi in range(args.warmup):
+        one_pass(args.steps + wi)
     torch.cuda.synchronize()
 
     fit_s, enc_ms, pre_ms, app_ms, att_ms = [], [], [], [], []
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    results = [one_pass(True) for _ in range(args.steps)]
+    results = [one_pass(pi) for pi in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     for t_fit, (e0, e1, e2), ev in results:

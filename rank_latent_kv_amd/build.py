@@ -24,11 +24,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
 DEVICE = [f"--offload-arch={ARCH}", "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_SOURCES = ["palu_host.cpp", "palu_eigen.cpp"]
-DEVICE_SOURCES = ["palu_kernels.hip", "palu_prefill.hip"]
-# Per-source extras.  The prefill kernel's inputs are never NaN (reading the
-# max of MFMA results needs no quieting), and its MFMA accumulators stay in
-# ordinary VGPRs (no AGPR copies around the softmax).
-SOURCE_FLAGS = {"palu_prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+DEVICE_SOURCES = ["palu_kernels.hip", "palu_decode.hip", "palu_prefill.hip"]
+# Per-source extras.  The attention kernels' inputs are never NaN (reading
+# the max of MFMA results needs no quieting), and their MFMA accumulators
+# stay in ordinary VGPRs (no AGPR copies around the softmax).
+SOURCE_FLAGS = {"palu_prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "palu_decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _run(cmd, verbose):

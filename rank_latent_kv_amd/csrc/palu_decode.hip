@@ -1,0 +1,813 @@
+// Decode attention over the latent cache, for gfx950 (MI355X).
+//
+//   attend_kernel / combine_kernel : single-query decode attention computed
+//       from the stored latents (PALU page, "How it works", decode step 3)
+//       with the query absorbed into the key basis, split over token ranges,
+//       then merged by log-sum-exp and projected back with the value basis.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "palu_device.h"
+#include "palu_internal.h"
+
+namespace palu {
+
+namespace {
+
+// -------------------------------------------------------------- attend ----
+//
+// Workgroup = (call row i, kv head h, split s).  Split s covers complete
+// token groups [s*chunk, min(nfull, (s+1)*chunk)); the last split also
+// covers the incomplete group (fp32 tail latents).  With the query absorbed
+// into the key basis, score_t = qs * q . (V_K l_t + mu_K) = qt . l_t + const
+// with qt = qs V_K^T q (qs = scale * log2 e); the constant q . mu_K is the
+// same for every token of a head and cancels in the softmax.
+//
+// Each wave owns 16 "streams" n = slot * g + head: per iteration it takes
+// S = 16 / g consecutive token groups (slots) and runs, for both 16-token
+// halves of the groups,
+//   scores  D[t][n] = sum_k A[t][k] B[k][n]    (v_mfma_f32_16x16x32_f16)
+// where k runs over (slot, 8-channel block) pairs, A holds the token's
+// latents of that block dequantised to fp16 (code * scale16 + zero16 with
+// packed fp16 arithmetic), and B is the block-diagonal constant qt in fp16
+// (B[(slot j, block)][n] = qt[head(n)][block] if j == slot(n), else 0), so
+// every output lane is a useful score.  Values use a second MFMA per slot,
+//   O[n][c] += sum_t p[n][t] lv[t][c],
+// with A = softmax weights of the slot's streams (fp16) and B = that group's
+// dequantised value latents.  The online softmax keeps one running max per
+// stream and rescales only when a new block maximum exceeds it by more than
+// kRescaleSlack (log2 units), so weights stay <= 2^kRescaleSlack.
+//
+// Channel order inside an 8-channel block follows the code extraction:
+// halves [c0, c4, c1, c5, c2, c6, c3, c7]; A and B use the same order.
+
+constexpr int kWaves = 4;
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kStageBudgetWords = 24 * 1024;   // both record buffers together (96 KiB)
+
+// LDS layout of one attend workgroup (byte offsets).  Shared by the kernel
+// and the host, which sizes the dynamic LDS from it.
+struct AttendLds {
+    int qt, qt16, kpw, blk, stage, sb;           // sb: words per stage buffer
+    int pp;                                      // token groups per pass
+    int ts, mst, lst, ost, tp;                   // merge state: byte offsets inside a stage buffer
+    int total, nbk, nub;
+};
+
+
+// Dynamic LDS of one attend workgroup; the same for every split size.
+__host__ __device__ inline AttendLds attend_lds(int g, int nbk, int rk, int rv, int wk, int wv, bool vq) {
+    AttendLds L;
+    const int S = 16 / g, P = kWaves * S;
+    L.nbk = nbk;
+    L.nub = (S * L.nbk + 3) / 4;
+    int o = 0;
+    L.qt = lds_take(o, g * kHeadDim * 4);
+    L.qt16 = lds_take(o, g * 16 * 16);
+    L.kpw = lds_take(o, kWaves * S * L.nbk * 8 * 4);
+    L.blk = lds_take(o, L.nbk * 16);             // key block addressing (base, stride, width, channels)
+    // two stage buffers.  Each holds one pass of records (+ 16-byte
+    // alignment slack); a pass is the 4 S groups the waves take, fewer when
+    // that would not fit the budget.  The last split's tail latents go to
+    // the buffer its last pass leaves free, and after the main loop the
+    // other buffer holds the merge state.
+    const int rec_words = wk + (vq ? wv : 0);
+    const int fit = (kStageBudgetWords / 2 - 16) / rec_words;
+    L.pp = fit < P ? (fit > 1 ? fit : 1) : P;
+    int m = 0;
+    L.ts = lds_take(m, g * (kWaves * 16 + 1) * 4);
+    L.mst = lds_take(m, (kWaves + 1) * 16 * 4);
+    L.lst = lds_take(m, (kWaves + 1) * 16 * 4);
+    L.ost = lds_take(m, (kWaves + 1) * 16 * rv * 4);
+    L.tp = lds_take(m, g * 32 * 4);
+    int sb = L.pp * rec_words + 16;
+    const int tail_words = 32 * rk + (vq ? 32 * rv : 16 * rv);
+    sb = sb > tail_words ? sb : tail_words;
+    sb = sb > m / 4 ? sb : m / 4;
+    L.sb = (sb + 3) & ~3;
+    L.stage = lds_take(o, 2 * L.sb * 4);
+    L.total = o;
+    return L;
+}
+
+
+// Workgroup = (call row i, kv head h, split s); see the section comment.
+// GEN = false serves PALU-shaped layouts (a 4-bit segment, then 2-bit
+// channels) with closed-form record addressing; GEN = true any coder, through
+// a per-block address table in LDS.
+// G = query heads per kv head, NBV = value-channel blocks of 16.  A split is
+// processed in passes of up to 4 S token groups (S per wave); the records of
+// pass p + 1 are copied global -> LDS (direct 16-byte loads into LDS, no
+// registers) into the other of two buffers while pass p is computed.
+template <int G, int NBV, bool VQ, bool GEN>
+__global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
+    constexpr int g = G, S = 16 / G, NS = S * G;
+    constexpr bool vq = VQ;                      // V stored as mixed-bit codes
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int ln = lane & 15, kb = lane >> 4;
+
+    // ---- work item: grid (split, kv head, row); one 16-byte row descriptor
+    const int s = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+    const AttendRow rw = a.row[i];
+    // Pin the kernel arguments the prologue needs before the first branch so
+    // their scalar loads are issued together (one round trip instead of a
+    // chain of dependent ones).
+    asm volatile("" ::"s"(a.k.records), "s"(a.v.records), "s"(a.k.tail), "s"(a.v.tail), "s"(a.k.basis_t16),
+                 "s"(a.q), "s"(a.k.head_stride), "s"(a.v.head_stride), "s"(a.k.r), "s"(a.k.cd.meta0), "s"(a.k.words),
+                 "s"(a.v.r), "s"(a.v.cd.meta0), "s"(a.v.words), "s"(a.v.fp16_latents), "s"(a.chunk), "s"(a.hpg),
+                 "s"(a.Hq), "s"(a.Hkv), "s"(a.qscale), "s"(rw.slot), "s"(rw.len), "s"(rw.qi), "s"(rw.sel_ns));
+    const int ns = rw.sel_ns >> 1, qi = rw.qi;
+    if (s >= ns) return;                          // whole workgroup: no barrier reached
+    const int slot = rw.slot, len = rw.len;
+    const int nfull = len >> 5, ntail = len & 31;
+    const int jb = s * a.chunk;
+    const int je = jb + a.chunk < nfull ? jb + a.chunk : nfull;
+    const int ntg = je > jb ? je - jb : 0;
+    const bool do_tail = (s == ns - 1) && ntail > 0;
+    const int grp = h / a.hpg;
+    const int rk = a.k.r;
+    const int rv = a.v.r;
+    const int WK = a.k.words, WV = a.v.words;
+    const int kmeta = a.k.cd.meta0, vmeta = a.v.cd.meta0;
+    // PALU-shaped layouts: nhk 4-bit channels, then 2-bit ones
+    const int nhk = a.k.cd.bits[0] == 4 ? a.k.cd.c0[1] : 0, nlk = rk - nhk, nbh = (nhk + 7) >> 3;
+    const int nhv = a.v.cd.bits[0] == 4 ? a.v.cd.c0[1] : 0;
+
+    const AttendLds L = attend_lds(g, coder_blocks(a.k.cd), rk, rv, WK, WV, vq);
+    const int nbk = L.nbk, nub = L.nub, npair = S * nbk;
+    const int PP = L.pp;                          // groups per pass (<= P)
+    const int npass = (ntg + PP - 1) / PP;
+    float *qt = reinterpret_cast<float *>(lds + L.qt);
+    uint4 *qt16 = reinterpret_cast<uint4 *>(lds + L.qt16);
+    _Float16 *qt16h = reinterpret_cast<_Float16 *>(lds + L.qt16);
+    uint32_t *kpw = reinterpret_cast<uint32_t *>(lds + L.kpw) + wv * (S * nbk * 8);   // this wave's
+    // stage buffer tb holds the tail latents (the one the last pass leaves
+    // free); after the main loop the other one holds the merge state
+    const int tb = npass & 1;
+    const int tail_off = L.stage + tb * L.sb * 4, post = L.stage + (1 - tb) * L.sb * 4;
+    const uint32_t *tails = reinterpret_cast<const uint32_t *>(lds + tail_off);
+    float *ts = reinterpret_cast<float *>(lds + post + L.ts);
+    float *mst = reinterpret_cast<float *>(lds + post + L.mst);
+    float *lst = reinterpret_cast<float *>(lds + post + L.lst);
+    float *ost = reinterpret_cast<float *>(lds + post + L.ost);
+    float *tp = reinterpret_cast<float *>(lds + post + L.tp);
+
+    const int64_t hb = static_cast<int64_t>(slot) * a.Hkv + h;
+    const uint32_t *kg = a.k.records + hb * a.k.head_stride;
+    const uint32_t *vg = a.v.records + hb * a.v.head_stride;
+
+    // ---- 1. copies global -> LDS: a pass of records (K records, then V
+    //         records; each block starts at the 16-byte boundary at or below
+    //         its first word) and, in the last split, the tail latents
+    auto pass_words = [&](int p, int &nk4, int &nv4, int &koff, int &voff) {
+        const int64_t g0 = jb + p * PP, g1 = g0 + PP < je ? g0 + PP : je;
+        const int64_t ka = (g0 * WK) & ~3LL, va = (g0 * WV) & ~3LL;
+        nk4 = static_cast<int>((g1 * WK - ka + 3) >> 2);
+        nv4 = vq ? static_cast<int>((g1 * WV - va + 3) >> 2) : 0;
+        koff = static_cast<int>(g0 * WK - ka);
+        voff = 4 * nk4 + static_cast<int>(g0 * WV - va);
+    };
+    auto copy_pass = [&](int p) {
+        int nk4, nv4, koff, voff;
+        pass_words(p, nk4, nv4, koff, voff);
+        const int64_t g0 = jb + p * PP;
+        const u4v *ks = reinterpret_cast<const u4v *>(kg + ((g0 * WK) & ~3LL));
+        const u4v *vs = reinterpret_cast<const u4v *>(vg + ((g0 * WV) & ~3LL));
+        const int n4 = nk4 + nv4, boff = L.stage + (p & 1) * L.sb * 4;
+        for (int c = wv; c * 64 < n4; c += kWaves) {
+            const int e = c * 64 + lane;
+            if (e < n4)
+                __builtin_amdgcn_global_load_lds(e < nk4 ? ks + e : vs + (e - nk4), lds + boff + c * 1024, 16, 0, 0);
+        }
+    };
+    const int64_t tsel = (hb * 2 + (rw.sel_ns & 1)) * kTokGroup;
+    const int tk_words = do_tail ? min((ntail * rk + 3) & ~3, kTokGroup * rk) : 0;
+    const int tv_words = do_tail ? (vq ? min((ntail * rv + 3) & ~3, kTokGroup * rv) : 16 * rv) : 0;
+    auto copy_tail = [&]() {
+        const u4v *tks = reinterpret_cast<const u4v *>(a.k.tail + tsel * rk);
+        const u4v *tvs = vq ? reinterpret_cast<const u4v *>(a.v.tail + tsel * rv)
+                            : reinterpret_cast<const u4v *>(vg + static_cast<int64_t>(nfull) * WV);
+        const int ntk4 = tk_words >> 2, n4 = ntk4 + (tv_words >> 2);
+        for (int c = wv; c * 64 < n4; c += kWaves) {
+            const int e = c * 64 + lane;
+            if (e < n4)
+                __builtin_amdgcn_global_load_lds(e < ntk4 ? tks + e : tvs + (e - ntk4), lds + tail_off + c * 1024, 16,
+                                                 0, 0);
+        }
+    };
+    if (npass > 0) copy_pass(0);
+    else if (do_tail) copy_tail();
+
+    // ---- 2. absorbed query qt = qs V_K^T q on MFMA: rows = query heads of
+    //         this kv head, K = d, columns = 16 score-operand positions of
+    //         the position-ordered fp16 key basis (wave w takes blocks w and
+    //         w + 4).  The result goes straight to the fp16 score operand
+    //         qt16[head][position] (padding positions come out 0) and, for
+    //         the tail stream, to fp32 qt[head][channel]; only the waves
+    //         that own a block load the query and the basis.
+    {
+        const int np = 8 * nbk;                      // positions (<= 128)
+        const int nbc = (np + 15) >> 4;              // 16-position blocks (<= 8)
+        const bool own0 = wv < nbc, own1 = wv + kWaves < nbc;
+        if (own0) {
+            const int qrow = qi * a.Hq + h * g;
+            // rows ln >= g repeat a valid query; their MFMA output rows are never stored
+            const uint16_t *qsrc = a.q + static_cast<int64_t>(qrow + (ln < g ? ln : 0)) * kHeadDim + 8 * kb;
+            uint4 qa[4], bb[2][4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) qa[st] = *reinterpret_cast<const uint4 *>(qsrc + 32 * st);
+            // bf16 queries: exact per-row power-of-two rescale into fp16,
+            // undone on the MFMA result (output row 4 kb + v = query row)
+            float qsc[4] = {a.qscale, a.qscale, a.qscale, a.qscale};
+            if (a.bf16) {
+                const int kq = bf16_rows_to_fp16(qa);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) qsc[v] = ldexpf(a.qscale, __shfl(kq, 4 * kb + v));
+            }
+            const uint16_t *bt = a.k.basis_t16 + slot * a.k.set_bt16 + static_cast<int64_t>(grp) * np * kHeadDim;
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                if (x == 1 && !own1) break;
+                int n = 16 * (wv + kWaves * x) + ln;
+                n = n < np ? n : np - 1;              // clamped rows are never stored
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    bb[x][st] = *reinterpret_cast<const uint4 *>(bt + static_cast<int64_t>(n) * kHeadDim + 32 * st +
+                                                                 8 * kb);
+            }
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                if (x == 1 && !own1) break;
+                f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(qa[st].x, qa[st].y, qa[st].z, qa[st].w),
+                                                                as_h8(bb[x][st].x, bb[x][st].y, bb[x][st].z,
+                                                                      bb[x][st].w),
+                                                                acc, 0, 0, 0);
+                const int n = 16 * (wv + kWaves * x) + ln;
+                const int q = n >> 3, idx = n & 7;
+                const KBlock kbq = key_block(a.k.cd, q < nbk ? q : nbk - 1);
+                const int chan0 = kbq.chan0, chanend = kbq.chanend;
+                const int c = chan0 + (idx >> 1) + 4 * (idx & 1);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int hh = 4 * kb + v;
+                    if (hh < g && n < np) {
+                        const float val = acc[v] * qsc[v];
+                        qt16h[hh * np + n] = static_cast<_Float16>(val);
+                        if (c < chanend) qt[hh * rk + c] = val;
+                    }
+                }
+            }
+        }
+    }
+    // ---- 3. key block addressing table (one entry per 8-channel block)
+    int4 *blk = reinterpret_cast<int4 *>(lds + L.blk);
+    if (GEN && tid < nbk) {
+        const KBlock b = key_block(a.k.cd, tid);
+        blk[tid] = make_int4(b.base, b.stride, b.w, b.chan0 | (b.chanend << 16));
+    }
+    __builtin_amdgcn_s_waitcnt(0);                    // this wave's copies have landed
+    __syncthreads();
+
+    // ---- 4. main loop: passes of PP token groups, wave w takes pass-relative
+    //         groups [w S, w S + S)
+    const int slot_n = ln / g, head_n = ln - (ln / g) * g;
+    const bool live_n = ln < NS;
+    float m_run = -INFINITY, l_run = 0.0f;
+    f4 oacc[NBV];
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) oacc[nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
+    // per-lane value-channel addressing (column c = 16 nb + ln, clamped)
+    int vch[NBV], vw0[NBV], vw1[NBV], vs0[NBV], vs1[NBV], vwid[NBV], vwc[NBV];
+    uint32_t vcm[NBV];
+    int row_slot[4];                                 // slot of value-output row 4*kb + v
+#pragma unroll
+    for (int v = 0; v < 4; ++v) row_slot[v] = (4 * kb + v) / g;
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) {
+        int c = 16 * nb + ln;
+        c = c < rv ? c : rv - 1;
+        int2 vc = make_int2(0, 2);                   // base bit, width
+        if constexpr (VQ && GEN) vc = value_channel(a.v.cd, c);
+        else if constexpr (VQ) vc = c < nhv ? make_int2(128 * c, 4) : make_int2(128 * nhv + 64 * (c - nhv), 2);
+        const int wc = vc.y;
+        const int b0 = vc.x + 4 * kb * wc, b1 = b0 + 16 * wc;
+        vch[nb] = c;
+        vw0[nb] = b0 >> 5;
+        vw1[nb] = b1 >> 5;
+        vs0[nb] = b0 & 31;
+        vs1[nb] = b1 & 31;          // differs from vs0 only for 1-bit codes (b1 - b0 = 16 wc)
+        vwid[nb] = 4 * wc;          // 4 tokens; width 8 takes whole words instead
+        vwc[nb] = wc;
+        const uint32_t m = (1u << wc) - 1u;
+        vcm[nb] = m | (m << 16);
+    }
+    const uint32_t kmagic = vgpr_const(0x64006400u), km4 = vgpr_const(0x000F000Fu),
+                   km2 = vgpr_const(0x00030003u);
+    const FastDiv div_nbk4(a.inv_nbk4);
+    const int tb0 = wv * S;                          // pass-relative group of slot 0
+    for (int pi = 0; pi < npass; ++pi) {
+        if (pi + 1 < npass) copy_pass(pi + 1);       // into the other buffer
+        else if (do_tail) copy_tail();               // the last pass leaves buffer tb free
+        int nk4, nv4, koff, voff;
+        pass_words(pi, nk4, nv4, koff, voff);
+        const int npg = min(PP, ntg - pi * PP);      // groups in this pass (>= 1)
+        const int64_t g0 = jb + pi * PP;             // absolute group of pass group 0
+        const uint32_t *stage = reinterpret_cast<const uint32_t *>(lds + L.stage) + (pi & 1) * L.sb;
+
+        // (a) this wave's K scale/zero pairs per (slot, channel block):
+        //     words 0..3 scale pairs (k, k + 4), words 4..7 zero pairs;
+        //     padding channels are 0; slots past the pass repeat its last group
+        for (int e = lane; e < S * nbk * 4; e += 64) {
+            const int m = div_nbk4.quo(e), r2 = e - m * nbk * 4;
+            const int q = r2 >> 2, k = r2 & 3;
+            int chan0, chanend;
+            if constexpr (GEN) {
+                const int cc = blk[q].w;
+                chan0 = cc & 0xFFFF;
+                chanend = cc >> 16;
+            } else {
+                chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
+                chanend = q < nbh ? nhk : rk;
+            }
+            int tg = tb0 + m;
+            tg = tg < npg ? tg : npg - 1;
+            const uint32_t *rec = stage + koff + tg * WK + kmeta;
+            const uint32_t wa = chan0 + k < chanend ? rec[chan0 + k] : 0u;
+            const uint32_t wb = chan0 + k + 4 < chanend ? rec[chan0 + k + 4] : 0u;
+            uint32_t *dst = kpw + (m * nbk + q) * 8;
+            dst[k] = perm_b32(wb, wa, 0x05040100u);
+            dst[4 + k] = perm_b32(wb, wa, 0x07060302u);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // (b) scores
+        f4 sacc0 = {0.0f, 0.0f, 0.0f, 0.0f}, sacc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int u = 0; u < nub; ++u) {
+            const int p = 4 * u + kb;
+            int q, j;
+            if constexpr (S % 4 == 0) {
+                q = (4 * u) / S;            // the same for every lane of the wave
+                j = p - q * S;
+            } else {
+                q = p / S;
+                j = p - q * S;
+            }
+            // invalid pairs and groups past the pass are read from a valid
+            // (clamped) record; their scores belong to masked streams
+            int tg = tb0 + j;
+            tg = tg < npg ? tg : npg - 1;
+            const int qc = q < nbk ? q : nbk - 1;
+            const uint32_t *rec = stage + koff + tg * WK;
+            const uint4 *kp = reinterpret_cast<const uint4 *>(kpw + (j * nbk + qc) * 8);
+            const uint4 sp = kp[0], zp = kp[1];
+            const bool ok = p < npair && live_n && j == slot_n;
+            const uint4 bq = ok ? qt16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
+            const f16x8 bop = as_h8(bq.x, bq.y, bq.z, bq.w);
+            f16x8 a0, a1;
+            if constexpr (!GEN) {
+                const bool w4 = qc < nbh;
+                const int base = w4 ? 32 * qc : 128 * nhk + 16 * (qc - nbh);
+                const int stride = w4 ? 4 * nhk : 2 * nlk;
+                const int bit0 = base + ln * stride, bit1 = bit0 + 16 * stride;
+                const uint32_t X0 = __builtin_amdgcn_alignbit(rec[(bit0 >> 5) + 1], rec[bit0 >> 5], bit0 & 31);
+                const uint32_t X1 = __builtin_amdgcn_alignbit(rec[(bit1 >> 5) + 1], rec[bit1 >> 5], bit1 & 31);
+                if constexpr (S % 4 == 0) {
+                    if (w4) {
+                        a0 = dequant8<true>(X0, sp, zp, km4, kmagic);
+                        a1 = dequant8<true>(X1, sp, zp, km4, kmagic);
+                    } else {
+                        a0 = dequant8<false>(X0, sp, zp, km2, kmagic);
+                        a1 = dequant8<false>(X1, sp, zp, km2, kmagic);
+                    }
+                } else {
+                    a0 = dequant8_any(X0, w4, sp, zp);
+                    a1 = dequant8_any(X1, w4, sp, zp);
+                }
+            } else {
+                const int4 bq4 = blk[qc];                // base, stride, width
+                const int wq = bq4.z;
+                const int bit0 = bq4.x + ln * bq4.y, bit1 = bit0 + 16 * bq4.y;
+                const uint32_t X0 = __builtin_amdgcn_alignbit(rec[(bit0 >> 5) + 1], rec[bit0 >> 5], bit0 & 31);
+                const uint32_t X1 = __builtin_amdgcn_alignbit(rec[(bit1 >> 5) + 1], rec[bit1 >> 5], bit1 & 31);
+                // 8-bit blocks span 64 bits: the second word of each window
+                const uint32_t Y0 = wq == 8 ? __builtin_amdgcn_alignbit(rec[(bit0 >> 5) + 2], rec[(bit0 >> 5) + 1],
+                                                                       bit0 & 31) : 0u;
+                const uint32_t Y1 = wq == 8 ? __builtin_amdgcn_alignbit(rec[(bit1 >> 5) + 2], rec[(bit1 >> 5) + 1],
+                                                                       bit1 & 31) : 0u;
+                a0 = dequant8_w(X0, Y0, wq, sp, zp);
+                a1 = dequant8_w(X1, Y1, wq, sp, zp);
+            }
+            sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bop, sacc0, 0, 0, 0);
+            sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bop, sacc1, 0, 0, 0);
+        }
+
+        // (c) online softmax of stream ln (rows 4*kb + v of both 16-token halves)
+        const bool sv = live_n && (tb0 + slot_n) < npg;
+        const float sc[8] = {sacc0[0], sacc0[1], sacc0[2], sacc0[3], sacc1[0], sacc1[1], sacc1[2], sacc1[3]};
+        float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        mloc = sv ? mloc : -INFINITY;
+        const bool need = mloc > m_run + kRescaleSlack;
+        if (__any(need)) {
+            float mm = fmaxf(mloc, __shfl_xor(mloc, 16));
+            mm = fmaxf(mm, __shfl_xor(mm, 32));
+            const bool upd = mm > m_run + kRescaleSlack;
+            const float m_new = upd ? mm : m_run;
+            const float alpha = upd ? exp2f(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float av = __shfl(alpha, 4 * kb + v);
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb) oacc[nb][v] *= av;
+            }
+            m_run = m_new;
+        }
+        // weights of streams whose group is past the pass never reach a
+        // value MFMA (their slot's A rows are zero), so only l is masked
+        const float msafe = m_run == -INFINITY ? 0.0f : m_run;
+        float pr[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(sc[k] - msafe);
+        const float psum = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+        l_run += sv ? psum : 0.0f;
+        const uint32_t pp0 = pack_rtz(pr[0], pr[4]), pp1 = pack_rtz(pr[1], pr[5]);
+        const uint32_t pp2 = pack_rtz(pr[2], pr[6]), pp3 = pack_rtz(pr[3], pr[7]);
+
+        // (d) values: one MFMA per slot and 16-channel block on exact codes
+        //     (1024 + code in fp16); per-group scale and zero are applied in
+        //     the epilogue: sum_t p (code s + z) = s (D - 1024 P) + z P, with
+        //     the weight sum P = sum_t p of each stream from one more MFMA
+        //     against a constant-one operand (so it sums exactly the fp16
+        //     weights used).  fp16 value latents are read from memory, all
+        //     slots' loads issued before the first MFMA.
+        f4 dacc[NBV];
+#pragma unroll
+        for (int nb = 0; nb < NBV; ++nb) dacc[nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
+        f4 dP = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f16x8 ones8 = as_h8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+        // fp16 value latents: with few (slot, block) pairs all loads are
+        // issued up front, else each slot's loads right before its MFMAs
+        constexpr bool kPreV = !VQ && S * NBV <= 8;
+        uint2 vlo[kPreV ? S : 1][NBV], vhi[kPreV ? S : 1][NBV];
+        if constexpr (kPreV) {
+#pragma unroll
+            for (int m = 0; m < S; ++m) {
+                const int tg = tb0 + m < npg ? tb0 + m : npg - 1;
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb) {
+                    const uint16_t *r16 = reinterpret_cast<const uint16_t *>(vg + (g0 + tg) * WV) + vch[nb] * 32;
+                    vlo[m][nb] = *reinterpret_cast<const uint2 *>(r16 + 4 * kb);
+                    vhi[m][nb] = *reinterpret_cast<const uint2 *>(r16 + 16 + 4 * kb);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < S; ++m) {
+            if (tb0 + m >= npg) break;               // wave-uniform
+            const bool arow = live_n && slot_n == m;
+            const f16x8 aop = arow ? as_h8(pp0, pp1, pp2, pp3) : as_h8(0u, 0u, 0u, 0u);
+            if (vq) dP = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, ones8, dP, 0, 0, 0);
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                uint32_t bp0, bp1, bp2, bp3;
+                if constexpr (VQ) {
+                    const uint32_t *rec = stage + voff + (tb0 + m) * WV;
+                    const uint32_t L0 = rec[vw0[nb]], L1 = rec[vw1[nb]];
+                    const int wc = vwc[nb];
+                    if (GEN && wc == 8) {
+                        // tokens 4 kb + k (word L0, byte k) and 16 + 4 kb + k (L1)
+                        bp0 = perm_b32(L1, L0, 0x0C040C00u) | kmagic;
+                        bp1 = perm_b32(L1, L0, 0x0C050C01u) | kmagic;
+                        bp2 = perm_b32(L1, L0, 0x0C060C02u) | kmagic;
+                        bp3 = perm_b32(L1, L0, 0x0C070C03u) | kmagic;
+                    } else {
+                        const uint32_t X = __builtin_amdgcn_ubfe(L0, vs0[nb], vwid[nb]) |
+                                           (__builtin_amdgcn_ubfe(L1, GEN ? vs1[nb] : vs0[nb], vwid[nb]) << 16);
+                        bp0 = (X & vcm[nb]) | kmagic;
+                        bp1 = ((X >> wc) & vcm[nb]) | kmagic;
+                        bp2 = ((X >> (2 * wc)) & vcm[nb]) | kmagic;
+                        bp3 = ((X >> (3 * wc)) & vcm[nb]) | kmagic;
+                    }
+                } else {
+                    uint2 lo, hi;
+                    if constexpr (kPreV) {
+                        lo = vlo[m][nb];
+                        hi = vhi[m][nb];
+                    } else {
+                        const uint16_t *r16 =
+                            reinterpret_cast<const uint16_t *>(vg + (g0 + tb0 + m) * WV) + vch[nb] * 32;
+                        lo = *reinterpret_cast<const uint2 *>(r16 + 4 * kb);
+                        hi = *reinterpret_cast<const uint2 *>(r16 + 16 + 4 * kb);
+                    }
+                    bp0 = perm_b32(hi.x, lo.x, 0x05040100u);
+                    bp1 = perm_b32(hi.x, lo.x, 0x07060302u);
+                    bp2 = perm_b32(hi.y, lo.y, 0x05040100u);
+                    bp3 = perm_b32(hi.y, lo.y, 0x07060302u);
+                }
+                dacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, as_h8(bp0, bp1, bp2, bp3), dacc[nb], 0, 0, 0);
+            }
+        }
+        if (vq) {
+            // (e) epilogue per output row 4*kb + v (stream): the row's group
+            //     scale s and z - 1024 s from its metadata word; rows of
+            //     groups past the pass have D = P = 0
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                int tgr = tb0 + row_slot[v];
+                tgr = tgr < npg ? tgr : npg - 1;
+                const uint32_t *meta = stage + voff + tgr * WV + vmeta;
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb) {
+                    const uint32_t mw = meta[vch[nb]];
+                    const float sc16 = h2f(mw);
+                    const float zr = fmaf(-1024.0f, sc16, h2f(mw >> 16));
+                    oacc[nb][v] = fmaf(sc16, dacc[nb][v], fmaf(zr, dP[v], oacc[nb][v]));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) oacc[nb] += dacc[nb];
+        }
+        __builtin_amdgcn_s_waitcnt(0);                // the next pass's copies have landed
+        __syncthreads();                              // and every wave is done with this buffer
+    }
+
+    // ---- 5. per-wave stream results to LDS
+    const FastDiv div_rv(a.inv_rv);
+    float lsum = l_run;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    float msum = fmaxf(m_run, __shfl_xor(m_run, 16));
+    msum = fmaxf(msum, __shfl_xor(msum, 32));
+    if (lane < 16) {
+        mst[wv * 16 + lane] = msum;
+        lst[wv * 16 + lane] = lsum;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBV; ++nb) {
+        const int c = 16 * nb + ln;
+        if (c < rv) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ost[(wv * 16 + 4 * kb + v) * rv + c] = oacc[nb][v];
+        }
+    }
+
+    // ---- 6. incomplete group (fp32 latents staged in LDS; fp16 value
+    //         latents of the partial record), as one more stream per head:
+    //         thread (head tid / 32, token tid % 32), softmax within the 32
+    //         lanes of a head
+    if (do_tail) {
+        const float *tk = reinterpret_cast<const float *>(tails);
+        const int hh = tid >> 5, t = tid & 31;
+        const bool ok = hh < g && t < ntail;
+        float sc = -INFINITY;
+        if (ok) {
+            float acc = 0.0f;
+            for (int c = 0; c < rk; ++c) acc = fmaf(qt[hh * rk + c], tk[t * rk + c], acc);
+            sc = acc;
+        }
+        float mx = row_max(sc);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        const float pv = ok ? exp2f(sc - mx) : 0.0f;
+        float ls = row_sum(pv);
+        ls += __shfl_xor(ls, 16);
+        if (hh < g) {
+            tp[hh * 32 + t] = pv;
+            if (t == 0) {
+                mst[kWaves * 16 + hh] = mx;
+                lst[kWaves * 16 + hh] = ls;
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < g * rv; e += 256) {
+            const int hv = div_rv.quo(e), c = e - hv * rv;
+            float acc = 0.0f;
+            if (vq) {
+                const float *tv = reinterpret_cast<const float *>(tails + tk_words);
+                for (int t2 = 0; t2 < ntail; ++t2) acc = fmaf(tp[hv * 32 + t2], tv[t2 * rv + c], acc);
+            } else {
+                const _Float16 *tv = reinterpret_cast<const _Float16 *>(tails + tk_words) + c * 32;
+                for (int t2 = 0; t2 < ntail; ++t2) acc = fmaf(tp[hv * 32 + t2], static_cast<float>(tv[t2]), acc);
+            }
+            ost[(kWaves * 16 + hv) * rv + c] = acc;
+        }
+    }
+    __syncthreads();
+
+    // ---- 7. merge the streams of each head and write the split's partial.
+    //         Stream k of a head: k < kWaves * S -> wave k / S, slot k % S
+    //         (LDS stream (k / S) * 16 + (k % S) * g + head); k = kWaves * S
+    //         -> the tail stream kWaves * 16 + head.  Wave w merges heads
+    //         w, w + 4 with its lanes over streams.
+    const int nsw = kWaves * S + (do_tail ? 1 : 0);   // <= 65
+    float *wts = ts;                                   // [g][65]
+    float *part = a.partial + (static_cast<int64_t>(qi) * a.Hq + h * g) * kMaxSplits * (rv + 2) +
+                  static_cast<int64_t>(s) * (rv + 2);
+    const int64_t head_stride = static_cast<int64_t>(kMaxSplits) * (rv + 2);
+    for (int hh = wv; hh < g; hh += kWaves) {
+        const int k1 = lane + 64;
+        const int sid0 = lane < kWaves * S ? (lane / S) * 16 + (lane % S) * g + hh : kWaves * 16 + hh;
+        const float m0 = lane < nsw ? mst[sid0] : -INFINITY;
+        const float l0 = lane < nsw ? lst[sid0] : 0.0f;
+        const float m1 = k1 < nsw ? mst[kWaves * 16 + hh] : -INFINITY;   // only k = 64 (the tail at S = 16)
+        const float l1 = k1 < nsw ? lst[kWaves * 16 + hh] : 0.0f;
+        const float M = wave_max(fmaxf(m0, m1));
+        const float w0 = m0 == -INFINITY ? 0.0f : exp2f(m0 - M);
+        const float w1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - M);
+        const float lt = wave_sum(fmaf(w0, l0, w1 * l1));
+        if (lane < nsw) wts[hh * 65 + lane] = w0;
+        if (k1 < nsw) wts[hh * 65 + k1] = w1;
+        if (lane == 0) {
+            part[hh * head_stride] = M;
+            part[hh * head_stride + 1] = lt;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < g * rv; e += 256) {
+        const int hh = div_rv.quo(e), c = e - hh * rv;
+        const float *wrow = wts + hh * 65;
+        float acc = 0.0f;
+#pragma unroll 4
+        for (int k = 0; k < nsw; ++k) {
+            const int sidx = k < kWaves * S ? (k / S) * 16 + (k % S) * g + hh : kWaves * 16 + hh;
+            acc = fmaf(wrow[k], ost[sidx * rv + c], acc);
+        }
+        part[hh * head_stride + 2 + c] = acc;
+    }
+}
+
+// One workgroup of one wave per (call row, query head): merge the splits by
+// log-sum-exp and project back with the value basis,
+// o = V_V (o_lat / l) + mu_V, rounded to fp16.  The row's split partials and
+// its group's value basis and mean are first copied to LDS with independent
+// 16-byte loads, so the kernel waits on memory once; all later steps read LDS.
+__host__ __device__ inline int combine_lds_floats(int ns, int rv) {
+    return ((ns * (rv + 2) + 3) & ~3) + kHeadDim * rv + kHeadDim + ((ns + 3) & ~3) + ((rv + 3) & ~3);
+}
+
+__global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
+    extern __shared__ __align__(16) float cl[];
+    const int lane = threadIdx.x;
+    const int qh = blockIdx.x, i = blockIdx.y;   // grid (Hq, B)
+    // all argument loads issued together (one scalar round trip)
+    asm volatile("" ::"s"(a.partial), "s"(a.out), "s"(a.v.basis_cm), "s"(a.v.mu), "s"(a.v.r), "s"(a.gqa),
+                 "s"(a.hpg), "s"(a.Hq), "s"(a.nsplit_call[i]), "s"(a.slot_call[i]), "s"(a.v.set_bcm), "s"(a.v.set_mu));
+    const int h = qh / a.gqa, grp = h / a.hpg, ns = a.nsplit_call[i], rv = a.v.r;
+    const int64_t slot = a.slot_call[i];
+    const int np = ns * (rv + 2), npa = (np + 3) & ~3;
+    float *pl = cl;                            // [ns][rv + 2]: m, l, o_lat
+    float *bl = cl + npa;                      // [rv][D] value basis (channel-major)
+    float *ml = bl + kHeadDim * rv;            // [D] value mean
+    float *wl = ml + kHeadDim;                 // [ns] split weights
+    float *ol = wl + ((ns + 3) & ~3);          // [rv] merged latent output
+    const float *part = a.partial + (static_cast<int64_t>(i) * a.Hq + qh) * kMaxSplits * (rv + 2);
+    const float *bv = a.v.basis_cm + slot * a.v.set_bcm + static_cast<int64_t>(grp) * rv * kHeadDim;
+    const float *mv = a.v.mu + slot * a.v.set_mu + grp * kHeadDim;
+
+    // 1. copy to LDS: whole 16-byte pieces of the partials, the basis
+    //    (128 rv floats) and the mean; the < 4 trailing partial floats singly
+    {
+        const int n4p = np >> 2, n4b = (kHeadDim * rv) >> 2, n4 = n4p + n4b + kHeadDim / 4;
+        for (int base = 0; base < n4; base += 64 * 8) {
+            float4 buf[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = base + 64 * u + lane;
+                const float4 *src = e < n4p ? reinterpret_cast<const float4 *>(part) + e
+                                  : e < n4p + n4b ? reinterpret_cast<const float4 *>(bv) + (e - n4p)
+                                                  : reinterpret_cast<const float4 *>(mv) + (e - n4p - n4b);
+                buf[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (e < n4) buf[u] = *src;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = base + 64 * u + lane;
+                float4 *dst = e < n4p ? reinterpret_cast<float4 *>(pl) + e
+                            : e < n4p + n4b ? reinterpret_cast<float4 *>(bl) + (e - n4p)
+                                            : reinterpret_cast<float4 *>(ml) + (e - n4p - n4b);
+                if (e < n4) *dst = buf[u];
+            }
+        }
+        if (lane < np - 4 * n4p) pl[4 * n4p + lane] = part[4 * n4p + lane];
+    }
+    __syncthreads();
+
+    // 2. split weights relative to the largest split maximum, and l
+    const bool s0 = lane < ns, s1 = lane + 64 < ns;
+    const float m0 = s0 ? pl[lane * (rv + 2)] : -INFINITY;
+    const float m1 = s1 ? pl[(lane + 64) * (rv + 2)] : -INFINITY;
+    const float M = wave_max(fmaxf(m0, m1));
+    const float w0 = s0 ? exp2f(m0 - M) : 0.0f, w1 = s1 ? exp2f(m1 - M) : 0.0f;
+    const float l = wave_sum(fmaf(w0, s0 ? pl[lane * (rv + 2) + 1] : 0.0f,
+                                  w1 * (s1 ? pl[(lane + 64) * (rv + 2) + 1] : 0.0f)));
+    if (s0) wl[lane] = w0;
+    if (s1) wl[lane + 64] = w1;
+    __syncthreads();
+
+    // 3. merged latent output per channel
+    const float inv_l = 1.0f / l;
+    for (int c = lane; c < rv; c += 64) {
+        float acc = 0.0f;
+        for (int sp = 0; sp < ns; ++sp) acc = fmaf(wl[sp], pl[sp * (rv + 2) + 2 + c], acc);
+        ol[c] = acc * inv_l;
+    }
+    __syncthreads();
+
+    // 4. output projection, two adjacent outputs per lane
+    const int d0 = 2 * lane;
+    float o0 = ml[d0], o1 = ml[d0 + 1];
+    for (int c = 0; c < rv; ++c) {
+        const float oc = ol[c];
+        const float2 b = *reinterpret_cast<const float2 *>(bl + c * kHeadDim + d0);   // conflict-free
+        o0 = fmaf(b.x, oc, o0);
+        o1 = fmaf(b.y, oc, o1);
+    }
+    reinterpret_cast<uint32_t *>(a.out + (static_cast<int64_t>(i) * a.Hq + qh) * kHeadDim)[lane] =
+        out_bits(o0, a.bf16) | (out_bits(o1, a.bf16) << 16);
+}
+
+}  // namespace
+
+size_t attend_lds_bytes(int gqa, int nbk, int r_k, int r_v, int words_k, int words_v, bool vq) {
+    return static_cast<size_t>(attend_lds(gqa, nbk, r_k, r_v, words_k, words_v, vq).total);
+}
+
+template <int G, int NBV, bool VQ, bool GEN>
+static hipError_t launch_attend_tg(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+    static bool configured = false;
+    if (!configured) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<G, NBV, VQ, GEN>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    hipLaunchKernelGGL((attend_kernel<G, NBV, VQ, GEN>), dim3(a.nsplit_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
+    return hipGetLastError();
+}
+
+// A PALU-shaped coder: one 4-bit or 2-bit segment, or 4-bit then 2-bit.
+static bool palu_shaped(const Coder &cd) {
+    if (cd.nseg == 1) return cd.bits[0] == 4 || cd.bits[0] == 2;
+    return cd.nseg == 2 && cd.bits[0] == 4 && cd.bits[1] == 2;
+}
+
+template <int G, int NBV, bool VQ>
+static hipError_t launch_attend_t(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+    const bool gen = !palu_shaped(a.k.cd) || (VQ && !palu_shaped(a.v.cd));
+    return gen ? launch_attend_tg<G, NBV, VQ, true>(a, lds_bytes, s) : launch_attend_tg<G, NBV, VQ, false>(a, lds_bytes, s);
+}
+
+template <int G, bool VQ>
+static hipError_t launch_attend_v(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+    const int nbv = (a.v.r + 15) / 16;
+    if (nbv <= 1) return launch_attend_t<G, 1, VQ>(a, lds_bytes, s);
+    if (nbv <= 2) return launch_attend_t<G, 2, VQ>(a, lds_bytes, s);
+    if (nbv <= 4) return launch_attend_t<G, 4, VQ>(a, lds_bytes, s);
+    return launch_attend_t<G, 8, VQ>(a, lds_bytes, s);
+}
+
+template <int G>
+static hipError_t launch_attend_g(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+    return a.v.fp16_latents ? launch_attend_v<G, false>(a, lds_bytes, s) : launch_attend_v<G, true>(a, lds_bytes, s);
+}
+
+hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+    switch (a.gqa) {
+        case 1: return launch_attend_g<1>(a, lds_bytes, s);
+        case 2: return launch_attend_g<2>(a, lds_bytes, s);
+        case 3: return launch_attend_g<3>(a, lds_bytes, s);
+        case 4: return launch_attend_g<4>(a, lds_bytes, s);
+        case 5: return launch_attend_g<5>(a, lds_bytes, s);
+        case 6: return launch_attend_g<6>(a, lds_bytes, s);
+        case 7: return launch_attend_g<7>(a, lds_bytes, s);
+        case 8: return launch_attend_g<8>(a, lds_bytes, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_combine(const AttendArgs &a, hipStream_t s) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(combine_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const size_t lds = static_cast<size_t>(combine_lds_floats(a.nsplit_max, a.v.r)) * sizeof(float);
+    hipLaunchKernelGGL(combine_kernel, dim3(a.Hq, a.B), dim3(64), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace palu
