@@ -493,63 +493,79 @@ int queue_gram(palu_cache *c, const void *k, const void *v, int b0, int B, int S
     return PALU_OK;
 }
 
-// One fitted (tensor, group) problem: eigenpairs of the scatter matrix
-// about the mean, X^T X - s s^T / N.
+// One fitted (tensor, group) problem: eigenvalues of the scatter matrix
+// about the mean, X^T X - s s^T / N, then eigenvectors of the k largest.
 struct FitProblem {
     const double *gram;   // D*D Gram, then D column sums
     double n;             // rows
-    std::vector<double> w, z;
+    SymEigen se;          // reduction and eigenvalues (descending)
+    int k = 0;            // eigenvectors wanted
+    std::vector<double> z;   // [D][k]
     bool ok = false;
 };
 
-// Eigendecompositions of all problems on host threads (they are independent).
-void solve_all(int D, std::vector<FitProblem> &pr) {
-    for (auto &p : pr) {
-        p.z.assign(static_cast<size_t>(D) * D, 0.0);
-        p.w.assign(D, 0.0);
-    }
-    const int np = static_cast<int>(pr.size());
+// f(i) for i < count on host threads (the problems are independent).
+template <typename F>
+void parallel_for(int count, F f) {
     const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
-    const int nthreads = static_cast<int>(std::min<unsigned>(hw, static_cast<unsigned>(np)));
+    const int nthreads = static_cast<int>(std::min<unsigned>(hw, static_cast<unsigned>(std::max(1, count))));
     std::vector<std::thread> pool;
     for (int th = 0; th < nthreads; ++th)
         pool.emplace_back([&, th]() {
-            std::vector<double> cov(static_cast<size_t>(D) * D);
-            for (int i = th; i < np; i += nthreads) {
-                FitProblem &p = pr[i];
-                const double *sum = p.gram + D * D;
-                for (int a = 0; a < D; ++a)
-                    for (int b = 0; b < D; ++b) cov[a * D + b] = p.gram[a * D + b] - sum[a] * sum[b] / p.n;
-                for (int a = 0; a < D; ++a)
-                    for (int b = 0; b < a; ++b) {
-                        const double m = 0.5 * (cov[a * D + b] + cov[b * D + a]);
-                        cov[a * D + b] = cov[b * D + a] = m;
-                    }
-                p.ok = sym_eigen(cov.data(), D, p.w.data(), p.z.data());
-            }
+            for (int i = th; i < count; i += nthreads) f(i);
         });
     for (auto &t : pool) t.join();
 }
 
-// Basis of one problem: eigenvectors by descending eigenvalue, each signed
-// so that its largest-magnitude component is positive, into full [D][D]
-// (column = channel); squared singular values s2, sigma and the mean.
-void basis_of(const FitProblem &p, int D, double *full, double *s2, double *sigma, float *mu) {
-    std::vector<int> order(D);
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return p.w[a] > p.w[b]; });
-    for (int cidx = 0; cidx < D; ++cidx) {
-        const int src = order[cidx];
-        s2[cidx] = p.w[src] > 0.0 ? p.w[src] : 0.0;
-        sigma[cidx] = std::sqrt(s2[cidx]);
-        int arg = 0;
-        for (int d = 1; d < D; ++d)
-            if (std::fabs(p.z[d * D + src]) > std::fabs(p.z[arg * D + src])) arg = d;
-        const double sg = p.z[arg * D + src] < 0.0 ? -1.0 : 1.0;
-        for (int d = 0; d < D; ++d) full[d * D + cidx] = sg * p.z[d * D + src];
+// Step 1 of every problem: scatter matrix, reduction, eigenvalues.
+void solve_values(int D, std::vector<FitProblem> &pr) {
+    parallel_for(static_cast<int>(pr.size()), [&](int i) {
+        FitProblem &p = pr[i];
+        std::vector<double> cov(static_cast<size_t>(D) * D);
+        const double *sum = p.gram + D * D;
+        for (int a = 0; a < D; ++a)
+            for (int b = 0; b < D; ++b) cov[a * D + b] = p.gram[a * D + b] - sum[a] * sum[b] / p.n;
+        for (int a = 0; a < D; ++a)
+            for (int b = 0; b < a; ++b) {
+                const double m = 0.5 * (cov[a * D + b] + cov[b * D + a]);
+                cov[a * D + b] = cov[b * D + a] = m;
+            }
+        p.ok = sym_eigenvalues(cov.data(), D, p.se);
+    });
+}
+
+// Step 2: eigenvectors of the p.k largest eigenvalues of every problem.
+void solve_vectors(int D, std::vector<FitProblem> &pr) {
+    parallel_for(static_cast<int>(pr.size()), [&](int i) {
+        FitProblem &p = pr[i];
+        p.z.assign(static_cast<size_t>(D) * p.k, 0.0);
+        sym_top_vectors(p.se, p.k, p.z.data());
+    });
+}
+
+// Squared singular values s2 (clamped at 0), sigma and the mean of a problem.
+void spectrum_of(const FitProblem &p, int D, double *s2, double *sigma, float *mu) {
+    for (int c = 0; c < D; ++c) {
+        s2[c] = p.se.w[c] > 0.0 ? p.se.w[c] : 0.0;
+        sigma[c] = std::sqrt(s2[c]);
     }
     const double *sum = p.gram + D * D;
     for (int d = 0; d < D; ++d) mu[d] = static_cast<float>(sum[d] / p.n);
+}
+
+// Basis columns c < r of a problem (descending eigenvalue order), each
+// signed so that its largest-magnitude component is positive, into fp32
+// dst[d * r + c].
+void basis_of(const FitProblem &p, int D, int r, float *dst) {
+    for (int c = 0; c < r; ++c) {
+        int arg = 0;
+        for (int d = 1; d < D; ++d)
+            if (std::fabs(p.z[static_cast<size_t>(d) * p.k + c]) > std::fabs(p.z[static_cast<size_t>(arg) * p.k + c]))
+                arg = d;
+        const double sg = p.z[static_cast<size_t>(arg) * p.k + c] < 0.0 ? -1.0 : 1.0;
+        for (int d = 0; d < D; ++d)
+            dst[static_cast<size_t>(d) * r + c] = static_cast<float>(sg * p.z[static_cast<size_t>(d) * p.k + c]);
+    }
 }
 
 // Smallest rank whose leading squared singular values reach tau of the
@@ -620,10 +636,13 @@ int fit_per_seq(palu_cache *c, const void *k, const void *v, const int32_t *ids,
             p.gram = gram.data() + per * b + static_cast<size_t>(pb) * kGramElems;
             p.n = static_cast<double>(hpg) * seq_lens[b];
         }
-    solve_all(D, pr);
+    solve_values(D, pr);
     for (const auto &p : pr)
         if (!p.ok) return fail(PALU_ERR_HIP, "eigensolver did not converge");
-    std::vector<double> full(static_cast<size_t>(D) * D), s2(D);
+    for (int b = 0; b < B; ++b)
+        for (int pb = 0; pb < 2 * G; ++pb) pr[static_cast<size_t>(b) * 2 * G + pb].k = c->r[pb / G];
+    solve_vectors(D, pr);
+    std::vector<double> s2(D);
     for (int b = 0; b < B; ++b) {
         const int slot = ids ? ids[b] : b;
         c->len[slot] = 0;
@@ -633,11 +652,10 @@ int fit_per_seq(palu_cache *c, const void *k, const void *v, const int32_t *ids,
             std::vector<float> basis(c->basis_elems(t)), mu(c->mu_elems());
             std::vector<double> sigma(c->mu_elems());
             for (int g = 0; g < G; ++g) {
-                basis_of(pr[(static_cast<size_t>(b) * 2 + t) * G + g], D, full.data(), s2.data(),
-                         sigma.data() + static_cast<size_t>(g) * D, mu.data() + static_cast<size_t>(g) * D);
-                for (int d = 0; d < D; ++d)
-                    for (int cidx = 0; cidx < rr; ++cidx)
-                        basis[(static_cast<size_t>(g) * D + d) * rr + cidx] = static_cast<float>(full[d * D + cidx]);
+                const FitProblem &p = pr[(static_cast<size_t>(b) * 2 + t) * G + g];
+                spectrum_of(p, D, s2.data(), sigma.data() + static_cast<size_t>(g) * D,
+                            mu.data() + static_cast<size_t>(g) * D);
+                basis_of(p, D, rr, basis.data() + static_cast<size_t>(g) * D * rr);
             }
             if (int err = install_basis(c, t, slot, basis.data(), mu.data(), sigma.data())) return err;
         }
@@ -678,32 +696,37 @@ PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t
         pr[pb].gram = gram.data() + static_cast<size_t>(pb) * kGramElems;
         pr[pb].n = static_cast<double>(n_rows);
     }
-    solve_all(D, pr);
+    solve_values(D, pr);
     for (const auto &p : pr)
         if (!p.ok) return fail(PALU_ERR_HIP, "eigensolver did not converge");
+    // ranks from the eigenvalues (the minimum over groups), then only that
+    // many eigenvectors per problem
+    int rt[2];
+    std::vector<double> s2(static_cast<size_t>(2) * G * D), sigma(static_cast<size_t>(2) * G * D);
+    std::vector<float> mu(static_cast<size_t>(2) * G * D);
     for (int t = 0; t < 2; ++t) {
-        std::vector<double> full(static_cast<size_t>(G) * D * D), s2(static_cast<size_t>(G) * D),
-            sigma(static_cast<size_t>(G) * D);
-        std::vector<float> mu(static_cast<size_t>(G) * D);
         int rr = D;
         for (int g = 0; g < G; ++g) {
-            double *sg = s2.data() + static_cast<size_t>(g) * D;
-            basis_of(pr[t * G + g], D, full.data() + static_cast<size_t>(g) * D * D, sg,
-                     sigma.data() + static_cast<size_t>(g) * D, mu.data() + static_cast<size_t>(g) * D);
-            rr = std::min(rr, c->cfg.rank > 0 ? std::min(c->cfg.rank, D) : energy_rank(sg, D, c->cfg.energy_threshold));
+            const size_t off = (static_cast<size_t>(t) * G + g) * D;
+            spectrum_of(pr[t * G + g], D, s2.data() + off, sigma.data() + off, mu.data() + off);
+            rr = std::min(rr, c->cfg.rank > 0 ? std::min(c->cfg.rank, D)
+                                              : energy_rank(s2.data() + off, D, c->cfg.energy_threshold));
         }
         if (rr > c->r_max)
             return fail(PALU_ERR_CAPACITY, "fitted rank " + std::to_string(rr) + " exceeds max_rank " +
                                                std::to_string(c->r_max));
+        rt[t] = rr;
+        for (int g = 0; g < G; ++g) pr[t * G + g].k = rr;
+    }
+    solve_vectors(D, pr);
+    for (int t = 0; t < 2; ++t) {
+        const int rr = rt[t];
         size_shared(c, t, rr);
         std::vector<float> basis(c->basis_elems(t));
-        for (int g = 0; g < G; ++g)
-            for (int d = 0; d < D; ++d)
-                for (int cidx = 0; cidx < rr; ++cidx)
-                    basis[(static_cast<size_t>(g) * D + d) * rr + cidx] =
-                        static_cast<float>(full[(static_cast<size_t>(g) * D + d) * D + cidx]);
+        for (int g = 0; g < G; ++g) basis_of(pr[t * G + g], D, rr, basis.data() + static_cast<size_t>(g) * D * rr);
         if (int err = set_coder(c, t)) return err;
-        if (int err = install_basis(c, t, 0, basis.data(), mu.data(), sigma.data())) return err;
+        const size_t off = static_cast<size_t>(t) * G * D;
+        if (int err = install_basis(c, t, 0, basis.data(), mu.data() + off, sigma.data() + off)) return err;
     }
     return PALU_OK;
 }

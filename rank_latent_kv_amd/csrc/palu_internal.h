@@ -4,6 +4,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include <hip/hip_runtime_api.h>
 
@@ -199,10 +200,19 @@ hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, const
 // rows of the position-ordered fp16 basis copy (8 per channel block)
 PALU_HD inline int basis_t16_rows(const Coder &cd) { return 8 * coder_blocks(cd); }
 
-// Host symmetric eigensolver (palu_eigen.cpp): Householder tridiagonalisation
-// followed by implicit-shift QL.  a: n x n row-major symmetric (destroyed);
-// w: eigenvalues (unsorted); z: n x n row-major, column j = eigenvector j.
-// Returns false if the iteration did not converge.
-bool sym_eigen(double *a, int n, double *w, double *z);
+// Host symmetric eigensolver (palu_eigen.cpp), in two steps for the fit:
+// sym_eigenvalues reduces a (n x n row-major symmetric, destroyed) to
+// tridiagonal form, keeps the reflectors and finds every eigenvalue
+// (descending in w; false if the iteration did not converge);
+// sym_top_vectors then writes the eigenvectors of the k largest into z
+// (n x k row-major, column j <-> w[j]), unit length and mutually orthogonal.
+struct SymEigen {
+    int n = 0;
+    std::vector<double> hv, beta;   // reflector vectors [n][n] and coefficients
+    std::vector<double> d, e;       // tridiagonal matrix
+    std::vector<double> w;          // eigenvalues, descending
+};
+bool sym_eigenvalues(double *a, int n, SymEigen &s);
+void sym_top_vectors(const SymEigen &s, int k, double *z);
 
 }  // namespace palu

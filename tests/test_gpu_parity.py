@@ -319,6 +319,29 @@ def test_fit_parity_small_workloads(torch, name):
                                        atol=1e-5 * f.sigma[g][0] ** 2)
 
 
+@pytest.mark.parametrize("lens,rank", [([3], 0), ([1, 2], 0), ([5, 4], 6), ([40], 0)])
+def test_fit_rank_deficient(torch, lens, rank):
+    """Fewer rows than head_dim: the scatter matrices are singular (many
+    eigenvalues at rounding level).  The fit must converge, keep an
+    orthonormal basis, and match the oracle's rank and captured energy."""
+    lens = np.asarray(lens, np.int32)
+    w = synth.small_workload(batch=len(lens), n_q_heads=4, n_kv_heads=2, n_head_groups=1, prefill=int(lens.max()),
+                             rank=rank, seed=77)
+    S = int(lens.max())
+    k, v = synth.batch_kv(w, 0, S), synth.batch_kv(w, 1, S)
+    cache = _cache(torch, w, S, rank=rank)
+    cache.fit(_dev(torch, k), _dev(torch, v), lens)
+    for tensor, x in ((0, k), (1, v)):
+        f = oracle.fit(x, lens, 1, rank=rank, tau=w.energy)
+        r, basis, mu, _ = cache.get_basis(tensor)
+        assert r == f.r, (tensor, r, f.r)
+        np.testing.assert_allclose(basis[0].T.astype(np.float64) @ basis[0], np.eye(r), atol=1e-5)
+        np.testing.assert_allclose(mu[0], f.mu[0], atol=1e-5)
+        rows = np.concatenate([x[b, h, :lens[b]] for b in range(len(lens)) for h in range(2)])
+        if np.sum((rows.astype(np.float64) - f.mu[0]) ** 2) > 0:
+            assert abs(_energy(rows, f.mu[0], basis[0]) - _energy(rows, f.mu[0], f.V(0))) <= 1e-4
+
+
 # --------------------------------------------------- full-size, sampled
 
 def _full_size_check(torch, name, sample_seqs, sample_heads, steps=2):

@@ -224,6 +224,34 @@ def test_export_import_carries_bases(torch):
         dst.import_seq(1, bytes(bad))
 
 
+def test_fit_tiny_prompts(torch):
+    """Per-sequence fits of 1- to 3-token prompts (a zero or rank-deficient
+    scatter matrix): the fit converges, the bases are orthonormal, the mean
+    is the prompt's mean, and codes and decode match the oracle under the
+    installed bases."""
+    B, rank, groups = 3, 8, 1
+    ws = _workloads(B, 2, groups, rank, True, 97)
+    lens = np.array([1, 2, 3], np.int32)
+    k, v = _rows(ws, 0, 8), _rows(ws, 1, 8)
+    cache = _cache(torch, ws[0], B, 8, rank)
+    cache.fit(_dev(torch, k), _dev(torch, v), lens)
+    cache.encode_append(_dev(torch, k), _dev(torch, v), n_new=lens + 1)
+    q = np.concatenate([synth.queries(w, b, 1) for b, w in enumerate(ws)])
+    out = cache.decode_attend(_dev(torch, q)).cpu().numpy()
+    for b in range(B):
+        for tensor, x in ((0, k), (1, v)):
+            r, basis, mu, _ = cache.get_basis(tensor, seq=b)
+            np.testing.assert_allclose(basis[0].T.astype(np.float64) @ basis[0], np.eye(r), atol=1e-5)
+            rows = np.concatenate([x[b, h, :lens[b]] for h in range(2)]).astype(np.float64)
+            np.testing.assert_allclose(mu[0], rows.mean(axis=0), atol=1e-5)
+        layer = oracle.OracleLayer(128, 4, 2, groups, _fit_of_slot(cache, b, 0), _fit_of_slot(cache, b, 1))
+        n = int(lens[b]) + 1
+        _state_equal(cache, layer, k[b, :, :n], v[b, :, :n], b)
+        ks = [layer.encode_head(k[b, h, :n], h, 0) for h in range(2)]
+        vs = [layer.encode_head(v[b, h, :n], h, 1) for h in range(2)]
+        _check_attention(out[b], layer.attend(ks, vs, q[b]), f"decode row {b}")
+
+
 def test_slots_without_bases_are_refused(torch):
     from rank_latent_kv_amd.palu import PaluError
     ws = _workloads(2, 2, 1, 8, True, 99)
