@@ -133,8 +133,11 @@ int palu_cache_bind(palu_cache *cache, void *dev_buf, size_t bytes);
  *   k, v     : device fp16 or bf16 (input_dtype) [B][H][S_stride][D]
  *   seq_lens : host int32 [B], 0 <= seq_lens[b] <= S_stride, sum > 0
  * Synchronous (the eigensolve runs on the host).  Empties every sequence
- * slot (stored codes of an older basis are meaningless).  Errors:
- * INVALID_ARG, NOT_BOUND, HIP. */
+ * slot (stored codes of an older basis are meaningless).  With per-sequence
+ * bases (per_seq_basis = 1) row b is fitted alone into slot b, as
+ * palu_fit_seq with seq_ids = 0 .. B-1 (every seq_lens[b] > 0), and only
+ * those slots are emptied.  Errors: INVALID_ARG, CAPACITY, NOT_BOUND, HIP
+ * (also when the eigensolver does not converge). */
 int palu_fit(palu_cache *cache, const void *k, const void *v,
              const int32_t *seq_lens, int32_t B, int32_t S_stride, void *stream);
 
@@ -142,11 +145,14 @@ int palu_fit(palu_cache *cache, const void *k, const void *v,
  *   basis : host fp32 [G][D][r], basis[g][d][c] = component d of channel c,
  *           channels in descending singular-value order
  *   mu    : host fp32 [G][D]
- * 1 <= r <= max_rank.  Synchronous.  Empties every sequence slot. */
+ * 1 <= r <= max_rank.  Synchronous.  Empties every sequence slot.  With
+ * per-sequence bases it installs the basis in every slot (r must equal the
+ * cache's rank). */
 int palu_set_basis(palu_cache *cache, int32_t tensor, int32_t r,
                    const float *basis, const float *mu);
 
-/* Reads the basis of tensor 0 (K) or 1 (V).  r receives the rank; basis
+/* Reads the shared basis of tensor 0 (K) or 1 (V) (INVALID_ARG with
+ * per-sequence bases: see palu_get_basis_seq).  r receives the rank; basis
  * (host fp32 [G][D][r]), mu (host fp32 [G][D]) and sigma (host fp64 [G][D],
  * singular values of the centred stacks, zeros if set by palu_set_basis)
  * may each be NULL.  Errors: INVALID_ARG, NOT_FITTED. */
