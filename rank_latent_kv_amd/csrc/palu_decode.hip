@@ -635,16 +635,32 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         }
     }
     __syncthreads();
-    for (int e = tid; e < g * rv; e += 256) {
-        const int hh = div_rv.quo(e), c = e - hh * rv;
+    // weighted sum over the streams of every (head, channel) output: four
+    // lanes of a quad per output, each over every fourth stream, then a quad
+    // reduction (one lane per output when there are more than 64 outputs)
+    auto stream_row = [&](int k, int hh) {
+        return k < kWaves * S ? (k / S) * 16 + (k % S) * g + hh : kWaves * 16 + hh;
+    };
+    if (g * rv <= 64) {
+        const int e = tid >> 2, sub = tid & 3;
+        const bool live = e < g * rv;
+        const int ee = live ? e : 0;
+        const int hh = div_rv.quo(ee), c = ee - hh * rv;
         const float *wrow = wts + hh * 65;
         float acc = 0.0f;
+        for (int k = sub; k < nsw; k += 4) acc = fmaf(wrow[k], ost[stream_row(k, hh) * rv + c], acc);
+        acc += dpp<kDppXor1>(acc);
+        acc += dpp<kDppXor2>(acc);
+        if (live && sub == 0) part[hh * head_stride + 2 + c] = acc;
+    } else {
+        for (int e = tid; e < g * rv; e += 256) {
+            const int hh = div_rv.quo(e), c = e - hh * rv;
+            const float *wrow = wts + hh * 65;
+            float acc = 0.0f;
 #pragma unroll 4
-        for (int k = 0; k < nsw; ++k) {
-            const int sidx = k < kWaves * S ? (k / S) * 16 + (k % S) * g + hh : kWaves * 16 + hh;
-            acc = fmaf(wrow[k], ost[sidx * rv + c], acc);
+            for (int k = 0; k < nsw; ++k) acc = fmaf(wrow[k], ost[stream_row(k, hh) * rv + c], acc);
+            part[hh * head_stride + 2 + c] = acc;
         }
-        part[hh * head_stride + 2 + c] = acc;
     }
 }
 
@@ -716,12 +732,24 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
     if (s1) wl[lane + 64] = w1;
     __syncthreads();
 
-    // 3. merged latent output per channel
+    // 3. merged latent output per channel: with r_v <= 16, four lanes per
+    //    channel (lanes c, c + 16, c + 32, c + 48), each over every fourth
+    //    split, then summed across the four rows of 16 lanes
     const float inv_l = 1.0f / l;
-    for (int c = lane; c < rv; c += 64) {
+    if (rv <= 16) {
+        const int c = lane & 15, part0 = lane >> 4;
+        const int cc = c < rv ? c : 0;
         float acc = 0.0f;
-        for (int sp = 0; sp < ns; ++sp) acc = fmaf(wl[sp], pl[sp * (rv + 2) + 2 + c], acc);
-        ol[c] = acc * inv_l;
+        for (int sp = part0; sp < ns; sp += 4) acc = fmaf(wl[sp], pl[sp * (rv + 2) + 2 + cc], acc);
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        if (lane < rv) ol[lane] = acc * inv_l;
+    } else {
+        for (int c = lane; c < rv; c += 64) {
+            float acc = 0.0f;
+            for (int sp = 0; sp < ns; ++sp) acc = fmaf(wl[sp], pl[sp * (rv + 2) + 2 + c], acc);
+            ol[c] = acc * inv_l;
+        }
     }
     __syncthreads();
 
