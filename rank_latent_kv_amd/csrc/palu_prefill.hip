@@ -52,9 +52,13 @@ constexpr int kVRow = 40;   // halves per value-tile row: 32 tokens + 8 padding
 
 __host__ __device__ inline int pf_krow(int ks) { return 32 * ks + 8; }   // halves per key-tile row
 
+// Rings of raw record buffers and tile pairs: groups 2i and 2i + 1 are
+// computed while 2i + 2 and 2i + 3 are built and 2i + 4 and 2i + 5 copied.
+constexpr int kPfRing = 4;
+
 struct PrefillLds {
-    int raw, raw_words;    // two raw record buffers (K record, then V record)
-    int tiles, ktile, vtile;   // two (key tile, value tile) pairs; bytes of each tile
+    int raw, raw_words;    // kPfRing raw record buffers (K record, then V record)
+    int tiles, ktile, vtile;   // kPfRing (key tile, value tile) pairs; bytes of each tile
     int basis;             // epilogue: fp32 value basis [D][r_V] + mean [D] (aliases the above)
     int tab;               // key block table (int4 per block) + value channel table (int2 per channel)
     int olat;              // per wave [16 NQ][16 NBV] fp32 normalised latent outputs
@@ -67,8 +71,8 @@ __host__ __device__ inline PrefillLds prefill_lds(int ks, int nbv, int nq, int w
     L.ktile = 32 * pf_krow(ks) * 2;
     L.vtile = 16 * nbv * kVRow * 2;
     int a = 0;
-    L.raw = lds_take(a, 2 * L.raw_words * 4);
-    L.tiles = lds_take(a, 2 * (L.ktile + L.vtile));
+    L.raw = lds_take(a, kPfRing * L.raw_words * 4);
+    L.tiles = lds_take(a, kPfRing * (L.ktile + L.vtile));
     int b = 0;
     L.basis = lds_take(b, (kHeadDim * rv + kHeadDim) * 4);
     int o = a > b ? a : b;
@@ -146,7 +150,7 @@ void prefill_kernel(PrefillArgs a) {
     const uint32_t *kg = a.k.records + hb * a.k.head_stride;
     const uint32_t *vg = a.v.records + hb * a.v.head_stride;
 
-    // ---- raw records of group j (< nfull) -> raw buffer j & 1
+    // ---- raw records of group j (< nfull) -> raw buffer j % kPfRing
     auto rec_offsets = [&](int j, int &koff, int &nk4, int &voff, int &nv4) {
         const int64_t ka = (static_cast<int64_t>(j) * WK) & ~3LL, va = (static_cast<int64_t>(j) * WV) & ~3LL;
         koff = static_cast<int>(static_cast<int64_t>(j) * WK - ka);
@@ -160,31 +164,32 @@ void prefill_kernel(PrefillArgs a) {
         const u4v *ks = reinterpret_cast<const u4v *>(kg + ((static_cast<int64_t>(j) * WK) & ~3LL));
         const u4v *vs = reinterpret_cast<const u4v *>(vg + ((static_cast<int64_t>(j) * WV) & ~3LL));
         const int n4 = nk4 + nv4;
-        unsigned char *dst = lds + L.raw + (j & 1) * L.raw_words * 4;
+        unsigned char *dst = lds + L.raw + (j & (kPfRing - 1)) * L.raw_words * 4;
         for (int c = wv; c * 64 < n4; c += kPfWaves) {
             const int e = c * 64 + lane;
             if (e < n4) __builtin_amdgcn_global_load_lds(e < nk4 ? ks + e : vs + (e - nk4), dst + c * 1024, 16, 0, 0);
         }
     };
 
-    // ---- fp16 tiles of group j -> tile pair j & 1 (data parts only).  The
-    //      items come in rounds of 64 (one per lane): key rounds, then value
-    //      rounds; round r goes to wave (j + r) % 4, so whole waves build
-    //      (no partly filled item loops in every wave) and the building
-    //      rotates over the waves from group to group.
+    // ---- fp16 tiles of group j -> tile pair j % kPfRing (data parts only).
+    //      The items come in rounds of 64 (one per lane): key rounds, then
+    //      value rounds; round r goes to wave (rot + r) % 4, so whole waves
+    //      build (no partly filled item loops in every wave) and the two
+    //      groups built together share the waves evenly.
     const int nrk = (32 * nbk + 63) >> 6, nrv = (4 * rv + 63) >> 6;
-    auto build_tiles = [&](int j) {
-        _Float16 *kt = reinterpret_cast<_Float16 *>(lds + L.tiles + (j & 1) * (L.ktile + L.vtile));
-        _Float16 *vt = reinterpret_cast<_Float16 *>(lds + L.tiles + (j & 1) * (L.ktile + L.vtile) + L.ktile);
+    auto build_tiles = [&](int j, int rot) {
+        const int slot = j & (kPfRing - 1);
+        _Float16 *kt = reinterpret_cast<_Float16 *>(lds + L.tiles + slot * (L.ktile + L.vtile));
+        _Float16 *vt = reinterpret_cast<_Float16 *>(lds + L.tiles + slot * (L.ktile + L.vtile) + L.ktile);
         const bool full = j < nfull;
         int koff = 0, nk4 = 0, voff = 0, nv4 = 0;
         if (full) rec_offsets(j, koff, nk4, voff, nv4);
-        const uint32_t *raw = reinterpret_cast<const uint32_t *>(lds + L.raw) + (j & 1) * L.raw_words;
+        const uint32_t *raw = reinterpret_cast<const uint32_t *>(lds + L.raw) + slot * L.raw_words;
         const uint32_t *kr = raw + koff, *vr = raw + voff;
         const float *tk = a.k.tail + (hb * 2 + rw.sel) * kTokGroup * rk;
         const float *tv = vq ? a.v.tail + (hb * 2 + rw.sel) * kTokGroup * rv : nullptr;
         const uint16_t *r16 = reinterpret_cast<const uint16_t *>(vg + static_cast<int64_t>(nfull) * WV);
-        for (int r = (wv - j) & (kPfWaves - 1); r < nrk + nrv; r += kPfWaves) {
+        for (int r = (wv - rot) & (kPfWaves - 1); r < nrk + nrv; r += kPfWaves) {
             if (r < nrk) {
                 // key item: (8-position block q < nbk, token t)
                 const int e = 64 * r + lane;
@@ -284,16 +289,16 @@ void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // ---- the tiles' constant parts, written once for both buffers: key
+    // ---- the tiles' constant parts, written once for every buffer: key
     //      positions past the last channel block are 0; value channel r_V is
     //      all ones and the channels after it are 0
-    for (int e = tid; e < 2 * 32 * (4 * KS - nbk); e += 256) {
-        const int bf = e & 1, r = e >> 1, t = r & 31, q = nbk + (r >> 5);
+    for (int e = tid; e < kPfRing * 32 * (4 * KS - nbk); e += 256) {
+        const int bf = e & (kPfRing - 1), r = e / kPfRing, t = r & 31, q = nbk + (r >> 5);
         *reinterpret_cast<uint4 *>(lds + L.tiles + bf * (L.ktile + L.vtile) + (t * krow + 8 * q) * 2) =
             make_uint4(0u, 0u, 0u, 0u);
     }
-    for (int e = tid; e < 2 * 4 * (16 * NBV - rv); e += 256) {
-        const int bf = e & 1, r = e >> 1, tb = r & 3, c = rv + (r >> 2);
+    for (int e = tid; e < kPfRing * 4 * (16 * NBV - rv); e += 256) {
+        const int bf = e & (kPfRing - 1), r = e / kPfRing, tb = r & 3, c = rv + (r >> 2);
         const uint32_t w = c == rv ? 0x3C003C00u : 0u;
         *reinterpret_cast<uint4 *>(lds + L.tiles + bf * (L.ktile + L.vtile) + L.ktile + (c * kVRow + 8 * tb) * 2) =
             make_uint4(w, w, w, w);
@@ -311,8 +316,8 @@ void prefill_kernel(PrefillArgs a) {
     //      rows (16 positions x 32 d), B = the column's query (32 d x 16
     //      columns); D[position][column] packed straight into the fp16 score
     //      operand qb (K index 8 kb + 2 v + hh <- position 32 ks + 16 hh + 4 kb + v)
-    if (nfull > 0) copy_raw(0);
-    if (nfull > 1 && ngroups > 1) copy_raw(1);
+    for (int j = 0; j < kPfRing; ++j)
+        if (j < nfull && j < ngroups) copy_raw(j);
     f16x8 qb[NQ][KS];
     {
         const uint16_t *bt = a.k.basis_t16 + rw.slot * a.k.set_bt16 + static_cast<int64_t>(grp) * np * kHeadDim;
@@ -351,7 +356,8 @@ void prefill_kernel(PrefillArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    build_tiles(0);
+    build_tiles(0, 0);
+    if (ngroups > 1) build_tiles(1, nrk + nrv);
     __syncthreads();
 
     // ---- key loop
@@ -363,12 +369,12 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb) oacc[t][nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
     }
-    for (int j = 0; j < ngroups; ++j) {
-        if (j + 2 < ngroups && j + 2 < nfull) copy_raw(j + 2);
-        if (j + 1 < ngroups) build_tiles(j + 1);
+    // group j's scores, softmax and value contraction from its tiles
+    auto compute_group = [&](int j) {
         if (32 * j <= pw_hi) {                       // wave-uniform
-            const _Float16 *kt = reinterpret_cast<const _Float16 *>(lds + L.tiles + (j & 1) * (L.ktile + L.vtile));
-            const _Float16 *vt = reinterpret_cast<const _Float16 *>(lds + L.tiles + (j & 1) * (L.ktile + L.vtile) +
+            const int slot = j & (kPfRing - 1);
+            const _Float16 *kt = reinterpret_cast<const _Float16 *>(lds + L.tiles + slot * (L.ktile + L.vtile));
+            const _Float16 *vt = reinterpret_cast<const _Float16 *>(lds + L.tiles + slot * (L.ktile + L.vtile) +
                                                                     L.ktile);
             f16x8 ka[2][KS];
 #pragma unroll
@@ -454,8 +460,18 @@ void prefill_kernel(PrefillArgs a) {
                     oacc[t][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb[nb], oacc[t][nb], 0, 0, 0);
             }
         }
+    };
+    // groups in pairs: copy the raw records two pairs ahead, build the
+    // tiles of the next pair, compute this pair; one barrier per pair
+    for (int j = 0; j < ngroups; j += 2) {
+        if (j + 4 < ngroups && j + 4 < nfull) copy_raw(j + 4);
+        if (j + 5 < ngroups && j + 5 < nfull) copy_raw(j + 5);
+        if (j + 2 < ngroups) build_tiles(j + 2, j + 2);
+        if (j + 3 < ngroups) build_tiles(j + 3, j + 2 + nrk + nrv);
+        compute_group(j);
+        if (j + 1 < ngroups) compute_group(j + 1);
         __builtin_amdgcn_s_waitcnt(0);                // this wave's record copies have landed
-        __syncthreads();                              // and every wave is done with this group's tiles
+        __syncthreads();                              // and every wave is done with this pair's tiles
     }
 
     // ---- normalise by the ones column (channel r_V) and park the latent
