@@ -986,7 +986,7 @@ PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(c->D));
     const int ks = prefill_ks(coder_blocks(kd.cd)), nbv = prefill_nbv(vd.r);
-    const int qp = 64 * prefill_nq(ks, nbv) / c->gqa;   // query positions per workgroup
+    const int qp = 16 * kPrefillWaves * prefill_nq(ks, nbv) / c->gqa;   // query positions per workgroup
     const size_t row_elems = static_cast<size_t>(c->Hq) * T_stride * c->D;
     for (int b0 = 0; b0 < B; b0 += kMaxCallSeqs) {
         const int nb = std::min(kMaxCallSeqs, B - b0);

@@ -165,6 +165,9 @@ struct PrefillArgs {
     PrefillRow row[kMaxCallSeqs];
 };
 
+// Waves of one prefill attention workgroup (16 NQ query columns each).
+constexpr int kPrefillWaves = 4;
+
 // Score K-steps (32 key-basis positions each), value blocks (16 channels,
 // one of them the all-ones column that yields the softmax denominator) and
 // query tiles per wave (16 columns each) of the prefill kernel variant that
@@ -174,7 +177,7 @@ int prefill_nbv(int r_v);
 int prefill_nq(int ks, int nbv);
 // LDS bytes of one prefill workgroup.
 size_t prefill_lds_bytes(int nbk, int r_k, int r_v, int words_k, int words_v);
-// Grid (tiles_max, Hkv, B), 256 threads (defined in palu_prefill.hip).
+// Grid (tiles_max, Hkv, B), 64 kPrefillWaves threads (defined in palu_prefill.hip).
 hipError_t launch_prefill(const PrefillArgs &a, size_t lds_bytes, hipStream_t s);
 
 // LDS bytes of one attend workgroup (independent of the split size).

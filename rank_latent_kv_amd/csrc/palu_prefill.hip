@@ -45,7 +45,8 @@ namespace palu {
 
 namespace {
 
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = kPrefillWaves;
+constexpr int kPfThreads = 64 * kPfWaves;
 constexpr float kPfSlack = 8.0f;
 constexpr int kVRow = 40;   // halves per value-tile row: 32 tokens + 8 padding
 
@@ -98,7 +99,7 @@ __device__ __forceinline__ f16x8 pair_operand(const uint2 &lo, const uint2 &hi) 
 // GEN = false: PALU-shaped layouts (a 4-bit segment, then 2-bit channels),
 // closed-form record addressing; GEN = true: any coder, through LDS tables.
 template <int KS, int NBV, int NQ, bool GEN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KS + NBV <= 2 ? 4 : 1)))
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(KS + NBV <= 2 ? 4 : 1)))
 void prefill_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -292,12 +293,12 @@ void prefill_kernel(PrefillArgs a) {
     // ---- the tiles' constant parts, written once for every buffer: key
     //      positions past the last channel block are 0; value channel r_V is
     //      all ones and the channels after it are 0
-    for (int e = tid; e < kPfRing * 32 * (4 * KS - nbk); e += 256) {
+    for (int e = tid; e < kPfRing * 32 * (4 * KS - nbk); e += kPfThreads) {
         const int bf = e & (kPfRing - 1), r = e / kPfRing, t = r & 31, q = nbk + (r >> 5);
         *reinterpret_cast<uint4 *>(lds + L.tiles + bf * (L.ktile + L.vtile) + (t * krow + 8 * q) * 2) =
             make_uint4(0u, 0u, 0u, 0u);
     }
-    for (int e = tid; e < kPfRing * 4 * (16 * NBV - rv); e += 256) {
+    for (int e = tid; e < kPfRing * 4 * (16 * NBV - rv); e += kPfThreads) {
         const int bf = e & (kPfRing - 1), r = e / kPfRing, tb = r & 3, c = rv + (r >> 2);
         const uint32_t w = c == rv ? 0x3C003C00u : 0u;
         *reinterpret_cast<uint4 *>(lds + L.tiles + bf * (L.ktile + L.vtile) + L.ktile + (c * kVRow + 8 * tb) * 2) =
@@ -498,7 +499,7 @@ void prefill_kernel(PrefillArgs a) {
     {
         const float4 *bv = reinterpret_cast<const float4 *>(a.v.basis_cm + rw.slot * a.v.set_bcm +
                                                             static_cast<int64_t>(grp) * rv * kHeadDim);
-        for (int e = tid; e < kHeadDim * rv / 4; e += 256) reinterpret_cast<float4 *>(bl)[e] = bv[e];
+        for (int e = tid; e < kHeadDim * rv / 4; e += kPfThreads) reinterpret_cast<float4 *>(bl)[e] = bv[e];
         if (tid < kHeadDim) ml[tid] = a.v.mu[rw.slot * a.v.set_mu + grp * kHeadDim + tid];
     }
     __syncthreads();
@@ -533,7 +534,7 @@ hipError_t launch_prefill_tg(const PrefillArgs &a, size_t lds_bytes, hipStream_t
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL((prefill_kernel<KS, NBV, NQ, GEN>), dim3(a.tiles_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
+    hipLaunchKernelGGL((prefill_kernel<KS, NBV, NQ, GEN>), dim3(a.tiles_max, a.Hkv, a.B), dim3(kPfThreads), lds_bytes, s, a);
     return hipGetLastError();
 }
 
