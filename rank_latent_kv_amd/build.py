@@ -25,10 +25,11 @@ DEVICE = [f"--offload-arch={ARCH}", "-fhip-fp32-correctly-rounded-divide-sqrt",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_SOURCES = ["palu_host.cpp", "palu_eigen.cpp"]
 DEVICE_SOURCES = ["palu_kernels.hip", "palu_decode.hip", "palu_prefill.hip"]
-# Per-source extras.  The attention kernels' inputs are never NaN (reading
-# the max of MFMA results needs no quieting), and their MFMA accumulators
-# stay in ordinary VGPRs (no AGPR copies around the softmax).
-SOURCE_FLAGS = {"palu_prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+# Per-source extras.  No kernel handles NaN inputs (the quantiser's and the
+# softmax's max / min need no quieting); the attention kernels' MFMA
+# accumulators stay in ordinary VGPRs (no AGPR copies around the softmax).
+SOURCE_FLAGS = {"palu_kernels.hip": ["-fno-honor-nans"],
+                "palu_prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
                 "palu_decode.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
