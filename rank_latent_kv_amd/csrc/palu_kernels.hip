@@ -215,13 +215,14 @@ struct EncLane {
 };
 
 // Quantise / store channel c of this lane's latent (see the section comment).
-__device__ __forceinline__ void encode_channel(const EncodeArgs &a, const TensorDev &T, const EncLane &e, int c,
-                                               float lat, const float *told, float *tnew, uint32_t *rec_lds,
-                                               uint16_t *rec16, int layout, bool any_complete) {
-    const int r = T.r;
+// ct = the channel's entry of the code table: bit of token 0, bits per
+// token, width, metadata word.
+__device__ __forceinline__ void encode_channel(const EncLane &e, int c, int r, bool fp16, const int4 ct, float lat,
+                                               const float *told, float *tnew, uint32_t *rec_lds, uint16_t *rec16,
+                                               bool any_complete) {
     // fp16 latents have no tail buffer (told and tnew are null): only new
     // positions are stored
-    if (T.fp16_latents) {
+    if (fp16) {
         if (e.is_new) rec16[c * 32 + e.t] = static_cast<uint16_t>(f2h_bits(lat));
         return;
     }
@@ -234,8 +235,8 @@ __device__ __forceinline__ void encode_channel(const EncodeArgs &a, const Tensor
     // groups use the result
     const float mn = half_min(lat), mx = half_max(lat);
     if (e.complete) {
-        const int2 bw = code_bit(T.cd, layout, c, e.t);   // bit position, width (c is wave-uniform)
-        const float levels = static_cast<float>((1 << bw.y) - 1);
+        const int bit = ct.x + e.t * ct.y;
+        const float levels = static_cast<float>((1 << ct.z) - 1);
         const float scale = (mx - mn) / levels;
         int q = 0;
         if (scale > 0.0f) {
@@ -244,8 +245,8 @@ __device__ __forceinline__ void encode_channel(const EncodeArgs &a, const Tensor
             q = static_cast<int>(uq);
         }
         // codes never straddle a word: a code of width w sits at a multiple of w
-        if (q) atomicOr(rec_lds + (bw.x >> 5), static_cast<uint32_t>(q) << (bw.x & 31));
-        if (e.t == 0) rec_lds[T.cd.meta0 + c] = f2h_bits(scale) | (f2h_bits(mn) << 16);
+        if (q) atomicOr(rec_lds + (bit >> 5), static_cast<uint32_t>(q) << (bit & 31));
+        if (e.t == 0) rec_lds[ct.w] = f2h_bits(scale) | (f2h_bits(mn) << 16);
     } else if (e.touched && e.is_new) {
         tnew[e.t * r + c] = lat;
     }
@@ -312,11 +313,12 @@ __device__ __forceinline__ void project_to_lds(const uint16_t *xrow, const float
 // Dynamic LDS of one encode workgroup: basis (chunks of 32 channels, each
 // [D][32] except the last, [D][nc rounded up to 4]: D rp floats in all) +
 // mean [D] + per wave two record buffers (none for fp16 latents) and a
-// [32 channels][64 lanes] latent buffer.
+// [32 channels][64 lanes] latent buffer, then the code table (one int4 per
+// channel).
 __host__ __device__ inline int encode_rec_words(int words, bool fp16) { return fp16 ? 0 : words; }
 __host__ __device__ inline int encode_lds_bytes(int r, int words, bool fp16) {
     const int rp = (r + 3) & ~3;
-    return (kHeadDim * rp + kHeadDim + kEncWaves * (2 * encode_rec_words(words, fp16) + 32 * 64)) * 4;
+    return (kHeadDim * rp + kHeadDim + kEncWaves * (2 * encode_rec_words(words, fp16) + 32 * 64) + 4 * r) * 4;
 }
 
 template <bool BF16>
@@ -357,6 +359,15 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
         }
         if (tid < kHeadDim) msh[tid] = T.mu[slot * T.set_mu + grp * kHeadDim + tid];
     }
+    // code table: per channel the record bit of token 0, the bits between
+    // consecutive tokens, the width and the metadata word (read as one
+    // broadcast per channel instead of a walk over the segment list)
+    const int WR = encode_rec_words(W, T.fp16_latents);
+    int4 *ctab = reinterpret_cast<int4 *>(msh + kHeadDim + kEncWaves * (2 * WR + 32 * 64));
+    if (tid < r && !T.fp16_latents) {
+        const int2 b0 = code_bit(T.cd, tz, tid, 0), b1 = code_bit(T.cd, tz, tid, 1);
+        ctab[tid] = make_int4(b0.x, b1.x - b0.x, b0.y, T.cd.meta0 + tid);
+    }
     __syncthreads();
     const int jp = (j0 >> 1) + u;                    // group pair of this wave
     if (2 * jp > jl) return;                         // wave-uniform; no barrier follows
@@ -371,10 +382,10 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     e.touched = j >= j0 && j <= jl;
     e.complete = e.touched && o + n >= 32 * j + 32;
     // complete groups that get a quantised record (fp16 latents have none)
-    const bool any_complete = !T.fp16_latents && __any(e.complete);
+    const bool fp16 = T.fp16_latents;
+    const bool any_complete = !fp16 && __any(e.complete);
     const int64_t head_base = static_cast<int64_t>(slot) * a.H + h;
 
-    const int WR = encode_rec_words(W, T.fp16_latents);
     uint32_t *rec_lds = reinterpret_cast<uint32_t *>(msh + kHeadDim) + (wv * 2 + e.half) * WR;
     float *lat = msh + kHeadDim + kEncWaves * 2 * WR + wv * 32 * 64;   // this wave's [32][64]
     if (any_complete) {
@@ -419,7 +430,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
             default: project_to_lds<32, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
         }
         for (int k = 0; k < nc; ++k)
-            encode_channel(a, T, e, c0 + k, lat[k * 64 + lane], told, tnew, rec_lds, rec16, tz, any_complete);
+            encode_channel(e, c0 + k, r, fp16, fp16 ? make_int4(0, 0, 0, 0) : ctab[c0 + k], lat[k * 64 + lane], told,
+                           tnew, rec_lds, rec16, any_complete);
     }
 
     // 3. complete groups: LDS record -> memory
