@@ -314,6 +314,53 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                    km2 = vgpr_const(0x00030003u);
     const FastDiv div_nbk4(a.inv_nbk4);
     const int tb0 = wv * S;                          // pass-relative group of slot 0
+    // (a) below gathers S nbk 4 (slot, block, pair) items per pass.  When
+    // one round of 64 lanes covers them, each lane's item is fixed: its
+    // slot, the two metadata words it reads (padding channels read word 0
+    // and are masked to 0) and the word it writes are computed once here.
+    const bool kp_one = S * nbk * 4 <= 64;
+    int kp_m = 0, kp_ca = 0, kp_cb = 0, kp_dst = 0;
+    uint32_t kp_ma = 0u, kp_mb = 0u;
+    if (kp_one && lane < S * nbk * 4) {
+        const int m = div_nbk4.quo(lane), r2 = lane - m * nbk * 4;
+        const int q = r2 >> 2, k = r2 & 3;
+        int chan0, chanend;
+        if constexpr (GEN) {
+            const int cc = blk[q].w;
+            chan0 = cc & 0xFFFF;
+            chanend = cc >> 16;
+        } else {
+            chan0 = q < nbh ? 8 * q : nhk + 8 * (q - nbh);
+            chanend = q < nbh ? nhk : rk;
+        }
+        kp_m = m;
+        kp_ca = chan0 + k < chanend ? kmeta + chan0 + k : 0;
+        kp_cb = chan0 + k + 4 < chanend ? kmeta + chan0 + k + 4 : 0;
+        kp_ma = chan0 + k < chanend ? 0xFFFFFFFFu : 0u;
+        kp_mb = chan0 + k + 4 < chanend ? 0xFFFFFFFFu : 0u;
+        kp_dst = (m * nbk + q) * 8 + k;
+    }
+    // the score operand B of the first two score steps (the same in every
+    // pass), held in registers when there are at most two steps
+    auto score_b = [&](int u) -> uint4 {
+        const int p = 4 * u + kb;
+        int q, j;
+        if constexpr (S % 4 == 0) {
+            q = (4 * u) / S;
+            j = p - q * S;
+        } else {
+            q = p / S;
+            j = p - q * S;
+        }
+        const int qc = q < nbk ? q : nbk - 1;
+        const bool ok = p < npair && live_n && j == slot_n;
+        return ok ? qt16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
+    };
+    uint4 bq_pre[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+    if (nub <= 2) {
+        bq_pre[0] = score_b(0);
+        if (nub == 2) bq_pre[1] = score_b(1);
+    }
     for (int pi = 0; pi < npass; ++pi) {
         if (pi + 1 < npass) copy_pass(pi + 1);       // into the other buffer
         else if (do_tail) copy_tail();               // the last pass leaves buffer tb free
@@ -326,7 +373,16 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         // (a) this wave's K scale/zero pairs per (slot, channel block):
         //     words 0..3 scale pairs (k, k + 4), words 4..7 zero pairs;
         //     padding channels are 0; slots past the pass repeat its last group
-        for (int e = lane; e < S * nbk * 4; e += 64) {
+        if (kp_one) {
+            if (lane < S * nbk * 4) {
+                int tg = tb0 + kp_m;
+                tg = tg < npg ? tg : npg - 1;
+                const uint32_t *rec = stage + koff + tg * WK;
+                const uint32_t wa = rec[kp_ca] & kp_ma, wb = rec[kp_cb] & kp_mb;
+                kpw[kp_dst] = perm_b32(wb, wa, 0x05040100u);
+                kpw[kp_dst + 4] = perm_b32(wb, wa, 0x07060302u);
+            }
+        } else for (int e = lane; e < S * nbk * 4; e += 64) {
             const int m = div_nbk4.quo(e), r2 = e - m * nbk * 4;
             const int q = r2 >> 2, k = r2 & 3;
             int chan0, chanend;
@@ -353,7 +409,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 
         // (b) scores
         f4 sacc0 = {0.0f, 0.0f, 0.0f, 0.0f}, sacc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int u = 0; u < nub; ++u) {
+        auto score_step = [&](int u, const uint4 bq) {
             const int p = 4 * u + kb;
             int q, j;
             if constexpr (S % 4 == 0) {
@@ -371,8 +427,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             const uint32_t *rec = stage + koff + tg * WK;
             const uint4 *kp = reinterpret_cast<const uint4 *>(kpw + (j * nbk + qc) * 8);
             const uint4 sp = kp[0], zp = kp[1];
-            const bool ok = p < npair && live_n && j == slot_n;
-            const uint4 bq = ok ? qt16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
             const f16x8 bop = as_h8(bq.x, bq.y, bq.z, bq.w);
             f16x8 a0, a1;
             if constexpr (!GEN) {
@@ -410,6 +464,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             }
             sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bop, sacc0, 0, 0, 0);
             sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bop, sacc1, 0, 0, 0);
+        };
+        if (nub <= 2) {
+            score_step(0, bq_pre[0]);
+            if (nub == 2) score_step(1, bq_pre[1]);
+        } else {
+            for (int u = 0; u < nub; ++u) score_step(u, score_b(u));
         }
 
         // (c) online softmax of stream ln (rows 4*kb + v of both 16-token halves)
