@@ -313,16 +313,22 @@ __device__ __forceinline__ void project_to_lds(const uint16_t *xrow, const float
 // Dynamic LDS of one encode workgroup: basis (chunks of 32 channels, each
 // [D][32] except the last, [D][nc rounded up to 4]: D rp floats in all) +
 // mean [D] + per wave two record buffers (none for fp16 latents) and a
-// [32 channels][64 lanes] latent buffer, then the code table (one int4 per
-// channel).
+// [channels][64 lanes] latent buffer (rows for the widest chunk: r rounded
+// up to 4, at most 32), then the code table (one int4 per channel).
 __host__ __device__ inline int encode_rec_words(int words, bool fp16) { return fp16 ? 0 : words; }
+__host__ __device__ inline int encode_lat_rows(int r) { return ((r + 3) & ~3) < 32 ? ((r + 3) & ~3) : 32; }
 __host__ __device__ inline int encode_lds_bytes(int r, int words, bool fp16) {
     const int rp = (r + 3) & ~3;
-    return (kHeadDim * rp + kHeadDim + kEncWaves * (2 * encode_rec_words(words, fp16) + 32 * 64) + 4 * r) * 4;
+    return (kHeadDim * rp + kHeadDim + kEncWaves * (2 * encode_rec_words(words, fp16) + encode_lat_rows(r) * 64) +
+            4 * r) * 4;
 }
 
+// Five waves per SIMD (at most 96 VGPRs; the latent buffer is sized by the
+// rank so that LDS admits five workgroups per CU at ranks up to 16): the
+// projection's LDS broadcast reads and the quantiser's reductions are latency
+// chains that the extra wave hides.
 template <bool BF16>
-__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void encode_kernel(EncodeArgs a) {
     extern __shared__ __align__(16) float esh[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -363,7 +369,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     // consecutive tokens, the width and the metadata word (read as one
     // broadcast per channel instead of a walk over the segment list)
     const int WR = encode_rec_words(W, T.fp16_latents);
-    int4 *ctab = reinterpret_cast<int4 *>(msh + kHeadDim + kEncWaves * (2 * WR + 32 * 64));
+    const int LR = encode_lat_rows(r);
+    int4 *ctab = reinterpret_cast<int4 *>(msh + kHeadDim + kEncWaves * (2 * WR + LR * 64));
     if (tid < r && !T.fp16_latents) {
         const int2 b0 = code_bit(T.cd, tz, tid, 0), b1 = code_bit(T.cd, tz, tid, 1);
         ctab[tid] = make_int4(b0.x, b1.x - b0.x, b0.y, T.cd.meta0 + tid);
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     const int64_t head_base = static_cast<int64_t>(slot) * a.H + h;
 
     uint32_t *rec_lds = reinterpret_cast<uint32_t *>(msh + kHeadDim) + (wv * 2 + e.half) * WR;
-    float *lat = msh + kHeadDim + kEncWaves * 2 * WR + wv * 32 * 64;   // this wave's [32][64]
+    float *lat = msh + kHeadDim + kEncWaves * 2 * WR + wv * LR * 64;   // this wave's [LR][64]
     if (any_complete) {
         for (int w = e.t; w < W; w += 32) rec_lds[w] = 0u;
     }
