@@ -752,6 +752,44 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
     const float *bv = a.v.basis_cm + slot * a.v.set_bcm + static_cast<int64_t>(grp) * rv * kHeadDim;
     const float *mv = a.v.mu + slot * a.v.set_mu + grp * kHeadDim;
 
+    if (ns <= 64 && rv <= 16) {
+        // Register path: lane s holds split s's (m, l, latent output) and,
+        // for its two outputs d = 2 lane, 2 lane + 1, the value basis of every
+        // channel and the mean; every load is issued before the first use, and
+        // the merge is a handful of wave reductions (no LDS round trips).
+        const bool live = lane < ns;
+        const float *ps = part + lane * (rv + 2);
+        const float m = live ? ps[0] : -INFINITY;
+        const float ls = live ? ps[1] : 0.0f;
+        float oz[16];
+        float2 bz[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            oz[c] = 0.0f;
+            bz[c] = make_float2(0.0f, 0.0f);
+            if (c < rv) {
+                if (live) oz[c] = ps[2 + c];
+                bz[c] = *reinterpret_cast<const float2 *>(bv + c * kHeadDim + 2 * lane);
+            }
+        }
+        const float2 mu = *reinterpret_cast<const float2 *>(mv + 2 * lane);
+        const float M = wave_max(m);
+        const float w = live ? exp2f(m - M) : 0.0f;
+        const float inv_l = 1.0f / wave_sum(w * ls);
+        float o0 = mu.x, o1 = mu.y;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            if (c < rv) {
+                const float oc = wave_sum(w * oz[c]) * inv_l;
+                o0 = fmaf(bz[c].x, oc, o0);
+                o1 = fmaf(bz[c].y, oc, o1);
+            }
+        }
+        reinterpret_cast<uint32_t *>(a.out + (static_cast<int64_t>(i) * a.Hq + qh) * kHeadDim)[lane] =
+            out_bits(o0, a.bf16) | (out_bits(o1, a.bf16) << 16);
+        return;
+    }
+
     // 1. copy to LDS: whole 16-byte pieces of the partials, the basis
     //    (128 rv floats) and the mean; the < 4 trailing partial floats singly
     {
