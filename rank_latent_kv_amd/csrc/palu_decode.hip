@@ -112,8 +112,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int ln = lane & 15, kb = lane >> 4;
 
-    // ---- work item: grid (split, kv head, row); one 16-byte row descriptor
-    const int s = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+    // ---- work item: grid (kv head, row, split), kv head fastest.  Workgroups
+    //      go to the XCDs round-robin by linear id, so every XCD gets the same
+    //      mix of heads and rows (with the split fastest, ragged rows left
+    //      the XCDs that draw high split indices idle while others queued
+    //      work); one 16-byte row descriptor
+    const int h = blockIdx.x, i = blockIdx.y, s = blockIdx.z;
     const AttendRow rw = a.row[i];
     // Pin the kernel arguments the prologue needs before the first branch so
     // their scalar loads are issued together (one round trip instead of a
@@ -872,14 +876,12 @@ size_t attend_lds_bytes(int gqa, int nbk, int r_k, int r_v, int words_k, int wor
 
 template <int G, int NBV, bool VQ, bool GEN>
 static hipError_t launch_attend_tg(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
-    static bool configured = false;
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<G, NBV, VQ, GEN>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
-    hipLaunchKernelGGL((attend_kernel<G, NBV, VQ, GEN>), dim3(a.nsplit_max, a.Hkv, a.B), dim3(256), lds_bytes, s, a);
+    // set once per process (thread-safe static initialisation)
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<G, NBV, VQ, GEN>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((attend_kernel<G, NBV, VQ, GEN>), dim3(a.Hkv, a.B, a.nsplit_max), dim3(256), lds_bytes, s, a);
     return hipGetLastError();
 }
 
@@ -924,13 +926,11 @@ hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
 }
 
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(combine_kernel),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // set once per process (thread-safe static initialisation)
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(combine_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
     const size_t lds = static_cast<size_t>(combine_lds_floats(a.nsplit_max, a.v.r)) * sizeof(float);
     hipLaunchKernelGGL(combine_kernel, dim3(a.Hq, a.B), dim3(64), lds, s, a);
     return hipGetLastError();

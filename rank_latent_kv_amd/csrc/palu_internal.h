@@ -142,7 +142,7 @@ struct AttendArgs {
     // the key channel blocks
     float inv_rv, inv_nbk4;
     int bf16;                 // q and out are bf16 (else fp16)
-    AttendRow row[kMaxCallSeqs];       // grid z order (longest first)
+    AttendRow row[kMaxCallSeqs];       // grid y order (longest first)
     int nsplit_call[kMaxCallSeqs];     // splits of call row i (combine)
     int slot_call[kMaxCallSeqs];       // cache slot of call row i (combine)
 };

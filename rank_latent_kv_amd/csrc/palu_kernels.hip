@@ -590,13 +590,11 @@ hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s) {
 
 template <bool BF16>
 static hipError_t launch_append1_t(const EncodeArgs &a, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(append1_kernel<BF16>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // set once per process (thread-safe static initialisation)
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(append1_kernel<BF16>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
     const int l0 = append1_lds_bytes(a.t[0].r, a.t[0].words), l1 = append1_lds_bytes(a.t[1].r, a.t[1].words);
     hipLaunchKernelGGL(append1_kernel<BF16>, dim3(a.B * a.H, 2), dim3(kApp1Threads),
                        static_cast<size_t>(l0 > l1 ? l0 : l1), s, a);
@@ -609,13 +607,11 @@ hipError_t launch_append1(const EncodeArgs &a, hipStream_t s) {
 
 template <bool BF16>
 static hipError_t launch_encode_t(const EncodeArgs &a, int max_units, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(encode_kernel<BF16>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // set once per process (thread-safe static initialisation)
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(encode_kernel<BF16>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
     const int l0 = encode_lds_bytes(a.t[0].r, a.t[0].words, a.t[0].fp16_latents),
               l1 = encode_lds_bytes(a.t[1].r, a.t[1].words, a.t[1].fp16_latents);
     hipLaunchKernelGGL(encode_kernel<BF16>, dim3((max_units + kEncWaves - 1) / kEncWaves, a.B * a.H, 2), dim3(256),

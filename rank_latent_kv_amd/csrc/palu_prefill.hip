@@ -527,13 +527,11 @@ void prefill_kernel(PrefillArgs a) {
 template <int KS, int NBV, bool GEN>
 hipError_t launch_prefill_tg(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
     constexpr int NQ = prefill_nq_c(KS, NBV);
-    static bool configured = false;
-    if (!configured) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<KS, NBV, NQ, GEN>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    // set once per process (thread-safe static initialisation)
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<KS, NBV, NQ, GEN>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((prefill_kernel<KS, NBV, NQ, GEN>), dim3(a.tiles_max, a.Hkv, a.B), dim3(kPfThreads), lds_bytes, s, a);
     return hipGetLastError();
 }
