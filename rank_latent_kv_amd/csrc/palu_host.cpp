@@ -102,6 +102,7 @@ struct palu_cache {
     int gram_nb_cap = 0;          // Gram blocks (partials) of one launch
     int64_t gram_tab_cap = 0;     // block-table entries of one fit
     int gram_resident = 0;        // Gram workgroups the device holds at once (0: not queried yet)
+    int n_cus = 0;                // compute units of the device (0: not queried yet)
     // byte offsets of each region inside the bound buffer
     size_t off_basis[2]{}, off_bt16[2]{}, off_bcm[2]{}, off_mu[2]{}, off_rec[2]{}, off_tail[2]{};
     size_t off_gram_part = 0, off_gram_out = 0, off_seg = 0, off_attend = 0, total = 0;
@@ -452,6 +453,18 @@ void gram_blocks(const int32_t *seq_lens, int B, int hpg, int G, int nb_target, 
 // Full Gram blocks per (tensor, group): as many as the device holds at once
 // over both tensors and all groups (one round of equal blocks), within
 // gram_nb_target.
+// Compute units of the current device (256 when the query fails).
+int device_cus(palu_cache *c) {
+    if (c->n_cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        c->n_cus = n;
+    }
+    return c->n_cus;
+}
+
 int gram_target(palu_cache *c) {
     if (c->gram_resident == 0) {
         int n = 0;
@@ -929,6 +942,10 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
             chunk = c->cfg.split_groups;
         } else {
             chunk = round_up(std::max<int64_t>(1, (units + kAttendTargetGroups - 1) / kAttendTargetGroups), per_pass);
+            // at least two passes per split while that still leaves a
+            // workgroup per CU: the prologue and the merge of a split are
+            // then paid once per two passes
+            if (chunk < 2 * per_pass && units / (2 * per_pass) >= device_cus(c)) chunk = 2 * per_pass;
         }
         chunk = std::max<int64_t>(chunk, (max_full + kMaxSplits - 1) / kMaxSplits);
         int nsplit_max = 1;
@@ -939,7 +956,7 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
             aa.nsplit_call[i] = ns;
             nsplit_max = std::max(nsplit_max, ns);
         }
-        // longest rows first in the grid's z order (stable, so equal lengths keep call order)
+        // longest rows first in the grid's y order (stable, so equal lengths keep call order)
         std::stable_sort(aa.row, aa.row + nb, [](const AttendRow &x, const AttendRow &y) { return x.len > y.len; });
         const size_t lds = attend_lds_bytes(c->gqa, coder_blocks(aa.k.cd), aa.k.r, aa.v.r, aa.k.words, aa.v.words, vq);
         if (lds > kAttendLdsMax)
