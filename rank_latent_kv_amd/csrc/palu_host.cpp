@@ -932,8 +932,9 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
         // split size: a multiple of the groups one workgroup pass covers
         // (double-buffered passes keep the LDS independent of it), about
         // kAttendTargetGroups workgroups per launch, and large enough for the
-        // split limit; the same for every row, so a row has
-        // ceil(groups / chunk) splits
+        // split limit; launches with fewer groups than CUs x one pass split
+        // finer.  The same for every row, so a row has ceil(groups / chunk)
+        // splits
         const int per_pass = 4 * (16 / c->gqa);
         const bool vq = !aa.v.fp16_latents;
         auto round_up = [](int64_t v, int64_t m) { return (v + m - 1) / m * m; };
@@ -941,11 +942,20 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
         if (c->cfg.split_groups > 0) {
             chunk = c->cfg.split_groups;
         } else {
-            chunk = round_up(std::max<int64_t>(1, (units + kAttendTargetGroups - 1) / kAttendTargetGroups), per_pass);
-            // at least two passes per split while that still leaves a
-            // workgroup per CU: the prologue and the merge of a split are
-            // then paid once per two passes
-            if (chunk < 2 * per_pass && units / (2 * per_pass) >= device_cus(c)) chunk = 2 * per_pass;
+            const int cus = device_cus(c);
+            if (units / per_pass < cus) {
+                // too few groups to fill the CUs with full passes: spread
+                // them, about one workgroup per CU (a launch this small is
+                // bound by the latency of one workgroup)
+                chunk = std::max<int64_t>(1, (units + cus - 1) / cus);
+            } else {
+                chunk = round_up(std::max<int64_t>(1, (units + kAttendTargetGroups - 1) / kAttendTargetGroups),
+                                 per_pass);
+                // at least two passes per split while that still leaves a
+                // workgroup per CU: the prologue and the merge of a split
+                // are then paid once per two passes
+                if (chunk < 2 * per_pass && units / (2 * per_pass) >= cus) chunk = 2 * per_pass;
+            }
         }
         chunk = std::max<int64_t>(chunk, (max_full + kMaxSplits - 1) / kMaxSplits);
         int nsplit_max = 1;
