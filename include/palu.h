@@ -225,7 +225,9 @@ int palu_decode_attend(palu_cache *cache, const void *q, void *out,
  * Stream-ordered; reads only the cache (no scratch), so calls may overlap.
  * fp32 scores and accumulation, fp16 weights into the value contraction.
  * Errors: INVALID_ARG, NOT_BOUND, NOT_FITTED, CAPACITY (slot out of range or
- * n_q beyond the slot's length), UNSUPPORTED (LDS need above 160 KiB), HIP. */
+ * n_q beyond the slot's length), UNSUPPORTED (LDS need above 160 KiB, or
+ * more than 65535 query tiles per row: T_stride above 65535 x the tile's
+ * query positions, 16 x 4 x (query tiles per wave) / GQA), HIP. */
 int palu_prefill_attend(palu_cache *cache, const void *q, void *out,
                         const int32_t *seq_ids, const int32_t *n_q, int32_t B,
                         int32_t T_stride, float softmax_scale, void *stream);

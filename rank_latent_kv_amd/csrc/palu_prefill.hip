@@ -105,12 +105,16 @@ void prefill_kernel(PrefillArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, kb = lane >> 4;
-    const int i = blockIdx.z, h = blockIdx.y;
+    // grid (kv head, query tile, row), head fastest: round-robin XCD
+    // placement keeps the tiles of one (row, kv head) on one XCD, whose L2
+    // then serves their shared records and basis, and the row slowest keeps
+    // the rows in flight (the records the L2s must hold) few
+    const int h = blockIdx.x, i = blockIdx.z;
     const PrefillRow rw = a.row[i];
     const int nq = rw.nq;
     const int ntiles = (nq + a.qp - 1) / a.qp;
-    if (static_cast<int>(blockIdx.x) >= ntiles) return;   // whole workgroup, before any barrier
-    const int x = ntiles - 1 - static_cast<int>(blockIdx.x);   // longest tiles first
+    if (static_cast<int>(blockIdx.y) >= ntiles) return;   // whole workgroup, before any barrier
+    const int x = ntiles - 1 - static_cast<int>(blockIdx.y);   // longest tiles first
     const int g = a.gqa, len = rw.len;
     const int nfull = len >> 5, ntail = len & 31;
     const int grp = h / a.hpg;
@@ -532,7 +536,8 @@ hipError_t launch_prefill_tg(const PrefillArgs &a, size_t lds_bytes, hipStream_t
         hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<KS, NBV, NQ, GEN>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((prefill_kernel<KS, NBV, NQ, GEN>), dim3(a.tiles_max, a.Hkv, a.B), dim3(kPfThreads), lds_bytes, s, a);
+    hipLaunchKernelGGL((prefill_kernel<KS, NBV, NQ, GEN>), dim3(a.Hkv, a.tiles_max, a.B), dim3(kPfThreads), lds_bytes, s,
+                       a);
     return hipGetLastError();
 }
 
