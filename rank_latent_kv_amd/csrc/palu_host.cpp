@@ -39,7 +39,7 @@ constexpr int kGramMaxRowsPerBlock = 8192;   // bounds fp32 accumulation per blo
 // full Gram blocks per (tensor, group) at most: 1024 workgroups a fit
 inline int gram_nb_target(int G) { return std::max(1, 512 / G); }
 constexpr int kAttendTargetGroups = 1024;    // workgroups aimed for per decode launch
-constexpr int64_t kMaxGridZ = 65535;         // largest grid z dimension of a launch
+constexpr int64_t kMaxGridYZ = 65535;        // largest grid y or z dimension of a launch
 constexpr size_t kAttendLdsMax = 160 * 1024; // LDS per workgroup on gfx950
 
 int n_hi_of(int r, float frac) {
@@ -1015,7 +1015,7 @@ PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const 
     const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(c->D));
     const int ks = prefill_ks(coder_blocks(kd.cd)), nbv = prefill_nbv(vd.r);
     const int qp = 16 * kPrefillWaves * prefill_nq(ks, nbv) / c->gqa;   // query positions per workgroup
-    if ((static_cast<int64_t>(T_stride) + qp - 1) / qp > kMaxGridZ)
+    if ((static_cast<int64_t>(T_stride) + qp - 1) / qp > kMaxGridYZ)
         return fail(PALU_ERR_UNSUPPORTED, "prefill: more query tiles per row than the grid holds (T_stride too large)");
     const size_t row_elems = static_cast<size_t>(c->Hq) * T_stride * c->D;
     for (int b0 = 0; b0 < B; b0 += kMaxCallSeqs) {
