@@ -20,7 +20,7 @@ namespace {
 
 // -------------------------------------------------------------- attend ----
 //
-// Workgroup = (call row i, kv head h, split s).  Split s covers complete
+// Workgroup = (kv head h, call row i, split s).  Split s covers complete
 // token groups [s*chunk, min(nfull, (s+1)*chunk)); the last split also
 // covers the incomplete group (fp32 tail latents).  With the query absorbed
 // into the key basis, score_t = qs * q . (V_K l_t + mu_K) = qt . l_t + const
@@ -95,7 +95,7 @@ __host__ __device__ inline AttendLds attend_lds(int g, int nbk, int rk, int rv, 
 }
 
 
-// Workgroup = (call row i, kv head h, split s); see the section comment.
+// Workgroup = (kv head h, call row i, split s); see the section comment.
 // GEN = false serves PALU-shaped layouts (a 4-bit segment, then 2-bit
 // channels) with closed-form record addressing; GEN = true any coder, through
 // a per-block address table in LDS.

@@ -193,7 +193,7 @@ hipError_t launch_encode(const EncodeArgs &a, int max_units, hipStream_t s);
 // Appends of at most one token per row: one workgroup per (call row x head,
 // tensor), one thread per latent channel.
 hipError_t launch_append1(const EncodeArgs &a, hipStream_t s);
-// Grid (nsplit_max, Hkv, B): one workgroup per (split, kv head, row).
+// Grid (Hkv, B, nsplit_max): one workgroup per (kv head, row, split), the head fastest.
 hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s);
 // Position-ordered fp16 copy of a basis [G][D][r]: dst[g][n][d] =

@@ -10,7 +10,7 @@
 // accumulates o_lat = sum_t w_t lv_t in latent space and projects once at
 // the end: o = V_V o_lat / l + mu_V.
 //
-// Workgroup = (query tile x, kv head h, call row i), four waves.  Its 64 NQ
+// Workgroup = (kv head h, query tile x, call row i), four waves.  Its 64 NQ
 // columns are (query position, query head) pairs: column c holds position
 // c / g and head c % g of the kv head's g query heads.  Wave w owns columns
 // [16 NQ w, 16 NQ (w + 1)) as NQ MFMA tiles of 16.  The key loop walks the
