@@ -1040,9 +1040,14 @@ PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const 
             pa.row[i].slot = slot;
             pa.row[i].len = c->len[slot];
             pa.row[i].nq = n_q ? n_q[b0 + i] : T_stride;
-            pa.row[i].sel = c->sel[slot];
+            pa.row[i].sel_qi = c->sel[slot] | (i << 1);
             tiles = std::max(tiles, (pa.row[i].nq + qp - 1) / qp);
         }
+        // heaviest rows first in the grid's z order (the causal work of a row
+        // grows with its query count and length; stable for equal rows)
+        std::stable_sort(pa.row, pa.row + nb, [](const PrefillRow &x, const PrefillRow &y) {
+            return static_cast<int64_t>(x.nq) * x.len > static_cast<int64_t>(y.nq) * y.len;
+        });
         if (tiles == 0) continue;
         pa.tiles_max = tiles;
         hipError_t e = launch_prefill(pa, lds, s);

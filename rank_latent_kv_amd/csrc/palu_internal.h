@@ -149,8 +149,11 @@ struct AttendArgs {
 
 // One call row of a prefill attention launch: the queries are the last nq
 // positions [len - nq, len) of the slot.
+// One prefill row (16 bytes): cache slot, stored length, queries, and the
+// tail buffer in use | call index of the row << 1 (rows are launched
+// heaviest first; the call index addresses its queries and outputs).
 struct PrefillRow {
-    int slot, len, nq, sel;
+    int slot, len, nq, sel_qi;
 };
 
 struct PrefillArgs {

@@ -111,6 +111,7 @@ void prefill_kernel(PrefillArgs a) {
     // the rows in flight (the records the L2s must hold) few
     const int h = blockIdx.x, i = blockIdx.z;
     const PrefillRow rw = a.row[i];
+    const int64_t ci = rw.sel_qi >> 1;                       // the row's index in the call
     const int nq = rw.nq;
     const int ntiles = (nq + a.qp - 1) / a.qp;
     if (static_cast<int>(blockIdx.y) >= ntiles) return;   // whole workgroup, before any barrier
@@ -148,7 +149,7 @@ void prefill_kernel(PrefillArgs a) {
         const int c = c_lo + 16 * t + ln, pl = c / g, hd = c - pl * g;
         const int qi = min(q0 + pl, qlast);
         pcol[t] = pbase + qi;
-        qsrc[t] = a.q + ((static_cast<int64_t>(i) * a.Hq + h * g + hd) * a.T_stride + qi) * kHeadDim;
+        qsrc[t] = a.q + ((ci * a.Hq + h * g + hd) * a.T_stride + qi) * kHeadDim;
     }
 
     const int64_t hb = static_cast<int64_t>(rw.slot) * a.Hkv + h;
@@ -191,8 +192,8 @@ void prefill_kernel(PrefillArgs a) {
         if (full) rec_offsets(j, koff, nk4, voff, nv4);
         const uint32_t *raw = reinterpret_cast<const uint32_t *>(lds + L.raw) + slot * L.raw_words;
         const uint32_t *kr = raw + koff, *vr = raw + voff;
-        const float *tk = a.k.tail + (hb * 2 + rw.sel) * kTokGroup * rk;
-        const float *tv = vq ? a.v.tail + (hb * 2 + rw.sel) * kTokGroup * rv : nullptr;
+        const float *tk = a.k.tail + (hb * 2 + (rw.sel_qi & 1)) * kTokGroup * rk;
+        const float *tv = vq ? a.v.tail + (hb * 2 + (rw.sel_qi & 1)) * kTokGroup * rv : nullptr;
         const uint16_t *r16 = reinterpret_cast<const uint16_t *>(vg + static_cast<int64_t>(nfull) * WV);
         for (int r = (wv - rot) & (kPfWaves - 1); r < nrk + nrv; r += kPfWaves) {
             if (r < nrk) {
@@ -523,7 +524,7 @@ void prefill_kernel(PrefillArgs a) {
             acc0 = fmaf(b.x, oc, acc0);
             acc1 = fmaf(b.y, oc, acc1);
         }
-        uint16_t *dst = a.out + ((static_cast<int64_t>(i) * a.Hq + h * g + hd) * a.T_stride + qi) * kHeadDim;
+        uint16_t *dst = a.out + ((ci * a.Hq + h * g + hd) * a.T_stride + qi) * kHeadDim;
         reinterpret_cast<uint32_t *>(dst)[lane] = out_bits(acc0, a.bf16) | (out_bits(acc1, a.bf16) << 16);
     }
 }
