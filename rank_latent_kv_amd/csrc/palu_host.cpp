@@ -444,16 +444,17 @@ void gram_blocks(const int32_t *seq_lens, int B, int hpg, int G, int nb_target, 
     for (int b = 0; b < B; ++b) n_rows += static_cast<int64_t>(hpg) * seq_lens[b];
     int64_t R = std::max<int64_t>(kGramRowsPerBlockMin, (n_rows + nb_target - 1) / nb_target);
     R = std::min<int64_t>((R + 63) / 64 * 64, kGramMaxRowsPerBlock);
+    // a segment of L rows gets k = ceil(L / R) blocks; block i takes tiles
+    // i, i + k, i + 2k, ... (concurrent blocks read adjacent tiles)
     for (int b = 0; b < B; ++b)
-        for (int hh = 0; hh < hpg; ++hh)
-            for (int64_t t0 = 0; t0 < seq_lens[b]; t0 += R)
-                out.push_back(GramBlock{b * hpg + hh, static_cast<int>(t0),
-                                        static_cast<int>(std::min<int64_t>(t0 + R, seq_lens[b])), 0});
+        for (int hh = 0; hh < hpg; ++hh) {
+            const int64_t L = seq_lens[b], k = (L + R - 1) / R;
+            for (int64_t i = 0; i < k; ++i)
+                out.push_back(GramBlock{b * hpg + hh, static_cast<int>(64 * i), static_cast<int>(L),
+                                        static_cast<int>(64 * k)});
+        }
 }
 
-// Full Gram blocks per (tensor, group): as many as the device holds at once
-// over both tensors and all groups (one round of equal blocks), within
-// gram_nb_target.
 // Compute units of the current device (256 when the query fails).
 int device_cus(palu_cache *c) {
     if (c->n_cus == 0) {
@@ -466,6 +467,9 @@ int device_cus(palu_cache *c) {
     return c->n_cus;
 }
 
+// Full Gram blocks per (tensor, group): as many as the device holds at once
+// over both tensors and all groups (one round of equal blocks), within
+// gram_nb_target.
 int gram_target(palu_cache *c) {
     if (c->gram_resident == 0) {
         int n = 0;

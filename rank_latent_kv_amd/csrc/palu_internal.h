@@ -90,9 +90,12 @@ struct TensorDev {
     int64_t set_basis, set_bt16, set_bcm, set_mu;
 };
 
-// One Gram block: tokens [t0, t1) of segment seg = b * hpg + head-in-group.
+// One Gram block of segment seg = b * hpg + head-in-group: the 64-token
+// tiles starting at t0, t0 + stride, t0 + 2 stride, ... below t1 (the
+// segment's length).  The k blocks of a segment take every k-th tile
+// (stride 64 k), so the blocks of a segment stream adjacent tiles.
 struct GramBlock {
-    int seg, t0, t1, pad;
+    int seg, t0, t1, stride;
 };
 
 struct GramArgs {

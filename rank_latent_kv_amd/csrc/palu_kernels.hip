@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
     auto load = [&](int t, uint4 (&bt)[2][2]) {
 #pragma unroll
         for (int rp = 0; rp < 2; ++rp) {
-            const int r = t * kGramTile + 2 * p + rp;
+            const int r = t * bd.stride + 2 * p + rp;
 #pragma unroll
             for (int c = 0; c < 2; ++c)
                 bt[rp][c] = r < nrows ? *reinterpret_cast<const uint4 *>(src + static_cast<int64_t>(r) * kHeadDim +
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void gram_kernel(GramArgs a) {
     };
 
     f32x16 acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {}, accs = {};
-    const int ntile = (nrows + kGramTile - 1) / kGramTile;
+    const int ntile = (nrows + bd.stride - 1) / bd.stride;
     const int f = lane & 31, kh = lane >> 5;
     auto tile = [&](int t) {
         const uint32_t(*T)[kGramTStride / 2] = tt[t & 1];
