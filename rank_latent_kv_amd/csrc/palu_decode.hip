@@ -608,6 +608,11 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         __syncthreads();                              // and every wave is done with this buffer
     }
 
+    // A wave past its main loop takes a higher issue priority (within the
+    // kernel, s_setprio): workgroups that are merging finish sooner and free
+    // their CU slots for workgroups still queued (ragged batches launch more
+    // workgroups than the CUs hold at once).
+    __builtin_amdgcn_s_setprio(2);
     // ---- 5. per-wave stream results to LDS
     const FastDiv div_rv(a.inv_rv);
     float lsum = l_run;
