@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     //      mix of heads and rows (with the split fastest, ragged rows left
     //      the XCDs that draw high split indices idle while others queued
     //      work); one 16-byte row descriptor
-    const int h = blockIdx.x, i = blockIdx.y, s = blockIdx.z;
+    const int h = blockIdx.x, i = blockIdx.y, z = blockIdx.z;
     const AttendRow rw = a.row[i];
     // Pin the kernel arguments the prologue needs before the first branch so
     // their scalar loads are issued together (one round trip instead of a
@@ -127,9 +127,14 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                  "s"(a.v.r), "s"(a.v.cd.meta0), "s"(a.v.words), "s"(a.v.fp16_latents), "s"(a.chunk), "s"(a.hpg),
                  "s"(a.Hq), "s"(a.Hkv), "s"(a.qscale), "s"(rw.slot), "s"(rw.len), "s"(rw.qi), "s"(rw.sel_ns));
     const int ns = rw.sel_ns >> 1, qi = rw.qi;
-    if (s >= ns) return;                          // whole workgroup: no barrier reached
+    if (z >= ns) return;                          // whole workgroup: no barrier reached
     const int slot = rw.slot, len = rw.len;
     const int nfull = len >> 5, ntail = len & 31;
+    // split of this workgroup: when the row's last split is a full chunk
+    // and also carries the incomplete group it is the heaviest one, and it
+    // goes first in the dispatch order; otherwise splits go in order
+    const bool tail_first = ntail > 0 && nfull - (ns - 1) * a.chunk >= a.chunk;
+    const int s = tail_first ? (z == 0 ? ns - 1 : z - 1) : z;
     const int jb = s * a.chunk;
     const int je = jb + a.chunk < nfull ? jb + a.chunk : nfull;
     const int ntg = je > jb ? je - jb : 0;
