@@ -187,3 +187,32 @@ def small_workload(name: str = "tiny", *, batch=2, n_q_heads=4, n_kv_heads=2,
                     prefill, ragged, steps, rank, energy, latent_rank, rho,
                     sigma_n, quantize_values, outlier_frac, seed, hi_bit,
                     lo_bit, hi_fraction)
+
+
+def planted_spectrum_groups(crossings, n_rows: int, head_dim: int = 128, seed: int = 0,
+                            reach: float = 0.925, floor_dims: int = 30) -> np.ndarray:
+    """Rows with an exactly planted spectrum per group, for checking rank
+    rules: fp16 [1, G, n_rows, head_dim], group g = kv head g.
+
+    Group g is 1 mu^T + U diag(sigma) W^T with U orthonormal columns
+    orthogonal to the ones vector and W orthonormal, so the centred rows have
+    singular values sigma exactly (before the fp16 rounding).  The squared
+    sigmas are crossings[g] leading directions of energy about 1 (slightly
+    decreasing), then floor_dims equal ones holding the rest, sized so that
+    the leading directions hold the fraction `reach` of the energy."""
+    rng = np.random.default_rng([seed, 23])
+    G = len(crossings)
+    out = np.empty((1, G, n_rows, head_dim), np.float16)
+    for g, k in enumerate(crossings):
+        big = 1.0 + 0.01 * np.arange(k)[::-1]
+        floor_e = (big.sum() / reach - big.sum()) / floor_dims
+        e = np.concatenate([big, np.full(floor_dims, floor_e)])
+        s = np.sqrt(e / e.sum()) * 40.0
+        n = len(s)
+        U = rng.standard_normal((n_rows, n))
+        U -= U.mean(axis=0)
+        U, _ = np.linalg.qr(U)
+        W, _ = np.linalg.qr(rng.standard_normal((head_dim, n)))
+        mu = rng.normal(0.0, 0.5, head_dim)
+        out[0, g] = (mu[None, :] + (U * s[None, :]) @ W.T).astype(np.float16)
+    return out

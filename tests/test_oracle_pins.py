@@ -122,6 +122,25 @@ def test_energy_rank_in_range_and_shared_minimum():
     assert oracle.fit(x, [256] * w.batch, 4, rank=500).r == 128
 
 
+def test_shared_rank_is_minimum_over_groups_with_distinct_ranks():
+    """Four groups with planted 90%-energy crossings at 12, 3, 20 and 7
+    directions (the smallest neither first nor last): each group's own rank
+    is its crossing and the shared rank is their minimum, 3 (PALU page, "How
+    it works", prefill step 3).  A maximum, the first or the last group's
+    rank would give 20, 12 or 7."""
+    crossings = [12, 3, 20, 7]
+    x = synth.planted_spectrum_groups(crossings, 2048, 128, seed=1)
+    for g, k in enumerate(crossings):
+        # the fp16 rows keep the planted crossing with a margin of >= 1.5%
+        c = x[0, g].astype(np.float64)
+        sv = np.linalg.svd(c - c.mean(0), compute_uv=False) ** 2
+        cum = np.cumsum(sv) / sv.sum()
+        assert cum[k - 1] >= 0.915 and (k == 1 or cum[k - 2] <= 0.885)
+    f = oracle.fit(x, [2048], 4, rank=0, tau=0.90)
+    assert list(f.r_groups) == crossings
+    assert f.r == 3
+
+
 # ------------------------------------------------------------------ SVD
 
 @pytest.mark.parametrize("D,G,H", [(32, 2, 4), (128, 1, 2)])
@@ -177,8 +196,10 @@ def test_basis_sign_convention_on_rotated_data():
 
 
 def test_planted_subspace_recovered():
-    """Group SVD recovers a planted rank-r subspace to reconstruction MSE
-    < 1e-3 (PALU page, "Evidence")."""
+    """Data drawn from an 8-dimensional subspace plus small noise: the fitted
+    rank-8 basis spans that subspace (principal-angle cosines above 0.999)
+    and projecting onto it and back leaves a mean squared error below 1e-3
+    (PALU page, "Evidence")."""
     w = synth.small_workload(n_kv_heads=2, n_head_groups=1, prefill=512, latent_rank=8,
                              rho=0.9, sigma_n=0.005, rank=8, batch=1)
     x = synth.batch_kv(w, 0, 512)
@@ -314,6 +335,47 @@ def test_quantizer_nearest_level_brute_force(bits):
         rec = c * s16 + z16
         bound = scale / 2 + levels * abs(s16 - scale) + abs(z16 - mn) + 1e-7 * abs(mx)
         assert np.all(np.abs(rec - l[:, 0]) <= bound)
+
+
+def _rint_half_even(fr):
+    """Nearest integer to a Fraction, ties to even."""
+    from fractions import Fraction
+    n = fr.numerator // fr.denominator
+    rem = fr - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantizer_division_is_correctly_rounded(bits):
+    """Groups built so that some codes change if (l - min) / scale is taken
+    as (l - min) * (1 / scale): the oracle's codes equal the exact-rational
+    definition (each fp32 operation is the exact result rounded once to fp32,
+    then round half to even), token by token, on every such token."""
+    from fractions import Fraction
+    from quant_cases import division_sensitive_group
+    rng = np.random.default_rng(40 + bits)
+    levels = 2 ** bits - 1
+    F = lambda v: Fraction(float(v))
+    sensitive = 0
+    for trial in range(12):
+        l, n_sens = division_sensitive_group(rng, bits)
+        codes, sc, zr = oracle.quantize_group(l[:, None], n_hi=1 if bits == 4 else 0,
+                                              hi_bit=4, lo_bit=2)
+        mn, mx = F(l.min()), F(l.max())
+        scale = _round_frac_to_f32(F(_round_frac_to_f32(mx - mn)) / levels)
+        rcp = _round_frac_to_f32(1 / F(scale))
+        for t in range(32):
+            d = F(_round_frac_to_f32(F(l[t]) - mn))
+            u = _round_frac_to_f32(d / F(scale))
+            q = min(max(_rint_half_even(F(u)), 0), levels)
+            assert codes[t, 0] == q, (trial, t, l[t], codes[t, 0], q)
+            q_rcp = min(max(_rint_half_even(F(_round_frac_to_f32(d * F(rcp)))), 0), levels)
+            sensitive += q_rcp != q
+        assert sc[0] == np.float16(scale).view(np.uint16)
+    # the groups do separate the two forms of the division
+    assert sensitive >= 12
 
 
 def test_quantizer_constant_and_mixed_widths():
