@@ -133,11 +133,16 @@ int palu_cache_bind(palu_cache *cache, void *dev_buf, size_t bytes);
  *   k, v     : device fp16 or bf16 (input_dtype) [B][H][S_stride][D]
  *   seq_lens : host int32 [B], 0 <= seq_lens[b] <= S_stride, sum > 0
  * Synchronous (the eigensolve runs on the host).  Empties every sequence
- * slot (stored codes of an older basis are meaningless).  With per-sequence
+ * slot (stored codes of an older basis are meaningless) once the fit has
+ * succeeded; a fit that fails on its arguments, the fit workspace, the
+ * eigensolver or the rank (CAPACITY: rank above max_rank; UNSUPPORTED: a
+ * bit schedule that codes no channel at that rank) leaves the previous
+ * bases and stored tokens as they were (a HIP error while installing the
+ * new bases leaves the cache unfitted).  With per-sequence
  * bases (per_seq_basis = 1) row b is fitted alone into slot b, as
  * palu_fit_seq with seq_ids = 0 .. B-1 (every seq_lens[b] > 0), and only
- * those slots are emptied.  Errors: INVALID_ARG, CAPACITY, NOT_BOUND, HIP
- * (also when the eigensolver does not converge). */
+ * those slots are emptied.  Errors: INVALID_ARG, CAPACITY, NOT_BOUND,
+ * UNSUPPORTED, HIP (also when the eigensolver does not converge). */
 int palu_fit(palu_cache *cache, const void *k, const void *v,
              const int32_t *seq_lens, int32_t B, int32_t S_stride, void *stream);
 
@@ -274,9 +279,31 @@ typedef struct palu_stats {
     double assigned_avg_bits;        /* max of the realised K and V rates      */
     int32_t coded_k, coded_v;        /* latent channels stored (0-bit channels dropped):
                                         the tail width returned by palu_read_codes */
+    double energy_margin_k, energy_margin_v; /* energy-rule fits with shared bases: how far
+                                        the groups' spectra sit from changing the shared
+                                        rank r, min(max_g E_g(r) - tau, tau - max_g
+                                        E_g(r - 1)) with E_g(k) the energy fraction of
+                                        group g's first k channels (the first term alone
+                                        at r = 1); -1 for explicit ranks, installed bases
+                                        and per-sequence bases                        */
 } palu_stats;
 
 int palu_get_stats(const palu_cache *cache, palu_stats *out);
+
+/* The rank rule of the last shared-basis fit of tensor 0 (K) or 1 (V)
+ * (PALU page, "How it works", prefill step 3: a rank per group, the minimum
+ * shared by all groups).  For every group g < G:
+ *   r_groups[g]    : the group's own rank (the explicit rank clamped to D,
+ *                    or the smallest k whose leading squared singular
+ *                    values reach energy_threshold of the group's total)
+ *   energy_prev[g] : energy fraction of the group's first r - 1 channels,
+ *                    r = the shared rank (0 when r = 1)
+ *   energy_at[g]   : energy fraction of its first r channels
+ * Each pointer may be NULL; the arrays are host memory of G entries.
+ * Errors: INVALID_ARG (bad tensor, per-sequence bases), NOT_FITTED (no fit
+ * of this tensor since the last bind or palu_set_basis). */
+int palu_get_fit_info(const palu_cache *cache, int32_t tensor, int32_t *r_groups,
+                      double *energy_prev, double *energy_at);
 
 /* Empties every slot, keeping the basis. */
 int palu_reset(palu_cache *cache);
@@ -317,6 +344,16 @@ int palu_record_words(const palu_cache *cache, int32_t tensor, int32_t *words);
 int palu_export_bytes(const palu_cache *cache, int32_t seq, size_t *bytes);
 int palu_export_seq(const palu_cache *cache, int32_t seq, void *host_dst, size_t bytes);
 int palu_import_seq(palu_cache *cache, int32_t seq, const void *host_src, size_t bytes);
+
+/* Measurement aid, not a step of the method: reads `bytes` (a positive
+ * multiple of 16) of device memory at buf (16-byte aligned) with 16-byte
+ * loads from `grid` workgroups of 256 threads (1 <= grid <= 65536) and
+ * writes one 32-bit fold of what each workgroup read to sink (device,
+ * grid entries), so the reads cannot be elided.  Timing it gives the read
+ * bandwidth the device sustains; run over a buffer larger than the
+ * last-level cache it also evicts that cache between timed calls.
+ * Stream-ordered.  Errors: INVALID_ARG, HIP. */
+int palu_probe_read(const void *buf, size_t bytes, void *sink, int32_t grid, void *stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char *palu_last_error(void);

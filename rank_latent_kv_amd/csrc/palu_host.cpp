@@ -122,6 +122,12 @@ struct palu_cache {
     std::vector<float> basis_h[2], mu_h[2];   // nbs sets of [G][D][r] and [G][D]
     std::vector<double> sigma_h[2];           // nbs sets of [G][D]
     std::vector<int> len, sel;
+    // rank rule of the last shared fit of each tensor: per group its own
+    // rank and the energy fractions of the first r - 1 and r channels at
+    // the shared rank r (empty after palu_set_basis)
+    bool energy_rule[2] = {false, false};
+    std::vector<int> rank_g[2];
+    std::vector<double> frac_prev[2], frac_at[2];
 
     bool quantized(int t) const { return t == 0 || cfg.quantize_values; }
     int bset(int slot) const { return per_seq ? slot : 0; }
@@ -233,6 +239,16 @@ int check_slot(const palu_cache *c, int slot) {
 void reset_seqs(palu_cache *c) {
     std::fill(c->len.begin(), c->len.end(), 0);
     std::fill(c->sel.begin(), c->sel.end(), 0);
+}
+
+// Fails when tensor t at rank rr would store no latent channel (a bit
+// schedule of zeros there); touches nothing of the cache.
+int check_coder(const palu_cache *c, int t, int rr) {
+    if (!c->quantized(t)) return PALU_OK;
+    std::vector<int> coded;
+    coder_for(c->cfg, rr, &coded);
+    if (coded.empty()) return fail(PALU_ERR_UNSUPPORTED, "the bit schedule codes no channel at rank " + std::to_string(rr));
+    return PALU_OK;
 }
 
 // Sets tensor t's coder (segments, coded channels) for its rank.
@@ -429,7 +445,10 @@ PALU_API int palu_cache_bind(palu_cache *c, void *dev_buf, size_t bytes) {
         return fail(PALU_ERR_INVALID_ARG, "bound buffer must be 256-byte aligned");
     c->dev = static_cast<char *>(dev_buf);
     c->dev_bytes = bytes;
-    for (int t = 0; t < 2; ++t) std::fill(c->ready[t].begin(), c->ready[t].end(), 0);
+    for (int t = 0; t < 2; ++t) {
+        std::fill(c->ready[t].begin(), c->ready[t].end(), 0);
+        c->rank_g[t].clear();
+    }
     reset_seqs(c);
     return PALU_OK;
 }
@@ -691,8 +710,9 @@ PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t
     int64_t total = 0;
     for (int b = 0; b < B; ++b) total += seq_lens[b];
     if (total == 0) return fail(PALU_ERR_INVALID_ARG, "no valid tokens to fit");
-    c->ready[0][0] = c->ready[1][0] = 0;
-    reset_seqs(c);
+    // Until every check below has passed (block table, eigensolver, ranks,
+    // coder) the cache keeps its bases and stored tokens: the Gram kernels
+    // write only the fit scratch.
 
     const int64_t n_rows = total * c->hpg;
     std::vector<GramBlock> tab;
@@ -722,21 +742,48 @@ PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t
     int rt[2];
     std::vector<double> s2(static_cast<size_t>(2) * G * D), sigma(static_cast<size_t>(2) * G * D);
     std::vector<float> mu(static_cast<size_t>(2) * G * D);
+    std::vector<int> rank_g[2];
+    std::vector<double> frac_prev[2], frac_at[2];
     for (int t = 0; t < 2; ++t) {
         int rr = D;
+        rank_g[t].resize(G);
         for (int g = 0; g < G; ++g) {
             const size_t off = (static_cast<size_t>(t) * G + g) * D;
             spectrum_of(pr[t * G + g], D, s2.data() + off, sigma.data() + off, mu.data() + off);
-            rr = std::min(rr, c->cfg.rank > 0 ? std::min(c->cfg.rank, D)
-                                              : energy_rank(s2.data() + off, D, c->cfg.energy_threshold));
+            rank_g[t][g] = c->cfg.rank > 0 ? std::min(c->cfg.rank, D)
+                                           : energy_rank(s2.data() + off, D, c->cfg.energy_threshold);
+            rr = std::min(rr, rank_g[t][g]);
         }
         if (rr > c->r_max)
             return fail(PALU_ERR_CAPACITY, "fitted rank " + std::to_string(rr) + " exceeds max_rank " +
                                                std::to_string(c->r_max));
+        if (int err = check_coder(c, t, rr)) return err;
         rt[t] = rr;
         for (int g = 0; g < G; ++g) pr[t * G + g].k = rr;
+        // energy fractions of each group's first rr - 1 and rr channels
+        frac_prev[t].assign(G, 0.0);
+        frac_at[t].assign(G, 0.0);
+        for (int g = 0; g < G; ++g) {
+            const double *e = s2.data() + (static_cast<size_t>(t) * G + g) * D;
+            double tot = 0.0, acc = 0.0;
+            for (int i = 0; i < D; ++i) tot += e[i];
+            for (int i = 0; i < rr; ++i) {
+                if (i == rr - 1) frac_prev[t][g] = tot > 0.0 ? acc / tot : 0.0;
+                acc += e[i];
+            }
+            frac_at[t][g] = tot > 0.0 ? acc / tot : 1.0;
+        }
     }
     solve_vectors(D, pr);
+    // every check has passed: the old bases and stored tokens go
+    c->ready[0][0] = c->ready[1][0] = 0;
+    reset_seqs(c);
+    for (int t = 0; t < 2; ++t) {
+        c->energy_rule[t] = c->cfg.rank <= 0;
+        c->rank_g[t] = rank_g[t];
+        c->frac_prev[t] = frac_prev[t];
+        c->frac_at[t] = frac_at[t];
+    }
     for (int t = 0; t < 2; ++t) {
         const int rr = rt[t];
         size_shared(c, t, rr);
@@ -770,7 +817,9 @@ PALU_API int palu_set_basis(palu_cache *c, int32_t tensor, int32_t r, const floa
         return PALU_OK;
     }
     if (r < 1 || r > c->r_max) return fail(PALU_ERR_INVALID_ARG, "r must be in [1, max_rank]");
+    if (int e = check_coder(c, tensor, r)) return e;
     c->ready[tensor][0] = 0;
+    c->rank_g[tensor].clear();
     reset_seqs(c);
     size_shared(c, tensor, r);
     if (int e = set_coder(c, tensor)) return e;
@@ -1155,6 +1204,31 @@ PALU_API int palu_get_stats(const palu_cache *c, palu_stats *st) {
     st->fp16_key_bytes = tokens * c->H * c->D * 2;
     st->fp16_value_bytes = st->fp16_key_bytes;
     st->assigned_avg_bits = std::max(st->realised_bits_k, st->realised_bits_v);
+    for (int t = 0; t < 2; ++t) {
+        double m = -1.0;
+        if (!c->per_seq && c->energy_rule[t] && !c->rank_g[t].empty()) {
+            const double tau = c->cfg.energy_threshold;
+            const double at = *std::max_element(c->frac_at[t].begin(), c->frac_at[t].end());
+            const double prev = *std::max_element(c->frac_prev[t].begin(), c->frac_prev[t].end());
+            m = std::min(at - tau, c->r[t] > 1 ? tau - prev : at - tau);
+        }
+        (t == 0 ? st->energy_margin_k : st->energy_margin_v) = m;
+    }
+    return PALU_OK;
+}
+
+PALU_API int palu_get_fit_info(const palu_cache *c, int32_t tensor, int32_t *r_groups, double *energy_prev,
+                               double *energy_at) {
+    if (!c) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
+    if (tensor != 0 && tensor != 1) return fail(PALU_ERR_INVALID_ARG, "tensor must be 0 (K) or 1 (V)");
+    if (c->per_seq) return fail(PALU_ERR_INVALID_ARG, "no shared fit with per-sequence bases");
+    if (c->rank_g[tensor].empty() || !c->ready[tensor][0])
+        return fail(PALU_ERR_NOT_FITTED, "no fit of this tensor since the last bind or palu_set_basis");
+    for (int g = 0; g < c->G; ++g) {
+        if (r_groups) r_groups[g] = c->rank_g[tensor][g];
+        if (energy_prev) energy_prev[g] = c->frac_prev[tensor][g];
+        if (energy_at) energy_at[g] = c->frac_at[tensor][g];
+    }
     return PALU_OK;
 }
 
@@ -1396,3 +1470,14 @@ PALU_API int palu_import_seq(palu_cache *c, int32_t seq, const void *host_src, s
 PALU_API const char *palu_last_error(void) { return g_last_error.c_str(); }
 
 PALU_API void palu_cache_destroy(palu_cache *c) { delete c; }
+
+PALU_API int palu_probe_read(const void *buf, size_t bytes, void *sink, int32_t grid, void *stream) {
+    if (!buf || !sink) return fail(PALU_ERR_INVALID_ARG, "buf and sink must be non-NULL");
+    if (bytes == 0 || bytes % 16 != 0) return fail(PALU_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+    if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return fail(PALU_ERR_INVALID_ARG, "buf must be 16-byte aligned");
+    if (grid < 1 || grid > 65536) return fail(PALU_ERR_INVALID_ARG, "grid must be in [1, 65536]");
+    const hipError_t e =
+        launch_read_probe(buf, bytes / 16, static_cast<uint32_t *>(sink), grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "read probe launch");
+    return PALU_OK;
+}

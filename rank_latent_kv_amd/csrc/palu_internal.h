@@ -206,6 +206,9 @@ hipError_t launch_combine(const AttendArgs &a, hipStream_t s);
 // fp16(src[g][d][channel of position n]) for the coder's blocks, 0 where n
 // is padding.
 hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, const Coder &cd, hipStream_t s);
+// Read-bandwidth probe: grid workgroups of 256 threads stream n16 16-byte
+// words of src and write one fold per workgroup to sink[grid].
+hipError_t launch_read_probe(const void *src, size_t n16, uint32_t *sink, int grid, hipStream_t s);
 // rows of the position-ordered fp16 basis copy (8 per channel block)
 PALU_HD inline int basis_t16_rows(const Coder &cd) { return 8 * coder_blocks(cd); }
 

@@ -631,4 +631,34 @@ hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, const
 }
 
 
+// ---------------------------------------------------------- read probe ----
+//
+// Measurement aid: every thread walks the buffer with a grid stride, four
+// independent 16-byte loads in flight per step, XOR-folding what it reads;
+// one lane per workgroup stores the workgroup's fold so no load is dead.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4 *__restrict__ src, size_t n16,
+                                                         uint32_t *__restrict__ sink) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * 256;
+    size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = src[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+    __shared__ uint32_t wf[4];
+    if ((threadIdx.x & 63) == 0) wf[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = wf[0] ^ wf[1] ^ wf[2] ^ wf[3];
+}
+
+hipError_t launch_read_probe(const void *src, size_t n16, uint32_t *sink, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, s, static_cast<const uint4 *>(src), n16, sink);
+    return hipGetLastError();
+}
+
 }  // namespace palu

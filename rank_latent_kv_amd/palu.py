@@ -28,7 +28,8 @@ EXPORTED = ["palu_config_default", "palu_cache_create", "palu_cache_required_byt
             "palu_encode_append", "palu_decode_attend", "palu_prefill_attend", "palu_seq_len",
             "palu_read_codes",
             "palu_get_stats", "palu_reset", "palu_record_words", "palu_export_bytes",
-            "palu_export_seq", "palu_import_seq", "palu_last_error", "palu_cache_destroy"]
+            "palu_export_seq", "palu_import_seq", "palu_get_fit_info", "palu_probe_read",
+            "palu_last_error", "palu_cache_destroy"]
 
 
 class PaluError(RuntimeError):
@@ -57,7 +58,8 @@ class palu_stats(ctypes.Structure):
                 ("nominal_bits_k", ctypes.c_double), ("nominal_bits_v", ctypes.c_double),
                 ("realised_bits_k", ctypes.c_double), ("realised_bits_v", ctypes.c_double),
                 ("assigned_avg_bits", ctypes.c_double), ("coded_k", ctypes.c_int32),
-                ("coded_v", ctypes.c_int32)]
+                ("coded_v", ctypes.c_int32), ("energy_margin_k", ctypes.c_double),
+                ("energy_margin_v", ctypes.c_double)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -94,6 +96,8 @@ def lib():
         "palu_seq_len": [_vp, _i32, _i32p],
         "palu_read_codes": [_vp, _i32, _i32, _i32, _vp, _sz, _vp, _sz],
         "palu_get_stats": [_vp, ctypes.POINTER(palu_stats)],
+        "palu_get_fit_info": [_vp, _i32, _i32p, _vp, _vp],
+        "palu_probe_read": [_vp, _sz, _vp, _i32, _vp],
         "palu_reset": [_vp],
         "palu_record_words": [_vp, _i32, _i32p],
         "palu_export_bytes": [_vp, _i32, ctypes.POINTER(_sz)],
@@ -116,10 +120,14 @@ def _check(code: int):
         raise PaluError(code, lib().palu_last_error().decode())
 
 
-def _i32_array(vals):
+def _i32_array(vals, n: Optional[int] = None, name: str = "array"):
+    """int32 copy of a per-row host array and its pointer; None stays None.
+    With n given the array must hold exactly n entries (the C side reads n)."""
     if vals is None:
         return None
-    arr = np.ascontiguousarray(vals, dtype=np.int32)
+    arr = np.ascontiguousarray(vals, dtype=np.int32).reshape(-1)
+    if n is not None and arr.size != n:
+        raise ValueError(f"{name} has {arr.size} entries, expected one per row ({n})")
     return arr, arr.ctypes.data_as(_i32p)
 
 
@@ -148,7 +156,9 @@ def palu_cache_bind(cache: int, dev_ptr: int, nbytes: int):
 
 
 def palu_fit(cache: int, k_ptr: int, v_ptr: int, seq_lens, B: int, S_stride: int, stream: int):
-    arr, p = _i32_array(seq_lens)
+    if seq_lens is None:
+        raise ValueError("seq_lens is required")
+    arr, p = _i32_array(seq_lens, B, "seq_lens")
     _check(lib().palu_fit(cache, k_ptr, v_ptr, p, B, S_stride, stream))
 
 
@@ -171,8 +181,8 @@ def palu_get_basis(cache: int, tensor: int, G: int, D: int):
 
 def palu_fit_seq(cache: int, k_ptr: int, v_ptr: int, seq_ids, seq_lens, B: int, S_stride: int,
                  stream: int):
-    s = _i32_array(seq_ids)
-    n = _i32_array(seq_lens)
+    s = _i32_array(seq_ids, B, "seq_ids")
+    n = _i32_array(seq_lens, B, "seq_lens")
     _check(lib().palu_fit_seq(cache, k_ptr, v_ptr, s[1] if s else None, n[1] if n else None, B,
                               S_stride, stream))
 
@@ -196,23 +206,23 @@ def palu_get_basis_seq(cache: int, seq: int, tensor: int, G: int, D: int):
 
 def palu_encode_append(cache: int, k_ptr: int, v_ptr: int, seq_ids, n_new, B: int,
                        T_stride: int, stream: int):
-    s = _i32_array(seq_ids)
-    n = _i32_array(n_new)
+    s = _i32_array(seq_ids, B, "seq_ids")
+    n = _i32_array(n_new, B, "n_new")
     _check(lib().palu_encode_append(cache, k_ptr, v_ptr, s[1] if s else None,
                                     n[1] if n else None, B, T_stride, stream))
 
 
 def palu_decode_attend(cache: int, q_ptr: int, out_ptr: int, seq_ids, B: int,
                        softmax_scale: float, stream: int):
-    s = _i32_array(seq_ids)
+    s = _i32_array(seq_ids, B, "seq_ids")
     _check(lib().palu_decode_attend(cache, q_ptr, out_ptr, s[1] if s else None, B,
                                     softmax_scale, stream))
 
 
 def palu_prefill_attend(cache: int, q_ptr: int, out_ptr: int, seq_ids, n_q, B: int,
                         T_stride: int, softmax_scale: float, stream: int):
-    s = _i32_array(seq_ids)
-    n = _i32_array(n_q)
+    s = _i32_array(seq_ids, B, "seq_ids")
+    n = _i32_array(n_q, B, "n_q")
     _check(lib().palu_prefill_attend(cache, q_ptr, out_ptr, s[1] if s else None,
                                      n[1] if n else None, B, T_stride, softmax_scale, stream))
 
@@ -261,6 +271,21 @@ def palu_get_stats(cache: int) -> palu_stats:
     st = palu_stats()
     _check(lib().palu_get_stats(cache, ctypes.byref(st)))
     return st
+
+
+def palu_get_fit_info(cache: int, tensor: int, G: int):
+    """(per-group ranks int32 [G], energy fractions at r - 1 and at r
+    float64 [G] each) of the last shared fit of `tensor`."""
+    rg = np.empty(G, np.int32)
+    ep = np.empty(G, np.float64)
+    ea = np.empty(G, np.float64)
+    _check(lib().palu_get_fit_info(cache, tensor, rg.ctypes.data_as(_i32p), ep.ctypes.data,
+                                   ea.ctypes.data))
+    return rg, ep, ea
+
+
+def palu_probe_read(buf_ptr: int, nbytes: int, sink_ptr: int, grid: int, stream: int):
+    _check(lib().palu_probe_read(buf_ptr, nbytes, sink_ptr, grid, stream))
 
 
 def palu_reset(cache: int):
@@ -332,21 +357,35 @@ class LatentKVCache:
     def _stream(self):
         return self.torch.cuda.current_stream(self.storage.device).cuda_stream
 
-    def _check_half(self, t, shape_tail, name):
+    def _check_rank(self, t, dims, name):
+        if not isinstance(t, self.torch.Tensor) or t.dim() != dims:
+            raise ValueError(f"{name} must be a {dims}-dimensional tensor")
+
+    def _check_half(self, t, shape_tail, name, shape=None):
+        """t must be a contiguous tensor of the input type on the cache's
+        device, ending in shape_tail (or of exactly `shape`)."""
         torch = self.torch
         want = torch.bfloat16 if self.cfg.input_dtype == 1 else torch.float16
-        if t.dtype != want or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {want} CUDA tensor")
-        if tuple(t.shape[-len(shape_tail):]) != tuple(shape_tail):
+        if not isinstance(t, torch.Tensor) or t.dtype != want or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {want} tensor")
+        if t.device != self.storage.device:
+            raise ValueError(f"{name} is on {t.device}, the cache on {self.storage.device}")
+        if shape is not None:
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        elif t.dim() < len(shape_tail) or tuple(t.shape[-len(shape_tail):]) != tuple(shape_tail):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected [..., {shape_tail}]")
 
     def fit(self, k, v, seq_lens: Optional[Sequence[int]] = None, seq_ids=None):
         """k, v: fp16 [B, H, S, D].  With per-sequence bases, row b is fitted
         into slot seq_ids[b] (default b)."""
+        self._check_rank(k, 4, "k")
         self._check_half(k, (self.H, k.shape[2], self.D), "k")
-        self._check_half(v, tuple(k.shape[1:]), "v")
+        self._check_half(v, None, "v", tuple(k.shape))
         B, _, S, _ = k.shape
         lens = [S] * B if seq_lens is None else list(seq_lens)
+        _i32_array(lens, B, "seq_lens")
+        _i32_array(seq_ids, B, "seq_ids")
         if seq_ids is None:
             palu_fit(self.handle, k.data_ptr(), v.data_ptr(), lens, B, S, self._stream())
         else:
@@ -369,17 +408,23 @@ class LatentKVCache:
     def encode_append(self, k, v, seq_ids=None, n_new=None):
         """k, v: fp16 [B, H, T, D]; appends n_new[b] (default T) tokens of row
         b to slot seq_ids[b] (default b)."""
+        self._check_rank(k, 4, "k")
         self._check_half(k, (self.H, k.shape[2], self.D), "k")
-        self._check_half(v, tuple(k.shape[1:]), "v")
+        self._check_half(v, None, "v", tuple(k.shape))
         B, _, T, _ = k.shape
+        _i32_array(seq_ids, B, "seq_ids")
+        _i32_array(n_new, B, "n_new")
         palu_encode_append(self.handle, k.data_ptr(), v.data_ptr(), seq_ids, n_new, B, T,
                            self._stream())
 
     def decode_attend(self, q, seq_ids=None, softmax_scale: float = 0.0, out=None):
         """q: fp16 [B, Hq, D] -> fp16 [B, Hq, D]."""
+        self._check_rank(q, 3, "q")
         self._check_half(q, (self.Hq, self.D), "q")
         if out is None:
             out = self.torch.empty_like(q)
+        self._check_half(out, None, "out", tuple(q.shape))
+        _i32_array(seq_ids, q.shape[0], "seq_ids")
         palu_decode_attend(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, q.shape[0],
                            softmax_scale, self._stream())
         return out
@@ -388,9 +433,17 @@ class LatentKVCache:
         """q: fp16 [B, Hq, T, D]; row b's first n_q[b] (default T) queries
         sit at the slot's last n_q[b] positions and attend causally.
         Returns fp16 [B, Hq, T, D] (entries past n_q[b] are left as they were)."""
+        self._check_rank(q, 4, "q")
         self._check_half(q, (self.Hq, q.shape[2], self.D), "q")
+        if q.data_ptr() % 16:
+            raise ValueError("q must be 16-byte aligned")
         if out is None:
             out = self.torch.empty_like(q)
+        self._check_half(out, None, "out", tuple(q.shape))
+        if out.data_ptr() % 16:
+            raise ValueError("out must be 16-byte aligned")
+        _i32_array(seq_ids, q.shape[0], "seq_ids")
+        _i32_array(n_q, q.shape[0], "n_q")
         palu_prefill_attend(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, n_q, q.shape[0],
                             q.shape[2], softmax_scale, self._stream())
         return out
@@ -423,6 +476,11 @@ class LatentKVCache:
 
     def stats(self) -> dict:
         return palu_get_stats(self.handle).as_dict()
+
+    def fit_info(self, tensor: int):
+        """(per-group ranks, energy fraction at r - 1, at r) of the last
+        shared fit of tensor 0 (K) or 1 (V)."""
+        return palu_get_fit_info(self.handle, tensor, self.G)
 
     def reset(self):
         palu_reset(self.handle)

@@ -139,7 +139,7 @@ def test_calls_before_bind_or_fit_fail_cleanly():
         with pytest.raises(palu.PaluError) as ei:
             palu.palu_get_stats(h)
         assert ei.value.code == 3
-        for lens, B, S in [([17, 3], 2, 16), ([-1, 3], 2, 16), ([0, 0], 2, 16), ([4], 3, 16),
+        for lens, B, S in [([17, 3], 2, 16), ([-1, 3], 2, 16), ([0, 0], 2, 16), ([4, 4, 4], 3, 16),
                            ([300, 3], 2, 300)]:
             with pytest.raises(palu.PaluError) as ei:
                 palu.palu_fit(h, 1, 1, lens, B, S, 0)
@@ -202,3 +202,104 @@ def test_per_seq_basis_config_and_host_checks():
     finally:
         for c in (h, shared, one):
             palu.palu_cache_destroy(c)
+
+
+# ------------------------------------------- binding checks before any call
+
+def _host_cache(**kw):
+    """A LatentKVCache-shaped object whose bound storage is a CPU tensor:
+    every check below must raise before anything reaches the library."""
+    import torch
+    c = palu.LatentKVCache.__new__(palu.LatentKVCache)
+    c.torch = torch
+    c.cfg = _cfg(**kw)
+    c.D, c.H, c.Hq, c.G = 128, 8, 32, 4
+    c.max_batch, c.max_seq_len = 4, 64
+    c.storage = torch.empty(0, dtype=torch.uint8)
+    c.handle = None
+    return c
+
+
+def test_binding_rejects_bad_out_before_launch():
+    import torch
+    c = _host_cache()
+    q = torch.zeros((2, 32, 128), dtype=torch.float16)
+    bad_outs = [torch.zeros((1, 32, 128), dtype=torch.float16),        # too few rows
+                torch.zeros((2, 32, 64), dtype=torch.float16),         # short rows
+                torch.zeros((2, 32, 128), dtype=torch.float32),        # wrong type
+                torch.zeros((2, 128, 32), dtype=torch.float16).transpose(1, 2)]   # not contiguous
+    for out in bad_outs:
+        with pytest.raises(ValueError):
+            c.decode_attend(q, out=out)
+    qp = torch.zeros((2, 32, 16, 128), dtype=torch.float16)
+    for out in (torch.zeros((2, 32, 8, 128), dtype=torch.float16),
+                torch.zeros((2, 32, 16, 128), dtype=torch.bfloat16)):
+        with pytest.raises(ValueError):
+            c.prefill_attend(qp, out=out)
+    with pytest.raises(ValueError):
+        c.decode_attend(torch.zeros((32, 128), dtype=torch.float16))  # missing batch dim
+    with pytest.raises(ValueError):
+        c.decode_attend(torch.zeros((2, 8, 128), dtype=torch.float16))  # wrong head count
+
+
+def test_binding_rejects_tensors_on_another_device():
+    import torch
+    c = _host_cache()
+    c.storage = torch.empty(0, dtype=torch.uint8, device="meta")
+    q = torch.zeros((2, 32, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        c.decode_attend(q, out=torch.empty_like(q))
+
+
+@pytest.mark.parametrize("call", ["fit", "fit_seq", "encode", "decode", "prefill"])
+def test_per_row_arrays_must_have_one_entry_per_row(call):
+    """The C side reads B entries of every per-row host array: shorter or
+    longer arrays are rejected in the binding."""
+    B = 3
+    with pytest.raises(ValueError):
+        if call == "fit":
+            palu.palu_fit(0, 0, 0, [5, 5], B, 8, 0)
+        elif call == "fit_seq":
+            palu.palu_fit_seq(0, 0, 0, [0, 1, 2, 3], [5, 5, 5], B, 8, 0)
+        elif call == "encode":
+            palu.palu_encode_append(0, 0, 0, None, [1, 1], B, 1, 0)
+        elif call == "decode":
+            palu.palu_decode_attend(0, 0, 0, [0, 1], B, 0.0, 0)
+        else:
+            palu.palu_prefill_attend(0, 0, 0, [0, 1, 2], [4], B, 4, 0.0, 0)
+    # and through the cache object, with tensors of the right shapes
+    import torch
+    c = _host_cache()
+    k = torch.zeros((B, 8, 4, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        if call in ("fit", "fit_seq"):
+            c.fit(k, k.clone(), seq_lens=[4, 4], seq_ids=None if call == "fit" else [0, 1, 2])
+        elif call == "encode":
+            c.encode_append(k, k.clone(), seq_ids=[0, 1])
+        elif call == "decode":
+            q = torch.zeros((B, 32, 128), dtype=torch.float16)
+            c.decode_attend(q, seq_ids=[0, 1, 2, 3])
+        else:
+            q = torch.zeros((B, 32, 4, 128), dtype=torch.float16)
+            c.prefill_attend(q, n_q=[1, 1])
+
+
+def test_fit_info_needs_a_fit():
+    h = palu.palu_cache_create(_cfg(), 2, 64)
+    try:
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_get_fit_info(h, 0, 4)
+        assert ei.value.code == 3
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_get_fit_info(h, 2, 4)
+        assert ei.value.code == 1
+    finally:
+        palu.palu_cache_destroy(h)
+
+
+def test_read_probe_rejects_bad_arguments():
+    for args in [(0, 1 << 20, 1, 64), (16, 1 << 20, 0, 64), (16, 0, 16, 64), (16, 24, 16, 64),
+                 (8, 1 << 20, 16, 64), (16, 1 << 20, 16, 0), (16, 1 << 20, 16, 65537)]:
+        with pytest.raises(palu.PaluError) as ei:
+            palu.palu_probe_read(args[0], args[1], args[2], args[3], 0)
+        assert ei.value.code == 1, args
