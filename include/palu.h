@@ -215,6 +215,23 @@ int palu_decode_attend(palu_cache *cache, const void *q, void *out,
                        const int32_t *seq_ids, int32_t B, float softmax_scale,
                        void *stream);
 
+/* palu_decode_attend for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results, with the split partials in a
+ * file-scope device array of the library (16 MiB per GPU, held until the
+ * process ends) instead of the bound storage.  The call allocates nothing
+ * (no hipMalloc or allocating library routine); the caller still passes q,
+ * out and the bound cache.  Every call on a GPU shares that GPU's array, so
+ * calls that overlap on one GPU (other streams, other caches, other
+ * threads) race: order them on one stream.  Nothing in the array has to
+ * start at zero (each call writes every partial it reads).
+ * Errors: as palu_decode_attend, and UNSUPPORTED when a launch's partials
+ * (rows x n_q_heads x splits x (r_v + 2) x 4 bytes, at most 64 rows per
+ * launch) exceed 16 MiB. */
+int palu_decode_attend_noalloc(palu_cache *cache, const void *q, void *out,
+                               const int32_t *seq_ids, int32_t B, float softmax_scale,
+                               void *stream);
+
 /* Causal prefill attention over the stored latents (PALU page, "How it
  * works", prefill step 6: the stored latents feed the attention call that
  * follows the encode), computed directly from the codes like

@@ -9,6 +9,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "palu_device.h"
@@ -687,9 +688,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     //         w, w + 4 with its lanes over streams.
     const int nsw = kWaves * S + (do_tail ? 1 : 0);   // <= 65
     float *wts = ts;                                   // [g][65]
-    float *part = a.partial + (static_cast<int64_t>(qi) * a.Hq + h * g) * kMaxSplits * (rv + 2) +
+    float *part = a.partial + (static_cast<int64_t>(qi) * a.Hq + h * g) * a.nsplit_max * (rv + 2) +
                   static_cast<int64_t>(s) * (rv + 2);
-    const int64_t head_stride = static_cast<int64_t>(kMaxSplits) * (rv + 2);
+    const int64_t head_stride = static_cast<int64_t>(a.nsplit_max) * (rv + 2);
     for (int hh = wv; hh < g; hh += kWaves) {
         const int k1 = lane + 64;
         const int sid0 = lane < kWaves * S ? (lane / S) * 16 + (lane % S) * g + hh : kWaves * 16 + hh;
@@ -762,7 +763,7 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
     float *ml = bl + kHeadDim * rv;            // [D] value mean
     float *wl = ml + kHeadDim;                 // [ns] split weights
     float *ol = wl + ((ns + 3) & ~3);          // [rv] merged latent output
-    const float *part = a.partial + (static_cast<int64_t>(i) * a.Hq + qh) * kMaxSplits * (rv + 2);
+    const float *part = a.partial + (static_cast<int64_t>(i) * a.Hq + qh) * a.nsplit_max * (rv + 2);
     const float *bv = a.v.basis_cm + slot * a.v.set_bcm + static_cast<int64_t>(grp) * rv * kHeadDim;
     const float *mv = a.v.mu + slot * a.v.set_mu + grp * kHeadDim;
 
@@ -933,6 +934,32 @@ hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
         case 8: return launch_attend_g<8>(a, lds_bytes, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+// Split partials of the allocation-free decode entry point: one array per
+// device, alive until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it only stands for the symbol); it passes the
+// device address looked up below.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch_address(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // with this device current: its own copy of the array
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s) {

@@ -938,8 +938,14 @@ PALU_API int palu_encode_append(palu_cache *c, const void *k, const void *v, con
     return PALU_OK;
 }
 
-PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids, int32_t B,
-                                float softmax_scale, void *stream) {
+namespace {
+
+// Decode attention of palu_decode_attend and palu_decode_attend_noalloc.
+// The split partials go to the bound buffer (fixed == nullptr) or to the
+// file-scope device array at `fixed` (kStaticScratchBytes), which every call
+// of one launch group reuses in stream order.
+int decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids, int32_t B,
+                  float softmax_scale, void *stream, float *fixed) {
     if (int e = check_fitted(c)) return e;
     if (!q || !out) return fail(PALU_ERR_INVALID_ARG, "q and out must be non-NULL");
     if (B <= 0) return fail(PALU_ERR_INVALID_ARG, "B must be positive");
@@ -954,12 +960,15 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(c->D));
     const size_t row_elems = static_cast<size_t>(c->Hq) * c->D;
+    std::vector<AttendArgs> launches;
     for (int b0 = 0; b0 < B; b0 += kMaxCallSeqs) {
         const int nb = std::min(kMaxCallSeqs, B - b0);
-        AttendArgs aa{};
+        launches.emplace_back();
+        AttendArgs &aa = launches.back();
+        aa = AttendArgs{};
         aa.q = static_cast<const uint16_t *>(q) + b0 * row_elems;
         aa.out = static_cast<uint16_t *>(out) + b0 * row_elems;
-        aa.partial = reinterpret_cast<float *>(c->dev + c->off_attend);
+        aa.partial = fixed ? fixed : reinterpret_cast<float *>(c->dev + c->off_attend);
 
         aa.k = c->tensor_dev(0);
         aa.v = c->tensor_dev(1);
@@ -1033,13 +1042,40 @@ PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const i
             aa.inv_rv = one / static_cast<float>(aa.v.r);
             aa.inv_nbk4 = one / static_cast<float>(4 * nbk);
         }
+        if (fixed) {
+            const size_t need = sizeof(float) * static_cast<size_t>(nb) * c->Hq * nsplit_max * (aa.v.r + 2);
+            if (need > kStaticScratchBytes)
+                return fail(PALU_ERR_UNSUPPORTED,
+                            "split partials need " + std::to_string(need) + " bytes, above the " +
+                                std::to_string(kStaticScratchBytes) + "-byte static scratch (fewer rows per call, "
+                                "or a larger split_groups, or palu_decode_attend)");
+        }
+    }
+    for (const AttendArgs &aa : launches) {
+        const size_t lds =
+            attend_lds_bytes(c->gqa, coder_blocks(aa.k.cd), aa.k.r, aa.v.r, aa.k.words, aa.v.words, !aa.v.fp16_latents);
         hipError_t e = launch_attend(aa, lds, s);
         if (e != hipSuccess) return hip_fail(e, "attend launch");
         e = launch_combine(aa, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");
-
     }
     return PALU_OK;
+}
+
+}  // namespace
+
+PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids, int32_t B,
+                                float softmax_scale, void *stream) {
+    return decode_attend(c, q, out, seq_ids, B, softmax_scale, stream, nullptr);
+}
+
+PALU_API int palu_decode_attend_noalloc(palu_cache *c, const void *q, void *out, const int32_t *seq_ids,
+                                        int32_t B, float softmax_scale, void *stream) {
+    if (int e = check_fitted(c)) return e;
+    void *p = nullptr;
+    const hipError_t e = static_scratch_address(&p);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    return decode_attend(c, q, out, seq_ids, B, softmax_scale, stream, static_cast<float *>(p));
 }
 
 PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids,

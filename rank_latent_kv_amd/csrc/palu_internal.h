@@ -135,7 +135,7 @@ struct AttendRow {
 struct AttendArgs {
     const uint16_t *q;        // fp16 or bf16 [B][Hq][D]
     uint16_t *out;            // same type as q, [B][Hq][D]
-    float *partial;           // [B][Hq][kMaxSplits][2 + r_v]
+    float *partial;           // [B][Hq][nsplit_max][2 + r_v]
     TensorDev k, v;
     int B, Hq, Hkv, gqa, hpg;
     int chunk;                // complete token groups per split
@@ -202,6 +202,11 @@ hipError_t launch_append1(const EncodeArgs &a, hipStream_t s);
 // Grid (Hkv, B, nsplit_max): one workgroup per (kv head, row, split), the head fastest.
 hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_combine(const AttendArgs &a, hipStream_t s);
+// Bytes of the file-scope device array that holds the split partials of the
+// allocation-free decode entry point, and its address on the current device
+// (looked up once per device; defined in palu_decode.hip).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch_address(void **ptr);
 // Position-ordered fp16 copy of a basis [G][D][r]: dst[g][n][d] =
 // fp16(src[g][d][channel of position n]) for the coder's blocks, 0 where n
 // is padding.

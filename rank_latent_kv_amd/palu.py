@@ -25,7 +25,8 @@ ERROR_NAMES = {1: "PALU_ERR_INVALID_ARG", 2: "PALU_ERR_UNSUPPORTED", 3: "PALU_ER
 EXPORTED = ["palu_config_default", "palu_cache_create", "palu_cache_required_bytes",
             "palu_cache_bind", "palu_fit", "palu_set_basis", "palu_get_basis",
             "palu_fit_seq", "palu_set_basis_seq", "palu_get_basis_seq",
-            "palu_encode_append", "palu_decode_attend", "palu_prefill_attend", "palu_seq_len",
+            "palu_encode_append", "palu_decode_attend", "palu_decode_attend_noalloc",
+            "palu_prefill_attend", "palu_seq_len",
             "palu_read_codes",
             "palu_get_stats", "palu_reset", "palu_record_words", "palu_export_bytes",
             "palu_export_seq", "palu_import_seq", "palu_get_fit_info", "palu_probe_read",
@@ -92,6 +93,7 @@ def lib():
         "palu_get_basis_seq": [_vp, _i32, _i32, _i32p, _vp, _vp, _vp],
         "palu_encode_append": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, _vp],
         "palu_decode_attend": [_vp, _vp, _vp, _i32p, _i32, ctypes.c_float, _vp],
+        "palu_decode_attend_noalloc": [_vp, _vp, _vp, _i32p, _i32, ctypes.c_float, _vp],
         "palu_prefill_attend": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, ctypes.c_float, _vp],
         "palu_seq_len": [_vp, _i32, _i32p],
         "palu_read_codes": [_vp, _i32, _i32, _i32, _vp, _sz, _vp, _sz],
@@ -217,6 +219,13 @@ def palu_decode_attend(cache: int, q_ptr: int, out_ptr: int, seq_ids, B: int,
     s = _i32_array(seq_ids, B, "seq_ids")
     _check(lib().palu_decode_attend(cache, q_ptr, out_ptr, s[1] if s else None, B,
                                     softmax_scale, stream))
+
+
+def palu_decode_attend_noalloc(cache: int, q_ptr: int, out_ptr: int, seq_ids, B: int,
+                               softmax_scale: float, stream: int):
+    s = _i32_array(seq_ids, B, "seq_ids")
+    _check(lib().palu_decode_attend_noalloc(cache, q_ptr, out_ptr, s[1] if s else None, B,
+                                            softmax_scale, stream))
 
 
 def palu_prefill_attend(cache: int, q_ptr: int, out_ptr: int, seq_ids, n_q, B: int,
@@ -427,6 +436,17 @@ class LatentKVCache:
         _i32_array(seq_ids, q.shape[0], "seq_ids")
         palu_decode_attend(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, q.shape[0],
                            softmax_scale, self._stream())
+        return out
+
+    def decode_attend_noalloc(self, q, out, seq_ids=None, softmax_scale: float = 0.0):
+        """decode_attend with the split partials in the library's static
+        device array: allocates nothing (the caller passes out)."""
+        self._check_rank(q, 3, "q")
+        self._check_half(q, (self.Hq, self.D), "q")
+        self._check_half(out, None, "out", tuple(q.shape))
+        _i32_array(seq_ids, q.shape[0], "seq_ids")
+        palu_decode_attend_noalloc(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, q.shape[0],
+                                   softmax_scale, self._stream())
         return out
 
     def prefill_attend(self, q, seq_ids=None, n_q=None, softmax_scale: float = 0.0, out=None):
