@@ -417,8 +417,15 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // (b) scores
-        f4 sacc0 = {0.0f, 0.0f, 0.0f, 0.0f}, sacc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        // (b) scores.  PALU-shaped layouts: A = the codes as exact fp16
+        //     1024 + code, B = qt16 * scale16 (the group's scales folded into
+        //     the query operand, the same for all 32 tokens); the rest of
+        //     sum_c qt_c (s_c code_c + z_c) comes from two more MFMAs into
+        //     zacc whose A rows are all equal: the fp16 zeros against qt16
+        //     (products exact) and -1024 against the scaled operand.  Every
+        //     row of zacc holds the same value, the stream's constant.
+        f4 sacc0 = {0.0f, 0.0f, 0.0f, 0.0f}, sacc1 = {0.0f, 0.0f, 0.0f, 0.0f}, zacc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f16x8 kneg1024 = as_h8(0xE400E400u, 0xE400E400u, 0xE400E400u, 0xE400E400u);
         auto score_step = [&](int u, const uint4 bq) {
             const int p = 4 * u + kb;
             int q, j;
@@ -448,16 +455,22 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                 const uint32_t X1 = __builtin_amdgcn_alignbit(rec[(bit1 >> 5) + 1], rec[bit1 >> 5], bit1 & 31);
                 if constexpr (S % 4 == 0) {
                     if (w4) {
-                        a0 = dequant8<true>(X0, sp, zp, km4, kmagic);
-                        a1 = dequant8<true>(X1, sp, zp, km4, kmagic);
+                        a0 = codes8<true>(X0, km4, kmagic);
+                        a1 = codes8<true>(X1, km4, kmagic);
                     } else {
-                        a0 = dequant8<false>(X0, sp, zp, km2, kmagic);
-                        a1 = dequant8<false>(X1, sp, zp, km2, kmagic);
+                        a0 = codes8<false>(X0, km2, kmagic);
+                        a1 = codes8<false>(X1, km2, kmagic);
                     }
                 } else {
-                    a0 = dequant8_any(X0, w4, sp, zp);
-                    a1 = dequant8_any(X1, w4, sp, zp);
+                    a0 = codes8_any(X0, w4);
+                    a1 = codes8_any(X1, w4);
                 }
+                const f16x8 bs = bop * as_h8(sp.x, sp.y, sp.z, sp.w);
+                sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bs, sacc0, 0, 0, 0);
+                sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bs, sacc1, 0, 0, 0);
+                zacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(zp.x, zp.y, zp.z, zp.w), bop, zacc, 0, 0, 0);
+                zacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kneg1024, bs, zacc, 0, 0, 0);
+                return;
             } else {
                 const int4 bq4 = blk[qc];                // base, stride, width
                 const int wq = bq4.z;
@@ -485,8 +498,10 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         // (c) online softmax of stream ln (rows 4*kb + v of both 16-token halves)
         const bool sv = live_n && (tb0 + slot_n) < npg;
         const float sc[8] = {sacc0[0], sacc0[1], sacc0[2], sacc0[3], sacc1[0], sacc1[1], sacc1[2], sacc1[3]};
+        // the stream's constant (0 for the generic coders): score = sc + zc
+        const float zc = zacc[0];
         float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))) + zc;
         mloc = sv ? mloc : -INFINITY;
         const bool need = mloc > m_run + kRescaleSlack;
         if (__any(need)) {
@@ -506,7 +521,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         }
         // weights of streams whose group is past the pass never reach a
         // value MFMA (their slot's A rows are zero), so only l is masked
-        const float msafe = m_run == -INFINITY ? 0.0f : m_run;
+        const float msafe = (m_run == -INFINITY ? 0.0f : m_run) - zc;
         float pr[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(sc[k] - msafe);
@@ -589,7 +604,22 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                 dacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, as_h8(bp0, bp1, bp2, bp3), dacc[nb], 0, 0, 0);
             }
         }
-        if (vq) {
+        if (vq && G % 4 == 0) {
+            // (e) epilogue: with 4 or 8 query heads a lane's four output rows
+            //     4 kb + v belong to one token group, so its scale s and
+            //     z - 1024 s are decoded once per channel block
+            int tgr = tb0 + row_slot[0];
+            tgr = tgr < npg ? tgr : npg - 1;
+            const uint32_t *meta = stage + voff + tgr * WV + vmeta;
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                const uint32_t mw = meta[vch[nb]];
+                const float sc16 = h2f(mw);
+                const float zr = fmaf(-1024.0f, sc16, h2f(mw >> 16));
+#pragma unroll
+                for (int v = 0; v < 4; ++v) oacc[nb][v] = fmaf(sc16, dacc[nb][v], fmaf(zr, dP[v], oacc[nb][v]));
+            }
+        } else if (vq) {
             // (e) epilogue per output row 4*kb + v (stream): the row's group
             //     scale s and z - 1024 s from its metadata word; rows of
             //     groups past the pass have D = P = 0
@@ -805,6 +835,53 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
         return;
     }
 
+    if (ns <= 64 && rv <= 64) {
+        // Channel path: lane c owns latent channel c.  Lane s's split
+        // maximum gives the row maximum and the split weights w_s (broadcast
+        // by readlane); lane c sums w_s o_s[c] over the splits (one coalesced
+        // row of the partials per split), then every lane projects its two
+        // outputs d = 2 lane, 2 lane + 1 with the value basis, 16 channels
+        // at a time (loads issued before the first use), taking channel c's
+        // merged latent from lane c.  No LDS.
+        const bool live = lane < ns;
+        const float m = live ? part[lane * (rv + 2)] : -INFINITY;
+        const float ls = live ? part[lane * (rv + 2) + 1] : 0.0f;
+        const float M = wave_max(m);
+        const float w = live ? exp2f(m - M) : 0.0f;
+        const float inv_l = 1.0f / wave_sum(w * ls);
+        const int cc = lane < rv ? lane : rv - 1;
+        float acc = 0.0f;
+        for (int s0 = 0; s0 < ns; s0 += 8) {
+            float oz[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) oz[u] = s0 + u < ns ? part[(s0 + u) * (rv + 2) + 2 + cc] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < ns) acc = fmaf(lane_value(w, s0 + u), oz[u], acc);
+        }
+        const float oc = acc * inv_l;
+        const float2 mu = *reinterpret_cast<const float2 *>(mv + 2 * lane);
+        float o0 = mu.x, o1 = mu.y;
+        for (int c0 = 0; c0 < rv; c0 += 16) {
+            float2 bz[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                bz[u] = c0 + u < rv ? *reinterpret_cast<const float2 *>(bv + (c0 + u) * kHeadDim + 2 * lane)
+                                    : make_float2(0.0f, 0.0f);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (c0 + u < rv) {
+                    const float occ = lane_value(oc, c0 + u);
+                    o0 = fmaf(bz[u].x, occ, o0);
+                    o1 = fmaf(bz[u].y, occ, o1);
+                }
+            }
+        }
+        reinterpret_cast<uint32_t *>(a.out + (static_cast<int64_t>(i) * a.Hq + qh) * kHeadDim)[lane] =
+            out_bits(o0, a.bf16) | (out_bits(o1, a.bf16) << 16);
+        return;
+    }
+
     // 1. copy to LDS: whole 16-byte pieces of the partials, the basis
     //    (128 rv floats) and the mean; the < 4 trailing partial floats singly
     {
@@ -968,7 +1045,10 @@ hipError_t launch_combine(const AttendArgs &a, hipStream_t s) {
         hipFuncSetAttribute(reinterpret_cast<const void *>(combine_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    const size_t lds = static_cast<size_t>(combine_lds_floats(a.nsplit_max, a.v.r)) * sizeof(float);
+    // the register and channel paths (at most 64 splits, r_V <= 64) use no LDS
+    const size_t lds = a.nsplit_max <= 64 && a.v.r <= 64
+                           ? 0
+                           : static_cast<size_t>(combine_lds_floats(a.nsplit_max, a.v.r)) * sizeof(float);
     hipLaunchKernelGGL(combine_kernel, dim3(a.Hq, a.B), dim3(64), lds, s, a);
     return hipGetLastError();
 }

@@ -253,6 +253,24 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t X, const uint4 &sp, const uin
                  dequant_pair(((U >> (3 * wc)) & cm) | magic, sp.w, zp.w));
 }
 
+// 8 codes of one token from a 32-bit window -> fp16 pairs 1024 + code
+// (channel k, channel k + 4), k = 0..3, exact.
+template <bool W4>
+__device__ __forceinline__ f16x8 codes8(uint32_t X, uint32_t cm, uint32_t magic) {
+    const uint32_t U = W4 ? X : perm_b32(X, X, 0x0C010C00u);
+    constexpr int wc = W4 ? 4 : 2;
+    return as_h8((U & cm) | magic, ((U >> wc) & cm) | magic, ((U >> (2 * wc)) & cm) | magic,
+                 ((U >> (3 * wc)) & cm) | magic);
+}
+
+__device__ __forceinline__ f16x8 codes8_any(uint32_t X, bool w4) {
+    const uint32_t U = w4 ? X : perm_b32(X, X, 0x0C010C00u);
+    const int wc = w4 ? 4 : 2;
+    const uint32_t cm = w4 ? 0x000F000Fu : 0x00030003u;
+    return as_h8((U & cm) | 0x64006400u, ((U >> wc) & cm) | 0x64006400u, ((U >> (2 * wc)) & cm) | 0x64006400u,
+                 ((U >> (3 * wc)) & cm) | 0x64006400u);
+}
+
 __device__ __forceinline__ f16x8 dequant8_any(uint32_t X, bool w4, const uint4 &sp, const uint4 &zp) {
     const uint32_t U = w4 ? X : perm_b32(X, X, 0x0C010C00u);
     const int wc = w4 ? 4 : 2;
