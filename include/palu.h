@@ -215,6 +215,33 @@ int palu_decode_attend(palu_cache *cache, const void *q, void *out,
                        const int32_t *seq_ids, int32_t B, float softmax_scale,
                        void *stream);
 
+/* One decode step (PALU page, "How it works", decode steps 1-3: project,
+ * quantise and append the new token, then attend over everything stored),
+ * fused so that it can be captured once in a HIP graph and replayed for
+ * later steps: row b appends one token (k_new / v_new: device fp16 or bf16
+ * [B][H][1][D]) to slot seq_ids[b], then its queries attend over the slot's
+ * tokens, including the new one, exactly as palu_encode_append followed by
+ * palu_decode_attend.  Every kernel of the call reads the slots' lengths
+ * from device memory and the call leaves the new lengths there, so a graph
+ * replay appends at the right position without host involvement.  The host
+ * keeps its own copy of the lengths, advanced when the call is made (not
+ * when a graph replays it): after replaying captured steps call
+ * palu_sync_lengths before any other call on the cache.  A replay that
+ * finds a slot full stores no token and attends over what is stored.
+ *   q, out   : device [B][Hq][D] as in palu_decode_attend
+ *   seq_ids  : host int32 [B] (NULL = 0..B-1), distinct; empty slots allowed
+ * Stream-ordered; uses the split scratch of the bound storage (no
+ * concurrent decode calls on one cache).  Errors: INVALID_ARG, NOT_BOUND,
+ * NOT_FITTED, CAPACITY (a slot out of range or full), UNSUPPORTED, HIP. */
+int palu_decode_step(palu_cache *cache, const void *k_new, const void *v_new, const void *q,
+                     void *out, const int32_t *seq_ids, int32_t B, float softmax_scale,
+                     void *stream);
+
+/* Copies the slots' lengths from device memory to the host's copy (after
+ * graph replays of palu_decode_step).  Synchronous: waits for all device
+ * work.  Errors: INVALID_ARG, NOT_BOUND, HIP. */
+int palu_sync_lengths(palu_cache *cache);
+
 /* palu_decode_attend for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): the same kernels and results, with the split partials in a

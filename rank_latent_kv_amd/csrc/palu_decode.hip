@@ -127,9 +127,21 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                  "s"(a.q), "s"(a.k.head_stride), "s"(a.v.head_stride), "s"(a.k.r), "s"(a.k.cd.meta0), "s"(a.k.words),
                  "s"(a.v.r), "s"(a.v.cd.meta0), "s"(a.v.words), "s"(a.v.fp16_latents), "s"(a.chunk), "s"(a.hpg),
                  "s"(a.Hq), "s"(a.Hkv), "s"(a.qscale), "s"(rw.slot), "s"(rw.len), "s"(rw.qi), "s"(rw.sel_ns));
-    const int ns = rw.sel_ns >> 1, qi = rw.qi;
+    const int qi = rw.qi, slot = rw.slot;
+    int ns = rw.sel_ns >> 1, len = rw.len, tsl = rw.sel_ns & 1;
+    if (a.dev_len) {
+        // decode step: the row's length after this step's one-token append
+        // (none at the capacity), its tail buffer, and its splits; one
+        // workgroup hands (length, splits) to the combine kernel
+        len = min(a.len_dev[slot] + 1, a.max_len);
+        tsl = a.sel_dev[slot];
+        ns = max(1, ((len >> 5) + a.chunk - 1) / a.chunk);
+        if (h == 0 && z == 0 && threadIdx.x == 0) {
+            a.row_info[2 * qi] = len;
+            a.row_info[2 * qi + 1] = ns;
+        }
+    }
     if (z >= ns) return;                          // whole workgroup: no barrier reached
-    const int slot = rw.slot, len = rw.len;
     const int nfull = len >> 5, ntail = len & 31;
     // split of this workgroup: when the row's last split is a full chunk
     // and also carries the incomplete group it is the heaviest one, and it
@@ -196,7 +208,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                 __builtin_amdgcn_global_load_lds(e < nk4 ? ks + e : vs + (e - nk4), lds + boff + c * 1024, 16, 0, 0);
         }
     };
-    const int64_t tsel = (hb * 2 + (rw.sel_ns & 1)) * kTokGroup;
+    const int64_t tsel = (hb * 2 + tsl) * kTokGroup;
     const int tk_words = do_tail ? min((ntail * rk + 3) & ~3, kTokGroup * rk) : 0;
     const int tv_words = do_tail ? (vq ? min((ntail * rv + 3) & ~3, kTokGroup * rv) : 16 * rv) : 0;
     auto copy_tail = [&]() {
@@ -785,8 +797,15 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
     // all argument loads issued together (one scalar round trip)
     asm volatile("" ::"s"(a.partial), "s"(a.out), "s"(a.v.basis_cm), "s"(a.v.mu), "s"(a.v.r), "s"(a.gqa),
                  "s"(a.hpg), "s"(a.Hq), "s"(a.nsplit_call[i]), "s"(a.slot_call[i]), "s"(a.v.set_bcm), "s"(a.v.set_mu));
-    const int h = qh / a.gqa, grp = h / a.hpg, ns = a.nsplit_call[i], rv = a.v.r;
+    const int h = qh / a.gqa, grp = h / a.hpg, rv = a.v.r;
     const int64_t slot = a.slot_call[i];
+    int ns = a.nsplit_call[i];
+    if (a.dev_len) {
+        // decode step: splits from the attend kernel; the row's new length
+        // is committed here, after every reader of the old one has run
+        ns = a.row_info[2 * i + 1];
+        if (qh == 0 && lane == 0) a.len_dev[slot] = a.row_info[2 * i];
+    }
     const int np = ns * (rv + 2), npa = (np + 3) & ~3;
     float *pl = cl;                            // [ns][rv + 2]: m, l, o_lat
     float *bl = cl + npa;                      // [rv][D] value basis (channel-major)

@@ -106,7 +106,7 @@ struct palu_cache {
     int n_cus = 0;                // compute units of the device (0: not queried yet)
     // byte offsets of each region inside the bound buffer
     size_t off_basis[2]{}, off_bt16[2]{}, off_bcm[2]{}, off_mu[2]{}, off_rec[2]{}, off_tail[2]{};
-    size_t off_gram_part = 0, off_gram_out = 0, off_seg = 0, off_attend = 0, total = 0;
+    size_t off_gram_part = 0, off_gram_out = 0, off_seg = 0, off_attend = 0, off_len = 0, total = 0;
     char *dev = nullptr;
     size_t dev_bytes = 0;
     // basis sets: one per slot with per-sequence bases (the rank, and so
@@ -239,6 +239,21 @@ int check_slot(const palu_cache *c, int slot) {
 void reset_seqs(palu_cache *c) {
     std::fill(c->len.begin(), c->len.end(), 0);
     std::fill(c->sel.begin(), c->sel.end(), 0);
+}
+
+int *dev_len(const palu_cache *c) { return reinterpret_cast<int *>(c->dev + c->off_len); }
+int *dev_sel(const palu_cache *c) { return dev_len(c) + c->max_batch; }
+int *dev_row_info(const palu_cache *c) { return dev_len(c) + 2 * c->max_batch; }
+
+// The host's lengths and tail buffers -> their device copies (read by the
+// decode step).  Called by the synchronous calls that change them on the
+// host only; stream-ordered calls keep the copies current in their kernels.
+int push_lengths(palu_cache *c) {
+    if (!c->dev) return PALU_OK;
+    hipError_t e = hipMemcpy(dev_len(c), c->len.data(), sizeof(int) * c->max_batch, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(dev_sel(c), c->sel.data(), sizeof(int) * c->max_batch, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "length upload");
+    return PALU_OK;
 }
 
 // Fails when tensor t at rank rr would store no latent channel (a bit
@@ -425,6 +440,9 @@ PALU_API int palu_cache_create(const palu_config *cfg, int32_t max_batch, int32_
     // decode rows may repeat slots, so a launch can hold kMaxCallSeqs rows
     // whatever max_batch is
     c->off_attend = take(sizeof(float) * static_cast<size_t>(kMaxCallSeqs) * c->Hq * kMaxSplits * (c->r_max + 2));
+    // per-slot length and tail buffer (device copies of len / sel), then
+    // (length, splits) of each row of a decode step
+    c->off_len = take(sizeof(int32_t) * (2 * static_cast<size_t>(max_batch) + 2 * kMaxCallSeqs));
     c->total = off;
     *out = c;
     return PALU_OK;
@@ -449,6 +467,8 @@ PALU_API int palu_cache_bind(palu_cache *c, void *dev_buf, size_t bytes) {
         std::fill(c->ready[t].begin(), c->ready[t].end(), 0);
         c->rank_g[t].clear();
     }
+    // the device copies of the lengths are written by the fit or basis
+    // installation that every slot needs before its first token
     reset_seqs(c);
     return PALU_OK;
 }
@@ -697,7 +717,7 @@ int fit_per_seq(palu_cache *c, const void *k, const void *v, const int32_t *ids,
             if (int err = install_basis(c, t, slot, basis.data(), mu.data(), sigma.data())) return err;
         }
     }
-    return PALU_OK;
+    return push_lengths(c);
 }
 
 }  // namespace
@@ -778,6 +798,7 @@ PALU_API int palu_fit(palu_cache *c, const void *k, const void *v, const int32_t
     // every check has passed: the old bases and stored tokens go
     c->ready[0][0] = c->ready[1][0] = 0;
     reset_seqs(c);
+    if (int err = push_lengths(c)) return err;
     for (int t = 0; t < 2; ++t) {
         c->energy_rule[t] = c->cfg.rank <= 0;
         c->rank_g[t] = rank_g[t];
@@ -814,13 +835,14 @@ PALU_API int palu_set_basis(palu_cache *c, int32_t tensor, int32_t r, const floa
         for (int set = 0; set < c->nbs; ++set)
             if (int e = install_basis(c, tensor, set, basis, mu, nullptr)) return e;
         reset_seqs(c);
-        return PALU_OK;
+        return push_lengths(c);
     }
     if (r < 1 || r > c->r_max) return fail(PALU_ERR_INVALID_ARG, "r must be in [1, max_rank]");
     if (int e = check_coder(c, tensor, r)) return e;
     c->ready[tensor][0] = 0;
     c->rank_g[tensor].clear();
     reset_seqs(c);
+    if (int e = push_lengths(c)) return e;
     size_shared(c, tensor, r);
     if (int e = set_coder(c, tensor)) return e;
     return install_basis(c, tensor, 0, basis, mu, nullptr);
@@ -836,6 +858,7 @@ PALU_API int palu_set_basis_seq(palu_cache *c, int32_t seq, int32_t tensor, int3
     if (r != c->r[tensor]) return fail(PALU_ERR_INVALID_ARG, "r must equal the cache's rank");
     c->len[seq] = 0;
     c->sel[seq] = 0;
+    if (int e = push_lengths(c)) return e;
     return install_basis(c, tensor, seq, basis, mu, nullptr);
 }
 
@@ -901,6 +924,9 @@ PALU_API int palu_encode_append(palu_cache *c, const void *k, const void *v, con
         ea.T_stride = T_stride;
         ea.hpg = c->hpg;
         ea.bf16 = c->cfg.input_dtype;
+        ea.len_dev = dev_len(c);
+        ea.sel_dev = dev_sel(c);
+        ea.max_len = c->max_seq_len;
         int max_units = 0;   // group pairs touched by a row (one wave each)
         for (int i = 0; i < nb; ++i) {
             const int b = b0 + i;
@@ -944,19 +970,31 @@ namespace {
 // The split partials go to the bound buffer (fixed == nullptr) or to the
 // file-scope device array at `fixed` (kStaticScratchBytes), which every call
 // of one launch group reuses in stream order.
+// With step (palu_decode_step) every row first appends one token (K and V
+// from step[0] / step[1], [B][H][1][D]) and every kernel reads and advances
+// the lengths in device memory, so a captured call replays correctly later.
 int decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids, int32_t B,
-                  float softmax_scale, void *stream, float *fixed) {
+                  float softmax_scale, void *stream, float *fixed, const void *const *step = nullptr) {
     if (int e = check_fitted(c)) return e;
     if (!q || !out) return fail(PALU_ERR_INVALID_ARG, "q and out must be non-NULL");
     if (B <= 0) return fail(PALU_ERR_INVALID_ARG, "B must be positive");
     if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
         return fail(PALU_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    if (step && (!step[0] || !step[1])) return fail(PALU_ERR_INVALID_ARG, "k_new and v_new must be non-NULL");
+    std::vector<char> seen(step ? c->max_batch : 0, 0);
     for (int b = 0; b < B; ++b) {
         const int slot = seq_ids ? seq_ids[b] : b;
         if (int e = check_slot(c, slot)) return e;
-        if (c->len[slot] <= 0)
+        if (step) {
+            if (seen[slot]) return fail(PALU_ERR_INVALID_ARG, "sequence slot listed twice in one call");
+            seen[slot] = 1;
+            if (c->len[slot] + 1 > c->max_seq_len)
+                return fail(PALU_ERR_CAPACITY, "append to slot " + std::to_string(slot) + " exceeds max_seq_len");
+        } else if (c->len[slot] <= 0) {
             return fail(PALU_ERR_CAPACITY, "sequence slot " + std::to_string(slot) + " holds no tokens");
+        }
     }
+    const int add = step ? 1 : 0;   // tokens the call appends before attending
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(c->D));
     const size_t row_elems = static_cast<size_t>(c->Hq) * c->D;
@@ -984,11 +1022,11 @@ int decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_id
         for (int i = 0; i < nb; ++i) {
             const int slot = seq_ids ? seq_ids[b0 + i] : b0 + i;
             aa.row[i].slot = slot;
-            aa.row[i].len = c->len[slot];
+            aa.row[i].len = c->len[slot] + add;
             aa.row[i].qi = i;
             aa.row[i].sel_ns = c->sel[slot];
             aa.slot_call[i] = slot;
-            const int nfull = c->len[slot] / kTokGroup;
+            const int nfull = (c->len[slot] + add) / kTokGroup;
             units += static_cast<int64_t>(c->H) * std::max(1, nfull);
             max_full = std::max(max_full, nfull);
         }
@@ -1021,6 +1059,12 @@ int decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_id
             }
         }
         chunk = std::max<int64_t>(chunk, (max_full + kMaxSplits - 1) / kMaxSplits);
+        if (step) {
+            // a replayed step sees longer rows: the grid and the partials'
+            // split stride cover any length up to the capacity
+            const int cap_full = c->max_seq_len / kTokGroup;
+            chunk = std::max<int64_t>(chunk, (cap_full + kMaxSplits - 1) / kMaxSplits);
+        }
         int nsplit_max = 1;
         for (int i = 0; i < nb; ++i) {
             const int nfull = aa.row[i].len / kTokGroup;
@@ -1028,6 +1072,14 @@ int decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_id
             aa.row[i].sel_ns |= ns << 1;
             aa.nsplit_call[i] = ns;
             nsplit_max = std::max(nsplit_max, ns);
+        }
+        if (step) {
+            nsplit_max = std::max(1, static_cast<int>((c->max_seq_len / kTokGroup + chunk - 1) / chunk));
+            aa.dev_len = 1;
+            aa.len_dev = dev_len(c);
+            aa.sel_dev = dev_sel(c);
+            aa.row_info = dev_row_info(c);
+            aa.max_len = c->max_seq_len;
         }
         // longest rows first in the grid's y order (stable, so equal lengths keep call order)
         std::stable_sort(aa.row, aa.row + nb, [](const AttendRow &x, const AttendRow &y) { return x.len > y.len; });
@@ -1051,14 +1103,39 @@ int decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_id
                                 "or a larger split_groups, or palu_decode_attend)");
         }
     }
-    for (const AttendArgs &aa : launches) {
+    for (size_t li = 0; li < launches.size(); ++li) {
+        const AttendArgs &aa = launches[li];
+        hipError_t e;
+        if (step) {
+            // this launch's rows append their token (lengths from device memory)
+            const int b0 = static_cast<int>(li) * kMaxCallSeqs;
+            const size_t kv_elems = static_cast<size_t>(c->H) * c->D;
+            EncodeArgs ea{};
+            ea.x[0] = static_cast<const uint16_t *>(step[0]) + b0 * kv_elems;
+            ea.x[1] = static_cast<const uint16_t *>(step[1]) + b0 * kv_elems;
+            ea.t[0] = aa.k;
+            ea.t[1] = aa.v;
+            ea.B = aa.B;
+            ea.H = c->H;
+            ea.T_stride = 1;
+            ea.hpg = c->hpg;
+            ea.bf16 = c->cfg.input_dtype;
+            ea.len_dev = dev_len(c);
+            ea.sel_dev = dev_sel(c);
+            ea.dev_len = 1;
+            ea.max_len = c->max_seq_len;
+            for (int i = 0; i < aa.B; ++i) ea.slot[i] = aa.slot_call[i];
+            if ((e = launch_append1(ea, s)) != hipSuccess) return hip_fail(e, "append launch");
+        }
         const size_t lds =
             attend_lds_bytes(c->gqa, coder_blocks(aa.k.cd), aa.k.r, aa.v.r, aa.k.words, aa.v.words, !aa.v.fp16_latents);
-        hipError_t e = launch_attend(aa, lds, s);
+        e = launch_attend(aa, lds, s);
         if (e != hipSuccess) return hip_fail(e, "attend launch");
         e = launch_combine(aa, s);
         if (e != hipSuccess) return hip_fail(e, "combine launch");
     }
+    if (step)
+        for (int b = 0; b < B; ++b) c->len[seq_ids ? seq_ids[b] : b] += 1;   // one token never moves the tail buffer
     return PALU_OK;
 }
 
@@ -1067,6 +1144,21 @@ int decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_id
 PALU_API int palu_decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids, int32_t B,
                                 float softmax_scale, void *stream) {
     return decode_attend(c, q, out, seq_ids, B, softmax_scale, stream, nullptr);
+}
+
+PALU_API int palu_decode_step(palu_cache *c, const void *k_new, const void *v_new, const void *q, void *out,
+                              const int32_t *seq_ids, int32_t B, float softmax_scale, void *stream) {
+    const void *kv[2] = {k_new, v_new};
+    return decode_attend(c, q, out, seq_ids, B, softmax_scale, stream, nullptr, kv);
+}
+
+PALU_API int palu_sync_lengths(palu_cache *c) {
+    if (int e = check_bound(c)) return e;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(c->len.data(), dev_len(c), sizeof(int) * c->max_batch, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(c->sel.data(), dev_sel(c), sizeof(int) * c->max_batch, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "length download");
+    return PALU_OK;
 }
 
 PALU_API int palu_decode_attend_noalloc(palu_cache *c, const void *q, void *out, const int32_t *seq_ids,
@@ -1271,7 +1363,7 @@ PALU_API int palu_get_fit_info(const palu_cache *c, int32_t tensor, int32_t *r_g
 PALU_API int palu_reset(palu_cache *c) {
     if (!c) return fail(PALU_ERR_INVALID_ARG, "cache is NULL");
     reset_seqs(c);
-    return PALU_OK;
+    return push_lengths(c);
 }
 
 PALU_API int palu_record_words(const palu_cache *c, int32_t tensor, int32_t *words) {
@@ -1470,6 +1562,7 @@ PALU_API int palu_import_seq(palu_cache *c, int32_t seq, const void *host_src, s
         if (h != basis_hash(c, part)) return fail(PALU_ERR_INVALID_ARG, "saved bases do not match their hash");
         c->len[seq] = 0;
         c->sel[seq] = 0;
+        if (int err = push_lengths(c)) return err;
         for (int t = 0; t < 2; ++t)
             if (int e = install_basis(c, t, seq, part[2 * t], part[2 * t + 1], nullptr)) return e;
     } else {
@@ -1500,7 +1593,7 @@ PALU_API int palu_import_seq(palu_cache *c, int32_t seq, const void *host_src, s
     if (e != hipSuccess) return hip_fail(e, "import synchronize");
     c->len[seq] = len;
     c->sel[seq] = 0;
-    return PALU_OK;
+    return push_lengths(c);
 }
 
 PALU_API const char *palu_last_error(void) { return g_last_error.c_str(); }

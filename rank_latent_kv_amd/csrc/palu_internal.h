@@ -117,6 +117,13 @@ struct EncodeArgs {
     TensorDev t[2];
     int B, H, T_stride, hpg;
     int bf16;                 // inputs are bf16 (else fp16)
+    // Per-slot stored length and live tail buffer in device memory.  With
+    // dev_len = 0 the lengths below come from the host and one workgroup per
+    // row writes the new length and buffer there; with dev_len = 1 (one token
+    // per row, lengths read from there) nothing writes them: the decode step
+    // that follows commits the new length.
+    int *len_dev, *sel_dev;
+    int dev_len, max_len;
     int slot[kMaxCallSeqs];
     int old_len[kMaxCallSeqs];
     int n_new[kMaxCallSeqs];
@@ -145,6 +152,15 @@ struct AttendArgs {
     // the key channel blocks
     float inv_rv, inv_nbk4;
     int bf16;                 // q and out are bf16 (else fp16)
+    // dev_len = 1 (decode step after a one-token append): a row's length is
+    // min(len_dev[slot] + 1, max_len) and its tail buffer sel_dev[slot], its
+    // split count follows from chunk; the attend kernel hands (length,
+    // splits) of call row i to the combine kernel in row_info[2 i], which
+    // then commits the length to len_dev.
+    int *len_dev;
+    const int *sel_dev;
+    int *row_info;
+    int dev_len, max_len;
     AttendRow row[kMaxCallSeqs];       // grid y order (longest first)
     int nsplit_call[kMaxCallSeqs];     // splits of call row i (combine)
     int slot_call[kMaxCallSeqs];       // cache slot of call row i (combine)
@@ -196,8 +212,8 @@ hipError_t gram_resident_blocks(int *n);
 hipError_t launch_gram_reduce(const GramReduceArgs &a, hipStream_t s);
 // One wave per (pair of touched token groups, call row x head, tensor).
 hipError_t launch_encode(const EncodeArgs &a, int max_units, hipStream_t s);
-// Appends of at most one token per row: one workgroup per (call row x head,
-// tensor), one thread per latent channel.
+// Appends of at most one token per row: one workgroup of one wave per (call
+// row x head, tensor), one lane per latent channel.
 hipError_t launch_append1(const EncodeArgs &a, hipStream_t s);
 // Grid (Hkv, B, nsplit_max): one workgroup per (kv head, row, split), the head fastest.
 hipError_t launch_attend(const AttendArgs &a, size_t lds_bytes, hipStream_t s);

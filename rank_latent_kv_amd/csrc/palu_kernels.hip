@@ -336,6 +336,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
     const int bi = blockIdx.y / a.H, h = blockIdx.y - (blockIdx.y / a.H) * a.H;
     const int tz = blockIdx.z;
     const int o = a.old_len[bi], n = a.n_new[bi];
+    // the row's new length and tail buffer, mirrored in device memory
+    if (blockIdx.x == 0 && h == 0 && tz == 0 && tid == 0 && a.len_dev) {
+        a.len_dev[a.slot[bi]] = o + n;
+        a.sel_dev[a.slot[bi]] = a.sel_new[bi];
+    }
     if (n <= 0) return;                              // whole workgroup
     const int j0 = o >> 5, jl = (o + n - 1) >> 5;
     if (2 * ((j0 >> 1) + blockIdx.x * kEncWaves) > jl) return;   // whole workgroup
@@ -463,75 +468,112 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
 // channel's 32 latents (31 from the tail, the new one) are quantised in
 // token order and the codes OR-ed into an LDS copy of the record.
 
-constexpr int kApp1Threads = 128;
+// One wave per (call row x kv head, tensor).  Lane c owns latent channel c
+// (and c + 64 when r > 64): its basis row (channel-major copy, 128 floats)
+// comes into registers with the first loads, the centred input y = x - mu is
+// broadcast through LDS, and the channel's latent is the fixed-order fp32
+// chain fma(y_d, V[d][c], acc), d = 0..D-1.  An incomplete group keeps the
+// latent in the fp32 tail; a token that completes its group quantises the
+// group's 32 latents per channel (lane = channel) and ORs the codes into an
+// LDS copy of the record.
+constexpr int kApp1Threads = 64;
 
-__host__ __device__ inline int append1_lds_bytes(int r, int words) {
-    return (kHeadDim + r * kHeadDim + words) * 4;     // y [D], basis [D][r], record
-}
+__host__ __device__ inline int append1_lds_bytes(int words) { return (kHeadDim + words) * 4; }
 
 template <bool BF16>
 __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
     extern __shared__ __align__(16) float ash[];
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x;
     const int bi = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
     const int tz = blockIdx.y;
-    const int o = a.old_len[bi], n = a.n_new[bi];
+    const int slot = a.slot[bi];
+    int o, n, sel_old, sel_new;
+    if (a.dev_len) {
+        // one token per row at the stored length (nothing past the capacity)
+        o = a.len_dev[slot];
+        n = o < a.max_len ? 1 : 0;
+        sel_old = sel_new = a.sel_dev[slot];   // one token never moves the tail buffer
+    } else {
+        o = a.old_len[bi];
+        n = a.n_new[bi];
+        sel_old = a.sel_old[bi];
+        sel_new = a.sel_new[bi];
+        if (h == 0 && tz == 0 && lane == 0 && a.len_dev) {
+            a.len_dev[slot] = o + n;
+            a.sel_dev[slot] = sel_new;
+        }
+    }
     if (n <= 0) return;                               // whole workgroup
     const TensorDev &T = tz ? a.t[1] : a.t[0];
     const int r = T.r, W = T.words;
-    const int grp = h / a.hpg, slot = a.slot[bi];
+    const int grp = h / a.hpg;
     const int64_t head_base = static_cast<int64_t>(slot) * a.H + h;
     const int j = o >> 5, t = o & 31;                 // group and position of the new token
-    const bool complete = t == 31;
+    const bool complete = t == 31 && !T.fp16_latents;
     float *ys = ash;
-    float *vs = ash + kHeadDim;
-    uint32_t *rec = reinterpret_cast<uint32_t *>(vs + r * kHeadDim);
+    uint32_t *rec = reinterpret_cast<uint32_t *>(ash + kHeadDim);
 
-    // 1. y = float(x) - mu and the basis -> LDS
+    // 1. y = float(x) - mu, two elements per lane, to LDS; the record copy
+    //    is cleared when the group completes
     const uint16_t *xin = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim;
-    if (tid < kHeadDim) ys[tid] = in2f<BF16>(xin[tid]) - T.mu[slot * T.set_mu + grp * kHeadDim + tid];
-    const float *vb = T.basis + slot * T.set_basis + static_cast<int64_t>(grp) * kHeadDim * r;
-    for (int e = tid; e < kHeadDim * r; e += kApp1Threads) vs[e] = vb[e];
-    if (complete && !T.fp16_latents)
-        for (int w = tid; w < W; w += kApp1Threads) rec[w] = 0u;
+    const uint32_t xp = reinterpret_cast<const uint32_t *>(xin)[lane];
+    const float2 mu = reinterpret_cast<const float2 *>(T.mu + slot * T.set_mu + grp * kHeadDim)[lane];
+    reinterpret_cast<float2 *>(ys)[lane] = make_float2(in2f<BF16>(xp & 0xFFFFu) - mu.x, in2f<BF16>(xp >> 16) - mu.y);
+    if (complete)
+        for (int w = lane; w < W; w += kApp1Threads) rec[w] = 0u;
     __syncthreads();
 
-    // 2. channel c of the latent: acc = fma(y_d, V[d][c], acc), d = 0..D-1
-    const int c = tid;
-    float lat = 0.0f;
-    if (c < r)
-        for (int d = 0; d < kHeadDim; ++d) lat = __builtin_fmaf(ys[d], vs[d * r + c], lat);
-    if (T.fp16_latents) {                             // uniform: no tail, no quantiser
-        if (c < r) {
+    const float *bcm = T.basis_cm + slot * T.set_bcm + static_cast<int64_t>(grp) * r * kHeadDim;
+    const float4 *ys4 = reinterpret_cast<const float4 *>(ys);
+    const float *told = T.tail + (head_base * 2 + sel_old) * 32 * r;
+    for (int c = lane; c < r; c += kApp1Threads) {
+        // 2. the chain, with the channel's basis row in registers; when the
+        //    group completes, its 31 older latents are loaded alongside
+        float4 vb[kHeadDim / 4];
+        const float4 *row = reinterpret_cast<const float4 *>(bcm + static_cast<int64_t>(c) * kHeadDim);
+#pragma unroll
+        for (int d4 = 0; d4 < kHeadDim / 4; ++d4) vb[d4] = row[d4];
+        float lv[32];
+        if (complete) {
+#pragma unroll
+            for (int tt = 0; tt < 31; ++tt) lv[tt] = told[tt * r + c];
+        }
+        float lat = 0.0f;
+#pragma unroll
+        for (int d4 = 0; d4 < kHeadDim / 4; ++d4) {
+            const float4 y = ys4[d4];
+            lat = __builtin_fmaf(y.x, vb[d4].x, lat);
+            lat = __builtin_fmaf(y.y, vb[d4].y, lat);
+            lat = __builtin_fmaf(y.z, vb[d4].z, lat);
+            lat = __builtin_fmaf(y.w, vb[d4].w, lat);
+        }
+        if (T.fp16_latents) {                         // uniform: no tail, no quantiser
             uint16_t *rec16 = reinterpret_cast<uint16_t *>(T.records + head_base * T.head_stride +
                                                            static_cast<int64_t>(j) * W);
             rec16[c * 32 + t] = static_cast<uint16_t>(f2h_bits(lat));
+            continue;
         }
-        return;
-    }
-    if (!complete) {                                  // uniform
-        if (c < r) T.tail[(head_base * 2 + a.sel_new[bi]) * 32 * r + t * r + c] = lat;
-        return;
-    }
-
-    // 3. the group completes: channel c over its 32 latents in token order
-    if (c < r) {
-        const float *told = T.tail + (head_base * 2 + a.sel_old[bi]) * 32 * r;
-        float mn = told[c], mx = mn;                  // token 0 (t == 31 here, so it is old)
+        if (!complete) {                              // uniform
+            T.tail[(head_base * 2 + sel_new) * 32 * r + t * r + c] = lat;
+            continue;
+        }
+        // 3. the group completes: channel c over its 32 latents in token order
+        lv[31] = lat;
+        float mn = lv[0], mx = mn;
+#pragma unroll
         for (int tt = 1; tt < 32; ++tt) {
-            const float v = tt == 31 ? lat : told[tt * r + c];
-            mn = v < mn ? v : mn;
-            mx = v > mx ? v : mx;
+            mn = lv[tt] < mn ? lv[tt] : mn;
+            mx = lv[tt] > mx ? lv[tt] : mx;
         }
         const int2 b0 = code_bit(T.cd, tz, c, 0);    // token 0's bit, width
         const int tstep = tz == 0 ? code_bit(T.cd, 0, c, 1).x - b0.x : b0.y;   // bits between tokens
         const float levels = static_cast<float>((1 << b0.y) - 1);
         const float scale = (mx - mn) / levels;
+#pragma unroll
         for (int tt = 0; tt < 32; ++tt) {
-            const float v = tt == 31 ? lat : told[tt * r + c];
             int q = 0;
             if (scale > 0.0f) {
-                float uq = rintf((v - mn) / scale);
+                float uq = rintf((lv[tt] - mn) / scale);
                 uq = uq < 0.0f ? 0.0f : (uq > levels ? levels : uq);
                 q = static_cast<int>(uq);
             }
@@ -540,9 +582,10 @@ __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
         }
         rec[T.cd.meta0 + c] = f2h_bits(scale) | (f2h_bits(mn) << 16);
     }
+    if (!complete) return;                            // uniform
     __syncthreads();
     uint32_t *dst = T.records + head_base * T.head_stride + static_cast<int64_t>(j) * W;
-    for (int w = tid; w < W; w += kApp1Threads) dst[w] = rec[w];
+    for (int w = lane; w < W; w += kApp1Threads) dst[w] = rec[w];
 }
 
 // dst[g][n][d] = fp16(V[g][d][chan(n)]) for the score-operand position n
@@ -595,7 +638,7 @@ static hipError_t launch_append1_t(const EncodeArgs &a, hipStream_t s) {
         hipFuncSetAttribute(reinterpret_cast<const void *>(append1_kernel<BF16>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    const int l0 = append1_lds_bytes(a.t[0].r, a.t[0].words), l1 = append1_lds_bytes(a.t[1].r, a.t[1].words);
+    const int l0 = append1_lds_bytes(a.t[0].words), l1 = append1_lds_bytes(a.t[1].words);
     hipLaunchKernelGGL(append1_kernel<BF16>, dim3(a.B * a.H, 2), dim3(kApp1Threads),
                        static_cast<size_t>(l0 > l1 ? l0 : l1), s, a);
     return hipGetLastError();

@@ -25,7 +25,8 @@ ERROR_NAMES = {1: "PALU_ERR_INVALID_ARG", 2: "PALU_ERR_UNSUPPORTED", 3: "PALU_ER
 EXPORTED = ["palu_config_default", "palu_cache_create", "palu_cache_required_bytes",
             "palu_cache_bind", "palu_fit", "palu_set_basis", "palu_get_basis",
             "palu_fit_seq", "palu_set_basis_seq", "palu_get_basis_seq",
-            "palu_encode_append", "palu_decode_attend", "palu_decode_attend_noalloc",
+            "palu_encode_append", "palu_decode_attend", "palu_decode_step", "palu_sync_lengths",
+            "palu_decode_attend_noalloc",
             "palu_prefill_attend", "palu_seq_len",
             "palu_read_codes",
             "palu_get_stats", "palu_reset", "palu_record_words", "palu_export_bytes",
@@ -94,6 +95,8 @@ def lib():
         "palu_encode_append": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, _vp],
         "palu_decode_attend": [_vp, _vp, _vp, _i32p, _i32, ctypes.c_float, _vp],
         "palu_decode_attend_noalloc": [_vp, _vp, _vp, _i32p, _i32, ctypes.c_float, _vp],
+        "palu_decode_step": [_vp, _vp, _vp, _vp, _vp, _i32p, _i32, ctypes.c_float, _vp],
+        "palu_sync_lengths": [_vp],
         "palu_prefill_attend": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, ctypes.c_float, _vp],
         "palu_seq_len": [_vp, _i32, _i32p],
         "palu_read_codes": [_vp, _i32, _i32, _i32, _vp, _sz, _vp, _sz],
@@ -219,6 +222,17 @@ def palu_decode_attend(cache: int, q_ptr: int, out_ptr: int, seq_ids, B: int,
     s = _i32_array(seq_ids, B, "seq_ids")
     _check(lib().palu_decode_attend(cache, q_ptr, out_ptr, s[1] if s else None, B,
                                     softmax_scale, stream))
+
+
+def palu_decode_step(cache: int, k_ptr: int, v_ptr: int, q_ptr: int, out_ptr: int, seq_ids, B: int,
+                     softmax_scale: float, stream: int):
+    s = _i32_array(seq_ids, B, "seq_ids")
+    _check(lib().palu_decode_step(cache, k_ptr, v_ptr, q_ptr, out_ptr, s[1] if s else None, B,
+                                  softmax_scale, stream))
+
+
+def palu_sync_lengths(cache: int):
+    _check(lib().palu_sync_lengths(cache))
 
 
 def palu_decode_attend_noalloc(cache: int, q_ptr: int, out_ptr: int, seq_ids, B: int,
@@ -437,6 +451,24 @@ class LatentKVCache:
         palu_decode_attend(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, q.shape[0],
                            softmax_scale, self._stream())
         return out
+
+    def decode_step(self, k_new, v_new, q, out, seq_ids=None, softmax_scale: float = 0.0):
+        """Append one token per row (k_new, v_new: [B, H, 1, D]) and attend
+        (q, out: [B, Hq, D]) in one graph-replayable call."""
+        self._check_rank(q, 3, "q")
+        self._check_half(q, (self.Hq, self.D), "q")
+        B = q.shape[0]
+        self._check_half(k_new, None, "k_new", (B, self.H, 1, self.D))
+        self._check_half(v_new, None, "v_new", (B, self.H, 1, self.D))
+        self._check_half(out, None, "out", tuple(q.shape))
+        _i32_array(seq_ids, B, "seq_ids")
+        palu_decode_step(self.handle, k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), out.data_ptr(),
+                         seq_ids, B, softmax_scale, self._stream())
+        return out
+
+    def sync_lengths(self):
+        """Host lengths <- device lengths (after replaying captured steps)."""
+        palu_sync_lengths(self.handle)
 
     def decode_attend_noalloc(self, q, out, seq_ids=None, softmax_scale: float = 0.0):
         """decode_attend with the split partials in the library's static
