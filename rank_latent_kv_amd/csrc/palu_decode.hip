@@ -104,7 +104,7 @@ __host__ __device__ inline AttendLds attend_lds(int g, int nbk, int rk, int rv, 
 // processed in passes of up to 4 S token groups (S per wave); the records of
 // pass p + 1 are copied global -> LDS (direct 16-byte loads into LDS, no
 // registers) into the other of two buffers while pass p is computed.
-template <int G, int NBV, bool VQ, bool GEN>
+template <int G, int NBV, bool VQ, bool GEN, int NBKF>
 __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     constexpr int g = G, S = 16 / G, NS = S * G;
     constexpr bool vq = VQ;                      // V stored as mixed-bit codes
@@ -379,9 +379,56 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         return ok ? qt16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
     };
     uint4 bq_pre[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
-    if (nub <= 2) {
-        bq_pre[0] = score_b(0);
-        if (nub == 2) bq_pre[1] = score_b(1);
+    // Fast path: 4 query heads per kv head (S = 4), PALU layout, quantised
+    // values, at most 4 key blocks.  Lane kb then always serves slot kb and
+    // score step u is key block u, so everything a lane addresses is fixed:
+    // the score operands B of every step stay in registers, the metadata of
+    // (slot kb, block u) is at a constant offset, and the bit of the lane's
+    // token in block u's plane is precomputed.  The score MFMA's row ln of
+    // half h holds token 8 (ln / 4) + 4 h + ln % 4, so the softmax weights
+    // a lane holds (rows 4 kb .. 4 kb + 3 of both halves) are the tokens
+    // 8 kb .. 8 kb + 7, and each value operand comes from one word: the
+    // lane's 8 tokens of its channel (4-bit: word kb of the channel; 2-bit:
+    // half kb % 2 of word kb / 2, its second byte moved up by a permute).
+    // (the host launches this variant only with 4 query heads per kv
+    // head, a PALU-shaped key coder of at most 4 blocks and quantised values)
+    // NBKF > 0: this variant, for exactly NBKF key blocks
+    constexpr bool FAST = NBKF > 0 && G == 4 && !GEN && VQ;
+    constexpr bool fast = FAST;
+    constexpr int NF = NBKF > 0 ? NBKF : 1;
+    uint4 bqf[NF];
+    int bitA[NF];
+    int vwf[NBV];
+    uint32_t vsel[NBV];
+    if constexpr (FAST) {
+        if (fast) {
+            const int t0 = 8 * (ln >> 2) + (ln & 3);
+#pragma unroll
+            for (int u = 0; u < NF; ++u) {
+                bqf[u] = score_b(u);
+                const bool w4 = u < nbh;
+                const int base = w4 ? 32 * u : 128 * nhk + 16 * (u - nbh);
+                const int stride = w4 ? 4 * nhk : 2 * nlk;
+                bitA[u] = base + t0 * stride;
+            }
+#pragma unroll
+            for (int nb = 0; nb < NBV; ++nb) {
+                const int c = vch[nb];
+                if (c < nhv) {
+                    vwf[nb] = 4 * c + kb;
+                    vsel[nb] = 0x03020100u;
+                } else {
+                    vwf[nb] = 4 * nhv + 2 * (c - nhv) + (kb >> 1);
+                    vsel[nb] = (kb & 1) ? 0x0C030C02u : 0x0C010C00u;
+                }
+            }
+        }
+    }
+    if constexpr (!fast) {
+        if (nub <= 2) {
+            bq_pre[0] = score_b(0);
+            if (nub == 2) bq_pre[1] = score_b(1);
+        }
     }
     for (int pi = 0; pi < npass; ++pi) {
         if (pi + 1 < npass) copy_pass(pi + 1);       // into the other buffer
@@ -500,11 +547,44 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bop, sacc0, 0, 0, 0);
             sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bop, sacc1, 0, 0, 0);
         };
-        if (nub <= 2) {
-            score_step(0, bq_pre[0]);
-            if (nub == 2) score_step(1, bq_pre[1]);
+        if constexpr (fast) {
+            const int tgl = tb0 + kb < npg ? tb0 + kb : npg - 1;
+            const uint32_t *rec = stage + koff + tgl * WK;
+            const uint4 *kpl = reinterpret_cast<const uint4 *>(kpw + kb * nbk * 8);
+#pragma unroll
+            for (int u = 0; u < NF; ++u) {
+                {
+                    // the second half's token is 4 tokens further (stride: bits per token)
+                    const int stride = u < nbh ? 4 * nhk : 2 * nlk;
+                    const int bitB = bitA[u] + 4 * stride;
+                    const int wa = bitA[u] >> 5, wb = bitB >> 5;
+                    const uint32_t X0 = __builtin_amdgcn_alignbit(rec[wa + 1], rec[wa], bitA[u] & 31);
+                    const uint32_t X1 = __builtin_amdgcn_alignbit(rec[wb + 1], rec[wb], bitB & 31);
+                    const uint4 sp = kpl[2 * u], zp = kpl[2 * u + 1];
+                    f16x8 a0, a1;
+                    if (u < nbh) {
+                        a0 = codes8<true>(X0, km4, kmagic);
+                        a1 = codes8<true>(X1, km4, kmagic);
+                    } else {
+                        a0 = codes8<false>(X0, km2, kmagic);
+                        a1 = codes8<false>(X1, km2, kmagic);
+                    }
+                    const f16x8 bop = as_h8(bqf[u].x, bqf[u].y, bqf[u].z, bqf[u].w);
+                    const f16x8 bs = bop * as_h8(sp.x, sp.y, sp.z, sp.w);
+                    sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bs, sacc0, 0, 0, 0);
+                    sacc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bs, sacc1, 0, 0, 0);
+                    zacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(zp.x, zp.y, zp.z, zp.w), bop, zacc, 0, 0,
+                                                                  0);
+                    zacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kneg1024, bs, zacc, 0, 0, 0);
+                }
+            }
         } else {
-            for (int u = 0; u < nub; ++u) score_step(u, score_b(u));
+            if (nub <= 2) {
+                score_step(0, bq_pre[0]);
+                if (nub == 2) score_step(1, bq_pre[1]);
+            } else {
+                for (int u = 0; u < nub; ++u) score_step(u, score_b(u));
+            }
         }
 
         // (c) online softmax of stream ln (rows 4*kb + v of both 16-token halves)
@@ -579,7 +659,17 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 #pragma unroll
             for (int nb = 0; nb < NBV; ++nb) {
                 uint32_t bp0, bp1, bp2, bp3;
-                if constexpr (VQ) {
+                if constexpr (fast) {
+                    // tokens (8 kb + j, 8 kb + 4 + j) of channel vch[nb] in pair j
+                    const uint32_t *rec = stage + voff + (tb0 + m) * WV;
+                    const uint32_t Wd = rec[vwf[nb]];
+                    const uint32_t U = perm_b32(Wd, Wd, vsel[nb]);
+                    const int wc = vwc[nb];
+                    bp0 = (U & vcm[nb]) | kmagic;
+                    bp1 = ((U >> wc) & vcm[nb]) | kmagic;
+                    bp2 = ((U >> (2 * wc)) & vcm[nb]) | kmagic;
+                    bp3 = ((U >> (3 * wc)) & vcm[nb]) | kmagic;
+                } else if constexpr (VQ) {
                     const uint32_t *rec = stage + voff + (tb0 + m) * WV;
                     const uint32_t L0 = rec[vw0[nb]], L1 = rec[vw1[nb]];
                     const int wc = vwc[nb];
@@ -981,15 +1071,32 @@ size_t attend_lds_bytes(int gqa, int nbk, int r_k, int r_v, int words_k, int wor
     return static_cast<size_t>(attend_lds(gqa, nbk, r_k, r_v, words_k, words_v, vq).total);
 }
 
-template <int G, int NBV, bool VQ, bool GEN>
-static hipError_t launch_attend_tg(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+template <int G, int NBV, bool VQ, bool GEN, int NBKF>
+static hipError_t launch_attend_tgf(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
     // set once per process (thread-safe static initialisation)
     static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<G, NBV, VQ, GEN>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&attend_kernel<G, NBV, VQ, GEN, NBKF>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((attend_kernel<G, NBV, VQ, GEN>), dim3(a.Hkv, a.B, a.nsplit_max), dim3(256), lds_bytes, s, a);
+    hipLaunchKernelGGL((attend_kernel<G, NBV, VQ, GEN, NBKF>), dim3(a.Hkv, a.B, a.nsplit_max), dim3(256), lds_bytes, s,
+                       a);
     return hipGetLastError();
+}
+
+// The fast variant serves 4 query heads per kv head with a PALU-shaped key
+// coder of at most 4 channel blocks and quantised values.
+template <int G, int NBV, bool VQ, bool GEN>
+static hipError_t launch_attend_tg(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+    if constexpr (G == 4 && VQ && !GEN) {
+        switch (coder_blocks(a.k.cd)) {
+            case 1: return launch_attend_tgf<G, NBV, VQ, GEN, 1>(a, lds_bytes, s);
+            case 2: return launch_attend_tgf<G, NBV, VQ, GEN, 2>(a, lds_bytes, s);
+            case 3: return launch_attend_tgf<G, NBV, VQ, GEN, 3>(a, lds_bytes, s);
+            case 4: return launch_attend_tgf<G, NBV, VQ, GEN, 4>(a, lds_bytes, s);
+            default: break;
+        }
+    }
+    return launch_attend_tgf<G, NBV, VQ, GEN, 0>(a, lds_bytes, s);
 }
 
 // A PALU-shaped coder: one 4-bit or 2-bit segment, or 4-bit then 2-bit.
