@@ -391,7 +391,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     // lane's 8 tokens of its channel (4-bit: word kb of the channel; 2-bit:
     // half kb % 2 of word kb / 2, its second byte moved up by a permute).
     // (the host launches this variant only with 4 query heads per kv
-    // head, a PALU-shaped key coder of at most 4 blocks and quantised values)
+    // head, quantised values and a PALU key coder of at most 4 blocks whose
+    // first block is the only 4-bit one: 1 to 8 hi channels)
     // NBKF > 0: this variant, for exactly NBKF key blocks
     constexpr bool FAST = NBKF > 0 && G == 4 && !GEN && VQ;
     constexpr bool fast = FAST;
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 #pragma unroll
             for (int u = 0; u < NF; ++u) {
                 bqf[u] = score_b(u);
-                const bool w4 = u < nbh;
+                const bool w4 = u == 0;
                 const int base = w4 ? 32 * u : 128 * nhk + 16 * (u - nbh);
                 const int stride = w4 ? 4 * nhk : 2 * nlk;
                 bitA[u] = base + t0 * stride;
@@ -555,20 +556,14 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             for (int u = 0; u < NF; ++u) {
                 {
                     // the second half's token is 4 tokens further (stride: bits per token)
-                    const int stride = u < nbh ? 4 * nhk : 2 * nlk;
+                    const int stride = u == 0 ? 4 * nhk : 2 * nlk;
                     const int bitB = bitA[u] + 4 * stride;
                     const int wa = bitA[u] >> 5, wb = bitB >> 5;
                     const uint32_t X0 = __builtin_amdgcn_alignbit(rec[wa + 1], rec[wa], bitA[u] & 31);
                     const uint32_t X1 = __builtin_amdgcn_alignbit(rec[wb + 1], rec[wb], bitB & 31);
                     const uint4 sp = kpl[2 * u], zp = kpl[2 * u + 1];
-                    f16x8 a0, a1;
-                    if (u < nbh) {
-                        a0 = codes8<true>(X0, km4, kmagic);
-                        a1 = codes8<true>(X1, km4, kmagic);
-                    } else {
-                        a0 = codes8<false>(X0, km2, kmagic);
-                        a1 = codes8<false>(X1, km2, kmagic);
-                    }
+                    const f16x8 a0 = u == 0 ? codes8<true>(X0, km4, kmagic) : codes8<false>(X0, km2, kmagic);
+                    const f16x8 a1 = u == 0 ? codes8<true>(X1, km4, kmagic) : codes8<false>(X1, km2, kmagic);
                     const f16x8 bop = as_h8(bqf[u].x, bqf[u].y, bqf[u].z, bqf[u].w);
                     const f16x8 bs = bop * as_h8(sp.x, sp.y, sp.z, sp.w);
                     sacc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bs, sacc0, 0, 0, 0);
@@ -1087,8 +1082,10 @@ static hipError_t launch_attend_tgf(const AttendArgs &a, size_t lds_bytes, hipSt
 // coder of at most 4 channel blocks and quantised values.
 template <int G, int NBV, bool VQ, bool GEN>
 static hipError_t launch_attend_tg(const AttendArgs &a, size_t lds_bytes, hipStream_t s) {
+    const bool hi_first = a.k.cd.nseg == 2 && a.k.cd.bits[0] == 4 && a.k.cd.bits[1] == 2 && a.k.cd.c0[1] >= 1 &&
+                          a.k.cd.c0[1] <= 8;
     if constexpr (G == 4 && VQ && !GEN) {
-        switch (coder_blocks(a.k.cd)) {
+        if (hi_first) switch (coder_blocks(a.k.cd)) {
             case 1: return launch_attend_tgf<G, NBV, VQ, GEN, 1>(a, lds_bytes, s);
             case 2: return launch_attend_tgf<G, NBV, VQ, GEN, 2>(a, lds_bytes, s);
             case 3: return launch_attend_tgf<G, NBV, VQ, GEN, 3>(a, lds_bytes, s);
