@@ -403,7 +403,9 @@ PALU_API int palu_cache_create(const palu_config *cfg, int32_t max_batch, int32_
     c->sb_mu = static_cast<int64_t>(c->G) * c->D;
     for (int t = 0; t < 2; ++t) {
         c->ready[t].assign(c->nbs, 0);
-        c->off_basis[t] = take(sizeof(float) * c->nbs * c->sb_basis);
+        // + 4 floats of slack: the encode projection reads whole groups of
+        // 4 channels, up to 3 past the last row of the last basis
+        c->off_basis[t] = take(sizeof(float) * (c->nbs * c->sb_basis + 4));
         // only the key basis is absorbed into queries: no fp16 copy of V's
         c->off_bt16[t] = t == 0 ? take(sizeof(uint16_t) * c->nbs * c->sb_bt16) : 0;
         c->off_bcm[t] = take(sizeof(float) * c->nbs * c->sb_bcm);

@@ -188,145 +188,140 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(GramReduceArgs a) {
 //
 // One wave per pair of token groups (64 positions, lane = position) of one
 // (call row, kv head, tensor); four independent waves per workgroup, no
-// workgroup barriers.  Wave unit u of a row covers groups 2 (j0/2 + u) and
-// 2 (j0/2 + u) + 1, j0 = old_len / 32.  A lane's position is new (in
-// [old, old + n)), old (an earlier position of group j0, read back from the
-// tail buffer) or outside the call.  Per lane y_d = float(x_d) - mu_d in
-// fp32, then per channel the fixed-order chain acc = fma(y_d, V[d][c], acc),
-// d = 0..D-1; the group's basis (rows padded to a multiple of 4 floats) and
-// mean are staged in LDS once per workgroup and read as broadcasts.  The 32
-// lanes of a complete group quantise it (min/max by lane reductions, IEEE
-// division, round-half-even) and OR their codes into an LDS copy of the
-// record at the layout's bit positions; an incomplete group's new latents go
-// to the tail buffer; fp16 value latents are stored directly.
+// workgroup barriers after the code table.  Wave unit u of a row covers
+// groups 2 (j0/2 + u) and 2 (j0/2 + u) + 1, j0 = old_len / 32.  A lane's
+// position is new (in [old, old + n)), old (an earlier position of group j0,
+// read back from the tail buffer) or outside the call.  Per lane
+// y_d = float(x_d) - mu_d in fp32 (one mixed-precision fma per fp16 element,
+// the same single rounding), then per channel the fixed-order chain
+// acc = fma(y_d, V[d][c], acc), d = 0..D-1.  The basis and the mean are the
+// same for every lane: they come in through scalar loads and enter the fmas
+// as SGPR operands, so the projection reads no LDS.
+//
+// A complete group is quantised in three passes over its channels: (1) the
+// minimum and maximum over each 32-lane half by DPP (the results land in
+// lanes 31 and 63); (2) one lane per (group, channel) forms
+// scale = (max - min) / levels by IEEE division, its reciprocal and the
+// metadata word; (3) every lane forms its code
+// round-half-even((l - min) / scale) and ORs it into an LDS copy of the
+// record at the layout's bit position.  The IEEE quotient decides each code:
+// the reciprocal product is within 2^-21 relative of it (reciprocal within
+// 1 ulp, one product rounding), so for quotients below 256 the two round to
+// the same integer unless the product lies within 2^-11 of a half-integer,
+// and there the lane divides.  An incomplete group's new latents go to the
+// tail buffer; fp16 value latents are stored directly.
 
 constexpr int kEncWaves = 4;
-
-// max / min over the 32 lanes of each half-wave
-__device__ __forceinline__ float half_max(float v) {
-    v = row_max(v);
-    return fmaxf(v, __shfl_xor(v, 16));
-}
-__device__ __forceinline__ float half_min(float v) { return -half_max(-v); }
 
 struct EncLane {
     int t, half;                // token in its group, which group of the pair
     bool is_new, is_old, complete, touched;
 };
 
-// Quantise / store channel c of this lane's latent (see the section comment).
-// ct = the channel's entry of the code table: bit of token 0, bits per
-// token, width, metadata word.
-__device__ __forceinline__ void encode_channel(const EncLane &e, int c, int r, bool fp16, const int4 ct, float lat,
-                                               const float *told, float *tnew, uint32_t *rec_lds, uint16_t *rec16,
-                                               bool any_complete) {
-    // fp16 latents have no tail buffer (told and tnew are null): only new
-    // positions are stored
-    if (fp16) {
-        if (e.is_new) rec16[c * 32 + e.t] = static_cast<uint16_t>(f2h_bits(lat));
-        return;
-    }
-    if (e.is_old) lat = told[e.t * r + c];
-    if (!any_complete) {                             // wave-uniform: no group completes
-        if (e.touched && e.is_new) tnew[e.t * r + c] = lat;
-        return;
-    }
-    // every lane takes part in the half-wave reductions; only complete
-    // groups use the result
-    const float mn = half_min(lat), mx = half_max(lat);
-    if (e.complete) {
-        const int bit = ct.x + e.t * ct.y;
-        const float levels = static_cast<float>((1 << ct.z) - 1);
-        const float scale = (mx - mn) / levels;
-        int q = 0;
-        if (scale > 0.0f) {
-            float uq = rintf((lat - mn) / scale);
-            uq = uq < 0.0f ? 0.0f : (uq > levels ? levels : uq);
-            q = static_cast<int>(uq);
-        }
-        // codes never straddle a word: a code of width w sits at a multiple of w
-        if (q) atomicOr(rec_lds + (bit >> 5), static_cast<uint32_t>(q) << (bit & 31));
-        if (e.t == 0) rec_lds[ct.w] = f2h_bits(scale) | (f2h_bits(mn) << 16);
-    } else if (e.touched && e.is_new) {
-        tnew[e.t * r + c] = lat;
-    }
+
+// Constant-address-space view of a basis or mean: uniform loads from it are
+// scalar loads, and the values are SGPR operands of the fmas.
+typedef const float __attribute__((address_space(4))) ConstF;
+
+// float(h) - mu for the low (HI = false) or high fp16 half of a word: the
+// mixed-precision fma h * 1 - mu, exact product and one rounding, equal to
+// the fp32 subtraction.
+template <bool HI>
+__device__ __forceinline__ float centred_f16(uint32_t w, float mu) {
+    float y;
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(y) : "v"(w), "s"(mu));
+    else
+        asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(y) : "v"(w), "s"(mu));
+    return y;
+}
+
+// The value of lane 15 of the previous 16-lane row, in rows 1 and 3 (rows 0
+// and 2 keep their own): after a row reduction, lanes 31 and 63 combine it
+// into the reduction over their 32-lane half.
+__device__ __forceinline__ float from_prev_row(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                                 0x142, 0xA, 0xF, false));
 }
 
 // W consecutive channels of this lane's latent: W independent fixed-order
-// chains over d = 0..D-1, run in four quarters of 32 rows so that only 32
-// values y_d = float(x_d) - mu_d are live at a time.  vch is the channel
-// chunk's basis in LDS, [D][RW] with RW = W rounded up to 4 (a compile-time
-// stride, so every row is an immediate offset); rows are read as 16-byte
-// broadcasts (8- and 4-byte ones for the last W % 4 channels).
-template <int W, bool BF16>
-__device__ __forceinline__ void project_to_lds(const uint16_t *xrow, const float *msh, const float *vch, float *lat,
-                                               int lane) {
-    constexpr int RW = (W + 3) & ~3;
+// chains over d = 0..D-1, run in steps of QD rows (32, or 16 for more than 16
+// chains) so that only QD values y_d are live at a time.  vb points at the
+// chunk's first channel in the [D][r] basis.  RS = r when it is known at
+// compile time (the chunk is the whole row and W = r: constant offsets);
+// RS = 0 strides the rows by the runtime r, and W may exceed the chunk's
+// channels by up to 3: those chains read the next row's first values (or,
+// after the last row, the basis region's slack) and are not used.
+template <int W, int RS, bool BF16>
+__device__ __forceinline__ void project_chunk(const uint16_t *xrow, ConstF *mu, ConstF *vb, int r, float *lat,
+                                              int lane) {
+    constexpr int QD = W > 16 ? 16 : 32, NX = QD / 8;   // rows per step, 16-byte input pieces per step
+    const int rs = RS ? RS : r;
     float l[W];
 #pragma unroll
     for (int k = 0; k < W; ++k) l[k] = 0.0f;
-    // the next quarter's 64 bytes are loaded while this one is computed
-    uint4 xa[4];
+    // the next step's input is loaded while this one is computed
+    uint4 xa[NX];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) xa[k] = *reinterpret_cast<const uint4 *>(xrow + 8 * k);
-    for (int q = 0; q < kHeadDim / 32; ++q) {
-        uint4 xb[4];
-        const int qn = q + 1 < kHeadDim / 32 ? q + 1 : q;
+    for (int k = 0; k < NX; ++k) xa[k] = *reinterpret_cast<const uint4 *>(xrow + 8 * k);
+#pragma unroll (W > 16 ? 2 : kHeadDim / QD)
+    for (int q = 0; q < kHeadDim / QD; ++q) {
+        uint4 xb[NX];
+        const int qn = q + 1 < kHeadDim / QD ? q + 1 : q;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) xb[k] = *reinterpret_cast<const uint4 *>(xrow + 32 * qn + 8 * k);
-        float y[32];
+        for (int k = 0; k < NX; ++k) xb[k] = *reinterpret_cast<const uint4 *>(xrow + QD * qn + 8 * k);
+        float y[QD];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < NX; ++k) {
             const uint32_t wq[4] = {xa[k].x, xa[k].y, xa[k].z, xa[k].w};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                y[8 * k + 2 * m] = in2f<BF16>(wq[m]) - msh[32 * q + 8 * k + 2 * m];
-                y[8 * k + 2 * m + 1] = in2f_hi<BF16>(wq[m]) - msh[32 * q + 8 * k + 2 * m + 1];
+                const int d = QD * q + 8 * k + 2 * m;
+                if constexpr (BF16) {
+                    y[8 * k + 2 * m] = in2f<true>(wq[m]) - mu[d];
+                    y[8 * k + 2 * m + 1] = in2f_hi<true>(wq[m]) - mu[d + 1];
+                } else {
+                    y[8 * k + 2 * m] = centred_f16<false>(wq[m], mu[d]);
+                    y[8 * k + 2 * m + 1] = centred_f16<true>(wq[m], mu[d + 1]);
+                }
             }
         }
+        // a runtime stride is re-read per step (opaque to the compiler), so
+        // the row offsets are formed here rather than hoisted out of every
+        // width's code into the kernel's prologue
+        int rsq = rs;
+        if constexpr (RS == 0) asm volatile("" : "+s"(rsq));
+        ConstF *vq = vb + QD * q * rsq;
 #pragma unroll
-        for (int dd = 0; dd < 32; ++dd) {
-            const float *vrow = vch + (32 * q + dd) * RW;
+        for (int dd = 0; dd < QD; ++dd) {
+            ConstF *vrow = vq + dd * rsq;
 #pragma unroll
-            for (int k = 0; k + 4 <= W; k += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(vrow + k);
-                l[k] = __builtin_fmaf(y[dd], v.x, l[k]);
-                l[k + 1] = __builtin_fmaf(y[dd], v.y, l[k + 1]);
-                l[k + 2] = __builtin_fmaf(y[dd], v.z, l[k + 2]);
-                l[k + 3] = __builtin_fmaf(y[dd], v.w, l[k + 3]);
-            }
-            constexpr int k2 = W & ~3;
-            if constexpr ((W & 3) >= 2) {
-                const float2 v = *reinterpret_cast<const float2 *>(vrow + k2);
-                l[k2] = __builtin_fmaf(y[dd], v.x, l[k2]);
-                l[k2 + 1] = __builtin_fmaf(y[dd], v.y, l[k2 + 1]);
-            }
-            if constexpr (W & 1) l[W - 1] = __builtin_fmaf(y[dd], vrow[W - 1], l[W - 1]);
+            for (int k = 0; k < W; ++k) l[k] = __builtin_fmaf(y[dd], vrow[k], l[k]);
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) xa[k] = xb[k];
+        for (int k = 0; k < NX; ++k) xa[k] = xb[k];
     }
 #pragma unroll
     for (int k = 0; k < W; ++k) lat[k * 64 + lane] = l[k];
 }
 
-// Dynamic LDS of one encode workgroup: basis (chunks of 32 channels, each
-// [D][32] except the last, [D][nc rounded up to 4]: D rp floats in all) +
-// mean [D] + per wave two record buffers (none for fp16 latents) and a
-// [channels][64 lanes] latent buffer (rows for the widest chunk: r rounded
-// up to 4, at most 32), then the code table (one int4 per channel).
-__host__ __device__ inline int encode_rec_words(int words, bool fp16) { return fp16 ? 0 : words; }
+// Dynamic LDS of one encode workgroup, per wave: the quantiser's 64 (group,
+// channel) entries (float4; none for fp16 latents), two record buffers
+// (words rounded up to even; none for fp16 latents) and a [channels][64
+// lanes] latent buffer (rows for the widest chunk: r rounded up to 4, at most
+// 32); then the code table (one int4 per channel).  Every part starts on a
+// 16-byte boundary.
+__host__ __device__ inline int encode_rec_words(int words, bool fp16) { return fp16 ? 0 : (words + 1) & ~1; }
 __host__ __device__ inline int encode_lat_rows(int r) { return ((r + 3) & ~3) < 32 ? ((r + 3) & ~3) : 32; }
+__host__ __device__ inline int encode_sc_floats(bool fp16) { return fp16 ? 0 : 256; }
 __host__ __device__ inline int encode_lds_bytes(int r, int words, bool fp16) {
-    const int rp = (r + 3) & ~3;
-    return (kHeadDim * rp + kHeadDim + kEncWaves * (2 * encode_rec_words(words, fp16) + encode_lat_rows(r) * 64) +
+    return (kEncWaves * (encode_sc_floats(fp16) + 2 * encode_rec_words(words, fp16) + encode_lat_rows(r) * 64) +
             4 * r) * 4;
 }
 
-// Five waves per SIMD (at most 96 VGPRs; the latent buffer is sized by the
-// rank so that LDS admits five workgroups per CU at ranks up to 16): the
-// projection's LDS broadcast reads and the quantiser's reductions are latency
-// chains that the extra wave hides.
+// Five waves per SIMD (at most 96 VGPRs): the quantiser's reductions and the
+// scalar-load waits of the projection are latency chains that the extra
+// waves hide.
 template <bool BF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void encode_kernel(EncodeArgs a) {
     extern __shared__ __align__(16) float esh[];
@@ -345,38 +340,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
     const int j0 = o >> 5, jl = (o + n - 1) >> 5;
     if (2 * ((j0 >> 1) + blockIdx.x * kEncWaves) > jl) return;   // whole workgroup
     const TensorDev &T = tz ? a.t[1] : a.t[0];
-    const int r = T.r, rp = (r + 3) & ~3, W = T.words;
+    const int r = T.r, W = T.words;
     const int grp = h / a.hpg, slot = a.slot[bi];
+    const bool fp16 = T.fp16_latents;
+    const int SC = encode_sc_floats(fp16), WR = encode_rec_words(W, fp16), LR = encode_lat_rows(r);
 
-    // 0. the group's basis in 32-channel chunks (chunk j = channels 32 j ..,
-    //    [D][32], the last [D][rwl], rwl = its channels rounded up to 4,
-    //    zero-padded) and mean -> LDS
-    float *vsh = esh;
-    float *msh = esh + kHeadDim * rp;
-    {
-        const float *vb = T.basis + slot * T.set_basis + static_cast<int64_t>(grp) * kHeadDim * r;
-        const int cl = (r - 1) & ~31;                 // first channel of the last chunk
-        const int rwl = rp - cl, full = kHeadDim * cl;
-        for (int e = tid; e < kHeadDim * rp; e += 256) {
-            int d, c;
-            if (e < full) {
-                d = (e & 4095) >> 5;
-                c = ((e >> 12) << 5) + (e & 31);
-            } else {
-                d = (e - full) / rwl;
-                c = cl + (e - full) - d * rwl;
-            }
-            vsh[e] = c < r ? vb[d * r + c] : 0.0f;
-        }
-        if (tid < kHeadDim) msh[tid] = T.mu[slot * T.set_mu + grp * kHeadDim + tid];
-    }
     // code table: per channel the record bit of token 0, the bits between
     // consecutive tokens, the width and the metadata word (read as one
     // broadcast per channel instead of a walk over the segment list)
-    const int WR = encode_rec_words(W, T.fp16_latents);
-    const int LR = encode_lat_rows(r);
-    int4 *ctab = reinterpret_cast<int4 *>(msh + kHeadDim + kEncWaves * (2 * WR + LR * 64));
-    if (tid < r && !T.fp16_latents) {
+    int4 *ctab = reinterpret_cast<int4 *>(esh + kEncWaves * (SC + 2 * WR + LR * 64));
+    if (tid < r && !fp16) {
         const int2 b0 = code_bit(T.cd, tz, tid, 0), b1 = code_bit(T.cd, tz, tid, 1);
         ctab[tid] = make_int4(b0.x, b1.x - b0.x, b0.y, T.cd.meta0 + tid);
     }
@@ -394,12 +367,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
     e.touched = j >= j0 && j <= jl;
     e.complete = e.touched && o + n >= 32 * j + 32;
     // complete groups that get a quantised record (fp16 latents have none)
-    const bool fp16 = T.fp16_latents;
     const bool any_complete = !fp16 && __any(e.complete);
+    const bool any_old = !fp16 && __any(e.is_old);
     const int64_t head_base = static_cast<int64_t>(slot) * a.H + h;
 
-    uint32_t *rec_lds = reinterpret_cast<uint32_t *>(msh + kHeadDim) + (wv * 2 + e.half) * WR;
-    float *lat = msh + kHeadDim + kEncWaves * 2 * WR + wv * LR * 64;   // this wave's [LR][64]
+    float4 *sc = reinterpret_cast<float4 *>(esh) + wv * (SC / 4);                     // [2 halves][32 channels]
+    uint32_t *rec_lds = reinterpret_cast<uint32_t *>(esh + kEncWaves * SC) + (wv * 2 + e.half) * WR;
+    float *lat = esh + kEncWaves * (SC + 2 * WR) + wv * LR * 64;                       // this wave's [LR][64]
     if (any_complete) {
         for (int w = e.t; w < W; w += 32) rec_lds[w] = 0u;
     }
@@ -409,41 +383,122 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
     const int row = e.is_new ? p - o : 0;
     const uint16_t *xrow = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim +
                            static_cast<int64_t>(row) * kHeadDim;
+    ConstF *mu = (ConstF *)(T.mu + slot * T.set_mu + grp * kHeadDim);   // address-space cast
+    ConstF *vbase = (ConstF *)(T.basis + slot * T.set_basis + static_cast<int64_t>(grp) * kHeadDim * r);
 
     // 2. latents in chunks of up to 32 channels (one fma chain per channel),
     //    parked in LDS, then quantised / stored channel by channel
-    const float *told = T.fp16_latents ? nullptr : T.tail + (head_base * 2 + a.sel_old[bi]) * 32 * r;
-    float *tnew = T.fp16_latents ? nullptr : T.tail + (head_base * 2 + a.sel_new[bi]) * 32 * r;
+    const float *told = fp16 ? nullptr : T.tail + (head_base * 2 + a.sel_old[bi]) * 32 * r;
+    float *tnew = fp16 ? nullptr : T.tail + (head_base * 2 + a.sel_new[bi]) * 32 * r;
     uint16_t *rec16 = reinterpret_cast<uint16_t *>(T.records + head_base * T.head_stride +
                                                    static_cast<int64_t>(j) * W);
     for (int c0 = 0; c0 < r; c0 += 32) {
         const int nc = r - c0 < 32 ? r - c0 : 32;
-        // exactly nc chains up to 16 channels, a multiple of 4 above
-        switch (nc <= 16 ? nc : 16 + ((nc - 13) >> 2)) {
-            case 1: project_to_lds<1, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 2: project_to_lds<2, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 3: project_to_lds<3, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 4: project_to_lds<4, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 5: project_to_lds<5, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 6: project_to_lds<6, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 7: project_to_lds<7, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 8: project_to_lds<8, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 9: project_to_lds<9, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 10: project_to_lds<10, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 11: project_to_lds<11, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 12: project_to_lds<12, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 13: project_to_lds<13, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 14: project_to_lds<14, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 15: project_to_lds<15, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 16: project_to_lds<16, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 17: project_to_lds<20, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 18: project_to_lds<24, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            case 19: project_to_lds<28, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
-            default: project_to_lds<32, BF16>(xrow, msh, vsh + kHeadDim * c0, lat, lane); break;
+        ConstF *vb = vbase + c0;
+        if (nc == r && (nc <= 16 || (nc & 3) == 0)) {
+            // the whole row in one chunk of a compiled width
+            switch (nc <= 16 ? nc : 12 + (nc >> 2)) {
+                case 1: project_chunk<1, 1, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 2: project_chunk<2, 2, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 3: project_chunk<3, 3, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 4: project_chunk<4, 4, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 5: project_chunk<5, 5, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 6: project_chunk<6, 6, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 7: project_chunk<7, 7, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 8: project_chunk<8, 8, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 9: project_chunk<9, 9, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 10: project_chunk<10, 10, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 11: project_chunk<11, 11, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 12: project_chunk<12, 12, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 13: project_chunk<13, 13, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 14: project_chunk<14, 14, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 15: project_chunk<15, 15, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 16: project_chunk<16, 16, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 17: project_chunk<20, 20, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 18: project_chunk<24, 24, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 19: project_chunk<28, 28, BF16>(xrow, mu, vb, r, lat, lane); break;
+                default: project_chunk<32, 32, BF16>(xrow, mu, vb, r, lat, lane); break;
+            }
+        } else {
+            // other chunks: runtime row stride, width rounded up to 4
+            switch ((nc + 3) >> 2) {
+                case 1: project_chunk<4, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 2: project_chunk<8, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 3: project_chunk<12, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 4: project_chunk<16, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 5: project_chunk<20, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 6: project_chunk<24, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                case 7: project_chunk<28, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                default: project_chunk<32, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+            }
         }
-        for (int k = 0; k < nc; ++k)
-            encode_channel(e, c0 + k, r, fp16, fp16 ? make_int4(0, 0, 0, 0) : ctab[c0 + k], lat[k * 64 + lane], told,
-                           tnew, rec_lds, rec16, any_complete);
+        if (fp16) {
+            // fp16 latents: only new positions are stored
+            if (e.is_new)
+                for (int k = 0; k < nc; ++k) rec16[(c0 + k) * 32 + e.t] = static_cast<uint16_t>(f2h_bits(lat[k * 64 + lane]));
+            continue;
+        }
+        // pass 1: each channel's value (old positions from the tail buffer),
+        // new latents of an incomplete group to the tail, and per half the
+        // minimum and maximum (lanes 31 and 63 record them)
+        if (any_old) {
+            // old positions of the first group: their latents from the tail
+            // buffer, into the latent buffer
+            for (int k = 0; k < nc; ++k)
+                if (e.is_old) lat[k * 64 + lane] = told[e.t * r + c0 + k];
+        }
+        for (int k = 0; k < nc; ++k) {
+            const int c = c0 + k;
+            const float v = lat[k * 64 + lane];
+            if (!e.complete && e.touched && e.is_new) tnew[e.t * r + c] = v;
+            if (any_complete) {                      // wave-uniform
+                float mx = row_max(v), mn = -row_max(-v);
+                mx = fmaxf(mx, from_prev_row(mx));
+                mn = fminf(mn, from_prev_row(mn));
+                if (e.t == 31) *reinterpret_cast<float2 *>(sc + e.half * 32 + k) = make_float2(mn, mx);
+            }
+        }
+        if (!any_complete) continue;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // pass 2: lane (half, k) takes its group's channel c0 + k: scale by
+        // IEEE division, the reciprocal (normal scales only; 0 makes every
+        // code of the channel a division) and the metadata word
+        {
+            const int k = lane & 31;
+            if (k < nc && e.complete) {
+                const int c = c0 + k;
+                const int4 ct = ctab[c];
+                const float2 mm = *reinterpret_cast<const float2 *>(sc + e.half * 32 + k);
+                const float levels = static_cast<float>((1 << ct.z) - 1);
+                const float scale = (mm.y - mm.x) / levels;
+                const float inv = scale >= 0x1p-126f && scale < 0x1p+126f ? __builtin_amdgcn_rcpf(scale) : 0.0f;
+                sc[e.half * 32 + k] = make_float4(mm.x, scale, inv, levels);
+                rec_lds[ct.w] = f2h_bits(scale) | (f2h_bits(mm.x) << 16);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // pass 3: codes of the complete groups
+        if (e.complete) {
+            for (int k = 0; k < nc; ++k) {
+                const float4 s = sc[e.half * 32 + k];
+                const int4 ct = ctab[c0 + k];
+                const float x = lat[k * 64 + lane] - s.x;
+                float uq = 0.0f;
+                if (s.y > 0.0f) {
+                    const float pq = x * s.z;
+                    const float f = __builtin_amdgcn_fractf(pq);
+                    uq = s.z == 0.0f || fabsf(f - 0.5f) <= 0x1p-11f ? rintf(x / s.y) : rintf(pq);
+                    uq = uq < 0.0f ? 0.0f : (uq > s.w ? s.w : uq);
+                }
+                const int bit = ct.x + static_cast<int>(__umul24(e.t, ct.y));
+                // codes never straddle a word: a code of width w sits at a multiple of w
+                atomicOr(rec_lds + (bit >> 5), static_cast<uint32_t>(static_cast<int>(uq)) << (bit & 31));
+            }
+        }
     }
 
     // 3. complete groups: LDS record -> memory
