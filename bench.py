@@ -49,10 +49,11 @@ HBM_PEAK_GBPS = 8000.0
 # Non-packed fp32 VALU issue rate of MI355X: 256 CUs x 4 SIMDs x 16 lanes x
 # 2.4 GHz (the published 157.3 TFLOP/s counts packed fp32 FMAs: x2 x2).
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# Lane operations a causal softmax pair needs at least on the vector unit:
-# one exp2, one running-max comparison and half of an fp32 -> fp16 pair
+# Vector issue slots a causal softmax pair needs at least, in lane
+# operations: one exp2 (a transcendental, issued at half the rate: two
+# slots), one running-max comparison and half of an fp32 -> fp16 pair
 # conversion (the two contractions run on the matrix cores).
-PREFILL_OPS_PER_PAIR = 2.5
+PREFILL_OPS_PER_PAIR = 3.5
 METRIC = "latent decode-attend tok/s + HBM GB/s (% of peak); encode Mtok/s"
 # Host threads of one job on the GPU machines (their CPU share per GPU).
 MAX_HOST_THREADS = 16
