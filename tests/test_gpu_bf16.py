@@ -29,7 +29,7 @@ def torch():
 
 def _bdev(torch, bits):
     """bf16 bit patterns (uint16) -> a bf16 CUDA tensor holding them."""
-    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    t = torch.from_numpy(np.array(bits, dtype=np.uint16).view(np.int16)).cuda()
     return t.view(torch.bfloat16)
 
 
@@ -83,16 +83,18 @@ def test_fit_matches_oracle(torch):
             np.testing.assert_allclose(mu[g], f.mu[g], atol=1e-5)
 
 
-@pytest.mark.parametrize("vq", [True, False])
-def test_encode_decode_prefill(torch, vq):
+# ranks 27 and 40 take the encode projection's runtime-stride chunks (a
+# width rounded up to 4; two chunks of 32 and 8 channels)
+@pytest.mark.parametrize("vq,rank", [(True, 16), (False, 16), (True, 27), (True, 40)])
+def test_encode_decode_prefill(torch, vq, rank):
     lens = np.array([45, 96, 7], np.int32)
     w = synth.small_workload(batch=3, n_q_heads=8, n_kv_heads=2, n_head_groups=1, prefill=96,
-                             rank=16, quantize_values=vq, seed=62)
+                             rank=rank, quantize_values=vq, seed=62)
     total = 100
     k = synth.batch_kv(w, 0, total, bf16=True)
     v = synth.batch_kv(w, 1, total, bf16=True)
-    fk = oracle.fit(k[:, :, :96], lens, 1, rank=16, tau=w.energy, bf16=True)
-    fv = oracle.fit(v[:, :, :96], lens, 1, rank=16, tau=w.energy, bf16=True)
+    fk = oracle.fit(k[:, :, :96], lens, 1, rank=rank, tau=w.energy, bf16=True)
+    fv = oracle.fit(v[:, :, :96], lens, 1, rank=rank, tau=w.energy, bf16=True)
     cache = _cache(w, total)
     cache.set_basis(0, fk.bases(), fk.mu)
     cache.set_basis(1, fv.bases(), fv.mu)
