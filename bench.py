@@ -219,6 +219,52 @@ def time_decode(torch, cache, q, out, stream, n, flush=None):
     return float(np.mean(ms)), float(np.median(ms))
 
 
+# Steps the cache holds room for after the timed passes: the eager and
+# graph-replayed decode steps of time_step_graph append one token each.
+GRAPH_STEPS = 48
+
+
+def time_step_graph(torch, cache, k_new, v_new, q, stream, n_eager=8, n_graph=8, n_replay=3):
+    """One decode step (palu_decode_step: one-token append per row, then
+    decode-attend) run eagerly, then n_graph steps captured in one HIP graph
+    (torch.cuda.graph over the library's launches on the capture stream) and
+    replayed n_replay times, and a one-step graph replayed n_replay times:
+    mean time per step between fence-free events.  Appends
+    n_eager + (n_graph + 1) n_replay tokens (within GRAPH_STEPS) and
+    resynchronises the host's lengths afterwards."""
+    out = torch.empty_like(q)
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(n_eager + 2 * n_replay)]
+
+    def timed(i, fn):
+        a, b = evs[i]
+        a.record(stream)
+        fn()
+        b.record(stream)
+        return a, b
+
+    eager = [timed(i, lambda: cache.decode_step(k_new, v_new, q, out)) for i in range(n_eager)]
+    torch.cuda.synchronize()
+    graphs = []
+    for n in (n_graph, 1):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                cache.decode_step(k_new, v_new, q, out)
+        torch.cuda.synchronize()
+        graphs.append(g)
+    multi = [timed(n_eager + i, graphs[0].replay) for i in range(n_replay)]
+    single = [timed(n_eager + n_replay + i, graphs[1].replay) for i in range(n_replay)]
+    torch.cuda.synchronize()
+    cache.sync_lengths()
+    del graphs
+    us = lambda pairs, n: float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3 / n
+    return {"eager_us": round(us(eager[1:], 1), 2), "graph_us": round(us(multi, n_graph), 2),
+            "graph_steps": n_graph, "one_step_graph_us": round(us(single, 1), 2),
+            "note": "per step: one-token append of every sequence + decode-attend (palu_decode_step): "
+                    "launched eagerly; as one captured graph of graph_steps steps (time per step); as a "
+                    "captured graph of one step (time per replay, which includes the graph launch)"}
+
+
 def gen_inputs(w, n_extra, bf16=False):
     """Host K/V of every sequence (prefill + n_extra positions), generated on
     host threads: two lists of fp16 [H, len + n_extra, D] arrays."""
@@ -355,7 +401,7 @@ def main():
     gen_s = time.time() - t0
 
     cache = LatentKVCache(w.head_dim, w.n_kv_heads, w.n_q_heads, w.n_head_groups, w.batch,
-                          S + T, rank=args.per_seq_rank or w.rank or 0, energy_threshold=w.energy,
+                          S + T + GRAPH_STEPS, rank=args.per_seq_rank or w.rank or 0, energy_threshold=w.energy,
                           quantize_values=w.quantize_values, input_dtype=args.input_dtype,
                           bit_schedule=schedule, per_seq_basis=args.per_seq_rank > 0)
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=tdt, device=dev)
@@ -467,6 +513,8 @@ def main():
                               "energy_at_r_minus_1": [round(float(x), 6) for x in ep],
                               "margin": round(float(st["energy_margin_" + name]), 6)}
 
+    step_graph = time_step_graph(torch, cache, kdec[T - 1], vdec[T - 1], q_last, stream)
+
     workloads = {}
     if not variant and args.workloads != "none":
         names = list(synth.WORKLOADS) if args.workloads == "all" else args.workloads.split(",")
@@ -514,6 +562,7 @@ def main():
         "read_bandwidth": read_bw,
         "decode_attend_us": round(att_mean_ms * 1e3, 2),
         "append_us": round(float(np.mean(app_ms)) * 1e3, 2),
+        "decode_step_graph": step_graph,
         "encode_mtok_s": round(encode_mtok_s, 2),
         "encode_ms": round(enc_mean_ms, 4),
         "encode_roofline": {"bound": "hbm", "achieved": round(enc_gbps, 1), "peak": HBM_PEAK_GBPS,
