@@ -233,6 +233,49 @@ def test_slot_mapping_and_row_order(torch):
         _check_attention(out[row], layer.attend(ks, vs, q[row]), f"row {row} slot {sl}")
 
 
+def test_calls_beyond_one_launch_group(torch):
+    """A call holds at most 64 rows per launch: an encode of 70 slots (two
+    launch groups) and a decode call of 150 rows over those slots, some
+    repeated (three launch groups sharing the split partials, and the
+    allocation-free entry point's static partials), every output against
+    the oracle."""
+    n_slots, rows = 70, 150
+    w = synth.small_workload(batch=n_slots, n_q_heads=4, n_kv_heads=2, n_head_groups=1, prefill=70,
+                             steps=1, rank=10, seed=91)
+    rng = np.random.default_rng(91)
+    lens = rng.integers(1, 71, size=n_slots).astype(np.int32)
+    S = int(lens.max())
+    k_all = synth.batch_kv(w, 0, S)
+    v_all = synth.batch_kv(w, 1, S)
+    fk = oracle.fit(k_all, lens, 1, rank=10, tau=w.energy)
+    fv = oracle.fit(v_all, lens, 1, rank=10, tau=w.energy)
+    cache = _cache(torch, w, S, max_batch=n_slots)
+    cache.set_basis(0, fk.bases(), fk.mu)
+    cache.set_basis(1, fv.bases(), fv.mu)
+    layer = oracle.OracleLayer(w.head_dim, w.n_q_heads, w.n_kv_heads, 1, fk, fv)
+    cache.encode_append(_dev(torch, k_all), _dev(torch, v_all), n_new=lens)
+    torch.cuda.synchronize()
+    for sl in (0, 63, 64, 69):
+        assert cache.seq_len(sl) == lens[sl]
+        _compare_state(cache, layer, (k_all[sl, :, :lens[sl]], v_all[sl, :, :lens[sl]]), sl)
+    call = rng.integers(0, n_slots, size=rows).astype(np.int32)
+    q = np.stack([synth.queries(w, int(b), 1)[0] for b in range(rows)])   # [rows, Hq, D]
+    out = cache.decode_attend(_dev(torch, q), seq_ids=call).cpu().numpy()
+    out_na = torch.empty_like(_dev(torch, q))
+    cache.decode_attend_noalloc(_dev(torch, q), out_na, seq_ids=call)
+    out_na = out_na.cpu().numpy()
+    states = {}
+    for row, sl in enumerate(call):
+        sl = int(sl)
+        if sl not in states:
+            n = int(lens[sl])
+            states[sl] = ([layer.encode_head(k_all[sl, h, :n], h, 0) for h in range(w.n_kv_heads)],
+                          [layer.encode_head(v_all[sl, h, :n], h, 1) for h in range(w.n_kv_heads)])
+        ref = layer.attend(*states[sl], q[row])
+        _check_attention(out[row], ref, f"row {row} slot {sl}")
+        _check_attention(out_na[row], ref, f"allocation-free row {row} slot {sl}")
+
+
 def test_append_order_invariance(torch):
     w = synth.small_workload(batch=3, n_q_heads=4, n_kv_heads=2, n_head_groups=2, prefill=150,
                              steps=1, rank=12, seed=21)
