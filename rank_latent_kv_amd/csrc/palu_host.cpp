@@ -1058,6 +1058,16 @@ int decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_id
                 // workgroup per CU: the prologue and the merge of a split
                 // are then paid once per two passes
                 if (chunk < 2 * per_pass && units / (2 * per_pass) >= cus) chunk = 2 * per_pass;
+                // ragged rows round their last split up: grow the split by
+                // whole passes until the launch's exact workgroup count fits
+                // the target (no second, partial round of workgroups)
+                auto wg_count = [&](int64_t ch) {
+                    int64_t n = 0;
+                    for (int i = 0; i < nb; ++i)
+                        n += std::max<int64_t>(1, (aa.row[i].len / kTokGroup + ch - 1) / ch);
+                    return n * c->H;
+                };
+                while (wg_count(chunk) > kAttendTargetGroups && chunk < max_full) chunk += per_pass;
             }
         }
         chunk = std::max<int64_t>(chunk, (max_full + kMaxSplits - 1) / kMaxSplits);
