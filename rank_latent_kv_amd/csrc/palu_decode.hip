@@ -104,8 +104,11 @@ __host__ __device__ inline AttendLds attend_lds(int g, int nbk, int rk, int rv, 
 // processed in passes of up to 4 S token groups (S per wave); the records of
 // pass p + 1 are copied global -> LDS (direct 16-byte loads into LDS, no
 // registers) into the other of two buffers while pass p is computed.
+// The fast variants with up to two value blocks are held to 128 VGPRs (four
+// waves per SIMD); the widest of them would otherwise take 129.
 template <int G, int NBV, bool VQ, bool GEN, int NBKF>
-__global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NBKF > 0 && NBV <= 2 ? 4 : 1)))
+void attend_kernel(AttendArgs a) {
     constexpr int g = G, S = 16 / G, NS = S * G;
     constexpr bool vq = VQ;                      // V stored as mixed-bit codes
     extern __shared__ __align__(16) unsigned char lds[];
@@ -168,7 +171,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     float *qt = reinterpret_cast<float *>(lds + L.qt);
     uint4 *qt16 = reinterpret_cast<uint4 *>(lds + L.qt16);
     _Float16 *qt16h = reinterpret_cast<_Float16 *>(lds + L.qt16);
-    uint32_t *kpw = reinterpret_cast<uint32_t *>(lds + L.kpw) + wv * (S * nbk * 8);   // this wave's
     // stage buffer tb holds the tail latents (the one the last pass leaves
     // free); after the main loop the other one holds the merge state
     const int tb = npass & 1;
@@ -195,7 +197,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         koff = static_cast<int>(g0 * WK - ka);
         voff = 4 * nk4 + static_cast<int>(g0 * WV - va);
     };
-    auto copy_pass = [&](int p) {
+    // (dst = the LDS base the copies write through)
+    auto copy_pass = [&](unsigned char *dst, int p) {
         int nk4, nv4, koff, voff;
         pass_words(p, nk4, nv4, koff, voff);
         const int64_t g0 = jb + p * PP;
@@ -205,13 +208,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         for (int c = wv; c * 64 < n4; c += kWaves) {
             const int e = c * 64 + lane;
             if (e < n4)
-                __builtin_amdgcn_global_load_lds(e < nk4 ? ks + e : vs + (e - nk4), lds + boff + c * 1024, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(e < nk4 ? ks + e : vs + (e - nk4), dst + boff + c * 1024, 16, 0, 0);
         }
     };
     const int64_t tsel = (hb * 2 + tsl) * kTokGroup;
     const int tk_words = do_tail ? min((ntail * rk + 3) & ~3, kTokGroup * rk) : 0;
     const int tv_words = do_tail ? (vq ? min((ntail * rv + 3) & ~3, kTokGroup * rv) : 16 * rv) : 0;
-    auto copy_tail = [&]() {
+    auto copy_tail = [&](unsigned char *dst) {
         const u4v *tks = reinterpret_cast<const u4v *>(a.k.tail + tsel * rk);
         const u4v *tvs = vq ? reinterpret_cast<const u4v *>(a.v.tail + tsel * rv)
                             : reinterpret_cast<const u4v *>(vg + static_cast<int64_t>(nfull) * WV);
@@ -219,12 +222,24 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         for (int c = wv; c * 64 < n4; c += kWaves) {
             const int e = c * 64 + lane;
             if (e < n4)
-                __builtin_amdgcn_global_load_lds(e < ntk4 ? tks + e : tvs + (e - ntk4), lds + tail_off + c * 1024, 16,
+                __builtin_amdgcn_global_load_lds(e < ntk4 ? tks + e : tvs + (e - ntk4), dst + tail_off + c * 1024, 16,
                                                  0, 0);
         }
     };
-    if (npass > 0) copy_pass(0);
-    else if (do_tail) copy_tail();
+    // With fp16 value latents, what the first pass would copy while it runs
+    // (the second pass's records, or the tail latents when there is one
+    // pass) goes out now too: the second buffer is free, and the first pass
+    // then waits only on its value loads (fp16-value batch 29.9 -> 29.0 us
+    // per call).  With quantised values it stays in the first pass: issuing
+    // it here left the memory pipe idle during that pass and measured
+    // slower on many-pass splits (serving batch 51.5 -> 53.0 us).
+    constexpr bool kEarly = !VQ;
+    if (npass > 0) copy_pass(lds, 0);
+    else if (do_tail) copy_tail(lds);
+    if (kEarly) {
+        if (npass > 1) copy_pass(lds, 1);
+        else if (npass == 1 && do_tail) copy_tail(lds);
+    }
 
     // ---- 2. absorbed query qt = qs V_K^T q on MFMA: rows = query heads of
     //         this kv head, K = d, columns = 16 score-operand positions of
@@ -364,7 +379,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     }
     // the score operand B of the first two score steps (the same in every
     // pass), held in registers when there are at most two steps
-    auto score_b = [&](int u) -> uint4 {
+    auto score_b = [&](const uint4 *q16, int u) -> uint4 {
         const int p = 4 * u + kb;
         int q, j;
         if constexpr (S % 4 == 0) {
@@ -376,7 +391,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         }
         const int qc = q < nbk ? q : nbk - 1;
         const bool ok = p < npair && live_n && j == slot_n;
-        return ok ? qt16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
+        return ok ? q16[head_n * nbk + qc] : make_uint4(0u, 0u, 0u, 0u);
     };
     uint4 bq_pre[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
     // Fast path: 4 query heads per kv head (S = 4), PALU layout, quantised
@@ -406,7 +421,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
             const int t0 = 8 * (ln >> 2) + (ln & 3);
 #pragma unroll
             for (int u = 0; u < NF; ++u) {
-                bqf[u] = score_b(u);
+                bqf[u] = score_b(qt16, u);
                 const bool w4 = u == 0;
                 const int base = w4 ? 32 * u : 128 * nhk + 16 * (u - nbh);
                 const int stride = w4 ? 4 * nhk : 2 * nlk;
@@ -427,18 +442,57 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     }
     if constexpr (!fast) {
         if (nub <= 2) {
-            bq_pre[0] = score_b(0);
-            if (nub == 2) bq_pre[1] = score_b(1);
+            bq_pre[0] = score_b(qt16, 0);
+            if (nub == 2) bq_pre[1] = score_b(qt16, 1);
         }
     }
-    for (int pi = 0; pi < npass; ++pi) {
-        if (pi + 1 < npass) copy_pass(pi + 1);       // into the other buffer
-        else if (do_tail) copy_tail();               // the last pass leaves buffer tb free
-        int nk4, nv4, koff, voff;
-        pass_words(pi, nk4, nv4, koff, voff);
+    // One pass.  Every LDS access in it goes through lw, and the copies of
+    // the next pass through ldma; both are restrict-qualified and both are
+    // the LDS base.  As distinct values (fp16 value latents) they tell the
+    // compiler that the copies in flight write nothing the pass reads, and
+    // it no longer waits for those copies at the pass's first LDS read (nor,
+    // counters being in order, at the value loads issued before them).  As
+    // one value (quantised values) the qualification is dropped and the
+    // first LDS read waits for the copies: letting them overlap the pass
+    // measured 1% slower on the long-context shape there.  Either way the
+    // copies land before the barrier that ends the pass (explicit wait).
+    // (everything else by value: capturing all by reference cost 2 to 4
+    // VGPRs in most variants)
+    using LdsPtr = std::conditional_t<VQ, unsigned char *, unsigned char *__restrict__>;
+    auto run_pass = [=, &oacc, &m_run, &l_run](int pi, LdsPtr lw, LdsPtr ldma) mutable {
+        uint32_t *kpw = reinterpret_cast<uint32_t *>(lw + L.kpw) + wv * (S * nbk * 8);
+        const uint4 *qt16 = reinterpret_cast<const uint4 *>(lw + L.qt16);
+        const int4 *blk = reinterpret_cast<const int4 *>(lw + L.blk);
         const int npg = min(PP, ntg - pi * PP);      // groups in this pass (>= 1)
         const int64_t g0 = jb + pi * PP;             // absolute group of pass group 0
-        const uint32_t *stage = reinterpret_cast<const uint32_t *>(lds + L.stage) + (pi & 1) * L.sb;
+        // fp16 value latents are read from memory straight into the value
+        // operands.  With at most 16 (slot, block) pairs all of a pass's
+        // loads are issued here, before the next pass's copies, so that they
+        // are in flight while the scores are computed and the wait for them
+        // does not also wait for those copies; otherwise each slot's loads
+        // are issued right before its MFMAs.  Slots past the pass read the
+        // last group (never used).
+        constexpr bool kPreV = !VQ && S * NBV <= 16;
+        uint2 vlo[kPreV ? S : 1][NBV], vhi[kPreV ? S : 1][NBV];
+        if constexpr (kPreV) {
+#pragma unroll
+            for (int m = 0; m < S; ++m) {
+                const int tg = tb0 + m < npg ? tb0 + m : npg - 1;
+#pragma unroll
+                for (int nb = 0; nb < NBV; ++nb) {
+                    const uint16_t *r16 = reinterpret_cast<const uint16_t *>(vg + (g0 + tg) * WV) + vch[nb] * 32;
+                    vlo[m][nb] = *reinterpret_cast<const uint2 *>(r16 + 4 * kb);
+                    vhi[m][nb] = *reinterpret_cast<const uint2 *>(r16 + 16 + 4 * kb);
+                }
+            }
+        }
+        if (pi > 0 || !kEarly) {                      // (else pass 0's went out with the first)
+            if (pi + 1 < npass) copy_pass(ldma, pi + 1);  // into the other buffer
+            else if (do_tail) copy_tail(ldma);            // the last pass leaves buffer tb free
+        }
+        int nk4, nv4, koff, voff;
+        pass_words(pi, nk4, nv4, koff, voff);
+        const uint32_t *stage = reinterpret_cast<const uint32_t *>(lw + L.stage) + (pi & 1) * L.sb;
 
         // (a) this wave's K scale/zero pairs per (slot, channel block):
         //     words 0..3 scale pairs (k, k + 4), words 4..7 zero pairs;
@@ -578,7 +632,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
                 score_step(0, bq_pre[0]);
                 if (nub == 2) score_step(1, bq_pre[1]);
             } else {
-                for (int u = 0; u < nub; ++u) score_step(u, score_b(u));
+                for (int u = 0; u < nub; ++u) score_step(u, score_b(qt16, u));
             }
         }
 
@@ -622,29 +676,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         //     the epilogue: sum_t p (code s + z) = s (D - 1024 P) + z P, with
         //     the weight sum P = sum_t p of each stream from one more MFMA
         //     against a constant-one operand (so it sums exactly the fp16
-        //     weights used).  fp16 value latents are read from memory, all
-        //     slots' loads issued before the first MFMA.
+        //     weights used).  fp16 value latents come from registers
+        //     loaded at the start of the pass, or from memory per slot.
         f4 dacc[NBV];
 #pragma unroll
         for (int nb = 0; nb < NBV; ++nb) dacc[nb] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
         f4 dP = {0.0f, 0.0f, 0.0f, 0.0f};
         const f16x8 ones8 = as_h8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-        // fp16 value latents: with few (slot, block) pairs all loads are
-        // issued up front, else each slot's loads right before its MFMAs
-        constexpr bool kPreV = !VQ && S * NBV <= 8;
-        uint2 vlo[kPreV ? S : 1][NBV], vhi[kPreV ? S : 1][NBV];
-        if constexpr (kPreV) {
-#pragma unroll
-            for (int m = 0; m < S; ++m) {
-                const int tg = tb0 + m < npg ? tb0 + m : npg - 1;
-#pragma unroll
-                for (int nb = 0; nb < NBV; ++nb) {
-                    const uint16_t *r16 = reinterpret_cast<const uint16_t *>(vg + (g0 + tg) * WV) + vch[nb] * 32;
-                    vlo[m][nb] = *reinterpret_cast<const uint2 *>(r16 + 4 * kb);
-                    vhi[m][nb] = *reinterpret_cast<const uint2 *>(r16 + 16 + 4 * kb);
-                }
-            }
-        }
 #pragma unroll
         for (int m = 0; m < S; ++m) {
             if (tb0 + m >= npg) break;               // wave-uniform
@@ -739,7 +777,14 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         }
         __builtin_amdgcn_s_waitcnt(0);                // the next pass's copies have landed
         __syncthreads();                              // and every wave is done with this buffer
+    };
+    // two opaque zero offsets make the bases distinct values
+    int lz0 = 0, lz1 = 0;
+    if constexpr (!VQ) {
+        asm volatile("" : "+s"(lz0));
+        asm volatile("" : "+s"(lz1));
     }
+    for (int pi = 0; pi < npass; ++pi) run_pass(pi, lds + lz0, lds + lz1);
 
     // A wave past its main loop takes a higher issue priority (within the
     // kernel, s_setprio): workgroups that are merging finish sooner and free
