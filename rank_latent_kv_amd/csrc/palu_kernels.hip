@@ -542,6 +542,23 @@ __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
     const int bi = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
     const int tz = blockIdx.y;
     const int slot = a.slot[bi];
+    const TensorDev &T = tz ? a.t[1] : a.t[0];
+    const int r = T.r, W = T.words;
+    const int grp = h / a.hpg;
+    // The loads that do not depend on the row's stored length go out with
+    // it, in one round trip: the token, the mean and this lane's basis row
+    // (channel lane; a second pass takes channels from 64 on).  Every
+    // address is valid whatever the length; an empty append discards them.
+    const uint16_t *xin = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim;
+    const uint32_t xp = reinterpret_cast<const uint32_t *>(xin)[lane];
+    const float2 mu = reinterpret_cast<const float2 *>(T.mu + slot * T.set_mu + grp * kHeadDim)[lane];
+    const float *bcm = T.basis_cm + slot * T.set_bcm + static_cast<int64_t>(grp) * r * kHeadDim;
+    float4 vb[kHeadDim / 4];
+    if (lane < r) {
+        const float4 *row = reinterpret_cast<const float4 *>(bcm + static_cast<int64_t>(lane) * kHeadDim);
+#pragma unroll
+        for (int d4 = 0; d4 < kHeadDim / 4; ++d4) vb[d4] = row[d4];
+    }
     int o, n, sel_old, sel_new;
     if (a.dev_len) {
         // one token per row at the stored length (nothing past the capacity)
@@ -559,9 +576,6 @@ __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
         }
     }
     if (n <= 0) return;                               // whole workgroup
-    const TensorDev &T = tz ? a.t[1] : a.t[0];
-    const int r = T.r, W = T.words;
-    const int grp = h / a.hpg;
     const int64_t head_base = static_cast<int64_t>(slot) * a.H + h;
     const int j = o >> 5, t = o & 31;                 // group and position of the new token
     const bool complete = t == 31 && !T.fp16_latents;
@@ -570,24 +584,21 @@ __global__ __launch_bounds__(kApp1Threads) void append1_kernel(EncodeArgs a) {
 
     // 1. y = float(x) - mu, two elements per lane, to LDS; the record copy
     //    is cleared when the group completes
-    const uint16_t *xin = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim;
-    const uint32_t xp = reinterpret_cast<const uint32_t *>(xin)[lane];
-    const float2 mu = reinterpret_cast<const float2 *>(T.mu + slot * T.set_mu + grp * kHeadDim)[lane];
     reinterpret_cast<float2 *>(ys)[lane] = make_float2(in2f<BF16>(xp & 0xFFFFu) - mu.x, in2f<BF16>(xp >> 16) - mu.y);
     if (complete)
         for (int w = lane; w < W; w += kApp1Threads) rec[w] = 0u;
     __syncthreads();
 
-    const float *bcm = T.basis_cm + slot * T.set_bcm + static_cast<int64_t>(grp) * r * kHeadDim;
     const float4 *ys4 = reinterpret_cast<const float4 *>(ys);
     const float *told = T.tail + (head_base * 2 + sel_old) * 32 * r;
     for (int c = lane; c < r; c += kApp1Threads) {
         // 2. the chain, with the channel's basis row in registers; when the
         //    group completes, its 31 older latents are loaded alongside
-        float4 vb[kHeadDim / 4];
-        const float4 *row = reinterpret_cast<const float4 *>(bcm + static_cast<int64_t>(c) * kHeadDim);
+        if (c != lane) {
+            const float4 *row = reinterpret_cast<const float4 *>(bcm + static_cast<int64_t>(c) * kHeadDim);
 #pragma unroll
-        for (int d4 = 0; d4 < kHeadDim / 4; ++d4) vb[d4] = row[d4];
+            for (int d4 = 0; d4 < kHeadDim / 4; ++d4) vb[d4] = row[d4];
+        }
         float lv[32];
         if (complete) {
 #pragma unroll
