@@ -497,6 +497,13 @@ void attend_kernel(AttendArgs a) {
         // (a) this wave's K scale/zero pairs per (slot, channel block):
         //     words 0..3 scale pairs (k, k + 4), words 4..7 zero pairs;
         //     padding channels are 0; slots past the pass repeat its last group
+        // (with S a multiple of 4, only the slots of live score steps: the
+        // pass's slots rounded up to a multiple of 4)
+        int n_gather = S * nbk * 4;
+        if constexpr (S % 4 == 0) {
+            const int live = tb0 < npg ? min(S, (npg - tb0 + 3) & ~3) : 0;
+            n_gather = live * nbk * 4;
+        }
         if (kp_one) {
             if (lane < S * nbk * 4) {
                 int tg = tb0 + kp_m;
@@ -506,7 +513,7 @@ void attend_kernel(AttendArgs a) {
                 kpw[kp_dst] = perm_b32(wb, wa, 0x05040100u);
                 kpw[kp_dst + 4] = perm_b32(wb, wa, 0x07060302u);
             }
-        } else for (int e = lane; e < S * nbk * 4; e += 64) {
+        } else for (int e = lane; e < n_gather; e += 64) {
             const int m = div_nbk4.quo(e), r2 = e - m * nbk * 4;
             const int q = r2 >> 2, k = r2 & 3;
             int chan0, chanend;
@@ -628,11 +635,21 @@ void attend_kernel(AttendArgs a) {
                 }
             }
         } else {
+            // with S a multiple of 4, step u covers slots 4 (u % (S / 4)) ..
+            // + 3 of one key block; a step whose slots all lie past the pass
+            // only feeds masked streams and is skipped (one or two query heads
+            // per kv head on short passes: 4 of 16 steps when the pass has
+            // at most 4 groups)
+            auto step_live = [&](int u) {
+                if constexpr (S % 4 == 0) return tb0 + 4 * (u % (S / 4)) < npg;
+                else return true;
+            };
             if (nub <= 2) {
                 score_step(0, bq_pre[0]);
-                if (nub == 2) score_step(1, bq_pre[1]);
+                if (nub == 2 && step_live(1)) score_step(1, bq_pre[1]);
             } else {
-                for (int u = 0; u < nub; ++u) score_step(u, score_b(qt16, u));
+                for (int u = 0; u < nub; ++u)
+                    if (step_live(u)) score_step(u, score_b(qt16, u));   // wave-uniform
             }
         }
 
