@@ -838,9 +838,25 @@ void attend_kernel(AttendArgs a) {
         const bool ok = hh < g && t < ntail;
         float sc = -INFINITY;
         if (ok) {
-            float acc = 0.0f;
-            for (int c = 0; c < rk; ++c) acc = fmaf(qt[hh * rk + c], tk[t * rk + c], acc);
-            sc = acc;
+            // four independent chains; lane t starts at channel t mod rk and
+            // wraps, so the 32 lanes of a head read different LDS banks (the
+            // row stride of rk floats put them on one or two banks when rk
+            // is a multiple of 32)
+            const float *qrow = qt + hh * rk, *krow = tk + t * rk;
+            const int t0 = t - rk * (t / rk);
+            float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+            auto span = [&](int c, int ce) {
+                for (; c + 4 <= ce; c += 4) {
+                    a0 = fmaf(qrow[c], krow[c], a0);
+                    a1 = fmaf(qrow[c + 1], krow[c + 1], a1);
+                    a2 = fmaf(qrow[c + 2], krow[c + 2], a2);
+                    a3 = fmaf(qrow[c + 3], krow[c + 3], a3);
+                }
+                for (; c < ce; ++c) a0 = fmaf(qrow[c], krow[c], a0);
+            };
+            span(t0, rk);
+            span(0, t0);
+            sc = (a0 + a1) + (a2 + a3);
         }
         float mx = row_max(sc);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -857,15 +873,29 @@ void attend_kernel(AttendArgs a) {
         __syncthreads();
         for (int e = tid; e < g * rv; e += 256) {
             const int hv = div_rv.quo(e), c = e - hv * rv;
-            float acc = 0.0f;
+            const float *pw = tp + hv * 32;
+            float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;   // four independent chains
+            int t2 = 0;
             if (vq) {
-                const float *tv = reinterpret_cast<const float *>(tails + tk_words);
-                for (int t2 = 0; t2 < ntail; ++t2) acc = fmaf(tp[hv * 32 + t2], tv[t2 * rv + c], acc);
+                const float *tv = reinterpret_cast<const float *>(tails + tk_words) + c;
+                for (; t2 + 4 <= ntail; t2 += 4) {
+                    a0 = fmaf(pw[t2], tv[t2 * rv], a0);
+                    a1 = fmaf(pw[t2 + 1], tv[(t2 + 1) * rv], a1);
+                    a2 = fmaf(pw[t2 + 2], tv[(t2 + 2) * rv], a2);
+                    a3 = fmaf(pw[t2 + 3], tv[(t2 + 3) * rv], a3);
+                }
+                for (; t2 < ntail; ++t2) a0 = fmaf(pw[t2], tv[t2 * rv], a0);
             } else {
                 const _Float16 *tv = reinterpret_cast<const _Float16 *>(tails + tk_words) + c * 32;
-                for (int t2 = 0; t2 < ntail; ++t2) acc = fmaf(tp[hv * 32 + t2], static_cast<float>(tv[t2]), acc);
+                for (; t2 + 4 <= ntail; t2 += 4) {
+                    a0 = fmaf(pw[t2], static_cast<float>(tv[t2]), a0);
+                    a1 = fmaf(pw[t2 + 1], static_cast<float>(tv[t2 + 1]), a1);
+                    a2 = fmaf(pw[t2 + 2], static_cast<float>(tv[t2 + 2]), a2);
+                    a3 = fmaf(pw[t2 + 3], static_cast<float>(tv[t2 + 3]), a3);
+                }
+                for (; t2 < ntail; ++t2) a0 = fmaf(pw[t2], static_cast<float>(tv[t2]), a0);
             }
-            ost[(kWaves * 16 + hv) * rv + c] = acc;
+            ost[(kWaves * 16 + hv) * rv + c] = (a0 + a1) + (a2 + a3);
         }
     }
     __syncthreads();
