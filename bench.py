@@ -92,8 +92,9 @@ KERNEL_SRC = os.path.join(ROOT, "rank_latent_kv_amd", "csrc", "palu_decode.hip")
 PROFILE = os.path.join(ROOT, "profiles", "decode_attend_long_b4_s32768_e90.md")
 
 # GPU clock cycles of the spin queued ahead of the prefill encode's start
-# event (about 50 us)
-ENCODE_LEAD_CYCLES = 120_000
+# event (about 200 us: the host's launch path, about 30 us, now and then
+# took longer than a 50 us lead and the wait entered the encode's events)
+ENCODE_LEAD_CYCLES = 480_000
 
 
 def measured_traffic(workload):
