@@ -931,7 +931,8 @@ void attend_kernel(AttendArgs a) {
     __syncthreads();
     // weighted sum over the streams of every (head, channel) output: four
     // lanes of a quad per output, each over every fourth stream, then a quad
-    // reduction (one lane per output when there are more than 64 outputs)
+    // reduction (one lane per output with four independent chains when
+    // there are more than 64 outputs)
     auto stream_row = [&](int k, int hh) {
         return k < kWaves * S ? (k / S) * 16 + (k % S) * g + hh : kWaves * 16 + hh;
     };
@@ -950,10 +951,16 @@ void attend_kernel(AttendArgs a) {
         for (int e = tid; e < g * rv; e += 256) {
             const int hh = div_rv.quo(e), c = e - hh * rv;
             const float *wrow = wts + hh * 65;
-            float acc = 0.0f;
-#pragma unroll 4
-            for (int k = 0; k < nsw; ++k) acc = fmaf(wrow[k], ost[stream_row(k, hh) * rv + c], acc);
-            part[hh * head_stride + 2 + c] = acc;
+            float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+            int k = 0;
+            for (; k + 4 <= nsw; k += 4) {
+                a0 = fmaf(wrow[k], ost[stream_row(k, hh) * rv + c], a0);
+                a1 = fmaf(wrow[k + 1], ost[stream_row(k + 1, hh) * rv + c], a1);
+                a2 = fmaf(wrow[k + 2], ost[stream_row(k + 2, hh) * rv + c], a2);
+                a3 = fmaf(wrow[k + 3], ost[stream_row(k + 3, hh) * rv + c], a3);
+            }
+            for (; k < nsw; ++k) a0 = fmaf(wrow[k], ost[stream_row(k, hh) * rv + c], a0);
+            part[hh * head_stride + 2 + c] = (a0 + a1) + (a2 + a3);
         }
     }
 }
