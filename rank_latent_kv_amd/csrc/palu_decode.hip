@@ -1024,14 +1024,16 @@ __global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
         const float M = wave_max(m);
         const float w = live ? exp2f(m - M) : 0.0f;
         const float inv_l = 1.0f / wave_sum(w * ls);
+        // all 16 channel sums, unguarded: they are independent, so their
+        // DPP steps interleave (channels past r_V sum zeros and add 0 * 0)
+        float oc[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) oc[c] = wave_sum(w * oz[c]) * inv_l;
         float o0 = mu.x, o1 = mu.y;
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-            if (c < rv) {
-                const float oc = wave_sum(w * oz[c]) * inv_l;
-                o0 = fmaf(bz[c].x, oc, o0);
-                o1 = fmaf(bz[c].y, oc, o1);
-            }
+            o0 = fmaf(bz[c].x, oc[c], o0);
+            o1 = fmaf(bz[c].y, oc[c], o1);
         }
         reinterpret_cast<uint32_t *>(a.out + (static_cast<int64_t>(i) * a.Hq + qh) * kHeadDim)[lane] =
             out_bits(o0, a.bf16) | (out_bits(o1, a.bf16) << 16);
