@@ -200,6 +200,17 @@ def test_multi_iteration_splits(torch, gqa, rank, vq):
     _run_small(torch, w, lens=[n0, 32 * split + 5], split_groups=split)
 
 
+@pytest.mark.parametrize("gqa,split", [(1, 1), (1, 3), (1, 5), (1, 9), (2, 1), (2, 5), (2, 6)])
+def test_short_splits_small_gqa(torch, gqa, split):
+    # splits of a few groups with one or two query heads per kv head: the
+    # score steps and scale/zero gather rounds whose slots lie past such a
+    # short pass are skipped; lengths leave a partial last split and a tail
+    w = synth.small_workload(batch=2, n_q_heads=2 * gqa, n_kv_heads=2, n_head_groups=1,
+                             prefill=32 * (3 * split + 1) + 11, steps=2, rank=20,
+                             seed=500 + 10 * gqa + split)
+    _run_small(torch, w, lens=[32 * (3 * split + 1) + 11, 32 * split + 7], split_groups=split)
+
+
 def test_slot_mapping_and_row_order(torch):
     # slots are filled through seq_ids in a scrambled order; decode calls
     # address a subset of slots, in an order unrelated to their lengths (the
