@@ -281,6 +281,32 @@ int palu_prefill_attend(palu_cache *cache, const void *q, void *out,
                         const int32_t *seq_ids, const int32_t *n_q, int32_t B,
                         int32_t T_stride, float softmax_scale, void *stream);
 
+/* Bytes of the workspace palu_prefill_attend_ws needs for these slots at
+ * their current lengths: one pre-decoded key + value tile pair per kv head
+ * and complete 32-token group (a few KiB each).  seq_ids as in
+ * palu_prefill_attend.  Errors: INVALID_ARG, NOT_BOUND, NOT_FITTED,
+ * CAPACITY (slot out of range). */
+int palu_prefill_workspace_bytes(const palu_cache *cache, const int32_t *seq_ids, int32_t B,
+                                 size_t *bytes);
+
+/* palu_prefill_attend with a caller-provided device workspace (PALU page,
+ * "How it works", prefill step 6, as above): every complete group's fp16
+ * key and value tiles are decoded from the codes once, into the workspace,
+ * and the attention kernel streams them instead of decoding each group
+ * once per query tile that reads it.  Same arguments, the same output
+ * bits as palu_prefill_attend, plus
+ *   workspace       : device, 16-byte aligned, at least
+ *                     palu_prefill_workspace_bytes for these slots; the call
+ *                     writes it (stream-ordered), so calls that share one
+ *                     workspace must not overlap
+ *   workspace_bytes : its size
+ * Errors: as palu_prefill_attend; INVALID_ARG also for a NULL, misaligned
+ * or too small workspace. */
+int palu_prefill_attend_ws(palu_cache *cache, const void *q, void *out,
+                           const int32_t *seq_ids, const int32_t *n_q, int32_t B,
+                           int32_t T_stride, float softmax_scale,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
 /* Tokens stored in a slot. */
 int palu_seq_len(const palu_cache *cache, int32_t seq, int32_t *len);
 

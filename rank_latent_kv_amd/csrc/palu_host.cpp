@@ -1182,9 +1182,19 @@ PALU_API int palu_decode_attend_noalloc(palu_cache *c, const void *q, void *out,
     return decode_attend(c, q, out, seq_ids, B, softmax_scale, stream, static_cast<float *>(p));
 }
 
-PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids,
-                                 const int32_t *n_q, int32_t B, int32_t T_stride, float softmax_scale,
-                                 void *stream) {
+namespace {
+
+// Bytes of the pre-decoded tiles of the complete groups of the given slots.
+size_t prefill_ws_need(const palu_cache *c, const int32_t *seq_ids, int32_t B) {
+    const TensorDev kd = c->tensor_dev(0), vd = c->tensor_dev(1);
+    const size_t tb = prefill_tile_bytes(coder_blocks(kd.cd), vd.r);
+    size_t tiles = 0;
+    for (int b = 0; b < B; ++b) tiles += static_cast<size_t>(c->H) * (c->len[seq_ids ? seq_ids[b] : b] / kTokGroup);
+    return tiles * tb;
+}
+
+int prefill_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids, const int32_t *n_q, int32_t B,
+                   int32_t T_stride, float softmax_scale, void *stream, void *ws, size_t ws_bytes) {
     if (int e = check_fitted(c)) return e;
     if (!q || !out) return fail(PALU_ERR_INVALID_ARG, "q and out must be non-NULL");
     if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
@@ -1204,9 +1214,18 @@ PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const 
     const size_t lds = prefill_lds_bytes(coder_blocks(kd.cd), kd.r, vd.r, kd.words, vd.words);
     if (lds > kAttendLdsMax)
         return fail(PALU_ERR_UNSUPPORTED, "prefill workgroup needs more than 160 KiB of LDS at these ranks");
+    if (ws) {
+        if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(PALU_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+        const size_t need = prefill_ws_need(c, seq_ids, B);
+        if (ws_bytes < need)
+            return fail(PALU_ERR_INVALID_ARG, "workspace of " + std::to_string(ws_bytes) + " bytes, " +
+                                                  std::to_string(need) + " needed (palu_prefill_workspace_bytes)");
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(c->D));
     const int ks = prefill_ks(coder_blocks(kd.cd)), nbv = prefill_nbv(vd.r);
+    const size_t tile_bytes = prefill_tile_bytes(coder_blocks(kd.cd), vd.r);
+    int64_t tile_next = 0;                             // first free tile of the workspace
     const int qp = 16 * kPrefillWaves * prefill_nq(ks, nbv) / c->gqa;   // query positions per workgroup
     if ((static_cast<int64_t>(T_stride) + qp - 1) / qp > kMaxGridYZ)
         return fail(PALU_ERR_UNSUPPORTED, "prefill: more query tiles per row than the grid holds (T_stride too large)");
@@ -1227,7 +1246,7 @@ PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const 
         pa.qp = qp;
         pa.qscale = static_cast<float>(scale * 1.4426950408889634);
         pa.bf16 = c->cfg.input_dtype;
-        int tiles = 0;
+        int tiles = 0, max_nfull = 0;
         for (int i = 0; i < nb; ++i) {
             const int slot = seq_ids ? seq_ids[b0 + i] : b0 + i;
             pa.row[i].slot = slot;
@@ -1235,6 +1254,14 @@ PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const 
             pa.row[i].nq = n_q ? n_q[b0 + i] : T_stride;
             pa.row[i].sel_qi = c->sel[slot] | (i << 1);
             tiles = std::max(tiles, (pa.row[i].nq + qp - 1) / qp);
+            // tiles of call row i: kv head h's complete groups from tile_base + h nfull
+            pa.tile_base[i] = tile_next;
+            tile_next += static_cast<int64_t>(c->H) * (c->len[slot] / kTokGroup);
+            max_nfull = std::max(max_nfull, c->len[slot] / kTokGroup);
+        }
+        if (ws) {
+            pa.ws_tiles = static_cast<uint8_t *>(ws);
+            pa.tile_bytes = static_cast<int>(tile_bytes);
         }
         // heaviest rows first in the grid's z order (the causal work of a row
         // grows with its query count and length; stable for equal rows)
@@ -1243,10 +1270,39 @@ PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const 
         });
         if (tiles == 0) continue;
         pa.tiles_max = tiles;
+        if (ws) {
+            hipError_t e = launch_prefill_tiles(pa, max_nfull, s);
+            if (e != hipSuccess) return hip_fail(e, "prefill tile launch");
+        }
         hipError_t e = launch_prefill(pa, lds, s);
         if (e != hipSuccess) return hip_fail(e, "prefill launch");
     }
     return PALU_OK;
+}
+
+}  // namespace
+
+PALU_API int palu_prefill_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_ids,
+                                 const int32_t *n_q, int32_t B, int32_t T_stride, float softmax_scale,
+                                 void *stream) {
+    return prefill_attend(c, q, out, seq_ids, n_q, B, T_stride, softmax_scale, stream, nullptr, 0);
+}
+
+PALU_API int palu_prefill_workspace_bytes(const palu_cache *c, const int32_t *seq_ids, int32_t B, size_t *bytes) {
+    if (!c || !bytes) return fail(PALU_ERR_INVALID_ARG, "cache or bytes is NULL");
+    if (int e = check_fitted(c)) return e;
+    if (B <= 0) return fail(PALU_ERR_INVALID_ARG, "B must be positive");
+    for (int b = 0; b < B; ++b)
+        if (int e = check_slot(c, seq_ids ? seq_ids[b] : b)) return e;
+    *bytes = prefill_ws_need(c, seq_ids, B);
+    return PALU_OK;
+}
+
+PALU_API int palu_prefill_attend_ws(palu_cache *c, const void *q, void *out, const int32_t *seq_ids,
+                                    const int32_t *n_q, int32_t B, int32_t T_stride, float softmax_scale,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
+    if (!workspace) return fail(PALU_ERR_INVALID_ARG, "workspace is NULL (palu_prefill_attend needs none)");
+    return prefill_attend(c, q, out, seq_ids, n_q, B, T_stride, softmax_scale, stream, workspace, workspace_bytes);
 }
 
 PALU_API int palu_seq_len(const palu_cache *c, int32_t seq, int32_t *len) {

@@ -185,6 +185,13 @@ struct PrefillArgs {
     float qscale;             // softmax scale * log2(e)
     int bf16;                 // q and out are bf16 (else fp16)
     PrefillRow row[kMaxCallSeqs];
+    // Pre-decoded tiles (nullptr: the prefill kernel decodes each group
+    // itself): the fp16 key and value tiles of complete group j of call row
+    // i and kv head h are tile_bytes bytes at tile tile_base[i] + h nfull + j
+    // (nfull = the row's complete groups).
+    uint8_t *ws_tiles;
+    int tile_bytes;
+    int64_t tile_base[kMaxCallSeqs];
 };
 
 // Waves of one prefill attention workgroup (16 NQ query columns each).
@@ -199,8 +206,13 @@ int prefill_nbv(int r_v);
 int prefill_nq(int ks, int nbv);
 // LDS bytes of one prefill workgroup.
 size_t prefill_lds_bytes(int nbk, int r_k, int r_v, int words_k, int words_v);
+// Bytes of one complete group's pre-decoded key + value tiles.
+size_t prefill_tile_bytes(int nbk, int r_v);
 // Grid (tiles_max, Hkv, B), 64 kPrefillWaves threads (defined in palu_prefill.hip).
 hipError_t launch_prefill(const PrefillArgs &a, size_t lds_bytes, hipStream_t s);
+// Pre-decodes the tiles of every complete group of the call's rows into
+// a.ws_tiles (one wave per group; max_nfull = the rows' largest count).
+hipError_t launch_prefill_tiles(const PrefillArgs &a, int max_nfull, hipStream_t s);
 
 // LDS bytes of one attend workgroup (independent of the split size).
 size_t attend_lds_bytes(int gqa, int nbk, int r_k, int r_v, int words_k, int words_v, bool vq);

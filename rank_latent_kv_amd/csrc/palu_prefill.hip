@@ -51,7 +51,7 @@ constexpr float kPfSlack = 8.0f;
 constexpr int kVRow = 40;   // halves per value-tile row: 32 tokens + 8 padding
 
 
-__host__ __device__ inline int pf_krow(int ks) { return 32 * ks + 8; }   // halves per key-tile row
+__host__ __device__ constexpr int pf_krow(int ks) { return 32 * ks + 8; }   // halves per key-tile row
 
 // Rings of raw record buffers and tile pairs: groups 2i and 2i + 1 are
 // computed while 2i + 2 and 2i + 3 are built and 2i + 4 and 2i + 5 copied.
@@ -96,9 +96,132 @@ __device__ __forceinline__ f16x8 pair_operand(const uint2 &lo, const uint2 &hi) 
                  perm_b32(hi.y, lo.y, 0x05040100u), perm_b32(hi.y, lo.y, 0x07060302u));
 }
 
+// ---- one 16-byte item of a complete group's fp16 tiles for the tile
+//      pre-decode kernel: the same operations in the same order as the
+//      prefill kernel's own decode of a complete group (build_tiles there,
+//      kept inline: as a shared function it changed that kernel's register
+//      allocation), so both write the same bits
+// Key item: the 8 score-operand positions of key block kq (base bit, bit
+// stride, width, chan0 | chanend << 16) for token t, dequantised from the
+// group's K record kr (scale/zero words from kmeta).
+template <bool GEN>
+__device__ __forceinline__ uint4 tile_key_item(const uint32_t *kr, int kmeta, int4 kq, int t) {
+    const int chan0 = kq.w & 0xFFFF, chanend = kq.w >> 16;
+    const int bit = kq.x + t * kq.y;
+    const uint32_t X = __builtin_amdgcn_alignbit(kr[(bit >> 5) + 1], kr[bit >> 5], bit & 31);
+    const uint32_t Y = GEN && kq.z == 8 ? __builtin_amdgcn_alignbit(kr[(bit >> 5) + 2], kr[(bit >> 5) + 1], bit & 31)
+                                        : 0u;
+    uint32_t sp[4], zp[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t wa = chan0 + k < chanend ? kr[kmeta + chan0 + k] : 0u;
+        const uint32_t wb = chan0 + k + 4 < chanend ? kr[kmeta + chan0 + k + 4] : 0u;
+        sp[k] = perm_b32(wb, wa, 0x05040100u);
+        zp[k] = perm_b32(wb, wa, 0x07060302u);
+    }
+    const uint4 spv = make_uint4(sp[0], sp[1], sp[2], sp[3]), zpv = make_uint4(zp[0], zp[1], zp[2], zp[3]);
+    return __builtin_bit_cast(uint4, GEN ? dequant8_w(X, Y, kq.z, spv, zpv) : dequant8_any(X, kq.z == 4, spv, zpv));
+}
+
+// Value item of a complete group with quantised values: tokens 8 tb ..
+// 8 tb + 7 of channel c (vcw = base bit, width), dequantised from the
+// group's V record vr (scale/zero word of the channel at vmeta + c).
+template <bool GEN>
+__device__ __forceinline__ uint4 tile_value_item(const uint32_t *vr, int vmeta, int2 vcw, int c, int tb) {
+    const int wc = vcw.y;
+    const int bit = vcw.x + 8 * tb * wc;
+    const uint32_t mw = vr[vmeta + c];
+    const uint32_t spair = (mw & 0xFFFFu) | (mw << 16), zpair = (mw >> 16) | (mw & 0xFFFF0000u);
+    uint32_t wd[4];
+    if (GEN && wc == 8) {
+        // 8 tokens = 2 whole words; token u is byte u of the pair
+        const uint32_t Xa = vr[bit >> 5], Xb = vr[(bit >> 5) + 1];
+        wd[0] = dequant_pair(perm_b32(Xb, Xa, 0x0C010C00u) | 0x64006400u, spair, zpair);
+        wd[1] = dequant_pair(perm_b32(Xb, Xa, 0x0C030C02u) | 0x64006400u, spair, zpair);
+        wd[2] = dequant_pair(perm_b32(Xb, Xa, 0x0C050C04u) | 0x64006400u, spair, zpair);
+        wd[3] = dequant_pair(perm_b32(Xb, Xa, 0x0C070C06u) | 0x64006400u, spair, zpair);
+    } else {
+        const uint32_t X = __builtin_amdgcn_alignbit(vr[(bit >> 5) + 1], vr[bit >> 5], bit & 31);
+        const uint32_t m = (1u << wc) - 1u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = (X >> (2 * k * wc)) & m, hi = (X >> ((2 * k + 1) * wc)) & m;
+            wd[k] = dequant_pair(lo | (hi << 16) | 0x64006400u, spair, zpair);
+        }
+    }
+    return make_uint4(wd[0], wd[1], wd[2], wd[3]);
+}
+
+// Tile pre-decode: the fp16 key and value tiles of every complete group of
+// the call's rows, byte for byte as the prefill kernel lays a tile pair out
+// in LDS (zero key positions past the key blocks, the all-ones value
+// channel r_V, zero channels after it, zero row padding), into the
+// workspace at tile tile_base[call row] + kv head * nfull + group.  One wave
+// per group, one 16-byte item per lane and round.  A prompt's groups are
+// then decoded once, not once per query tile that reads them.
+template <int KS, int NBV, bool GEN>
+__global__ __launch_bounds__(256) void prefill_tiles_kernel(PrefillArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = blockIdx.y, i = blockIdx.z;
+    const PrefillRow rw = a.row[i];
+    const int nfull = rw.len >> 5;
+    const int j = blockIdx.x * 4 + wv;
+    if (j >= nfull) return;                          // per wave: the kernel has no barrier
+    const int64_t ci = rw.sel_qi >> 1;
+    const int rk = a.k.r, rv = a.v.r, nbk = coder_blocks(a.k.cd);
+    const bool vq = !a.v.fp16_latents;
+    const int nhk = a.k.cd.bits[0] == 4 ? a.k.cd.c0[1] : 0, nlk = rk - nhk, nbh = (nhk + 7) >> 3;
+    const int nhv = a.v.cd.bits[0] == 4 ? a.v.cd.c0[1] : 0;
+    const int64_t hb = static_cast<int64_t>(rw.slot) * a.Hkv + h;
+    const uint32_t *kr = a.k.records + hb * a.k.head_stride + static_cast<int64_t>(j) * a.k.words;
+    const uint32_t *vr = a.v.records + hb * a.v.head_stride + static_cast<int64_t>(j) * a.v.words;
+    constexpr int kq16 = pf_krow(KS) / 8, vq16 = kVRow / 8;   // 16-byte items per key / value tile row
+    constexpr int nk16 = 32 * kq16, nv16 = 16 * NBV * vq16;
+    uint4 *dst = reinterpret_cast<uint4 *>(a.ws_tiles + (a.tile_base[ci] + static_cast<int64_t>(h) * nfull + j) *
+                                                            static_cast<int64_t>(a.tile_bytes));
+    for (int e = lane; e < nk16 + nv16; e += 64) {
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (e < nk16) {
+            const int t = e / kq16, q = e - t * kq16;   // token, 8-position block
+            if (q < nbk) {
+                int4 kq;
+                if constexpr (GEN) {
+                    const KBlock b = key_block(a.k.cd, q);
+                    kq = make_int4(b.base, b.stride, b.w, b.chan0 | (b.chanend << 16));
+                } else {
+                    const bool w4 = q < nbh;
+                    kq = make_int4(w4 ? 32 * q : 128 * nhk + 16 * (q - nbh), w4 ? 4 * nhk : 2 * nlk, w4 ? 4 : 2,
+                                   (w4 ? 8 * q : nhk + 8 * (q - nbh)) | ((w4 ? nhk : rk) << 16));
+                }
+                val = tile_key_item<GEN>(kr, a.k.cd.meta0, kq, t);
+            }
+        } else {
+            const int e2 = e - nk16, c = e2 / vq16, tb = e2 - c * vq16;   // channel, 8-token block
+            if (tb < 4) {
+                if (c < rv) {
+                    if (vq) {
+                        const int2 vcw = GEN ? value_channel(a.v.cd, c)
+                                             : (c < nhv ? make_int2(128 * c, 4)
+                                                        : make_int2(128 * nhv + 64 * (c - nhv), 2));
+                        val = tile_value_item<GEN>(vr, a.v.cd.meta0, vcw, c, tb);
+                    } else {
+                        val = *reinterpret_cast<const uint4 *>(vr + c * 16 + 4 * tb);
+                    }
+                } else if (c == rv) {
+                    val = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+                }
+            }
+        }
+        dst[e] = val;
+    }
+}
+
 // GEN = false: PALU-shaped layouts (a 4-bit segment, then 2-bit channels),
 // closed-form record addressing; GEN = true: any coder, through LDS tables.
-template <int KS, int NBV, int NQ, bool GEN>
+// PRE = true: complete groups come pre-decoded from a.ws_tiles (a
+// compile-time choice: a runtime one cost both variants registers).
+template <int KS, int NBV, int NQ, bool GEN, bool PRE>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(KS + NBV <= 2 ? 4 : 1)))
 void prefill_kernel(PrefillArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -174,6 +297,20 @@ void prefill_kernel(PrefillArgs a) {
         for (int c = wv; c * 64 < n4; c += kPfWaves) {
             const int e = c * 64 + lane;
             if (e < n4) __builtin_amdgcn_global_load_lds(e < nk4 ? ks + e : vs + (e - nk4), dst + c * 1024, 16, 0, 0);
+        }
+    };
+
+    // ---- pre-decoded tiles of group j (< nfull) -> tile pair j % kPfRing,
+    //      whole (data and constant parts), with direct 16-byte loads
+    constexpr bool pre = PRE;
+    auto copy_tile = [&](unsigned char *base, int j) {
+        const int nb16 = a.tile_bytes >> 4;
+        const u4v *src = reinterpret_cast<const u4v *>(
+            a.ws_tiles + (a.tile_base[ci] + static_cast<int64_t>(h) * nfull + j) * static_cast<int64_t>(a.tile_bytes));
+        unsigned char *dst = base + L.tiles + (j & (kPfRing - 1)) * (L.ktile + L.vtile);
+        for (int c = wv; c * 64 < nb16; c += kPfWaves) {
+            const int e = c * 64 + lane;
+            if (e < nb16) __builtin_amdgcn_global_load_lds(src + e, dst + c * 1024, 16, 0, 0);
         }
     };
 
@@ -324,8 +461,13 @@ void prefill_kernel(PrefillArgs a) {
     //      rows (16 positions x 32 d), B = the column's query (32 d x 16
     //      columns); D[position][column] packed straight into the fp16 score
     //      operand qb (K index 8 kb + 2 v + hh <- position 32 ks + 16 hh + 4 kb + v)
-    for (int j = 0; j < kPfRing; ++j)
-        if (j < nfull && j < ngroups) copy_raw(lds, j);
+    if constexpr (pre) {
+        for (int j = 0; j < 2; ++j)
+            if (j < nfull && j < ngroups) copy_tile(lds, j);
+    } else {
+        for (int j = 0; j < kPfRing; ++j)
+            if (j < nfull && j < ngroups) copy_raw(lds, j);
+    }
     f16x8 qb[NQ][KS];
     {
         const uint16_t *bt = a.k.basis_t16 + rw.slot * a.k.set_bt16 + static_cast<int64_t>(grp) * np * kHeadDim;
@@ -364,8 +506,9 @@ void prefill_kernel(PrefillArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    build_tiles(lds, 0, 0);
-    if (ngroups > 1) build_tiles(lds, 1, nrk + nrv);
+    // (with pre-decoded tiles only the incomplete group is built here)
+    if (!pre || nfull == 0) build_tiles(lds, 0, 0);
+    if (ngroups > 1 && (!pre || nfull <= 1)) build_tiles(lds, 1, nrk + nrv);
     __syncthreads();
 
     // ---- key loop
@@ -480,10 +623,22 @@ void prefill_kernel(PrefillArgs a) {
     // (The helpers are captured by value; they hold the loop-carried state
     // by reference.)
     auto pair = [=](int j, unsigned char *__restrict__ lw, unsigned char *__restrict__ ldma) {
-        if (j + 4 < ngroups && j + 4 < nfull) copy_raw(ldma, j + 4);
-        if (j + 5 < ngroups && j + 5 < nfull) copy_raw(ldma, j + 5);
-        if (j + 2 < ngroups) build_tiles(lw, j + 2, j + 2);
-        if (j + 3 < ngroups) build_tiles(lw, j + 3, j + 2 + nrk + nrv);
+        if constexpr (pre) {
+            // pre-decoded tiles of the next pair (the incomplete group built)
+            if (j + 2 < ngroups) {
+                if (j + 2 < nfull) copy_tile(ldma, j + 2);
+                else build_tiles(lw, j + 2, j + 2);
+            }
+            if (j + 3 < ngroups) {
+                if (j + 3 < nfull) copy_tile(ldma, j + 3);
+                else build_tiles(lw, j + 3, j + 2 + nrk + nrv);
+            }
+        } else {
+            if (j + 4 < ngroups && j + 4 < nfull) copy_raw(ldma, j + 4);
+            if (j + 5 < ngroups && j + 5 < nfull) copy_raw(ldma, j + 5);
+            if (j + 2 < ngroups) build_tiles(lw, j + 2, j + 2);
+            if (j + 3 < ngroups) build_tiles(lw, j + 3, j + 2 + nrk + nrv);
+        }
         compute_group(lw, j);
         if (j + 1 < ngroups) compute_group(lw, j + 1);
         __builtin_amdgcn_s_waitcnt(0);                // this wave's record copies have landed
@@ -544,16 +699,29 @@ void prefill_kernel(PrefillArgs a) {
 }
 
 template <int KS, int NBV, bool GEN>
-hipError_t launch_prefill_tg(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
+hipError_t launch_prefill_tiles_tg(const PrefillArgs &a, int max_nfull, hipStream_t s) {
+    hipLaunchKernelGGL((prefill_tiles_kernel<KS, NBV, GEN>), dim3((max_nfull + 3) / 4, a.Hkv, a.B), dim3(256), 0, s,
+                       a);
+    return hipGetLastError();
+}
+
+template <int KS, int NBV, bool GEN, bool PRE>
+hipError_t launch_prefill_tgp(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
     constexpr int NQ = prefill_nq_c(KS, NBV);
     // set once per process (thread-safe static initialisation)
     static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<KS, NBV, NQ, GEN>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_kernel<KS, NBV, NQ, GEN, PRE>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((prefill_kernel<KS, NBV, NQ, GEN>), dim3(a.Hkv, a.tiles_max, a.B), dim3(kPfThreads), lds_bytes, s,
-                       a);
+    hipLaunchKernelGGL((prefill_kernel<KS, NBV, NQ, GEN, PRE>), dim3(a.Hkv, a.tiles_max, a.B), dim3(kPfThreads),
+                       lds_bytes, s, a);
     return hipGetLastError();
+}
+
+template <int KS, int NBV, bool GEN>
+hipError_t launch_prefill_tg(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
+    return a.ws_tiles ? launch_prefill_tgp<KS, NBV, GEN, true>(a, lds_bytes, s)
+                      : launch_prefill_tgp<KS, NBV, GEN, false>(a, lds_bytes, s);
 }
 
 // A PALU-shaped coder: one 4-bit or 2-bit segment, or 4-bit then 2-bit.
@@ -566,6 +734,25 @@ template <int KS, int NBV>
 hipError_t launch_prefill_t(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {
     const bool gen = !palu_shaped_pf(a.k.cd) || (!a.v.fp16_latents && !palu_shaped_pf(a.v.cd));
     return gen ? launch_prefill_tg<KS, NBV, true>(a, lds_bytes, s) : launch_prefill_tg<KS, NBV, false>(a, lds_bytes, s);
+}
+
+template <int KS, int NBV>
+hipError_t launch_prefill_tiles_t(const PrefillArgs &a, int max_nfull, hipStream_t s) {
+    const bool gen = !palu_shaped_pf(a.k.cd) || (!a.v.fp16_latents && !palu_shaped_pf(a.v.cd));
+    return gen ? launch_prefill_tiles_tg<KS, NBV, true>(a, max_nfull, s)
+               : launch_prefill_tiles_tg<KS, NBV, false>(a, max_nfull, s);
+}
+
+template <int KS>
+hipError_t launch_prefill_tiles_v(const PrefillArgs &a, int max_nfull, hipStream_t s) {
+    switch (prefill_nbv(a.v.r)) {
+        case 1: return launch_prefill_tiles_t<KS, 1>(a, max_nfull, s);
+        case 2: return launch_prefill_tiles_t<KS, 2>(a, max_nfull, s);
+        case 3: return launch_prefill_tiles_t<KS, 3>(a, max_nfull, s);
+        case 5: return launch_prefill_tiles_t<KS, 5>(a, max_nfull, s);
+        case 9: return launch_prefill_tiles_t<KS, 9>(a, max_nfull, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int KS>
@@ -599,6 +786,21 @@ size_t prefill_lds_bytes(int nbk, int r_k, int r_v, int words_k, int words_v) {
     (void)r_k;
     const int ks = prefill_ks(nbk), nbv = prefill_nbv(r_v);
     return static_cast<size_t>(prefill_lds(ks, nbv, prefill_nq(ks, nbv), words_k, words_v, r_v, nbk).total);
+}
+
+size_t prefill_tile_bytes(int nbk, int r_v) {
+    const int ks = prefill_ks(nbk), nbv = prefill_nbv(r_v);
+    return static_cast<size_t>(32 * pf_krow(ks) * 2 + 16 * nbv * kVRow * 2);
+}
+
+hipError_t launch_prefill_tiles(const PrefillArgs &a, int max_nfull, hipStream_t s) {
+    if (max_nfull <= 0) return hipSuccess;
+    switch (prefill_ks(coder_blocks(a.k.cd))) {
+        case 1: return launch_prefill_tiles_v<1>(a, max_nfull, s);
+        case 2: return launch_prefill_tiles_v<2>(a, max_nfull, s);
+        case 4: return launch_prefill_tiles_v<4>(a, max_nfull, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, size_t lds_bytes, hipStream_t s) {

@@ -27,7 +27,7 @@ EXPORTED = ["palu_config_default", "palu_cache_create", "palu_cache_required_byt
             "palu_fit_seq", "palu_set_basis_seq", "palu_get_basis_seq",
             "palu_encode_append", "palu_decode_attend", "palu_decode_step", "palu_sync_lengths",
             "palu_decode_attend_noalloc",
-            "palu_prefill_attend", "palu_seq_len",
+            "palu_prefill_attend", "palu_prefill_workspace_bytes", "palu_prefill_attend_ws", "palu_seq_len",
             "palu_read_codes",
             "palu_get_stats", "palu_reset", "palu_record_words", "palu_export_bytes",
             "palu_export_seq", "palu_import_seq", "palu_get_fit_info", "palu_probe_read",
@@ -98,6 +98,8 @@ def lib():
         "palu_decode_step": [_vp, _vp, _vp, _vp, _vp, _i32p, _i32, ctypes.c_float, _vp],
         "palu_sync_lengths": [_vp],
         "palu_prefill_attend": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, ctypes.c_float, _vp],
+        "palu_prefill_workspace_bytes": [_vp, _i32p, _i32, ctypes.POINTER(_sz)],
+        "palu_prefill_attend_ws": [_vp, _vp, _vp, _i32p, _i32p, _i32, _i32, ctypes.c_float, _vp, _sz, _vp],
         "palu_seq_len": [_vp, _i32, _i32p],
         "palu_read_codes": [_vp, _i32, _i32, _i32, _vp, _sz, _vp, _sz],
         "palu_get_stats": [_vp, ctypes.POINTER(palu_stats)],
@@ -248,6 +250,21 @@ def palu_prefill_attend(cache: int, q_ptr: int, out_ptr: int, seq_ids, n_q, B: i
     n = _i32_array(n_q, B, "n_q")
     _check(lib().palu_prefill_attend(cache, q_ptr, out_ptr, s[1] if s else None,
                                      n[1] if n else None, B, T_stride, softmax_scale, stream))
+
+
+def palu_prefill_workspace_bytes(cache: int, seq_ids, B: int) -> int:
+    s = _i32_array(seq_ids, B, "seq_ids")
+    n = _sz()
+    _check(lib().palu_prefill_workspace_bytes(cache, s[1] if s else None, B, ctypes.byref(n)))
+    return n.value
+
+
+def palu_prefill_attend_ws(cache: int, q_ptr: int, out_ptr: int, seq_ids, n_q, B: int, T_stride: int,
+                           softmax_scale: float, ws_ptr: int, ws_bytes: int, stream: int):
+    s = _i32_array(seq_ids, B, "seq_ids")
+    n = _i32_array(n_q, B, "n_q")
+    _check(lib().palu_prefill_attend_ws(cache, q_ptr, out_ptr, s[1] if s else None, n[1] if n else None, B,
+                                        T_stride, softmax_scale, ws_ptr, ws_bytes, stream))
 
 
 def palu_seq_len(cache: int, seq: int) -> int:
@@ -481,10 +498,15 @@ class LatentKVCache:
                                    softmax_scale, self._stream())
         return out
 
-    def prefill_attend(self, q, seq_ids=None, n_q=None, softmax_scale: float = 0.0, out=None):
+    def prefill_attend(self, q, seq_ids=None, n_q=None, softmax_scale: float = 0.0, out=None,
+                       workspace=None):
         """q: fp16 [B, Hq, T, D]; row b's first n_q[b] (default T) queries
         sit at the slot's last n_q[b] positions and attend causally.
-        Returns fp16 [B, Hq, T, D] (entries past n_q[b] are left as they were)."""
+        Returns fp16 [B, Hq, T, D] (entries past n_q[b] are left as they were).
+        workspace: None = a device buffer this object keeps and grows for the
+        pre-decoded tiles (palu_prefill_attend_ws); a uint8 device tensor =
+        that buffer; False = no workspace (palu_prefill_attend, which decodes
+        each group in the attention kernel; the same output bits)."""
         self._check_rank(q, 4, "q")
         self._check_half(q, (self.Hq, q.shape[2], self.D), "q")
         if q.data_ptr() % 16:
@@ -496,8 +518,22 @@ class LatentKVCache:
             raise ValueError("out must be 16-byte aligned")
         _i32_array(seq_ids, q.shape[0], "seq_ids")
         _i32_array(n_q, q.shape[0], "n_q")
-        palu_prefill_attend(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, n_q, q.shape[0],
-                            q.shape[2], softmax_scale, self._stream())
+        if workspace is False:
+            palu_prefill_attend(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, n_q, q.shape[0],
+                                q.shape[2], softmax_scale, self._stream())
+            return out
+        need = palu_prefill_workspace_bytes(self.handle, seq_ids, q.shape[0])
+        if workspace is None:
+            ws = getattr(self, "_prefill_ws", None)
+            if ws is None or ws.numel() < need:
+                ws = self.torch.empty(max(need, 256), dtype=self.torch.uint8, device=q.device)
+                self._prefill_ws = ws
+        else:
+            ws = workspace
+            if ws.dtype != self.torch.uint8 or not ws.is_cuda or not ws.is_contiguous():
+                raise ValueError("workspace must be a contiguous uint8 device tensor")
+        palu_prefill_attend_ws(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, n_q, q.shape[0], q.shape[2],
+                               softmax_scale, ws.data_ptr(), ws.numel(), self._stream())
         return out
 
     def seq_len(self, seq: int) -> int:

@@ -97,6 +97,8 @@ def test_codes_decode_prefill(torch, case):
         m = min(40, n)
         qp = synth.prefill_queries(w, b, n)[:, n - m:]
         pre = cache.prefill_attend(_dev(torch, qp[None]), seq_ids=[b], n_q=[m]).cpu().numpy()[0]
+        pre0 = cache.prefill_attend(_dev(torch, qp[None]), seq_ids=[b], n_q=[m], workspace=False).cpu().numpy()[0]
+        assert np.array_equal(pre[:, :m].view(np.uint16), pre0[:, :m].view(np.uint16))
         _check_attention(pre, layer.prefill_attend(ks, vs, qp, np.arange(n - m, n)), f"prefill row {b}")
 
 

@@ -78,6 +78,11 @@ def test_full_prompt_ragged(torch, gqa, rank, groups, vq):
     q = np.stack([synth.prefill_queries(w, b, S) for b in range(4)])
     out = cache.prefill_attend(_dev(torch, q), n_q=lens).cpu().numpy()
     _check_call(layer, k_all, v_all, lens, q, lens, out, what=f"gqa {gqa} rank {rank}")
+    # the kernel's own decode of each group (no workspace) gives the same bits
+    # as the pre-decoded tiles
+    out0 = cache.prefill_attend(_dev(torch, q), n_q=lens, workspace=False).cpu().numpy()
+    for b in range(4):
+        assert np.array_equal(out[b, :, :lens[b]].view(np.uint16), out0[b, :, :lens[b]].view(np.uint16)), b
 
 
 @pytest.mark.parametrize("gqa", [1, 3])
@@ -94,6 +99,29 @@ def test_several_tiles_and_sharp_softmax(torch, gqa):
         out = cache.prefill_attend(_dev(torch, q), n_q=lens, softmax_scale=scale).cpu().numpy()
         _check_call(layer, k_all, v_all, lens, q, lens, out, scale=scale or None,
                     what=f"scale {scale}")
+
+
+def test_workspace_sizes_and_errors(torch):
+    from rank_latent_kv_amd.palu import PaluError, palu_prefill_workspace_bytes
+    lens = np.array([100, 31, 64], np.int32)
+    w = synth.small_workload(batch=3, n_q_heads=4, n_kv_heads=2, prefill=100, rank=16, seed=11)
+    k_all, v_all, cache, layer = _prepared(torch, w, lens, 1, 16, True)
+    cache.encode_append(_dev(torch, k_all), _dev(torch, v_all), n_new=lens)
+    # one tile pair per kv head and complete group: (3 + 0 + 2) groups x 2 heads
+    need = palu_prefill_workspace_bytes(cache.handle, None, 3)
+    per = palu_prefill_workspace_bytes(cache.handle, [0], 1) // 6
+    assert need == 10 * per and per > 0
+    assert palu_prefill_workspace_bytes(cache.handle, [1], 1) == 0
+    q = _dev(torch, np.stack([synth.prefill_queries(w, b, 100) for b in range(3)]))
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(PaluError, match="INVALID_ARG"):
+        cache.prefill_attend(q, n_q=lens, workspace=small)
+    odd = torch.empty(need + 32, dtype=torch.uint8, device="cuda")[8:]
+    with pytest.raises(PaluError, match="INVALID_ARG"):
+        cache.prefill_attend(q, n_q=lens, workspace=odd)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = cache.prefill_attend(q, n_q=lens, workspace=ws).cpu().numpy()
+    _check_call(layer, k_all, v_all, lens, q.cpu().numpy(), lens, out, what="caller workspace")
 
 
 def test_chunked_prefill_offsets(torch):
