@@ -35,9 +35,12 @@
 // wave's positions.  The online softmax is lazy: it rescales only when a
 // group's maximum exceeds the running one by more than kPfSlack (log2
 // units).  Weights 2^(s - m) are rounded to fp16, and
-// O[col][c] += sum_t P[col][t] Vhat[t][c] runs on MFMA.  In both MFMAs the
-// K index 8 kb + 2 v + hh stands for token (or position) 16 hh + 4 kb + v,
-// the order the score accumulator already holds.
+// O[col][c] += sum_t P[col][t] Vhat[t][c] runs on MFMA.  In both MFMAs K
+// index i stands for token (or position) i: score half hh takes the tokens
+// 2 row + hh as its rows (and the query absorption the positions likewise),
+// so the accumulator values v of halves 0 and 1 are the adjacent tokens
+// 8 kb + 2 v and 8 kb + 2 v + 1, and every operand is one 16-byte LDS read
+// of 8 consecutive tile elements.
 #include "palu_device.h"
 #include "palu_internal.h"
 
@@ -87,13 +90,6 @@ __host__ __device__ inline PrefillLds prefill_lds(int ks, int nbv, int nq, int w
 // value accumulators (4 NBV per tile) stay within about 64 registers.
 __host__ __device__ constexpr int prefill_nq_c(int ks, int nbv) {
     return 16 / (ks + nbv) >= 4 ? 4 : (16 / (ks + nbv) >= 2 ? 2 : 1);
-}
-
-// MFMA operand for K index 8 kb + 2 v + hh <- element 16 hh + 4 kb + v of a
-// row: lo = elements 4 kb .. 4 kb + 3, hi = elements 16 + 4 kb .. 19 + 4 kb.
-__device__ __forceinline__ f16x8 pair_operand(const uint2 &lo, const uint2 &hi) {
-    return as_h8(perm_b32(hi.x, lo.x, 0x05040100u), perm_b32(hi.x, lo.x, 0x07060302u),
-                 perm_b32(hi.y, lo.y, 0x05040100u), perm_b32(hi.y, lo.y, 0x07060302u));
 }
 
 // ---- one 16-byte item of a complete group's fp16 tiles for the tile
@@ -459,8 +455,9 @@ void prefill_kernel(PrefillArgs a) {
     // ---- prologue: records of groups 0 and 1 in flight while the query is
     //      absorbed: qt = qs V_K^T q on MFMA, A = position-ordered key basis
     //      rows (16 positions x 32 d), B = the column's query (32 d x 16
-    //      columns); D[position][column] packed straight into the fp16 score
-    //      operand qb (K index 8 kb + 2 v + hh <- position 32 ks + 16 hh + 4 kb + v)
+    //      columns; block 2 ks + hh takes positions 32 ks + 2 row + hh);
+    //      D[position][column] packed straight into the fp16 score operand
+    //      qb (K index 8 kb + 2 v + hh <- position 32 ks + 8 kb + 2 v + hh)
     if constexpr (pre) {
         for (int j = 0; j < 2; ++j)
             if (j < nfull && j < ngroups) copy_tile(lds, j);
@@ -482,7 +479,7 @@ void prefill_kernel(PrefillArgs a) {
             f4 acc[2 * KS];
 #pragma unroll
             for (int blk = 0; blk < 2 * KS; ++blk) {
-                const int n = 16 * blk + ln;
+                const int n = 32 * (blk >> 1) + 2 * ln + (blk & 1);
                 acc[blk] = (f4){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
@@ -527,20 +524,20 @@ void prefill_kernel(PrefillArgs a) {
             const _Float16 *kt = reinterpret_cast<const _Float16 *>(base + L.tiles + slot * (L.ktile + L.vtile));
             const _Float16 *vt = reinterpret_cast<const _Float16 *>(base + L.tiles + slot * (L.ktile + L.vtile) +
                                                                     L.ktile);
-            f16x8 ka[2][KS];
+            f16x8 ka[2][KS];     // half hh, row ln: token 2 ln + hh
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const _Float16 *p = kt + (16 * hh + ln) * krow + 32 * ks + 4 * kb;
-                    ka[hh][ks] = pair_operand(*reinterpret_cast<const uint2 *>(p), *reinterpret_cast<const uint2 *>(p + 16));
+                    const uint4 w = *reinterpret_cast<const uint4 *>(kt + (2 * ln + hh) * krow + 32 * ks + 8 * kb);
+                    ka[hh][ks] = as_h8(w.x, w.y, w.z, w.w);
                 }
             }
-            f16x8 vb[NBV];
+            f16x8 vb[NBV];       // channel 16 nb + ln, tokens 8 kb .. 8 kb + 7
 #pragma unroll
             for (int nb = 0; nb < NBV; ++nb) {
-                const _Float16 *p = vt + (16 * nb + ln) * kVRow + 4 * kb;
-                vb[nb] = pair_operand(*reinterpret_cast<const uint2 *>(p), *reinterpret_cast<const uint2 *>(p + 16));
+                const uint4 w = *reinterpret_cast<const uint4 *>(vt + (16 * nb + ln) * kVRow + 8 * kb);
+                vb[nb] = as_h8(w.x, w.y, w.z, w.w);
             }
             const bool masked = 32 * j + 31 > pw_lo;    // wave-uniform
             // (a) every tile's scores first (the softmax of tile t then finds
@@ -564,20 +561,24 @@ void prefill_kernel(PrefillArgs a) {
             if (masked) {
 #pragma unroll
                 for (int t = 0; t < NQ; ++t) {
-                    const int lim = pcol[t] - 32 * j - 4 * kb;   // token 16 hh + 4 kb + v allowed iff 16 hh + v <= lim
+                    const int lim = pcol[t] - 32 * j - 8 * kb;   // token 8 kb + 2 v + hh allowed iff 2 v + hh <= lim
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) xv[t][k] = 16 * (k >> 2) + (k & 3) <= lim ? xv[t][k] : -INFINITY;
+                    for (int k = 0; k < 8; ++k) xv[t][k] = 2 * (k & 3) + (k >> 2) <= lim ? xv[t][k] : -INFINITY;
                 }
             }
-            // (c) lazy rescale: one test for the whole wave and all tiles
-            float mloc[NQ], mall = -INFINITY;
+            // (c) lazy rescale: one test for the whole wave and all tiles,
+            //     on the maximum of all the lane's values (three-input max
+            //     steps); the per-tile maxima only when a rescale is due
+            float mall = xv[0][0];
 #pragma unroll
-            for (int t = 0; t < NQ; ++t) {
-                mloc[t] = fmaxf(fmaxf(fmaxf(xv[t][0], xv[t][1]), fmaxf(xv[t][2], xv[t][3])),
-                                fmaxf(fmaxf(xv[t][4], xv[t][5]), fmaxf(xv[t][6], xv[t][7])));
-                mall = fmaxf(mall, mloc[t]);
-            }
+            for (int i = 1; i + 1 < 8 * NQ; i += 2) mall = fmaxf(fmaxf(mall, xv[i / 8][i % 8]), xv[(i + 1) / 8][(i + 1) % 8]);
+            mall = fmaxf(mall, xv[NQ - 1][7]);
             if (j == 0 || __builtin_amdgcn_ballot_w64(mall > kPfSlack) != 0) {
+                float mloc[NQ];
+#pragma unroll
+                for (int t = 0; t < NQ; ++t)
+                    mloc[t] = fmaxf(fmaxf(fmaxf(xv[t][0], xv[t][1]), fmaxf(xv[t][2], xv[t][3])),
+                                    fmaxf(fmaxf(xv[t][4], xv[t][5]), fmaxf(xv[t][6], xv[t][7])));
 #pragma unroll
                 for (int t = 0; t < NQ; ++t) {
                     // column maximum of s - m over the 4 lanes that hold the
