@@ -522,16 +522,19 @@ class LatentKVCache:
             palu_prefill_attend(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, n_q, q.shape[0],
                                 q.shape[2], softmax_scale, self._stream())
             return out
+        if workspace is not None:
+            ws = workspace
+            if (not isinstance(ws, self.torch.Tensor) or ws.dtype != self.torch.uint8 or not ws.is_cuda
+                    or not ws.is_contiguous()):
+                raise ValueError("workspace must be a contiguous uint8 device tensor")
+            if ws.device != q.device:
+                raise ValueError("workspace must be on q's device")
         need = palu_prefill_workspace_bytes(self.handle, seq_ids, q.shape[0])
         if workspace is None:
             ws = getattr(self, "_prefill_ws", None)
             if ws is None or ws.numel() < need:
                 ws = self.torch.empty(max(need, 256), dtype=self.torch.uint8, device=q.device)
                 self._prefill_ws = ws
-        else:
-            ws = workspace
-            if ws.dtype != self.torch.uint8 or not ws.is_cuda or not ws.is_contiguous():
-                raise ValueError("workspace must be a contiguous uint8 device tensor")
         palu_prefill_attend_ws(self.handle, q.data_ptr(), out.data_ptr(), seq_ids, n_q, q.shape[0], q.shape[2],
                                softmax_scale, ws.data_ptr(), ws.numel(), self._stream())
         return out

@@ -236,6 +236,10 @@ def test_binding_rejects_bad_out_before_launch():
                 torch.zeros((2, 32, 16, 128), dtype=torch.bfloat16)):
         with pytest.raises(ValueError):
             c.prefill_attend(qp, out=out)
+    # the tile workspace: a uint8 device tensor (checked before any call)
+    for ws in (torch.zeros(64, dtype=torch.uint8), torch.zeros(16, dtype=torch.float32), 1234):
+        with pytest.raises(ValueError):
+            c.prefill_attend(qp, workspace=ws)
     with pytest.raises(ValueError):
         c.decode_attend(torch.zeros((32, 128), dtype=torch.float16))  # missing batch dim
     with pytest.raises(ValueError):
