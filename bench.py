@@ -20,12 +20,13 @@ system-scope fence a default HIP event adds.  Next to it the line reports:
     8 TB/s HBM peak;
   * read_bandwidth: what a plain 16-byte-load stream over 1 GiB reaches on
     the same device (the library's read probe);
-  * workloads: decode-only warm and cold times, bytes and bandwidth, and
-    the prefill encode rate, for each of the five workloads;
+  * workloads: decode-only warm and cold times, bytes and bandwidth, the
+    prefill encode rate and the prefill attention time (back-to-back calls),
+    for each of the five workloads;
   * encode_roofline: the prefill encode against HBM (fp16 K/V read, records
     and tails written) and against the non-packed fp32 VALU issue rate;
-  * prefill_attend: time and causal score pairs per second against the
-    VALU issue rate (2.5 lane operations per pair);
+  * prefill_attend: time inside the step and causal score pairs per second
+    against the VALU issue rate (3.5 lane-operation slots per pair);
   * cpu_baseline: the oracle on the host cores (decode, encode, fit), one
     thread and all threads of the job's CPU share.
 
@@ -278,9 +279,32 @@ def gen_inputs(w, n_extra, bf16=False):
     return lens, out
 
 
+def workload_prefill(torch, dev, stream, cache, w, lens, n_calls=3):
+    """Causal prefill attention of every prompt position over the encoded
+    prompt: mean ms of n_calls back-to-back calls after one untimed call."""
+    from concurrent.futures import ThreadPoolExecutor
+    S = int(lens.max())
+    qpre = torch.zeros((w.batch, w.n_q_heads, S, w.head_dim), dtype=torch.float16, device=dev)
+    with ThreadPoolExecutor(host_threads()) as pool:
+        for b, qb in enumerate(pool.map(lambda b: synth.prefill_queries(w, b, int(lens[b])), range(w.batch))):
+            qpre[b, :, :lens[b]] = torch.from_numpy(qb).to(dev)
+    out = torch.empty_like(qpre)
+    cache.prefill_attend(qpre, n_q=lens, out=out)
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(n_calls)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        cache.prefill_attend(qpre, n_q=lens, out=out)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    del qpre, out
+    return ms
+
+
 def workload_decode(torch, dev, stream, flush, w, n_warm=32, n_cold=16):
-    """One workload's decode-only figures: fit and encode the prefill, append
-    one token per sequence, then time decode-attend warm and cold."""
+    """One workload's decode-only figures: fit and encode the prefill, time
+    the prefill attention, append one token per sequence, then time
+    decode-attend warm and cold."""
     from rank_latent_kv_amd.palu import LatentKVCache, palu_record_words
     t0 = time.time()
     lens, host = gen_inputs(w, 1)
@@ -310,6 +334,8 @@ def workload_decode(torch, dev, stream, flush, w, n_warm=32, n_cold=16):
         e1.record(stream)
         torch.cuda.synchronize()
         enc_ms.append(e0.elapsed_time(e1))
+    pre_ms = workload_prefill(torch, dev, stream, cache, w, lens)
+    pairs = w.n_q_heads * float(np.sum(lens.astype(np.float64) * (lens + 1) / 2))
     cache.encode_append(knew, vnew)
     q = torch.from_numpy(np.stack([synth.queries(w, b, 1)[0] for b in range(w.batch)])).to(dev)
     out = torch.empty_like(q)
@@ -328,7 +354,9 @@ def workload_decode(torch, dev, stream, flush, w, n_warm=32, n_cold=16):
            "cold_frac": round(nb / (cold_mean / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
            "decode_tok_s_warm": round(w.batch / (warm_mean / 1e3), 1),
            "encode_ms": round(enc, 4), "encode_mtok_s": round(float(lens.sum()) / (enc / 1e3) / 1e6, 2),
-           "encode_gbps": round(eb / (enc / 1e3) / 1e9, 1), "input_gen_s": round(gen_s, 1)}
+           "encode_gbps": round(eb / (enc / 1e3) / 1e9, 1),
+           "prefill_ms": round(pre_ms, 3), "prefill_pairs_per_s": round(pairs / (pre_ms / 1e3), 1),
+           "input_gen_s": round(gen_s, 1)}
     del cache, kpre, vpre
     torch.cuda.empty_cache()
     return res
