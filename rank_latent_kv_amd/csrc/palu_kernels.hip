@@ -186,10 +186,11 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(GramReduceArgs a) {
 
 // -------------------------------------------------------------- encode ----
 //
-// One wave per pair of token groups (64 positions, lane = position) of one
-// (call row, kv head, tensor); four independent waves per workgroup, no
-// workgroup barriers after the code table.  Wave unit u of a row covers
-// groups 2 (j0/2 + u) and 2 (j0/2 + u) + 1, j0 = old_len / 32.  A lane's
+// One wave per REPS consecutive pairs of token groups, one pair (64
+// positions, lane = position) after the other, of one (call row, kv head,
+// tensor); four independent waves per workgroup, no workgroup barriers after
+// the code table.  Unit u of a row covers groups 2 (j0/2 + u) and
+// 2 (j0/2 + u) + 1, j0 = old_len / 32.  A lane's
 // position is new (in [old, old + n)), old (an earlier position of group j0,
 // read back from the tail buffer) or outside the call.  Per lane
 // y_d = float(x_d) - mu_d in fp32 (one mixed-precision fma per fp16 element,
@@ -319,15 +320,19 @@ __host__ __device__ inline int encode_lds_bytes(int r, int words, bool fp16) {
             4 * r) * 4;
 }
 
-// Five waves per SIMD (at most 96 VGPRs): the quantiser's reductions and the
-// scalar-load waits of the projection are latency chains that the extra
-// waves hide.
-template <bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void encode_kernel(EncodeArgs a) {
+// Ranks up to 16 (REPS = 1): five waves per SIMD (at most 96 VGPRs), the
+// quantiser's reductions and the scalar-load waits of the projection being
+// latency chains that the extra waves hide.  Wider ranks (REPS = 2): up to
+// 32 fma chains per lane need the registers of four waves per SIMD, and
+// each wave takes two group pairs, so that the basis it streams through
+// scalar loads serves twice the positions.
+template <bool BF16, int REPS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(REPS > 1 ? 4 : 5))) void encode_kernel(
+    EncodeArgs a) {
     extern __shared__ __align__(16) float esh[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int u = blockIdx.x * kEncWaves + wv;
+    const int u = (blockIdx.x * kEncWaves + wv) * REPS;      // first unit of this wave
     const int bi = blockIdx.y / a.H, h = blockIdx.y - (blockIdx.y / a.H) * a.H;
     const int tz = blockIdx.z;
     const int o = a.old_len[bi], n = a.n_new[bi];
@@ -338,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
     }
     if (n <= 0) return;                              // whole workgroup
     const int j0 = o >> 5, jl = (o + n - 1) >> 5;
-    if (2 * ((j0 >> 1) + blockIdx.x * kEncWaves) > jl) return;   // whole workgroup
+    if (2 * ((j0 >> 1) + blockIdx.x * kEncWaves * REPS) > jl) return;   // whole workgroup
     const TensorDev &T = tz ? a.t[1] : a.t[0];
     const int r = T.r, W = T.words;
     const int grp = h / a.hpg, slot = a.slot[bi];
@@ -354,162 +359,168 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void e
         ctab[tid] = make_int4(b0.x, b1.x - b0.x, b0.y, T.cd.meta0 + tid);
     }
     __syncthreads();
-    const int jp = (j0 >> 1) + u;                    // group pair of this wave
-    if (2 * jp > jl) return;                         // wave-uniform; no barrier follows
+    for (int rep = 0; rep < REPS; ++rep) {
+        const int jp = (j0 >> 1) + u + rep;              // group pair of this pass
+        if (2 * jp > jl) break;                          // wave-uniform; no barrier follows
 
-    const int p = 64 * jp + lane;                    // this lane's position
-    EncLane e;
-    const int j = p >> 5;
-    e.t = p & 31;
-    e.half = lane >> 5;
-    e.is_new = p >= o && p < o + n;
-    e.is_old = p < o && j == j0;
-    e.touched = j >= j0 && j <= jl;
-    e.complete = e.touched && o + n >= 32 * j + 32;
-    // complete groups that get a quantised record (fp16 latents have none)
-    const bool any_complete = !fp16 && __any(e.complete);
-    const bool any_old = !fp16 && __any(e.is_old);
-    const int64_t head_base = static_cast<int64_t>(slot) * a.H + h;
+        const int p = 64 * jp + lane;                    // this lane's position
+        EncLane e;
+        const int j = p >> 5;
+        e.t = p & 31;
+        e.half = lane >> 5;
+        e.is_new = p >= o && p < o + n;
+        e.is_old = p < o && j == j0;
+        e.touched = j >= j0 && j <= jl;
+        e.complete = e.touched && o + n >= 32 * j + 32;
+        // complete groups that get a quantised record (fp16 latents have none)
+        const bool any_complete = !fp16 && __any(e.complete);
+        const bool any_old = !fp16 && __any(e.is_old);
+        const int64_t head_base = static_cast<int64_t>(slot) * a.H + h;
 
-    float4 *sc = reinterpret_cast<float4 *>(esh) + wv * (SC / 4);                     // [2 halves][32 channels]
-    uint32_t *rec_lds = reinterpret_cast<uint32_t *>(esh + kEncWaves * SC) + (wv * 2 + e.half) * WR;
-    float *lat = esh + kEncWaves * (SC + 2 * WR) + wv * LR * 64;                       // this wave's [LR][64]
-    if (any_complete) {
-        for (int w = e.t; w < W; w += 32) rec_lds[w] = 0u;
-    }
+        float4 *sc = reinterpret_cast<float4 *>(esh) + wv * (SC / 4);                     // [2 halves][32 channels]
+        uint32_t *rec_lds = reinterpret_cast<uint32_t *>(esh + kEncWaves * SC) + (wv * 2 + e.half) * WR;
+        float *lat = esh + kEncWaves * (SC + 2 * WR) + wv * LR * 64;                       // this wave's [LR][64]
+        if (any_complete) {
+            for (int w = e.t; w < W; w += 32) rec_lds[w] = 0u;
+        }
 
-    // 1. this lane's input row (a valid row is read for every lane; only
-    //    new positions use theirs)
-    const int row = e.is_new ? p - o : 0;
-    const uint16_t *xrow = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim +
-                           static_cast<int64_t>(row) * kHeadDim;
-    ConstF *mu = (ConstF *)(T.mu + slot * T.set_mu + grp * kHeadDim);   // address-space cast
-    ConstF *vbase = (ConstF *)(T.basis + slot * T.set_basis + static_cast<int64_t>(grp) * kHeadDim * r);
+        // 1. this lane's input row (a valid row is read for every lane; only
+        //    new positions use theirs)
+        const int row = e.is_new ? p - o : 0;
+        const uint16_t *xrow = a.x[tz] + (static_cast<int64_t>(bi) * a.H + h) * a.T_stride * kHeadDim +
+                               static_cast<int64_t>(row) * kHeadDim;
+        ConstF *mu = (ConstF *)(T.mu + slot * T.set_mu + grp * kHeadDim);   // address-space cast
+        ConstF *vbase = (ConstF *)(T.basis + slot * T.set_basis + static_cast<int64_t>(grp) * kHeadDim * r);
 
-    // 2. latents in chunks of up to 32 channels (one fma chain per channel),
-    //    parked in LDS, then quantised / stored channel by channel
-    const float *told = fp16 ? nullptr : T.tail + (head_base * 2 + a.sel_old[bi]) * 32 * r;
-    float *tnew = fp16 ? nullptr : T.tail + (head_base * 2 + a.sel_new[bi]) * 32 * r;
-    uint16_t *rec16 = reinterpret_cast<uint16_t *>(T.records + head_base * T.head_stride +
-                                                   static_cast<int64_t>(j) * W);
-    for (int c0 = 0; c0 < r; c0 += 32) {
-        const int nc = r - c0 < 32 ? r - c0 : 32;
-        ConstF *vb = vbase + c0;
-        if (nc == r && (nc <= 16 || (nc & 3) == 0)) {
-            // the whole row in one chunk of a compiled width
-            switch (nc <= 16 ? nc : 12 + (nc >> 2)) {
-                case 1: project_chunk<1, 1, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 2: project_chunk<2, 2, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 3: project_chunk<3, 3, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 4: project_chunk<4, 4, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 5: project_chunk<5, 5, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 6: project_chunk<6, 6, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 7: project_chunk<7, 7, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 8: project_chunk<8, 8, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 9: project_chunk<9, 9, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 10: project_chunk<10, 10, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 11: project_chunk<11, 11, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 12: project_chunk<12, 12, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 13: project_chunk<13, 13, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 14: project_chunk<14, 14, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 15: project_chunk<15, 15, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 16: project_chunk<16, 16, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 17: project_chunk<20, 20, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 18: project_chunk<24, 24, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 19: project_chunk<28, 28, BF16>(xrow, mu, vb, r, lat, lane); break;
-                default: project_chunk<32, 32, BF16>(xrow, mu, vb, r, lat, lane); break;
-            }
-        } else {
-            // other chunks: runtime row stride, width rounded up to 4
-            switch ((nc + 3) >> 2) {
-                case 1: project_chunk<4, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 2: project_chunk<8, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 3: project_chunk<12, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 4: project_chunk<16, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 5: project_chunk<20, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 6: project_chunk<24, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
-                case 7: project_chunk<28, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
-                default: project_chunk<32, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
-            }
-        }
-        if (fp16) {
-            // fp16 latents: only new positions are stored
-            if (e.is_new)
-                for (int k = 0; k < nc; ++k) rec16[(c0 + k) * 32 + e.t] = static_cast<uint16_t>(f2h_bits(lat[k * 64 + lane]));
-            continue;
-        }
-        // pass 1: each channel's value (old positions from the tail buffer),
-        // new latents of an incomplete group to the tail, and per half the
-        // minimum and maximum (lanes 31 and 63 record them)
-        if (any_old) {
-            // old positions of the first group: their latents from the tail
-            // buffer, into the latent buffer
-            for (int k = 0; k < nc; ++k)
-                if (e.is_old) lat[k * 64 + lane] = told[e.t * r + c0 + k];
-        }
-        for (int k = 0; k < nc; ++k) {
-            const int c = c0 + k;
-            const float v = lat[k * 64 + lane];
-            if (!e.complete && e.touched && e.is_new) tnew[e.t * r + c] = v;
-            if (any_complete) {                      // wave-uniform
-                float mx = row_max(v), mn = -row_max(-v);
-                mx = fmaxf(mx, from_prev_row(mx));
-                mn = fminf(mn, from_prev_row(mn));
-                if (e.t == 31) *reinterpret_cast<float2 *>(sc + e.half * 32 + k) = make_float2(mn, mx);
-            }
-        }
-        if (!any_complete) continue;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // pass 2: lane (half, k) takes its group's channel c0 + k: scale by
-        // IEEE division, the reciprocal (normal scales only; 0 makes every
-        // code of the channel a division) and the metadata word
-        {
-            const int k = lane & 31;
-            if (k < nc && e.complete) {
-                const int c = c0 + k;
-                const int4 ct = ctab[c];
-                const float2 mm = *reinterpret_cast<const float2 *>(sc + e.half * 32 + k);
-                const float levels = static_cast<float>((1 << ct.z) - 1);
-                const float scale = (mm.y - mm.x) / levels;
-                const float inv = scale >= 0x1p-126f && scale < 0x1p+126f ? __builtin_amdgcn_rcpf(scale) : 0.0f;
-                sc[e.half * 32 + k] = make_float4(mm.x, scale, inv, levels);
-                rec_lds[ct.w] = f2h_bits(scale) | (f2h_bits(mm.x) << 16);
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // pass 3: codes of the complete groups
-        if (e.complete) {
-            for (int k = 0; k < nc; ++k) {
-                const float4 s = sc[e.half * 32 + k];
-                const int4 ct = ctab[c0 + k];
-                const float x = lat[k * 64 + lane] - s.x;
-                float uq = 0.0f;
-                if (s.y > 0.0f) {
-                    const float pq = x * s.z;
-                    const float f = __builtin_amdgcn_fractf(pq);
-                    uq = s.z == 0.0f || fabsf(f - 0.5f) <= 0x1p-11f ? rintf(x / s.y) : rintf(pq);
-                    uq = uq < 0.0f ? 0.0f : (uq > s.w ? s.w : uq);
+        // 2. latents in chunks of up to 32 channels (one fma chain per channel),
+        //    parked in LDS, then quantised / stored channel by channel
+        const float *told = fp16 ? nullptr : T.tail + (head_base * 2 + a.sel_old[bi]) * 32 * r;
+        float *tnew = fp16 ? nullptr : T.tail + (head_base * 2 + a.sel_new[bi]) * 32 * r;
+        uint16_t *rec16 = reinterpret_cast<uint16_t *>(T.records + head_base * T.head_stride +
+                                                       static_cast<int64_t>(j) * W);
+        for (int c0 = 0; c0 < r; c0 += 32) {
+            const int nc = r - c0 < 32 ? r - c0 : 32;
+            ConstF *vb = vbase + c0;
+            if (nc == r && (nc <= 16 || (nc & 3) == 0)) {
+                // the whole row in one chunk of a compiled width
+                switch (nc <= 16 ? nc : 12 + (nc >> 2)) {
+                    case 1: project_chunk<1, 1, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 2: project_chunk<2, 2, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 3: project_chunk<3, 3, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 4: project_chunk<4, 4, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 5: project_chunk<5, 5, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 6: project_chunk<6, 6, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 7: project_chunk<7, 7, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 8: project_chunk<8, 8, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 9: project_chunk<9, 9, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 10: project_chunk<10, 10, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 11: project_chunk<11, 11, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 12: project_chunk<12, 12, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 13: project_chunk<13, 13, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 14: project_chunk<14, 14, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 15: project_chunk<15, 15, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 16: project_chunk<16, 16, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 17: project_chunk<20, 20, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 18: project_chunk<24, 24, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 19: project_chunk<28, 28, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    default: project_chunk<32, 32, BF16>(xrow, mu, vb, r, lat, lane); break;
                 }
-                const int bit = ct.x + static_cast<int>(__umul24(e.t, ct.y));
-                // codes never straddle a word: a code of width w sits at a multiple of w
-                atomicOr(rec_lds + (bit >> 5), static_cast<uint32_t>(static_cast<int>(uq)) << (bit & 31));
+            } else {
+                // other chunks: runtime row stride, width rounded up to 4
+                switch ((nc + 3) >> 2) {
+                    case 1: project_chunk<4, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 2: project_chunk<8, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 3: project_chunk<12, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 4: project_chunk<16, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 5: project_chunk<20, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 6: project_chunk<24, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    case 7: project_chunk<28, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                    default: project_chunk<32, 0, BF16>(xrow, mu, vb, r, lat, lane); break;
+                }
+            }
+            if (fp16) {
+                // fp16 latents: only new positions are stored
+                if (e.is_new)
+                    for (int k = 0; k < nc; ++k) rec16[(c0 + k) * 32 + e.t] = static_cast<uint16_t>(f2h_bits(lat[k * 64 + lane]));
+                continue;
+            }
+            // pass 1: each channel's value (old positions from the tail buffer),
+            // new latents of an incomplete group to the tail, and per half the
+            // minimum and maximum (lanes 31 and 63 record them)
+            if (any_old) {
+                // old positions of the first group: their latents from the tail
+                // buffer, into the latent buffer
+                for (int k = 0; k < nc; ++k)
+                    if (e.is_old) lat[k * 64 + lane] = told[e.t * r + c0 + k];
+            }
+            for (int k = 0; k < nc; ++k) {
+                const int c = c0 + k;
+                const float v = lat[k * 64 + lane];
+                if (!e.complete && e.touched && e.is_new) tnew[e.t * r + c] = v;
+                if (any_complete) {                      // wave-uniform
+                    float mx = row_max(v), mn = -row_max(-v);
+                    mx = fmaxf(mx, from_prev_row(mx));
+                    mn = fminf(mn, from_prev_row(mn));
+                    if (e.t == 31) *reinterpret_cast<float2 *>(sc + e.half * 32 + k) = make_float2(mn, mx);
+                }
+            }
+            if (!any_complete) continue;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // pass 2: lane (half, k) takes its group's channel c0 + k: scale by
+            // IEEE division, the reciprocal (normal scales only; 0 makes every
+            // code of the channel a division) and the metadata word
+            {
+                const int k = lane & 31;
+                if (k < nc && e.complete) {
+                    const int c = c0 + k;
+                    const int4 ct = ctab[c];
+                    const float2 mm = *reinterpret_cast<const float2 *>(sc + e.half * 32 + k);
+                    const float levels = static_cast<float>((1 << ct.z) - 1);
+                    const float scale = (mm.y - mm.x) / levels;
+                    const float inv = scale >= 0x1p-126f && scale < 0x1p+126f ? __builtin_amdgcn_rcpf(scale) : 0.0f;
+                    sc[e.half * 32 + k] = make_float4(mm.x, scale, inv, levels);
+                    rec_lds[ct.w] = f2h_bits(scale) | (f2h_bits(mm.x) << 16);
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // pass 3: codes of the complete groups
+            if (e.complete) {
+                for (int k = 0; k < nc; ++k) {
+                    const float4 s = sc[e.half * 32 + k];
+                    const int4 ct = ctab[c0 + k];
+                    const float x = lat[k * 64 + lane] - s.x;
+                    float uq = 0.0f;
+                    if (s.y > 0.0f) {
+                        const float pq = x * s.z;
+                        const float f = __builtin_amdgcn_fractf(pq);
+                        uq = s.z == 0.0f || fabsf(f - 0.5f) <= 0x1p-11f ? rintf(x / s.y) : rintf(pq);
+                        uq = uq < 0.0f ? 0.0f : (uq > s.w ? s.w : uq);
+                    }
+                    const int bit = ct.x + static_cast<int>(__umul24(e.t, ct.y));
+                    // codes never straddle a word: a code of width w sits at a multiple of w
+                    atomicOr(rec_lds + (bit >> 5), static_cast<uint32_t>(static_cast<int>(uq)) << (bit & 31));
+                }
             }
         }
-    }
 
-    // 3. complete groups: LDS record -> memory
-    if (any_complete) {
+        // 3. complete groups: LDS record -> memory
+        if (any_complete) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (e.complete) {
+                uint32_t *rec = T.records + head_base * T.head_stride + static_cast<int64_t>(j) * W;
+                for (int w = e.t; w < W; w += 32) rec[w] = rec_lds[w];
+            }
+        }
+        // the next pass reuses this wave's LDS buffers
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (e.complete) {
-            uint32_t *rec = T.records + head_base * T.head_stride + static_cast<int64_t>(j) * W;
-            for (int w = e.t; w < W; w += 32) rec[w] = rec_lds[w];
-        }
     }
 }
 
@@ -714,22 +725,26 @@ hipError_t launch_append1(const EncodeArgs &a, hipStream_t s) {
     return a.bf16 ? launch_append1_t<true>(a, s) : launch_append1_t<false>(a, s);
 }
 
-template <bool BF16>
+template <bool BF16, int REPS>
 static hipError_t launch_encode_t(const EncodeArgs &a, int max_units, hipStream_t s) {
     // set once per process (thread-safe static initialisation)
     static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(encode_kernel<BF16>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(encode_kernel<BF16, REPS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
     const int l0 = encode_lds_bytes(a.t[0].r, a.t[0].words, a.t[0].fp16_latents),
               l1 = encode_lds_bytes(a.t[1].r, a.t[1].words, a.t[1].fp16_latents);
-    hipLaunchKernelGGL(encode_kernel<BF16>, dim3((max_units + kEncWaves - 1) / kEncWaves, a.B * a.H, 2), dim3(256),
+    constexpr int per_wg = kEncWaves * REPS;
+    hipLaunchKernelGGL((encode_kernel<BF16, REPS>), dim3((max_units + per_wg - 1) / per_wg, a.B * a.H, 2), dim3(256),
                        static_cast<size_t>(l0 > l1 ? l0 : l1), s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_encode(const EncodeArgs &a, int max_units, hipStream_t s) {
-    return a.bf16 ? launch_encode_t<true>(a, max_units, s) : launch_encode_t<false>(a, max_units, s);
+    // two group pairs per wave above rank 16 (either tensor)
+    const bool wide = a.t[0].r > 16 || a.t[1].r > 16;
+    if (a.bf16) return wide ? launch_encode_t<true, 2>(a, max_units, s) : launch_encode_t<true, 1>(a, max_units, s);
+    return wide ? launch_encode_t<false, 2>(a, max_units, s) : launch_encode_t<false, 1>(a, max_units, s);
 }
 
 hipError_t launch_basis_t16(const float *src, uint16_t *dst, int G, int r, const Coder &cd, hipStream_t s) {
