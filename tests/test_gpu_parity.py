@@ -287,10 +287,13 @@ def test_calls_beyond_one_launch_group(torch):
         _check_attention(out_na[row], ref, f"allocation-free row {row} slot {sl}")
 
 
-def test_append_order_invariance(torch):
+@pytest.mark.parametrize("rank", [12, 32])
+def test_append_order_invariance(torch, rank):
     w = synth.small_workload(batch=3, n_q_heads=4, n_kv_heads=2, n_head_groups=2, prefill=150,
-                             steps=1, rank=12, seed=21)
+                             steps=1, rank=rank, seed=21)
     # same tokens appended in chunks of 1, 7, 32, 33, ... -> identical codes
+    # (rank 32: the encode kernel's two-group-pairs-per-wave variant, with
+    # chunks that start inside a group and end inside a wave's second pair)
     _run_small(torch, w, chunks=[1, 7, 32, 33, 5, 40, 1, 64])
     _run_small(torch, w, chunks=[1] * 150)
 
