@@ -56,7 +56,7 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 # conversion (the two contractions run on the matrix cores).
 PREFILL_OPS_PER_PAIR = 3.5
 METRIC = "latent decode-attend tok/s + HBM GB/s (% of peak); encode Mtok/s"
-# Host threads of one job on the GPU machines (their CPU share per GPU).
+# Host threads a benchmark job may use (a CPU share of 16 threads per GPU).
 MAX_HOST_THREADS = 16
 FLUSH_BYTES = 1 << 30          # > 256 MB last-level cache
 PROBE_GRID = 4096
