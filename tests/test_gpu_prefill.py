@@ -7,8 +7,9 @@ tokens up to its own position.  Outputs must satisfy
 GQA factors 1-8, ranks from 1 to D (every key K-step and value-block
 variant), fp16 value latents, ragged lengths with incomplete groups, several
 query tiles, chunked prefill (queries offset into the slot), repeated slots,
-empty rows, sharp softmax scales, and sampled rows at the long-context
-workload's full size.
+empty rows, sharp softmax scales, sampled rows at the long-context
+workload's full size, and three full-length rows of the ragged serving
+workload.
 """
 import numpy as np
 import pytest
@@ -230,6 +231,49 @@ def test_full_size_long_context_sampled(torch):
                                      quantize_values=w.quantize_values)
             ref = sub.prefill_attend(ks, vs, qs[b][h * g:(h + 1) * g][:, pos], pos)
             _check_attention(got[h * g:(h + 1) * g], ref, f"row {b} kv head {h}")
+
+
+def test_serving_shape_rows_sampled(torch):
+    """Three rows of the ragged serving workload (r = 32; 8 kv heads, each its
+    own head group) at their full lengths, the shortest, a middle and the
+    longest of the 64: prefill of every position in one call; sampled (row,
+    head, position) outputs against the oracle."""
+    w = synth.WORKLOADS["serve_b64_s1k16k_r32"]
+    all_lens = synth.prefill_lengths(w)
+    order = np.argsort(all_lens, kind="stable")
+    seqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    lens = all_lens[seqs].astype(np.int32)
+    B, S = len(seqs), int(lens.max())
+    k_all = synth.batch_kv(w, 0, S, seqs=seqs)
+    v_all = synth.batch_kv(w, 1, S, seqs=seqs)
+    cache = _cache(torch, w, S, max_batch=B)
+    kd, vd = _dev(torch, k_all), _dev(torch, v_all)
+    cache.fit(kd, vd, lens)
+    cache.encode_append(kd, vd, n_new=lens)
+    from test_gpu_parity import _layer
+    layer = _layer(cache, w)
+    qs = [synth.prefill_queries(w, b, int(lens[i])) for i, b in enumerate(seqs)]
+    q = torch.zeros((B, w.n_q_heads, S, w.head_dim), dtype=torch.float16, device="cuda")
+    for i in range(B):
+        q[i, :, :lens[i]] = torch.from_numpy(qs[i]).cuda()
+    out = cache.prefill_attend(q, n_q=lens)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    rng = np.random.default_rng(6)
+    g = w.n_q_heads // w.n_kv_heads
+    for i in range(B):
+        n = int(lens[i])
+        pos = np.unique(np.concatenate([[0, 1, 31, 32, n // 2, n - 33, n - 1], rng.integers(0, n, 4)]))
+        got = out[i][:, pos].cpu().numpy()
+        for hq in (0, 13, 31):
+            h = hq // g
+            ks = [layer.encode_head(k_all[i, h, :n], h, 0)]
+            vs = [layer.encode_head(v_all[i, h, :n], h, 1)]
+            sub = oracle.OracleLayer(w.head_dim, g, 1, 1, _sub_fit(layer.fit[0], layer.group_of(h)),
+                                     _sub_fit(layer.fit[1], layer.group_of(h)),
+                                     quantize_values=w.quantize_values)
+            ref = sub.prefill_attend(ks, vs, qs[i][h * g:(h + 1) * g][:, pos], pos)
+            _check_attention(got[h * g:(h + 1) * g], ref, f"sequence {seqs[i]} (length {n}) kv head {h}")
 
 
 def _sub_fit(f, grp):
