@@ -8,8 +8,8 @@ GQA factors 1-8, ranks from 1 to D (every key K-step and value-block
 variant), fp16 value latents, ragged lengths with incomplete groups, several
 query tiles, chunked prefill (queries offset into the slot), repeated slots,
 empty rows, sharp softmax scales, sampled rows at the long-context
-workload's full size, and three full-length rows of the ragged serving
-workload.
+workload's full size, and full-length rows of the ragged serving and the
+fp16-value-latent workloads.
 """
 import numpy as np
 import pytest
@@ -233,15 +233,17 @@ def test_full_size_long_context_sampled(torch):
             _check_attention(got[h * g:(h + 1) * g], ref, f"row {b} kv head {h}")
 
 
-def test_serving_shape_rows_sampled(torch):
-    """Three rows of the ragged serving workload (r = 32; 8 kv heads, each its
-    own head group) at their full lengths, the shortest, a middle and the
-    longest of the 64: prefill of every position in one call; sampled (row,
+@pytest.mark.parametrize("name", ["serve_b64_s1k16k_r32", "vlat16_b8_s8192_r64"])
+def test_workload_rows_sampled(torch, name):
+    """Full-length rows of the ragged serving workload (r = 32; 8 kv heads,
+    each its own head group: the shortest, a middle and the longest of the
+    64) and of the fp16-value-latent workload (r = 64: two key K-steps, five
+    value blocks): prefill of every position in one call; sampled (row,
     head, position) outputs against the oracle."""
-    w = synth.WORKLOADS["serve_b64_s1k16k_r32"]
+    w = synth.WORKLOADS[name]
     all_lens = synth.prefill_lengths(w)
     order = np.argsort(all_lens, kind="stable")
-    seqs = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    seqs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
     lens = all_lens[seqs].astype(np.int32)
     B, S = len(seqs), int(lens.max())
     k_all = synth.batch_kv(w, 0, S, seqs=seqs)
