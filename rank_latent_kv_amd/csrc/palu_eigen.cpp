@@ -25,6 +25,20 @@ namespace palu {
 
 namespace {
 
+// sqrt(f^2 + g^2): directly when the squares can neither overflow nor
+// lose the smaller operand to underflow, else with the larger magnitude
+// factored out.  The rotations of a QL sweep form one dependency chain, so
+// this (and one reciprocal per rotation instead of two divisions) sets the
+// sweep's speed; std::hypot took most of it.
+inline double pythag(double f, double g) {
+    const double af = std::fabs(f), ag = std::fabs(g);
+    const double a = std::max(af, ag);
+    if (a > 1e-150 && a < 1e150) return std::sqrt(f * f + g * g);
+    if (a == 0.0) return 0.0;
+    const double q = std::min(af, ag) / a;
+    return a * std::sqrt(1.0 + q * q);
+}
+
 // Implicit-shift QL on the tridiagonal (d, e); the rotations are applied to
 // the rows of zt (which enters holding Q^T, so row i is column i of Q and the
 // two rows a rotation touches are contiguous), or to nothing when zt is
@@ -56,7 +70,7 @@ bool tridiagonal_ql(double *d, double *e, int n, double *zt) {
             for (; i >= l; --i) {
                 const double f = s * e[i];
                 const double b = c * e[i];
-                r = std::hypot(f, g);
+                r = pythag(f, g);
                 e[i + 1] = r;
                 if (r == 0.0) {  // split: restart on the smaller problem
                     d[i + 1] -= p;
@@ -64,8 +78,9 @@ bool tridiagonal_ql(double *d, double *e, int n, double *zt) {
                     underflow = true;
                     break;
                 }
-                s = f / r;
-                c = g / r;
+                const double inv = 1.0 / r;
+                s = f * inv;
+                c = g * inv;
                 g = d[i + 1] - p;
                 r = (d[i] - g) * s + 2.0 * c * b;
                 p = s * r;
@@ -112,12 +127,19 @@ void reduce_keep(double *a, int n, double *d, double *e, double *hv, double *bet
         for (int i = 0; i < m; ++i) vv += v[i] * v[i];
         if (vv == 0.0) continue;
         const double bt = 2.0 / vv;
+        // p = bt A v over the trailing block, as a sum of its rows (the
+        // block is exactly symmetric: the rank-2 updates below keep it so),
+        // so that the inner loop runs over independent entries of p and
+        // vectorises; each p[i] still sums its terms in order j = 0 .. m-1
+        for (int i = 0; i < m; ++i) p[i] = 0.0;
+        for (int j = 0; j < m; ++j) {
+            const double vj = v[j];
+            const double *row = a + (k + 1 + j) * n + (k + 1);
+            for (int i = 0; i < m; ++i) p[i] += row[i] * vj;
+        }
         double pv = 0.0;
         for (int i = 0; i < m; ++i) {
-            double acc = 0.0;
-            const double *row = a + (k + 1 + i) * n + (k + 1);
-            for (int j = 0; j < m; ++j) acc += row[j] * v[j];
-            p[i] = bt * acc;
+            p[i] *= bt;
             pv += p[i] * v[i];
         }
         const double K = 0.5 * bt * pv;
