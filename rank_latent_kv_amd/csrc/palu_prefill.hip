@@ -25,8 +25,12 @@
 // A complete group comes from its packed record (code * fp16 scale + fp16
 // zero in fp16, the decode kernel's dequantisation).  The incomplete group
 // comes from the fp32 tail (or the partial fp16 record) rounded to fp16.
-// Records are copied global -> LDS two groups ahead (direct 16-byte loads
-// into LDS); tiles are built one group ahead; one barrier per group.
+// Groups go in pairs, one barrier per pair.  Without a workspace (PRE =
+// false) records are copied global -> LDS two pairs ahead (direct 16-byte
+// loads into LDS) and the tiles built one pair ahead; with one (PRE = true)
+// prefill_tiles_kernel has decoded every complete group's tile pair into it
+// once, with the same arithmetic, and the tile pairs are copied global ->
+// LDS one pair ahead instead (only the incomplete group is built here).
 //
 // Per wave and group: scores S^T[t][col] = sum_k Khat[t][k] Qt[col][k] on
 // v_mfma_f32_16x16x32_f16 (two 16-token halves, KS K-steps, NQ column
