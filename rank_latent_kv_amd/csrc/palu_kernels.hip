@@ -257,6 +257,7 @@ template <int W, int RS, bool BF16>
 __device__ __forceinline__ void project_chunk(const uint16_t *xrow, ConstF *mu, ConstF *vb, int r, float *lat,
                                               int lane) {
     constexpr int QD = W > 16 ? 16 : 32, NX = QD / 8;   // rows per step, 16-byte input pieces per step
+    constexpr int kSteps = kHeadDim / QD, kStepUnroll = W > 16 ? 2 : kSteps;
     const int rs = RS ? RS : r;
     float l[W];
 #pragma unroll
@@ -265,8 +266,8 @@ __device__ __forceinline__ void project_chunk(const uint16_t *xrow, ConstF *mu, 
     uint4 xa[NX];
 #pragma unroll
     for (int k = 0; k < NX; ++k) xa[k] = *reinterpret_cast<const uint4 *>(xrow + 8 * k);
-#pragma unroll (W > 16 ? 2 : kHeadDim / QD)
-    for (int q = 0; q < kHeadDim / QD; ++q) {
+#pragma unroll kStepUnroll
+    for (int q = 0; q < kSteps; ++q) {
         uint4 xb[NX];
         const int qn = q + 1 < kHeadDim / QD ? q + 1 : q;
 #pragma unroll
