@@ -3,10 +3,16 @@
 // eigensolve, and kernel launches.  Implements include/palu.h.
 #include <hip/hip_runtime_api.h>
 
+#include <unistd.h>
+
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <condition_variable>
 #include <cstdint>
 #include <cstring>
+#include <functional>
+#include <mutex>
 #include <numeric>
 #include <string>
 #include <thread>
@@ -563,17 +569,99 @@ struct FitProblem {
     bool ok = false;
 };
 
+// Host worker threads kept for the life of the process: spawning and
+// joining eight threads per call cost 0.1-0.2 ms, and a fit makes two such
+// calls.  Items are handed out one at a time to the workers and to the
+// calling thread; calls from several host threads queue on call_mu_.  Each
+// call waits until every worker has seen it, so no worker still reads a
+// call's job when the next one starts.  A forked child (which has none of
+// its parent's threads) starts workers of its own.
+class HostPool {
+public:
+    void run(int count, const std::function<void(int)> &f) {
+        if (count <= 1) {
+            for (int i = 0; i < count; ++i) f(i);
+            return;
+        }
+        std::lock_guard<std::mutex> call(call_mu_);
+        start_workers();
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            job_ = &f;
+            count_ = count;
+            next_.store(0);
+            pending_ = static_cast<int>(workers_->size());
+            ++gen_;
+        }
+        cv_.notify_all();
+        take_items();
+        std::unique_lock<std::mutex> lk(mu_);
+        done_cv_.wait(lk, [&] { return pending_ == 0; });
+        job_ = nullptr;
+    }
+    ~HostPool() {
+        if (!workers_ || pid_ != getpid()) return;
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            stop_ = true;
+        }
+        cv_.notify_all();
+        for (auto &t : *workers_) t.join();
+        delete workers_;
+    }
+
+private:
+    void start_workers() {
+        if (workers_ && pid_ == getpid()) return;
+        // (after a fork the parent's thread objects are dropped unjoined:
+        // leaked on purpose, their threads do not exist here)
+        pid_ = getpid();
+        stop_ = false;
+        const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+        const int n = static_cast<int>(std::min(hw, 16u)) - 1;
+        workers_ = new std::vector<std::thread>();
+        // the generation before this call's: a worker that starts late
+        // still takes part in it (gen_ changes only under call_mu_)
+        const uint64_t g0 = gen_;
+        for (int w = 0; w < n; ++w) workers_->emplace_back([this, g0] { worker(g0); });
+    }
+    void take_items() {
+        for (int i = next_.fetch_add(1); i < count_; i = next_.fetch_add(1)) (*job_)(i);
+    }
+    void worker(uint64_t seen) {
+        for (;;) {
+            {
+                std::unique_lock<std::mutex> lk(mu_);
+                cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+                if (stop_) return;
+                seen = gen_;
+            }
+            take_items();
+            std::lock_guard<std::mutex> lk(mu_);
+            if (--pending_ == 0) done_cv_.notify_one();
+        }
+    }
+
+    std::mutex call_mu_, mu_;
+    std::condition_variable cv_, done_cv_;
+    std::vector<std::thread> *workers_ = nullptr;
+    pid_t pid_ = 0;
+    const std::function<void(int)> *job_ = nullptr;
+    int count_ = 0, pending_ = 0;
+    std::atomic<int> next_{0};
+    uint64_t gen_ = 0;
+    bool stop_ = false;
+};
+
+HostPool &host_pool() {
+    static HostPool pool;
+    return pool;
+}
+
 // f(i) for i < count on host threads (the problems are independent).
 template <typename F>
 void parallel_for(int count, F f) {
-    const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
-    const int nthreads = static_cast<int>(std::min<unsigned>(hw, static_cast<unsigned>(std::max(1, count))));
-    std::vector<std::thread> pool;
-    for (int th = 0; th < nthreads; ++th)
-        pool.emplace_back([&, th]() {
-            for (int i = th; i < count; i += nthreads) f(i);
-        });
-    for (auto &t : pool) t.join();
+    host_pool().run(count, std::function<void(int)>(f));
 }
 
 // Step 1 of every problem: scatter matrix, reduction, eigenvalues.
