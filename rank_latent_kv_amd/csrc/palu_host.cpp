@@ -1146,6 +1146,8 @@ int decode_attend(palu_cache *c, const void *q, void *out, const int32_t *seq_id
                 // workgroup per CU: the prologue and the merge of a split
                 // are then paid once per two passes
                 if (chunk < 2 * per_pass && units / (2 * per_pass) >= cus) chunk = 2 * per_pass;
+                // and four while that still leaves two per CU
+                if (chunk < 4 * per_pass && units / (4 * per_pass) >= 2 * cus) chunk = 4 * per_pass;
                 // ragged rows round their last split up: grow the split by
                 // whole passes until the launch's exact workgroup count fits
                 // the target (no second, partial round of workgroups)
